@@ -1,0 +1,258 @@
+"""ctypes binding of libkfac (include/kfac.h): argument marshalling only.
+
+Every function has the name of the C entry point it calls and takes torch tensors
+that live on the current HIP device; it passes their data pointers, the sizes and
+the current torch stream (or the one given) to the library, and raises KfacError
+when the library returns a non-zero status. Nothing here computes any part of the
+K-FAC step, and there is no fallback: without the built library, import fails.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkfac.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is not built; run `python -m fac_second_order_amd.build` "
+        "(hipcc, gfx950) first. There is no CPU fallback.")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+KFAC_F16 = 0
+KFAC_F32 = 1
+_STATUS = {0: "KFAC_OK", -1: "KFAC_ERR_INVALID", -2: "KFAC_ERR_UNSUPPORTED",
+           -3: "KFAC_ERR_WORKSPACE", -4: "KFAC_ERR_HIP"}
+
+
+class KfacError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        msg = _lib.kfac_last_error().decode(errors="replace")
+        super().__init__(f"{where}: {_STATUS.get(status, status)}: {msg}")
+
+
+class kfac_layer(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_int32) for f in
+                ("n", "h", "w", "c_in", "h_out", "w_out", "c_out",
+                 "kh", "kw", "sh", "sw", "ph", "pw", "bias")]
+
+
+class kfac_bn(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int32), ("hw", ctypes.c_int32), ("c", ctypes.c_int32)]
+
+
+_c = ctypes
+_vp, _i32, _sz, _f32 = _c.c_void_p, _c.c_int32, _c.c_size_t, _c.c_float
+_P = _c.POINTER
+
+
+def _sig(name, res, *args):
+    f = getattr(_lib, name)
+    f.restype = res
+    f.argtypes = list(args)
+    return f
+
+
+_sig("kfac_version", _i32)
+_sig("kfac_status_string", _c.c_char_p, _i32)
+_sig("kfac_last_error", _c.c_char_p)
+_sig("kfac_factors_workspace", _i32, _P(kfac_layer), _i32, _i32, _P(_sz))
+_sig("kfac_factors", _i32, _P(kfac_layer), _i32, _i32, _P(_vp), _P(_vp), _P(_vp), _P(_vp), _f32,
+     _vp, _sz, _vp)
+_sig("kfac_pack_sym_workspace", _i32, _i32, _P(_i32), _P(_sz))
+_sig("kfac_pack_sym", _i32, _i32, _P(_i32), _P(_vp), _P(_vp), _i32, _vp, _sz, _vp)
+_sig("kfac_invert_workspace", _i32, _i32, _P(_i32), _P(_sz))
+_sig("kfac_invert", _i32, _i32, _P(_i32), _P(_vp), _P(_vp), _P(_f32), _vp, _P(_vp), _vp, _sz, _vp)
+_sig("kfac_precondition_workspace", _i32, _i32, _P(_i32), _P(_i32), _P(_sz))
+_sig("kfac_precondition", _i32, _i32, _P(_i32), _P(_i32), _P(_vp), _P(_vp), _P(_vp), _i32, _P(_vp),
+     _vp, _sz, _vp)
+_sig("kfac_bn_diag_workspace", _i32, _P(kfac_bn), _i32, _P(_sz))
+_sig("kfac_bn_diag", _i32, _P(kfac_bn), _i32, _i32, _P(_vp), _P(_vp), _P(_vp), _P(_vp), _f32, _f32,
+     _vp, _sz, _vp)
+_sig("kfac_timing_kernels", _i32)
+_sig("kfac_kernel_name", _c.c_char_p, _i32)
+_sig("kfac_timing_enable", _i32, _i32)
+_sig("kfac_timing_reset", _i32)
+_sig("kfac_timing_read", _i32, _i32, _P(_c.c_double), _P(_c.c_int64))
+
+
+def _check(status, where):
+    if status != 0:
+        raise KfacError(status, where)
+
+
+def _ptrs(tensors):
+    arr = (_vp * max(1, len(tensors)))()
+    for i, t in enumerate(tensors):
+        arr[i] = None if t is None else t.data_ptr()
+    return arr
+
+
+def _ints(vals):
+    arr = (_i32 * max(1, len(vals)))()
+    for i, v in enumerate(vals):
+        arr[i] = int(v)
+    return arr
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return _vp(s.cuda_stream)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float16:
+        return KFAC_F16
+    if t.dtype == torch.float32:
+        return KFAC_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _layers(layers):
+    arr = (kfac_layer * max(1, len(layers)))()
+    for i, l in enumerate(layers):
+        for f, _ in kfac_layer._fields_:
+            setattr(arr[i], f, int(getattr(l, f) if not isinstance(l, dict) else l[f]))
+    return arr
+
+
+def _bns(layers):
+    arr = (kfac_bn * max(1, len(layers)))()
+    for i, l in enumerate(layers):
+        for f, _ in kfac_bn._fields_:
+            setattr(arr[i], f, int(getattr(l, f) if not isinstance(l, dict) else l[f]))
+    return arr
+
+
+def _ws(workspace, nbytes, device):
+    """The caller's workspace, or a fresh torch allocation of nbytes (256-aligned)."""
+    if nbytes == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+    ptr = workspace.data_ptr()
+    pad = (-ptr) % 256
+    return _vp(ptr + pad), workspace.numel() * workspace.element_size() - pad
+
+
+# ---------------------------------------------------------------------------
+# entry points
+# ---------------------------------------------------------------------------
+
+def kfac_version():
+    return _lib.kfac_version()
+
+
+def kfac_factors_workspace(layers, in_dtype=KFAC_F16):
+    out = _sz()
+    _check(_lib.kfac_factors_workspace(_layers(layers), len(layers), in_dtype, _c.byref(out)),
+           "kfac_factors_workspace")
+    return out.value
+
+
+def kfac_factors(layers, act, gout, A_packed, G_packed, ema_decay=0.0, workspace=None, stream=None):
+    """A_packed[l], G_packed[l] <- packed factors of layer l (see kfac.h)."""
+    first = next(t for t in list(act) + list(gout) if t is not None)
+    dt = _dtype_code(first)
+    for t in list(act) + list(gout):
+        if t is not None and (t.dtype != first.dtype or not t.is_contiguous()):
+            raise TypeError("factor inputs must share one dtype and be contiguous")
+    need = kfac_factors_workspace(layers, dt)
+    ws, wsb = _ws(workspace, need, first.device)
+    _check(_lib.kfac_factors(_layers(layers), len(layers), dt, _ptrs(act), _ptrs(gout),
+                             _ptrs(A_packed), _ptrs(G_packed), float(ema_decay), ws, wsb,
+                             _stream(stream)), "kfac_factors")
+
+
+def kfac_pack_sym_workspace(n):
+    out = _sz()
+    _check(_lib.kfac_pack_sym_workspace(len(n), _ints(n), _c.byref(out)), "kfac_pack_sym_workspace")
+    return out.value
+
+
+def kfac_pack_sym(n, full, packed, direction, workspace=None, stream=None):
+    """direction 0: packed <- upper(full); 1: full <- symmetric(packed)."""
+    need = kfac_pack_sym_workspace(n)
+    ws, wsb = _ws(workspace, need, full[0].device if full else None)
+    _check(_lib.kfac_pack_sym(len(n), _ints(n), _ptrs(full), _ptrs(packed), int(direction), ws, wsb,
+                              _stream(stream)), "kfac_pack_sym")
+
+
+def kfac_invert_workspace(n):
+    out = _sz()
+    _check(_lib.kfac_invert_workspace(len(n), _ints(n), _c.byref(out)), "kfac_invert_workspace")
+    return out.value
+
+
+def kfac_invert(n, mat, inv, shift, info, chol=None, workspace=None, stream=None):
+    """inv[m] <- (sym(mat[m]) + shift[m] I)^-1; info (int32 device tensor) <- breakdown index."""
+    need = kfac_invert_workspace(n)
+    ws, wsb = _ws(workspace, need, mat[0].device if mat else None)
+    sh = (_f32 * max(1, len(n)))(*[float(s) for s in shift])
+    if info.dtype != torch.int32 or info.numel() < len(n):
+        raise TypeError("info must be an int32 tensor with one entry per matrix")
+    _check(_lib.kfac_invert(len(n), _ints(n), _ptrs(mat), _ptrs(inv), sh, _vp(info.data_ptr()),
+                            _ptrs(chol) if chol is not None else None, ws, wsb, _stream(stream)),
+           "kfac_invert")
+
+
+def kfac_precondition_workspace(d_g, d_a):
+    out = _sz()
+    _check(_lib.kfac_precondition_workspace(len(d_g), _ints(d_g), _ints(d_a), _c.byref(out)),
+           "kfac_precondition_workspace")
+    return out.value
+
+
+def kfac_precondition(d_g, d_a, G_inv, A_inv, grad, out, workspace=None, stream=None):
+    """out[l] <- G_inv[l] @ grad[l] @ A_inv[l] (fp32)."""
+    dt = _dtype_code(grad[0])
+    need = kfac_precondition_workspace(d_g, d_a)
+    ws, wsb = _ws(workspace, need, grad[0].device)
+    _check(_lib.kfac_precondition(len(d_g), _ints(d_g), _ints(d_a), _ptrs(G_inv), _ptrs(A_inv),
+                                  _ptrs(grad), dt, _ptrs(out), ws, wsb, _stream(stream)),
+           "kfac_precondition")
+
+
+def kfac_bn_diag_workspace(layers):
+    out = _sz()
+    _check(_lib.kfac_bn_diag_workspace(_bns(layers), len(layers), _c.byref(out)), "kfac_bn_diag_workspace")
+    return out.value
+
+
+def kfac_bn_diag(layers, xhat, gout, fisher, precond, ema_decay=0.0, shift=1e-3, workspace=None,
+                 stream=None):
+    """fisher[l], precond[l] ([2, c] fp32) <- BN diagonal Fisher and grad/(F+shift)."""
+    dt = _dtype_code(xhat[0])
+    need = kfac_bn_diag_workspace(layers)
+    ws, wsb = _ws(workspace, need, xhat[0].device)
+    _check(_lib.kfac_bn_diag(_bns(layers), len(layers), dt, _ptrs(xhat), _ptrs(gout), _ptrs(fisher),
+                             _ptrs(precond), float(ema_decay), float(shift), ws, wsb, _stream(stream)),
+           "kfac_bn_diag")
+
+
+# timing -------------------------------------------------------------------
+
+def kfac_timing_kernels():
+    return _lib.kfac_timing_kernels()
+
+
+def kfac_kernel_name(i):
+    return _lib.kfac_kernel_name(int(i)).decode()
+
+
+def kfac_timing_enable(on=True):
+    _check(_lib.kfac_timing_enable(1 if on else 0), "kfac_timing_enable")
+
+
+def kfac_timing_reset():
+    _check(_lib.kfac_timing_reset(), "kfac_timing_reset")
+
+
+def kfac_timing_read(i):
+    ms = _c.c_double()
+    n = _c.c_int64()
+    _check(_lib.kfac_timing_read(int(i), _c.byref(ms), _c.byref(n)), "kfac_timing_read")
+    return ms.value, n.value

@@ -1,0 +1,294 @@
+// BatchNorm diagonal Fisher for all BN layers in two launches.
+// Osawa et al. (CVPR 2019), Section 1 contributions: BatchNorm's Fisher is taken
+// diagonal; the diagonal is that of the empirical Fisher of Section 3.1, eq. (3),
+// over the per-sample gradients of gamma and beta.
+//
+// Stage 1 (bn_partial_kernel) streams x-hat and the output gradient once from HBM
+// with 16-byte loads along the channel dimension (NHWC, channels contiguous). A work
+// item is (layer, sample, spatial chunk, channel block); it writes the chunk's
+// per-channel partial sums (sum g*x, sum g) to the workspace.
+// Stage 2 (bn_finish_kernel), one thread per channel, adds the chunks of each
+// sample in a fixed order (deterministic), squares the per-sample sums, averages
+// over samples, blends with the stored Fisher when asked and divides.
+#include "common.hpp"
+
+namespace kfac {
+
+struct BnDesc {
+  const void* xhat;
+  const void* gout;
+  float* fisher;
+  float* precond;
+  float2* partial;  // [n][nchunk][c] (sum g*x, sum g)
+  int32_t n, hw, c;
+  int32_t vl;       // vector lanes per row segment (<= 256)
+  int32_t rowpar;   // rows processed side by side (256 / vl)
+  int32_t cblocks;  // channel blocks of vl*ev channels
+  int32_t rows_per_chunk, nchunk;
+  int32_t vec;      // 1: 16-byte vectors along channels
+  int32_t pad_;
+};
+
+template <class T>
+struct Vec16;
+template <>
+struct Vec16<_Float16> {
+  static constexpr int ev = 8;
+};
+template <>
+struct Vec16<float> {
+  static constexpr int ev = 4;
+};
+
+template <class T, int EV>
+__device__ inline void load_vec(const T* p, float* out) {
+  if constexpr (EV == 1) {
+    out[0] = static_cast<float>(p[0]);
+  } else if constexpr (sizeof(T) == 2) {
+    v8h v = *reinterpret_cast<const v8h*>(p);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) out[q] = static_cast<float>(v[q]);
+  } else {
+    v4f v = *reinterpret_cast<const v4f*>(p);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) out[q] = v[q];
+  }
+}
+
+template <class T, int EV>
+__device__ void bn_partial_body(const BnDesc& d, int item) {
+  // item -> (sample, chunk, channel block)
+  const int cb = item % d.cblocks;
+  const int rest = item / d.cblocks;
+  const int chunk = rest % d.nchunk;
+  const int s = rest / d.nchunk;
+  const int lane = threadIdx.x % d.vl;
+  const int rp = threadIdx.x / d.vl;
+  const int c0 = cb * d.vl * EV + lane * EV;
+  const int r_begin = chunk * d.rows_per_chunk;
+  const int r_end = min(d.hw, r_begin + d.rows_per_chunk);
+  float sg[EV], sb[EV];
+#pragma unroll
+  for (int q = 0; q < EV; ++q) sg[q] = sb[q] = 0.f;
+  const bool active = rp < d.rowpar && c0 < d.c;
+  if (active) {
+    const T* X = static_cast<const T*>(d.xhat) + (int64_t(s) * d.hw) * d.c + c0;
+    const T* G = static_cast<const T*>(d.gout) + (int64_t(s) * d.hw) * d.c + c0;
+    for (int r = r_begin + rp; r < r_end; r += d.rowpar) {
+      float x[EV], g[EV];
+      load_vec<T, EV>(X + int64_t(r) * d.c, x);
+      load_vec<T, EV>(G + int64_t(r) * d.c, g);
+#pragma unroll
+      for (int q = 0; q < EV; ++q) {
+        sg[q] = fmaf(g[q], x[q], sg[q]);
+        sb[q] += g[q];
+      }
+    }
+  }
+  // reduce the rowpar partial rows that share a channel through LDS
+  __shared__ float2 red[256 * 8];
+#pragma unroll
+  for (int q = 0; q < EV; ++q) red[threadIdx.x * EV + q] = make_float2(sg[q], sb[q]);
+  __syncthreads();
+  const int width = d.vl * EV;  // channels in this block
+  for (int ch = threadIdx.x; ch < width; ch += blockDim.x) {
+    const int c = cb * width + ch;
+    if (c >= d.c) continue;
+    const int l = ch / EV, q = ch % EV;
+    float a = 0.f, b = 0.f;
+    for (int r = 0; r < d.rowpar; ++r) {
+      float2 v = red[(r * d.vl + l) * EV + q];
+      a += v.x;
+      b += v.y;
+    }
+    d.partial[(int64_t(s) * d.nchunk + chunk) * d.c + c] = make_float2(a, b);
+  }
+}
+
+__global__ void __launch_bounds__(256) bn_partial_kernel(const BnDesc* __restrict__ desc,
+                                                         const int32_t* __restrict__ begin,
+                                                         int count, int f32) {
+  const int p = find_problem(begin, count, blockIdx.x);
+  const BnDesc d = desc[p];
+  const int item = blockIdx.x - begin[p];
+  if (f32) {
+    if (d.vec) bn_partial_body<float, 4>(d, item);
+    else bn_partial_body<float, 1>(d, item);
+  } else {
+    if (d.vec) bn_partial_body<_Float16, 8>(d, item);
+    else bn_partial_body<_Float16, 1>(d, item);
+  }
+}
+
+__global__ void __launch_bounds__(256) bn_finish_kernel(const BnDesc* __restrict__ desc,
+                                                        const int32_t* __restrict__ cbegin,
+                                                        int count, int total, float decay,
+                                                        float shift) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= total) return;
+  const int p = find_problem(cbegin, count, t);
+  const BnDesc d = desc[p];
+  const int c = t - cbegin[p];
+  float fg = 0.f, fb = 0.f, gg = 0.f, gb = 0.f;
+  for (int s = 0; s < d.n; ++s) {
+    float a = 0.f, b = 0.f;
+    for (int k = 0; k < d.nchunk; ++k) {
+      float2 v = d.partial[(int64_t(s) * d.nchunk + k) * d.c + c];
+      a += v.x;
+      b += v.y;
+    }
+    fg = fmaf(a, a, fg);
+    fb = fmaf(b, b, fb);
+    gg += a;
+    gb += b;
+  }
+  const float inv_n = 1.0f / static_cast<float>(d.n);
+  fg *= inv_n;
+  fb *= inv_n;
+  gg *= inv_n;
+  gb *= inv_n;
+  if (decay != 0.f) {
+    fg = decay * d.fisher[c] + (1.f - decay) * fg;
+    fb = decay * d.fisher[d.c + c] + (1.f - decay) * fb;
+  }
+  d.fisher[c] = fg;
+  d.fisher[d.c + c] = fb;
+  d.precond[c] = gg / (fg + shift);
+  d.precond[d.c + c] = gb / (fb + shift);
+}
+
+// Plans one layer: 16-byte vectors along channels when `vec`, else scalar loads.
+static BnDesc plan_layer(const kfac_bn& L, int esize, bool vec) {
+  BnDesc d{};
+  d.n = L.n;
+  d.hw = L.hw;
+  d.c = L.c;
+  const int ev_full = 16 / esize;
+  d.vec = (vec && d.c % ev_full == 0) ? 1 : 0;
+  const int ev = d.vec ? ev_full : 1;
+  const int groups = (d.c + ev - 1) / ev;
+  d.vl = groups < 256 ? groups : 256;
+  d.rowpar = 256 / d.vl;
+  d.cblocks = (groups + d.vl - 1) / d.vl;
+  const int64_t row_bytes = int64_t(d.vl) * ev * esize;
+  int64_t rpc = (64 * 1024) / row_bytes;  // about 64 KB of each tensor per work item
+  if (rpc < d.rowpar) rpc = d.rowpar;
+  rpc = (rpc / d.rowpar) * d.rowpar;
+  if (rpc > d.hw) rpc = d.hw;
+  d.rows_per_chunk = static_cast<int32_t>(rpc);
+  d.nchunk = static_cast<int32_t>((d.hw + rpc - 1) / rpc);
+  return d;
+}
+
+static size_t partial_count(const BnDesc& d) { return size_t(d.n) * d.nchunk * d.c; }
+
+// Workspace: descriptors, two offset tables, then the partial sums. The bound takes
+// the larger partial buffer of the vector and scalar plans of each layer for either
+// input dtype, so any alignment seen at call time fits.
+static size_t bn_ws_bound(const kfac_bn* L, int count) {
+  size_t part = 0;
+  for (int l = 0; l < count; ++l) {
+    size_t m = 0;
+    for (int esize : {2, 4})
+      for (bool vec : {true, false}) {
+        size_t c = partial_count(plan_layer(L[l], esize, vec));
+        m = c > m ? c : m;
+      }
+    part += m;
+  }
+  return align256(sizeof(BnDesc) * count) + 2 * align256(sizeof(int32_t) * count) +
+         align256(sizeof(float2) * part);
+}
+
+}  // namespace kfac
+
+using namespace kfac;
+
+static kfac_status bn_validate(const kfac_bn* L, int32_t count, kfac_dtype dt) {
+  if (count < 0) return fail(KFAC_ERR_INVALID, "count must be >= 0");
+  if (count > 0 && !L) return fail(KFAC_ERR_INVALID, "layers is NULL");
+  if (dt != KFAC_F16 && dt != KFAC_F32) return fail(KFAC_ERR_UNSUPPORTED, "dtype %d not supported", dt);
+  for (int l = 0; l < count; ++l) {
+    if (L[l].n < 1 || L[l].hw < 1 || L[l].c < 1)
+      return fail(KFAC_ERR_INVALID, "bn layer %d: n, hw, c must be >= 1", l);
+    if (int64_t(L[l].n) * L[l].hw * L[l].c >= (int64_t(1) << 40))
+      return fail(KFAC_ERR_INVALID, "bn layer %d too large", l);
+  }
+  return KFAC_OK;
+}
+
+extern "C" kfac_status kfac_bn_diag_workspace(const kfac_bn* layers, int32_t count, size_t* bytes) {
+  if (!bytes) return fail(KFAC_ERR_INVALID, "bytes is NULL");
+  kfac_status st = bn_validate(layers, count, KFAC_F16);
+  if (st) return st;
+  *bytes = count ? bn_ws_bound(layers, count) : 0;
+  return KFAC_OK;
+}
+
+extern "C" kfac_status kfac_bn_diag(const kfac_bn* layers, int32_t count, kfac_dtype in_dtype,
+                                    const void* const* xhat, const void* const* gout,
+                                    float* const* fisher, float* const* precond, float ema_decay,
+                                    float shift, void* workspace, size_t ws_bytes, void* stream) {
+  kfac_status st = bn_validate(layers, count, in_dtype);
+  if (st) return st;
+  if (!(ema_decay >= 0.f && ema_decay <= 1.f)) return fail(KFAC_ERR_INVALID, "ema_decay must be in [0, 1]");
+  if (!(shift == shift)) return fail(KFAC_ERR_INVALID, "shift is NaN");
+  if (count == 0) return KFAC_OK;
+  if (!xhat || !gout || !fisher || !precond) return fail(KFAC_ERR_INVALID, "NULL pointer array");
+  const int esize = in_dtype == KFAC_F16 ? 2 : 4;
+  std::vector<BnDesc> desc(count);
+  std::vector<int32_t> begin(count), cbegin(count);
+  int64_t items = 0, channels = 0;
+  size_t part = 0;
+  for (int l = 0; l < count; ++l) {
+    if (!xhat[l] || !gout[l] || !fisher[l] || !precond[l])
+      return fail(KFAC_ERR_INVALID, "bn layer %d: NULL pointer", l);
+    const uintptr_t a = reinterpret_cast<uintptr_t>(xhat[l]) | reinterpret_cast<uintptr_t>(gout[l]);
+    if (a % esize || (reinterpret_cast<uintptr_t>(fisher[l]) | reinterpret_cast<uintptr_t>(precond[l])) & 3)
+      return fail(KFAC_ERR_INVALID, "bn layer %d: misaligned pointer", l);
+    desc[l] = plan_layer(layers[l], esize, a % 16 == 0);
+    begin[l] = static_cast<int32_t>(items);
+    items += int64_t(desc[l].n) * desc[l].nchunk * desc[l].cblocks;
+    cbegin[l] = static_cast<int32_t>(channels);
+    channels += desc[l].c;
+    part += partial_count(desc[l]);
+  }
+  if (items >= (int64_t(1) << 31) || channels >= (int64_t(1) << 31))
+    return fail(KFAC_ERR_INVALID, "bn problem too large");
+  st = check_device();
+  if (st) return st;
+  const size_t need = align256(sizeof(BnDesc) * count) + 2 * align256(sizeof(int32_t) * count) +
+                      align256(sizeof(float2) * part);
+  st = check_workspace(workspace, ws_bytes, need);
+  if (st) return st;
+  Carver cv(workspace);
+  BnDesc* d_desc = cv.take<BnDesc>(count);
+  int32_t* d_begin = cv.take<int32_t>(count);
+  int32_t* d_cbegin = cv.take<int32_t>(count);
+  float2* partial = cv.take<float2>(part);
+  size_t off = 0;
+  for (int l = 0; l < count; ++l) {
+    BnDesc& d = desc[l];
+    d.xhat = xhat[l];
+    d.gout = gout[l];
+    d.fisher = fisher[l];
+    d.precond = precond[l];
+    d.partial = partial + off;
+    off += partial_count(d);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = upload(d_desc, desc.data(), sizeof(BnDesc) * count, s);
+  if (st) return st;
+  st = upload(d_begin, begin.data(), sizeof(int32_t) * count, s);
+  if (st) return st;
+  st = upload(d_cbegin, cbegin.data(), sizeof(int32_t) * count, s);
+  if (st) return st;
+  KFAC_LAUNCH(K_BN_PARTIAL, bn_partial_kernel, dim3(static_cast<unsigned>(items)), dim3(256), 0, s,
+              d_desc, d_begin, count, in_dtype == KFAC_F32 ? 1 : 0);
+  KFAC_CHECK_LAUNCH("bn_partial_kernel");
+  const unsigned blocks = static_cast<unsigned>((channels + 255) / 256);
+  KFAC_LAUNCH(K_BN_FINISH, bn_finish_kernel, dim3(blocks), dim3(256), 0, s, d_desc, d_cbegin, count,
+              static_cast<int>(channels), ema_decay, shift);
+  KFAC_CHECK_LAUNCH("bn_finish_kernel");
+  return KFAC_OK;
+}

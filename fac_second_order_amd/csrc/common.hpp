@@ -1,0 +1,119 @@
+// Shared internals of libkfac: error reporting, device check, workspace carving,
+// descriptor-table upload and per-kernel event timing. gfx950 (CDNA4) only.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+#include <vector>
+
+#include "kfac.h"
+
+namespace kfac {
+
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+
+// ---- errors (thread-local text) -------------------------------------------
+kfac_status fail(kfac_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+kfac_status hip_fail(hipError_t e, const char* what);
+#define KFAC_HIP(call)                                   \
+  do {                                                   \
+    hipError_t e_ = (call);                              \
+    if (e_ != hipSuccess) return ::kfac::hip_fail(e_, #call); \
+  } while (0)
+
+// Returns KFAC_OK when the current device is gfx950 (cached per device).
+kfac_status check_device();
+
+// ---- workspace carving ----------------------------------------------------
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct Carver {
+  char* base;
+  size_t used = 0;
+  explicit Carver(void* b = nullptr) : base(static_cast<char*>(b)) {}
+  // Reserves `bytes` (256-byte aligned); returns nullptr when only sizing.
+  template <class T>
+  T* take(size_t count) {
+    size_t off = used;
+    used += align256(count * sizeof(T));
+    return base ? reinterpret_cast<T*>(base + off) : nullptr;
+  }
+};
+
+kfac_status check_workspace(const void* ws, size_t ws_bytes, size_t need);
+
+// ---- descriptor tables ----------------------------------------------------
+// Copies a host table into device memory by kernel arguments (2 KB per launch):
+// stream-ordered, needs no pinned host memory and keeps no host pointer.
+kfac_status upload(void* dst_device, const void* src_host, size_t bytes, hipStream_t stream);
+
+// ---- per-kernel timing ----------------------------------------------------
+enum KernelId {
+  K_UPLOAD = 0,
+  K_SYRK,
+  K_SYRK_REDUCE,
+  K_PACK,
+  K_UNPACK,
+  K_INV_PREP,
+  K_INV_PIVOT,
+  K_INV_PANEL,
+  K_INV_UPDATE,
+  K_INV_FINISH,
+  K_GEMM,
+  K_BN_PARTIAL,
+  K_BN_FINISH,
+  K_COUNT
+};
+
+// Records a start/end event pair around a launch when timing is enabled on the
+// calling thread; a no-op otherwise.
+struct TimerScope {
+  int id;
+  hipStream_t stream;
+  bool on;
+  hipEvent_t ev_end;
+  TimerScope(int id_, hipStream_t s);
+  ~TimerScope();
+};
+
+#define KFAC_LAUNCH(id, kernel, grid, block, shmem, stream, ...)                 \
+  do {                                                                         \
+    ::kfac::TimerScope ts_(id, stream);                                        \
+    hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);       \
+  } while (0)
+
+#define KFAC_CHECK_LAUNCH(what)                                   \
+  do {                                                            \
+    hipError_t e_ = hipGetLastError();                            \
+    if (e_ != hipSuccess) return ::kfac::hip_fail(e_, what);      \
+  } while (0)
+
+// ---- small device helpers --------------------------------------------------
+// Index of the problem owning work item `w`: largest p with begin[p] <= w.
+__device__ inline int find_problem(const int32_t* begin, int count, int w) {
+  int lo = 0, hi = count - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (begin[mid] <= w) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Upper-triangle tile t (row-major over i <= j) of an nb x nb tile grid.
+__device__ inline void upper_tile(int t, int nb, int& ti, int& tj) {
+  int i = 0;
+  while (t >= nb - i) { t -= nb - i; ++i; }
+  ti = i;
+  tj = i + t;
+}
+
+// Offset of (i, j), i <= j, in the row-by-row upper-triangle packing of order n.
+__host__ __device__ inline int64_t packed_off(int64_t i, int64_t j, int64_t n) {
+  return i * n - (i * (i - 1)) / 2 + (j - i);
+}
+
+}  // namespace kfac

@@ -1,0 +1,145 @@
+// Preconditioned gradients G^-1 dW A^-1 of many layers, two grouped launches.
+// Osawa et al. (CVPR 2019), Section 3.2, eq. (6)-(7): with dW stored [d_G, d_A]
+// and vec taken row by row, (G (x) A)^-1 vec(dW) = vec(G^-1 dW A^-1).
+//
+// Both GEMMs run on the fp32 MFMA tile engine in the form C = A_rows^T B_rows, so
+// every operand is read along its rows:
+//   1) T^T = (G^-1 dW)^T: A operand G^-1 (symmetric, so its rows are its
+//      columns), B operand dW; the tile is written transposed into the workspace.
+//   2) P = T A^-1: A operand rows of T^T, B operand A^-1.
+#include "tile_f32.hpp"
+
+namespace kfac {
+
+struct GemmDesc {
+  const float* A;  // A operand, read as A[k][m] (row-major, lda)
+  const void* B;   // B operand, read as B[k][n] (row-major, ldb)
+  float* C;        // C[m][n] (ldc), or C[n][m] when c_trans
+  int32_t M, N, K;
+  int32_t lda, ldb, ldc;
+  int32_t b_f16;
+  int32_t c_trans;
+  int32_t tm, tn;  // tiles along M and N
+};
+
+__global__ void __launch_bounds__(256) gemm_tn_kernel(const GemmDesc* __restrict__ desc,
+                                                      const int32_t* __restrict__ begin, int count) {
+  const int p = find_problem(begin, count, blockIdx.x);
+  const GemmDesc& d = desc[p];
+  const int t = blockIdx.x - begin[p];
+  const int mt = t / d.tn, nt = t % d.tn;
+  const int m0 = mt * TB, n0 = nt * TB;
+  __shared__ float As[KT * LDT], Bs[KT * LDT];
+  Quad q;
+  quad_zero(q);
+  for (int kc = 0; kc < d.K; kc += KT) {
+    stage_rows(As, d.A, d.lda, kc, d.K, m0, d.M);
+    if (d.b_f16) stage_rows_h(Bs, static_cast<const _Float16*>(d.B), d.ldb, kc, d.K, n0, d.N);
+    else stage_rows(Bs, static_cast<const float*>(d.B), d.ldb, kc, d.K, n0, d.N);
+    __syncthreads();
+    quad_mma(q, As, Bs, 1.f);
+    __syncthreads();
+  }
+  const int rv = min(TB, d.M - m0), cv = min(TB, d.N - n0);
+  if (d.c_trans) quad_store_t(q, d.C + int64_t(n0) * d.ldc + m0, d.ldc, rv, cv);
+  else quad_store(q, d.C + int64_t(m0) * d.ldc + n0, d.ldc, rv, cv);
+}
+
+static size_t precond_ws(int count, const int32_t* dg, const int32_t* da) {
+  size_t f = 0;
+  for (int l = 0; l < count; ++l) f += size_t(dg[l]) * da[l];
+  return 2 * align256(sizeof(GemmDesc) * count) + 2 * align256(sizeof(int32_t) * count) +
+         align256(sizeof(float) * f);
+}
+
+}  // namespace kfac
+
+using namespace kfac;
+
+static kfac_status precond_validate(int32_t count, const int32_t* dg, const int32_t* da) {
+  if (count < 0) return fail(KFAC_ERR_INVALID, "count must be >= 0");
+  if (count > 0 && (!dg || !da)) return fail(KFAC_ERR_INVALID, "d_g or d_a is NULL");
+  for (int l = 0; l < count; ++l)
+    if (dg[l] < 1 || da[l] < 1 || dg[l] > 65536 || da[l] > 65536)
+      return fail(KFAC_ERR_INVALID, "layer %d: d_g = %d, d_a = %d out of range", l, dg[l], da[l]);
+  return KFAC_OK;
+}
+
+extern "C" kfac_status kfac_precondition_workspace(int32_t count, const int32_t* d_g, const int32_t* d_a,
+                                                   size_t* bytes) {
+  if (!bytes) return fail(KFAC_ERR_INVALID, "bytes is NULL");
+  kfac_status st = precond_validate(count, d_g, d_a);
+  if (st) return st;
+  *bytes = count ? precond_ws(count, d_g, d_a) : 0;
+  return KFAC_OK;
+}
+
+extern "C" kfac_status kfac_precondition(int32_t count, const int32_t* d_g, const int32_t* d_a,
+                                         const float* const* G_inv, const float* const* A_inv,
+                                         const void* const* grad, kfac_dtype grad_dtype,
+                                         float* const* out, void* workspace, size_t ws_bytes,
+                                         void* stream) {
+  kfac_status st = precond_validate(count, d_g, d_a);
+  if (st) return st;
+  if (grad_dtype != KFAC_F16 && grad_dtype != KFAC_F32)
+    return fail(KFAC_ERR_UNSUPPORTED, "grad dtype %d not supported", grad_dtype);
+  if (count == 0) return KFAC_OK;
+  if (!G_inv || !A_inv || !grad || !out) return fail(KFAC_ERR_INVALID, "NULL pointer array");
+  const int esize = grad_dtype == KFAC_F16 ? 2 : 4;
+  for (int l = 0; l < count; ++l) {
+    if (!G_inv[l] || !A_inv[l] || !grad[l] || !out[l]) return fail(KFAC_ERR_INVALID, "layer %d: NULL pointer", l);
+    if ((reinterpret_cast<uintptr_t>(G_inv[l]) | reinterpret_cast<uintptr_t>(A_inv[l]) |
+         reinterpret_cast<uintptr_t>(out[l])) & 3 || reinterpret_cast<uintptr_t>(grad[l]) % esize)
+      return fail(KFAC_ERR_INVALID, "layer %d: misaligned pointer", l);
+  }
+  st = check_device();
+  if (st) return st;
+  st = check_workspace(workspace, ws_bytes, precond_ws(count, d_g, d_a));
+  if (st) return st;
+  Carver cv(workspace);
+  GemmDesc* d1 = cv.take<GemmDesc>(count);
+  GemmDesc* d2 = cv.take<GemmDesc>(count);
+  int32_t* b1 = cv.take<int32_t>(count);
+  int32_t* b2 = cv.take<int32_t>(count);
+  size_t f = 0;
+  for (int l = 0; l < count; ++l) f += size_t(d_g[l]) * d_a[l];
+  float* tt = cv.take<float>(f);
+  std::vector<GemmDesc> g1(count), g2(count);
+  std::vector<int32_t> e1(count), e2(count);
+  int64_t n1 = 0, n2 = 0;
+  size_t off = 0;
+  for (int l = 0; l < count; ++l) {
+    const int G = d_g[l], A = d_a[l];
+    float* T = tt + off;  // T^T: [d_a][d_g]
+    off += size_t(G) * A;
+    GemmDesc x{};
+    x.A = G_inv[l]; x.B = grad[l]; x.C = T;
+    x.M = G; x.N = A; x.K = G;
+    x.lda = G; x.ldb = A; x.ldc = G;
+    x.b_f16 = grad_dtype == KFAC_F16; x.c_trans = 1;
+    x.tm = (G + TB - 1) / TB; x.tn = (A + TB - 1) / TB;
+    g1[l] = x;
+    e1[l] = static_cast<int32_t>(n1);
+    n1 += int64_t(x.tm) * x.tn;
+    GemmDesc y{};
+    y.A = T; y.B = A_inv[l]; y.C = out[l];
+    y.M = G; y.N = A; y.K = A;
+    y.lda = G; y.ldb = A; y.ldc = A;
+    y.b_f16 = 0; y.c_trans = 0;
+    y.tm = x.tm; y.tn = x.tn;
+    g2[l] = y;
+    e2[l] = static_cast<int32_t>(n2);
+    n2 += int64_t(y.tm) * y.tn;
+  }
+  if (n1 >= (int64_t(1) << 31)) return fail(KFAC_ERR_INVALID, "too many tiles");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = upload(d1, g1.data(), sizeof(GemmDesc) * count, s))) return st;
+  if ((st = upload(d2, g2.data(), sizeof(GemmDesc) * count, s))) return st;
+  if ((st = upload(b1, e1.data(), sizeof(int32_t) * count, s))) return st;
+  if ((st = upload(b2, e2.data(), sizeof(int32_t) * count, s))) return st;
+  KFAC_LAUNCH(K_GEMM, gemm_tn_kernel, dim3(static_cast<unsigned>(n1)), dim3(256), 0, s, d1, b1, count);
+  KFAC_CHECK_LAUNCH("gemm_tn_kernel (G^-1 dW)");
+  KFAC_LAUNCH(K_GEMM, gemm_tn_kernel, dim3(static_cast<unsigned>(n2)), dim3(256), 0, s, d2, b2, count);
+  KFAC_CHECK_LAUNCH("gemm_tn_kernel (T A^-1)");
+  return KFAC_OK;
+}

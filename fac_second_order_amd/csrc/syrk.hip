@@ -1,0 +1,592 @@
+// Kronecker factors A = E[a a^T] and G = E[g g^T] of many layers in one launch.
+// Osawa et al. (CVPR 2019), Section 3.2, eq. (5): G comes from the loss gradients
+// with respect to a layer's outputs, A from the layer's inputs; E is the mini-batch
+// mean of eq. (1), taken here over all N*H_out*W_out patch rows. Section 1
+// (contributions): the factors are symmetric, so only the upper triangle is formed
+// and stored, and the products use half precision.
+//
+// Each factor is S = X^T X / R for a virtual row matrix X[R, d]. For A, X is the
+// im2col patch matrix of the NHWC activation and is never written out: each
+// 16-byte fp16 vector of 8 patch columns (one kernel tap, 8 channels) is gathered
+// straight from the activation tensor into registers, transposed in registers and
+// stored column-major into LDS, where the MFMA operands are read with 16-byte LDS
+// loads. For G, X is the output-gradient tensor viewed as [R, C_out].
+//
+// Work item = (factor, row split, upper tile ti <= tj of 128x128). Waves compute
+// 64x64 quadrants with v_mfma_f32_32x32x16_f16 (fp16 in, fp32 accumulate); the
+// quadrant strictly below the diagonal of a diagonal tile is skipped. The bias
+// column (constant 1) is not multiplied: its entries are column sums, accumulated
+// by the diagonal tiles from the same LDS data, and R for the corner. Row splits
+// write fp32 partial tiles that a second kernel adds in split order, so results
+// are deterministic. The epilogue multiplies by fp32(1/R), optionally blends with
+// the stored factor (exponential moving average), and writes the packed upper
+// triangle. Work items are renumbered so that each of the 8 XCDs runs a contiguous
+// range (tiles of one row split share that XCD's L2).
+//
+// fp32 inputs take a plain path (element gathers, v_mfma_f32_32x32x2f32).
+#include "common.hpp"
+
+namespace kfac {
+
+constexpr int ST = 128;           // output tile edge
+constexpr int KC = 64;            // patch rows per LDS chunk (fp16)
+constexpr int LDK = KC + 8;       // LDS row pitch in halves (144 B)
+constexpr int KC32 = 32;          // patch rows per LDS chunk (fp32 path)
+constexpr int LDN32 = ST + 4;     // LDS row pitch in floats (fp32 path)
+
+struct SyrkDesc {
+  const void* src;
+  float* out;      // packed upper triangle, d(d+1)/2
+  float* partial;  // [splits][nt][ST*ST] when splits > 1
+  float* pcol;     // [splits][nb][ST] bias column partial sums
+  int32_t mode;    // 0: rows [R, ld]; 1: im2col of NHWC [n, H, W, C]
+  int32_t vec;     // 16-byte gathers allowed
+  int32_t d_core;  // columns of X (without the bias column)
+  int32_t d;       // factor order (d_core + bias)
+  int32_t bias;
+  int32_t R;
+  int32_t H, W, C, Ho, Wo, kh, kw, sh, sw, ph, pw;
+  int32_t ld;
+  int32_t nb, nt, splits, rows_per_split;
+  float inv_r, r_f;
+};
+
+// Position of the first of 8 columns handled by a thread (constant over rows).
+struct ColPos {
+  int c0;        // first virtual column
+  int ki, kj;    // kernel tap (im2col)
+  int ci;        // first channel (im2col)
+};
+
+__device__ inline ColPos col_pos(const SyrkDesc& d, int c0) {
+  ColPos p;
+  p.c0 = c0;
+  if (d.mode == 1) {
+    const int tap = c0 / d.C;
+    p.ci = c0 - tap * d.C;
+    p.ki = tap / d.kw;
+    p.kj = tap - p.ki * d.kw;
+  } else {
+    p.ki = p.kj = p.ci = 0;
+  }
+  return p;
+}
+
+// Value of X[row][c] (0 outside the image or beyond d_core), any input dtype.
+template <class T>
+__device__ inline float x_elem(const SyrkDesc& d, int64_t row, int c) {
+  if (c >= d.d_core) return 0.f;
+  const T* src = static_cast<const T*>(d.src);
+  if (d.mode == 0) return static_cast<float>(src[row * d.ld + c]);
+  const int hw = d.Ho * d.Wo;
+  const int64_t n = row / hw;
+  const int rem = static_cast<int>(row - n * hw);
+  const int oh = rem / d.Wo, ow = rem - (rem / d.Wo) * d.Wo;
+  const int tap = c / d.C, ci = c - tap * d.C;
+  const int ki = tap / d.kw, kj = tap - ki * d.kw;
+  const int ih = oh * d.sh + ki - d.ph, iw = ow * d.sw + kj - d.pw;
+  if (ih < 0 || ih >= d.H || iw < 0 || iw >= d.W) return 0.f;
+  return static_cast<float>(src[((n * d.H + ih) * d.W + iw) * d.C + ci]);
+}
+
+// 8 consecutive columns of row `row` as fp16 (zeros when !valid).
+__device__ inline v8h gather8(const SyrkDesc& d, bool valid, int64_t row, const ColPos& p) {
+  v8h z = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (!valid || p.c0 >= d.d_core) return z;
+  const _Float16* src = static_cast<const _Float16*>(d.src);
+  if (d.vec) {  // 8 columns share one tap and lie inside d_core (d_core % 8 == 0)
+    if (d.mode == 0) return *reinterpret_cast<const v8h*>(src + row * d.ld + p.c0);
+    const int hw = d.Ho * d.Wo;
+    const int64_t n = row / hw;
+    const int rem = static_cast<int>(row - n * hw);
+    const int oh = rem / d.Wo, ow = rem - (rem / d.Wo) * d.Wo;
+    const int ih = oh * d.sh + p.ki - d.ph, iw = ow * d.sw + p.kj - d.pw;
+    if (ih < 0 || ih >= d.H || iw < 0 || iw >= d.W) return z;
+    return *reinterpret_cast<const v8h*>(src + ((n * d.H + ih) * d.W + iw) * d.C + p.ci);
+  }
+  v8h v;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) v[q] = static_cast<_Float16>(x_elem<_Float16>(d, row, p.c0 + q));
+  return v;
+}
+
+// Maps a hardware block id to a virtual work id so that XCD x (blocks b with
+// b % 8 == x) runs the contiguous range [x*per, (x+1)*per). Returns -1 for padding.
+__device__ inline int xcd_virtual(int b, int grid, int total) {
+  const int per = grid / 8;
+  const int v = (b % 8) * per + b / 8;
+  return v < total ? v : -1;
+}
+
+__device__ inline float blend(float v, const float* out, int64_t o, float decay) {
+  return decay != 0.f ? decay * out[o] + (1.f - decay) * v : v;
+}
+
+// Writes the bias column entries (column sums) and the bias corner of a direct tile.
+__device__ inline void write_bias_direct(const SyrkDesc& d, int ti, int t, float colsum,
+                                         float decay) {
+  const int tid = threadIdx.x;
+  if (tid < ST) {
+    const int i = ti * ST + tid;
+    if (i < d.d_core) {
+      const int64_t o = packed_off(i, d.d_core, d.d);
+      d.out[o] = blend(colsum * d.inv_r, d.out, o, decay);
+    }
+  }
+  if (t == 0 && tid == 0) {
+    const int64_t o = packed_off(d.d_core, d.d_core, d.d);
+    d.out[o] = blend(d.r_f * d.inv_r, d.out, o, decay);
+  }
+}
+
+__global__ void __launch_bounds__(256) syrk_f16_kernel(const SyrkDesc* __restrict__ desc,
+                                                       const int32_t* __restrict__ begin,
+                                                       int count, int total, float decay) {
+  const int v = xcd_virtual(blockIdx.x, gridDim.x, total);
+  if (v < 0) return;
+  const int p = find_problem(begin, count, v);
+  const SyrkDesc& d = desc[p];
+  const int local = v - begin[p];
+  const int t = local % d.nt, s = local / d.nt;
+  int ti, tj;
+  upper_tile(t, d.nb, ti, tj);
+  const bool diag = ti == tj;
+
+  __shared__ __attribute__((aligned(16))) _Float16 lds[2][ST * LDK];
+  _Float16* Xa = lds[0];
+  _Float16* Xb = diag ? lds[0] : lds[1];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const bool skip = diag && wm > wn;  // quadrant strictly below the diagonal
+  const int cg = tid & 15, rg = tid >> 4;
+  const ColPos pa = col_pos(d, ti * ST + cg * 8);
+  const ColPos pb = col_pos(d, tj * ST + cg * 8);
+  const int64_t r_begin = int64_t(s) * d.rows_per_split;
+  const int64_t r_end = min(int64_t(d.R), r_begin + d.rows_per_split);
+  const bool want_col = diag && d.bias && tid < ST;
+
+  v16f acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
+  float colsum = 0.f;
+
+  for (int64_t r0 = r_begin; r0 < r_end; r0 += KC) {
+    v8h va[4], vb[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t row = r0 + rg * 4 + q;
+      va[q] = gather8(d, row < r_end, row, pa);
+      if (!diag) vb[q] = gather8(d, row < r_end, row, pb);
+    }
+    __syncthreads();  // previous chunk fully consumed
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      v4h w = {va[0][e], va[1][e], va[2][e], va[3][e]};
+      *reinterpret_cast<v4h*>(Xa + (cg * 8 + e) * LDK + rg * 4) = w;
+      if (!diag) {
+        v4h u = {vb[0][e], vb[1][e], vb[2][e], vb[3][e]};
+        *reinterpret_cast<v4h*>(Xb + (cg * 8 + e) * LDK + rg * 4) = u;
+      }
+    }
+    __syncthreads();
+    if (want_col) {
+#pragma unroll
+      for (int k = 0; k < KC; k += 8) {
+        v8h c = *reinterpret_cast<const v8h*>(Xa + tid * LDK + k);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) colsum += static_cast<float>(c[q]);
+      }
+    }
+    if (!skip) {
+#pragma unroll
+      for (int ks = 0; ks < KC / 16; ++ks) {
+        const int ko = ks * 16 + (lane >> 5) * 8;
+        const v8h a0 = *reinterpret_cast<const v8h*>(Xa + (wm * 64 + (lane & 31)) * LDK + ko);
+        const v8h a1 = *reinterpret_cast<const v8h*>(Xa + (wm * 64 + 32 + (lane & 31)) * LDK + ko);
+        const v8h b0 = *reinterpret_cast<const v8h*>(Xb + (wn * 64 + (lane & 31)) * LDK + ko);
+        const v8h b1 = *reinterpret_cast<const v8h*>(Xb + (wn * 64 + 32 + (lane & 31)) * LDK + ko);
+        acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0, acc[0][0], 0, 0, 0);
+        acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b1, acc[0][1], 0, 0, 0);
+        acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b0, acc[1][0], 0, 0, 0);
+        acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1, acc[1][1], 0, 0, 0);
+      }
+    }
+  }
+
+  if (d.splits == 1) {
+    if (!skip) {
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int i = ti * ST + wm * 64 + a * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+            const int j = tj * ST + wn * 64 + b * 32 + (lane & 31);
+            if (i <= j && j < d.d_core) {
+              const int64_t o = packed_off(i, j, d.d);
+              d.out[o] = blend(acc[a][b][e] * d.inv_r, d.out, o, decay);
+            }
+          }
+    }
+    if (diag && d.bias) write_bias_direct(d, ti, t, colsum, decay);
+  } else {
+    float* P = d.partial + (int64_t(s) * d.nt + t) * (ST * ST);
+    if (!skip) {
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int r = wm * 64 + a * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+            const int c = wn * 64 + b * 32 + (lane & 31);
+            P[r * ST + c] = acc[a][b][e];
+          }
+    }
+    if (want_col) d.pcol[(int64_t(s) * d.nb + ti) * ST + tid] = colsum;
+  }
+}
+
+// fp32 inputs: element gathers into LDS laid out [k][column], fp32 MFMA.
+__global__ void __launch_bounds__(256) syrk_f32_kernel(const SyrkDesc* __restrict__ desc,
+                                                       const int32_t* __restrict__ begin,
+                                                       int count, int total, float decay) {
+  const int v = xcd_virtual(blockIdx.x, gridDim.x, total);
+  if (v < 0) return;
+  const int p = find_problem(begin, count, v);
+  const SyrkDesc& d = desc[p];
+  const int local = v - begin[p];
+  const int t = local % d.nt, s = local / d.nt;
+  int ti, tj;
+  upper_tile(t, d.nb, ti, tj);
+  const bool diag = ti == tj;
+
+  __shared__ float la[KC32 * LDN32], lb[KC32 * LDN32];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const bool skip = diag && wm > wn;
+  const int64_t r_begin = int64_t(s) * d.rows_per_split;
+  const int64_t r_end = min(int64_t(d.R), r_begin + d.rows_per_split);
+  const bool want_col = diag && d.bias && tid < ST;
+
+  v16f acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
+  float colsum = 0.f;
+
+  for (int64_t r0 = r_begin; r0 < r_end; r0 += KC32) {
+    __syncthreads();
+    for (int e = tid; e < KC32 * ST; e += 256) {
+      const int k = e / ST, c = e % ST;
+      const int64_t row = r0 + k;
+      const bool ok = row < r_end;
+      la[k * LDN32 + c] = ok ? x_elem<float>(d, row, ti * ST + c) : 0.f;
+      lb[k * LDN32 + c] = ok ? x_elem<float>(d, row, tj * ST + c) : 0.f;
+    }
+    __syncthreads();
+    if (want_col)
+      for (int k = 0; k < KC32; ++k) colsum += la[k * LDN32 + tid];
+    if (!skip) {
+      for (int k = 0; k < KC32; k += 2) {
+        const int kk = k + (lane >> 5);
+        const float a0 = la[kk * LDN32 + wm * 64 + (lane & 31)];
+        const float a1 = la[kk * LDN32 + wm * 64 + 32 + (lane & 31)];
+        const float b0 = lb[kk * LDN32 + wn * 64 + (lane & 31)];
+        const float b1 = lb[kk * LDN32 + wn * 64 + 32 + (lane & 31)];
+        acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);
+        acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[0][1], 0, 0, 0);
+        acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
+        acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
+      }
+    }
+  }
+  if (d.splits == 1) {
+    if (!skip) {
+      for (int a = 0; a < 2; ++a)
+        for (int b = 0; b < 2; ++b)
+          for (int e = 0; e < 16; ++e) {
+            const int i = ti * ST + wm * 64 + a * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+            const int j = tj * ST + wn * 64 + b * 32 + (lane & 31);
+            if (i <= j && j < d.d_core) {
+              const int64_t o = packed_off(i, j, d.d);
+              d.out[o] = blend(acc[a][b][e] * d.inv_r, d.out, o, decay);
+            }
+          }
+    }
+    if (diag && d.bias) write_bias_direct(d, ti, t, colsum, decay);
+  } else {
+    float* P = d.partial + (int64_t(s) * d.nt + t) * (ST * ST);
+    if (!skip) {
+      for (int a = 0; a < 2; ++a)
+        for (int b = 0; b < 2; ++b)
+          for (int e = 0; e < 16; ++e) {
+            const int r = wm * 64 + a * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+            const int c = wn * 64 + b * 32 + (lane & 31);
+            P[r * ST + c] = acc[a][b][e];
+          }
+    }
+    if (want_col) d.pcol[(int64_t(s) * d.nb + ti) * ST + tid] = colsum;
+  }
+}
+
+// Adds the row-split partial tiles in split order, scales, blends and packs.
+__global__ void __launch_bounds__(256) syrk_reduce_kernel(const SyrkDesc* __restrict__ desc,
+                                                          const int32_t* __restrict__ rbegin,
+                                                          const int32_t* __restrict__ rprob,
+                                                          int rcount, float decay) {
+  const int q = find_problem(rbegin, rcount, blockIdx.x);
+  const SyrkDesc& d = desc[rprob[q]];
+  const int t = blockIdx.x - rbegin[q];
+  int ti, tj;
+  upper_tile(t, d.nb, ti, tj);
+  const int64_t tstride = int64_t(d.nt) * ST * ST;
+  const float* P = d.partial + int64_t(t) * ST * ST;
+  for (int e = threadIdx.x; e < ST * ST; e += 256) {
+    const int i = ti * ST + e / ST, j = tj * ST + e % ST;
+    if (i <= j && j < d.d_core) {
+      float sum = 0.f;
+      for (int s = 0; s < d.splits; ++s) sum += P[s * tstride + e];
+      const int64_t o = packed_off(i, j, d.d);
+      d.out[o] = blend(sum * d.inv_r, d.out, o, decay);
+    }
+  }
+  if (ti == tj && d.bias && threadIdx.x < ST) {
+    const int i = ti * ST + threadIdx.x;
+    if (i < d.d_core) {
+      float sum = 0.f;
+      for (int s = 0; s < d.splits; ++s) sum += d.pcol[(int64_t(s) * d.nb + ti) * ST + threadIdx.x];
+      const int64_t o = packed_off(i, d.d_core, d.d);
+      d.out[o] = blend(sum * d.inv_r, d.out, o, decay);
+    }
+  }
+  if (t == 0 && d.bias && threadIdx.x == 0) {
+    const int64_t o = packed_off(d.d_core, d.d_core, d.d);
+    d.out[o] = blend(d.r_f * d.inv_r, d.out, o, decay);
+  }
+}
+
+// ---- host planning ------------------------------------------------------------
+struct SyrkPlan {
+  std::vector<SyrkDesc> desc;
+  std::vector<int32_t> begin;        // work-item offsets
+  std::vector<int32_t> rbegin, rprob;  // reduce tiles of split problems
+  int64_t items = 0, ritems = 0;
+  size_t partial_floats = 0;
+};
+
+// One factor problem from a layer (which = 0: A, 1: G).
+static SyrkDesc make_problem(const kfac_layer& L, int which) {
+  SyrkDesc d{};
+  d.R = L.n * L.h_out * L.w_out;
+  if (which == 0) {
+    d.mode = 1;
+    d.H = L.h; d.W = L.w; d.C = L.c_in; d.Ho = L.h_out; d.Wo = L.w_out;
+    d.kh = L.kh; d.kw = L.kw; d.sh = L.sh; d.sw = L.sw; d.ph = L.ph; d.pw = L.pw;
+    d.d_core = L.c_in * L.kh * L.kw;
+    d.bias = L.bias ? 1 : 0;
+    if (L.kh == 1 && L.kw == 1 && L.sh == 1 && L.sw == 1 && L.ph == 0 && L.pw == 0 &&
+        L.h == L.h_out && L.w == L.w_out) {  // 1x1 stride-1: the activation is X itself
+      d.mode = 0;
+      d.ld = L.c_in;
+    }
+  } else {
+    d.mode = 0;
+    d.d_core = L.c_out;
+    d.ld = L.c_out;
+    d.bias = 0;
+  }
+  d.d = d.d_core + d.bias;
+  d.nb = (d.d_core + ST - 1) / ST;
+  d.nt = d.nb * (d.nb + 1) / 2;
+  d.inv_r = 1.0f / static_cast<float>(d.R);
+  d.r_f = static_cast<float>(d.R);
+  return d;
+}
+
+// Row splits: spread the work so that the launch holds several thousand tiles of
+// at least 1024 rows each; the split count of a factor never exceeds 256.
+static void plan_splits(std::vector<SyrkDesc>& ds) {
+  double work = 0;
+  for (auto& d : ds) work += double(d.nt) * d.R;
+  double per = work / 4096.0;
+  if (per < 1024) per = 1024;
+  for (auto& d : ds) {
+    int64_t splits = static_cast<int64_t>((d.R + per - 1) / per);
+    if (splits < 1) splits = 1;
+    if (splits > 256) splits = 256;
+    int64_t rows = (d.R + splits - 1) / splits;
+    rows = (rows + KC - 1) / KC * KC;
+    d.rows_per_split = static_cast<int32_t>(rows);
+    d.splits = static_cast<int32_t>((d.R + rows - 1) / rows);
+  }
+}
+
+static void finish_plan(SyrkPlan& pl) {
+  pl.begin.clear(); pl.rbegin.clear(); pl.rprob.clear();
+  pl.items = pl.ritems = 0;
+  pl.partial_floats = 0;
+  for (size_t p = 0; p < pl.desc.size(); ++p) {
+    SyrkDesc& d = pl.desc[p];
+    pl.begin.push_back(static_cast<int32_t>(pl.items));
+    pl.items += int64_t(d.splits) * d.nt;
+    if (d.splits > 1) {
+      pl.rbegin.push_back(static_cast<int32_t>(pl.ritems));
+      pl.rprob.push_back(static_cast<int32_t>(p));
+      pl.ritems += d.nt;
+      pl.partial_floats += size_t(d.splits) * d.nt * ST * ST + size_t(d.splits) * d.nb * ST;
+    }
+  }
+}
+
+static size_t syrk_ws_bytes(const SyrkPlan& pl) {
+  const size_t np = pl.desc.size(), nr = pl.rprob.size();
+  return align256(sizeof(SyrkDesc) * np) + align256(sizeof(int32_t) * np) +
+         2 * align256(sizeof(int32_t) * (nr ? nr : 1)) + align256(sizeof(float) * pl.partial_floats);
+}
+
+}  // namespace kfac
+
+using namespace kfac;
+
+static kfac_status layers_validate(const kfac_layer* L, int32_t count, kfac_dtype dt) {
+  if (count < 0) return fail(KFAC_ERR_INVALID, "count must be >= 0");
+  if (count > 0 && !L) return fail(KFAC_ERR_INVALID, "layers is NULL");
+  if (dt != KFAC_F16 && dt != KFAC_F32) return fail(KFAC_ERR_UNSUPPORTED, "dtype %d not supported", dt);
+  for (int l = 0; l < count; ++l) {
+    const kfac_layer& x = L[l];
+    if (x.n < 1 || x.h < 1 || x.w < 1 || x.c_in < 1 || x.c_out < 1 || x.kh < 1 || x.kw < 1 ||
+        x.sh < 1 || x.sw < 1 || x.ph < 0 || x.pw < 0 || x.h_out < 1 || x.w_out < 1)
+      return fail(KFAC_ERR_INVALID, "layer %d: sizes must be positive", l);
+    if (x.h_out != (x.h + 2 * x.ph - x.kh) / x.sh + 1 || x.w_out != (x.w + 2 * x.pw - x.kw) / x.sw + 1 ||
+        x.h + 2 * x.ph < x.kh || x.w + 2 * x.pw < x.kw)
+      return fail(KFAC_ERR_INVALID, "layer %d: h_out/w_out do not match the convolution", l);
+    if (x.bias != 0 && x.bias != 1) return fail(KFAC_ERR_INVALID, "layer %d: bias must be 0 or 1", l);
+    const int64_t rows = int64_t(x.n) * x.h_out * x.w_out;
+    const int64_t da = int64_t(x.c_in) * x.kh * x.kw + x.bias;
+    if (rows >= (int64_t(1) << 31) || da > 65536 || x.c_out > 65536 ||
+        int64_t(x.n) * x.h * x.w * x.c_in >= (int64_t(1) << 40))
+      return fail(KFAC_ERR_INVALID, "layer %d: too large", l);
+  }
+  return KFAC_OK;
+}
+
+// Problems in call order: A of layer l, then G of layer l. Row splits are planned
+// over all 2*count factors (so the workspace query bounds every call); factors whose
+// input pointer is NULL are then dropped.
+static kfac_status build_plan(const kfac_layer* L, int32_t count, kfac_dtype dt, const void* const* act,
+                              const void* const* gout, float* const* A, float* const* G, SyrkPlan& pl) {
+  const int esize = dt == KFAC_F16 ? 2 : 4;
+  std::vector<SyrkDesc> all;
+  for (int l = 0; l < count; ++l)
+    for (int which = 0; which < 2; ++which) all.push_back(make_problem(L[l], which));
+  plan_splits(all);
+  for (int l = 0; l < count; ++l) {
+    for (int which = 0; which < 2; ++which) {
+      SyrkDesc d = all[2 * l + which];
+      if (act) {
+        const void* src = which == 0 ? act[l] : gout[l];
+        if (!src) continue;
+        float* out = which == 0 ? A[l] : G[l];
+        if (!out) return fail(KFAC_ERR_INVALID, "layer %d: output for factor %d is NULL", l, which);
+        if (reinterpret_cast<uintptr_t>(src) % esize || reinterpret_cast<uintptr_t>(out) % 4)
+          return fail(KFAC_ERR_INVALID, "layer %d: misaligned pointer", l);
+        d.src = src;
+        d.out = out;
+        const int width = d.mode == 1 ? d.C : d.ld;
+        d.vec = (dt == KFAC_F16 && width % 8 == 0 && d.d_core % 8 == 0 &&
+                 reinterpret_cast<uintptr_t>(src) % 16 == 0) ? 1 : 0;
+      }
+      pl.desc.push_back(d);
+    }
+  }
+  finish_plan(pl);
+  if (pl.items >= (int64_t(1) << 31) - 8 || pl.ritems >= (int64_t(1) << 31))
+    return fail(KFAC_ERR_INVALID, "too many tiles");
+  return KFAC_OK;
+}
+
+extern "C" kfac_status kfac_factors_workspace(const kfac_layer* layers, int32_t count, kfac_dtype in_dtype,
+                                              size_t* bytes) {
+  if (!bytes) return fail(KFAC_ERR_INVALID, "bytes is NULL");
+  kfac_status st = layers_validate(layers, count, in_dtype);
+  if (st) return st;
+  if (count == 0) { *bytes = 0; return KFAC_OK; }
+  SyrkPlan pl;
+  st = build_plan(layers, count, in_dtype, nullptr, nullptr, nullptr, nullptr, pl);
+  if (st) return st;
+  *bytes = syrk_ws_bytes(pl);
+  return KFAC_OK;
+}
+
+extern "C" kfac_status kfac_factors(const kfac_layer* layers, int32_t count, kfac_dtype in_dtype,
+                                    const void* const* act, const void* const* gout,
+                                    float* const* A_packed, float* const* G_packed, float ema_decay,
+                                    void* workspace, size_t ws_bytes, void* stream) {
+  kfac_status st = layers_validate(layers, count, in_dtype);
+  if (st) return st;
+  if (!(ema_decay >= 0.f && ema_decay <= 1.f)) return fail(KFAC_ERR_INVALID, "ema_decay must be in [0, 1]");
+  if (count == 0) return KFAC_OK;
+  if (!act || !gout || !A_packed || !G_packed) return fail(KFAC_ERR_INVALID, "NULL pointer array");
+  SyrkPlan pl;
+  st = build_plan(layers, count, in_dtype, act, gout, A_packed, G_packed, pl);
+  if (st) return st;
+  if (pl.desc.empty()) return KFAC_OK;
+  st = check_device();
+  if (st) return st;
+  // The workspace query plans every factor; a call that skips factors needs less.
+  const size_t need = syrk_ws_bytes(pl);
+  st = check_workspace(workspace, ws_bytes, need);
+  if (st) return st;
+  const int np = static_cast<int>(pl.desc.size());
+  const int nr = static_cast<int>(pl.rprob.size());
+  Carver cv(workspace);
+  SyrkDesc* d_desc = cv.take<SyrkDesc>(np);
+  int32_t* d_begin = cv.take<int32_t>(np);
+  int32_t* d_rbegin = cv.take<int32_t>(nr ? nr : 1);
+  int32_t* d_rprob = cv.take<int32_t>(nr ? nr : 1);
+  float* part = cv.take<float>(pl.partial_floats);
+  size_t off = 0;
+  for (auto& d : pl.desc) {
+    if (d.splits > 1) {
+      d.partial = part + off;
+      off += size_t(d.splits) * d.nt * ST * ST;
+      d.pcol = part + off;
+      off += size_t(d.splits) * d.nb * ST;
+    }
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = upload(d_desc, pl.desc.data(), sizeof(SyrkDesc) * np, s);
+  if (st) return st;
+  st = upload(d_begin, pl.begin.data(), sizeof(int32_t) * np, s);
+  if (st) return st;
+  if (nr) {
+    st = upload(d_rbegin, pl.rbegin.data(), sizeof(int32_t) * nr, s);
+    if (st) return st;
+    st = upload(d_rprob, pl.rprob.data(), sizeof(int32_t) * nr, s);
+    if (st) return st;
+  }
+  const int total = static_cast<int>(pl.items);
+  const unsigned grid = static_cast<unsigned>((total + 7) / 8 * 8);
+  if (in_dtype == KFAC_F16) {
+    KFAC_LAUNCH(K_SYRK, syrk_f16_kernel, dim3(grid), dim3(256), 0, s, d_desc, d_begin, np, total, ema_decay);
+  } else {
+    KFAC_LAUNCH(K_SYRK, syrk_f32_kernel, dim3(grid), dim3(256), 0, s, d_desc, d_begin, np, total, ema_decay);
+  }
+  KFAC_CHECK_LAUNCH("syrk kernel");
+  if (nr) {
+    KFAC_LAUNCH(K_SYRK_REDUCE, syrk_reduce_kernel, dim3(static_cast<unsigned>(pl.ritems)), dim3(256), 0, s,
+                d_desc, d_rbegin, d_rprob, nr, ema_decay);
+    KFAC_CHECK_LAUNCH("syrk_reduce_kernel");
+  }
+  return KFAC_OK;
+}

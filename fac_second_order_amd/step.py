@@ -1,0 +1,87 @@
+"""One K-FAC step over a fixed set of layers: device buffers plus the sequence of
+library calls (factors -> unpack -> damped inverses -> preconditioning, and the
+BatchNorm diagonal). Python only allocates and sequences; every number is computed
+by libkfac's HIP kernels.
+
+Step order follows Osawa et al. (CVPR 2019): stage 1-2 of their Figure 1 (factors
+from the forward activations and backward gradients), eq. (6) (inverses of the
+damped factors) and eq. (7) (preconditioned gradients); BatchNorm uses the
+diagonal Fisher (Section 1, contributions)."""
+import math
+
+import torch
+
+from . import _lib as K
+
+
+class KfacStep:
+    """Buffers for `layers` (objects with the kfac_layer fields) and `bn_layers`
+    (objects with n, hw, c). Tikhonov damping gamma puts sqrt(gamma) on each
+    Kronecker factor (float32-rounded) and gamma on the BN diagonal."""
+
+    def __init__(self, layers, bn_layers=(), device="cuda", damping=1e-3, bn_shift=None,
+                 in_dtype=torch.float16):
+        self.layers = list(layers)
+        self.bn_layers = list(bn_layers)
+        self.device = torch.device(device)
+        self.shift = float(torch.tensor(math.sqrt(damping), dtype=torch.float32))
+        self.bn_shift = float(damping if bn_shift is None else bn_shift)
+        self.d_a = [l.c_in * l.kh * l.kw + (1 if l.bias else 0) for l in self.layers]
+        self.d_g = [l.c_out for l in self.layers]
+        dev = self.device
+        f32 = torch.float32
+        self.A_packed = [torch.empty(d * (d + 1) // 2, dtype=f32, device=dev) for d in self.d_a]
+        self.G_packed = [torch.empty(d * (d + 1) // 2, dtype=f32, device=dev) for d in self.d_g]
+        # factor k of the inverse batch: A of every layer, then G of every layer
+        self.n_all = self.d_a + self.d_g
+        self.full = [torch.empty(d, d, dtype=f32, device=dev) for d in self.n_all]
+        self.packed_all = self.A_packed + self.G_packed
+        self.info = torch.zeros(len(self.n_all), dtype=torch.int32, device=dev)
+        self.out = [torch.empty(g, a, dtype=f32, device=dev) for g, a in zip(self.d_g, self.d_a)]
+        self.fisher = [torch.zeros(2, b.c, dtype=f32, device=dev) for b in self.bn_layers]
+        self.bn_pre = [torch.empty(2, b.c, dtype=f32, device=dev) for b in self.bn_layers]
+        code = K.KFAC_F16 if in_dtype == torch.float16 else K.KFAC_F32
+        sizes = [K.kfac_factors_workspace(self.layers, code),
+                 K.kfac_pack_sym_workspace(self.n_all),
+                 K.kfac_invert_workspace(self.n_all),
+                 K.kfac_precondition_workspace(self.d_g, self.d_a)]
+        if self.bn_layers:
+            sizes.append(K.kfac_bn_diag_workspace(self.bn_layers))
+        # one workspace serves every call: they run one after another on one stream
+        self.workspace = torch.empty(max(sizes) + 256, dtype=torch.uint8, device=dev)
+
+    @property
+    def A_inv(self):
+        return self.full[:len(self.layers)]
+
+    @property
+    def G_inv(self):
+        return self.full[len(self.layers):]
+
+    def factors(self, act, gout, ema_decay=0.0, stream=None):
+        K.kfac_factors(self.layers, act, gout, self.A_packed, self.G_packed, ema_decay,
+                       self.workspace, stream)
+
+    def invert(self, stream=None):
+        K.kfac_pack_sym(self.n_all, self.full, self.packed_all, 1, self.workspace, stream)
+        K.kfac_invert(self.n_all, self.full, self.full, [self.shift] * len(self.n_all), self.info,
+                      None, self.workspace, stream)
+
+    def precondition(self, grads, stream=None):
+        K.kfac_precondition(self.d_g, self.d_a, self.G_inv, self.A_inv, grads, self.out,
+                            self.workspace, stream)
+
+    def bn(self, xhat, bn_gout, ema_decay=0.0, stream=None):
+        if self.bn_layers:
+            K.kfac_bn_diag(self.bn_layers, xhat, bn_gout, self.fisher, self.bn_pre, ema_decay,
+                           self.bn_shift, self.workspace, stream)
+
+    def step(self, act, gout, grads, xhat=(), bn_gout=(), ema_decay=0.0, refresh=True, stream=None):
+        """One step. refresh=False is a stale-curvature step: factors and inverses are
+        kept, the gradients are preconditioned with them, and BN divides its fresh
+        gradient by the stored Fisher (decay 1 keeps it)."""
+        if refresh:
+            self.factors(act, gout, ema_decay, stream)
+            self.invert(stream)
+        self.precondition(grads, stream)
+        self.bn(xhat, bn_gout, ema_decay if refresh else 1.0, stream)

@@ -1,0 +1,202 @@
+/*
+ * kfac.h - C ABI of the single-GPU K-FAC step for AMD Instinct MI355X (gfx950).
+ *
+ * The library computes one GPU's per-iteration K-FAC work as defined in Osawa,
+ * Tsuji, Ueno, Naruse, Yokota, Matsuoka, "Large-scale distributed second-order
+ * optimization using Kronecker-factored approximate curvature for deep
+ * convolutional neural networks" (CVPR 2019), cited below as [OTUNYM]:
+ *   - Kronecker factors A = E[a a^T] (from a layer's input activations, patch-expanded
+ *     for convolutions) and G = E[g g^T] (from the gradients of the loss with respect
+ *     to the layer's outputs): Section 3.2, eq. (5); E is the mini-batch mean of
+ *     Section 3.1, eq. (1).
+ *   - only one triangle of each symmetric factor is kept: Section 1, contributions.
+ *   - the inverse of each (damped) factor: Section 3.2, eq. (6).
+ *   - the preconditioned gradient G^-1 dW A^-1: Section 3.2, eq. (7).
+ *   - BatchNorm's Fisher taken diagonal: Section 1, contributions, with the
+ *     empirical Fisher of Section 3.1, eq. (3).
+ *
+ * Conventions for every entry point:
+ *   - Pointers named "device" are HIP device memory on the current device, allocated
+ *     and owned by the caller. Arrays of device pointers ("const void* const* act")
+ *     and every other array are host memory owned by the caller. The library reads
+ *     host arrays before the call returns and keeps no pointer afterwards.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL is the default stream) and
+ *     returns without synchronising. Outputs are valid once the stream reaches them.
+ *   - Scratch memory comes from the caller as `workspace` (device, 256-byte aligned)
+ *     of at least the size the matching *_workspace query returns. The library calls
+ *     no allocator on these paths. Two calls in flight at once on different streams
+ *     must not share a workspace.
+ *   - Argument, shape and size errors are detected before anything is enqueued and
+ *     returned as a negative kfac_status; nothing is written then. A failed HIP launch
+ *     returns KFAC_ERR_HIP. kfac_last_error() gives the text of the last error on the
+ *     calling thread.
+ *   - Device pointers to fp32 data must be 4-byte aligned, to fp16 data 2-byte
+ *     aligned; faster paths are taken when rows are 16-byte aligned.
+ *   - Only gfx950 is supported; on any other device the calls return
+ *     KFAC_ERR_UNSUPPORTED.
+ */
+#ifndef KFAC_H_
+#define KFAC_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t kfac_status;
+#define KFAC_OK 0
+#define KFAC_ERR_INVALID (-1)      /* bad pointer, shape, count or option      */
+#define KFAC_ERR_UNSUPPORTED (-2)  /* not a gfx950 device, or unsupported dtype */
+#define KFAC_ERR_WORKSPACE (-3)    /* workspace NULL, misaligned or too small   */
+#define KFAC_ERR_HIP (-4)          /* a HIP runtime call or launch failed       */
+
+typedef int32_t kfac_dtype;
+#define KFAC_F16 0                 /* IEEE binary16 */
+#define KFAC_F32 1                 /* IEEE binary32 */
+
+/* One convolution or fully connected layer. Activations are NHWC [n, h, w, c_in];
+ * output gradients are NHWC [n, h_out, w_out, c_out] and must satisfy
+ * h_out = (h + 2 ph - kh) / sh + 1 and w_out likewise (dilation 1, zero padding).
+ * A fully connected layer is h = w = h_out = w_out = kh = kw = sh = sw = 1, ph = pw = 0.
+ * With bias = 1 the activation factor gets a trailing constant-1 column, so
+ * d_A = c_in*kh*kw + 1; otherwise d_A = c_in*kh*kw. d_G = c_out. */
+typedef struct kfac_layer {
+  int32_t n, h, w, c_in;
+  int32_t h_out, w_out, c_out;
+  int32_t kh, kw, sh, sw, ph, pw;
+  int32_t bias;
+} kfac_layer;
+
+/* One BatchNorm layer: normalised input x-hat and output gradient, both [n, hw, c]
+ * (NHWC with the spatial dimensions flattened). */
+typedef struct kfac_bn {
+  int32_t n, hw, c;
+} kfac_bn;
+
+/* Library version: major*10000 + minor*100 + patch. */
+int32_t kfac_version(void);
+
+/* Static description of a status code (never NULL). */
+const char* kfac_status_string(kfac_status status);
+
+/* Text of the last error raised on the calling thread ("" if none). */
+const char* kfac_last_error(void);
+
+/* ---------------------------------------------------------------------------
+ * kfac_factors - Kronecker factors of `count` layers ([OTUNYM] eq. (5), eq. (1)).
+ *
+ * For layer l with R = n*h_out*w_out patch rows:
+ *   A_l = (1/R) X^T X, X[R, d_A] the patch matrix of act[l]: row (n, oh, ow) in C
+ *         order, column (i*kw + j)*c_in + ci = act[n, oh*sh+i-ph, ow*sw+j-pw, ci]
+ *         (0 outside the image), then the bias column of ones;
+ *   G_l = (1/R) Y^T Y, Y[R, c_out] = gout[l] viewed as rows.
+ * Inputs are fp16 or fp32 (`in_dtype`, for all tensors of the call); products
+ * are accumulated in fp32. Each sum is formed in fp32 and multiplied once by
+ * fp32(1/R).
+ * Output: A_packed[l] (d_A*(d_A+1)/2 floats) and G_packed[l] (d_G*(d_G+1)/2 floats),
+ * the upper triangle row by row: element (i, j), i <= j, at i*d - i*(i-1)/2 + (j-i).
+ * ema_decay = 0 overwrites the outputs (their old contents are not read); otherwise
+ * out = ema_decay*out + (1 - ema_decay)*batch_value (stale curvature, [OTUNYM]
+ * Section 1 contributions). 0 <= ema_decay <= 1; 1 keeps the stored factors.
+ * A NULL act[l] (or gout[l]) skips that factor. Results are deterministic: the same
+ * inputs give bit-identical outputs.
+ * ------------------------------------------------------------------------- */
+kfac_status kfac_factors_workspace(const kfac_layer* layers, int32_t count, kfac_dtype in_dtype,
+                                   size_t* bytes);
+kfac_status kfac_factors(const kfac_layer* layers, int32_t count, kfac_dtype in_dtype,
+                         const void* const* act, const void* const* gout,
+                         float* const* A_packed, float* const* G_packed, float ema_decay,
+                         void* workspace, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * kfac_pack_sym - symmetric storage conversion ([OTUNYM] Section 1: the factors
+ * are symmetric, so one triangle carries all of them).
+ *
+ * Matrix m is n[m] x n[m]: full[m] row-major, packed[m] its upper triangle row by
+ * row (n(n+1)/2 floats, same order as kfac_factors).
+ * direction 0: packed <- upper triangle of full (the lower triangle is not read).
+ * direction 1: full <- symmetric matrix (both triangles written from packed).
+ * Pure data movement: bit-exact. full and packed must not overlap.
+ * ------------------------------------------------------------------------- */
+kfac_status kfac_pack_sym_workspace(int32_t count, const int32_t* n, size_t* bytes);
+kfac_status kfac_pack_sym(int32_t count, const int32_t* n, float* const* full,
+                          float* const* packed, int32_t direction, void* workspace,
+                          size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * kfac_invert - damped inverses of `count` symmetric factors ([OTUNYM] eq. (6)).
+ *
+ * inv[m] = (F + shift[m]*I)^-1 for F = the symmetric matrix whose upper triangle is
+ * read from mat[m] (n[m] x n[m], row-major fp32; the lower triangle is not read).
+ * The damping shift (Tikhonov) is per matrix, e.g. sqrt(gamma) for each Kronecker
+ * factor. inv[m] receives the full symmetric inverse (both triangles, exactly
+ * symmetric). inv[m] may equal mat[m] (in place); otherwise they must not overlap.
+ * Method: blocked Cholesky M = U^T U without pivoting whose row panels are also
+ * applied to the already-inverted leading block, so the inverse is assembled in the
+ * same sweep.
+ * info (device, count int32) receives 0, or the 1-based column of the first pivot
+ * that is not positive and finite (the LAPACK potrf convention); inv[m] is then
+ * unspecified. If chol is not NULL, chol[m] (device, n x n row-major, may be NULL
+ * per matrix) receives the Cholesky factor U in its upper triangle (the strict lower
+ * triangle is not written).
+ * ------------------------------------------------------------------------- */
+kfac_status kfac_invert_workspace(int32_t count, const int32_t* n, size_t* bytes);
+kfac_status kfac_invert(int32_t count, const int32_t* n, const float* const* mat,
+                        float* const* inv, const float* shift, int32_t* info,
+                        float* const* chol, void* workspace, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * kfac_precondition - G^-1 dW A^-1 per layer ([OTUNYM] eq. (7)).
+ *
+ * Layer l: G_inv[l] is d_g[l] x d_g[l], A_inv[l] is d_a[l] x d_a[l] (full symmetric,
+ * row-major fp32, as kfac_invert writes them), grad[l] is d_g x d_a row-major
+ * (fp16 or fp32 per grad_dtype; with a bias column its last column is the bias
+ * gradient), out[l] is d_g x d_a row-major fp32. Computed in fp32 (fp16 gradients
+ * are widened exactly). out must not overlap the inputs.
+ * ------------------------------------------------------------------------- */
+kfac_status kfac_precondition_workspace(int32_t count, const int32_t* d_g, const int32_t* d_a,
+                                        size_t* bytes);
+kfac_status kfac_precondition(int32_t count, const int32_t* d_g, const int32_t* d_a,
+                              const float* const* G_inv, const float* const* A_inv,
+                              const void* const* grad, kfac_dtype grad_dtype,
+                              float* const* out, void* workspace, size_t ws_bytes,
+                              void* stream);
+
+/* ---------------------------------------------------------------------------
+ * kfac_bn_diag - diagonal Fisher of BatchNorm gamma/beta ([OTUNYM] Section 1
+ * contributions; diagonal of the empirical Fisher of eq. (3)).
+ *
+ * Layer l: xhat[l], gout[l] are [n, hw, c] (fp16 or fp32 per in_dtype). Per sample
+ * s_gamma[n,c] = sum_hw gout*xhat, s_beta[n,c] = sum_hw gout (fp32 accumulation).
+ * fisher[l] ([2][c] fp32: row 0 gamma, row 1 beta) <- mean_n s^2, blended as
+ * fisher = ema_decay*fisher + (1-ema_decay)*batch when ema_decay != 0 (old contents
+ * not read when ema_decay = 0; ema_decay = 1 keeps the stored Fisher, the stale
+ * curvature case). precond[l] ([2][c] fp32) <- (mean_n s)/(fisher+shift) with the
+ * blended fisher. 0 <= ema_decay <= 1.
+ * ------------------------------------------------------------------------- */
+kfac_status kfac_bn_diag_workspace(const kfac_bn* layers, int32_t count, size_t* bytes);
+kfac_status kfac_bn_diag(const kfac_bn* layers, int32_t count, kfac_dtype in_dtype,
+                         const void* const* xhat, const void* const* gout,
+                         float* const* fisher, float* const* precond, float ema_decay,
+                         float shift, void* workspace, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Per-kernel event timing, for measurement. When enabled on a thread, every
+ * kernel the library launches from that thread is bracketed by two HIP events on
+ * the launch stream. kfac_timing_read synchronises those events and returns, per
+ * kernel id, the summed duration in milliseconds and the number of launches since
+ * the last reset. Ids run from 0 to kfac_timing_kernels()-1; kfac_kernel_name(id)
+ * names them. Disabled by default; costs nothing when disabled.
+ * ------------------------------------------------------------------------- */
+int32_t kfac_timing_kernels(void);
+const char* kfac_kernel_name(int32_t id);
+kfac_status kfac_timing_enable(int32_t on);
+kfac_status kfac_timing_reset(void);
+kfac_status kfac_timing_read(int32_t id, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KFAC_H_ */

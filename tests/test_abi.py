@@ -1,0 +1,130 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol that
+include/kfac.h declares, answers workspace queries, and rejects bad arguments
+before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kfac.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:kfac_status|int32_t|const char\s*\*)\s*(kfac_\w+)\s*\(",
+                                 text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import fac_second_order_amd._lib as L
+    return L
+
+
+def test_header_declares_the_five_calls():
+    names = declared_functions()
+    for base in ("kfac_factors", "kfac_invert", "kfac_precondition", "kfac_bn_diag", "kfac_pack_sym"):
+        assert base in names and base + "_workspace" in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    so = ctypes.CDLL(lib.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(so, n)]
+    assert not missing, missing
+
+
+def test_status_strings_and_version(lib):
+    so = lib._lib
+    assert lib.kfac_version() >= 100
+    for code in (0, -1, -2, -3, -4):
+        assert so.kfac_status_string(code)
+    assert so.kfac_status_string(12345) == b"unknown status"
+
+
+def test_kernel_names(lib):
+    n = lib.kfac_timing_kernels()
+    names = [lib.kfac_kernel_name(i) for i in range(n)]
+    assert "inv_update_kernel" in names and "syrk_tile_kernel" in names
+    assert lib.kfac_kernel_name(n) == ""
+
+
+def test_workspace_queries_resnet50(lib):
+    L = synth.conv_layers(32)
+    n_all = [l.d_a for l in L] + [l.d_g for l in L]
+    assert lib.kfac_factors_workspace(L) > 0
+    assert lib.kfac_invert_workspace(n_all) > 0
+    assert lib.kfac_pack_sym_workspace(n_all) > 0
+    assert lib.kfac_precondition_workspace([l.d_g for l in L], [l.d_a for l in L]) > 0
+    assert lib.kfac_bn_diag_workspace(synth.bn_layers(32)) > 0
+    assert lib.kfac_invert_workspace([]) == 0
+
+
+def test_invert_workspace_covers_panels(lib):
+    # per matrix: three 128x128 pivot blocks and two 128 x n panels (fp32)
+    b = lib.kfac_invert_workspace([4609])
+    assert b >= 4 * (3 * 128 * 128 + 2 * 128 * 4609)
+
+
+def _status(fn, *args):
+    return fn(*args)
+
+
+def test_invalid_arguments_return_errors(lib):
+    so = lib._lib
+    c = ctypes
+    n = (c.c_int32 * 2)(4, 0)
+    sz = c.c_size_t()
+    assert so.kfac_pack_sym_workspace(2, n, c.byref(sz)) == -1
+    assert b"n[1]" in so.kfac_last_error()
+    n = (c.c_int32 * 1)(4)
+    ptrs = (c.c_void_p * 1)(None)
+    assert so.kfac_pack_sym(1, n, ptrs, ptrs, 2, None, 0, None) == -1       # bad direction
+    assert so.kfac_pack_sym(1, n, ptrs, ptrs, 0, None, 0, None) == -1       # NULL matrix
+    big = (c.c_int32 * 1)(40000)
+    assert so.kfac_invert_workspace(1, big, c.byref(sz)) == -1
+    assert so.kfac_pack_sym(-1, n, ptrs, ptrs, 0, None, 0, None) == -1
+    # count 0 is a no-op
+    assert so.kfac_pack_sym(0, None, None, None, 0, None, 0, None) == 0
+
+
+def test_invalid_layer_geometry(lib):
+    bad = synth.Layer("bad", 2, 8, 8, 4, 7, 8, 4, 3, 3, 1, 1, 1, 1, 1)   # h_out should be 8
+    with pytest.raises(lib.KfacError) as e:
+        lib.kfac_factors_workspace([bad])
+    assert "h_out" in str(e.value)
+    good = synth.Layer("ok", 2, 8, 8, 4, 8, 8, 4, 3, 3, 1, 1, 1, 1, 1)
+    so = lib._lib
+    arr = lib._layers([good])
+    p = (ctypes.c_void_p * 1)(None)
+    # ema_decay out of range is refused before any pointer is looked at
+    assert so.kfac_factors(arr, 1, 0, p, p, p, p, ctypes.c_float(1.5), None, 0, None) == -1
+    assert so.kfac_factors(arr, 1, 7, p, p, p, p, ctypes.c_float(0.0), None, 0, None) == -2
+
+
+def test_bn_and_precondition_validation(lib):
+    so = lib._lib
+    c = ctypes
+    bn = lib._bns([synth.BNLayer("b", 2, 0, 4)])
+    sz = c.c_size_t()
+    assert so.kfac_bn_diag_workspace(bn, 1, c.byref(sz)) == -1
+    dg = (c.c_int32 * 1)(0)
+    da = (c.c_int32 * 1)(5)
+    assert so.kfac_precondition_workspace(1, dg, da, c.byref(sz)) == -1
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    """The product path has no fallback: a missing libkfac.so is an ImportError."""
+    import importlib.util
+    src = os.path.join(ROOT, "fac_second_order_amd", "_lib.py")
+    pkg = tmp_path / "fake_pkg"
+    pkg.mkdir()
+    (pkg / "_lib.py").write_text(open(src).read())
+    spec = importlib.util.spec_from_file_location("fake_lib", str(pkg / "_lib.py"))
+    mod = importlib.util.module_from_spec(spec)
+    with pytest.raises(ImportError, match="not built"):
+        spec.loader.exec_module(mod)

@@ -1,0 +1,317 @@
+"""GPU parity of every C-ABI entry point against the fp64 oracle on identical seeded
+inputs, at sizes the oracle finishes in seconds that span several tiles and ragged
+edges, plus the edge cases (order 1, ragged blocks, breakdown, NaN, in place, EMA,
+determinism).
+
+Tolerances (relative Frobenius error, fp64):
+  factors from fp16 inputs 1e-2, preconditioned gradients 2e-2, fp32 inverses at
+  condition number <= 1e4: 1e-4 (the stated bars); packing and integer-input factors
+  bit-exact; BatchNorm vectors 1e-4 (fp32 sums of at most ~1.5e3 terms per
+  accumulator: n*u = 1.5e3 * 6e-8 = 9e-5).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_helpers import S_GAMMA, host, relF, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+# ---------------------------------------------------------------------------
+# symmetric packing (bit-exact)
+# ---------------------------------------------------------------------------
+
+PACK_SIZES = [1, 2, 3, 63, 64, 65, 127, 128, 129, 577, 1000]
+
+
+def test_pack_unpack_bitexact(kfac_gpu):
+    rng = synth.layer_rng(1000, 0)
+    mats = [rng.standard_normal((n, n)).astype(np.float32) for n in PACK_SIZES]
+    full = [to_dev(m) for m in mats]
+    packed = [torch.full((n * (n + 1) // 2,), np.nan, device=full[0].device) for n in PACK_SIZES]
+    say("kfac_pack_sym direction 0, sizes", PACK_SIZES)
+    kfac_gpu.kfac_pack_sym(PACK_SIZES, full, packed, 0)
+    for n, m, p in zip(PACK_SIZES, mats, packed):
+        assert np.array_equal(host(p), oracle.pack_upper(m)), n
+    out = [torch.full((n, n), np.nan, device=full[0].device) for n in PACK_SIZES]
+    say("kfac_pack_sym direction 1")
+    kfac_gpu.kfac_pack_sym(PACK_SIZES, out, packed, 1)
+    for n, m, o in zip(PACK_SIZES, mats, out):
+        assert np.array_equal(host(o), oracle.unpack_upper(oracle.pack_upper(m), n)), n
+
+
+# ---------------------------------------------------------------------------
+# BatchNorm diagonal Fisher
+# ---------------------------------------------------------------------------
+
+BN_CASES = [synth.BNLayer("a", 3, 7, 5), synth.BNLayer("b", 2, 49, 64),
+            synth.BNLayer("c", 4, 300, 24), synth.BNLayer("d", 2, 3, 2050),
+            synth.BNLayer("e", 1, 1, 1), synth.BNLayer("f", 5, 1000, 8)]
+
+
+@pytest.mark.parametrize("dtype", [np.float16, np.float32])
+def test_bn_diag(kfac_gpu, dtype):
+    rng = synth.layer_rng(1001, 0)
+    xs = [rng.standard_normal(b.shape).astype(dtype) for b in BN_CASES]
+    gs = [(rng.standard_normal(b.shape) * 0.1).astype(dtype) for b in BN_CASES]
+    F = [torch.zeros(2, b.c, device="cuda") for b in BN_CASES]
+    P = [torch.zeros(2, b.c, device="cuda") for b in BN_CASES]
+    say("kfac_bn_diag", dtype.__name__, [b.shape for b in BN_CASES])
+    kfac_gpu.kfac_bn_diag(BN_CASES, [to_dev(x) for x in xs], [to_dev(g) for g in gs], F, P, 0.0, 1e-3)
+    refs = []
+    for i, b in enumerate(BN_CASES):
+        ref = oracle.bn_diag_fisher(xs[i], gs[i], 1e-3)
+        refs.append(ref)
+        assert relF(host(F[i]), ref["fisher"]) <= 1e-4, b
+        assert relF(host(P[i]), ref["precond"]) <= 1e-4, b
+    # moving average with the stored Fisher, and decay 1 (stale Fisher, fresh gradient)
+    xs2 = [rng.standard_normal(b.shape).astype(dtype) for b in BN_CASES]
+    say("kfac_bn_diag ema 0.95")
+    kfac_gpu.kfac_bn_diag(BN_CASES, [to_dev(x) for x in xs2], [to_dev(g) for g in gs], F, P, 0.95, 1e-3)
+    for i, b in enumerate(BN_CASES):
+        ref = oracle.bn_diag_fisher(xs2[i], gs[i], 1e-3, 0.95, refs[i]["fisher"])
+        assert relF(host(F[i]), ref["fisher"]) <= 1e-4, b
+        assert relF(host(P[i]), ref["precond"]) <= 1e-4, b
+        refs[i] = ref
+    say("kfac_bn_diag stale (decay 1)")
+    F_before = [host(f) for f in F]
+    kfac_gpu.kfac_bn_diag(BN_CASES, [to_dev(x) for x in xs], [to_dev(g) for g in gs], F, P, 1.0, 1e-3)
+    for i, b in enumerate(BN_CASES):
+        fresh = oracle.bn_diag_fisher(xs[i], gs[i], 1e-3)
+        assert np.array_equal(host(F[i]), F_before[i]), b
+        assert relF(host(P[i]), fresh["grad"] / (F_before[i].astype(np.float64) + 1e-3)) <= 1e-4, b
+
+
+# ---------------------------------------------------------------------------
+# factors
+# ---------------------------------------------------------------------------
+
+FACTOR_LAYERS = [
+    synth.Layer("c3x3p1", 2, 9, 7, 16, 9, 7, 24, 3, 3, 1, 1, 1, 1, 1),
+    synth.Layer("c3x3s2", 3, 10, 10, 8, 5, 5, 8, 3, 3, 2, 2, 1, 1, 1),
+    synth.Layer("conv1like", 2, 15, 15, 3, 8, 8, 16, 7, 7, 2, 2, 3, 3, 1),
+    synth.Layer("c1x1", 2, 6, 6, 136, 6, 6, 200, 1, 1, 1, 1, 0, 0, 1),
+    synth.Layer("c1x1s2", 2, 7, 7, 40, 4, 4, 12, 1, 1, 2, 2, 0, 0, 1),
+    synth.Layer("fc_nobias", 5, 1, 1, 130, 1, 1, 3, 1, 1, 1, 1, 0, 0, 0),
+    synth.Layer("c3x3big", 2, 12, 12, 32, 12, 12, 64, 3, 3, 1, 1, 1, 1, 1),   # d_A = 289
+]
+
+
+def _oracle_factors(layer, act, gout):
+    return oracle.conv_factors(act, gout, layer.kh, layer.kw, layer.sh, layer.sw,
+                               layer.ph, layer.pw, layer.bias)
+
+
+def _run_factors(kfac, layers, act, gout, ema=0.0, A=None, G=None):
+    if A is None:
+        A = [torch.full((l.d_a * (l.d_a + 1) // 2,), np.nan, device="cuda") for l in layers]
+        G = [torch.full((l.d_g * (l.d_g + 1) // 2,), np.nan, device="cuda") for l in layers]
+    kfac.kfac_factors(layers, [to_dev(a) for a in act], [to_dev(g) for g in gout], A, G, ema)
+    return A, G
+
+
+def test_factors_fp16_geometries(kfac_gpu):
+    rng = synth.layer_rng(1002, 0)
+    act = [synth.relu_normal_f16(rng, l.act_shape) for l in FACTOR_LAYERS]
+    gout = [synth.normal_f16(rng, l.gout_shape, 0.1) for l in FACTOR_LAYERS]
+    say("kfac_factors fp16", [l.name for l in FACTOR_LAYERS])
+    A, G = _run_factors(kfac_gpu, FACTOR_LAYERS, act, gout)
+    for l, layer in enumerate(FACTOR_LAYERS):
+        Ar, Gr = _oracle_factors(layer, act[l], gout[l])
+        ea = relF(host(A[l]), oracle.pack_upper(Ar))
+        eg = relF(host(G[l]), oracle.pack_upper(Gr))
+        say(f"  {layer.name}: A relF {ea:.2e}  G relF {eg:.2e}")
+        assert ea <= 1e-2 and eg <= 1e-2, layer.name
+
+
+def test_factors_integer_inputs_bitexact(kfac_gpu):
+    """Inputs in {-2..2}: fp32 sums are exact integers, so each output is the single
+    fp32 product fp32(sum) * fp32(1/R)."""
+    rng = synth.layer_rng(1003, 0)
+    act = [rng.integers(-2, 3, size=l.act_shape).astype(np.float16) for l in FACTOR_LAYERS]
+    gout = [rng.integers(-2, 3, size=l.gout_shape).astype(np.float16) for l in FACTOR_LAYERS]
+    say("kfac_factors integer inputs")
+    A, G = _run_factors(kfac_gpu, FACTOR_LAYERS, act, gout)
+    for l, layer in enumerate(FACTOR_LAYERS):
+        X = oracle.im2col_nhwc(act[l], layer.kh, layer.kw, layer.sh, layer.sw, layer.ph, layer.pw,
+                               layer.bias)
+        Gam = gout[l].astype(np.float64).reshape(-1, layer.c_out)
+        inv_r = np.float32(1.0) / np.float32(X.shape[0])
+        for got, S in ((A[l], oracle.gram(X)), (G[l], oracle.gram(Gam))):
+            expect = oracle.pack_upper(S).astype(np.float32) * inv_r
+            assert np.array_equal(host(got), expect), layer.name
+
+
+def test_factors_fp32_fc_and_kronecker(kfac_gpu):
+    """The fc workload in fp32 (a[32x64], g[32x16], no bias): factors, damped inverses
+    and G^-1 dW A^-1 through the library, checked against the oracle and against the
+    explicit 1024x1024 Kronecker solve."""
+    seed = synth.config_seed("fc")
+    a = synth.normal_f32(synth.layer_rng(seed, 0), (32, 64))
+    g = synth.normal_f32(synth.layer_rng(seed, 1), (32, 16))
+    dW = (g.astype(np.float64).T @ a.astype(np.float64)) / 32.0
+    layer = synth.Layer("fc", 32, 1, 1, 64, 1, 1, 16, 1, 1, 1, 1, 0, 0, 0)
+    st = kfac_gpu.KfacStep([layer], [], "cuda", in_dtype=torch.float32)
+    say("fc fp32 chain")
+    st.factors([to_dev(a.reshape(32, 1, 1, 64))], [to_dev(g.reshape(32, 1, 1, 16))])
+    st.invert()
+    st.precondition([to_dev(dW.astype(np.float32))])
+    A, G = oracle.conv_factors(a.reshape(32, 1, 1, 64), g.reshape(32, 1, 1, 16), 1, 1, 1, 1, 0, 0, 0)
+    assert relF(host(st.A_packed[0]), oracle.pack_upper(A)) <= 1e-5
+    assert relF(host(st.G_packed[0]), oracle.pack_upper(G)) <= 1e-5
+    Ai, _ = oracle.damped_inverse(A, S_GAMMA)
+    Gi, _ = oracle.damped_inverse(G, S_GAMMA)
+    assert relF(host(st.A_inv[0]), Ai) <= 1e-4
+    assert relF(host(st.G_inv[0]), Gi) <= 1e-4
+    K = np.kron(G + S_GAMMA * np.eye(16), A + S_GAMMA * np.eye(64))
+    ref = np.linalg.solve(K, dW.reshape(-1)).reshape(16, 64)
+    e = relF(host(st.out[0]), ref)
+    say(f"  P vs Kronecker solve relF {e:.2e}")
+    assert e <= 2e-2
+    assert int(host(st.info).sum()) == 0
+
+
+def test_factors_ema_and_determinism(kfac_gpu):
+    rng = synth.layer_rng(1004, 0)
+    layers = FACTOR_LAYERS[:4]
+    act = [synth.relu_normal_f16(rng, l.act_shape) for l in layers]
+    gout = [synth.normal_f16(rng, l.gout_shape, 0.1) for l in layers]
+    act2 = [synth.relu_normal_f16(rng, l.act_shape) for l in layers]
+    say("kfac_factors determinism + ema")
+    A1, G1 = _run_factors(kfac_gpu, layers, act, gout)
+    A2, G2 = _run_factors(kfac_gpu, layers, act, gout)
+    for x, y in zip(A1 + G1, A2 + G2):
+        assert torch.equal(x, y)
+    _run_factors(kfac_gpu, layers, act2, gout, ema=0.95, A=A1, G=G1)
+    for l, layer in enumerate(layers):
+        Ar, Gr = _oracle_factors(layer, act[l], gout[l])
+        Ar2, Gr2 = _oracle_factors(layer, act2[l], gout[l])
+        assert relF(host(A1[l]), oracle.pack_upper(oracle.ema_update(Ar, Ar2, 0.95))) <= 1e-2
+        assert relF(host(G1[l]), oracle.pack_upper(oracle.ema_update(Gr, Gr2, 0.95))) <= 1e-2
+
+
+def test_factors_skip_null(kfac_gpu):
+    """A NULL activation skips that A factor and leaves its buffer untouched."""
+    layer = FACTOR_LAYERS[0]
+    rng = synth.layer_rng(1005, 0)
+    act = synth.relu_normal_f16(rng, layer.act_shape)
+    gout = synth.normal_f16(rng, layer.gout_shape, 0.1)
+    A = [torch.full((layer.d_a * (layer.d_a + 1) // 2,), 7.0, device="cuda")]
+    G = [torch.zeros(layer.d_g * (layer.d_g + 1) // 2, device="cuda")]
+    kfac_gpu.kfac_factors([layer], [None], [to_dev(gout)], A, G)
+    assert bool((A[0] == 7.0).all())
+    _, Gr = _oracle_factors(layer, act, gout)
+    assert relF(host(G[0]), oracle.pack_upper(Gr)) <= 1e-2
+
+
+# ---------------------------------------------------------------------------
+# damped inverses
+# ---------------------------------------------------------------------------
+
+INV_SIZES = [1, 2, 3, 31, 64, 65, 127, 128, 129, 200, 257, 300, 513]
+
+
+def spd_factor(rng, n, kappa):
+    """Symmetric factor F (fp32) with cond(F + 1e-3 I) <= kappa: Gram of a
+    log-scaled Gaussian matrix with 4n rows, rescaled by its largest eigenvalue."""
+    sig = np.logspace(0, -3, n)
+    X = rng.standard_normal((4 * n, n)) * sig
+    F = X.T @ X / (4 * n)
+    lam = np.linalg.eigvalsh(F)[-1]
+    F *= (kappa - 1) * 1e-3 / lam
+    return F.astype(np.float32)
+
+
+def test_invert_sizes_and_chol(kfac_gpu):
+    rng = synth.layer_rng(1006, 0)
+    Fs = [spd_factor(rng, n, 1e4) for n in INV_SIZES]
+    mat = [to_dev(F) for F in Fs]
+    inv = [torch.full((n, n), np.nan, device="cuda") for n in INV_SIZES]
+    chol = [torch.zeros(n, n, device="cuda") for n in INV_SIZES]
+    info = torch.full((len(INV_SIZES),), -7, dtype=torch.int32, device="cuda")
+    say("kfac_invert sizes", INV_SIZES)
+    kfac_gpu.kfac_invert(INV_SIZES, mat, inv, [1e-3] * len(INV_SIZES), info, chol)
+    assert host(info).tolist() == [0] * len(INV_SIZES)
+    for n, F, X, U in zip(INV_SIZES, Fs, inv, chol):
+        M = F.astype(np.float64) + 1e-3 * np.eye(n)
+        ref, _ = oracle.damped_inverse(F, 1e-3)
+        x = host(X)
+        e = relF(x, ref)
+        Uref, _ = oracle.cholesky_upper(M)
+        eu = relF(np.triu(host(U)), Uref)
+        say(f"  n={n}: inverse relF {e:.2e}  chol relF {eu:.2e}  cond {np.linalg.cond(M):.1e}")
+        assert np.array_equal(x, x.T), n
+        assert e <= 1e-4, n
+        assert eu <= 1e-4, n
+
+
+def test_invert_in_place_matches(kfac_gpu):
+    rng = synth.layer_rng(1007, 0)
+    sizes = [129, 300]
+    Fs = [spd_factor(rng, n, 1e3) for n in sizes]
+    a = [to_dev(F) for F in Fs]
+    b = [to_dev(F) for F in Fs]
+    out = [torch.empty(n, n, device="cuda") for n in sizes]
+    info = torch.zeros(2, dtype=torch.int32, device="cuda")
+    kfac_gpu.kfac_invert(sizes, a, out, [1e-3, 1e-3], info)
+    kfac_gpu.kfac_invert(sizes, b, b, [1e-3, 1e-3], info)
+    for x, y in zip(out, b):
+        assert torch.equal(x, y)
+
+
+def test_invert_breakdown_info(kfac_gpu):
+    """Non-positive pivots report the 1-based column (LAPACK potrf convention),
+    including in a later 128-block and for NaN input."""
+    n = 300
+    cases = []
+    F1 = np.eye(n, dtype=np.float32) * 2
+    cases.append((F1, -3.0))                         # first pivot negative
+    F2 = np.eye(n, dtype=np.float32) * 2
+    F2[199, 199] = 0.5
+    cases.append((F2, -1.0))                         # pivot 200 (second block) negative
+    F3 = np.eye(n, dtype=np.float32)
+    F3[5, 7] = np.nan
+    cases.append((F3, 0.1))                          # NaN reaches pivot 8
+    F4 = np.eye(4, dtype=np.float32)
+    F4[2, 2] = 0.0
+    cases.append((F4, 0.0))                          # exact zero pivot 3
+    sizes = [F.shape[0] for F, _ in cases]
+    expect = []
+    for F, s in cases:
+        M = np.triu(F.astype(np.float64)) + np.triu(F.astype(np.float64), 1).T + s * np.eye(F.shape[0])
+        expect.append(oracle.cholesky_upper(M)[1])
+    assert expect == [1, 200, 8, 3]
+    mats = [to_dev(F) for F, _ in cases]
+    info = torch.zeros(len(cases), dtype=torch.int32, device="cuda")
+    say("kfac_invert breakdown cases")
+    kfac_gpu.kfac_invert(sizes, mats, mats, [s for _, s in cases], info)
+    assert host(info).tolist() == expect
+
+
+# ---------------------------------------------------------------------------
+# preconditioning
+# ---------------------------------------------------------------------------
+
+PRE_DIMS = [(16, 64), (64, 577), (100, 257), (3, 5), (129, 130), (1, 1)]
+
+
+@pytest.mark.parametrize("gdtype", [np.float32, np.float16])
+def test_precondition(kfac_gpu, gdtype):
+    rng = synth.layer_rng(1008, 0)
+    Gi = [rng.standard_normal((g, g)).astype(np.float32) for g, _ in PRE_DIMS]
+    Ai = [rng.standard_normal((a, a)).astype(np.float32) for _, a in PRE_DIMS]
+    Gi = [(x + x.T) / 2 for x in Gi]
+    Ai = [(x + x.T) / 2 for x in Ai]
+    grads = [(rng.standard_normal((g, a)) * 0.1).astype(gdtype) for g, a in PRE_DIMS]
+    out = [torch.full((g, a), np.nan, device="cuda") for g, a in PRE_DIMS]
+    say("kfac_precondition", gdtype.__name__, PRE_DIMS)
+    kfac_gpu.kfac_precondition([g for g, _ in PRE_DIMS], [a for _, a in PRE_DIMS],
+                               [to_dev(x) for x in Gi], [to_dev(x) for x in Ai],
+                               [to_dev(x) for x in grads], out)
+    for (g, a), G_, A_, dW, o in zip(PRE_DIMS, Gi, Ai, grads, out):
+        e = relF(host(o), oracle.precondition(G_, dW, A_))
+        assert e <= 2e-2, (g, a, e)
+        assert e <= 1e-5, (g, a, e)   # fp32 products of exactly widened inputs
