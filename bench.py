@@ -1,0 +1,254 @@
+"""Throughput of the single-GPU K-FAC step on ResNet-50 shapes at 32 samples per GPU.
+
+One step = Kronecker factors of all 54 layers (53 convolutions and the classifier,
+fp16 inputs) -> unpack to full symmetric -> 108 damped inverses -> G^-1 dW A^-1 for
+all 54 layers (fp32 gradients) -> diagonal Fisher of all 53 BatchNorm layers.
+Inputs are synthetic and seeded, resident in HBM before timing starts.
+
+Prints one JSON line: steps/s (`value`), the roofline of the kernel that takes the
+most time (algorithmic work / its average launch duration from HIP events recorded
+on its launch stream inside the timed region) and the fp64 oracle timed on the host
+cores on a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import synth  # noqa: E402
+
+PEAK_FP32_MFMA = 157.3   # TFLOP/s, MI355X dense fp32 matrix
+PEAK_FP16_MFMA = 2516.6  # TFLOP/s, MI355X dense fp16 matrix
+PEAK_HBM = 8000.0        # GB/s
+TB = 128                 # block of the inverse
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--batch", type=int, default=32)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-timing", action="store_true",
+                    help="time the steps without per-kernel events (roofline then null)")
+    ap.add_argument("--copy-calibration", type=float, default=0.0,
+                    help="also run a plain copy of this many GiB (for counter calibration)")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work (what the method must do), per step
+# ---------------------------------------------------------------------------
+
+def work(layers, bns):
+    syrk = sum(l.rows * l.d_a * (l.d_a + 1) + l.rows * l.d_g * (l.d_g + 1) for l in layers)
+    n_all = [l.d_a for l in layers] + [l.d_g for l in layers]
+    inv = sum(n ** 3 for n in n_all)
+    pre = sum(2 * l.d_g ** 2 * l.d_a + 2 * l.d_g * l.d_a ** 2 for l in layers)
+    pack_bytes = sum(n * (n + 1) // 2 * 4 + n * n * 4 for n in n_all)
+    bn_bytes = sum(2 * b.n * b.hw * b.c * 2 + 4 * b.c * 4 for b in bns)
+    # per-launch algorithmic flops of the inverse's trailing update at block step k:
+    # for every matrix still active, its upper triangle takes a rank-b_k update (n^2 b_k)
+    nb_max = max(math.ceil(n / TB) for n in n_all)
+    upd = []
+    for k in range(nb_max):
+        upd.append(sum(n * n * min(TB, n - k * TB) for n in n_all if n > k * TB))
+    assert abs(sum(upd) - inv) < 1e-6 * inv
+    return {"syrk_flop": syrk, "inv_flop": inv, "pre_flop": pre, "pack_bytes": pack_bytes,
+            "bn_bytes": bn_bytes, "update_flop_per_launch": upd}
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample, scaled stage by stage
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(layers, bns, budget_s=25.0):
+    """Times the fp64 oracle on every third layer (factors, inverses, preconditioning)
+    and every third BatchNorm layer, and scales each stage by its share of the
+    algorithmic work (flops for the matrix stages, bytes for BN) to a full step."""
+    import oracle
+    seed = 300
+    samp = layers[::3]
+    samp_bn = bns[::3]
+    s = float(np.float32(np.sqrt(1e-3)))
+    t = {"factors": 0.0, "invert": 0.0, "precondition": 0.0, "bn": 0.0}
+    w_full = work(layers, bns)
+    w_samp = work(samp, samp_bn)
+    t_start = time.perf_counter()
+    for i, l in enumerate(samp):
+        rng = synth.layer_rng(seed, i)
+        act = synth.relu_normal_f16(rng, l.act_shape)
+        gout = synth.normal_f16(rng, l.gout_shape)
+        grad = synth.normal_f32(rng, (l.d_g, l.d_a), 0.1)
+        t0 = time.perf_counter()
+        A, G = oracle.conv_factors(act, gout, l.kh, l.kw, l.sh, l.sw, l.ph, l.pw, l.bias)
+        t1 = time.perf_counter()
+        Ai, _ = oracle.damped_inverse(A.astype(np.float32), s)
+        Gi, _ = oracle.damped_inverse(G.astype(np.float32), s)
+        t2 = time.perf_counter()
+        oracle.precondition(Gi, grad, Ai)
+        t3 = time.perf_counter()
+        t["factors"] += t1 - t0
+        t["invert"] += t2 - t1
+        t["precondition"] += t3 - t2
+        if time.perf_counter() - t_start > 4 * budget_s:
+            raise RuntimeError("oracle sample exceeded its time budget")
+    for i, b in enumerate(samp_bn):
+        rng = synth.layer_rng(seed + 1, i)
+        x = synth.normal_f16(rng, b.shape)
+        g = synth.normal_f16(rng, b.shape)
+        t0 = time.perf_counter()
+        oracle.bn_diag_fisher(x, g, 1e-3)
+        t["bn"] += time.perf_counter() - t0
+    scale = {"factors": w_full["syrk_flop"] / w_samp["syrk_flop"],
+             "invert": w_full["inv_flop"] / w_samp["inv_flop"],
+             "precondition": w_full["pre_flop"] / w_samp["pre_flop"],
+             "bn": w_full["bn_bytes"] / w_samp["bn_bytes"]}
+    est = sum(t[k] * scale[k] for k in t)
+    sampled = sum(t.values())
+    cores = len(os.sched_getaffinity(0))
+    return {"value": 1.0 / est, "unit": "steps/s", "cores": cores, "kind": "oracle",
+            "sample": (f"fp64 oracle on every third of the 54 K-FAC layers ({len(samp)}) and of the "
+                       f"53 BN layers ({len(samp_bn)}), {sampled:.1f} s measured; each stage scaled by "
+                       f"its share of algorithmic work to a full step of {est:.1f} s "
+                       f"(factors {t['factors']*scale['factors']:.1f}, inverses "
+                       f"{t['invert']*scale['invert']:.1f}, precondition "
+                       f"{t['precondition']*scale['precondition']:.1f}, BN {t['bn']*scale['bn']:.1f} s)")}
+
+
+# ---------------------------------------------------------------------------
+# GPU step
+# ---------------------------------------------------------------------------
+
+def make_inputs(layers, bns, device, seed=3):
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+
+    def normal(shape, std, dtype):
+        x = torch.randn(shape, generator=g, device=device, dtype=torch.float32) * std
+        return x.to(dtype)
+
+    act = [normal(l.act_shape, 1.0, torch.float16).relu_() for l in layers]
+    gout = [normal(l.gout_shape, 1.0, torch.float16) for l in layers]
+    grads = [normal((l.d_g, l.d_a), 0.1, torch.float32) for l in layers]
+    xhat = [normal(b.shape, 1.0, torch.float16) for b in bns]
+    bgout = [normal(b.shape, 1.0, torch.float16) for b in bns]
+    return act, gout, grads, xhat, bgout
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's K-FAC step; runs on more than one GPU are not "
+              "part of this build (the multi-GPU sharding is a design note only).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import fac_second_order_amd as kfac
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    layers = synth.conv_layers(args.batch)
+    bns = synth.bn_layers(args.batch)
+    w = work(layers, bns)
+    act, gout, grads, xhat, bgout = make_inputs(layers, bns, dev)
+    st = kfac.KfacStep(layers, bns, dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        st.step(act, gout, grads, xhat, bgout)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if int(st.info.abs().sum()) != 0:
+        raise RuntimeError("Cholesky breakdown on a damped factor: " + str(st.info.tolist()))
+
+    timing = not args.no_kernel_timing
+    if timing:
+        kfac.kfac_timing_reset()
+        kfac.kfac_timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kern = {}
+    if timing:
+        kfac.kfac_timing_enable(False)
+        for i in range(kfac.kfac_timing_kernels()):
+            ms, n = kfac.kfac_timing_read(i)
+            if n:
+                kern[kfac.kfac_kernel_name(i)] = (ms, n)
+        kfac.kfac_timing_reset()
+
+    ms_step = 1e3 * elapsed / args.steps
+    value = args.steps / elapsed
+
+    roofline = None
+    if kern:
+        name, (ms, n) = max(kern.items(), key=lambda kv: kv[1][0])
+        per_launch = {  # algorithmic work of one average launch, and its bound
+            "inv_update_kernel": (sum(w["update_flop_per_launch"]) * args.steps, "mfma", PEAK_FP32_MFMA),
+            "syrk_tile_kernel": (w["syrk_flop"] * args.steps, "mfma", PEAK_FP16_MFMA),
+            "gemm_tn_kernel": (w["pre_flop"] * args.steps, "mfma", PEAK_FP32_MFMA),
+        }
+        if name in per_launch:
+            total_work, bound, peak = per_launch[name]
+            achieved = total_work / (ms * 1e-3) / 1e12      # = per-launch work / average duration
+            roofline = {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
+                        "frac": round(achieved / peak, 4), "traffic": None, "kernel": name,
+                        "launches": n, "avg_launch_us": round(1e3 * ms / n, 2),
+                        "algorithmic_per_launch": total_work / n}
+        elif name in ("bn_partial_kernel", "unpack_kernel"):
+            b = w["bn_bytes"] if name == "bn_partial_kernel" else w["pack_bytes"]
+            achieved = b * args.steps / (ms * 1e-3) / 1e9
+            roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM, "unit": "GB/s",
+                        "frac": round(achieved / PEAK_HBM, 4), "traffic": None, "kernel": name,
+                        "launches": n, "avg_launch_us": round(1e3 * ms / n, 2),
+                        "algorithmic_per_launch": b * args.steps / n}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(layers, bns)
+
+    if args.copy_calibration > 0:
+        nbytes = int(args.copy_calibration * (1 << 30))
+        a = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+    out = {
+        "metric": "K-FAC steps/sec (ResNet-50 shapes, batch 32, 1 GPU); TFLOP/s vs MFMA peak",
+        "value": round(value, 3), "unit": "steps/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "resnet50_kfac_step", "batch_per_gpu": args.batch,
+                   "kfac_layers": len(layers), "factors": 2 * len(layers), "bn_layers": len(bns),
+                   "damping": 1e-3, "inputs": "fp16 ReLU(N(0,1)) activations, fp16 N(0,1) output "
+                   "and BN gradients, fp32 N(0,1e-2) weight gradients"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels_ms_per_step": {k: round(v[0] / args.steps, 4) for k, v in
+                                sorted(kern.items(), key=lambda kv: -kv[1][0])},
+        "step_tflop": round((w["syrk_flop"] + w["inv_flop"] + w["pre_flop"]) / 1e12, 4),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
