@@ -8,13 +8,14 @@
 // that were already eliminated, so the inverse is assembled in the same sweep
 // (the symmetric Gauss-Jordan form of the Cholesky inverse). With S the working
 // matrix (upper triangle only) and k the pivot block, one step is
-//   pivot:  U_kk = chol(S_kk) and E = U_kk^-T, in one workgroup with the 128x128
-//           block held in registers (one LDS row broadcast and one barrier per
-//           column); also P^-1 = E^T E;
+//   pivot:  U_kk = chol(S_kk) and E = U_kk^-T, by one workgroup with the block in
+//           registers: per column, one LDS broadcast of the scaled pivot row and one
+//           barrier; rows above the pivot are finished and skipped;
 //   panel:  for every column block j != k: V_j = S_kj, Y_j = E V_j (the Cholesky
-//           row panel U_kj when j > k) and W_j = E^T Y_j = P^-1 V_j, on MFMA;
-//   update: S_ij -= Y_i^T Y_j for all upper tiles i, j != k (fp32 MFMA), and
-//           S_kj = W_j, S_ik = W_i^T, S_kk = -P^-1.
+//           row panel U_kj when j > k) and W_j = E^T Y_j = P^-1 V_j, on MFMA, with
+//           S_kj = W_j (S_jk = W_j^T for j < k) written in place; the block j = k
+//           writes S_kk = -E^T E = -P^-1;
+//   update: S_ij -= Y_i^T Y_j for all upper tiles i, j != k (fp32 MFMA).
 // After the last step S = -M^-1; the finish kernel negates it and writes both
 // triangles. All matrices of a call step together: they are ordered by block
 // count, so the ones still active at step k are a prefix of the list.
@@ -31,12 +32,12 @@ struct InvDesc {
   int32_t* info;   // this matrix's info entry
   float* E;        // [TB][TB]  U_kk^-T (lower triangular)
   float* Ui;       // [TB][TB]  U_kk^-1 (upper triangular)
-  float* Pn;       // [TB][TB]  -P^-1
-  float* Y;        // [TB][n]   Y panels (rows = pivot rows)
-  float* W;        // [TB][n]   W panels
+  float* Y;        // [TB][ldy] Y panels (rows = pivot rows)
   int32_t n, nb;
   float shift;
   int32_t nb64;    // 64-wide blocks (prep/finish tiles)
+  int32_t ldy;     // n rounded up to a multiple of 4 (16-byte rows)
+  int32_t pad_;
 };
 
 constexpr int FT = 64;  // prep/finish tile edge
@@ -62,151 +63,157 @@ __global__ void __launch_bounds__(256) inv_prep_kernel(const InvDesc* __restrict
   if (ti == 0 && tj == 0 && threadIdx.x == 0) *d.info = 0;
 }
 
-// Pivot block of step k: Cholesky in registers, E = U^-T, P^-1 = E^T E.
-// 1024 threads; thread t owns the 4x4 sub-block (rows 4*(t/32).., cols 4*(t%32)..).
-__global__ void __launch_bounds__(1024) inv_pivot_kernel(const InvDesc* __restrict__ desc, int k) {
+// Cholesky of the pivot block P (bk x bk, upper triangle in LDS tile L with pitch
+// LDT) and E = U^-T, by the PT threads of a block. Thread (wave w, lane l) holds rows
+// NW*r + w (r = 0..RPW-1) and columns 2l, 2l+1 of a combined matrix whose strict
+// upper triangle becomes U, strict lower triangle E and diagonal 1/U_ii. At column kk
+// the scaled pivot row r = M_kk^-1/2 * M_k. (with r_kk = M_kk^-1/2) is broadcast
+// through LDS (also in a wave-interleaved copy, so each wave fetches its multipliers
+// with 16-byte reads); every row i > kk then loses u_i * r with u_i = r_i, after its
+// entry in column kk is cleared. Rows <= kk are final and skipped. Padding
+// rows/columns (>= bk) hold the identity and stay unchanged. Writes E and U^-1 = E^T
+// (row-major, TB x TB) to the workspace, U into chol when asked, and the 1-based
+// failing column into info.
+constexpr int PT = 512;           // threads of the pivot kernel
+constexpr int NW = PT / 64;       // waves
+constexpr int RPW = TB / NW;      // rows per wave
+
+__global__ void __launch_bounds__(PT) inv_pivot_kernel(const InvDesc* __restrict__ desc, int k) {
   const InvDesc& d = desc[blockIdx.x];
   const int n = d.n, k0 = k * TB, bk = min(TB, n - k0);
-  const int t = threadIdx.x, br = t >> 5, bc = t & 31;
-  __shared__ float zrow[2][TB], erow[2][TB];
-  __shared__ float Es[TB][LDT];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  __shared__ __attribute__((aligned(16))) float prow[2][TB];    // scaled pivot row, by column
+  __shared__ __attribute__((aligned(16))) float prowi[2][TB];   // column i at (i%NW)*RPW + i/NW
+  __shared__ float dval[2];
+  __shared__ float diagU[TB];
+  __shared__ float L[TB * LDT];
 
-  float Z[4][4], E[4][4];
+  float2 M[RPW];
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int i = 4 * br + r, j = 4 * bc + c;
-      float z = (i == j) ? 1.f : 0.f;
-      if (i < bk && j < bk) {
-        const int a = min(i, j), b = max(i, j);
-        z = d.S[int64_t(k0 + a) * n + k0 + b];
-      }
-      Z[r][c] = z;
-      E[r][c] = (i == j) ? 1.f : 0.f;
-    }
-
-  int failed = 0;  // 1-based local column of the first bad pivot
+  for (int r = 0; r < RPW; ++r) {
+    const int i = NW * r + w;
+    const int j0 = 2 * lane, j1 = 2 * lane + 1;
+    float a = (i == j0) ? 1.f : 0.f, b = (i == j1) ? 1.f : 0.f;
+    if (i < bk && j0 < bk) a = d.S[int64_t(k0 + min(i, j0)) * n + k0 + max(i, j0)];
+    if (i < bk && j1 < bk) b = d.S[int64_t(k0 + min(i, j1)) * n + k0 + max(i, j1)];
+    M[r] = make_float2(a, b);
+  }
+  int failed = 0;
   for (int kk = 0; kk < bk; ++kk) {
     const int buf = kk & 1;
-    if (br == (kk >> 2)) {
-      const int r = kk & 3;
+    const int kl = kk >> 1;  // lane holding column kk
+    if (w == kk % NW) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        zrow[buf][4 * bc + c] = Z[r][c];
-        erow[buf][4 * bc + c] = E[r][c];
+      for (int r = 0; r < RPW; ++r) {
+        if (NW * r + w == kk) {  // uniform: this wave's row kk
+          const float2 m = M[r];
+          const float mine = (kk & 1) ? m.y : m.x;
+          const float piv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine), kl));
+          const float sq = sqrtf(piv);
+          const float rs = 1.0f / sq;
+          float2 sc = make_float2(m.x * rs, m.y * rs);
+          if (lane == kl) {
+            if (kk & 1) sc.y = rs; else sc.x = rs;
+          }
+          M[r] = sc;
+          reinterpret_cast<float2*>(prow[buf])[lane] = sc;
+          const int i0 = 2 * lane, i1 = 2 * lane + 1;
+          prowi[buf][(i0 % NW) * RPW + i0 / NW] = sc.x;
+          prowi[buf][(i1 % NW) * RPW + i1 / NW] = sc.y;
+          if (lane == 0) {
+            dval[buf] = piv;
+            diagU[kk] = sq;
+          }
+        }
       }
     }
     __syncthreads();
-    const float piv = zrow[buf][kk];
+    const float piv = dval[buf];
     if (!(piv > 0.f) || !isfinite(piv)) {  // same value in every thread: uniform exit
       failed = kk + 1;
       break;
     }
-    const float sq = sqrtf(piv);
-    const float rs = 1.0f / sq;
-    float ui[4], uj[4], ej[4];
+    const float2 rj = reinterpret_cast<const float2*>(prow[buf])[lane];
+    float u[RPW];  // multipliers u_i = r_i of this wave's rows
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      ui[q] = zrow[buf][4 * br + q] * rs;
-      uj[q] = zrow[buf][4 * bc + q] * rs;
-      ej[q] = erow[buf][4 * bc + q] * rs;
+    for (int q = 0; q < RPW / 4; ++q) {
+      const float4 x = reinterpret_cast<const float4*>(prowi[buf] + w * RPW)[q];
+      u[4 * q] = x.x; u[4 * q + 1] = x.y; u[4 * q + 2] = x.z; u[4 * q + 3] = x.w;
     }
+    const bool mycol = lane == kl;
+    const bool odd = kk & 1;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = 4 * br + r;
-      if (i == kk) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int j = 4 * bc + c;
-          if (j > kk) Z[r][c] = uj[c];
-          else if (j == kk) Z[r][c] = sq;
-          E[r][c] = ej[c];
+    for (int r = 0; r < RPW; ++r) {
+      if (NW * r + w > kk) {  // uniform per wave
+        float2 m = M[r];
+        if (mycol) {
+          if (odd) m.y = 0.f; else m.x = 0.f;
         }
-      } else if (i > kk) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int j = 4 * bc + c;
-          if (j > kk) Z[r][c] = fmaf(-ui[r], uj[c], Z[r][c]);
-          E[r][c] = fmaf(-ui[r], ej[c], E[r][c]);
-        }
+        m.x = fmaf(-u[r], rj.x, m.x);
+        m.y = fmaf(-u[r], rj.y, m.y);
+        M[r] = m;
       }
     }
   }
-
+  // E (strict lower + diagonal) into L, then coalesced writes of E and E^T
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int i = 4 * br + r, j = 4 * bc + c;
-      Es[i][j] = E[r][c];
-      d.E[i * TB + j] = E[r][c];
-      d.Ui[j * TB + i] = E[r][c];
-      if (d.chol && i <= j && j < bk) d.chol[int64_t(k0 + i) * n + k0 + j] = Z[r][c];
+  for (int r = 0; r < RPW; ++r) {
+    const int i = NW * r + w;
+    const float2 m = M[r];
+    L[i * LDT + 2 * lane] = (2 * lane <= i) ? m.x : 0.f;
+    L[i * LDT + 2 * lane + 1] = (2 * lane + 1 <= i) ? m.y : 0.f;
+    if (d.chol) {
+      if (i < 2 * lane && 2 * lane < bk) d.chol[int64_t(k0 + i) * n + k0 + 2 * lane] = m.x;
+      if (i < 2 * lane + 1 && 2 * lane + 1 < bk) d.chol[int64_t(k0 + i) * n + k0 + 2 * lane + 1] = m.y;
     }
-  __syncthreads();
-  float acc[4][4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) acc[r][c] = 0.f;
-  for (int q = 0; q < bk; ++q) {
-    float ei[4], ej[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      ei[r] = Es[q][4 * br + r];
-      ej[r] = Es[q][4 * bc + r];
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) acc[r][c] = fmaf(ei[r], ej[c], acc[r][c]);
   }
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) d.Pn[(4 * br + r) * TB + 4 * bc + c] = -acc[r][c];
-  if (failed && t == 0 && *d.info == 0) *d.info = k0 + failed;
+  __syncthreads();
+  for (int e = tid; e < TB * TB; e += PT) {
+    const int i = e / TB, j = e % TB;
+    d.E[e] = L[i * LDT + j];
+    d.Ui[e] = L[j * LDT + i];
+  }
+  if (d.chol)
+    for (int i = tid; i < bk; i += PT) d.chol[int64_t(k0 + i) * n + k0 + i] = diagU[i];
+  if (failed && tid == 0 && *d.info == 0) *d.info = k0 + failed;
 }
 
-// Panel of step k: for column block j != k, Y_j = E V_j and W_j = E^T Y_j.
+// Panel of step k: for column block j != k, Y_j = E V_j and W_j = E^T Y_j, with W_j
+// written into S in place; column block j = k writes S_kk = -E^T E.
 __global__ void __launch_bounds__(256) inv_panel_kernel(const InvDesc* __restrict__ desc,
                                                         const int32_t* __restrict__ begin,
                                                         int count, int k) {
   const int p = find_problem(begin, count, blockIdx.x);
   const InvDesc& d = desc[p];
-  const int c = blockIdx.x - begin[p];
-  const int j = c < k ? c : c + 1;
+  const int j = blockIdx.x - begin[p];
   const int n = d.n, k0 = k * TB, bk = min(TB, n - k0);
   const int j0 = j * TB, bj = min(TB, n - j0);
-  __shared__ float Ys[TB * LDT];
-  __shared__ float As[KT * LDT], Bs[KT * LDT];
+  __shared__ __attribute__((aligned(16))) float lds[4 * CHUNK];
+  __shared__ __attribute__((aligned(16))) float Ys[TB * LDP];
 
   Quad q;
   quad_zero(q);
-  for (int kc = 0; kc < bk; kc += KT) {
-    stage_rows(As, d.Ui, TB, kc, bk, 0, bk);            // A[p][m] = Ui[p][m] = E[m][p]
-    if (j > k) stage_rows(Bs, d.S + int64_t(k0) * n + j0, n, kc, bk, 0, bj);   // V = S_kj
-    else stage_cols(Bs, d.S + int64_t(j0) * n + k0, n, kc, bk, 0, bj);        // V = S_jk^T
-    __syncthreads();
-    quad_mma(q, As, Bs, 1.f);
-    __syncthreads();
+  const Operand Eop = op_rows(d.E, TB, bk, 0, bk);   // A[p][m] = E[p][m] = Ui[m][p]
+  if (j == k) {  // S_kk = -E^T E (upper triangle)
+    quad_gemm(q, Eop, Eop, bk, -1.f, lds);
+    quad_store_upper(q, d.S + int64_t(k0) * n + k0, n, bk);
+    return;
   }
-  quad_to_lds(q, Ys);  // rows >= bk are zero (their A columns were zero)
-  quad_store(q, d.Y + j0, n, bk, bj);
+  const Operand Uop = op_rows(d.Ui, TB, bk, 0, bk);  // A[p][m] = Ui[p][m] = E[m][p]
+  const Operand V = j > k ? op_rows(d.S + int64_t(k0) * n + j0, n, bk, 0, bj)    // V = S_kj
+                          : op_cols(d.S + int64_t(j0) * n + k0, n, bk, 0, bj);   // V = S_jk^T
+  quad_gemm(q, Uop, V, bk, 1.f, lds);
+  quad_store(q, d.Y + j0, d.ldy, bk, bj);
   if (d.chol && j > k) quad_store(q, d.chol + int64_t(k0) * n + j0, n, bk, bj);
+  quad_to_lds(q, Ys, LDP);  // rows >= bk are zero (their A columns were zero)
   quad_zero(q);
   __syncthreads();
-  for (int kc = 0; kc < bk; kc += KT) {
-    stage_rows(As, d.E, TB, kc, bk, 0, bk);             // A[p][m] = E[p][m] = Ui[m][p]
-    __syncthreads();
-    quad_mma(q, As, Ys + kc * LDT, 1.f);
-    __syncthreads();
-  }
-  quad_store(q, d.W + j0, n, bk, bj);
+  quad_gemm_lds_b(q, Eop, Ys, LDP, bk, 1.f, lds);
+  if (j > k) quad_store(q, d.S + int64_t(k0) * n + j0, n, bk, bj);        // S_kj = W_j
+  else quad_store_t(q, d.S + int64_t(j0) * n + k0, n, bk, bj, lds);       // S_jk = W_j^T
 }
 
-// Update of step k over the upper 128-tiles of every active matrix.
+// Update of step k: S_ij -= Y_i^T Y_j over the upper 128-tiles with i, j != k.
 __global__ void __launch_bounds__(256) inv_update_kernel(const InvDesc* __restrict__ desc,
                                                          const int32_t* __restrict__ begin,
                                                          int count, int k) {
@@ -214,50 +221,15 @@ __global__ void __launch_bounds__(256) inv_update_kernel(const InvDesc* __restri
   const InvDesc& d = desc[p];
   int ti, tj;
   upper_tile(blockIdx.x - begin[p], d.nb, ti, tj);
+  if (ti == k || tj == k) return;  // written by the panel kernel
   const int n = d.n, k0 = k * TB, bk = min(TB, n - k0);
   const int i0 = ti * TB, j0 = tj * TB;
   const int bi = min(TB, n - i0), bj = min(TB, n - j0);
-  __shared__ float buf[TB * LDT];
-  float* S = d.S;
-
-  if (ti == k && tj == k) {  // S_kk = -P^-1
-    for (int e = threadIdx.x; e < bk * bk; e += 256) {
-      const int r = e / bk, c = e % bk;
-      if (r <= c) S[int64_t(k0 + r) * n + k0 + c] = d.Pn[r * TB + c];
-    }
-    return;
-  }
-  if (ti == k) {  // S_kj = W_j (rows of the pivot block)
-    for (int e = threadIdx.x; e < bk * bj; e += 256) {
-      const int r = e / bj, c = e % bj;
-      S[int64_t(k0 + r) * n + j0 + c] = d.W[int64_t(r) * n + j0 + c];
-    }
-    return;
-  }
-  if (tj == k) {  // S_ik = W_i^T (column of the pivot block, above it)
-    for (int e = threadIdx.x; e < bk * bi; e += 256) {
-      const int r = e / bi, c = e % bi;  // W row r (pivot row), column i0 + c
-      buf[r * LDT + c] = d.W[int64_t(r) * n + i0 + c];
-    }
-    __syncthreads();
-    for (int e = threadIdx.x; e < bi * bk; e += 256) {
-      const int r = e / bk, c = e % bk;  // S row i0 + r, column k0 + c
-      S[int64_t(i0 + r) * n + k0 + c] = buf[c * LDT + r];
-    }
-    return;
-  }
-  float* As = buf;
-  float* Bs = buf + KT * LDT;
+  __shared__ __attribute__((aligned(16))) float lds[4 * CHUNK];
   Quad q;
-  float* C = S + int64_t(i0) * n + j0;
+  float* C = d.S + int64_t(i0) * n + j0;
   quad_load(q, C, n, bi, bj);
-  for (int kc = 0; kc < bk; kc += KT) {
-    stage_rows(As, d.Y, n, kc, bk, i0, n);
-    stage_rows(Bs, d.Y, n, kc, bk, j0, n);
-    __syncthreads();
-    quad_mma(q, As, Bs, -1.f);
-    __syncthreads();
-  }
+  quad_gemm(q, op_rows(d.Y, d.ldy, bk, i0, n), op_rows(d.Y, d.ldy, bk, j0, n), bk, -1.f, lds);
   quad_store(q, C, n, bi, bj);
 }
 
@@ -311,9 +283,9 @@ static void plan_inv(int count, const int32_t* n, InvPlan& pl) {
     pl.panel_begin[q] = static_cast<int32_t>(panels);
     pl.t64_begin[q] = static_cast<int32_t>(t64);
     tiles += int64_t(nb) * (nb + 1) / 2;
-    panels += nb - 1;
+    panels += nb;
     t64 += int64_t(nb64) * (nb64 + 1) / 2;
-    pl.floats += size_t(3) * TB * TB + size_t(2) * TB * nn;
+    pl.floats += size_t(2) * TB * TB + size_t(TB) * ((nn + 3) / 4 * 4);
     if (nb > pl.max_nb) pl.max_nb = nb;
   }
   pl.active.assign(pl.max_nb, 0);
@@ -393,9 +365,8 @@ extern "C" kfac_status kfac_invert(int32_t count, const int32_t* n, const float*
     d.shift = shift[m];
     d.E = wsf + off; off += size_t(TB) * TB;
     d.Ui = wsf + off; off += size_t(TB) * TB;
-    d.Pn = wsf + off; off += size_t(TB) * TB;
-    d.Y = wsf + off; off += size_t(TB) * n[m];
-    d.W = wsf + off; off += size_t(TB) * n[m];
+    d.ldy = (n[m] + 3) / 4 * 4;
+    d.Y = wsf + off; off += size_t(TB) * d.ldy;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   st = upload(d_desc, desc.data(), sizeof(InvDesc) * count, s);
@@ -412,7 +383,7 @@ extern "C" kfac_status kfac_invert(int32_t count, const int32_t* n, const float*
     return static_cast<unsigned>(begin[count - 1] + per(pl.order[count - 1]));
   };
   auto tiles_of = [&](int m) { int nb = (n[m] + TB - 1) / TB; return nb * (nb + 1) / 2; };
-  auto panels_of = [&](int m) { return (n[m] + TB - 1) / TB - 1; };
+  auto panels_of = [&](int m) { return (n[m] + TB - 1) / TB; };
   auto t64_of = [&](int m) { int nb = (n[m] + FT - 1) / FT; return nb * (nb + 1) / 2; };
 
   KFAC_LAUNCH(K_INV_PREP, inv_prep_kernel, dim3(grid_of(pl.t64_begin, count, t64_of)), dim3(256), 0, s,
@@ -420,13 +391,11 @@ extern "C" kfac_status kfac_invert(int32_t count, const int32_t* n, const float*
   KFAC_CHECK_LAUNCH("inv_prep_kernel");
   for (int k = 0; k < pl.max_nb; ++k) {
     const int a = pl.active[k];
-    KFAC_LAUNCH(K_INV_PIVOT, inv_pivot_kernel, dim3(a), dim3(1024), 0, s, d_desc, k);
+    KFAC_LAUNCH(K_INV_PIVOT, inv_pivot_kernel, dim3(a), dim3(PT), 0, s, d_desc, k);
     KFAC_CHECK_LAUNCH("inv_pivot_kernel");
-    const unsigned panels = grid_of(pl.panel_begin, a, panels_of);
-    if (panels) {
-      KFAC_LAUNCH(K_INV_PANEL, inv_panel_kernel, dim3(panels), dim3(256), 0, s, d_desc, d_panel, a, k);
-      KFAC_CHECK_LAUNCH("inv_panel_kernel");
-    }
+    KFAC_LAUNCH(K_INV_PANEL, inv_panel_kernel, dim3(grid_of(pl.panel_begin, a, panels_of)), dim3(256), 0, s,
+                d_desc, d_panel, a, k);
+    KFAC_CHECK_LAUNCH("inv_panel_kernel");
     KFAC_LAUNCH(K_INV_UPDATE, inv_update_kernel, dim3(grid_of(pl.tile_begin, a, tiles_of)), dim3(256), 0, s,
                 d_desc, d_tile, a, k);
     KFAC_CHECK_LAUNCH("inv_update_kernel");

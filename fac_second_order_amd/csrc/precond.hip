@@ -29,19 +29,15 @@ __global__ void __launch_bounds__(256) gemm_tn_kernel(const GemmDesc* __restrict
   const int t = blockIdx.x - begin[p];
   const int mt = t / d.tn, nt = t % d.tn;
   const int m0 = mt * TB, n0 = nt * TB;
-  __shared__ float As[KT * LDT], Bs[KT * LDT];
+  __shared__ __attribute__((aligned(16))) float lds[4 * CHUNK];
   Quad q;
   quad_zero(q);
-  for (int kc = 0; kc < d.K; kc += KT) {
-    stage_rows(As, d.A, d.lda, kc, d.K, m0, d.M);
-    if (d.b_f16) stage_rows_h(Bs, static_cast<const _Float16*>(d.B), d.ldb, kc, d.K, n0, d.N);
-    else stage_rows(Bs, static_cast<const float*>(d.B), d.ldb, kc, d.K, n0, d.N);
-    __syncthreads();
-    quad_mma(q, As, Bs, 1.f);
-    __syncthreads();
-  }
+  const Operand A = op_rows(d.A, d.lda, d.K, m0, d.M);
+  const Operand B = d.b_f16 ? op_rows_h(static_cast<const _Float16*>(d.B), d.ldb, d.K, n0, d.N)
+                            : op_rows(static_cast<const float*>(d.B), d.ldb, d.K, n0, d.N);
+  quad_gemm(q, A, B, d.K, 1.f, lds);
   const int rv = min(TB, d.M - m0), cv = min(TB, d.N - n0);
-  if (d.c_trans) quad_store_t(q, d.C + int64_t(n0) * d.ldc + m0, d.ldc, rv, cv);
+  if (d.c_trans) quad_store_t(q, d.C + int64_t(n0) * d.ldc + m0, d.ldc, rv, cv, lds);
   else quad_store(q, d.C + int64_t(m0) * d.ldc + n0, d.ldc, rv, cv);
 }
 

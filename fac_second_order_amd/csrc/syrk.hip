@@ -51,62 +51,113 @@ struct SyrkDesc {
   float inv_r, r_f;
 };
 
-// Position of the first of 8 columns handled by a thread (constant over rows).
-struct ColPos {
-  int c0;        // first virtual column
-  int ki, kj;    // kernel tap (im2col)
-  int ci;        // first channel (im2col)
-};
-
-__device__ inline ColPos col_pos(const SyrkDesc& d, int c0) {
-  ColPos p;
-  p.c0 = c0;
-  if (d.mode == 1) {
-    const int tap = c0 / d.C;
-    p.ci = c0 - tap * d.C;
-    p.ki = tap / d.kw;
-    p.kj = tap - p.ki * d.kw;
-  } else {
-    p.ki = p.kj = p.ci = 0;
-  }
-  return p;
-}
-
-// Value of X[row][c] (0 outside the image or beyond d_core), any input dtype.
+// Value of X[row][c] (0 outside the image or beyond d_core), any input dtype
+// (plain path for fp32 inputs).
 template <class T>
-__device__ inline float x_elem(const SyrkDesc& d, int64_t row, int c) {
+__device__ inline float x_elem(const SyrkDesc& d, int row, int c) {
   if (c >= d.d_core) return 0.f;
   const T* src = static_cast<const T*>(d.src);
-  if (d.mode == 0) return static_cast<float>(src[row * d.ld + c]);
+  if (d.mode == 0) return static_cast<float>(src[int64_t(row) * d.ld + c]);
   const int hw = d.Ho * d.Wo;
-  const int64_t n = row / hw;
-  const int rem = static_cast<int>(row - n * hw);
+  const int n = row / hw;
+  const int rem = row - n * hw;
   const int oh = rem / d.Wo, ow = rem - (rem / d.Wo) * d.Wo;
   const int tap = c / d.C, ci = c - tap * d.C;
   const int ki = tap / d.kw, kj = tap - ki * d.kw;
   const int ih = oh * d.sh + ki - d.ph, iw = ow * d.sw + kj - d.pw;
   if (ih < 0 || ih >= d.H || iw < 0 || iw >= d.W) return 0.f;
-  return static_cast<float>(src[((n * d.H + ih) * d.W + iw) * d.C + ci]);
+  return static_cast<float>(src[((int64_t(n) * d.H + ih) * d.W + iw) * d.C + ci]);
 }
 
-// 8 consecutive columns of row `row` as fp16 (zeros when !valid).
-__device__ inline v8h gather8(const SyrkDesc& d, bool valid, int64_t row, const ColPos& p) {
-  v8h z = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (!valid || p.c0 >= d.d_core) return z;
-  const _Float16* src = static_cast<const _Float16*>(d.src);
-  if (d.vec) {  // 8 columns share one tap and lie inside d_core (d_core % 8 == 0)
-    if (d.mode == 0) return *reinterpret_cast<const v8h*>(src + row * d.ld + p.c0);
-    const int hw = d.Ho * d.Wo;
-    const int64_t n = row / hw;
-    const int rem = static_cast<int>(row - n * hw);
-    const int oh = rem / d.Wo, ow = rem - (rem / d.Wo) * d.Wo;
-    const int ih = oh * d.sh + p.ki - d.ph, iw = ow * d.sw + p.kj - d.pw;
-    if (ih < 0 || ih >= d.H || iw < 0 || iw >= d.W) return z;
-    return *reinterpret_cast<const v8h*>(src + ((n * d.H + ih) * d.W + iw) * d.C + p.ci);
+// Row decode of one chunk of patch rows, shared through LDS: element offset of the
+// row's (ih0, iw0) pixel and the top-left input coordinates of its receptive field
+// (ih0 = oh*sh - ph, iw0 = ow*sw - pw). Rows past the end get an ih0 that fails every
+// bounds check. In row mode (G factors, 1x1 stride-1 convolutions) the offset is
+// row*ld and ih0 = iw0 = 0 with H = W = 1.
+struct RowTab {
+  int64_t off[KC];
+  int32_t ih[KC];
+  int32_t iw[KC];
+};
+
+constexpr int32_t kNoRow = -(1 << 29);
+
+__device__ inline void fill_rowtab(const SyrkDesc& d, RowTab& t, int r0, int r_end) {
+  const int tid = threadIdx.x;
+  if (tid >= KC) return;
+  const int row = r0 + tid;
+  if (row >= r_end) {
+    t.off[tid] = 0;
+    t.ih[tid] = kNoRow;
+    t.iw[tid] = 0;
+    return;
   }
-  v8h v;
+  if (d.mode == 0) {
+    t.off[tid] = int64_t(row) * d.ld;
+    t.ih[tid] = 0;
+    t.iw[tid] = 0;
+    return;
+  }
+  const int hw = d.Ho * d.Wo;
+  const int n = row / hw;
+  const int rem = row - n * hw;
+  const int oh = rem / d.Wo;
+  const int ow = rem - oh * d.Wo;
+  const int ih0 = oh * d.sh - d.ph, iw0 = ow * d.sw - d.pw;
+  t.off[tid] = ((int64_t(n) * d.H + ih0) * d.W + iw0) * d.C;
+  t.ih[tid] = ih0;
+  t.iw[tid] = iw0;
+}
+
+// Per-thread column data for its 8 columns [c0, c0+8): tap offsets inside the input
+// tensor and tap coordinates for the bounds checks (constant over rows).
+struct ColTab {
+  int32_t coff[8];
+  int32_t ki[8];
+  int32_t kj[8];
+};
+
+__device__ inline void fill_coltab(const SyrkDesc& d, int c0, ColTab& ct) {
 #pragma unroll
-  for (int q = 0; q < 8; ++q) v[q] = static_cast<_Float16>(x_elem<_Float16>(d, row, p.c0 + q));
+  for (int q = 0; q < 8; ++q) {
+    const int c = c0 + q;
+    if (c >= d.d_core) {
+      ct.coff[q] = 0;
+      ct.ki[q] = kNoRow;
+      ct.kj[q] = 0;
+    } else if (d.mode == 0) {
+      ct.coff[q] = c;
+      ct.ki[q] = 0;
+      ct.kj[q] = 0;
+    } else {
+      const int tap = c / d.C, ci = c - tap * d.C;
+      const int ki = tap / d.kw, kj = tap - ki * d.kw;
+      ct.coff[q] = (ki * d.W + kj) * d.C + ci;
+      ct.ki[q] = ki;
+      ct.kj[q] = kj;
+    }
+  }
+}
+
+// 8 consecutive columns of the chunk row rr as fp16 (zeros outside the image, past
+// the last row or past d_core).
+__device__ inline v8h gather8(const SyrkDesc& d, const RowTab& t, int rr, const ColTab& ct) {
+  const _Float16* src = static_cast<const _Float16*>(d.src);
+  const int ih = t.ih[rr], iw = t.iw[rr];
+  const int64_t off = t.off[rr];
+  v8h v;
+  if (d.vec) {  // the 8 columns share one tap: one 16-byte load
+    const bool ok = unsigned(ih + ct.ki[0]) < unsigned(d.H) && unsigned(iw + ct.kj[0]) < unsigned(d.W);
+    if (ok) return *reinterpret_cast<const v8h*>(src + off + ct.coff[0]);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = static_cast<_Float16>(0.f);
+    return v;
+  }
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const bool ok = unsigned(ih + ct.ki[q]) < unsigned(d.H) && unsigned(iw + ct.kj[q]) < unsigned(d.W);
+    v[q] = ok ? src[off + ct.coff[q]] : static_cast<_Float16>(0.f);
+  }
   return v;
 }
 
@@ -153,6 +204,7 @@ __global__ void __launch_bounds__(256) syrk_f16_kernel(const SyrkDesc* __restric
   const bool diag = ti == tj;
 
   __shared__ __attribute__((aligned(16))) _Float16 lds[2][ST * LDK];
+  __shared__ RowTab tab[2];
   _Float16* Xa = lds[0];
   _Float16* Xb = diag ? lds[0] : lds[1];
 
@@ -160,10 +212,11 @@ __global__ void __launch_bounds__(256) syrk_f16_kernel(const SyrkDesc* __restric
   const int wm = wave >> 1, wn = wave & 1;
   const bool skip = diag && wm > wn;  // quadrant strictly below the diagonal
   const int cg = tid & 15, rg = tid >> 4;
-  const ColPos pa = col_pos(d, ti * ST + cg * 8);
-  const ColPos pb = col_pos(d, tj * ST + cg * 8);
-  const int64_t r_begin = int64_t(s) * d.rows_per_split;
-  const int64_t r_end = min(int64_t(d.R), r_begin + d.rows_per_split);
+  ColTab ca, cb;
+  fill_coltab(d, ti * ST + cg * 8, ca);
+  if (!diag) fill_coltab(d, tj * ST + cg * 8, cb);
+  const int r_begin = s * d.rows_per_split;
+  const int r_end = min(d.R, r_begin + d.rows_per_split);
   const bool want_col = diag && d.bias && tid < ST;
 
   v16f acc[2][2];
@@ -175,15 +228,19 @@ __global__ void __launch_bounds__(256) syrk_f16_kernel(const SyrkDesc* __restric
       for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
   float colsum = 0.f;
 
-  for (int64_t r0 = r_begin; r0 < r_end; r0 += KC) {
-    v8h va[4], vb[4];
+  // prologue: row table and registers of the first chunk
+  fill_rowtab(d, tab[0], r_begin, r_end);
+  __syncthreads();
+  v8h va[4], vb[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int64_t row = r0 + rg * 4 + q;
-      va[q] = gather8(d, row < r_end, row, pa);
-      if (!diag) vb[q] = gather8(d, row < r_end, row, pb);
-    }
-    __syncthreads();  // previous chunk fully consumed
+  for (int q = 0; q < 4; ++q) {
+    va[q] = gather8(d, tab[0], rg * 4 + q, ca);
+    if (!diag) vb[q] = gather8(d, tab[0], rg * 4 + q, cb);
+  }
+  int c = 0;
+  for (int r0 = r_begin; r0 < r_end; r0 += KC, ++c) {
+    const bool more = r0 + KC < r_end;
+    __syncthreads();  // the previous chunk's LDS operands are consumed
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       v4h w = {va[0][e], va[1][e], va[2][e], va[3][e]};
@@ -193,13 +250,22 @@ __global__ void __launch_bounds__(256) syrk_f16_kernel(const SyrkDesc* __restric
         *reinterpret_cast<v4h*>(Xb + (cg * 8 + e) * LDK + rg * 4) = u;
       }
     }
+    if (more) fill_rowtab(d, tab[(c + 1) & 1], r0 + KC, r_end);
     __syncthreads();
+    if (more) {  // next chunk's global loads overlap this chunk's MFMAs
+      const RowTab& tn = tab[(c + 1) & 1];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        va[q] = gather8(d, tn, rg * 4 + q, ca);
+        if (!diag) vb[q] = gather8(d, tn, rg * 4 + q, cb);
+      }
+    }
     if (want_col) {
 #pragma unroll
       for (int k = 0; k < KC; k += 8) {
-        v8h c = *reinterpret_cast<const v8h*>(Xa + tid * LDK + k);
+        v8h cv = *reinterpret_cast<const v8h*>(Xa + tid * LDK + k);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) colsum += static_cast<float>(c[q]);
+        for (int q = 0; q < 8; ++q) colsum += static_cast<float>(cv[q]);
       }
     }
     if (!skip) {
@@ -245,8 +311,8 @@ __global__ void __launch_bounds__(256) syrk_f16_kernel(const SyrkDesc* __restric
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
             const int r = wm * 64 + a * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-            const int c = wn * 64 + b * 32 + (lane & 31);
-            P[r * ST + c] = acc[a][b][e];
+            const int cc = wn * 64 + b * 32 + (lane & 31);
+            P[r * ST + cc] = acc[a][b][e];
           }
     }
     if (want_col) d.pcol[(int64_t(s) * d.nb + ti) * ST + tid] = colsum;
@@ -271,8 +337,8 @@ __global__ void __launch_bounds__(256) syrk_f32_kernel(const SyrkDesc* __restric
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const bool skip = diag && wm > wn;
-  const int64_t r_begin = int64_t(s) * d.rows_per_split;
-  const int64_t r_end = min(int64_t(d.R), r_begin + d.rows_per_split);
+  const int r_begin = s * d.rows_per_split;
+  const int r_end = min(d.R, r_begin + d.rows_per_split);
   const bool want_col = diag && d.bias && tid < ST;
 
   v16f acc[2][2];
@@ -284,11 +350,11 @@ __global__ void __launch_bounds__(256) syrk_f32_kernel(const SyrkDesc* __restric
       for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
   float colsum = 0.f;
 
-  for (int64_t r0 = r_begin; r0 < r_end; r0 += KC32) {
+  for (int r0 = r_begin; r0 < r_end; r0 += KC32) {
     __syncthreads();
     for (int e = tid; e < KC32 * ST; e += 256) {
       const int k = e / ST, c = e % ST;
-      const int64_t row = r0 + k;
+      const int row = r0 + k;
       const bool ok = row < r_end;
       la[k * LDN32 + c] = ok ? x_elem<float>(d, row, ti * ST + c) : 0.f;
       lb[k * LDN32 + c] = ok ? x_elem<float>(d, row, tj * ST + c) : 0.f;
@@ -339,37 +405,50 @@ __global__ void __launch_bounds__(256) syrk_f32_kernel(const SyrkDesc* __restric
   }
 }
 
-// Adds the row-split partial tiles in split order, scales, blends and packs.
+// Adds the row-split partial tiles in split order, scales, blends and packs. One
+// block per 1024 entries of a tile (RED_PARTS blocks per tile), 4 entries per thread.
+constexpr int RED_PARTS = ST * ST / 1024;
+
 __global__ void __launch_bounds__(256) syrk_reduce_kernel(const SyrkDesc* __restrict__ desc,
                                                           const int32_t* __restrict__ rbegin,
                                                           const int32_t* __restrict__ rprob,
                                                           int rcount, float decay) {
   const int q = find_problem(rbegin, rcount, blockIdx.x);
   const SyrkDesc& d = desc[rprob[q]];
-  const int t = blockIdx.x - rbegin[q];
+  const int local = blockIdx.x - rbegin[q];
+  const int t = local / RED_PARTS, part = local % RED_PARTS;
   int ti, tj;
   upper_tile(t, d.nb, ti, tj);
   const int64_t tstride = int64_t(d.nt) * ST * ST;
-  const float* P = d.partial + int64_t(t) * ST * ST;
-  for (int e = threadIdx.x; e < ST * ST; e += 256) {
-    const int i = ti * ST + e / ST, j = tj * ST + e % ST;
-    if (i <= j && j < d.d_core) {
-      float sum = 0.f;
-      for (int s = 0; s < d.splits; ++s) sum += P[s * tstride + e];
-      const int64_t o = packed_off(i, j, d.d);
-      d.out[o] = blend(sum * d.inv_r, d.out, o, decay);
+  const int e0 = part * 1024 + threadIdx.x * 4;
+  const int i = ti * ST + e0 / ST, j0 = tj * ST + e0 % ST;
+  if (i < d.d_core && j0 + 3 >= i && j0 < d.d_core) {
+    const float* P = d.partial + int64_t(t) * ST * ST + e0;
+    float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s = 0; s < d.splits; ++s) {
+      const float4 x = *reinterpret_cast<const float4*>(P + s * tstride);
+      sum.x += x.x; sum.y += x.y; sum.z += x.z; sum.w += x.w;
+    }
+    const float v4[4] = {sum.x, sum.y, sum.z, sum.w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = j0 + u;
+      if (j >= i && j < d.d_core) {
+        const int64_t o = packed_off(i, j, d.d);
+        d.out[o] = blend(v4[u] * d.inv_r, d.out, o, decay);
+      }
     }
   }
-  if (ti == tj && d.bias && threadIdx.x < ST) {
-    const int i = ti * ST + threadIdx.x;
-    if (i < d.d_core) {
+  if (part == 0 && ti == tj && d.bias && threadIdx.x < ST) {
+    const int ib = ti * ST + threadIdx.x;
+    if (ib < d.d_core) {
       float sum = 0.f;
       for (int s = 0; s < d.splits; ++s) sum += d.pcol[(int64_t(s) * d.nb + ti) * ST + threadIdx.x];
-      const int64_t o = packed_off(i, d.d_core, d.d);
+      const int64_t o = packed_off(ib, d.d_core, d.d);
       d.out[o] = blend(sum * d.inv_r, d.out, o, decay);
     }
   }
-  if (t == 0 && d.bias && threadIdx.x == 0) {
+  if (t == 0 && part == 0 && d.bias && threadIdx.x == 0) {
     const int64_t o = packed_off(d.d_core, d.d_core, d.d);
     d.out[o] = blend(d.r_f * d.inv_r, d.out, o, decay);
   }
@@ -398,11 +477,13 @@ static SyrkDesc make_problem(const kfac_layer& L, int which) {
         L.h == L.h_out && L.w == L.w_out) {  // 1x1 stride-1: the activation is X itself
       d.mode = 0;
       d.ld = L.c_in;
+      d.H = d.W = 1;
     }
   } else {
     d.mode = 0;
     d.d_core = L.c_out;
     d.ld = L.c_out;
+    d.H = d.W = 1;
     d.bias = 0;
   }
   d.d = d.d_core + d.bias;
@@ -442,7 +523,7 @@ static void finish_plan(SyrkPlan& pl) {
     if (d.splits > 1) {
       pl.rbegin.push_back(static_cast<int32_t>(pl.ritems));
       pl.rprob.push_back(static_cast<int32_t>(p));
-      pl.ritems += d.nt;
+      pl.ritems += int64_t(d.nt) * RED_PARTS;
       pl.partial_floats += size_t(d.splits) * d.nt * ST * ST + size_t(d.splits) * d.nb * ST;
     }
   }

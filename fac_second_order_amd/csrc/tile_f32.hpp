@@ -1,7 +1,11 @@
 // fp32 MFMA tile engine: a 256-thread block accumulates a 128x128 fp32 tile
 // C[m][n] += sum_k A[k][m] * B[k][n] with both operands read as rows of k
-// ("A^T B" form), staged through LDS in chunks of 32 k. Four waves each own a
-// 64x64 quadrant made of 2x2 v_mfma_f32_32x32x2f32 blocks.
+// ("A^T B" form). K is consumed in chunks of 32: while the MFMAs work on chunk c out
+// of one LDS buffer, the global loads of chunk c+1 are in flight into registers and
+// then land in the other LDS buffer, so there is one barrier per chunk. Each thread
+// stages a 4(k) x 4(m) patch per operand with 16-byte loads when the rows are
+// 16-byte aligned (scalar loads otherwise). Four waves each own a 64x64 quadrant
+// made of 2x2 v_mfma_f32_32x32x2f32 blocks.
 //
 // MFMA lane layout (v_mfma_f32_32x32x2f32, wave64): A operand element (m, k) sits
 // in lane m + 32k, B operand element (k, n) in lane n + 32k; accumulator register e
@@ -13,7 +17,9 @@ namespace kfac {
 
 constexpr int TB = 128;       // tile edge
 constexpr int KT = 32;        // k per LDS chunk
-constexpr int LDT = TB + 1;   // LDS pitch (floats)
+constexpr int LDP = TB + 4;   // LDS pitch of staged chunks [k][m] (floats, 16-byte rows)
+constexpr int LDT = TB + 1;   // pitch of full 128x128 LDS tiles used outside the engine
+constexpr int CHUNK = KT * LDP;  // floats per staged operand chunk
 
 struct Quad {
   v16f c[2][2];
@@ -34,52 +40,131 @@ __device__ inline int quad_row(int wm, int a, int e, int lane) {
 }
 __device__ inline int quad_col(int wn, int b, int lane) { return wn * 64 + b * 32 + (lane & 31); }
 
-// LDS chunk [KT][LDT] <- rows [k0, k0+KT) x columns [c0, c0+TB) of a row-major
-// matrix (leading dimension ld); zero where k >= kvalid or column >= cvalid.
-__device__ inline void stage_rows(float* lds, const float* src, int64_t ld, int k0, int kvalid,
-                                  int c0, int cvalid) {
-  for (int e = threadIdx.x; e < KT * TB; e += 256) {
-    const int k = e / TB, c = e % TB;
-    const int gk = k0 + k, gc = c0 + c;
-    lds[k * LDT + c] = (gk < kvalid && gc < cvalid) ? src[int64_t(gk) * ld + gc] : 0.f;
+// One operand: element (k, m) of the logical [K][M] operand is src[k*ld + m] (rows),
+// or src[m*ld + k] when trans. Columns m0.. of the tile; valid k < kv, m < mv.
+struct Operand {
+  const void* src;
+  int64_t ld;
+  int kv, m0, mv;
+  bool f16, trans, vec4;  // vec4: rows are 16-byte aligned (rows form, fp32 only)
+};
+
+__device__ inline Operand op_rows(const float* src, int64_t ld, int kv, int m0, int mv) {
+  Operand o{src, ld, kv, m0, mv, false, false,
+            (ld % 4 == 0) && (reinterpret_cast<uintptr_t>(src) % 16 == 0) && (m0 % 4 == 0)};
+  return o;
+}
+__device__ inline Operand op_rows_h(const _Float16* src, int64_t ld, int kv, int m0, int mv) {
+  Operand o{src, ld, kv, m0, mv, true, false, false};
+  return o;
+}
+__device__ inline Operand op_cols(const float* src, int64_t ld, int kv, int m0, int mv) {
+  Operand o{src, ld, kv, m0, mv, false, true, false};
+  return o;
+}
+
+// Thread (kg = tid/32, mg = tid%32) stages k = 4kg..4kg+3 and m = 4mg..4mg+3 of a chunk.
+__device__ inline void op_fetch(const Operand& o, int k0, float4 (&r)[4]) {
+  const int kg = threadIdx.x >> 5, mg = threadIdx.x & 31;
+  const int m = o.m0 + 4 * mg;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int k = k0 + 4 * kg + q;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    if (k < o.kv) {
+      if (o.vec4 && m + 3 < o.mv) {
+        const float4 x = *reinterpret_cast<const float4*>(static_cast<const float*>(o.src) + k * o.ld + m);
+        v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+      } else if (o.trans) {
+        const float* s = static_cast<const float*>(o.src);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (m + u < o.mv) v[u] = s[int64_t(m + u) * o.ld + k];
+      } else if (o.f16) {
+        const _Float16* s = static_cast<const _Float16*>(o.src) + k * o.ld;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (m + u < o.mv) v[u] = static_cast<float>(s[m + u]);
+      } else {
+        const float* s = static_cast<const float*>(o.src) + k * o.ld;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (m + u < o.mv) v[u] = s[m + u];
+      }
+    }
+    r[q] = make_float4(v[0], v[1], v[2], v[3]);
   }
 }
 
-// Same, fp16 source widened exactly to fp32.
-__device__ inline void stage_rows_h(float* lds, const _Float16* src, int64_t ld, int k0, int kvalid,
-                                    int c0, int cvalid) {
-  for (int e = threadIdx.x; e < KT * TB; e += 256) {
-    const int k = e / TB, c = e % TB;
-    const int gk = k0 + k, gc = c0 + c;
-    lds[k * LDT + c] = (gk < kvalid && gc < cvalid) ? static_cast<float>(src[int64_t(gk) * ld + gc]) : 0.f;
-  }
+__device__ inline void op_store(float* lds, const float4 (&r)[4]) {
+  const int kg = threadIdx.x >> 5, mg = threadIdx.x & 31;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) *reinterpret_cast<float4*>(lds + (4 * kg + q) * LDP + 4 * mg) = r[q];
 }
 
-// LDS chunk [KT][LDT] <- transposed read: chunk[k][c] = src[(c0+c)*ld + k0+k].
-__device__ inline void stage_cols(float* lds, const float* src, int64_t ld, int k0, int kvalid,
-                                  int c0, int cvalid) {
-  for (int e = threadIdx.x; e < KT * TB; e += 256) {
-    const int c = e / KT, k = e % KT;
-    const int gk = k0 + k, gc = c0 + c;
-    lds[k * LDT + c] = (gk < kvalid && gc < cvalid) ? src[int64_t(gc) * ld + gk] : 0.f;
-  }
-}
-
-// acc += sign * As^T Bs over one staged chunk (KT values of k).
-__device__ inline void quad_mma(Quad& q, const float* As, const float* Bs, float sign) {
+// acc += sign * As^T Bs over one staged chunk (KT values of k), pitches in floats.
+__device__ inline void quad_mma_p(Quad& q, const float* As, int apitch, const float* Bs, int bpitch,
+                                  float sign) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int ml = lane & 31, kh = lane >> 5;
-#pragma unroll 4
+#pragma unroll 8
   for (int k = 0; k < KT; k += 2) {
-    const float* ar = As + (k + kh) * LDT + wm * 64 + ml;
-    const float* br = Bs + (k + kh) * LDT + wn * 64 + ml;
+    const float* ar = As + (k + kh) * apitch + wm * 64 + ml;
+    const float* br = Bs + (k + kh) * bpitch + wn * 64 + ml;
     const float a0 = ar[0] * sign, a1 = ar[32] * sign;
     const float b0 = br[0], b1 = br[32];
     q.c[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, q.c[0][0], 0, 0, 0);
     q.c[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, q.c[0][1], 0, 0, 0);
     q.c[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, q.c[1][0], 0, 0, 0);
     q.c[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, q.c[1][1], 0, 0, 0);
+  }
+}
+
+// acc += sign * A^T B over k in [0, K), pipelined. lds holds 4*CHUNK floats
+// (two buffers of the A and B chunks). Ends with a barrier.
+__device__ inline void quad_gemm(Quad& q, const Operand& A, const Operand& B, int K, float sign,
+                                 float* lds) {
+  const int nchunk = (K + KT - 1) / KT;
+  float4 ra[4], rb[4];
+  op_fetch(A, 0, ra);
+  op_fetch(B, 0, rb);
+  op_store(lds, ra);
+  op_store(lds + CHUNK, rb);
+  __syncthreads();
+  for (int c = 0; c < nchunk; ++c) {
+    float* cur = lds + (c & 1) * 2 * CHUNK;
+    float* nxt = lds + ((c + 1) & 1) * 2 * CHUNK;
+    const bool more = c + 1 < nchunk;
+    if (more) {
+      op_fetch(A, (c + 1) * KT, ra);
+      op_fetch(B, (c + 1) * KT, rb);
+    }
+    quad_mma_p(q, cur, LDP, cur + CHUNK, LDP, sign);
+    if (more) {
+      op_store(nxt, ra);
+      op_store(nxt + CHUNK, rb);
+    }
+    __syncthreads();
+  }
+}
+
+// Same with the B operand already resident in LDS as rows [k][n] (pitch bpitch).
+__device__ inline void quad_gemm_lds_b(Quad& q, const Operand& A, const float* Bl, int bpitch, int K,
+                                       float sign, float* lds) {
+  const int nchunk = (K + KT - 1) / KT;
+  float4 ra[4];
+  op_fetch(A, 0, ra);
+  op_store(lds, ra);
+  __syncthreads();
+  for (int c = 0; c < nchunk; ++c) {
+    float* cur = lds + (c & 1) * CHUNK;
+    float* nxt = lds + ((c + 1) & 1) * CHUNK;
+    const bool more = c + 1 < nchunk;
+    if (more) op_fetch(A, (c + 1) * KT, ra);
+    quad_mma_p(q, cur, LDP, Bl + c * KT * bpitch, bpitch, sign);
+    if (more) op_store(nxt, ra);
+    __syncthreads();
   }
 }
 
@@ -98,6 +183,21 @@ __device__ inline void quad_load(Quad& q, const float* src, int64_t ld, int rval
       }
 }
 
+// q += tile loaded from global.
+__device__ inline void quad_add_global(Quad& q, const float* src, int64_t ld, int rvalid, int cvalid) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int r = quad_row(wm, a, e, lane), c = quad_col(wn, b, lane);
+        if (r < rvalid && c < cvalid) q.c[a][b][e] += src[int64_t(r) * ld + c];
+      }
+}
+
 __device__ inline void quad_store(const Quad& q, float* dst, int64_t ld, int rvalid, int cvalid,
                                   float scale = 1.f) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -113,8 +213,8 @@ __device__ inline void quad_store(const Quad& q, float* dst, int64_t ld, int rva
       }
 }
 
-// Transposed store: dst[c*ld + r] = tile[r][c].
-__device__ inline void quad_store_t(const Quad& q, float* dst, int64_t ld, int rvalid, int cvalid) {
+// Upper-triangle store of a square tile: entries r <= c < nvalid.
+__device__ inline void quad_store_upper(const Quad& q, float* dst, int64_t ld, int nvalid) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 #pragma unroll
@@ -124,12 +224,14 @@ __device__ inline void quad_store_t(const Quad& q, float* dst, int64_t ld, int r
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int r = quad_row(wm, a, e, lane), c = quad_col(wn, b, lane);
-        if (r < rvalid && c < cvalid) dst[int64_t(c) * ld + r] = q.c[a][b][e];
+        if (r <= c && c < nvalid) dst[int64_t(r) * ld + c] = q.c[a][b][e];
       }
 }
 
-// Tile -> LDS [TB][LDT] (rows r, columns c), all 128x128 entries.
-__device__ inline void quad_to_lds(const Quad& q, float* lds) {
+// Transposed store through LDS (coalesced): dst[c*ld + r] = tile[r][c] for r < rvalid,
+// c < cvalid. lds needs TB*LDT floats; ends with a barrier.
+__device__ inline void quad_store_t(const Quad& q, float* dst, int64_t ld, int rvalid, int cvalid,
+                                    float* lds) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 #pragma unroll
@@ -138,7 +240,26 @@ __device__ inline void quad_to_lds(const Quad& q, float* lds) {
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int e = 0; e < 16; ++e)
-        lds[quad_row(wm, a, e, lane) * LDT + quad_col(wn, b, lane)] = q.c[a][b][e];
+        lds[quad_col(wn, b, lane) * LDT + quad_row(wm, a, e, lane)] = q.c[a][b][e];
+  __syncthreads();
+  for (int e = threadIdx.x; e < TB * TB; e += 256) {
+    const int c = e / TB, r = e % TB;  // output row c, column r: contiguous in r
+    if (r < rvalid && c < cvalid) dst[int64_t(c) * ld + r] = lds[c * LDT + r];
+  }
+  __syncthreads();
+}
+
+// Tile -> LDS [TB][pitch] (rows r, columns c), all 128x128 entries.
+__device__ inline void quad_to_lds(const Quad& q, float* lds, int pitch) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        lds[quad_row(wm, a, e, lane) * pitch + quad_col(wn, b, lane)] = q.c[a][b][e];
 }
 
 }  // namespace kfac
