@@ -37,7 +37,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--batch", type=int, default=32)
+    ap.add_argument("--batch", type=int, default=None, help="default 32 (128 for --workload stale)")
+    ap.add_argument("--workload", choices=["resnet50", "stale"], default="resnet50",
+                    help="resnet50: one full K-FAC step per step (batch 32); stale: refresh "
+                         "every 10 steps with EMA 0.95, preconditioning only otherwise (batch 128)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true",
                     help="time the steps without per-kernel events (roofline then null)")
@@ -130,8 +133,9 @@ def cpu_baseline(layers, bns, budget_s=25.0):
 # GPU step
 # ---------------------------------------------------------------------------
 
-def make_inputs(layers, bns, device, seed=3):
+def make_inputs(layers, bns, device, seed=3, grad_dtype=None, gout_std=1.0):
     import torch
+    grad_dtype = grad_dtype or torch.float32
     g = torch.Generator(device=device)
     g.manual_seed(seed)
 
@@ -140,11 +144,63 @@ def make_inputs(layers, bns, device, seed=3):
         return x.to(dtype)
 
     act = [normal(l.act_shape, 1.0, torch.float16).relu_() for l in layers]
-    gout = [normal(l.gout_shape, 1.0, torch.float16) for l in layers]
-    grads = [normal((l.d_g, l.d_a), 0.1, torch.float32) for l in layers]
+    gout = [normal(l.gout_shape, gout_std, torch.float16) for l in layers]
+    grads = [normal((l.d_g, l.d_a), 0.1, grad_dtype) for l in layers]
     xhat = [normal(b.shape, 1.0, torch.float16) for b in bns]
-    bgout = [normal(b.shape, 1.0, torch.float16) for b in bns]
+    bgout = [normal(b.shape, gout_std, torch.float16) for b in bns]
     return act, gout, grads, xhat, bgout
+
+
+def run_stale(args):
+    """Stale curvature at batch 128: every 10th step refreshes the factors (EMA 0.95,
+    the first refresh overwrites) and the inverses; every step preconditions one of
+    ten fp16 N(0,1e-2) gradient sets. Two activation/gradient sets alternate across
+    refreshes. Reports amortised steps/s over `steps` steps."""
+    import torch
+    import fac_second_order_amd as kfac
+    dev = torch.device("cuda:0")
+    batch = args.batch or 128
+    layers = synth.conv_layers(batch)
+    bns = synth.bn_layers(batch)
+    sets = [make_inputs(layers, bns, dev, seed=50 + s, grad_dtype=torch.float16, gout_std=0.1)
+            for s in range(2)]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(60)
+    grads = [[(torch.randn((l.d_g, l.d_a), generator=gen, device=dev) * 0.1).half() for l in layers]
+             for _ in range(10)]
+    st = kfac.KfacStep(layers, bns, dev)
+    nref = [0]
+
+    def step(t):
+        refresh = t % 10 == 0
+        s = nref[0] % 2 if refresh else (nref[0] - 1) % 2
+        act, gout, _, xhat, bgout = sets[s]
+        decay = 0.0 if (refresh and nref[0] == 0) else 0.95
+        st.step(act, gout, grads[t % 10], xhat, bgout, ema_decay=decay, refresh=refresh)
+        if refresh:
+            nref[0] += 1
+
+    steps = args.steps if args.steps % 10 == 0 else 100   # whole refresh cycles only
+    for t in range(10):          # one warm-up cycle (refresh + 9 stale steps)
+        step(t)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(steps):
+        step(t)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    if int(st.info.abs().sum()) != 0:
+        raise RuntimeError("Cholesky breakdown on a damped factor")
+    out = {
+        "metric": "K-FAC amortised steps/sec (ResNet-50 shapes, batch 128, refresh every 10, EMA 0.95, 1 GPU)",
+        "value": round(steps / elapsed, 3), "unit": "steps/s", "n_gpus": 1, "steps": steps, "warmup": 10,
+        "ms_per_step": round(1e3 * elapsed / steps, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "resnet50_kfac_stale_schedule", "batch_per_gpu": batch, "refresh_every": 10,
+                   "ema_decay": 0.95, "grad_dtype": "f16"},
+        "roofline": None, "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
 
 
 def main():
@@ -158,6 +214,10 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.workload == "stale":
+        run_stale(args)
+        return
+    args.batch = args.batch or 32
     layers = synth.conv_layers(args.batch)
     bns = synth.bn_layers(args.batch)
     w = work(layers, bns)

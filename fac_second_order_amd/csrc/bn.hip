@@ -19,7 +19,7 @@ struct BnDesc {
   const void* gout;
   float* fisher;
   float* precond;
-  float2* partial;  // [n][nchunk][c] (sum g*x, sum g)
+  v2f* partial;     // [n][nchunk][c] (sum g*x, sum g)
   int32_t n, hw, c;
   int32_t vl;       // vector lanes per row segment (<= 256)
   int32_t rowpar;   // rows processed side by side (256 / vl)
@@ -43,13 +43,13 @@ struct Vec16<float> {
 template <class T, int EV>
 __device__ inline void load_vec(const T* p, float* out) {
   if constexpr (EV == 1) {
-    out[0] = static_cast<float>(p[0]);
+    out[0] = static_cast<float>(gp(p)[0]);
   } else if constexpr (sizeof(T) == 2) {
-    v8h v = *reinterpret_cast<const v8h*>(p);
+    v8h v = *reinterpret_cast<const KG v8h*>(gp(p));
 #pragma unroll
     for (int q = 0; q < 8; ++q) out[q] = static_cast<float>(v[q]);
   } else {
-    v4f v = *reinterpret_cast<const v4f*>(p);
+    v4f v = *reinterpret_cast<const KG v4f*>(gp(p));
 #pragma unroll
     for (int q = 0; q < 4; ++q) out[q] = v[q];
   }
@@ -101,7 +101,7 @@ __device__ void bn_partial_body(const BnDesc& d, int item) {
       a += v.x;
       b += v.y;
     }
-    d.partial[(int64_t(s) * d.nchunk + chunk) * d.c + c] = make_float2(a, b);
+    gp(d.partial)[(int64_t(s) * d.nchunk + chunk) * d.c + c] = v2f{a, b};
   }
 }
 
@@ -133,7 +133,7 @@ __global__ void __launch_bounds__(256) bn_finish_kernel(const BnDesc* __restrict
   for (int s = 0; s < d.n; ++s) {
     float a = 0.f, b = 0.f;
     for (int k = 0; k < d.nchunk; ++k) {
-      float2 v = d.partial[(int64_t(s) * d.nchunk + k) * d.c + c];
+      const v2f v = gp(d.partial)[(int64_t(s) * d.nchunk + k) * d.c + c];
       a += v.x;
       b += v.y;
     }
@@ -148,13 +148,13 @@ __global__ void __launch_bounds__(256) bn_finish_kernel(const BnDesc* __restrict
   gg *= inv_n;
   gb *= inv_n;
   if (decay != 0.f) {
-    fg = decay * d.fisher[c] + (1.f - decay) * fg;
-    fb = decay * d.fisher[d.c + c] + (1.f - decay) * fb;
+    fg = decay * gp(d.fisher)[c] + (1.f - decay) * fg;
+    fb = decay * gp(d.fisher)[d.c + c] + (1.f - decay) * fb;
   }
-  d.fisher[c] = fg;
-  d.fisher[d.c + c] = fb;
-  d.precond[c] = gg / (fg + shift);
-  d.precond[d.c + c] = gb / (fb + shift);
+  gp(d.fisher)[c] = fg;
+  gp(d.fisher)[d.c + c] = fb;
+  gp(d.precond)[c] = gg / (fg + shift);
+  gp(d.precond)[d.c + c] = gb / (fb + shift);
 }
 
 // Plans one layer: 16-byte vectors along channels when `vec`, else scalar loads.
@@ -197,7 +197,7 @@ static size_t bn_ws_bound(const kfac_bn* L, int count) {
     part += m;
   }
   return align256(sizeof(BnDesc) * count) + 2 * align256(sizeof(int32_t) * count) +
-         align256(sizeof(float2) * part);
+         align256(sizeof(v2f) * part);
 }
 
 }  // namespace kfac
@@ -258,14 +258,14 @@ extern "C" kfac_status kfac_bn_diag(const kfac_bn* layers, int32_t count, kfac_d
   st = check_device();
   if (st) return st;
   const size_t need = align256(sizeof(BnDesc) * count) + 2 * align256(sizeof(int32_t) * count) +
-                      align256(sizeof(float2) * part);
+                      align256(sizeof(v2f) * part);
   st = check_workspace(workspace, ws_bytes, need);
   if (st) return st;
   Carver cv(workspace);
   BnDesc* d_desc = cv.take<BnDesc>(count);
   int32_t* d_begin = cv.take<int32_t>(count);
   int32_t* d_cbegin = cv.take<int32_t>(count);
-  float2* partial = cv.take<float2>(part);
+  v2f* partial = cv.take<v2f>(part);
   size_t off = 0;
   for (int l = 0; l < count; ++l) {
     BnDesc& d = desc[l];

@@ -13,6 +13,7 @@ namespace kfac {
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 
@@ -91,6 +92,20 @@ struct TimerScope {
     hipError_t e_ = hipGetLastError();                            \
     if (e_ != hipSuccess) return ::kfac::hip_fail(e_, what);      \
   } while (0)
+
+// ---- global address space -----------------------------------------------------
+// Pointers read from descriptor tables are generic; casting them to the global
+// address space makes the compiler emit global_* instead of flat_* accesses, whose
+// completion is tracked apart from LDS (flat loads would also hold LDS waits).
+#define KG __attribute__((address_space(1)))
+template <class T>
+__device__ __forceinline__ const KG T* gp(const T* p) {
+  return (const KG T*)(p);
+}
+template <class T>
+__device__ __forceinline__ KG T* gp(T* p) {
+  return (KG T*)(p);
+}
 
 // ---- small device helpers --------------------------------------------------
 // Index of the problem owning work item `w`: largest p with begin[p] <= w.

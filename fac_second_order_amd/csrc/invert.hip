@@ -55,127 +55,174 @@ __global__ void __launch_bounds__(256) inv_prep_kernel(const InvDesc* __restrict
   for (int r = threadIdx.x >> 6; r < FT; r += 4) {
     const int64_t i = int64_t(ti) * FT + r;
     if (i < n && j < n && i <= j) {
-      float v = d.mat[i * n + j];
+      float v = gp(d.mat)[i * n + j];
       if (i == j) v += d.shift;
-      d.S[i * n + j] = v;
+      gp(d.S)[i * n + j] = v;
     }
   }
-  if (ti == 0 && tj == 0 && threadIdx.x == 0) *d.info = 0;
+  if (ti == 0 && tj == 0 && threadIdx.x == 0) *gp(d.info) = 0;
 }
 
-// Cholesky of the pivot block P (bk x bk, upper triangle in LDS tile L with pitch
-// LDT) and E = U^-T, by the PT threads of a block. Thread (wave w, lane l) holds rows
-// NW*r + w (r = 0..RPW-1) and columns 2l, 2l+1 of a combined matrix whose strict
-// upper triangle becomes U, strict lower triangle E and diagonal 1/U_ii. At column kk
-// the scaled pivot row r = M_kk^-1/2 * M_k. (with r_kk = M_kk^-1/2) is broadcast
-// through LDS (also in a wave-interleaved copy, so each wave fetches its multipliers
-// with 16-byte reads); every row i > kk then loses u_i * r with u_i = r_i, after its
-// entry in column kk is cleared. Rows <= kk are final and skipped. Padding
-// rows/columns (>= bk) hold the identity and stay unchanged. Writes E and U^-1 = E^T
+// Cholesky of the pivot block P (bk x bk, upper triangle in S) and E = U^-T, by the
+// PT threads of one block. Wave w holds rows RPW*w .. RPW*w+RPW-1 and lane l
+// columns 2l, 2l+1 of a combined matrix whose strict upper triangle becomes U,
+// strict lower triangle E and diagonal 1/U_ii. Scalar step kk: the pivot row is
+// scaled, r = M_kk^-1/2 * M_k. with r_kk = M_kk^-1/2; every row i > kk clears its
+// entry in column kk and loses u_i * r with u_i = r_i; rows <= kk are final.
+// Columns are taken GP at a time: the wave that owns rows c0..c0+GP-1 runs the GP
+// steps on them in registers (broadcasts by readlane, no barrier), publishes the GP
+// scaled rows through LDS, and after one barrier every later row applies the GP
+// updates. Waves whose rows are all final skip the update. Padding rows/columns
+// (>= bk) hold the identity and stay unchanged. Writes E and U^-1 = E^T
 // (row-major, TB x TB) to the workspace, U into chol when asked, and the 1-based
 // failing column into info.
 constexpr int PT = 512;           // threads of the pivot kernel
 constexpr int NW = PT / 64;       // waves
-constexpr int RPW = TB / NW;      // rows per wave
+constexpr int RPW = TB / NW;      // rows per wave (contiguous)
+constexpr int GP = 4;             // pivot columns per barrier
+
+__device__ __forceinline__ float lane_bcast(float v, int src_lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src_lane));
+}
+
+// The owner wave's GP steps on its rows QQ*GP .. QQ*GP+GP-1 (columns c0 ..).
+template <int QQ>
+__device__ __forceinline__ void pivot_group(float2 (&M)[RPW], int c0, int gcnt, int lane,
+                                            float (*prow)[TB], float* dval, float* diagU) {
+#pragma unroll
+  for (int g = 0; g < GP; ++g) {
+    if (g < gcnt) {
+      const int a = c0 + g, al = a >> 1;
+      const bool aodd = a & 1;
+      const float2 m = M[QQ * GP + g];
+      const float piv = lane_bcast(aodd ? m.y : m.x, al);
+      const float rs = rsqrtf(piv);
+      float2 sc = make_float2(m.x * rs, m.y * rs);
+      if (lane == al) {
+        if (aodd) sc.y = rs; else sc.x = rs;
+      }
+      M[QQ * GP + g] = sc;
+      reinterpret_cast<float2*>(prow[g])[lane] = sc;
+      if (lane == 0) {
+        dval[g] = piv;
+        diagU[a] = piv * rs;
+      }
+#pragma unroll
+      for (int g2 = g + 1; g2 < GP; ++g2) {
+        if (g2 < gcnt) {
+          const int b = c0 + g2;
+          const float u = lane_bcast((b & 1) ? sc.y : sc.x, b >> 1);
+          float2 mb = M[QQ * GP + g2];
+          if (lane == al) {
+            if (aodd) mb.y = 0.f; else mb.x = 0.f;
+          }
+          mb.x = fmaf(-u, sc.x, mb.x);
+          mb.y = fmaf(-u, sc.y, mb.y);
+          M[QQ * GP + g2] = mb;
+        }
+      }
+    }
+  }
+}
 
 __global__ void __launch_bounds__(PT) inv_pivot_kernel(const InvDesc* __restrict__ desc, int k) {
   const InvDesc& d = desc[blockIdx.x];
   const int n = d.n, k0 = k * TB, bk = min(TB, n - k0);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  __shared__ __attribute__((aligned(16))) float prow[2][TB];    // scaled pivot row, by column
-  __shared__ __attribute__((aligned(16))) float prowi[2][TB];   // column i at (i%NW)*RPW + i/NW
-  __shared__ float dval[2];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, scalar
+  __shared__ __attribute__((aligned(16))) float prow[2][GP][TB];  // scaled pivot rows
+  __shared__ __attribute__((aligned(16))) float dval[2][GP];
   __shared__ float diagU[TB];
   __shared__ float L[TB * LDT];
 
   float2 M[RPW];
 #pragma unroll
   for (int r = 0; r < RPW; ++r) {
-    const int i = NW * r + w;
+    const int i = RPW * w + r;
     const int j0 = 2 * lane, j1 = 2 * lane + 1;
     float a = (i == j0) ? 1.f : 0.f, b = (i == j1) ? 1.f : 0.f;
-    if (i < bk && j0 < bk) a = d.S[int64_t(k0 + min(i, j0)) * n + k0 + max(i, j0)];
-    if (i < bk && j1 < bk) b = d.S[int64_t(k0 + min(i, j1)) * n + k0 + max(i, j1)];
+    if (i < bk && j0 < bk) a = gp(d.S)[int64_t(k0 + min(i, j0)) * n + k0 + max(i, j0)];
+    if (i < bk && j1 < bk) b = gp(d.S)[int64_t(k0 + min(i, j1)) * n + k0 + max(i, j1)];
     M[r] = make_float2(a, b);
   }
   int failed = 0;
-  for (int kk = 0; kk < bk; ++kk) {
-    const int buf = kk & 1;
-    const int kl = kk >> 1;  // lane holding column kk
-    if (w == kk % NW) {
-#pragma unroll
-      for (int r = 0; r < RPW; ++r) {
-        if (NW * r + w == kk) {  // uniform: this wave's row kk
-          const float2 m = M[r];
-          const float mine = (kk & 1) ? m.y : m.x;
-          const float piv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine), kl));
-          const float sq = sqrtf(piv);
-          const float rs = 1.0f / sq;
-          float2 sc = make_float2(m.x * rs, m.y * rs);
-          if (lane == kl) {
-            if (kk & 1) sc.y = rs; else sc.x = rs;
-          }
-          M[r] = sc;
-          reinterpret_cast<float2*>(prow[buf])[lane] = sc;
-          const int i0 = 2 * lane, i1 = 2 * lane + 1;
-          prowi[buf][(i0 % NW) * RPW + i0 / NW] = sc.x;
-          prowi[buf][(i1 % NW) * RPW + i1 / NW] = sc.y;
-          if (lane == 0) {
-            dval[buf] = piv;
-            diagU[kk] = sq;
-          }
-        }
-      }
+  for (int c0 = 0; c0 < bk; c0 += GP) {
+    const int buf = (c0 / GP) & 1;
+    const int gcnt = min(GP, bk - c0);
+    if (w == c0 / RPW) {
+      const int q = (c0 % RPW) / GP;
+      if (q == 0) pivot_group<0>(M, c0, gcnt, lane, prow[buf], dval[buf], diagU);
+      else if (q == 1) pivot_group<1>(M, c0, gcnt, lane, prow[buf], dval[buf], diagU);
+      else if (q == 2) pivot_group<2>(M, c0, gcnt, lane, prow[buf], dval[buf], diagU);
+      else pivot_group<3>(M, c0, gcnt, lane, prow[buf], dval[buf], diagU);
     }
     __syncthreads();
-    const float piv = dval[buf];
-    if (!(piv > 0.f) || !isfinite(piv)) {  // same value in every thread: uniform exit
-      failed = kk + 1;
-      break;
-    }
-    const float2 rj = reinterpret_cast<const float2*>(prow[buf])[lane];
-    float u[RPW];  // multipliers u_i = r_i of this wave's rows
+    {
+      const float4 pv = *reinterpret_cast<const float4*>(dval[buf]);
+      const float pp[4] = {pv.x, pv.y, pv.z, pv.w};
 #pragma unroll
-    for (int q = 0; q < RPW / 4; ++q) {
-      const float4 x = reinterpret_cast<const float4*>(prowi[buf] + w * RPW)[q];
-      u[4 * q] = x.x; u[4 * q + 1] = x.y; u[4 * q + 2] = x.z; u[4 * q + 3] = x.w;
+      for (int g = GP - 1; g >= 0; --g)  // keep the first bad column
+        if (g < gcnt && (!(pp[g] > 0.f) || !isfinite(pp[g]))) failed = c0 + g + 1;
     }
-    const bool mycol = lane == kl;
-    const bool odd = kk & 1;
+    if (failed) break;  // same decision in every thread
+    const int last = c0 + gcnt - 1;  // rows > last take the GP updates
+    if (RPW * w + RPW - 1 > last) {
+      float2 rjs[GP];
+      float us[GP][RPW];  // all multipliers first: one LDS round trip
 #pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-      if (NW * r + w > kk) {  // uniform per wave
-        float2 m = M[r];
-        if (mycol) {
-          if (odd) m.y = 0.f; else m.x = 0.f;
+      for (int g = 0; g < GP; ++g) {
+        rjs[g] = reinterpret_cast<const float2*>(prow[buf][g])[lane];
+#pragma unroll
+        for (int q = 0; q < RPW / 4; ++q) {
+          const float4 x = reinterpret_cast<const float4*>(prow[buf][g] + RPW * w)[q];
+          us[g][4 * q] = x.x; us[g][4 * q + 1] = x.y; us[g][4 * q + 2] = x.z; us[g][4 * q + 3] = x.w;
         }
-        m.x = fmaf(-u[r], rj.x, m.x);
-        m.y = fmaf(-u[r], rj.y, m.y);
-        M[r] = m;
+      }
+#pragma unroll
+      for (int g = 0; g < GP; ++g) {
+        if (g < gcnt) {
+          const int a = c0 + g, al = a >> 1;
+          const bool aodd = a & 1;
+          const float2 rj = rjs[g];
+          const float* u = us[g];
+          const bool mycol = lane == al;
+#pragma unroll
+          for (int r = 0; r < RPW; ++r) {
+            if (RPW * w + r > last) {
+              float2 m = M[r];
+              if (mycol) {
+                if (aodd) m.y = 0.f; else m.x = 0.f;
+              }
+              m.x = fmaf(-u[r], rj.x, m.x);
+              m.y = fmaf(-u[r], rj.y, m.y);
+              M[r] = m;
+            }
+          }
+        }
       }
     }
   }
   // E (strict lower + diagonal) into L, then coalesced writes of E and E^T
 #pragma unroll
   for (int r = 0; r < RPW; ++r) {
-    const int i = NW * r + w;
+    const int i = RPW * w + r;
     const float2 m = M[r];
     L[i * LDT + 2 * lane] = (2 * lane <= i) ? m.x : 0.f;
     L[i * LDT + 2 * lane + 1] = (2 * lane + 1 <= i) ? m.y : 0.f;
     if (d.chol) {
-      if (i < 2 * lane && 2 * lane < bk) d.chol[int64_t(k0 + i) * n + k0 + 2 * lane] = m.x;
-      if (i < 2 * lane + 1 && 2 * lane + 1 < bk) d.chol[int64_t(k0 + i) * n + k0 + 2 * lane + 1] = m.y;
+      if (i < 2 * lane && 2 * lane < bk) gp(d.chol)[int64_t(k0 + i) * n + k0 + 2 * lane] = m.x;
+      if (i < 2 * lane + 1 && 2 * lane + 1 < bk) gp(d.chol)[int64_t(k0 + i) * n + k0 + 2 * lane + 1] = m.y;
     }
   }
   __syncthreads();
   for (int e = tid; e < TB * TB; e += PT) {
     const int i = e / TB, j = e % TB;
-    d.E[e] = L[i * LDT + j];
-    d.Ui[e] = L[j * LDT + i];
+    gp(d.E)[e] = L[i * LDT + j];
+    gp(d.Ui)[e] = L[j * LDT + i];
   }
   if (d.chol)
-    for (int i = tid; i < bk; i += PT) d.chol[int64_t(k0 + i) * n + k0 + i] = diagU[i];
-  if (failed && tid == 0 && *d.info == 0) *d.info = k0 + failed;
+    for (int i = tid; i < bk; i += PT) gp(d.chol)[int64_t(k0 + i) * n + k0 + i] = diagU[i];
+  if (failed && tid == 0 && *gp(d.info) == 0) *gp(d.info) = k0 + failed;
 }
 
 // Panel of step k: for column block j != k, Y_j = E V_j and W_j = E^T Y_j, with W_j
@@ -248,15 +295,15 @@ __global__ void __launch_bounds__(256) inv_finish_kernel(const InvDesc* __restri
     const int64_t i = i0 + r, j = j0 + c;
     float v = 0.f;
     if (i < n && j < n && i <= j) {
-      v = -d.S[i * n + j];
-      d.S[i * n + j] = v;
+      v = -gp(d.S)[i * n + j];
+      gp(d.S)[i * n + j] = v;
     }
     s[r][c] = v;
   }
   __syncthreads();
   for (int r = threadIdx.x >> 6; r < FT; r += 4) {
     const int64_t j = j0 + r, i = i0 + c;
-    if (i < n && j < n && i < j) d.S[j * n + i] = s[c][r];
+    if (i < n && j < n && i < j) gp(d.S)[j * n + i] = s[c][r];
   }
 }
 

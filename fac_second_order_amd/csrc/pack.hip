@@ -30,7 +30,7 @@ __global__ void __launch_bounds__(256) pack_kernel(const PackDesc* __restrict__ 
   const int64_t j = int64_t(tj) * PT + c;
   for (int r = threadIdx.x >> 6; r < PT; r += 4) {
     const int64_t i = int64_t(ti) * PT + r;
-    if (i < n && j < n && i <= j) d.packed[packed_off(i, j, n)] = d.full[i * n + j];
+    if (i < n && j < n && i <= j) gp(d.packed)[packed_off(i, j, n)] = gp(d.full)[i * n + j];
   }
 }
 
@@ -48,8 +48,8 @@ __global__ void __launch_bounds__(256) unpack_kernel(const PackDesc* __restrict_
     const int64_t i = i0 + r, j = j0 + c;
     float v = 0.f;
     if (i < n && j < n && i <= j) {
-      v = d.packed[packed_off(i, j, n)];
-      d.full[i * n + j] = v;
+      v = gp(d.packed)[packed_off(i, j, n)];
+      gp(d.full)[i * n + j] = v;
     }
     s[r][c] = v;
   }
@@ -57,7 +57,7 @@ __global__ void __launch_bounds__(256) unpack_kernel(const PackDesc* __restrict_
   // mirror: full[j][i] = full[i][j] for i < j; this thread writes row j0+r, column i0+c
   for (int r = threadIdx.x >> 6; r < PT; r += 4) {
     const int64_t j = j0 + r, i = i0 + c;
-    if (i < n && j < n && i < j) d.full[j * n + i] = s[c][r];
+    if (i < n && j < n && i < j) gp(d.full)[j * n + i] = s[c][r];
   }
 }
 

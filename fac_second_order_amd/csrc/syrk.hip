@@ -56,7 +56,7 @@ struct SyrkDesc {
 template <class T>
 __device__ inline float x_elem(const SyrkDesc& d, int row, int c) {
   if (c >= d.d_core) return 0.f;
-  const T* src = static_cast<const T*>(d.src);
+  const KG T* src = gp(static_cast<const T*>(d.src));
   if (d.mode == 0) return static_cast<float>(src[int64_t(row) * d.ld + c]);
   const int hw = d.Ho * d.Wo;
   const int n = row / hw;
@@ -142,13 +142,13 @@ __device__ inline void fill_coltab(const SyrkDesc& d, int c0, ColTab& ct) {
 // 8 consecutive columns of the chunk row rr as fp16 (zeros outside the image, past
 // the last row or past d_core).
 __device__ inline v8h gather8(const SyrkDesc& d, const RowTab& t, int rr, const ColTab& ct) {
-  const _Float16* src = static_cast<const _Float16*>(d.src);
+  const KG _Float16* src = gp(static_cast<const _Float16*>(d.src));
   const int ih = t.ih[rr], iw = t.iw[rr];
   const int64_t off = t.off[rr];
   v8h v;
   if (d.vec) {  // the 8 columns share one tap: one 16-byte load
     const bool ok = unsigned(ih + ct.ki[0]) < unsigned(d.H) && unsigned(iw + ct.kj[0]) < unsigned(d.W);
-    if (ok) return *reinterpret_cast<const v8h*>(src + off + ct.coff[0]);
+    if (ok) return *reinterpret_cast<const KG v8h*>(src + off + ct.coff[0]);
 #pragma unroll
     for (int q = 0; q < 8; ++q) v[q] = static_cast<_Float16>(0.f);
     return v;
@@ -170,7 +170,7 @@ __device__ inline int xcd_virtual(int b, int grid, int total) {
 }
 
 __device__ inline float blend(float v, const float* out, int64_t o, float decay) {
-  return decay != 0.f ? decay * out[o] + (1.f - decay) * v : v;
+  return decay != 0.f ? decay * gp(out)[o] + (1.f - decay) * v : v;
 }
 
 // Writes the bias column entries (column sums) and the bias corner of a direct tile.
@@ -181,12 +181,12 @@ __device__ inline void write_bias_direct(const SyrkDesc& d, int ti, int t, float
     const int i = ti * ST + tid;
     if (i < d.d_core) {
       const int64_t o = packed_off(i, d.d_core, d.d);
-      d.out[o] = blend(colsum * d.inv_r, d.out, o, decay);
+      gp(d.out)[o] = blend(colsum * d.inv_r, d.out, o, decay);
     }
   }
   if (t == 0 && tid == 0) {
     const int64_t o = packed_off(d.d_core, d.d_core, d.d);
-    d.out[o] = blend(d.r_f * d.inv_r, d.out, o, decay);
+    gp(d.out)[o] = blend(d.r_f * d.inv_r, d.out, o, decay);
   }
 }
 
@@ -268,7 +268,7 @@ __global__ void __launch_bounds__(256) syrk_f16_kernel(const SyrkDesc* __restric
         for (int q = 0; q < 8; ++q) colsum += static_cast<float>(cv[q]);
       }
     }
-    if (!skip) {
+    {  // every wave runs its MFMAs (uniform control flow keeps acc in place)
 #pragma unroll
       for (int ks = 0; ks < KC / 16; ++ks) {
         const int ko = ks * 16 + (lane >> 5) * 8;
@@ -296,7 +296,7 @@ __global__ void __launch_bounds__(256) syrk_f16_kernel(const SyrkDesc* __restric
             const int j = tj * ST + wn * 64 + b * 32 + (lane & 31);
             if (i <= j && j < d.d_core) {
               const int64_t o = packed_off(i, j, d.d);
-              d.out[o] = blend(acc[a][b][e] * d.inv_r, d.out, o, decay);
+              gp(d.out)[o] = blend(acc[a][b][e] * d.inv_r, d.out, o, decay);
             }
           }
     }
@@ -312,10 +312,10 @@ __global__ void __launch_bounds__(256) syrk_f16_kernel(const SyrkDesc* __restric
           for (int e = 0; e < 16; ++e) {
             const int r = wm * 64 + a * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
             const int cc = wn * 64 + b * 32 + (lane & 31);
-            P[r * ST + cc] = acc[a][b][e];
+            gp(P)[r * ST + cc] = acc[a][b][e];
           }
     }
-    if (want_col) d.pcol[(int64_t(s) * d.nb + ti) * ST + tid] = colsum;
+    if (want_col) gp(d.pcol)[(int64_t(s) * d.nb + ti) * ST + tid] = colsum;
   }
 }
 
@@ -385,7 +385,7 @@ __global__ void __launch_bounds__(256) syrk_f32_kernel(const SyrkDesc* __restric
             const int j = tj * ST + wn * 64 + b * 32 + (lane & 31);
             if (i <= j && j < d.d_core) {
               const int64_t o = packed_off(i, j, d.d);
-              d.out[o] = blend(acc[a][b][e] * d.inv_r, d.out, o, decay);
+              gp(d.out)[o] = blend(acc[a][b][e] * d.inv_r, d.out, o, decay);
             }
           }
     }
@@ -398,10 +398,10 @@ __global__ void __launch_bounds__(256) syrk_f32_kernel(const SyrkDesc* __restric
           for (int e = 0; e < 16; ++e) {
             const int r = wm * 64 + a * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
             const int c = wn * 64 + b * 32 + (lane & 31);
-            P[r * ST + c] = acc[a][b][e];
+            gp(P)[r * ST + c] = acc[a][b][e];
           }
     }
-    if (want_col) d.pcol[(int64_t(s) * d.nb + ti) * ST + tid] = colsum;
+    if (want_col) gp(d.pcol)[(int64_t(s) * d.nb + ti) * ST + tid] = colsum;
   }
 }
 
@@ -426,7 +426,7 @@ __global__ void __launch_bounds__(256) syrk_reduce_kernel(const SyrkDesc* __rest
     const float* P = d.partial + int64_t(t) * ST * ST + e0;
     float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int s = 0; s < d.splits; ++s) {
-      const float4 x = *reinterpret_cast<const float4*>(P + s * tstride);
+      const v4f x = *reinterpret_cast<const KG v4f*>(gp(P) + s * tstride);
       sum.x += x.x; sum.y += x.y; sum.z += x.z; sum.w += x.w;
     }
     const float v4[4] = {sum.x, sum.y, sum.z, sum.w};
@@ -435,7 +435,7 @@ __global__ void __launch_bounds__(256) syrk_reduce_kernel(const SyrkDesc* __rest
       const int j = j0 + u;
       if (j >= i && j < d.d_core) {
         const int64_t o = packed_off(i, j, d.d);
-        d.out[o] = blend(v4[u] * d.inv_r, d.out, o, decay);
+        gp(d.out)[o] = blend(v4[u] * d.inv_r, d.out, o, decay);
       }
     }
   }
@@ -443,14 +443,14 @@ __global__ void __launch_bounds__(256) syrk_reduce_kernel(const SyrkDesc* __rest
     const int ib = ti * ST + threadIdx.x;
     if (ib < d.d_core) {
       float sum = 0.f;
-      for (int s = 0; s < d.splits; ++s) sum += d.pcol[(int64_t(s) * d.nb + ti) * ST + threadIdx.x];
+      for (int s = 0; s < d.splits; ++s) sum += gp(d.pcol)[(int64_t(s) * d.nb + ti) * ST + threadIdx.x];
       const int64_t o = packed_off(ib, d.d_core, d.d);
-      d.out[o] = blend(sum * d.inv_r, d.out, o, decay);
+      gp(d.out)[o] = blend(sum * d.inv_r, d.out, o, decay);
     }
   }
   if (t == 0 && part == 0 && d.bias && threadIdx.x == 0) {
     const int64_t o = packed_off(d.d_core, d.d_core, d.d);
-    d.out[o] = blend(d.r_f * d.inv_r, d.out, o, decay);
+    gp(d.out)[o] = blend(d.r_f * d.inv_r, d.out, o, decay);
   }
 }
 

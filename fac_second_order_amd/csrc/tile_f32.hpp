@@ -73,20 +73,20 @@ __device__ inline void op_fetch(const Operand& o, int k0, float4 (&r)[4]) {
     float v[4] = {0.f, 0.f, 0.f, 0.f};
     if (k < o.kv) {
       if (o.vec4 && m + 3 < o.mv) {
-        const float4 x = *reinterpret_cast<const float4*>(static_cast<const float*>(o.src) + k * o.ld + m);
+        const v4f x = *reinterpret_cast<const KG v4f*>(gp(static_cast<const float*>(o.src)) + k * o.ld + m);
         v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
       } else if (o.trans) {
-        const float* s = static_cast<const float*>(o.src);
+        const KG float* s = gp(static_cast<const float*>(o.src));
 #pragma unroll
         for (int u = 0; u < 4; ++u)
           if (m + u < o.mv) v[u] = s[int64_t(m + u) * o.ld + k];
       } else if (o.f16) {
-        const _Float16* s = static_cast<const _Float16*>(o.src) + k * o.ld;
+        const KG _Float16* s = gp(static_cast<const _Float16*>(o.src)) + k * o.ld;
 #pragma unroll
         for (int u = 0; u < 4; ++u)
           if (m + u < o.mv) v[u] = static_cast<float>(s[m + u]);
       } else {
-        const float* s = static_cast<const float*>(o.src) + k * o.ld;
+        const KG float* s = gp(static_cast<const float*>(o.src)) + k * o.ld;
 #pragma unroll
         for (int u = 0; u < 4; ++u)
           if (m + u < o.mv) v[u] = s[m + u];
@@ -179,7 +179,7 @@ __device__ inline void quad_load(Quad& q, const float* src, int64_t ld, int rval
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int r = quad_row(wm, a, e, lane), c = quad_col(wn, b, lane);
-        q.c[a][b][e] = (r < rvalid && c < cvalid) ? src[int64_t(r) * ld + c] : 0.f;
+        q.c[a][b][e] = (r < rvalid && c < cvalid) ? gp(src)[int64_t(r) * ld + c] : 0.f;
       }
 }
 
@@ -194,7 +194,7 @@ __device__ inline void quad_add_global(Quad& q, const float* src, int64_t ld, in
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int r = quad_row(wm, a, e, lane), c = quad_col(wn, b, lane);
-        if (r < rvalid && c < cvalid) q.c[a][b][e] += src[int64_t(r) * ld + c];
+        if (r < rvalid && c < cvalid) q.c[a][b][e] += gp(src)[int64_t(r) * ld + c];
       }
 }
 
@@ -209,7 +209,7 @@ __device__ inline void quad_store(const Quad& q, float* dst, int64_t ld, int rva
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int r = quad_row(wm, a, e, lane), c = quad_col(wn, b, lane);
-        if (r < rvalid && c < cvalid) dst[int64_t(r) * ld + c] = q.c[a][b][e] * scale;
+        if (r < rvalid && c < cvalid) gp(dst)[int64_t(r) * ld + c] = q.c[a][b][e] * scale;
       }
 }
 
@@ -224,7 +224,7 @@ __device__ inline void quad_store_upper(const Quad& q, float* dst, int64_t ld, i
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int r = quad_row(wm, a, e, lane), c = quad_col(wn, b, lane);
-        if (r <= c && c < nvalid) dst[int64_t(r) * ld + c] = q.c[a][b][e];
+        if (r <= c && c < nvalid) gp(dst)[int64_t(r) * ld + c] = q.c[a][b][e];
       }
 }
 
@@ -244,7 +244,7 @@ __device__ inline void quad_store_t(const Quad& q, float* dst, int64_t ld, int r
   __syncthreads();
   for (int e = threadIdx.x; e < TB * TB; e += 256) {
     const int c = e / TB, r = e % TB;  // output row c, column r: contiguous in r
-    if (r < rvalid && c < cvalid) dst[int64_t(c) * ld + r] = lds[c * LDT + r];
+    if (r < rvalid && c < cvalid) gp(dst)[int64_t(c) * ld + r] = lds[c * LDT + r];
   }
   __syncthreads();
 }
