@@ -31,6 +31,31 @@ PEAK_FP16_MFMA = 2516.6  # TFLOP/s, MI355X dense fp16 matrix
 PEAK_HBM = 8000.0        # GB/s
 TB = 128                 # block of the inverse
 
+# HBM bytes per launch of the dominant kernel, from two rocprofv3 --pmc passes
+# (FETCH_SIZE, then WRITE_SIZE), calibrated by a plain 1 GiB device copy (fetch x2.0,
+# write x1.0) and summarised in profiles/resnet50_step_hbm_counters.md. Reported only
+# while the kernel's source text still hashes to the value it was measured with.
+MEASURED_TRAFFIC = {"inv_update_kernel": (593484380, "af7706b9c328479c4d64b6506779c0f00abc5e05")}
+CSRC = os.path.join(ROOT, "fac_second_order_amd", "csrc")
+
+
+def kernel_source_sha(name):
+    import hashlib
+    if name != "inv_update_kernel":
+        return None
+    inv = open(os.path.join(CSRC, "invert.hip")).read()
+    body = inv[inv.index("// Update of step k:"):inv.index("// inv <- -S with both")]
+    text = body + open(os.path.join(CSRC, "tile_f32.hpp")).read() + \
+        open(os.path.join(CSRC, "common.hpp")).read()
+    return hashlib.sha1(text.encode()).hexdigest()
+
+
+def measured_traffic(name):
+    rec = MEASURED_TRAFFIC.get(name)
+    if rec is None or kernel_source_sha(name) != rec[1]:
+        return None
+    return rec[0]
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -268,7 +293,7 @@ def main():
             total_work, bound, peak = per_launch[name]
             achieved = total_work / (ms * 1e-3) / 1e12      # = per-launch work / average duration
             roofline = {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
-                        "frac": round(achieved / peak, 4), "traffic": None, "kernel": name,
+                        "frac": round(achieved / peak, 4), "traffic": measured_traffic(name), "kernel": name,
                         "launches": n, "avg_launch_us": round(1e3 * ms / n, 2),
                         "algorithmic_per_launch": total_work / n}
         elif name in ("bn_partial_kernel", "unpack_kernel"):
