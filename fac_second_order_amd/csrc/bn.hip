@@ -7,9 +7,9 @@
 // with 16-byte loads along the channel dimension (NHWC, channels contiguous). A work
 // item is (layer, sample, spatial chunk, channel block); it writes the chunk's
 // per-channel partial sums (sum g*x, sum g) to the workspace.
-// Stage 2 (bn_finish_kernel), one thread per channel, adds the chunks of each
-// sample in a fixed order (deterministic), squares the per-sample sums, averages
-// over samples, blends with the stored Fisher when asked and divides.
+// Stage 2 (bn_finish_kernel), 8 lanes per channel over the samples, adds the chunks
+// of each sample in a fixed order (deterministic), squares the per-sample sums,
+// averages over samples, blends with the stored Fisher when asked and divides.
 #include "common.hpp"
 
 namespace kfac {
@@ -120,27 +120,40 @@ __global__ void __launch_bounds__(256) bn_partial_kernel(const BnDesc* __restric
   }
 }
 
+// One block per 32 channels of a layer; 8 lanes per channel split the samples. Each
+// lane forms the per-sample sums s_n (chunks added in order) and accumulates s_n^2 and
+// s_n; the 8 lanes are then added in a fixed order, so the result is deterministic.
+constexpr int FIN_CH = 32, FIN_LANES = 8;
+
 __global__ void __launch_bounds__(256) bn_finish_kernel(const BnDesc* __restrict__ desc,
-                                                        const int32_t* __restrict__ cbegin,
-                                                        int count, int total, float decay,
-                                                        float shift) {
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= total) return;
-  const int p = find_problem(cbegin, count, t);
+                                                        const int32_t* __restrict__ gbegin,
+                                                        int count, float decay, float shift) {
+  const int p = find_problem(gbegin, count, blockIdx.x);
   const BnDesc d = desc[p];
-  const int c = t - cbegin[p];
+  const int c = (blockIdx.x - gbegin[p]) * FIN_CH + (threadIdx.x % FIN_CH);
+  const int q = threadIdx.x / FIN_CH;
   float fg = 0.f, fb = 0.f, gg = 0.f, gb = 0.f;
-  for (int s = 0; s < d.n; ++s) {
-    float a = 0.f, b = 0.f;
-    for (int k = 0; k < d.nchunk; ++k) {
-      const v2f v = gp(d.partial)[(int64_t(s) * d.nchunk + k) * d.c + c];
-      a += v.x;
-      b += v.y;
+  if (c < d.c) {
+    for (int s = q; s < d.n; s += FIN_LANES) {
+      float a = 0.f, b = 0.f;
+      for (int k = 0; k < d.nchunk; ++k) {
+        const v2f v = gp(d.partial)[(int64_t(s) * d.nchunk + k) * d.c + c];
+        a += v.x;
+        b += v.y;
+      }
+      fg = fmaf(a, a, fg);
+      fb = fmaf(b, b, fb);
+      gg += a;
+      gb += b;
     }
-    fg = fmaf(a, a, fg);
-    fb = fmaf(b, b, fb);
-    gg += a;
-    gb += b;
+  }
+  __shared__ float4 red[256];
+  red[threadIdx.x] = make_float4(fg, fb, gg, gb);
+  __syncthreads();
+  if (q != 0 || c >= d.c) return;
+  for (int l = 1; l < FIN_LANES; ++l) {
+    const float4 v = red[l * FIN_CH + threadIdx.x];
+    fg += v.x; fb += v.y; gg += v.z; gb += v.w;
   }
   const float inv_n = 1.0f / static_cast<float>(d.n);
   fg *= inv_n;
@@ -250,7 +263,7 @@ extern "C" kfac_status kfac_bn_diag(const kfac_bn* layers, int32_t count, kfac_d
     begin[l] = static_cast<int32_t>(items);
     items += int64_t(desc[l].n) * desc[l].nchunk * desc[l].cblocks;
     cbegin[l] = static_cast<int32_t>(channels);
-    channels += desc[l].c;
+    channels += (desc[l].c + FIN_CH - 1) / FIN_CH;  // finish blocks
     part += partial_count(desc[l]);
   }
   if (items >= (int64_t(1) << 31) || channels >= (int64_t(1) << 31))
@@ -286,9 +299,8 @@ extern "C" kfac_status kfac_bn_diag(const kfac_bn* layers, int32_t count, kfac_d
   KFAC_LAUNCH(K_BN_PARTIAL, bn_partial_kernel, dim3(static_cast<unsigned>(items)), dim3(256), 0, s,
               d_desc, d_begin, count, in_dtype == KFAC_F32 ? 1 : 0);
   KFAC_CHECK_LAUNCH("bn_partial_kernel");
-  const unsigned blocks = static_cast<unsigned>((channels + 255) / 256);
-  KFAC_LAUNCH(K_BN_FINISH, bn_finish_kernel, dim3(blocks), dim3(256), 0, s, d_desc, d_cbegin, count,
-              static_cast<int>(channels), ema_decay, shift);
+  KFAC_LAUNCH(K_BN_FINISH, bn_finish_kernel, dim3(static_cast<unsigned>(channels)), dim3(256), 0, s, d_desc,
+              d_cbegin, count, ema_decay, shift);
   KFAC_CHECK_LAUNCH("bn_finish_kernel");
   return KFAC_OK;
 }

@@ -50,6 +50,14 @@ __global__ void __launch_bounds__(256) inv_prep_kernel(const InvDesc* __restrict
   int ti, tj;
   upper_tile(blockIdx.x - begin[p], d.nb64, ti, tj);
   const int64_t n = d.n;
+  if (ti == 0 && tj == 0 && threadIdx.x == 0) *gp(d.info) = 0;
+  if (d.mat == d.S) {  // in place: only the diagonal changes
+    if (ti == tj && threadIdx.x < FT) {
+      const int64_t i = int64_t(ti) * FT + threadIdx.x;
+      if (i < n) gp(d.S)[i * n + i] += d.shift;
+    }
+    return;
+  }
   const int c = threadIdx.x & (FT - 1);
   const int64_t j = int64_t(tj) * FT + c;
   for (int r = threadIdx.x >> 6; r < FT; r += 4) {
@@ -60,7 +68,6 @@ __global__ void __launch_bounds__(256) inv_prep_kernel(const InvDesc* __restrict
       gp(d.S)[i * n + j] = v;
     }
   }
-  if (ti == 0 && tj == 0 && threadIdx.x == 0) *gp(d.info) = 0;
 }
 
 // Cholesky of the pivot block P (bk x bk, upper triangle in S) and E = U^-T, by the
