@@ -63,6 +63,7 @@ enum KernelId {
   K_INV_PIVOT,
   K_INV_PANEL,
   K_INV_UPDATE,
+  K_INV_ROWUPD,
   K_INV_FINISH,
   K_GEMM,
   K_BN_PARTIAL,
@@ -108,6 +109,18 @@ __device__ __forceinline__ KG T* gp(T* p) {
 }
 
 // ---- small device helpers --------------------------------------------------
+// Maps a hardware block id to a virtual work id so that XCD x (blocks b with
+// b % 8 == x, the order in which the dispatcher deals blocks to the 8 XCDs) runs the
+// contiguous range [x*per, (x+1)*per) and work items that share operands share that
+// XCD's L2. The grid is a multiple of 8; returns -1 for padding. Only for launches
+// whose work items cost about the same.
+__device__ inline int xcd_virtual(int b, int grid, int total) {
+  const int per = grid / 8;
+  const int v = (b % 8) * per + b / 8;
+  return v < total ? v : -1;
+}
+inline unsigned xcd_grid(int64_t total) { return static_cast<unsigned>((total + 7) / 8 * 8); }
+
 // Index of the problem owning work item `w`: largest p with begin[p] <= w.
 __device__ inline int find_problem(const int32_t* begin, int count, int w) {
   int lo = 0, hi = count - 1;

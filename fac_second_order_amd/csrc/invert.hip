@@ -7,18 +7,24 @@
 // pivoting) in which every block step is also applied to the rows and columns
 // that were already eliminated, so the inverse is assembled in the same sweep
 // (the symmetric Gauss-Jordan form of the Cholesky inverse). With S the working
-// matrix (upper triangle only) and k the pivot block, one step is
+// matrix (upper triangle in 128-blocks) and k the pivot block, one step is
 //   pivot:  U_kk = chol(S_kk) and E = U_kk^-T, by one workgroup with the block in
 //           registers: per column, one LDS broadcast of the scaled pivot row and one
 //           barrier; rows above the pivot are finished and skipped;
 //   panel:  for every column block j != k: V_j = S_kj, Y_j = E V_j (the Cholesky
 //           row panel U_kj when j > k) and W_j = E^T Y_j = P^-1 V_j, on MFMA, with
-//           S_kj = W_j (S_jk = W_j^T for j < k) written in place; the block j = k
-//           writes S_kk = -E^T E = -P^-1;
+//           S_kj = W_j (S_jk = W_j^T for j < k) written in place and Y_j kept in a
+//           row-major panel buffer; the block j = k writes S_kk = -E^T E = -P^-1;
 //   update: S_ij -= Y_i^T Y_j for all upper tiles i, j != k (fp32 MFMA).
-// After the last step S = -M^-1; the finish kernel negates it and writes both
-// triangles. All matrices of a call step together: they are ordered by block
-// count, so the ones still active at step k are a prefix of the list.
+// The update works on the square root Y of V^T P^-1 V, so its rounding errors scale
+// with |Y|^2 rather than with |V| |P^-1 V| (which an explicit P^-1 would give).
+// Steps are taken in pairs (k, k+1): after panel k only the tiles of block row
+// k+1 take step k's update (row update), then pivot and panel k+1 run, and one
+// update applies both steps, S_ij -= [Y_i; Y'_i]^T [Y_j; Y'_j], a rank-256 product
+// that reads and writes each tile once for two steps (tiles in block row k take
+// only step k+1's half). After the last step S = -M^-1; the finish kernel negates
+// it and writes both triangles. All matrices of a call step together: they are
+// ordered by block count, so the ones still active at step k are a prefix.
 #include <algorithm>
 
 #include "tile_f32.hpp"
@@ -32,7 +38,7 @@ struct InvDesc {
   int32_t* info;   // this matrix's info entry
   float* E;        // [TB][TB]  U_kk^-T (lower triangular)
   float* Ui;       // [TB][TB]  U_kk^-1 (upper triangular)
-  float* Y;        // [TB][ldy] Y panels (rows = pivot rows)
+  float* Y;        // [2*TB][ldy] Y panels of steps k (rows 0..) and k+1 (rows TB..)
   int32_t n, nb;
   float shift;
   int32_t nb64;    // 64-wide blocks (prep/finish tiles)
@@ -232,11 +238,12 @@ __global__ void __launch_bounds__(PT) inv_pivot_kernel(const InvDesc* __restrict
   if (failed && tid == 0 && *gp(d.info) == 0) *gp(d.info) = k0 + failed;
 }
 
-// Panel of step k: for column block j != k, Y_j = E V_j and W_j = E^T Y_j, with W_j
-// written into S in place; column block j = k writes S_kk = -E^T E.
+// Panel of step k into buffer slot `slot` (Y rows slot*TB ..): for column block
+// j != k, Y_j = E V_j and W_j = E^T Y_j, with W_j written into S in place; column
+// block j = k writes S_kk = -E^T E.
 __global__ void __launch_bounds__(256) inv_panel_kernel(const InvDesc* __restrict__ desc,
                                                         const int32_t* __restrict__ begin,
-                                                        int count, int k) {
+                                                        int count, int k, int slot) {
   const int p = find_problem(begin, count, blockIdx.x);
   const InvDesc& d = desc[p];
   const int j = blockIdx.x - begin[p];
@@ -257,7 +264,7 @@ __global__ void __launch_bounds__(256) inv_panel_kernel(const InvDesc* __restric
   const Operand V = j > k ? op_rows(d.S + int64_t(k0) * n + j0, n, bk, 0, bj)    // V = S_kj
                           : op_cols(d.S + int64_t(j0) * n + k0, n, bk, 0, bj);   // V = S_jk^T
   quad_gemm(q, Uop, V, bk, 1.f, lds);
-  quad_store(q, d.Y + j0, d.ldy, bk, bj);
+  quad_store(q, d.Y + int64_t(slot) * TB * d.ldy + j0, d.ldy, bk, bj);
   if (d.chol && j > k) quad_store(q, d.chol + int64_t(k0) * n + j0, n, bk, bj);
   quad_to_lds(q, Ys, LDP);  // rows >= bk are zero (their A columns were zero)
   quad_zero(q);
@@ -267,24 +274,56 @@ __global__ void __launch_bounds__(256) inv_panel_kernel(const InvDesc* __restric
   else quad_store_t(q, d.S + int64_t(j0) * n + k0, n, bk, bj, lds);       // S_jk = W_j^T
 }
 
-// Update of step k: S_ij -= Y_i^T Y_j over the upper 128-tiles with i, j != k.
+// Update of step k: S_ij -= Y_i^T Y_j over the upper 128-tile of row blocks i, j,
+// with rows [kb, ke) of the stacked panel buffer.
+__device__ __forceinline__ void update_tile(const InvDesc& d, int ti, int tj, int kb, int ke, float* lds) {
+  const int n = d.n, i0 = ti * TB, j0 = tj * TB;
+  const int bi = min(TB, n - i0), bj = min(TB, n - j0);
+  Quad q;
+  float* C = d.S + int64_t(i0) * n + j0;
+  quad_load(q, C, n, bi, bj);
+  // panel rows are 16-byte aligned with pitch ldy = n rounded up to 4 (workspace carve-out)
+  const float* Y = d.Y + int64_t(kb) * d.ldy;
+  quad_gemm<true>(q, op_rows(Y, d.ldy, ke - kb, i0, n), op_rows(Y, d.ldy, ke - kb, j0, n), ke - kb, -1.f, lds);
+  quad_store(q, C, n, bi, bj);
+}
+
+// Update after step k, or after steps k and k+1 when `pair` is set and the matrix
+// has block k+1: every upper tile outside block row k+1 (k when unpaired) takes the
+// rank-(bk + bk1) product of both steps, tiles in block row k only step k+1's half.
 __global__ void __launch_bounds__(256) inv_update_kernel(const InvDesc* __restrict__ desc,
+                                                         const int32_t* __restrict__ begin,
+                                                         int count, int k, int total, int pair) {
+  const int v = xcd_virtual(blockIdx.x, gridDim.x, total);
+  if (v < 0) return;
+  const int p = find_problem(begin, count, v);
+  const InvDesc& d = desc[p];
+  int ti, tj;
+  upper_tile(v - begin[p], d.nb, ti, tj);
+  const bool paired = pair && k + 1 < d.nb;
+  const int kx = paired ? k + 1 : k;  // written by its panel kernel
+  if (ti == kx || tj == kx) return;
+  const int bk = min(TB, d.n - k * TB);
+  int kb = 0, ke = bk;
+  if (paired) {
+    kb = (ti == k || tj == k) ? TB : 0;
+    ke = TB + min(TB, d.n - (k + 1) * TB);
+  }
+  __shared__ __attribute__((aligned(16))) float lds[4 * CHUNK];
+  update_tile(d, ti, tj, kb, ke, lds);
+}
+
+// Step k's update of block row k+1 before its pivot (paired steps): the tiles
+// (k+1, j) for j != k, stored as upper tiles (min, max).
+__global__ void __launch_bounds__(256) inv_rowupd_kernel(const InvDesc* __restrict__ desc,
                                                          const int32_t* __restrict__ begin,
                                                          int count, int k) {
   const int p = find_problem(begin, count, blockIdx.x);
   const InvDesc& d = desc[p];
-  int ti, tj;
-  upper_tile(blockIdx.x - begin[p], d.nb, ti, tj);
-  if (ti == k || tj == k) return;  // written by the panel kernel
-  const int n = d.n, k0 = k * TB, bk = min(TB, n - k0);
-  const int i0 = ti * TB, j0 = tj * TB;
-  const int bi = min(TB, n - i0), bj = min(TB, n - j0);
+  const int j = blockIdx.x - begin[p];
+  if (j == k) return;
   __shared__ __attribute__((aligned(16))) float lds[4 * CHUNK];
-  Quad q;
-  float* C = d.S + int64_t(i0) * n + j0;
-  quad_load(q, C, n, bi, bj);
-  quad_gemm(q, op_rows(d.Y, d.ldy, bk, i0, n), op_rows(d.Y, d.ldy, bk, j0, n), bk, -1.f, lds);
-  quad_store(q, C, n, bi, bj);
+  update_tile(d, min(j, k + 1), max(j, k + 1), 0, TB, lds);
 }
 
 // inv <- -S with both triangles written (S = inv in place).
@@ -318,7 +357,7 @@ struct InvPlan {
   std::vector<int> order;  // matrices sorted by block count, descending
   std::vector<int32_t> tile_begin, panel_begin, t64_begin;
   std::vector<int32_t> active;  // active[k] = matrices with nb > k
-  size_t floats = 0;            // E, Ui, Pn, Y, W for all matrices
+  size_t floats = 0;            // E, Ui, Y for all matrices
   int max_nb = 0;
 };
 
@@ -339,7 +378,7 @@ static void plan_inv(int count, const int32_t* n, InvPlan& pl) {
     tiles += int64_t(nb) * (nb + 1) / 2;
     panels += nb;
     t64 += int64_t(nb64) * (nb64 + 1) / 2;
-    pl.floats += size_t(2) * TB * TB + size_t(TB) * ((nn + 3) / 4 * 4);
+    pl.floats += size_t(2) * TB * TB + size_t(2) * TB * ((nn + 3) / 4 * 4);
     if (nb > pl.max_nb) pl.max_nb = nb;
   }
   pl.active.assign(pl.max_nb, 0);
@@ -420,7 +459,7 @@ extern "C" kfac_status kfac_invert(int32_t count, const int32_t* n, const float*
     d.E = wsf + off; off += size_t(TB) * TB;
     d.Ui = wsf + off; off += size_t(TB) * TB;
     d.ldy = (n[m] + 3) / 4 * 4;
-    d.Y = wsf + off; off += size_t(TB) * d.ldy;
+    d.Y = wsf + off; off += size_t(2) * TB * d.ldy;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   st = upload(d_desc, desc.data(), sizeof(InvDesc) * count, s);
@@ -443,16 +482,31 @@ extern "C" kfac_status kfac_invert(int32_t count, const int32_t* n, const float*
   KFAC_LAUNCH(K_INV_PREP, inv_prep_kernel, dim3(grid_of(pl.t64_begin, count, t64_of)), dim3(256), 0, s,
               d_desc, d_t64, count);
   KFAC_CHECK_LAUNCH("inv_prep_kernel");
-  for (int k = 0; k < pl.max_nb; ++k) {
-    const int a = pl.active[k];
-    KFAC_LAUNCH(K_INV_PIVOT, inv_pivot_kernel, dim3(a), dim3(PT), 0, s, d_desc, k);
-    KFAC_CHECK_LAUNCH("inv_pivot_kernel");
-    KFAC_LAUNCH(K_INV_PANEL, inv_panel_kernel, dim3(grid_of(pl.panel_begin, a, panels_of)), dim3(256), 0, s,
-                d_desc, d_panel, a, k);
-    KFAC_CHECK_LAUNCH("inv_panel_kernel");
-    KFAC_LAUNCH(K_INV_UPDATE, inv_update_kernel, dim3(grid_of(pl.tile_begin, a, tiles_of)), dim3(256), 0, s,
-                d_desc, d_tile, a, k);
+  auto update = [&](int a, int k, int pair) -> kfac_status {
+    const unsigned ut = grid_of(pl.tile_begin, a, tiles_of);
+    KFAC_LAUNCH(K_INV_UPDATE, inv_update_kernel, dim3(xcd_grid(ut)), dim3(256), 0, s, d_desc, d_tile, a, k,
+                static_cast<int>(ut), pair);
     KFAC_CHECK_LAUNCH("inv_update_kernel");
+    return KFAC_OK;
+  };
+  for (int k = 0; k < pl.max_nb; k += 2) {  // steps in pairs
+    const int a0 = pl.active[k];
+    const int a1 = k + 1 < pl.max_nb ? pl.active[k + 1] : 0;
+    KFAC_LAUNCH(K_INV_PIVOT, inv_pivot_kernel, dim3(a0), dim3(PT), 0, s, d_desc, k);
+    KFAC_CHECK_LAUNCH("inv_pivot_kernel");
+    KFAC_LAUNCH(K_INV_PANEL, inv_panel_kernel, dim3(grid_of(pl.panel_begin, a0, panels_of)), dim3(256), 0, s,
+                d_desc, d_panel, a0, k, 0);
+    KFAC_CHECK_LAUNCH("inv_panel_kernel");
+    if (a1 > 0) {
+      const unsigned pg = grid_of(pl.panel_begin, a1, panels_of);
+      KFAC_LAUNCH(K_INV_ROWUPD, inv_rowupd_kernel, dim3(pg), dim3(256), 0, s, d_desc, d_panel, a1, k);
+      KFAC_CHECK_LAUNCH("inv_rowupd_kernel");
+      KFAC_LAUNCH(K_INV_PIVOT, inv_pivot_kernel, dim3(a1), dim3(PT), 0, s, d_desc, k + 1);
+      KFAC_CHECK_LAUNCH("inv_pivot_kernel");
+      KFAC_LAUNCH(K_INV_PANEL, inv_panel_kernel, dim3(pg), dim3(256), 0, s, d_desc, d_panel, a1, k + 1, 1);
+      KFAC_CHECK_LAUNCH("inv_panel_kernel");
+    }
+    if ((st = update(a0, k, 1))) return st;
   }
   KFAC_LAUNCH(K_INV_FINISH, inv_finish_kernel, dim3(grid_of(pl.t64_begin, count, t64_of)), dim3(256), 0, s,
               d_desc, d_t64, count);

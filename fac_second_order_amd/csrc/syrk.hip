@@ -9,8 +9,8 @@
 // im2col patch matrix of the NHWC activation and is never written out: each
 // 16-byte fp16 vector of 8 patch columns (one kernel tap, 8 channels) is gathered
 // straight from the activation tensor into registers, transposed in registers and
-// stored column-major into LDS, where the MFMA operands are read with 16-byte LDS
-// loads. For G, X is the output-gradient tensor viewed as [R, C_out].
+// stored column-major (XOR-swizzled) into LDS, where the MFMA operands are read with
+// 16-byte LDS loads. For G, X is the output-gradient tensor viewed as [R, C_out].
 //
 // Work item = (factor, row split, upper tile ti <= tj of 128x128). Waves compute
 // 64x64 quadrants with v_mfma_f32_32x32x16_f16 (fp16 in, fp32 accumulate); the
@@ -33,6 +33,15 @@ constexpr int KC = 64;            // patch rows per LDS chunk (fp16)
 constexpr int LDK = KC + 8;       // LDS row pitch in halves (144 B)
 constexpr int KC32 = 32;          // patch rows per LDS chunk (fp32 path)
 constexpr int LDN32 = ST + 4;     // LDS row pitch in floats (fp32 path)
+
+// LDS operand layout [column m][patch row k] (fp16, pitch LDK), with the 16-byte
+// group of 8 rows XOR-swizzled by m/8: the transposing stores of a wave (16 column
+// groups x 4 row groups) then spread over all banks instead of piling 16 column
+// groups onto one bank, while each MFMA operand read (8 consecutive k of one m)
+// stays one aligned 16-byte load.
+__device__ __forceinline__ int xoff(int m, int k) {
+  return m * LDK + ((((k >> 3) ^ (m >> 3)) & 7) << 3) + (k & 7);
+}
 
 struct SyrkDesc {
   const void* src;
@@ -161,14 +170,6 @@ __device__ inline v8h gather8(const SyrkDesc& d, const RowTab& t, int rr, const 
   return v;
 }
 
-// Maps a hardware block id to a virtual work id so that XCD x (blocks b with
-// b % 8 == x) runs the contiguous range [x*per, (x+1)*per). Returns -1 for padding.
-__device__ inline int xcd_virtual(int b, int grid, int total) {
-  const int per = grid / 8;
-  const int v = (b % 8) * per + b / 8;
-  return v < total ? v : -1;
-}
-
 __device__ inline float blend(float v, const float* out, int64_t o, float decay) {
   return decay != 0.f ? decay * gp(out)[o] + (1.f - decay) * v : v;
 }
@@ -244,10 +245,10 @@ __global__ void __launch_bounds__(256) syrk_f16_kernel(const SyrkDesc* __restric
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       v4h w = {va[0][e], va[1][e], va[2][e], va[3][e]};
-      *reinterpret_cast<v4h*>(Xa + (cg * 8 + e) * LDK + rg * 4) = w;
+      *reinterpret_cast<v4h*>(Xa + xoff(cg * 8 + e, rg * 4)) = w;
       if (!diag) {
         v4h u = {vb[0][e], vb[1][e], vb[2][e], vb[3][e]};
-        *reinterpret_cast<v4h*>(Xb + (cg * 8 + e) * LDK + rg * 4) = u;
+        *reinterpret_cast<v4h*>(Xb + xoff(cg * 8 + e, rg * 4)) = u;
       }
     }
     if (more) fill_rowtab(d, tab[(c + 1) & 1], r0 + KC, r_end);
@@ -260,7 +261,7 @@ __global__ void __launch_bounds__(256) syrk_f16_kernel(const SyrkDesc* __restric
         if (!diag) vb[q] = gather8(d, tn, rg * 4 + q, cb);
       }
     }
-    if (want_col) {
+    if (want_col) {  // all 64 rows of column tid, in swizzled order
 #pragma unroll
       for (int k = 0; k < KC; k += 8) {
         v8h cv = *reinterpret_cast<const v8h*>(Xa + tid * LDK + k);
@@ -272,10 +273,10 @@ __global__ void __launch_bounds__(256) syrk_f16_kernel(const SyrkDesc* __restric
 #pragma unroll
       for (int ks = 0; ks < KC / 16; ++ks) {
         const int ko = ks * 16 + (lane >> 5) * 8;
-        const v8h a0 = *reinterpret_cast<const v8h*>(Xa + (wm * 64 + (lane & 31)) * LDK + ko);
-        const v8h a1 = *reinterpret_cast<const v8h*>(Xa + (wm * 64 + 32 + (lane & 31)) * LDK + ko);
-        const v8h b0 = *reinterpret_cast<const v8h*>(Xb + (wn * 64 + (lane & 31)) * LDK + ko);
-        const v8h b1 = *reinterpret_cast<const v8h*>(Xb + (wn * 64 + 32 + (lane & 31)) * LDK + ko);
+        const v8h a0 = *reinterpret_cast<const v8h*>(Xa + xoff(wm * 64 + (lane & 31), ko));
+        const v8h a1 = *reinterpret_cast<const v8h*>(Xa + xoff(wm * 64 + 32 + (lane & 31), ko));
+        const v8h b0 = *reinterpret_cast<const v8h*>(Xb + xoff(wn * 64 + (lane & 31), ko));
+        const v8h b1 = *reinterpret_cast<const v8h*>(Xb + xoff(wn * 64 + 32 + (lane & 31), ko));
         acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0, acc[0][0], 0, 0, 0);
         acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b1, acc[0][1], 0, 0, 0);
         acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b0, acc[1][0], 0, 0, 0);

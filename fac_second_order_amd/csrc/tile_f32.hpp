@@ -96,6 +96,30 @@ __device__ inline void op_fetch(const Operand& o, int k0, float4 (&r)[4]) {
   }
 }
 
+// Fast path for fp32 rows whose pitch is padded to a multiple of 4 floats, with src
+// 16-byte aligned and m0 % 4 == 0 (checked by the caller): each 4-group starting
+// below mv is read whole with one 16-byte load. Entries of a group at or beyond mv
+// are row padding: they only reach output rows or columns >= mv, which callers
+// never store.
+__device__ inline void op_fetch_rows4(const Operand& o, int k0, float4 (&r)[4]) {
+  const int kg = threadIdx.x >> 5, mg = threadIdx.x & 31;
+  const int m = o.m0 + 4 * mg;
+  const KG float* base = gp(static_cast<const float*>(o.src)) + m;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int k = k0 + 4 * kg + q;
+    v4f x = {0.f, 0.f, 0.f, 0.f};
+    if (k < o.kv && m < o.mv) x = *reinterpret_cast<const KG v4f*>(base + k * o.ld);
+    r[q] = make_float4(x.x, x.y, x.z, x.w);
+  }
+}
+
+template <bool ROWS4>
+__device__ inline void fetch(const Operand& o, int k0, float4 (&r)[4]) {
+  if constexpr (ROWS4) op_fetch_rows4(o, k0, r);
+  else op_fetch(o, k0, r);
+}
+
 __device__ inline void op_store(float* lds, const float4 (&r)[4]) {
   const int kg = threadIdx.x >> 5, mg = threadIdx.x & 31;
 #pragma unroll
@@ -122,30 +146,47 @@ __device__ inline void quad_mma_p(Quad& q, const float* As, int apitch, const fl
 }
 
 // acc += sign * A^T B over k in [0, K), pipelined. lds holds 4*CHUNK floats
-// (two buffers of the A and B chunks). Ends with a barrier.
+// (two buffers of the A and B chunks). Global loads run two chunks ahead of the
+// MFMAs in two register stages used alternately: while the MFMAs read chunk c from
+// one LDS buffer, chunks c+1 and c+2 are in flight; after the MFMAs, chunk c+1 goes
+// to the other buffer and its registers take chunk c+3. One barrier per chunk; ends
+// with a barrier. ROWS4: both operands qualify for op_fetch_rows4.
+template <bool ROWS4 = false>
 __device__ inline void quad_gemm(Quad& q, const Operand& A, const Operand& B, int K, float sign,
                                  float* lds) {
   const int nchunk = (K + KT - 1) / KT;
-  float4 ra[4], rb[4];
-  op_fetch(A, 0, ra);
-  op_fetch(B, 0, rb);
-  op_store(lds, ra);
-  op_store(lds + CHUNK, rb);
+  float4 ra0[4], rb0[4], ra1[4], rb1[4];
+  fetch<ROWS4>(A, 0, ra0);
+  fetch<ROWS4>(B, 0, rb0);
+  if (nchunk > 1) {
+    fetch<ROWS4>(A, KT, ra1);
+    fetch<ROWS4>(B, KT, rb1);
+  }
+  op_store(lds, ra0);
+  op_store(lds + CHUNK, rb0);
+  if (nchunk > 2) {
+    fetch<ROWS4>(A, 2 * KT, ra0);
+    fetch<ROWS4>(B, 2 * KT, rb0);
+  }
   __syncthreads();
-  for (int c = 0; c < nchunk; ++c) {
-    float* cur = lds + (c & 1) * 2 * CHUNK;
-    float* nxt = lds + ((c + 1) & 1) * 2 * CHUNK;
-    const bool more = c + 1 < nchunk;
-    if (more) {
-      op_fetch(A, (c + 1) * KT, ra);
-      op_fetch(B, (c + 1) * KT, rb);
-    }
+  // ra/rb: the stage holding chunk c+1
+  auto step = [&](int c, float4 (&ra)[4], float4 (&rb)[4]) {
+    const float* cur = lds + (c & 1) * 2 * CHUNK;
     quad_mma_p(q, cur, LDP, cur + CHUNK, LDP, sign);
-    if (more) {
+    if (c + 1 < nchunk) {
+      float* nxt = lds + ((c + 1) & 1) * 2 * CHUNK;
       op_store(nxt, ra);
       op_store(nxt + CHUNK, rb);
+      if (c + 3 < nchunk) {
+        fetch<ROWS4>(A, (c + 3) * KT, ra);
+        fetch<ROWS4>(B, (c + 3) * KT, rb);
+      }
     }
     __syncthreads();
+  };
+  for (int c = 0; c < nchunk; c += 2) {
+    step(c, ra1, rb1);
+    if (c + 1 < nchunk) step(c + 1, ra0, rb0);
   }
 }
 
@@ -172,6 +213,17 @@ __device__ inline void quad_gemm_lds_b(Quad& q, const Operand& A, const float* B
 __device__ inline void quad_load(Quad& q, const float* src, int64_t ld, int rvalid, int cvalid) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
+  if (rvalid >= TB && cvalid >= TB) {  // interior tile: no per-element checks
+    const KG float* s = gp(src) + int64_t(quad_row(wm, 0, 0, lane)) * ld + quad_col(wn, 0, lane);
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          q.c[a][b][e] = s[int64_t(a * 32 + 8 * (e >> 2) + (e & 3)) * ld + b * 32];
+    return;
+  }
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -202,6 +254,17 @@ __device__ inline void quad_store(const Quad& q, float* dst, int64_t ld, int rva
                                   float scale = 1.f) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
+  if (rvalid >= TB && cvalid >= TB) {  // interior tile
+    KG float* o = gp(dst) + int64_t(quad_row(wm, 0, 0, lane)) * ld + quad_col(wn, 0, lane);
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          o[int64_t(a * 32 + 8 * (e >> 2) + (e & 3)) * ld + b * 32] = q.c[a][b][e] * scale;
+    return;
+  }
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
