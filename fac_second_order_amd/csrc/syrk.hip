@@ -34,13 +34,15 @@ constexpr int LDK = KC + 8;       // LDS row pitch in halves (144 B)
 constexpr int KC32 = 32;          // patch rows per LDS chunk (fp32 path)
 constexpr int LDN32 = ST + 4;     // LDS row pitch in floats (fp32 path)
 
-// LDS operand layout [column m][patch row k] (fp16, pitch LDK), with the 16-byte
-// group of 8 rows XOR-swizzled by m/8: the transposing stores of a wave (16 column
-// groups x 4 row groups) then spread over all banks instead of piling 16 column
-// groups onto one bank, while each MFMA operand read (8 consecutive k of one m)
-// stays one aligned 16-byte load.
+// LDS operand layout [column m][patch row k] (fp16, pitch LDK = 36 dwords), with
+// the 16-byte group of 8 rows XOR-swizzled by m/16. Without it the transposing
+// 8-byte stores of a wave (16 column groups 8 columns apart x 4 row groups) land on
+// two bank offsets only, since 8 rows of pitch 36 dwords span 288 = 0 mod 32
+// dwords; with it they spread over the banks, and the MFMA operand reads (16
+// consecutive m, one aligned 16-byte group each) stay conflict-free because m/16
+// is constant within such a read group.
 __device__ __forceinline__ int xoff(int m, int k) {
-  return m * LDK + ((((k >> 3) ^ (m >> 3)) & 7) << 3) + (k & 7);
+  return m * LDK + ((((k >> 3) ^ (m >> 4)) & 7) << 3) + (k & 7);
 }
 
 struct SyrkDesc {
@@ -49,7 +51,8 @@ struct SyrkDesc {
   float* partial;  // [splits][nt][ST*ST] when splits > 1
   float* pcol;     // [splits][nb][ST] bias column partial sums
   int32_t mode;    // 0: rows [R, ld]; 1: im2col of NHWC [n, H, W, C]
-  int32_t vec;     // 16-byte gathers allowed
+  int32_t vec;     // 16-byte gathers (buffer loads) allowed
+  int32_t nbytes;  // input tensor bytes when vec (< 2^31): the buffer range
   int32_t d_core;  // columns of X (without the bias column)
   int32_t d;       // factor order (d_core + bias)
   int32_t bias;
@@ -149,25 +152,31 @@ __device__ inline void fill_coltab(const SyrkDesc& d, int c0, ColTab& ct) {
 }
 
 // 8 consecutive columns of the chunk row rr as fp16 (zeros outside the image, past
-// the last row or past d_core).
-__device__ inline v8h gather8(const SyrkDesc& d, const RowTab& t, int rr, const ColTab& ct) {
+// the last row or past d_core), element by element (inputs whose channel count or
+// alignment rules out 16-byte vectors).
+__device__ inline v8h gather8_elem(const SyrkDesc& d, const RowTab& t, int rr, const ColTab& ct) {
   const KG _Float16* src = gp(static_cast<const _Float16*>(d.src));
   const int ih = t.ih[rr], iw = t.iw[rr];
   const int64_t off = t.off[rr];
   v8h v;
-  if (d.vec) {  // the 8 columns share one tap: one 16-byte load
-    const bool ok = unsigned(ih + ct.ki[0]) < unsigned(d.H) && unsigned(iw + ct.kj[0]) < unsigned(d.W);
-    if (ok) return *reinterpret_cast<const KG v8h*>(src + off + ct.coff[0]);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) v[q] = static_cast<_Float16>(0.f);
-    return v;
-  }
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
     const bool ok = unsigned(ih + ct.ki[q]) < unsigned(d.H) && unsigned(iw + ct.kj[q]) < unsigned(d.W);
     v[q] = ok ? src[off + ct.coff[q]] : static_cast<_Float16>(0.f);
   }
   return v;
+}
+
+// The same when the 8 columns share one tap (d.vec): one 16-byte buffer load. A
+// padding tap, a row past the end or columns past d_core get an offset beyond the
+// buffer's range, for which the load returns zeros without touching memory.
+__device__ __forceinline__ v8h gather8_vec(__amdgpu_buffer_rsrc_t rsrc, const SyrkDesc& d, const RowTab& t,
+                                           int rr, const ColTab& ct) {
+  const int ih = t.ih[rr], iw = t.iw[rr];
+  const bool ok = (unsigned(ih + ct.ki[0]) < unsigned(d.H)) & (unsigned(iw + ct.kj[0]) < unsigned(d.W));
+  const unsigned off = static_cast<unsigned>(t.off[rr] + ct.coff[0]) * 2u;
+  const v4u x = __builtin_amdgcn_raw_buffer_load_b128(rsrc, ok ? off : 0x80000000u, 0, 0);
+  return __builtin_bit_cast(v8h, x);
 }
 
 __device__ inline float blend(float v, const float* out, int64_t o, float decay) {
@@ -188,6 +197,79 @@ __device__ inline void write_bias_direct(const SyrkDesc& d, int ti, int t, float
   if (t == 0 && tid == 0) {
     const int64_t o = packed_off(d.d_core, d.d_core, d.d);
     gp(d.out)[o] = blend(d.r_f * d.inv_r, d.out, o, decay);
+  }
+}
+
+// Main loop of a tile over patch rows [r_begin, r_end): gathers of the next chunk
+// overlap the MFMAs of the current one. DIAG: one operand (Xa == Xb); VEC: 16-byte
+// buffer-load gathers.
+template <bool DIAG, bool VEC>
+__device__ __forceinline__ void syrk_rows(const SyrkDesc& d, RowTab* tab, _Float16* Xa, _Float16* Xb,
+                                          const ColTab& ca, const ColTab& cb, int r_begin, int r_end,
+                                          bool want_col, v16f (&acc)[2][2], float& colsum) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int cg = tid & 15, rg = tid >> 4;
+  // raw buffer over the input tensor (used by the VEC gathers only)
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(d.src), 0, d.nbytes, 0x00020000);
+  auto gather = [&](const RowTab& t, int rr, const ColTab& ct) -> v8h {
+    if constexpr (VEC) return gather8_vec(rsrc, d, t, rr, ct);
+    else return gather8_elem(d, t, rr, ct);
+  };
+  fill_rowtab(d, tab[0], r_begin, r_end);
+  __syncthreads();
+  v8h va[4], vb[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    va[q] = gather(tab[0], rg * 4 + q, ca);
+    if constexpr (!DIAG) vb[q] = gather(tab[0], rg * 4 + q, cb);
+  }
+  int c = 0;
+  for (int r0 = r_begin; r0 < r_end; r0 += KC, ++c) {
+    const bool more = r0 + KC < r_end;
+    __syncthreads();  // the previous chunk's LDS operands are consumed
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      v4h w = {va[0][e], va[1][e], va[2][e], va[3][e]};
+      *reinterpret_cast<v4h*>(Xa + xoff(cg * 8 + e, rg * 4)) = w;
+      if constexpr (!DIAG) {
+        v4h u = {vb[0][e], vb[1][e], vb[2][e], vb[3][e]};
+        *reinterpret_cast<v4h*>(Xb + xoff(cg * 8 + e, rg * 4)) = u;
+      }
+    }
+    if (more) fill_rowtab(d, tab[(c + 1) & 1], r0 + KC, r_end);
+    __syncthreads();
+    if (more) {  // next chunk's global loads overlap this chunk's MFMAs
+      const RowTab& tn = tab[(c + 1) & 1];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        va[q] = gather(tn, rg * 4 + q, ca);
+        if constexpr (!DIAG) vb[q] = gather(tn, rg * 4 + q, cb);
+      }
+    }
+    if constexpr (DIAG) {
+      if (want_col) {  // all 64 rows of column tid, in swizzled order
+#pragma unroll
+        for (int k = 0; k < KC; k += 8) {
+          v8h cv = *reinterpret_cast<const v8h*>(Xa + tid * LDK + k);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) colsum += static_cast<float>(cv[q]);
+        }
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < KC / 16; ++ks) {
+      const int ko = ks * 16 + (lane >> 5) * 8;
+      const v8h a0 = *reinterpret_cast<const v8h*>(Xa + xoff(wm * 64 + (lane & 31), ko));
+      const v8h a1 = *reinterpret_cast<const v8h*>(Xa + xoff(wm * 64 + 32 + (lane & 31), ko));
+      const v8h b0 = *reinterpret_cast<const v8h*>(Xb + xoff(wn * 64 + (lane & 31), ko));
+      const v8h b1 = *reinterpret_cast<const v8h*>(Xb + xoff(wn * 64 + 32 + (lane & 31), ko));
+      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0, acc[0][0], 0, 0, 0);
+      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b1, acc[0][1], 0, 0, 0);
+      acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b0, acc[1][0], 0, 0, 0);
+      acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1, acc[1][1], 0, 0, 0);
+    }
   }
 }
 
@@ -228,61 +310,13 @@ __global__ void __launch_bounds__(256) syrk_f16_kernel(const SyrkDesc* __restric
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
   float colsum = 0.f;
-
-  // prologue: row table and registers of the first chunk
-  fill_rowtab(d, tab[0], r_begin, r_end);
-  __syncthreads();
-  v8h va[4], vb[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    va[q] = gather8(d, tab[0], rg * 4 + q, ca);
-    if (!diag) vb[q] = gather8(d, tab[0], rg * 4 + q, cb);
-  }
-  int c = 0;
-  for (int r0 = r_begin; r0 < r_end; r0 += KC, ++c) {
-    const bool more = r0 + KC < r_end;
-    __syncthreads();  // the previous chunk's LDS operands are consumed
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      v4h w = {va[0][e], va[1][e], va[2][e], va[3][e]};
-      *reinterpret_cast<v4h*>(Xa + xoff(cg * 8 + e, rg * 4)) = w;
-      if (!diag) {
-        v4h u = {vb[0][e], vb[1][e], vb[2][e], vb[3][e]};
-        *reinterpret_cast<v4h*>(Xb + xoff(cg * 8 + e, rg * 4)) = u;
-      }
-    }
-    if (more) fill_rowtab(d, tab[(c + 1) & 1], r0 + KC, r_end);
-    __syncthreads();
-    if (more) {  // next chunk's global loads overlap this chunk's MFMAs
-      const RowTab& tn = tab[(c + 1) & 1];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        va[q] = gather8(d, tn, rg * 4 + q, ca);
-        if (!diag) vb[q] = gather8(d, tn, rg * 4 + q, cb);
-      }
-    }
-    if (want_col) {  // all 64 rows of column tid, in swizzled order
-#pragma unroll
-      for (int k = 0; k < KC; k += 8) {
-        v8h cv = *reinterpret_cast<const v8h*>(Xa + tid * LDK + k);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) colsum += static_cast<float>(cv[q]);
-      }
-    }
-    {  // every wave runs its MFMAs (uniform control flow keeps acc in place)
-#pragma unroll
-      for (int ks = 0; ks < KC / 16; ++ks) {
-        const int ko = ks * 16 + (lane >> 5) * 8;
-        const v8h a0 = *reinterpret_cast<const v8h*>(Xa + xoff(wm * 64 + (lane & 31), ko));
-        const v8h a1 = *reinterpret_cast<const v8h*>(Xa + xoff(wm * 64 + 32 + (lane & 31), ko));
-        const v8h b0 = *reinterpret_cast<const v8h*>(Xb + xoff(wn * 64 + (lane & 31), ko));
-        const v8h b1 = *reinterpret_cast<const v8h*>(Xb + xoff(wn * 64 + 32 + (lane & 31), ko));
-        acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0, acc[0][0], 0, 0, 0);
-        acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b1, acc[0][1], 0, 0, 0);
-        acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b0, acc[1][0], 0, 0, 0);
-        acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1, acc[1][1], 0, 0, 0);
-      }
-    }
+  // block-uniform specialisations of the main loop
+  if (diag) {
+    if (d.vec) syrk_rows<true, true>(d, tab, Xa, Xb, ca, cb, r_begin, r_end, want_col, acc, colsum);
+    else syrk_rows<true, false>(d, tab, Xa, Xb, ca, cb, r_begin, r_end, want_col, acc, colsum);
+  } else {
+    if (d.vec) syrk_rows<false, true>(d, tab, Xa, Xb, ca, cb, r_begin, r_end, want_col, acc, colsum);
+    else syrk_rows<false, false>(d, tab, Xa, Xb, ca, cb, r_begin, r_end, want_col, acc, colsum);
   }
 
   if (d.splits == 1) {
@@ -585,8 +619,11 @@ static kfac_status build_plan(const kfac_layer* L, int32_t count, kfac_dtype dt,
         d.src = src;
         d.out = out;
         const int width = d.mode == 1 ? d.C : d.ld;
+        const int64_t bytes = d.mode == 1 ? int64_t(L[l].n) * d.H * d.W * d.C * esize
+                                          : int64_t(d.R) * d.ld * esize;
         d.vec = (dt == KFAC_F16 && width % 8 == 0 && d.d_core % 8 == 0 &&
-                 reinterpret_cast<uintptr_t>(src) % 16 == 0) ? 1 : 0;
+                 reinterpret_cast<uintptr_t>(src) % 16 == 0 && bytes < (int64_t(1) << 31)) ? 1 : 0;
+        d.nbytes = d.vec ? static_cast<int32_t>(bytes) : 0;
       }
       pl.desc.push_back(d);
     }
