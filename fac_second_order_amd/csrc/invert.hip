@@ -38,6 +38,7 @@ struct InvDesc {
   int32_t* info;   // this matrix's info entry
   float* E;        // [TB][TB]  U_kk^-T (lower triangular)
   float* Ui;       // [TB][TB]  U_kk^-1 (upper triangular)
+  float* P;        // [TB][TB]  P^-1 = E^T E (full)
   float* Y;        // [2*TB][ldy] Y panels of steps k (rows 0..) and k+1 (rows TB..)
   int32_t n, nb;
   float shift;
@@ -76,66 +77,87 @@ __global__ void __launch_bounds__(256) inv_prep_kernel(const InvDesc* __restrict
   }
 }
 
-// Cholesky of the pivot block P (bk x bk, upper triangle in S) and E = U^-T, by the
-// PT threads of one block. Wave w holds rows RPW*w .. RPW*w+RPW-1 and lane l
-// columns 2l, 2l+1 of a combined matrix whose strict upper triangle becomes U,
-// strict lower triangle E and diagonal 1/U_ii. Scalar step kk: the pivot row is
-// scaled, r = M_kk^-1/2 * M_k. with r_kk = M_kk^-1/2; every row i > kk clears its
-// entry in column kk and loses u_i * r with u_i = r_i; rows <= kk are final.
-// Columns are taken GP at a time: the wave that owns rows c0..c0+GP-1 runs the GP
-// steps on them in registers (broadcasts by readlane, no barrier), publishes the GP
-// scaled rows through LDS, and after one barrier every later row applies the GP
-// updates. Waves whose rows are all final skip the update. Padding rows/columns
-// (>= bk) hold the identity and stay unchanged. Writes E and U^-1 = E^T
-// (row-major, TB x TB) to the workspace, U into chol when asked, and the 1-based
-// failing column into info.
+// Pivot of step k: U = chol(P) and E = U^-T of the pivot block P (bk x bk, upper
+// triangle in S; padding rows and columns hold the identity), then P^-1 = E^T E.
+// One 512-thread block keeps the combined matrix M in LDS: its upper triangle
+// becomes U, its lower triangle (with the diagonal) E. In scalar form, step c
+// scales row c by p^-1/2 (p = M_cc) and gives its diagonal the value p^-1/2
+// (= E_cc), so row c becomes r; every later row i > c replaces its column-c entry
+// by 0 and then subtracts u_i r with u_i = r_i. The columns are taken in four
+// sub-steps J of 32 (block indices I, K in 0..3):
+//   a: wave 0 runs the 32 scalar steps on the diagonal block M_JJ in registers
+//      (one column per lane, pivot-row values by readlane), giving U_JJ and E_JJ;
+//   b: the rest of block row J is multiplied by E_JJ (MFMA): M_JK <- E_JJ M_JK,
+//      which makes U_JK (K > J) and E_JK (K < J);
+//   c: every later block row I > J subtracts M_JI^T times block row J, on the
+//      blocks it still needs: K > J with I <= K (the trailing upper triangle),
+//      K < J (the E part) and K = J, which becomes -M_JI^T E_JJ.
+// The lower blocks right of the current sub-step are never read before their own
+// sub-step overwrites them, so they start as zero. Writes E and U^-1 = E^T
+// (row-major, TB x TB), P^-1 to the workspace, S_kk = -P^-1, U into chol when asked,
+// and the 1-based failing column into info.
 constexpr int PT = 512;           // threads of the pivot kernel
-constexpr int NW = PT / 64;       // waves
-constexpr int RPW = TB / NW;      // rows per wave (contiguous)
-constexpr int GP = 4;             // pivot columns per barrier
+constexpr int SB = 32;            // sub-step width
+constexpr int MLD = TB + 4;       // LDS pitch of M
+constexpr int ELD = SB + 4;       // LDS pitch of the 32x32 E_JJ copies
+
+// acc[m][n] += sign * sum_p a[p*lda + m] * b[p*ldb + n] for p < 32 (one wave, LDS).
+// Accumulator register e of lane l holds element (8*(e/4) + 4*(l/32) + e%4, l%32).
+__device__ __forceinline__ void mma32(v16f& acc, const float* a, int lda, const float* b, int ldb,
+                                      float sign, int lane) {
+  const int ml = lane & 31, kh = lane >> 5;
+#pragma unroll
+  for (int k = 0; k < SB; k += 2) {
+    const float av = a[(k + kh) * lda + ml] * sign;
+    const float bv = b[(k + kh) * ldb + ml];
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
+  }
+}
+__device__ __forceinline__ int acc_row(int e, int lane) { return 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3); }
 
 __device__ __forceinline__ float lane_bcast(float v, int src_lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src_lane));
 }
 
-// The owner wave's GP steps on its rows QQ*GP .. QQ*GP+GP-1 (columns c0 ..).
-template <int QQ>
-__device__ __forceinline__ void pivot_group(float2 (&M)[RPW], int c0, int gcnt, int lane,
-                                            float (*prow)[TB], float* dval, float* diagU) {
+// Scalar steps on the 32x32 diagonal block at blk (pitch MLD) by one wave: lane j
+// (and its copy j + 32) holds column j, rows 0..31, so the row of every update is
+// known at compile time. In step c lane j's row-c entry becomes r_j and the later
+// rows t take -r_t r_j (after clearing column c), with r_t read from lane t. Writes
+// the block back, E_JJ to ej (rows, lower with diagonal) and ejt (its transpose),
+// U_cc to diagU; returns the first 1-based failing step or 0.
+__device__ __forceinline__ int chol32(float* blk, float* ej, float* ejt, float* diagU, int lane) {
+  const int j = lane & 31;
+  float d[SB];
 #pragma unroll
-  for (int g = 0; g < GP; ++g) {
-    if (g < gcnt) {
-      const int a = c0 + g, al = a >> 1;
-      const bool aodd = a & 1;
-      const float2 m = M[QQ * GP + g];
-      const float piv = lane_bcast(aodd ? m.y : m.x, al);
-      const float rs = rsqrtf(piv);
-      float2 sc = make_float2(m.x * rs, m.y * rs);
-      if (lane == al) {
-        if (aodd) sc.y = rs; else sc.x = rs;
-      }
-      M[QQ * GP + g] = sc;
-      reinterpret_cast<float2*>(prow[g])[lane] = sc;
-      if (lane == 0) {
-        dval[g] = piv;
-        diagU[a] = piv * rs;
-      }
+  for (int t = 0; t < SB; ++t) d[t] = blk[t * MLD + j];
+  int failed = 0;
+  float ujj = 0.f;
 #pragma unroll
-      for (int g2 = g + 1; g2 < GP; ++g2) {
-        if (g2 < gcnt) {
-          const int b = c0 + g2;
-          const float u = lane_bcast((b & 1) ? sc.y : sc.x, b >> 1);
-          float2 mb = M[QQ * GP + g2];
-          if (lane == al) {
-            if (aodd) mb.y = 0.f; else mb.x = 0.f;
-          }
-          mb.x = fmaf(-u, sc.x, mb.x);
-          mb.y = fmaf(-u, sc.y, mb.y);
-          M[QQ * GP + g2] = mb;
-        }
-      }
+  for (int c = 0; c < SB; ++c) {
+    const float p = lane_bcast(d[c], c);
+    if (failed == 0 && !(p > 0.f && isfinite(p))) failed = c + 1;
+    const float rs = rsqrtf(p);
+    const bool jc = j == c;
+    const float rj = jc ? rs : d[c] * rs;  // scaled pivot row; its diagonal is E_cc
+    if (jc) ujj = p * rs;
+    d[c] = rj;
+#pragma unroll
+    for (int t = c + 1; t < SB; ++t) {
+      const float u = lane_bcast(rj, t);  // r_t
+      d[t] = fmaf(-u, rj, jc ? 0.f : d[t]);
     }
   }
+  if (lane < SB) {
+    diagU[j] = ujj;
+#pragma unroll
+    for (int t = 0; t < SB; ++t) {
+      blk[t * MLD + j] = d[t];
+      const float e = j <= t ? d[t] : 0.f;  // E_JJ[t][j]
+      ej[t * ELD + j] = e;
+      ejt[j * ELD + t] = e;
+    }
+  }
+  return failed;
 }
 
 __global__ void __launch_bounds__(PT) inv_pivot_kernel(const InvDesc* __restrict__ desc, int k) {
@@ -143,135 +165,146 @@ __global__ void __launch_bounds__(PT) inv_pivot_kernel(const InvDesc* __restrict
   const int n = d.n, k0 = k * TB, bk = min(TB, n - k0);
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, scalar
-  __shared__ __attribute__((aligned(16))) float prow[2][GP][TB];  // scaled pivot rows
-  __shared__ __attribute__((aligned(16))) float dval[2][GP];
+  __shared__ __attribute__((aligned(16))) float M[TB * MLD];
+  __shared__ __attribute__((aligned(16))) float EJ[SB * ELD], EJT[SB * ELD];
   __shared__ float diagU[TB];
-  __shared__ float L[TB * LDT];
 
-  float2 M[RPW];
-#pragma unroll
-  for (int r = 0; r < RPW; ++r) {
-    const int i = RPW * w + r;
-    const int j0 = 2 * lane, j1 = 2 * lane + 1;
-    float a = (i == j0) ? 1.f : 0.f, b = (i == j1) ? 1.f : 0.f;
-    if (i < bk && j0 < bk) a = gp(d.S)[int64_t(k0 + min(i, j0)) * n + k0 + max(i, j0)];
-    if (i < bk && j1 < bk) b = gp(d.S)[int64_t(k0 + min(i, j1)) * n + k0 + max(i, j1)];
-    M[r] = make_float2(a, b);
+  for (int e = tid; e < TB * TB; e += PT) {
+    const int i = e / TB, j = e % TB;
+    float v = 0.f;
+    if (i <= j) v = j < bk ? gp(d.S)[int64_t(k0 + i) * n + k0 + j] : (i == j ? 1.f : 0.f);
+    M[i * MLD + j] = v;
   }
+  __syncthreads();
   int failed = 0;
-  for (int c0 = 0; c0 < bk; c0 += GP) {
-    const int buf = (c0 / GP) & 1;
-    const int gcnt = min(GP, bk - c0);
-    if (w == c0 / RPW) {
-      const int q = (c0 % RPW) / GP;
-      if (q == 0) pivot_group<0>(M, c0, gcnt, lane, prow[buf], dval[buf], diagU);
-      else if (q == 1) pivot_group<1>(M, c0, gcnt, lane, prow[buf], dval[buf], diagU);
-      else if (q == 2) pivot_group<2>(M, c0, gcnt, lane, prow[buf], dval[buf], diagU);
-      else pivot_group<3>(M, c0, gcnt, lane, prow[buf], dval[buf], diagU);
+  for (int J = 0; J < TB / SB; ++J) {
+    float* rowJ = M + J * SB * MLD;
+    if (w == 0) {
+      const int f = chol32(rowJ + J * SB, EJ, EJT, diagU + J * SB, lane);
+      if (failed == 0 && f) failed = J * SB + f;
     }
     __syncthreads();
-    {
-      const float4 pv = *reinterpret_cast<const float4*>(dval[buf]);
-      const float pp[4] = {pv.x, pv.y, pv.z, pv.w};
+    if (w < 3) {  // b: M_JK <- E_JJ M_JK for the three K != J
+      const int K = w < J ? w : w + 1;
+      float* X = rowJ + K * SB;
+      v16f acc;
 #pragma unroll
-      for (int g = GP - 1; g >= 0; --g)  // keep the first bad column
-        if (g < gcnt && (!(pp[g] > 0.f) || !isfinite(pp[g]))) failed = c0 + g + 1;
+      for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+      mma32(acc, EJT, ELD, X, MLD, 1.f, lane);  // sum_p E_JJ[m][p] X[p][n]
+#pragma unroll
+      for (int e = 0; e < 16; ++e) X[acc_row(e, lane) * MLD + (lane & 31)] = acc[e];
     }
-    if (failed) break;  // same decision in every thread
-    const int last = c0 + gcnt - 1;  // rows > last take the GP updates
-    if (RPW * w + RPW - 1 > last) {
-      float2 rjs[GP];
-      float us[GP][RPW];  // all multipliers first: one LDS round trip
+    __syncthreads();
+    // c: blocks (I, K) with I > J and (K <= J or I <= K), in a fixed order
+    int q = 0;
+    for (int I = J + 1; I < TB / SB; ++I)
+      for (int K = 0; K < TB / SB; ++K) {
+        if (K > J && I > K) continue;
+        if ((q++ & 7) != w) continue;
+        float* C = M + I * SB * MLD + K * SB;
+        v16f acc;
 #pragma unroll
-      for (int g = 0; g < GP; ++g) {
-        rjs[g] = reinterpret_cast<const float2*>(prow[buf][g])[lane];
+        for (int e = 0; e < 16; ++e) acc[e] = K == J ? 0.f : C[acc_row(e, lane) * MLD + (lane & 31)];
+        const float* B = K == J ? EJ : rowJ + K * SB;
+        mma32(acc, rowJ + I * SB, MLD, B, K == J ? ELD : MLD, -1.f, lane);
 #pragma unroll
-        for (int q = 0; q < RPW / 4; ++q) {
-          const float4 x = reinterpret_cast<const float4*>(prow[buf][g] + RPW * w)[q];
-          us[g][4 * q] = x.x; us[g][4 * q + 1] = x.y; us[g][4 * q + 2] = x.z; us[g][4 * q + 3] = x.w;
-        }
+        for (int e = 0; e < 16; ++e) C[acc_row(e, lane) * MLD + (lane & 31)] = acc[e];
       }
-#pragma unroll
-      for (int g = 0; g < GP; ++g) {
-        if (g < gcnt) {
-          const int a = c0 + g, al = a >> 1;
-          const bool aodd = a & 1;
-          const float2 rj = rjs[g];
-          const float* u = us[g];
-          const bool mycol = lane == al;
-#pragma unroll
-          for (int r = 0; r < RPW; ++r) {
-            if (RPW * w + r > last) {
-              float2 m = M[r];
-              if (mycol) {
-                if (aodd) m.y = 0.f; else m.x = 0.f;
-              }
-              m.x = fmaf(-u[r], rj.x, m.x);
-              m.y = fmaf(-u[r], rj.y, m.y);
-              M[r] = m;
-            }
-          }
-        }
-      }
-    }
+    __syncthreads();
   }
-  // E (strict lower + diagonal) into L, then coalesced writes of E and E^T
-#pragma unroll
-  for (int r = 0; r < RPW; ++r) {
-    const int i = RPW * w + r;
-    const float2 m = M[r];
-    L[i * LDT + 2 * lane] = (2 * lane <= i) ? m.x : 0.f;
-    L[i * LDT + 2 * lane + 1] = (2 * lane + 1 <= i) ? m.y : 0.f;
-    if (d.chol) {
-      if (i < 2 * lane && 2 * lane < bk) gp(d.chol)[int64_t(k0 + i) * n + k0 + 2 * lane] = m.x;
-      if (i < 2 * lane + 1 && 2 * lane + 1 < bk) gp(d.chol)[int64_t(k0 + i) * n + k0 + 2 * lane + 1] = m.y;
+  // U (strict upper of M, diagonal from diagU) into chol; then keep only E in M
+  if (d.chol)
+    for (int e = tid; e < TB * TB; e += PT) {
+      const int i = e / TB, j = e % TB;
+      if (i <= j && j < bk) gp(d.chol)[int64_t(k0 + i) * n + k0 + j] = i == j ? diagU[i] : M[i * MLD + j];
     }
+  __syncthreads();
+  for (int e = tid; e < TB * TB; e += PT) {
+    const int i = e / TB, j = e % TB;
+    if (i < j) M[i * MLD + j] = 0.f;
   }
   __syncthreads();
   for (int e = tid; e < TB * TB; e += PT) {
     const int i = e / TB, j = e % TB;
-    gp(d.E)[e] = L[i * LDT + j];
-    gp(d.Ui)[e] = L[j * LDT + i];
+    gp(d.E)[e] = M[i * MLD + j];
+    gp(d.Ui)[e] = M[j * MLD + i];
   }
-  if (d.chol)
-    for (int i = tid; i < bk; i += PT) gp(d.chol)[int64_t(k0 + i) * n + k0 + i] = diagU[i];
+  // P^-1 = E^T E on MFMA: wave w forms the 32x32 blocks (bi, bj) = (w / 2, 2(w % 2)
+  // .. +1); E is lower triangular, so the sum over p starts at 32 * max(bi, bj).
+  // Written to the workspace (full) and as S_kk = -P^-1 (upper triangle).
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const int qq = 2 * w + hh, bi = qq >> 2, bj = qq & 3;
+    v16f acc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+    const int ml = lane & 31, kh = lane >> 5;
+    for (int kk = 32 * max(bi, bj); kk < TB; kk += 2) {
+      const float a = M[(kk + kh) * MLD + 32 * bi + ml];
+      const float b = M[(kk + kh) * MLD + 32 * bj + ml];
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int i = 32 * bi + acc_row(e, lane), j = 32 * bj + ml;
+      gp(d.P)[i * TB + j] = acc[e];
+      if (i <= j && j < bk) gp(d.S)[int64_t(k0 + i) * n + k0 + j] = -acc[e];
+    }
+  }
   if (failed && tid == 0 && *gp(d.info) == 0) *gp(d.info) = k0 + failed;
 }
 
-// Panel of step k into buffer slot `slot` (Y rows slot*TB ..): for column block
-// j != k, Y_j = E V_j and W_j = E^T Y_j, with W_j written into S in place; column
-// block j = k writes S_kk = -E^T E.
-__global__ void __launch_bounds__(256) inv_panel_kernel(const InvDesc* __restrict__ desc,
-                                                        const int32_t* __restrict__ begin,
-                                                        int count, int k, int slot) {
+// Panel of step k into buffer slot `slot` (Y rows slot*TB ..), 512 threads: for
+// column block j != k, V_j = S_kj (S_jk^T for j < k) is staged in LDS, then two
+// 256-thread engines run side by side: threads 0..255 form Y_j = E V_j (the
+// Cholesky row panel U_kj when j > k) into the panel buffer, threads 256..511 form
+// W_j = P^-1 V_j, which goes into S in place (S_kj = W_j, or S_jk = W_j^T). The
+// pivot kernel wrote S_kk = -P^-1.
+constexpr int PP = 512;  // panel threads
+__global__ void __launch_bounds__(PP) inv_panel_kernel(const InvDesc* __restrict__ desc,
+                                                       const int32_t* __restrict__ begin,
+                                                       int count, int k, int slot) {
   const int p = find_problem(begin, count, blockIdx.x);
   const InvDesc& d = desc[p];
   const int j = blockIdx.x - begin[p];
+  if (j == k) return;
   const int n = d.n, k0 = k * TB, bk = min(TB, n - k0);
   const int j0 = j * TB, bj = min(TB, n - j0);
-  __shared__ __attribute__((aligned(16))) float lds[4 * CHUNK];
-  __shared__ __attribute__((aligned(16))) float Ys[TB * LDP];
-
+  const int tid = threadIdx.x, grp = tid >> 8;
+  __shared__ __attribute__((aligned(16))) float lds[2][2 * CHUNK];
+  __shared__ __attribute__((aligned(16))) float Vs[TB * LDP];
+  if (j > k) {
+    for (int e = tid; e < TB * TB; e += PP) {
+      const int r = e / TB, c = e % TB;
+      Vs[r * LDP + c] = (r < bk && c < bj) ? gp(d.S)[int64_t(k0 + r) * n + j0 + c] : 0.f;
+    }
+  } else {  // V[r][c] = S[j0 + c][k0 + r]: read along rows of S, transpose in LDS
+    for (int e = tid; e < TB * TB; e += PP) {
+      const int c = e / TB, r = e % TB;
+      Vs[r * LDP + c] = (r < bk && c < bj) ? gp(d.S)[int64_t(j0 + c) * n + k0 + r] : 0.f;
+    }
+  }
+  __syncthreads();
   Quad q;
   quad_zero(q);
-  const Operand Eop = op_rows(d.E, TB, bk, 0, bk);   // A[p][m] = E[p][m] = Ui[m][p]
-  if (j == k) {  // S_kk = -E^T E (upper triangle)
-    quad_gemm(q, Eop, Eop, bk, -1.f, lds);
-    quad_store_upper(q, d.S + int64_t(k0) * n + k0, n, bk);
-    return;
+  // group 0: A[p][m] = Ui[p][m] = E[m][p]; group 1: A[p][m] = P^-1[p][m]
+  const Operand Aop = op_rows(grp == 0 ? d.Ui : d.P, TB, bk, 0, bk);
+  quad_gemm_lds_b(q, Aop, Vs, LDP, bk, 1.f, lds[grp]);  // ends with a barrier
+  if (grp == 0) {
+    quad_store(q, d.Y + int64_t(slot) * TB * d.ldy + j0, d.ldy, bk, bj);
+    if (d.chol && j > k) quad_store(q, d.chol + int64_t(k0) * n + j0, n, bk, bj);
+  } else if (j > k) {
+    quad_store(q, d.S + int64_t(k0) * n + j0, n, bk, bj);  // S_kj = W_j
+  } else {
+    quad_to_lds(q, Vs, LDP);  // Vs is free: both engines have passed their last barrier
   }
-  const Operand Uop = op_rows(d.Ui, TB, bk, 0, bk);  // A[p][m] = Ui[p][m] = E[m][p]
-  const Operand V = j > k ? op_rows(d.S + int64_t(k0) * n + j0, n, bk, 0, bj)    // V = S_kj
-                          : op_cols(d.S + int64_t(j0) * n + k0, n, bk, 0, bj);   // V = S_jk^T
-  quad_gemm(q, Uop, V, bk, 1.f, lds);
-  quad_store(q, d.Y + int64_t(slot) * TB * d.ldy + j0, d.ldy, bk, bj);
-  if (d.chol && j > k) quad_store(q, d.chol + int64_t(k0) * n + j0, n, bk, bj);
-  quad_to_lds(q, Ys, LDP);  // rows >= bk are zero (their A columns were zero)
-  quad_zero(q);
-  __syncthreads();
-  quad_gemm_lds_b(q, Eop, Ys, LDP, bk, 1.f, lds);
-  if (j > k) quad_store(q, d.S + int64_t(k0) * n + j0, n, bk, bj);        // S_kj = W_j
-  else quad_store_t(q, d.S + int64_t(j0) * n + k0, n, bk, bj, lds);       // S_jk = W_j^T
+  if (j < k) {  // S_jk = W_j^T, coalesced along rows of S
+    __syncthreads();
+    for (int e = tid; e < TB * TB; e += PP) {
+      const int c = e / TB, r = e % TB;
+      if (r < bk && c < bj) gp(d.S)[int64_t(j0 + c) * n + k0 + r] = Vs[r * LDP + c];
+    }
+  }
 }
 
 // Update of step k: S_ij -= Y_i^T Y_j over the upper 128-tile of row blocks i, j,
@@ -357,7 +390,7 @@ struct InvPlan {
   std::vector<int> order;  // matrices sorted by block count, descending
   std::vector<int32_t> tile_begin, panel_begin, t64_begin;
   std::vector<int32_t> active;  // active[k] = matrices with nb > k
-  size_t floats = 0;            // E, Ui, Y for all matrices
+  size_t floats = 0;            // E, Ui, P, Y for all matrices
   int max_nb = 0;
 };
 
@@ -378,7 +411,7 @@ static void plan_inv(int count, const int32_t* n, InvPlan& pl) {
     tiles += int64_t(nb) * (nb + 1) / 2;
     panels += nb;
     t64 += int64_t(nb64) * (nb64 + 1) / 2;
-    pl.floats += size_t(2) * TB * TB + size_t(2) * TB * ((nn + 3) / 4 * 4);
+    pl.floats += size_t(3) * TB * TB + size_t(2) * TB * ((nn + 3) / 4 * 4);
     if (nb > pl.max_nb) pl.max_nb = nb;
   }
   pl.active.assign(pl.max_nb, 0);
@@ -458,6 +491,7 @@ extern "C" kfac_status kfac_invert(int32_t count, const int32_t* n, const float*
     d.shift = shift[m];
     d.E = wsf + off; off += size_t(TB) * TB;
     d.Ui = wsf + off; off += size_t(TB) * TB;
+    d.P = wsf + off; off += size_t(TB) * TB;
     d.ldy = (n[m] + 3) / 4 * 4;
     d.Y = wsf + off; off += size_t(2) * TB * d.ldy;
   }
@@ -494,7 +528,7 @@ extern "C" kfac_status kfac_invert(int32_t count, const int32_t* n, const float*
     const int a1 = k + 1 < pl.max_nb ? pl.active[k + 1] : 0;
     KFAC_LAUNCH(K_INV_PIVOT, inv_pivot_kernel, dim3(a0), dim3(PT), 0, s, d_desc, k);
     KFAC_CHECK_LAUNCH("inv_pivot_kernel");
-    KFAC_LAUNCH(K_INV_PANEL, inv_panel_kernel, dim3(grid_of(pl.panel_begin, a0, panels_of)), dim3(256), 0, s,
+    KFAC_LAUNCH(K_INV_PANEL, inv_panel_kernel, dim3(grid_of(pl.panel_begin, a0, panels_of)), dim3(PP), 0, s,
                 d_desc, d_panel, a0, k, 0);
     KFAC_CHECK_LAUNCH("inv_panel_kernel");
     if (a1 > 0) {
@@ -503,7 +537,7 @@ extern "C" kfac_status kfac_invert(int32_t count, const int32_t* n, const float*
       KFAC_CHECK_LAUNCH("inv_rowupd_kernel");
       KFAC_LAUNCH(K_INV_PIVOT, inv_pivot_kernel, dim3(a1), dim3(PT), 0, s, d_desc, k + 1);
       KFAC_CHECK_LAUNCH("inv_pivot_kernel");
-      KFAC_LAUNCH(K_INV_PANEL, inv_panel_kernel, dim3(pg), dim3(256), 0, s, d_desc, d_panel, a1, k + 1, 1);
+      KFAC_LAUNCH(K_INV_PANEL, inv_panel_kernel, dim3(pg), dim3(PP), 0, s, d_desc, d_panel, a1, k + 1, 1);
       KFAC_CHECK_LAUNCH("inv_panel_kernel");
     }
     if ((st = update(a0, k, 1))) return st;

@@ -7,6 +7,8 @@
 //   1) T^T = (G^-1 dW)^T: A operand G^-1 (symmetric, so its rows are its
 //      columns), B operand dW; the tile is written transposed into the workspace.
 //   2) P = T A^-1: A operand rows of T^T, B operand A^-1.
+#include <algorithm>
+
 #include "tile_f32.hpp"
 
 namespace kfac {
@@ -26,8 +28,9 @@ __global__ void __launch_bounds__(256) gemm_tn_kernel(const GemmDesc* __restrict
                                                       const int32_t* __restrict__ begin, int count) {
   const int p = find_problem(begin, count, blockIdx.x);
   const GemmDesc& d = desc[p];
+  // column-panel major: the tiles that share a B column panel run back to back
   const int t = blockIdx.x - begin[p];
-  const int mt = t / d.tn, nt = t % d.tn;
+  const int mt = t % d.tm, nt = t / d.tm;
   const int m0 = mt * TB, n0 = nt * TB;
   __shared__ __attribute__((aligned(16))) float lds[4 * CHUNK];
   Quad q;
@@ -100,7 +103,12 @@ extern "C" kfac_status kfac_precondition(int32_t count, const int32_t* d_g, cons
   size_t f = 0;
   for (int l = 0; l < count; ++l) f += size_t(d_g[l]) * d_a[l];
   float* tt = cv.take<float>(f);
-  std::vector<GemmDesc> g1(count), g2(count);
+  // Problems go in decreasing K (longest tiles first), each launch in its own order.
+  std::vector<int> o1(count), o2(count);
+  for (int l = 0; l < count; ++l) o1[l] = o2[l] = l;
+  std::stable_sort(o1.begin(), o1.end(), [&](int a, int b) { return d_g[a] > d_g[b]; });
+  std::stable_sort(o2.begin(), o2.end(), [&](int a, int b) { return d_a[a] > d_a[b]; });
+  std::vector<GemmDesc> x1(count), x2(count), g1(count), g2(count);
   std::vector<int32_t> e1(count), e2(count);
   int64_t n1 = 0, n2 = 0;
   size_t off = 0;
@@ -114,18 +122,22 @@ extern "C" kfac_status kfac_precondition(int32_t count, const int32_t* d_g, cons
     x.lda = G; x.ldb = A; x.ldc = G;
     x.b_f16 = grad_dtype == KFAC_F16; x.c_trans = 1;
     x.tm = (G + TB - 1) / TB; x.tn = (A + TB - 1) / TB;
-    g1[l] = x;
-    e1[l] = static_cast<int32_t>(n1);
-    n1 += int64_t(x.tm) * x.tn;
+    x1[l] = x;
     GemmDesc y{};
     y.A = T; y.B = A_inv[l]; y.C = out[l];
     y.M = G; y.N = A; y.K = A;
     y.lda = G; y.ldb = A; y.ldc = A;
     y.b_f16 = 0; y.c_trans = 0;
     y.tm = x.tm; y.tn = x.tn;
-    g2[l] = y;
-    e2[l] = static_cast<int32_t>(n2);
-    n2 += int64_t(y.tm) * y.tn;
+    x2[l] = y;
+  }
+  for (int q = 0; q < count; ++q) {
+    g1[q] = x1[o1[q]];
+    e1[q] = static_cast<int32_t>(n1);
+    n1 += int64_t(g1[q].tm) * g1[q].tn;
+    g2[q] = x2[o2[q]];
+    e2[q] = static_cast<int32_t>(n2);
+    n2 += int64_t(g2[q].tm) * g2[q].tn;
   }
   if (n1 >= (int64_t(1) << 31)) return fail(KFAC_ERR_INVALID, "too many tiles");
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -21,6 +21,10 @@ constexpr int LDP = TB + 4;   // LDS pitch of staged chunks [k][m] (floats, 16-b
 constexpr int LDT = TB + 1;   // pitch of full 128x128 LDS tiles used outside the engine
 constexpr int CHUNK = KT * LDP;  // floats per staged operand chunk
 
+// Thread index within the 256-thread engine group: blocks of 512 threads run two
+// engines side by side (threads 0..255 and 256..511).
+__device__ __forceinline__ int etid() { return threadIdx.x & 255; }
+
 struct Quad {
   v16f c[2][2];
 };
@@ -65,7 +69,7 @@ __device__ inline Operand op_cols(const float* src, int64_t ld, int kv, int m0, 
 
 // Thread (kg = tid/32, mg = tid%32) stages k = 4kg..4kg+3 and m = 4mg..4mg+3 of a chunk.
 __device__ inline void op_fetch(const Operand& o, int k0, float4 (&r)[4]) {
-  const int kg = threadIdx.x >> 5, mg = threadIdx.x & 31;
+  const int kg = etid() >> 5, mg = etid() & 31;
   const int m = o.m0 + 4 * mg;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -102,7 +106,7 @@ __device__ inline void op_fetch(const Operand& o, int k0, float4 (&r)[4]) {
 // are row padding: they only reach output rows or columns >= mv, which callers
 // never store.
 __device__ inline void op_fetch_rows4(const Operand& o, int k0, float4 (&r)[4]) {
-  const int kg = threadIdx.x >> 5, mg = threadIdx.x & 31;
+  const int kg = etid() >> 5, mg = etid() & 31;
   const int m = o.m0 + 4 * mg;
   const KG float* base = gp(static_cast<const float*>(o.src)) + m;
 #pragma unroll
@@ -121,7 +125,7 @@ __device__ inline void fetch(const Operand& o, int k0, float4 (&r)[4]) {
 }
 
 __device__ inline void op_store(float* lds, const float4 (&r)[4]) {
-  const int kg = threadIdx.x >> 5, mg = threadIdx.x & 31;
+  const int kg = etid() >> 5, mg = etid() & 31;
 #pragma unroll
   for (int q = 0; q < 4; ++q) *reinterpret_cast<float4*>(lds + (4 * kg + q) * LDP + 4 * mg) = r[q];
 }
@@ -129,7 +133,7 @@ __device__ inline void op_store(float* lds, const float4 (&r)[4]) {
 // acc += sign * As^T Bs over one staged chunk (KT values of k), pitches in floats.
 __device__ inline void quad_mma_p(Quad& q, const float* As, int apitch, const float* Bs, int bpitch,
                                   float sign) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = etid() & 63, wave = etid() >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int ml = lane & 31, kh = lane >> 5;
 #pragma unroll 8
@@ -211,7 +215,7 @@ __device__ inline void quad_gemm_lds_b(Quad& q, const Operand& A, const float* B
 
 // Tile <-> global (row-major, leading dimension ld), rows < rvalid, cols < cvalid.
 __device__ inline void quad_load(Quad& q, const float* src, int64_t ld, int rvalid, int cvalid) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = etid() & 63, wave = etid() >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   if (rvalid >= TB && cvalid >= TB) {  // interior tile: no per-element checks
     const KG float* s = gp(src) + int64_t(quad_row(wm, 0, 0, lane)) * ld + quad_col(wn, 0, lane);
@@ -237,7 +241,7 @@ __device__ inline void quad_load(Quad& q, const float* src, int64_t ld, int rval
 
 // q += tile loaded from global.
 __device__ inline void quad_add_global(Quad& q, const float* src, int64_t ld, int rvalid, int cvalid) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = etid() & 63, wave = etid() >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 #pragma unroll
   for (int a = 0; a < 2; ++a)
@@ -252,7 +256,7 @@ __device__ inline void quad_add_global(Quad& q, const float* src, int64_t ld, in
 
 __device__ inline void quad_store(const Quad& q, float* dst, int64_t ld, int rvalid, int cvalid,
                                   float scale = 1.f) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = etid() & 63, wave = etid() >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   if (rvalid >= TB && cvalid >= TB) {  // interior tile
     KG float* o = gp(dst) + int64_t(quad_row(wm, 0, 0, lane)) * ld + quad_col(wn, 0, lane);
@@ -278,7 +282,7 @@ __device__ inline void quad_store(const Quad& q, float* dst, int64_t ld, int rva
 
 // Upper-triangle store of a square tile: entries r <= c < nvalid.
 __device__ inline void quad_store_upper(const Quad& q, float* dst, int64_t ld, int nvalid) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = etid() & 63, wave = etid() >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 #pragma unroll
   for (int a = 0; a < 2; ++a)
@@ -292,10 +296,10 @@ __device__ inline void quad_store_upper(const Quad& q, float* dst, int64_t ld, i
 }
 
 // Transposed store through LDS (coalesced): dst[c*ld + r] = tile[r][c] for r < rvalid,
-// c < cvalid. lds needs TB*LDT floats; ends with a barrier.
+// c < cvalid. lds needs TB*LDT floats; ends with a barrier (256-thread blocks only).
 __device__ inline void quad_store_t(const Quad& q, float* dst, int64_t ld, int rvalid, int cvalid,
                                     float* lds) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = etid() & 63, wave = etid() >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 #pragma unroll
   for (int a = 0; a < 2; ++a)
@@ -305,7 +309,7 @@ __device__ inline void quad_store_t(const Quad& q, float* dst, int64_t ld, int r
       for (int e = 0; e < 16; ++e)
         lds[quad_col(wn, b, lane) * LDT + quad_row(wm, a, e, lane)] = q.c[a][b][e];
   __syncthreads();
-  for (int e = threadIdx.x; e < TB * TB; e += 256) {
+  for (int e = etid(); e < TB * TB; e += 256) {
     const int c = e / TB, r = e % TB;  // output row c, column r: contiguous in r
     if (r < rvalid && c < cvalid) gp(dst)[int64_t(c) * ld + r] = lds[c * LDT + r];
   }
@@ -314,7 +318,7 @@ __device__ inline void quad_store_t(const Quad& q, float* dst, int64_t ld, int r
 
 // Tile -> LDS [TB][pitch] (rows r, columns c), all 128x128 entries.
 __device__ inline void quad_to_lds(const Quad& q, float* lds, int pitch) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = etid() & 63, wave = etid() >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 #pragma unroll
   for (int a = 0; a < 2; ++a)
