@@ -86,7 +86,7 @@ __global__ void __launch_bounds__(256) inv_prep_kernel(const InvDesc* __restrict
 // by 0 and then subtracts u_i r with u_i = r_i. The columns are taken in four
 // sub-steps J of 32 (block indices I, K in 0..3):
 //   a: wave 0 runs the 32 scalar steps on the diagonal block M_JJ in registers
-//      (one column per lane, pivot-row values by readlane), giving U_JJ and E_JJ;
+//      (pivot rows broadcast through LDS), giving U_JJ and E_JJ;
 //   b: the rest of block row J is multiplied by E_JJ (MFMA): M_JK <- E_JJ M_JK,
 //      which makes U_JK (K > J) and E_JK (K < J);
 //   c: every later block row I > J subtracts M_JI^T times block row J, on the
@@ -119,136 +119,226 @@ __device__ __forceinline__ float lane_bcast(float v, int src_lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src_lane));
 }
 
-// Scalar steps on the 32x32 diagonal block at blk (pitch MLD) by one wave: lane j
-// (and its copy j + 32) holds column j, rows 0..31, so the row of every update is
-// known at compile time. In step c lane j's row-c entry becomes r_j and the later
-// rows t take -r_t r_j (after clearing column c), with r_t read from lane t. Writes
-// the block back, E_JJ to ej (rows, lower with diagonal) and ejt (its transpose),
-// U_cc to diagU; returns the first 1-based failing step or 0.
-__device__ __forceinline__ int chol32(float* blk, float* ej, float* ejt, float* diagU, int lane) {
-  const int j = lane & 31;
-  float d[SB];
+// Scalar steps on the 32x32 diagonal block at blk (pitch MLD) by one wave: lane
+// j + 32h holds rows t = 2q + h (q = 0..15) of column j, so both halves of the
+// wave share every step's work. Publishing row c: the lanes holding it scale it
+// into the pivot row r (diagonal entry p^-1/2 = E_cc) and write it to LDS split by
+// row parity (urow[t & 1][t >> 1] = r_t). Step c: with its column's r_j and the
+// r_t of its rows, a lane updates the rows t > c (column c cleared, then
+// M_tj -= r_t r_j). Row c+1 is updated and published first, and the broadcast of
+// step c+1 is read before the remaining rows of step c are updated, so LDS latency
+// overlaps arithmetic (LDS operations of one wave complete in order). Writes the
+// block back, E_JJ to ej (rows, lower with diagonal) and its transpose to ejt and
+// to uil (pitch MLD), U_cc to diagU; returns the first 1-based failing step or 0.
+__device__ __forceinline__ int chol32(float* blk, float* ej, float* ejt, float* uil, float* diagU,
+                                      float (*urow)[SB / 2], int lane) {
+  const int j = lane & 31, h = lane >> 5;
+  float d[SB / 2];
 #pragma unroll
-  for (int t = 0; t < SB; ++t) d[t] = blk[t * MLD + j];
+  for (int q = 0; q < SB / 2; ++q) d[q] = blk[(2 * q + h) * MLD + j];
   int failed = 0;
   float ujj = 0.f;
-#pragma unroll
-  for (int c = 0; c < SB; ++c) {
-    const float p = lane_bcast(d[c], c);
+  auto publish = [&](int c) {  // row c is final: scale it into the pivot row
+    const int hc = c & 1, qc = c >> 1;
+    const float p = lane_bcast(d[qc], c + 32 * hc);
     if (failed == 0 && !(p > 0.f && isfinite(p))) failed = c + 1;
     const float rs = rsqrtf(p);
-    const bool jc = j == c;
-    const float rj = jc ? rs : d[c] * rs;  // scaled pivot row; its diagonal is E_cc
-    if (jc) ujj = p * rs;
-    d[c] = rj;
+    if (h == hc) {
+      const bool jc = j == c;
+      const float r = jc ? rs : d[qc] * rs;
+      if (jc) ujj = p * rs;
+      d[qc] = r;
+      urow[j & 1][j >> 1] = r;
+    }
+  };
+  auto fetch = [&](float& rj, float (&u)[SB / 2]) {
+    rj = urow[j & 1][j >> 1];
 #pragma unroll
-    for (int t = c + 1; t < SB; ++t) {
-      const float u = lane_bcast(rj, t);  // r_t
-      d[t] = fmaf(-u, rj, jc ? 0.f : d[t]);
+    for (int v = 0; v < 4; ++v) {
+      const float4 x = reinterpret_cast<const float4*>(urow[h])[v];
+      u[4 * v] = x.x; u[4 * v + 1] = x.y; u[4 * v + 2] = x.z; u[4 * v + 3] = x.w;
+    }
+  };
+  float rj, u[SB / 2];
+  publish(0);
+  __builtin_amdgcn_wave_barrier();
+  fetch(rj, u);
+#pragma unroll
+  for (int c = 0; c < SB; ++c) {
+    if (c + 1 < SB) {
+      const bool jc = j == c;
+      const int q1 = (c + 1) >> 1, h1 = (c + 1) & 1;
+      if (h == h1) d[q1] = fmaf(-u[q1], rj, jc ? 0.f : d[q1]);  // row c+1
+      __builtin_amdgcn_wave_barrier();
+      publish(c + 1);
+      __builtin_amdgcn_wave_barrier();
+      float rj2, u2[SB / 2];
+      fetch(rj2, u2);  // step c+1's broadcast, in flight during the rest of step c
+      __builtin_amdgcn_wave_barrier();
+      if (c & 1) {  // slot q1 of the other half holds row c+2
+        if (h == 1) d[q1] = fmaf(-u[q1], rj, jc ? 0.f : d[q1]);
+      }
+#pragma unroll
+      for (int q = q1 + 1; q < SB / 2; ++q) d[q] = fmaf(-u[q], rj, jc ? 0.f : d[q]);
+      rj = rj2;
+#pragma unroll
+      for (int q = 0; q < SB / 2; ++q) u[q] = u2[q];
     }
   }
-  if (lane < SB) {
-    diagU[j] = ujj;
+  if (h == (j & 1)) diagU[j] = ujj;
 #pragma unroll
-    for (int t = 0; t < SB; ++t) {
-      blk[t * MLD + j] = d[t];
-      const float e = j <= t ? d[t] : 0.f;  // E_JJ[t][j]
-      ej[t * ELD + j] = e;
-      ejt[j * ELD + t] = e;
-    }
+  for (int q = 0; q < SB / 2; ++q) {
+    const int t = 2 * q + h;
+    blk[t * MLD + j] = d[q];
+    const float e = j <= t ? d[q] : 0.f;  // E_JJ[t][j]
+    ej[t * ELD + j] = e;
+    ejt[j * ELD + t] = e;
+    uil[j * MLD + t] = e;
   }
   return failed;
 }
 
+// Pivot of step k. Sub-step J runs, after barriers: A (wave 0 factors the diagonal
+// block while waves 1..7 finish sub-step J-1's updates outside block row J),
+// B (block row J times E_JJ), C (sub-step J's update of the next diagonal block
+// only, which A of J+1 needs first).
 __global__ void __launch_bounds__(PT) inv_pivot_kernel(const InvDesc* __restrict__ desc, int k) {
   const InvDesc& d = desc[blockIdx.x];
   const int n = d.n, k0 = k * TB, bk = min(TB, n - k0);
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, scalar
   __shared__ __attribute__((aligned(16))) float M[TB * MLD];
-  __shared__ __attribute__((aligned(16))) float EJ[SB * ELD], EJT[SB * ELD];
+  __shared__ __attribute__((aligned(16))) float PL[TB * MLD];  // U^-1 = E^T, then P^-1
+  __shared__ __attribute__((aligned(16))) float EJ[2][SB * ELD], EJT[2][SB * ELD];
+  __shared__ __attribute__((aligned(16))) float urow[2][SB / 2];
   __shared__ float diagU[TB];
 
-  for (int e = tid; e < TB * TB; e += PT) {
-    const int i = e / TB, j = e % TB;
-    float v = 0.f;
-    if (i <= j) v = j < bk ? gp(d.S)[int64_t(k0 + i) * n + k0 + j] : (i == j ? 1.f : 0.f);
-    M[i * MLD + j] = v;
+  {  // thread: column tid % 128, rows tid / 128 + 4q; all 32 loads in flight first
+    const int j = tid & (TB - 1), r0 = tid >> 7;
+    const KG float* src = gp(d.S) + int64_t(k0) * n + k0 + j;
+    float v[TB / 4];
+#pragma unroll
+    for (int q = 0; q < TB / 4; ++q) {
+      const int i = r0 + 4 * q;
+      v[q] = (i <= j && j < bk) ? src[int64_t(i) * n] : (i == j ? 1.f : 0.f);
+    }
+#pragma unroll
+    for (int q = 0; q < TB / 4; ++q) M[(r0 + 4 * q) * MLD + j] = v[q];
   }
+  for (int e = tid; e < TB * TB / 4; e += PT)
+    *reinterpret_cast<float4*>(PL + (e >> 5) * MLD + 4 * (e & 31)) = make_float4(0.f, 0.f, 0.f, 0.f);
   __syncthreads();
+
+  // one 32x32 block of sub-step J's trailing update: (I, K) -= M_JI^T B_K, with
+  // B_K = M_JK, or E_JJ for K = J (the block starting from zero)
+  auto update_block = [&](int J, int I, int K) {
+    const float* rowJ = M + J * SB * MLD;
+    float* C = M + I * SB * MLD + K * SB;
+    v16f acc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = K == J ? 0.f : C[acc_row(e, lane) * MLD + (lane & 31)];
+    const float* B = K == J ? EJ[J & 1] : rowJ + K * SB;
+    mma32(acc, rowJ + I * SB, MLD, B, K == J ? ELD : MLD, -1.f, lane);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) C[acc_row(e, lane) * MLD + (lane & 31)] = acc[e];
+  };
   int failed = 0;
   for (int J = 0; J < TB / SB; ++J) {
     float* rowJ = M + J * SB * MLD;
     if (w == 0) {
-      const int f = chol32(rowJ + J * SB, EJ, EJT, diagU + J * SB, lane);
+      const int f = chol32(rowJ + J * SB, EJ[J & 1], EJT[J & 1], PL + J * SB * MLD + J * SB, diagU + J * SB,
+                           urow, lane);
       if (failed == 0 && f) failed = J * SB + f;
+    } else if (J > 0) {
+      // the rest of sub-step J-1's update: blocks (I, K), I > J-1, (K <= J-1 or
+      // I <= K), other than (J, J)
+      const int P = J - 1;
+      int q = 0;
+      for (int I = J; I < TB / SB; ++I)
+        for (int K = 0; K < TB / SB; ++K) {
+          if ((K > P && I > K) || (I == J && K == J)) continue;
+          if (q++ % 7 == w - 1) update_block(P, I, K);
+        }
     }
     __syncthreads();
-    if (w < 3) {  // b: M_JK <- E_JJ M_JK for the three K != J
+    if (w < 3) {  // B: M_JK <- E_JJ M_JK for the three K != J
       const int K = w < J ? w : w + 1;
       float* X = rowJ + K * SB;
       v16f acc;
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[e] = 0.f;
-      mma32(acc, EJT, ELD, X, MLD, 1.f, lane);  // sum_p E_JJ[m][p] X[p][n]
+      mma32(acc, EJT[J & 1], ELD, X, MLD, 1.f, lane);  // sum_p E_JJ[m][p] X[p][n]
 #pragma unroll
       for (int e = 0; e < 16; ++e) X[acc_row(e, lane) * MLD + (lane & 31)] = acc[e];
+      if (K < J) {  // E_JK is final: its transpose is block (K, J) of U^-1
+#pragma unroll
+        for (int e = 0; e < 16; ++e) PL[(K * SB + (lane & 31)) * MLD + J * SB + acc_row(e, lane)] = acc[e];
+      }
     }
     __syncthreads();
-    // c: blocks (I, K) with I > J and (K <= J or I <= K), in a fixed order
-    int q = 0;
-    for (int I = J + 1; I < TB / SB; ++I)
-      for (int K = 0; K < TB / SB; ++K) {
-        if (K > J && I > K) continue;
-        if ((q++ & 7) != w) continue;
-        float* C = M + I * SB * MLD + K * SB;
-        v16f acc;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[e] = K == J ? 0.f : C[acc_row(e, lane) * MLD + (lane & 31)];
-        const float* B = K == J ? EJ : rowJ + K * SB;
-        mma32(acc, rowJ + I * SB, MLD, B, K == J ? ELD : MLD, -1.f, lane);
-#pragma unroll
-        for (int e = 0; e < 16; ++e) C[acc_row(e, lane) * MLD + (lane & 31)] = acc[e];
-      }
-    __syncthreads();
+    if (J + 1 < TB / SB) {
+      if (w == 0) update_block(J, J + 1, J + 1);  // C: what A of J+1 needs first
+      __syncthreads();
+    }
   }
-  // U (strict upper of M, diagonal from diagU) into chol; then keep only E in M
+  // U (strict upper of M, diagonal from diagU) into chol
   if (d.chol)
     for (int e = tid; e < TB * TB; e += PT) {
       const int i = e / TB, j = e % TB;
       if (i <= j && j < bk) gp(d.chol)[int64_t(k0 + i) * n + k0 + j] = i == j ? diagU[i] : M[i * MLD + j];
     }
   __syncthreads();
-  for (int e = tid; e < TB * TB; e += PT) {
-    const int i = e / TB, j = e % TB;
-    if (i < j) M[i * MLD + j] = 0.f;
+  // M <- E (zero above the diagonal), E and U^-1 to the workspace (16-byte stores)
+  for (int e = tid; e < TB * TB / 4; e += PT) {
+    const int i = e >> 5, j = 4 * (e & 31);
+    float4 x = *reinterpret_cast<const float4*>(M + i * MLD + j);
+    if (j > i) x.x = 0.f;
+    if (j + 1 > i) x.y = 0.f;
+    if (j + 2 > i) x.z = 0.f;
+    if (j + 3 > i) x.w = 0.f;
+    *reinterpret_cast<float4*>(M + i * MLD + j) = x;
+    *reinterpret_cast<KG v4f*>(gp(d.E) + i * TB + j) = v4f{x.x, x.y, x.z, x.w};
+    const float4 y = *reinterpret_cast<const float4*>(PL + i * MLD + j);
+    *reinterpret_cast<KG v4f*>(gp(d.Ui) + i * TB + j) = v4f{y.x, y.y, y.z, y.w};
   }
   __syncthreads();
-  for (int e = tid; e < TB * TB; e += PT) {
-    const int i = e / TB, j = e % TB;
-    gp(d.E)[e] = M[i * MLD + j];
-    gp(d.Ui)[e] = M[j * MLD + i];
-  }
-  // P^-1 = E^T E on MFMA: wave w forms the 32x32 blocks (bi, bj) = (w / 2, 2(w % 2)
-  // .. +1); E is lower triangular, so the sum over p starts at 32 * max(bi, bj).
-  // Written to the workspace (full) and as S_kk = -P^-1 (upper triangle).
+  // P^-1 = E^T E on MFMA, upper 32x32 blocks (bi <= bj) only, mirrored: the sum
+  // over p runs over the 32-row blocks kb >= bj (E is lower triangular). Block
+  // costs 4 - bj, dealt so that no wave has more than 4.
+  {
+    constexpr int kBlocks[8][2] = {{0, -1}, {1, -1}, {4, -1}, {2, 3}, {5, 6}, {7, 8}, {9, -1}, {-1, -1}};
+    constexpr int kBi[10] = {0, 0, 0, 0, 1, 1, 1, 2, 2, 3}, kBj[10] = {0, 1, 2, 3, 1, 2, 3, 2, 3, 3};
 #pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-    const int qq = 2 * w + hh, bi = qq >> 2, bj = qq & 3;
-    v16f acc;
+    for (int hh = 0; hh < 2; ++hh) {
+      const int qq = kBlocks[w][hh];
+      if (qq < 0) continue;
+      const int bi = kBi[qq], bj = kBj[qq];
+      v16f acc;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
-    const int ml = lane & 31, kh = lane >> 5;
-    for (int kk = 32 * max(bi, bj); kk < TB; kk += 2) {
-      const float a = M[(kk + kh) * MLD + 32 * bi + ml];
-      const float b = M[(kk + kh) * MLD + 32 * bj + ml];
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
+      for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+      for (int kb = bj; kb < TB / SB; ++kb)
+        mma32(acc, M + kb * SB * MLD + SB * bi, MLD, M + kb * SB * MLD + SB * bj, MLD, 1.f, lane);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int r = acc_row(e, lane), c = lane & 31;
+        PL[(SB * bi + r) * MLD + SB * bj + c] = acc[e];
+        if (bi != bj) PL[(SB * bj + c) * MLD + SB * bi + r] = acc[e];
+      }
     }
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int i = 32 * bi + acc_row(e, lane), j = 32 * bj + ml;
-      gp(d.P)[i * TB + j] = acc[e];
-      if (i <= j && j < bk) gp(d.S)[int64_t(k0 + i) * n + k0 + j] = -acc[e];
+  }
+  __syncthreads();
+  for (int e = tid; e < TB * TB / 4; e += PT) {
+    const int i = e >> 5, j = 4 * (e & 31);
+    const float4 x = *reinterpret_cast<const float4*>(PL + i * MLD + j);
+    *reinterpret_cast<KG v4f*>(gp(d.P) + i * TB + j) = v4f{x.x, x.y, x.z, x.w};
+  }
+  {  // S_kk = -P^-1, upper triangle, along rows of S
+    const int j = tid & (TB - 1), r0 = tid >> 7;
+    KG float* dst = gp(d.S) + int64_t(k0) * n + k0 + j;
+#pragma unroll 8
+    for (int q = 0; q < TB / 4; ++q) {
+      const int i = r0 + 4 * q;
+      if (i <= j && j < bk) dst[int64_t(i) * n] = -PL[i * MLD + j];
     }
   }
   if (failed && tid == 0 && *gp(d.info) == 0) *gp(d.info) = k0 + failed;
