@@ -407,7 +407,7 @@ __device__ __forceinline__ void update_tile(const InvDesc& d, int ti, int tj, in
   quad_load(q, C, n, bi, bj);
   // panel rows are 16-byte aligned with pitch ldy = n rounded up to 4 (workspace carve-out)
   const float* Y = d.Y + int64_t(kb) * d.ldy;
-  quad_gemm<true>(q, op_rows(Y, d.ldy, ke - kb, i0, n), op_rows(Y, d.ldy, ke - kb, j0, n), ke - kb, -1.f, lds);
+  quad_gemm_buf(q, op_rows(Y, d.ldy, ke - kb, i0, n), op_rows(Y, d.ldy, ke - kb, j0, n), ke - kb, -1.f, lds);
   quad_store(q, C, n, bi, bj);
 }
 

@@ -35,14 +35,12 @@ constexpr int KC32 = 32;          // patch rows per LDS chunk (fp32 path)
 constexpr int LDN32 = ST + 4;     // LDS row pitch in floats (fp32 path)
 
 // LDS operand layout [column m][patch row k] (fp16, pitch LDK = 36 dwords), with
-// the 16-byte group of 8 rows XOR-swizzled by m/16. Without it the transposing
-// 8-byte stores of a wave (16 column groups 8 columns apart x 4 row groups) land on
-// two bank offsets only, since 8 rows of pitch 36 dwords span 288 = 0 mod 32
-// dwords; with it they spread over the banks, and the MFMA operand reads (16
-// consecutive m, one aligned 16-byte group each) stay conflict-free because m/16
-// is constant within such a read group.
+// the 16-byte group of 8 rows XOR-swizzled by (m/8 ^ m/16). A thread stores the 8
+// rows of one column per 16-byte write; of the swizzles measured on gfx950 this one
+// gave the fastest factor pass (transposing stores conflict-free, MFMA operand reads
+// of 16 consecutive m in one aligned 16-byte group each).
 __device__ __forceinline__ int xoff(int m, int k) {
-  return m * LDK + ((((k >> 3) ^ (m >> 4)) & 7) << 3) + (k & 7);
+  return m * LDK + ((((k >> 3) ^ (m >> 3) ^ (m >> 4)) & 7) << 3) + (k & 7);
 }
 
 struct SyrkDesc {
@@ -87,16 +85,16 @@ __device__ inline float x_elem(const SyrkDesc& d, int row, int c) {
 // bounds check. In row mode (G factors, 1x1 stride-1 convolutions) the offset is
 // row*ld and ih0 = iw0 = 0 with H = W = 1.
 struct RowTab {
-  int64_t off[KC];
-  int32_t ih[KC];
-  int32_t iw[KC];
+  int64_t off[2 * KC];
+  int32_t ih[2 * KC];
+  int32_t iw[2 * KC];
 };
 
 constexpr int32_t kNoRow = -(1 << 29);
 
-__device__ inline void fill_rowtab(const SyrkDesc& d, RowTab& t, int r0, int r_end) {
+__device__ inline void fill_rowtab(const SyrkDesc& d, RowTab& t, int r0, int r_end, int rows) {
   const int tid = threadIdx.x;
-  if (tid >= KC) return;
+  if (tid >= rows) return;
   const int row = r0 + tid;
   if (row >= r_end) {
     t.off[tid] = 0;
@@ -201,74 +199,79 @@ __device__ inline void write_bias_direct(const SyrkDesc& d, int ti, int t, float
 }
 
 // Main loop of a tile over patch rows [r_begin, r_end): gathers of the next chunk
-// overlap the MFMAs of the current one. DIAG: one operand (Xa == Xb); VEC: 16-byte
+// overlap the MFMAs of the current one. An off-diagonal tile stages its two operands
+// (row block ti into X0, tj into X1) over chunks of KC rows; a diagonal tile has one
+// operand and stages chunks of 2 KC rows, the first KC in X0 and the rest in X1, so
+// that every thread gathers the same 8 rows x 8 columns in both kinds. VEC: 16-byte
 // buffer-load gathers.
 template <bool DIAG, bool VEC>
-__device__ __forceinline__ void syrk_rows(const SyrkDesc& d, RowTab* tab, _Float16* Xa, _Float16* Xb,
-                                          const ColTab& ca, const ColTab& cb, int r_begin, int r_end,
-                                          bool want_col, v16f (&acc)[2][2], float& colsum) {
+__device__ __forceinline__ void syrk_rows(const SyrkDesc& d, RowTab* tab, _Float16* X0, _Float16* X1,
+                                          const ColTab& ct, int r_begin, int r_end, bool want_col,
+                                          v16f (&acc)[2][2], float& colsum) {
+  constexpr int CK = DIAG ? 2 * KC : KC;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int cg = tid & 15, rg = tid >> 4;
+  // staging: thread = (half op, column group cg of 8, row group rg of 8)
+  const int op = tid >> 7, cg = tid & 15, rg = (tid >> 4) & 7;
+  const int rrow = (DIAG ? op * KC : 0) + rg * 8;
+  _Float16* Xo = op ? X1 : X0;
   // raw buffer over the input tensor (used by the VEC gathers only)
   const __amdgpu_buffer_rsrc_t rsrc =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(d.src), 0, d.nbytes, 0x00020000);
-  auto gather = [&](const RowTab& t, int rr, const ColTab& ct) -> v8h {
+  auto gather = [&](const RowTab& t, int rr) -> v8h {
     if constexpr (VEC) return gather8_vec(rsrc, d, t, rr, ct);
     else return gather8_elem(d, t, rr, ct);
   };
-  fill_rowtab(d, tab[0], r_begin, r_end);
-  __syncthreads();
-  v8h va[4], vb[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    va[q] = gather(tab[0], rg * 4 + q, ca);
-    if constexpr (!DIAG) vb[q] = gather(tab[0], rg * 4 + q, cb);
-  }
-  int c = 0;
-  for (int r0 = r_begin; r0 < r_end; r0 += KC, ++c) {
-    const bool more = r0 + KC < r_end;
-    __syncthreads();  // the previous chunk's LDS operands are consumed
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      v4h w = {va[0][e], va[1][e], va[2][e], va[3][e]};
-      *reinterpret_cast<v4h*>(Xa + xoff(cg * 8 + e, rg * 4)) = w;
-      if constexpr (!DIAG) {
-        v4h u = {vb[0][e], vb[1][e], vb[2][e], vb[3][e]};
-        *reinterpret_cast<v4h*>(Xb + xoff(cg * 8 + e, rg * 4)) = u;
-      }
-    }
-    if (more) fill_rowtab(d, tab[(c + 1) & 1], r0 + KC, r_end);
-    __syncthreads();
-    if (more) {  // next chunk's global loads overlap this chunk's MFMAs
-      const RowTab& tn = tab[(c + 1) & 1];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        va[q] = gather(tn, rg * 4 + q, ca);
-        if constexpr (!DIAG) vb[q] = gather(tn, rg * 4 + q, cb);
-      }
-    }
-    if constexpr (DIAG) {
-      if (want_col) {  // all 64 rows of column tid, in swizzled order
-#pragma unroll
-        for (int k = 0; k < KC; k += 8) {
-          v8h cv = *reinterpret_cast<const v8h*>(Xa + tid * LDK + k);
-#pragma unroll
-          for (int q = 0; q < 8; ++q) colsum += static_cast<float>(cv[q]);
-        }
-      }
-    }
+  auto mma = [&](const _Float16* A, const _Float16* B) {
 #pragma unroll
     for (int ks = 0; ks < KC / 16; ++ks) {
       const int ko = ks * 16 + (lane >> 5) * 8;
-      const v8h a0 = *reinterpret_cast<const v8h*>(Xa + xoff(wm * 64 + (lane & 31), ko));
-      const v8h a1 = *reinterpret_cast<const v8h*>(Xa + xoff(wm * 64 + 32 + (lane & 31), ko));
-      const v8h b0 = *reinterpret_cast<const v8h*>(Xb + xoff(wn * 64 + (lane & 31), ko));
-      const v8h b1 = *reinterpret_cast<const v8h*>(Xb + xoff(wn * 64 + 32 + (lane & 31), ko));
+      const v8h a0 = *reinterpret_cast<const v8h*>(A + xoff(wm * 64 + (lane & 31), ko));
+      const v8h a1 = *reinterpret_cast<const v8h*>(A + xoff(wm * 64 + 32 + (lane & 31), ko));
+      const v8h b0 = *reinterpret_cast<const v8h*>(B + xoff(wn * 64 + (lane & 31), ko));
+      const v8h b1 = *reinterpret_cast<const v8h*>(B + xoff(wn * 64 + 32 + (lane & 31), ko));
       acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0, acc[0][0], 0, 0, 0);
       acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b1, acc[0][1], 0, 0, 0);
       acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b0, acc[1][0], 0, 0, 0);
       acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1, acc[1][1], 0, 0, 0);
+    }
+  };
+  fill_rowtab(d, tab[0], r_begin, r_end, CK);
+  __syncthreads();
+  v8h v[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) v[q] = gather(tab[0], rrow + q);
+  int c = 0;
+  for (int r0 = r_begin; r0 < r_end; r0 += CK, ++c) {
+    const bool more = r0 + CK < r_end;
+    __syncthreads();  // the previous chunk's LDS operands are consumed
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const v8h w = {v[0][e], v[1][e], v[2][e], v[3][e], v[4][e], v[5][e], v[6][e], v[7][e]};
+      *reinterpret_cast<v8h*>(Xo + xoff(cg * 8 + e, rg * 8)) = w;
+    }
+    if (more) fill_rowtab(d, tab[(c + 1) & 1], r0 + CK, r_end, CK);
+    __syncthreads();
+    if (more) {  // next chunk's global loads overlap this chunk's MFMAs
+      const RowTab& tn = tab[(c + 1) & 1];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = gather(tn, rrow + q);
+    }
+    if constexpr (DIAG) {
+      if (want_col) {  // all 2 KC rows of column tid, in swizzled order
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int k = 0; k < KC; k += 8) {
+            v8h cv = *reinterpret_cast<const v8h*>((h ? X1 : X0) + tid * LDK + k);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) colsum += static_cast<float>(cv[q]);
+          }
+      }
+      mma(X0, X0);
+      mma(X1, X1);
+    } else {
+      mma(X0, X1);
     }
   }
 }
@@ -288,16 +291,13 @@ __global__ void __launch_bounds__(256) syrk_f16_kernel(const SyrkDesc* __restric
 
   __shared__ __attribute__((aligned(16))) _Float16 lds[2][ST * LDK];
   __shared__ RowTab tab[2];
-  _Float16* Xa = lds[0];
-  _Float16* Xb = diag ? lds[0] : lds[1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const bool skip = diag && wm > wn;  // quadrant strictly below the diagonal
-  const int cg = tid & 15, rg = tid >> 4;
-  ColTab ca, cb;
-  fill_coltab(d, ti * ST + cg * 8, ca);
-  if (!diag) fill_coltab(d, tj * ST + cg * 8, cb);
+  ColTab ct;  // the 8 columns this thread stages: of row block tj in threads 128.. of an
+              // off-diagonal tile, else of row block ti
+  fill_coltab(d, ((tid >> 7) ? tj : ti) * ST + (tid & 15) * 8, ct);
   const int r_begin = s * d.rows_per_split;
   const int r_end = min(d.R, r_begin + d.rows_per_split);
   const bool want_col = diag && d.bias && tid < ST;
@@ -312,11 +312,11 @@ __global__ void __launch_bounds__(256) syrk_f16_kernel(const SyrkDesc* __restric
   float colsum = 0.f;
   // block-uniform specialisations of the main loop
   if (diag) {
-    if (d.vec) syrk_rows<true, true>(d, tab, Xa, Xb, ca, cb, r_begin, r_end, want_col, acc, colsum);
-    else syrk_rows<true, false>(d, tab, Xa, Xb, ca, cb, r_begin, r_end, want_col, acc, colsum);
+    if (d.vec) syrk_rows<true, true>(d, tab, lds[0], lds[1], ct, r_begin, r_end, want_col, acc, colsum);
+    else syrk_rows<true, false>(d, tab, lds[0], lds[1], ct, r_begin, r_end, want_col, acc, colsum);
   } else {
-    if (d.vec) syrk_rows<false, true>(d, tab, Xa, Xb, ca, cb, r_begin, r_end, want_col, acc, colsum);
-    else syrk_rows<false, false>(d, tab, Xa, Xb, ca, cb, r_begin, r_end, want_col, acc, colsum);
+    if (d.vec) syrk_rows<false, true>(d, tab, lds[0], lds[1], ct, r_begin, r_end, want_col, acc, colsum);
+    else syrk_rows<false, false>(d, tab, lds[0], lds[1], ct, r_begin, r_end, want_col, acc, colsum);
   }
 
   if (d.splits == 1) {
@@ -541,7 +541,7 @@ static void plan_splits(std::vector<SyrkDesc>& ds) {
     if (splits < 1) splits = 1;
     if (splits > 256) splits = 256;
     int64_t rows = (d.R + splits - 1) / splits;
-    rows = (rows + KC - 1) / KC * KC;
+    rows = (rows + 2 * KC - 1) / (2 * KC) * (2 * KC);  // whole chunks of a diagonal tile
     d.rows_per_split = static_cast<int32_t>(rows);
     d.splits = static_cast<int32_t>((d.R + rows - 1) / rows);
   }
