@@ -122,6 +122,19 @@ __device__ inline int xcd_virtual(int b, int grid, int total) {
 }
 inline unsigned xcd_grid(int64_t total) { return static_cast<unsigned>((total + 7) / 8 * 8); }
 
+// Work items split into 8 contiguous segments, one per XCD, chosen by the host so
+// that the segments cost about the same (they differ in item count). Block b runs
+// on XCD b % 8 and takes that segment's item b / 8; a block past its segment's end
+// gets -1. Launch 8 * (longest segment) blocks.
+struct XcdSegs {
+  int32_t begin[8];
+  int32_t len[8];
+};
+__device__ inline int seg_item(int b, const XcdSegs& sg) {
+  const int x = b & 7, slot = b >> 3;
+  return slot < sg.len[x] ? sg.begin[x] + slot : -1;
+}
+
 // Index of the problem owning work item `w`: largest p with begin[p] <= w.
 __device__ inline int find_problem(const int32_t* begin, int count, int w) {
   int lo = 0, hi = count - 1;

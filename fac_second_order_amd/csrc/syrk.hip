@@ -24,23 +24,27 @@
 // range (tiles of one row split share that XCD's L2).
 //
 // fp32 inputs take a plain path (element gathers, v_mfma_f32_32x32x2f32).
+#include <algorithm>
+#include <cmath>
+
 #include "common.hpp"
 
 namespace kfac {
 
 constexpr int ST = 128;           // output tile edge
-constexpr int KC = 64;            // patch rows per LDS chunk (fp16)
-constexpr int LDK = KC + 8;       // LDS row pitch in halves (144 B)
+constexpr int KC = 128;           // patch rows per LDS operand buffer (fp16)
+constexpr int LDK = KC + 8;       // LDS row pitch in halves (272 B)
+constexpr int RPT = KC / 8;       // patch rows each staging thread gathers
 constexpr int KC32 = 32;          // patch rows per LDS chunk (fp32 path)
 constexpr int LDN32 = ST + 4;     // LDS row pitch in floats (fp32 path)
 
-// LDS operand layout [column m][patch row k] (fp16, pitch LDK = 36 dwords), with
+// LDS operand layout [column m][patch row k] (fp16, pitch LDK = 68 dwords), with
 // the 16-byte group of 8 rows XOR-swizzled by (m/8 ^ m/16). A thread stores the 8
 // rows of one column per 16-byte write; of the swizzles measured on gfx950 this one
 // gave the fastest factor pass (transposing stores conflict-free, MFMA operand reads
 // of 16 consecutive m in one aligned 16-byte group each).
 __device__ __forceinline__ int xoff(int m, int k) {
-  return m * LDK + ((((k >> 3) ^ (m >> 3) ^ (m >> 4)) & 7) << 3) + (k & 7);
+  return m * LDK + ((((k >> 3) ^ (m >> 3) ^ (m >> 4)) & 7) << 3) + (k & ~63) + (k & 7);
 }
 
 struct SyrkDesc {
@@ -59,6 +63,7 @@ struct SyrkDesc {
   int32_t ld;
   int32_t nb, nt, splits, rows_per_split;
   float inv_r, r_f;
+  double rhw, rwo;  // 1 / (Ho Wo) and 1 / Wo for the row decode
 };
 
 // Value of X[row][c] (0 outside the image or beyond d_core), any input dtype
@@ -84,6 +89,15 @@ __device__ inline float x_elem(const SyrkDesc& d, int row, int c) {
 // (ih0 = oh*sh - ph, iw0 = ow*sw - pw). Rows past the end get an ih0 that fails every
 // bounds check. In row mode (G factors, 1x1 stride-1 convolutions) the offset is
 // row*ld and ih0 = iw0 = 0 with H = W = 1.
+// n / dv for 0 <= n < 2^31 and dv > 0, with rdv = 1/dv rounded to fp64: the product
+// is within one of the quotient, and one correction step each way makes it exact.
+__device__ __forceinline__ int fast_div(int n, int dv, double rdv) {
+  int q = static_cast<int>(static_cast<double>(n) * rdv);
+  const int r = n - q * dv;
+  q += (r >= dv) - (r < 0);
+  return q;
+}
+
 struct RowTab {
   int64_t off[2 * KC];
   int32_t ih[2 * KC];
@@ -109,9 +123,9 @@ __device__ inline void fill_rowtab(const SyrkDesc& d, RowTab& t, int r0, int r_e
     return;
   }
   const int hw = d.Ho * d.Wo;
-  const int n = row / hw;
+  const int n = fast_div(row, hw, d.rhw);
   const int rem = row - n * hw;
-  const int oh = rem / d.Wo;
+  const int oh = fast_div(rem, d.Wo, d.rwo);
   const int ow = rem - oh * d.Wo;
   const int ih0 = oh * d.sh - d.ph, iw0 = ow * d.sw - d.pw;
   t.off[tid] = ((int64_t(n) * d.H + ih0) * d.W + iw0) * d.C;
@@ -211,9 +225,9 @@ __device__ __forceinline__ void syrk_rows(const SyrkDesc& d, RowTab* tab, _Float
   constexpr int CK = DIAG ? 2 * KC : KC;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  // staging: thread = (half op, column group cg of 8, row group rg of 8)
+  // staging: thread = (half op, column group cg of 8, row group rg of RPT)
   const int op = tid >> 7, cg = tid & 15, rg = (tid >> 4) & 7;
-  const int rrow = (DIAG ? op * KC : 0) + rg * 8;
+  const int rrow = (DIAG ? op * KC : 0) + rg * RPT;
   _Float16* Xo = op ? X1 : X0;
   // raw buffer over the input tensor (used by the VEC gathers only)
   const __amdgpu_buffer_rsrc_t rsrc =
@@ -238,24 +252,37 @@ __device__ __forceinline__ void syrk_rows(const SyrkDesc& d, RowTab* tab, _Float
   };
   fill_rowtab(d, tab[0], r_begin, r_end, CK);
   __syncthreads();
-  v8h v[8];
+  // rows held across the MFMAs: all RPT with 16-byte gathers; the element gathers
+  // (one register per fp16 value in flight) prefetch the first 8 and fetch the rest
+  // after storing them
+  constexpr int NV = VEC ? RPT : 8;
+  v8h v[NV];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) v[q] = gather(tab[0], rrow + q);
+  for (int q = 0; q < NV; ++q) v[q] = gather(tab[0], rrow + q);
   int c = 0;
   for (int r0 = r_begin; r0 < r_end; r0 += CK, ++c) {
     const bool more = r0 + CK < r_end;
     __syncthreads();  // the previous chunk's LDS operands are consumed
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const v8h w = {v[0][e], v[1][e], v[2][e], v[3][e], v[4][e], v[5][e], v[6][e], v[7][e]};
-      *reinterpret_cast<v8h*>(Xo + xoff(cg * 8 + e, rg * 8)) = w;
+    for (int g = 0; g < RPT / 8; ++g) {
+      const int gv = VEC ? g : 0;
+      if (!VEC && g > 0) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[q] = gather(tab[c & 1], rrow + 8 * g + q);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const v8h w = {v[8 * gv][e],     v[8 * gv + 1][e], v[8 * gv + 2][e], v[8 * gv + 3][e],
+                       v[8 * gv + 4][e], v[8 * gv + 5][e], v[8 * gv + 6][e], v[8 * gv + 7][e]};
+        *reinterpret_cast<v8h*>(Xo + xoff(cg * 8 + e, rg * RPT + 8 * g)) = w;
+      }
     }
     if (more) fill_rowtab(d, tab[(c + 1) & 1], r0 + CK, r_end, CK);
     __syncthreads();
     if (more) {  // next chunk's global loads overlap this chunk's MFMAs
       const RowTab& tn = tab[(c + 1) & 1];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) v[q] = gather(tn, rrow + q);
+      for (int q = 0; q < NV; ++q) v[q] = gather(tn, rrow + q);
     }
     if constexpr (DIAG) {
       if (want_col) {  // all 2 KC rows of column tid, in swizzled order
@@ -278,8 +305,8 @@ __device__ __forceinline__ void syrk_rows(const SyrkDesc& d, RowTab* tab, _Float
 
 __global__ void __launch_bounds__(256) syrk_f16_kernel(const SyrkDesc* __restrict__ desc,
                                                        const int32_t* __restrict__ begin,
-                                                       int count, int total, float decay) {
-  const int v = xcd_virtual(blockIdx.x, gridDim.x, total);
+                                                       int count, XcdSegs segs, float decay) {
+  const int v = seg_item(blockIdx.x, segs);
   if (v < 0) return;
   const int p = find_problem(begin, count, v);
   const SyrkDesc& d = desc[p];
@@ -357,8 +384,8 @@ __global__ void __launch_bounds__(256) syrk_f16_kernel(const SyrkDesc* __restric
 // fp32 inputs: element gathers into LDS laid out [k][column], fp32 MFMA.
 __global__ void __launch_bounds__(256) syrk_f32_kernel(const SyrkDesc* __restrict__ desc,
                                                        const int32_t* __restrict__ begin,
-                                                       int count, int total, float decay) {
-  const int v = xcd_virtual(blockIdx.x, gridDim.x, total);
+                                                       int count, XcdSegs segs, float decay) {
+  const int v = seg_item(blockIdx.x, segs);
   if (v < 0) return;
   const int p = find_problem(begin, count, v);
   const SyrkDesc& d = desc[p];
@@ -496,6 +523,8 @@ struct SyrkPlan {
   std::vector<int32_t> rbegin, rprob;  // reduce tiles of split problems
   int64_t items = 0, ritems = 0;
   size_t partial_floats = 0;
+  XcdSegs segs{};
+  int64_t seg_max = 0;               // longest XCD segment (items)
 };
 
 // One factor problem from a layer (which = 0: A, 1: G).
@@ -505,6 +534,8 @@ static SyrkDesc make_problem(const kfac_layer& L, int which) {
   if (which == 0) {
     d.mode = 1;
     d.H = L.h; d.W = L.w; d.C = L.c_in; d.Ho = L.h_out; d.Wo = L.w_out;
+    d.rhw = 1.0 / static_cast<double>(int64_t(L.h_out) * L.w_out);
+    d.rwo = 1.0 / static_cast<double>(L.w_out);
     d.kh = L.kh; d.kw = L.kw; d.sh = L.sh; d.sw = L.sw; d.ph = L.ph; d.pw = L.pw;
     d.d_core = L.c_in * L.kh * L.kw;
     d.bias = L.bias ? 1 : 0;
@@ -529,14 +560,25 @@ static SyrkDesc make_problem(const kfac_layer& L, int which) {
   return d;
 }
 
-// Row splits: spread the work so that the launch holds several thousand tiles of
-// at least 1024 rows each; the split count of a factor never exceeds 256.
-static void plan_splits(std::vector<SyrkDesc>& ds) {
+// Relative cost of one patch row of one tile: 16-byte gathers (fp16 input whose
+// channel count and d_core are multiples of 8) against element gathers, as measured
+// on gfx950 (about 4x per row).
+static double row_cost(const SyrkDesc& d, kfac_dtype dt) {
+  const int width = d.mode == 1 ? d.C : d.ld;
+  return (dt == KFAC_F16 && width % 8 == 0 && d.d_core % 8 == 0) ? 1.0 : 4.0;
+}
+
+// Row splits: spread the work so that the launch holds several thousand work items
+// (a tile over a range of rows) of about equal cost, and at least 1024 rows each;
+// the split count of a factor never exceeds 256. Equal item costs keep the
+// per-XCD ranges of items (contiguous, equal in count) equal in time.
+static void plan_splits(std::vector<SyrkDesc>& ds, kfac_dtype dt) {
   double work = 0;
-  for (auto& d : ds) work += double(d.nt) * d.R;
-  double per = work / 4096.0;
-  if (per < 1024) per = 1024;
+  for (auto& d : ds) work += double(d.nt) * d.R * row_cost(d, dt);
+  const double per_cost = work / 4096.0;
   for (auto& d : ds) {
+    double per = per_cost / row_cost(d, dt);
+    if (per < 1024) per = 1024;
     int64_t splits = static_cast<int64_t>((d.R + per - 1) / per);
     if (splits < 1) splits = 1;
     if (splits > 256) splits = 256;
@@ -605,7 +647,7 @@ static kfac_status build_plan(const kfac_layer* L, int32_t count, kfac_dtype dt,
   std::vector<SyrkDesc> all;
   for (int l = 0; l < count; ++l)
     for (int which = 0; which < 2; ++which) all.push_back(make_problem(L[l], which));
-  plan_splits(all);
+  plan_splits(all, dt);
   for (int l = 0; l < count; ++l) {
     for (int which = 0; which < 2; ++which) {
       SyrkDesc d = all[2 * l + which];
@@ -628,9 +670,52 @@ static kfac_status build_plan(const kfac_layer* L, int32_t count, kfac_dtype dt,
       pl.desc.push_back(d);
     }
   }
+  // Problems in decreasing cost per item (stable): each problem's items stay together
+  // (its tiles over one row range are neighbours, sharing those rows in L2), and each
+  // XCD segment starts with its longest items.
+  auto item_cost = [&](const SyrkDesc& d) {  // per-row cost as in row_cost, now that vec is known
+    return double(d.rows_per_split) * ((dt == KFAC_F16 && d.vec) ? 1.0 : 4.0);
+  };
+  std::stable_sort(pl.desc.begin(), pl.desc.end(),
+                   [&](const SyrkDesc& a, const SyrkDesc& b) { return item_cost(a) > item_cost(b); });
   finish_plan(pl);
   if (pl.items >= (int64_t(1) << 31) - 8 || pl.ritems >= (int64_t(1) << 31))
     return fail(KFAC_ERR_INVALID, "too many tiles");
+  // XCD segments of about equal cost (rows x per-row cost over the items in order)
+  double total = 0;
+  for (const SyrkDesc& d : pl.desc) total += item_cost(d) * d.nt * (double(d.R) / d.rows_per_split);
+  int64_t item = 0;
+  double acc = 0;
+  int x = 0;
+  pl.segs.begin[0] = 0;
+  for (const SyrkDesc& d : pl.desc) {
+    for (int sp = 0; sp < d.splits; ++sp) {
+      const int rows = std::min(d.rows_per_split, d.R - sp * d.rows_per_split);
+      const double c = item_cost(d) * (double(rows) / d.rows_per_split);
+      int64_t t = 0;
+      while (t < d.nt) {  // a segment starts at the first item reached with acc >= its share
+        int64_t k = d.nt - t;
+        if (x < 7) {
+          const double thr = total * (x + 1) / 8;
+          if (acc >= thr) {
+            pl.segs.begin[++x] = static_cast<int32_t>(item);
+            continue;
+          }
+          k = std::min<int64_t>(k, std::max<int64_t>(1, static_cast<int64_t>(std::ceil((thr - acc) / c))));
+        }
+        acc += double(k) * c;
+        item += k;
+        t += k;
+      }
+    }
+  }
+  while (x < 7) pl.segs.begin[++x] = static_cast<int32_t>(item);
+  pl.seg_max = 0;
+  for (int k = 0; k < 8; ++k) {
+    const int64_t e = k < 7 ? pl.segs.begin[k + 1] : pl.items;
+    pl.segs.len[k] = static_cast<int32_t>(e - pl.segs.begin[k]);
+    pl.seg_max = std::max<int64_t>(pl.seg_max, pl.segs.len[k]);
+  }
   return KFAC_OK;
 }
 
@@ -694,12 +779,11 @@ extern "C" kfac_status kfac_factors(const kfac_layer* layers, int32_t count, kfa
     st = upload(d_rprob, pl.rprob.data(), sizeof(int32_t) * nr, s);
     if (st) return st;
   }
-  const int total = static_cast<int>(pl.items);
-  const unsigned grid = static_cast<unsigned>((total + 7) / 8 * 8);
+  const unsigned grid = static_cast<unsigned>(8 * pl.seg_max);
   if (in_dtype == KFAC_F16) {
-    KFAC_LAUNCH(K_SYRK, syrk_f16_kernel, dim3(grid), dim3(256), 0, s, d_desc, d_begin, np, total, ema_decay);
+    KFAC_LAUNCH(K_SYRK, syrk_f16_kernel, dim3(grid), dim3(256), 0, s, d_desc, d_begin, np, pl.segs, ema_decay);
   } else {
-    KFAC_LAUNCH(K_SYRK, syrk_f32_kernel, dim3(grid), dim3(256), 0, s, d_desc, d_begin, np, total, ema_decay);
+    KFAC_LAUNCH(K_SYRK, syrk_f32_kernel, dim3(grid), dim3(256), 0, s, d_desc, d_begin, np, pl.segs, ema_decay);
   }
   KFAC_CHECK_LAUNCH("syrk kernel");
   if (nr) {

@@ -163,22 +163,37 @@ __device__ inline void op_store(float* lds, const float4 (&r)[4]) {
 }
 
 // acc += sign * As^T Bs over one staged chunk (KT values of k), pitches in floats.
+// The LDS reads run four k-steps ahead of the MFMAs that use them (explicit schedule
+// groups: left to itself the scheduler puts each read right before its MFMAs, which
+// exposes the LDS latency on every k-step).
 __device__ inline void quad_mma_p(Quad& q, const float* As, int apitch, const float* Bs, int bpitch,
                                   float sign) {
   const int lane = etid() & 63, wave = etid() >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int ml = lane & 31, kh = lane >> 5;
-#pragma unroll 8
-  for (int k = 0; k < KT; k += 2) {
-    const float* ar = As + (k + kh) * apitch + wm * 64 + ml;
-    const float* br = Bs + (k + kh) * bpitch + wn * 64 + ml;
-    const float a0 = ar[0] * sign, a1 = ar[32] * sign;
-    const float b0 = br[0], b1 = br[32];
-    q.c[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, q.c[0][0], 0, 0, 0);
-    q.c[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, q.c[0][1], 0, 0, 0);
-    q.c[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, q.c[1][0], 0, 0, 0);
-    q.c[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, q.c[1][1], 0, 0, 0);
+  float a0[KT / 2], a1[KT / 2], b0[KT / 2], b1[KT / 2];
+#pragma unroll
+  for (int t = 0; t < KT / 2; ++t) {
+    const float* ar = As + (2 * t + kh) * apitch + wm * 64 + ml;
+    const float* br = Bs + (2 * t + kh) * bpitch + wn * 64 + ml;
+    a0[t] = ar[0]; a1[t] = ar[32]; b0[t] = br[0]; b1[t] = br[32];
   }
+#pragma unroll
+  for (int t = 0; t < KT / 2; ++t) {
+    const float x0 = a0[t] * sign, x1 = a1[t] * sign;
+    q.c[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(x0, b0[t], q.c[0][0], 0, 0, 0);
+    q.c[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(x0, b1[t], q.c[0][1], 0, 0, 0);
+    q.c[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(x1, b0[t], q.c[1][0], 0, 0, 0);
+    q.c[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(x1, b1[t], q.c[1][1], 0, 0, 0);
+  }
+  // schedule: reads of 4 k-steps ahead, then per k-step 4 MFMAs and the reads of step t+4
+  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+  for (int t = 0; t < KT / 2 - 4; ++t) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
 }
 
 // acc += sign * A^T B over k in [0, K), pipelined. lds holds 4*CHUNK floats
