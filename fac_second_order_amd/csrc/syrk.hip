@@ -99,7 +99,8 @@ __device__ __forceinline__ int fast_div(int n, int dv, double rdv) {
 }
 
 struct RowTab {
-  int64_t off[2 * KC];
+  int32_t lo[2 * KC];  // element offset, low and high 32 bits (the 16-byte gathers,
+  int32_t hi[2 * KC];  // whose tensors stay below 2^31 bytes, read the low half only)
   int32_t ih[2 * KC];
   int32_t iw[2 * KC];
 };
@@ -111,13 +112,16 @@ __device__ inline void fill_rowtab(const SyrkDesc& d, RowTab& t, int r0, int r_e
   if (tid >= rows) return;
   const int row = r0 + tid;
   if (row >= r_end) {
-    t.off[tid] = 0;
+    t.lo[tid] = 0;
+    t.hi[tid] = 0;
     t.ih[tid] = kNoRow;
     t.iw[tid] = 0;
     return;
   }
   if (d.mode == 0) {
-    t.off[tid] = int64_t(row) * d.ld;
+    const int64_t o = int64_t(row) * d.ld;
+    t.lo[tid] = static_cast<int32_t>(o);
+    t.hi[tid] = static_cast<int32_t>(o >> 32);
     t.ih[tid] = 0;
     t.iw[tid] = 0;
     return;
@@ -128,7 +132,9 @@ __device__ inline void fill_rowtab(const SyrkDesc& d, RowTab& t, int r0, int r_e
   const int oh = fast_div(rem, d.Wo, d.rwo);
   const int ow = rem - oh * d.Wo;
   const int ih0 = oh * d.sh - d.ph, iw0 = ow * d.sw - d.pw;
-  t.off[tid] = ((int64_t(n) * d.H + ih0) * d.W + iw0) * d.C;
+  const int64_t o = ((int64_t(n) * d.H + ih0) * d.W + iw0) * d.C;
+  t.lo[tid] = static_cast<int32_t>(o);
+  t.hi[tid] = static_cast<int32_t>(o >> 32);
   t.ih[tid] = ih0;
   t.iw[tid] = iw0;
 }
@@ -169,7 +175,7 @@ __device__ inline void fill_coltab(const SyrkDesc& d, int c0, ColTab& ct) {
 __device__ inline v8h gather8_elem(const SyrkDesc& d, const RowTab& t, int rr, const ColTab& ct) {
   const KG _Float16* src = gp(static_cast<const _Float16*>(d.src));
   const int ih = t.ih[rr], iw = t.iw[rr];
-  const int64_t off = t.off[rr];
+  const int64_t off = (int64_t(t.hi[rr]) << 32) | static_cast<uint32_t>(t.lo[rr]);
   v8h v;
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
@@ -179,16 +185,35 @@ __device__ inline v8h gather8_elem(const SyrkDesc& d, const RowTab& t, int rr, c
   return v;
 }
 
-// The same when the 8 columns share one tap (d.vec): one 16-byte buffer load. A
-// padding tap, a row past the end or columns past d_core get an offset beyond the
-// buffer's range, for which the load returns zeros without touching memory.
-__device__ __forceinline__ v8h gather8_vec(__amdgpu_buffer_rsrc_t rsrc, const SyrkDesc& d, const RowTab& t,
-                                           int rr, const ColTab& ct) {
-  const int ih = t.ih[rr], iw = t.iw[rr];
-  const bool ok = (unsigned(ih + ct.ki[0]) < unsigned(d.H)) & (unsigned(iw + ct.kj[0]) < unsigned(d.W));
-  const unsigned off = static_cast<unsigned>(t.off[rr] + ct.coff[0]) * 2u;
-  const v4u x = __builtin_amdgcn_raw_buffer_load_b128(rsrc, ok ? off : 0x80000000u, 0, 0);
-  return __builtin_bit_cast(v8h, x);
+// The same when the 8 columns share one tap (d.vec), for the N consecutive chunk
+// rows rr0.. at once: one 16-byte buffer load per row. A padding tap, a row past the
+// end or columns past d_core get an offset beyond the buffer's range, for which the
+// load returns zeros without touching memory. All table entries are read before any
+// address is formed (one LDS round trip instead of one per row).
+template <int N>
+__device__ __forceinline__ void gather8_vec(__amdgpu_buffer_rsrc_t rsrc, int H, int W, const RowTab& t,
+                                            int rr0, const ColTab& ct, v8h (&v)[N]) {
+  int lo[N], ih[N], iw[N];
+#pragma unroll
+  for (int q = 0; q < N; q += 4) {
+    const v4i a = *reinterpret_cast<const v4i*>(t.lo + rr0 + q);
+    const v4i b = *reinterpret_cast<const v4i*>(t.ih + rr0 + q);
+    const v4i c = *reinterpret_cast<const v4i*>(t.iw + rr0 + q);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      lo[q + u] = a[u];
+      ih[q + u] = b[u];
+      iw[q + u] = c[u];
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int q = 0; q < N; ++q) {
+    const bool ok = (unsigned(ih[q] + ct.ki[0]) < unsigned(H)) & (unsigned(iw[q] + ct.kj[0]) < unsigned(W));
+    const unsigned off = static_cast<unsigned>(lo[q] + ct.coff[0]) * 2u;
+    const v4u x = __builtin_amdgcn_raw_buffer_load_b128(rsrc, ok ? off : 0x80000000u, 0, 0);
+    v[q] = __builtin_bit_cast(v8h, x);
+  }
 }
 
 __device__ inline float blend(float v, const float* out, int64_t o, float decay) {
@@ -232,9 +257,15 @@ __device__ __forceinline__ void syrk_rows(const SyrkDesc& d, RowTab* tab, _Float
   // raw buffer over the input tensor (used by the VEC gathers only)
   const __amdgpu_buffer_rsrc_t rsrc =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(d.src), 0, d.nbytes, 0x00020000);
-  auto gather = [&](const RowTab& t, int rr) -> v8h {
-    if constexpr (VEC) return gather8_vec(rsrc, d, t, rr, ct);
-    else return gather8_elem(d, t, rr, ct);
+  const int H = d.H, W = d.W;
+  // rows rr0.. of the chunk into v[0 .. NV)
+  auto gather = [&](const RowTab& t, int rr0, v8h(&v)[VEC ? RPT : 8]) {
+    if constexpr (VEC) {
+      gather8_vec<RPT>(rsrc, H, W, t, rr0, ct, v);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = gather8_elem(d, t, rr0 + q, ct);
+    }
   };
   auto mma = [&](const _Float16* A, const _Float16* B) {
 #pragma unroll
@@ -257,8 +288,7 @@ __device__ __forceinline__ void syrk_rows(const SyrkDesc& d, RowTab* tab, _Float
   // after storing them
   constexpr int NV = VEC ? RPT : 8;
   v8h v[NV];
-#pragma unroll
-  for (int q = 0; q < NV; ++q) v[q] = gather(tab[0], rrow + q);
+  gather(tab[0], rrow, v);
   int c = 0;
   for (int r0 = r_begin; r0 < r_end; r0 += CK, ++c) {
     const bool more = r0 + CK < r_end;
@@ -266,10 +296,7 @@ __device__ __forceinline__ void syrk_rows(const SyrkDesc& d, RowTab* tab, _Float
 #pragma unroll
     for (int g = 0; g < RPT / 8; ++g) {
       const int gv = VEC ? g : 0;
-      if (!VEC && g > 0) {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) v[q] = gather(tab[c & 1], rrow + 8 * g + q);
-      }
+      if (!VEC && g > 0) gather(tab[c & 1], rrow + 8 * g, v);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const v8h w = {v[8 * gv][e],     v[8 * gv + 1][e], v[8 * gv + 2][e], v[8 * gv + 3][e],
@@ -280,9 +307,7 @@ __device__ __forceinline__ void syrk_rows(const SyrkDesc& d, RowTab* tab, _Float
     if (more) fill_rowtab(d, tab[(c + 1) & 1], r0 + CK, r_end, CK);
     __syncthreads();
     if (more) {  // next chunk's global loads overlap this chunk's MFMAs
-      const RowTab& tn = tab[(c + 1) & 1];
-#pragma unroll
-      for (int q = 0; q < NV; ++q) v[q] = gather(tn, rrow + q);
+      gather(tab[(c + 1) & 1], rrow, v);
     }
     if constexpr (DIAG) {
       if (want_col) {  // all 2 KC rows of column tid, in swizzled order
