@@ -22,9 +22,11 @@ struct GemmDesc {
   int32_t b_f16;
   int32_t c_trans;
   int32_t tm, tn;  // tiles along M and N
+  int32_t buf;             // both operands below 2^31 bytes: branch-free buffer pipeline
+  int32_t a_mode, b_mode;  // LD_V4 / LD_F32 (fp32 operands) or LD_F16 (B fp16)
 };
 
-__global__ void __launch_bounds__(256) gemm_tn_kernel(const GemmDesc* __restrict__ desc,
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) gemm_tn_kernel(const GemmDesc* __restrict__ desc,
                                                       const int32_t* __restrict__ begin, int count) {
   const int p = find_problem(begin, count, blockIdx.x);
   const GemmDesc& d = desc[p];
@@ -38,10 +40,28 @@ __global__ void __launch_bounds__(256) gemm_tn_kernel(const GemmDesc* __restrict
   const Operand A = op_rows(d.A, d.lda, d.K, m0, d.M);
   const Operand B = d.b_f16 ? op_rows_h(static_cast<const _Float16*>(d.B), d.ldb, d.K, n0, d.N)
                             : op_rows(static_cast<const float*>(d.B), d.ldb, d.K, n0, d.N);
-  quad_gemm(q, A, B, d.K, 1.f, lds);
+  if (d.buf) {  // A in 16-byte groups (checked on the host), B in its own form
+    if (d.b_mode == LD_V4) quad_gemm_buf<LD_V4, LD_V4>(q, A, B, d.K, 1.f, lds);
+    else if (d.b_mode == LD_F32) quad_gemm_buf<LD_V4, LD_F32>(q, A, B, d.K, 1.f, lds);
+    else quad_gemm_buf<LD_V4, LD_F16>(q, A, B, d.K, 1.f, lds);
+  } else {
+    quad_gemm(q, A, B, d.K, 1.f, lds);
+  }
   const int rv = min(TB, d.M - m0), cv = min(TB, d.N - n0);
   if (d.c_trans) quad_store_t(q, d.C + int64_t(n0) * d.ldc + m0, d.ldc, rv, cv, lds);
   else quad_store(q, d.C + int64_t(m0) * d.ldc + n0, d.ldc, rv, cv);
+}
+
+// Load forms of a problem's operands: 16-byte groups for fp32 rows whose pitch is a
+// multiple of 4 floats on a 16-byte aligned base, single elements otherwise. The
+// buffer pipeline takes problems whose operands span less than 2^31 bytes each and
+// whose A operand has 16-byte groups (A is G^-1 or the T^T workspace, pitch d_G).
+static void set_modes(GemmDesc& g, int b_esize) {
+  const int64_t abytes = int64_t(g.K) * g.lda * 4, bbytes = int64_t(g.K) * g.ldb * b_esize;
+  g.a_mode = (g.lda % 4 == 0 && reinterpret_cast<uintptr_t>(g.A) % 16 == 0) ? LD_V4 : LD_F32;
+  g.buf = abytes < (int64_t(1) << 31) && bbytes < (int64_t(1) << 31) && g.a_mode == LD_V4;
+  if (g.b_f16) g.b_mode = LD_F16;
+  else g.b_mode = (g.ldb % 4 == 0 && reinterpret_cast<uintptr_t>(g.B) % 16 == 0) ? LD_V4 : LD_F32;
 }
 
 static size_t precond_ws(int count, const int32_t* dg, const int32_t* da) {
@@ -122,6 +142,7 @@ extern "C" kfac_status kfac_precondition(int32_t count, const int32_t* d_g, cons
     x.lda = G; x.ldb = A; x.ldc = G;
     x.b_f16 = grad_dtype == KFAC_F16; x.c_trans = 1;
     x.tm = (G + TB - 1) / TB; x.tn = (A + TB - 1) / TB;
+    set_modes(x, esize);
     x1[l] = x;
     GemmDesc y{};
     y.A = T; y.B = A_inv[l]; y.C = out[l];
@@ -129,6 +150,7 @@ extern "C" kfac_status kfac_precondition(int32_t count, const int32_t* d_g, cons
     y.lda = G; y.ldb = A; y.ldc = A;
     y.b_f16 = 0; y.c_trans = 0;
     y.tm = x.tm; y.tn = x.tn;
+    set_modes(y, 4);
     x2[l] = y;
   }
   for (int q = 0; q < count; ++q) {

@@ -118,35 +118,60 @@ __device__ inline void op_fetch_rows4(const Operand& o, int k0, float4 (&r)[4]) 
   }
 }
 
-// Raw buffer over rows [0, kv) of a rows-form fp32 operand (callers guarantee
-// kv * ld * 4 < 2^31). The base and size are made wave-uniform explicitly so that the
-// resource lives in scalar registers.
+// Load forms of a rows-form operand in the buffer pipeline: 16-byte groups (fp32 rows
+// as for op_fetch_rows4), single fp32 values, single fp16 values.
+constexpr int LD_V4 = 0, LD_F32 = 1, LD_F16 = 2;
+
+// Raw buffer over rows [0, kv) of a rows-form operand (callers guarantee that
+// kv * ld * element size < 2^31). The base and size are made wave-uniform explicitly
+// so that the resource lives in scalar registers.
+template <int MODE>
 __device__ inline __amdgpu_buffer_rsrc_t op_rsrc(const Operand& o) {
+  constexpr uint32_t es = MODE == LD_F16 ? 2u : 4u;
   const uint64_t a = reinterpret_cast<uint64_t>(o.src);
   const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
   const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
-  const uint32_t bytes = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(o.kv) * static_cast<uint32_t>(o.ld) * 4u);
+  const uint32_t bytes = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(o.kv) * static_cast<uint32_t>(o.ld) * es);
   void* base = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
   return __builtin_amdgcn_make_buffer_rsrc(base, 0, bytes, 0x00020000);
 }
 
-// Branch-free op_fetch_rows4 through a raw buffer: every load is issued, and a load
+// Branch-free staging loads through a raw buffer: every load is issued, and a load
 // outside the operand (k >= kv or m >= mv) gets an offset past the buffer's range, for
 // which it returns zeros without touching memory. With the same number of loads on
 // every path, the wait before an LDS store covers only the chunk being stored.
-__device__ inline void op_fetch_rows4_buf(const Operand& o, __amdgpu_buffer_rsrc_t rs, int k0,
-                                          float4 (&r)[4]) {
+// LD_V4 reads each 4-group starting below mv whole (the rows are padded, as for
+// op_fetch_rows4); the other forms read element by element.
+template <int MODE>
+__device__ inline void op_fetch_buf(const Operand& o, __amdgpu_buffer_rsrc_t rs, int k0, float4 (&r)[4]) {
   const int kg = etid() >> 5, mg = etid() & 31;
   const int m = o.m0 + 4 * mg;
   const int ld = static_cast<int>(o.ld);
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int k = k0 + 4 * kg + q;
-    const bool ok = (k < o.kv) & (m < o.mv);
-    const unsigned off = static_cast<unsigned>(k * ld + m) * 4u;
-    const v4u x = __builtin_amdgcn_raw_buffer_load_b128(rs, ok ? off : 0x80000000u, 0, 0);
-    const v4f f = __builtin_bit_cast(v4f, x);
-    r[q] = make_float4(f.x, f.y, f.z, f.w);
+    const bool rok = k < o.kv;
+    if constexpr (MODE == LD_V4) {
+      const unsigned off = static_cast<unsigned>(k * ld + m) * 4u;
+      const v4u x = __builtin_amdgcn_raw_buffer_load_b128(rs, (rok & (m < o.mv)) ? off : 0x80000000u, 0, 0);
+      const v4f f = __builtin_bit_cast(v4f, x);
+      r[q] = make_float4(f.x, f.y, f.z, f.w);
+    } else {
+      float v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bool ok = rok & (m + u < o.mv);
+        if constexpr (MODE == LD_F32) {
+          const unsigned off = static_cast<unsigned>(k * ld + m + u) * 4u;
+          v[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, ok ? off : 0x80000000u, 0, 0));
+        } else {
+          const unsigned off = static_cast<unsigned>(k * ld + m + u) * 2u;
+          const unsigned short h = __builtin_amdgcn_raw_buffer_load_b16(rs, ok ? off : 0x80000000u, 0, 0);
+          v[u] = static_cast<float>(__builtin_bit_cast(_Float16, h));
+        }
+      }
+      r[q] = make_float4(v[0], v[1], v[2], v[3]);
+    }
   }
 }
 
@@ -241,24 +266,25 @@ __device__ inline void quad_gemm(Quad& q, const Operand& A, const Operand& B, in
   }
 }
 
-// quad_gemm for two rows-form fp32 operands that both qualify for op_fetch_rows4 and
-// span less than 2^31 bytes each. Same pipeline, but every chunk load is issued
-// unconditionally (op_fetch_rows4_buf; chunks past K read as zeros, and K is padded
-// to an even chunk count), so that each LDS store waits only for its own chunk while
-// the next one stays in flight.
+// quad_gemm for two rows-form operands, each spanning less than 2^31 bytes, loaded in
+// the forms MA and MB. Same pipeline, but every chunk load is issued unconditionally
+// (op_fetch_buf; chunks past K read as zeros, and K is padded to an even chunk count),
+// so that each LDS store waits only for its own chunk while the next one stays in
+// flight.
+template <int MA = LD_V4, int MB = LD_V4>
 __device__ inline void quad_gemm_buf(Quad& q, const Operand& A, const Operand& B, int K, float sign,
                                      float* lds) {
   const int npair = (K + 2 * KT - 1) / (2 * KT);
-  const __amdgpu_buffer_rsrc_t rsa = op_rsrc(A), rsb = op_rsrc(B);
+  const __amdgpu_buffer_rsrc_t rsa = op_rsrc<MA>(A), rsb = op_rsrc<MB>(B);
   float4 ra0[4], rb0[4], ra1[4], rb1[4];
-  op_fetch_rows4_buf(A, rsa, 0, ra0);
-  op_fetch_rows4_buf(B, rsb, 0, rb0);
-  op_fetch_rows4_buf(A, rsa, KT, ra1);
-  op_fetch_rows4_buf(B, rsb, KT, rb1);
+  op_fetch_buf<MA>(A, rsa, 0, ra0);
+  op_fetch_buf<MB>(B, rsb, 0, rb0);
+  op_fetch_buf<MA>(A, rsa, KT, ra1);
+  op_fetch_buf<MB>(B, rsb, KT, rb1);
   op_store(lds, ra0);
   op_store(lds + CHUNK, rb0);
-  op_fetch_rows4_buf(A, rsa, 2 * KT, ra0);
-  op_fetch_rows4_buf(B, rsb, 2 * KT, rb0);
+  op_fetch_buf<MA>(A, rsa, 2 * KT, ra0);
+  op_fetch_buf<MB>(B, rsb, 2 * KT, rb0);
   __syncthreads();
   // ra/rb: the stage holding chunk c+1; afterwards it takes chunk c+3
   auto step = [&](int c, float4 (&ra)[4], float4 (&rb)[4]) {
@@ -267,8 +293,8 @@ __device__ inline void quad_gemm_buf(Quad& q, const Operand& A, const Operand& B
     float* nxt = lds + ((c + 1) & 1) * 2 * CHUNK;
     op_store(nxt, ra);
     op_store(nxt + CHUNK, rb);
-    op_fetch_rows4_buf(A, rsa, (c + 3) * KT, ra);
-    op_fetch_rows4_buf(B, rsb, (c + 3) * KT, rb);
+    op_fetch_buf<MA>(A, rsa, (c + 3) * KT, ra);
+    op_fetch_buf<MB>(B, rsb, (c + 3) * KT, rb);
     __syncthreads();
   };
   for (int c = 0; c < 2 * npair; c += 2) {
