@@ -363,15 +363,29 @@ __global__ void __launch_bounds__(PP) inv_panel_kernel(const InvDesc* __restrict
   const int tid = threadIdx.x, grp = tid >> 8;
   __shared__ __attribute__((aligned(16))) float lds[2][2 * CHUNK];
   __shared__ __attribute__((aligned(16))) float Vs[TB * LDP];
-  if (j > k) {
-    for (int e = tid; e < TB * TB; e += PP) {
-      const int r = e / TB, c = e % TB;
-      Vs[r * LDP + c] = (r < bk && c < bj) ? gp(d.S)[int64_t(k0 + r) * n + j0 + c] : 0.f;
-    }
-  } else {  // V[r][c] = S[j0 + c][k0 + r]: read along rows of S, transpose in LDS
-    for (int e = tid; e < TB * TB; e += PP) {
-      const int c = e / TB, r = e % TB;
-      Vs[r * LDP + c] = (r < bk && c < bj) ? gp(d.S)[int64_t(j0 + c) * n + k0 + r] : 0.f;
+  {  // all 32 loads of a thread in flight first (clamped addresses, zero outside)
+    const int lo = tid & (TB - 1), hi0 = tid >> 7;  // along a row of S / first row
+    float v[TB * TB / PP];
+    if (j > k) {  // V[r][c] = S[k0 + r][j0 + c]: thread column c = lo, rows hi0 + 4q
+      const int c = lo;
+#pragma unroll
+      for (int q = 0; q < TB * TB / PP; ++q) {
+        const int r = hi0 + 4 * q;
+        const float x = gp(d.S)[int64_t(k0 + min(r, bk - 1)) * n + j0 + min(c, bj - 1)];
+        v[q] = (r < bk && c < bj) ? x : 0.f;
+      }
+#pragma unroll
+      for (int q = 0; q < TB * TB / PP; ++q) Vs[(hi0 + 4 * q) * LDP + c] = v[q];
+    } else {  // V[r][c] = S[j0 + c][k0 + r]: read along rows of S, transpose in LDS
+      const int r = lo;
+#pragma unroll
+      for (int q = 0; q < TB * TB / PP; ++q) {
+        const int c = hi0 + 4 * q;
+        const float x = gp(d.S)[int64_t(j0 + min(c, bj - 1)) * n + k0 + min(r, bk - 1)];
+        v[q] = (r < bk && c < bj) ? x : 0.f;
+      }
+#pragma unroll
+      for (int q = 0; q < TB * TB / PP; ++q) Vs[r * LDP + hi0 + 4 * q] = v[q];
     }
   }
   __syncthreads();

@@ -303,21 +303,25 @@ __device__ inline void quad_gemm_buf(Quad& q, const Operand& A, const Operand& B
   }
 }
 
-// Same with the B operand already resident in LDS as rows [k][n] (pitch bpitch).
+// Same with the B operand already resident in LDS as rows [k][n] (pitch bpitch), and
+// an A operand of fp32 rows with 16-byte groups spanning less than 2^31 bytes: its
+// chunks come through the branch-free buffer loads (zeros past K), two ahead of the
+// MFMAs (one in LDS, one in registers). Ends with a barrier.
 __device__ inline void quad_gemm_lds_b(Quad& q, const Operand& A, const float* Bl, int bpitch, int K,
                                        float sign, float* lds) {
   const int nchunk = (K + KT - 1) / KT;
+  const __amdgpu_buffer_rsrc_t rs = op_rsrc<LD_V4>(A);
   float4 ra[4];
-  op_fetch(A, 0, ra);
+  op_fetch_buf<LD_V4>(A, rs, 0, ra);
   op_store(lds, ra);
+  op_fetch_buf<LD_V4>(A, rs, KT, ra);
   __syncthreads();
   for (int c = 0; c < nchunk; ++c) {
     float* cur = lds + (c & 1) * CHUNK;
     float* nxt = lds + ((c + 1) & 1) * CHUNK;
-    const bool more = c + 1 < nchunk;
-    if (more) op_fetch(A, (c + 1) * KT, ra);
     quad_mma_p(q, cur, LDP, Bl + c * KT * bpitch, bpitch, sign);
-    if (more) op_store(nxt, ra);
+    op_store(nxt, ra);
+    op_fetch_buf<LD_V4>(A, rs, (c + 2) * KT, ra);
     __syncthreads();
   }
 }
