@@ -413,22 +413,23 @@ __global__ void __launch_bounds__(PP) inv_panel_kernel(const InvDesc* __restrict
 
 // Update of step k: S_ij -= Y_i^T Y_j over the upper 128-tile of row blocks i, j,
 // with rows [kb, ke) of the stacked panel buffer.
+// 512-thread blocks (the oct engine).
 __device__ __forceinline__ void update_tile(const InvDesc& d, int ti, int tj, int kb, int ke, float* lds) {
   const int n = d.n, i0 = ti * TB, j0 = tj * TB;
   const int bi = min(TB, n - i0), bj = min(TB, n - j0);
-  Quad q;
+  Oct o;
   float* C = d.S + int64_t(i0) * n + j0;
-  quad_load(q, C, n, bi, bj);
+  oct_load(o, C, n, bi, bj);
   // panel rows are 16-byte aligned with pitch ldy = n rounded up to 4 (workspace carve-out)
   const float* Y = d.Y + int64_t(kb) * d.ldy;
-  quad_gemm_buf(q, op_rows(Y, d.ldy, ke - kb, i0, n), op_rows(Y, d.ldy, ke - kb, j0, n), ke - kb, -1.f, lds);
-  quad_store(q, C, n, bi, bj);
+  oct_gemm(o, op_rows(Y, d.ldy, ke - kb, i0, n), op_rows(Y, d.ldy, ke - kb, j0, n), ke - kb, -1.f, lds);
+  oct_store(o, C, n, bi, bj);
 }
 
 // Update after step k, or after steps k and k+1 when `pair` is set and the matrix
 // has block k+1: every upper tile outside block row k+1 (k when unpaired) takes the
 // rank-(bk + bk1) product of both steps, tiles in block row k only step k+1's half.
-__global__ void __launch_bounds__(256) inv_update_kernel(const InvDesc* __restrict__ desc,
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) inv_update_kernel(const InvDesc* __restrict__ desc,
                                                          const int32_t* __restrict__ begin,
                                                          int count, int k, int total, int pair) {
   const int v = xcd_virtual(blockIdx.x, gridDim.x, total);
@@ -452,7 +453,7 @@ __global__ void __launch_bounds__(256) inv_update_kernel(const InvDesc* __restri
 
 // Step k's update of block row k+1 before its pivot (paired steps): the tiles
 // (k+1, j) for j != k, stored as upper tiles (min, max).
-__global__ void __launch_bounds__(256) inv_rowupd_kernel(const InvDesc* __restrict__ desc,
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) inv_rowupd_kernel(const InvDesc* __restrict__ desc,
                                                          const int32_t* __restrict__ begin,
                                                          int count, int k) {
   const int p = find_problem(begin, count, blockIdx.x);
@@ -622,7 +623,7 @@ extern "C" kfac_status kfac_invert(int32_t count, const int32_t* n, const float*
   KFAC_CHECK_LAUNCH("inv_prep_kernel");
   auto update = [&](int a, int k, int pair) -> kfac_status {
     const unsigned ut = grid_of(pl.tile_begin, a, tiles_of);
-    KFAC_LAUNCH(K_INV_UPDATE, inv_update_kernel, dim3(xcd_grid(ut)), dim3(256), 0, s, d_desc, d_tile, a, k,
+    KFAC_LAUNCH(K_INV_UPDATE, inv_update_kernel, dim3(xcd_grid(ut)), dim3(512), 0, s, d_desc, d_tile, a, k,
                 static_cast<int>(ut), pair);
     KFAC_CHECK_LAUNCH("inv_update_kernel");
     return KFAC_OK;
@@ -637,7 +638,7 @@ extern "C" kfac_status kfac_invert(int32_t count, const int32_t* n, const float*
     KFAC_CHECK_LAUNCH("inv_panel_kernel");
     if (a1 > 0) {
       const unsigned pg = grid_of(pl.panel_begin, a1, panels_of);
-      KFAC_LAUNCH(K_INV_ROWUPD, inv_rowupd_kernel, dim3(pg), dim3(256), 0, s, d_desc, d_panel, a1, k);
+      KFAC_LAUNCH(K_INV_ROWUPD, inv_rowupd_kernel, dim3(pg), dim3(512), 0, s, d_desc, d_panel, a1, k);
       KFAC_CHECK_LAUNCH("inv_rowupd_kernel");
       KFAC_LAUNCH(K_INV_PIVOT, inv_pivot_kernel, dim3(a1), dim3(PT), 0, s, d_desc, k + 1);
       KFAC_CHECK_LAUNCH("inv_pivot_kernel");

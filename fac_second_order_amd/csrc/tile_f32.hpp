@@ -326,6 +326,149 @@ __device__ inline void quad_gemm_lds_b(Quad& q, const Operand& A, const float* B
   }
 }
 
+// ---- 512-thread variant ("oct"): eight waves share one 128x128 tile, wave w owning
+// rows 32*(w/2) .. +32 and columns 64*(w%2) .. +64 (two 32x32 blocks). With half the
+// accumulators and half the staging per thread, two blocks give every SIMD four waves,
+// so the tile load and store of one block overlap the other block's MFMAs. Same
+// chunking, LDS layout and pipeline as the 256-thread engine.
+struct Oct {
+  v16f c[2];
+};
+
+__device__ inline void oct_zero(Oct& o) {
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o.c[b][e] = 0.f;
+}
+
+__device__ inline int oct_row(int lane, int e) {
+  return 32 * ((threadIdx.x >> 6) >> 1) + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+}
+__device__ inline int oct_col(int lane, int b) { return 64 * ((threadIdx.x >> 6) & 1) + 32 * b + (lane & 31); }
+
+// Tile <-> global (row-major, leading dimension ld), rows < rvalid, cols < cvalid.
+__device__ inline void oct_load(Oct& o, const float* src, int64_t ld, int rvalid, int cvalid) {
+  const int lane = threadIdx.x & 63;
+  if (rvalid >= TB && cvalid >= TB) {
+    const KG float* s = gp(src) + int64_t(oct_row(lane, 0)) * ld + oct_col(lane, 0);
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o.c[b][e] = s[int64_t(8 * (e >> 2) + (e & 3)) * ld + 32 * b];
+    return;
+  }
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int r = oct_row(lane, e), c = oct_col(lane, b);
+      o.c[b][e] = (r < rvalid && c < cvalid) ? gp(src)[int64_t(r) * ld + c] : 0.f;
+    }
+}
+
+__device__ inline void oct_store(const Oct& o, float* dst, int64_t ld, int rvalid, int cvalid) {
+  const int lane = threadIdx.x & 63;
+  if (rvalid >= TB && cvalid >= TB) {
+    KG float* d = gp(dst) + int64_t(oct_row(lane, 0)) * ld + oct_col(lane, 0);
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) d[int64_t(8 * (e >> 2) + (e & 3)) * ld + 32 * b] = o.c[b][e];
+    return;
+  }
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int r = oct_row(lane, e), c = oct_col(lane, b);
+      if (r < rvalid && c < cvalid) gp(dst)[int64_t(r) * ld + c] = o.c[b][e];
+    }
+}
+
+// Staging: thread (kg = tid/32, mg = tid%32) loads k = 2kg, 2kg+1 and m = 4mg..4mg+3
+// of a chunk, branch-free through a raw buffer as op_fetch_buf<LD_V4>.
+__device__ inline void oct_fetch(const Operand& o, __amdgpu_buffer_rsrc_t rs, int k0, float4 (&r)[2]) {
+  const int kg = threadIdx.x >> 5, mg = threadIdx.x & 31;
+  const int m = o.m0 + 4 * mg;
+  const int ld = static_cast<int>(o.ld);
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int k = k0 + 2 * kg + q;
+    const unsigned off = static_cast<unsigned>(k * ld + m) * 4u;
+    const v4u x = __builtin_amdgcn_raw_buffer_load_b128(rs, ((k < o.kv) & (m < o.mv)) ? off : 0x80000000u, 0, 0);
+    const v4f f = __builtin_bit_cast(v4f, x);
+    r[q] = make_float4(f.x, f.y, f.z, f.w);
+  }
+}
+
+__device__ inline void oct_stage(float* lds, const float4 (&r)[2]) {
+  const int kg = threadIdx.x >> 5, mg = threadIdx.x & 31;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) *reinterpret_cast<float4*>(lds + (2 * kg + q) * LDP + 4 * mg) = r[q];
+}
+
+// acc += sign * As^T Bs over one staged chunk, LDS reads four k-steps ahead of the
+// MFMAs (explicit schedule groups, as in quad_mma_p).
+__device__ inline void oct_mma(Oct& o, const float* As, const float* Bs, float sign) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int ml = lane & 31, kh = lane >> 5;
+  float a0[KT / 2], b0[KT / 2], b1[KT / 2];
+#pragma unroll
+  for (int t = 0; t < KT / 2; ++t) {
+    const float* ar = As + (2 * t + kh) * LDP + wm * 32 + ml;
+    const float* br = Bs + (2 * t + kh) * LDP + wn * 64 + ml;
+    a0[t] = ar[0]; b0[t] = br[0]; b1[t] = br[32];
+  }
+#pragma unroll
+  for (int t = 0; t < KT / 2; ++t) {
+    const float x0 = a0[t] * sign;
+    o.c[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(x0, b0[t], o.c[0], 0, 0, 0);
+    o.c[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(x0, b1[t], o.c[1], 0, 0, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+  for (int t = 0; t < KT / 2 - 4; ++t) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+}
+
+// acc += sign * A^T B over k in [0, K) for two rows-form fp32 operands with 16-byte
+// groups, each spanning less than 2^31 bytes: the quad_gemm_buf pipeline (two chunks
+// ahead in registers, double-buffered LDS of 4*CHUNK floats, one barrier per chunk,
+// K padded to an even chunk count with zeros). Ends with a barrier.
+__device__ inline void oct_gemm(Oct& o, const Operand& A, const Operand& B, int K, float sign, float* lds) {
+  const int npair = (K + 2 * KT - 1) / (2 * KT);
+  const __amdgpu_buffer_rsrc_t rsa = op_rsrc<LD_V4>(A), rsb = op_rsrc<LD_V4>(B);
+  float4 ra0[2], rb0[2], ra1[2], rb1[2];
+  oct_fetch(A, rsa, 0, ra0);
+  oct_fetch(B, rsb, 0, rb0);
+  oct_fetch(A, rsa, KT, ra1);
+  oct_fetch(B, rsb, KT, rb1);
+  oct_stage(lds, ra0);
+  oct_stage(lds + CHUNK, rb0);
+  oct_fetch(A, rsa, 2 * KT, ra0);
+  oct_fetch(B, rsb, 2 * KT, rb0);
+  __syncthreads();
+  auto step = [&](int c, float4 (&ra)[2], float4 (&rb)[2]) {
+    const float* cur = lds + (c & 1) * 2 * CHUNK;
+    oct_mma(o, cur, cur + CHUNK, sign);
+    float* nxt = lds + ((c + 1) & 1) * 2 * CHUNK;
+    oct_stage(nxt, ra);
+    oct_stage(nxt + CHUNK, rb);
+    oct_fetch(A, rsa, (c + 3) * KT, ra);
+    oct_fetch(B, rsb, (c + 3) * KT, rb);
+    __syncthreads();
+  };
+  for (int c = 0; c < 2 * npair; c += 2) {
+    step(c, ra1, rb1);
+    step(c + 1, ra0, rb0);
+  }
+}
+
 // Tile <-> global (row-major, leading dimension ld), rows < rvalid, cols < cvalid.
 __device__ inline void quad_load(Quad& q, const float* src, int64_t ld, int rvalid, int cvalid) {
   const int lane = etid() & 63, wave = etid() >> 6;
