@@ -26,7 +26,7 @@ struct GemmDesc {
   int32_t a_mode, b_mode;  // LD_V4 / LD_F32 (fp32 operands) or LD_F16 (B fp16)
 };
 
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) gemm_tn_kernel(const GemmDesc* __restrict__ desc,
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) gemm_tn_kernel(const GemmDesc* __restrict__ desc,
                                                       const int32_t* __restrict__ begin, int count) {
   const int p = find_problem(begin, count, blockIdx.x);
   const GemmDesc& d = desc[p];
@@ -35,21 +35,21 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int mt = t % d.tm, nt = t / d.tm;
   const int m0 = mt * TB, n0 = nt * TB;
   __shared__ __attribute__((aligned(16))) float lds[4 * CHUNK];
-  Quad q;
-  quad_zero(q);
+  Oct q;
+  oct_zero(q);
   const Operand A = op_rows(d.A, d.lda, d.K, m0, d.M);
   const Operand B = d.b_f16 ? op_rows_h(static_cast<const _Float16*>(d.B), d.ldb, d.K, n0, d.N)
                             : op_rows(static_cast<const float*>(d.B), d.ldb, d.K, n0, d.N);
   if (d.buf) {  // A in 16-byte groups (checked on the host), B in its own form
-    if (d.b_mode == LD_V4) quad_gemm_buf<LD_V4, LD_V4>(q, A, B, d.K, 1.f, lds);
-    else if (d.b_mode == LD_F32) quad_gemm_buf<LD_V4, LD_F32>(q, A, B, d.K, 1.f, lds);
-    else quad_gemm_buf<LD_V4, LD_F16>(q, A, B, d.K, 1.f, lds);
+    if (d.b_mode == LD_V4) oct_gemm<LD_V4, LD_V4>(q, A, B, d.K, 1.f, lds);
+    else if (d.b_mode == LD_F32) oct_gemm<LD_V4, LD_F32>(q, A, B, d.K, 1.f, lds);
+    else oct_gemm<LD_V4, LD_F16>(q, A, B, d.K, 1.f, lds);
   } else {
-    quad_gemm(q, A, B, d.K, 1.f, lds);
+    oct_gemm<LD_V4, LD_V4, true>(q, A, B, d.K, 1.f, lds);
   }
   const int rv = min(TB, d.M - m0), cv = min(TB, d.N - n0);
-  if (d.c_trans) quad_store_t(q, d.C + int64_t(n0) * d.ldc + m0, d.ldc, rv, cv, lds);
-  else quad_store(q, d.C + int64_t(m0) * d.ldc + n0, d.ldc, rv, cv);
+  if (d.c_trans) oct_store_t(q, d.C + int64_t(n0) * d.ldc + m0, d.ldc, rv, cv, lds);
+  else oct_store(q, d.C + int64_t(m0) * d.ldc + n0, d.ldc, rv, cv);
 }
 
 // Load forms of a problem's operands: 16-byte groups for fp32 rows whose pitch is a
@@ -167,9 +167,9 @@ extern "C" kfac_status kfac_precondition(int32_t count, const int32_t* d_g, cons
   if ((st = upload(d2, g2.data(), sizeof(GemmDesc) * count, s))) return st;
   if ((st = upload(b1, e1.data(), sizeof(int32_t) * count, s))) return st;
   if ((st = upload(b2, e2.data(), sizeof(int32_t) * count, s))) return st;
-  KFAC_LAUNCH(K_GEMM, gemm_tn_kernel, dim3(static_cast<unsigned>(n1)), dim3(256), 0, s, d1, b1, count);
+  KFAC_LAUNCH(K_GEMM, gemm_tn_kernel, dim3(static_cast<unsigned>(n1)), dim3(512), 0, s, d1, b1, count);
   KFAC_CHECK_LAUNCH("gemm_tn_kernel (G^-1 dW)");
-  KFAC_LAUNCH(K_GEMM, gemm_tn_kernel, dim3(static_cast<unsigned>(n2)), dim3(256), 0, s, d2, b2, count);
+  KFAC_LAUNCH(K_GEMM, gemm_tn_kernel, dim3(static_cast<unsigned>(n2)), dim3(512), 0, s, d2, b2, count);
   KFAC_CHECK_LAUNCH("gemm_tn_kernel (T A^-1)");
   return KFAC_OK;
 }

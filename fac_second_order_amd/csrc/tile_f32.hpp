@@ -386,8 +386,25 @@ __device__ inline void oct_store(const Oct& o, float* dst, int64_t ld, int rvali
     }
 }
 
+// Transposed store through LDS (coalesced): dst[c*ld + r] = tile[r][c] for r < rvalid,
+// c < cvalid. lds needs TB*LDT floats; ends with a barrier.
+__device__ inline void oct_store_t(const Oct& o, float* dst, int64_t ld, int rvalid, int cvalid, float* lds) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) lds[oct_col(lane, b) * LDT + oct_row(lane, e)] = o.c[b][e];
+  __syncthreads();
+  for (int e = threadIdx.x; e < TB * TB; e += 512) {
+    const int c = e / TB, r = e % TB;  // output row c, column r: contiguous in r
+    if (r < rvalid && c < cvalid) gp(dst)[int64_t(c) * ld + r] = lds[c * LDT + r];
+  }
+  __syncthreads();
+}
+
 // Staging: thread (kg = tid/32, mg = tid%32) loads k = 2kg, 2kg+1 and m = 4mg..4mg+3
-// of a chunk, branch-free through a raw buffer as op_fetch_buf<LD_V4>.
+// of a chunk, branch-free through a raw buffer in the load form MODE, as op_fetch_buf.
+template <int MODE = LD_V4>
 __device__ inline void oct_fetch(const Operand& o, __amdgpu_buffer_rsrc_t rs, int k0, float4 (&r)[2]) {
   const int kg = threadIdx.x >> 5, mg = threadIdx.x & 31;
   const int m = o.m0 + 4 * mg;
@@ -395,10 +412,48 @@ __device__ inline void oct_fetch(const Operand& o, __amdgpu_buffer_rsrc_t rs, in
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int k = k0 + 2 * kg + q;
-    const unsigned off = static_cast<unsigned>(k * ld + m) * 4u;
-    const v4u x = __builtin_amdgcn_raw_buffer_load_b128(rs, ((k < o.kv) & (m < o.mv)) ? off : 0x80000000u, 0, 0);
-    const v4f f = __builtin_bit_cast(v4f, x);
-    r[q] = make_float4(f.x, f.y, f.z, f.w);
+    const bool rok = k < o.kv;
+    if constexpr (MODE == LD_V4) {
+      const unsigned off = static_cast<unsigned>(k * ld + m) * 4u;
+      const v4u x = __builtin_amdgcn_raw_buffer_load_b128(rs, (rok & (m < o.mv)) ? off : 0x80000000u, 0, 0);
+      const v4f f = __builtin_bit_cast(v4f, x);
+      r[q] = make_float4(f.x, f.y, f.z, f.w);
+    } else {
+      float v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bool ok = rok & (m + u < o.mv);
+        if constexpr (MODE == LD_F32) {
+          const unsigned off = static_cast<unsigned>(k * ld + m + u) * 4u;
+          v[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, ok ? off : 0x80000000u, 0, 0));
+        } else {
+          const unsigned off = static_cast<unsigned>(k * ld + m + u) * 2u;
+          const unsigned short h = __builtin_amdgcn_raw_buffer_load_b16(rs, ok ? off : 0x80000000u, 0, 0);
+          v[u] = static_cast<float>(__builtin_bit_cast(_Float16, h));
+        }
+      }
+      r[q] = make_float4(v[0], v[1], v[2], v[3]);
+    }
+  }
+}
+
+// The same through plain loads with per-element checks, for operands of any size
+// (rows, fp32 or fp16; no transposed form).
+__device__ inline void oct_fetch_plain(const Operand& o, int k0, float4 (&r)[2]) {
+  const int kg = threadIdx.x >> 5, mg = threadIdx.x & 31;
+  const int m = o.m0 + 4 * mg;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int64_t k = k0 + 2 * kg + q;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    if (k < o.kv) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (m + u < o.mv)
+          v[u] = o.f16 ? static_cast<float>(gp(static_cast<const _Float16*>(o.src))[k * o.ld + m + u])
+                       : gp(static_cast<const float*>(o.src))[k * o.ld + m + u];
+    }
+    r[q] = make_float4(v[0], v[1], v[2], v[3]);
   }
 }
 
@@ -436,22 +491,36 @@ __device__ inline void oct_mma(Oct& o, const float* As, const float* Bs, float s
   __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
 }
 
-// acc += sign * A^T B over k in [0, K) for two rows-form fp32 operands with 16-byte
-// groups, each spanning less than 2^31 bytes: the quad_gemm_buf pipeline (two chunks
-// ahead in registers, double-buffered LDS of 4*CHUNK floats, one barrier per chunk,
-// K padded to an even chunk count with zeros). Ends with a barrier.
+// acc += sign * A^T B over k in [0, K) for two rows-form operands loaded in the forms
+// MA and MB, each spanning less than 2^31 bytes: the quad_gemm_buf pipeline (two
+// chunks ahead in registers, double-buffered LDS of 4*CHUNK floats, one barrier per
+// chunk, K padded to an even chunk count with zeros). With PLAIN, plain loads with
+// per-element checks instead (operands of any size). Ends with a barrier.
+template <int MA = LD_V4, int MB = LD_V4, bool PLAIN = false>
 __device__ inline void oct_gemm(Oct& o, const Operand& A, const Operand& B, int K, float sign, float* lds) {
   const int npair = (K + 2 * KT - 1) / (2 * KT);
-  const __amdgpu_buffer_rsrc_t rsa = op_rsrc<LD_V4>(A), rsb = op_rsrc<LD_V4>(B);
+  // (unused with PLAIN: an empty range)
+  const __amdgpu_buffer_rsrc_t rsa = PLAIN ? __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(A.src), 0, 0, 0x00020000)
+                                           : op_rsrc<MA>(A);
+  const __amdgpu_buffer_rsrc_t rsb = PLAIN ? __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(B.src), 0, 0, 0x00020000)
+                                           : op_rsrc<MB>(B);
+  auto fa = [&](int k0, float4 (&r)[2]) {
+    if constexpr (PLAIN) oct_fetch_plain(A, k0, r);
+    else oct_fetch<MA>(A, rsa, k0, r);
+  };
+  auto fb = [&](int k0, float4 (&r)[2]) {
+    if constexpr (PLAIN) oct_fetch_plain(B, k0, r);
+    else oct_fetch<MB>(B, rsb, k0, r);
+  };
   float4 ra0[2], rb0[2], ra1[2], rb1[2];
-  oct_fetch(A, rsa, 0, ra0);
-  oct_fetch(B, rsb, 0, rb0);
-  oct_fetch(A, rsa, KT, ra1);
-  oct_fetch(B, rsb, KT, rb1);
+  fa(0, ra0);
+  fb(0, rb0);
+  fa(KT, ra1);
+  fb(KT, rb1);
   oct_stage(lds, ra0);
   oct_stage(lds + CHUNK, rb0);
-  oct_fetch(A, rsa, 2 * KT, ra0);
-  oct_fetch(B, rsb, 2 * KT, rb0);
+  fa(2 * KT, ra0);
+  fb(2 * KT, rb0);
   __syncthreads();
   auto step = [&](int c, float4 (&ra)[2], float4 (&rb)[2]) {
     const float* cur = lds + (c & 1) * 2 * CHUNK;
@@ -459,8 +528,8 @@ __device__ inline void oct_gemm(Oct& o, const Operand& A, const Operand& B, int 
     float* nxt = lds + ((c + 1) & 1) * 2 * CHUNK;
     oct_stage(nxt, ra);
     oct_stage(nxt + CHUNK, rb);
-    oct_fetch(A, rsa, (c + 3) * KT, ra);
-    oct_fetch(B, rsb, (c + 3) * KT, rb);
+    fa((c + 3) * KT, ra);
+    fb((c + 3) * KT, rb);
     __syncthreads();
   };
   for (int c = 0; c < 2 * npair; c += 2) {
