@@ -10,6 +10,7 @@ from ._lib import (  # noqa: F401
     kfac_invert_workspace, kfac_invert,
     kfac_precondition_workspace, kfac_precondition,
     kfac_bn_diag_workspace, kfac_bn_diag,
-    kfac_timing_kernels, kfac_kernel_name, kfac_timing_enable, kfac_timing_reset, kfac_timing_read,
+    kfac_timing_kernels, kfac_kernel_name, kfac_timing_enable, kfac_timing_only, kfac_timing_reset,
+    kfac_timing_read,
 )
 from .step import KfacStep  # noqa: F401

@@ -75,6 +75,7 @@ _sig("kfac_bn_diag", _i32, _P(kfac_bn), _i32, _i32, _P(_vp), _P(_vp), _P(_vp), _
 _sig("kfac_timing_kernels", _i32)
 _sig("kfac_kernel_name", _c.c_char_p, _i32)
 _sig("kfac_timing_enable", _i32, _i32)
+_sig("kfac_timing_only", _i32, _i32)
 _sig("kfac_timing_reset", _i32)
 _sig("kfac_timing_read", _i32, _i32, _P(_c.c_double), _P(_c.c_int64))
 
@@ -245,6 +246,11 @@ def kfac_kernel_name(i):
 
 def kfac_timing_enable(on=True):
     _check(_lib.kfac_timing_enable(1 if on else 0), "kfac_timing_enable")
+
+
+def kfac_timing_only(i=-1):
+    """Time only kernel id i (-1: every kernel)."""
+    _check(_lib.kfac_timing_only(int(i)), "kfac_timing_only")
 
 
 def kfac_timing_reset():

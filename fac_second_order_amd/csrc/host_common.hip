@@ -79,6 +79,7 @@ struct TimingRec {
 
 struct TimingState {
   bool on = false;
+  int only = -1;  // the one kernel id timed, or -1 for all
   std::vector<hipEvent_t> pool;
   size_t used = 0;
   std::vector<TimingRec> recs;
@@ -94,7 +95,8 @@ struct TimingState {
 
 static thread_local TimingState g_timing;
 
-TimerScope::TimerScope(int id_, hipStream_t s) : id(id_), stream(s), on(g_timing.on), ev_end(nullptr) {
+TimerScope::TimerScope(int id_, hipStream_t s)
+    : id(id_), stream(s), on(g_timing.on && (g_timing.only < 0 || g_timing.only == id_)), ev_end(nullptr) {
   if (!on) return;
   hipEvent_t st = g_timing.next();
   ev_end = g_timing.next();
@@ -142,6 +144,12 @@ const char* kfac_kernel_name(int32_t id) {
 
 kfac_status kfac_timing_enable(int32_t on) {
   g_timing.on = on != 0;
+  return KFAC_OK;
+}
+
+kfac_status kfac_timing_only(int32_t id) {
+  if (id < -1 || id >= K_COUNT) return fail(KFAC_ERR_INVALID, "kfac_timing_only: id %d out of range", id);
+  g_timing.only = id;
   return KFAC_OK;
 }
 

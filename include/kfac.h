@@ -189,10 +189,14 @@ kfac_status kfac_bn_diag(const kfac_bn* layers, int32_t count, kfac_dtype in_dty
  * kernel id, the summed duration in milliseconds and the number of launches since
  * the last reset. Ids run from 0 to kfac_timing_kernels()-1; kfac_kernel_name(id)
  * names them. Disabled by default; costs nothing when disabled.
+ * kfac_timing_only(id) restricts the bracketing to the kernel id (events on every
+ * launch cost stream time of their own), id = -1 to every kernel again (the
+ * default); ids outside [-1, kfac_timing_kernels()) give KFAC_ERR_INVALID.
  * ------------------------------------------------------------------------- */
 int32_t kfac_timing_kernels(void);
 const char* kfac_kernel_name(int32_t id);
 kfac_status kfac_timing_enable(int32_t on);
+kfac_status kfac_timing_only(int32_t id);
 kfac_status kfac_timing_reset(void);
 kfac_status kfac_timing_read(int32_t id, double* total_ms, int64_t* launches);
 

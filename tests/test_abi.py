@@ -53,6 +53,15 @@ def test_kernel_names(lib):
     assert lib.kfac_kernel_name(n) == ""
 
 
+def test_timing_only_validates_ids(lib):
+    so = lib._lib
+    n = lib.kfac_timing_kernels()
+    assert so.kfac_timing_only(n) == -1
+    assert so.kfac_timing_only(-2) == -1
+    assert so.kfac_timing_only(0) == 0
+    assert so.kfac_timing_only(-1) == 0
+
+
 def test_workspace_queries_resnet50(lib):
     L = synth.conv_layers(32)
     n_all = [l.d_a for l in L] + [l.d_g for l in L]
