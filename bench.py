@@ -2,7 +2,8 @@
 
 One step = Kronecker factors of all 54 layers (53 convolutions and the classifier,
 fp16 inputs) -> unpack to full symmetric -> 108 damped inverses -> G^-1 dW A^-1 for
-all 54 layers (fp32 gradients) -> diagonal Fisher of all 53 BatchNorm layers.
+all 54 layers (fp32 gradients) with the update w <- w - lr P of every weight in the
+same kernel -> diagonal Fisher of all 53 BatchNorm layers with the gamma/beta update.
 Inputs are synthetic and seeded, resident in HBM before timing starts.
 
 Prints one JSON line: steps/s (`value`), the roofline of the kernel that takes the
@@ -30,12 +31,13 @@ PEAK_FP32_MFMA = 157.3   # TFLOP/s, MI355X dense fp32 matrix
 PEAK_FP16_MFMA = 2516.6  # TFLOP/s, MI355X dense fp16 matrix
 PEAK_HBM = 8000.0        # GB/s
 TB = 128                 # block of the inverse
+LR = 0.01                # learning rate of the parameter update
 
 # HBM bytes per launch of the dominant kernel, from two rocprofv3 --pmc passes
 # (FETCH_SIZE, then WRITE_SIZE), calibrated by a plain 1 GiB device copy (fetch x2.0,
 # write x1.0) and summarised in profiles/resnet50_step_hbm_counters.md. Reported only
 # while the kernel's source text still hashes to the value it was measured with.
-MEASURED_TRAFFIC = {"inv_update_kernel": (601325099, "9e2f524ac2d1bbe91291fe387e960286b3cfc615")}
+MEASURED_TRAFFIC = {"inv_update_kernel": (601547387, "8b1e1a6feefabf4f7b36f46713960abbc67732a2")}
 CSRC = os.path.join(ROOT, "fac_second_order_amd", "csrc")
 
 
@@ -142,13 +144,14 @@ def cpu_baseline(layers, bns, budget_s=25.0):
         act = synth.relu_normal_f16(rng, l.act_shape)
         gout = synth.normal_f16(rng, l.gout_shape)
         grad = synth.normal_f32(rng, (l.d_g, l.d_a), 0.1)
+        wt = synth.normal_f32(rng, (l.d_g, l.d_a), 0.05)
         t0 = time.perf_counter()
         A, G = oracle.conv_factors(act, gout, l.kh, l.kw, l.sh, l.sw, l.ph, l.pw, l.bias)
         t1 = time.perf_counter()
         Ai, _ = oracle.damped_inverse(A.astype(np.float32), s)
         Gi, _ = oracle.damped_inverse(G.astype(np.float32), s)
         t2 = time.perf_counter()
-        oracle.precondition(Gi, grad, Ai)
+        oracle.sgd_update(wt, oracle.precondition(Gi, grad, Ai), LR)
         t3 = time.perf_counter()
         t["factors"] += t1 - t0
         t["invert"] += t2 - t1
@@ -159,8 +162,9 @@ def cpu_baseline(layers, bns, budget_s=25.0):
         rng = synth.layer_rng(seed + 1, i)
         x = synth.normal_f16(rng, b.shape)
         g = synth.normal_f16(rng, b.shape)
+        prm = np.stack([np.ones(b.c), np.zeros(b.c)])
         t0 = time.perf_counter()
-        oracle.bn_diag_fisher(x, g, 1e-3)
+        oracle.sgd_update(prm, oracle.bn_diag_fisher(x, g, 1e-3)["precond"], LR)
         t["bn"] += time.perf_counter() - t0
     scale = {"factors": w_full["syrk_flop"] / w_samp["syrk_flop"],
              "invert": w_full["inv_flop"] / w_samp["inv_flop"],
@@ -174,7 +178,7 @@ def cpu_baseline(layers, bns, budget_s=25.0):
                        f"53 BN layers ({len(samp_bn)}), {sampled:.1f} s measured; each stage scaled by "
                        f"its share of algorithmic work to a full step of {est:.1f} s "
                        f"(factors {t['factors']*scale['factors']:.1f}, inverses "
-                       f"{t['invert']*scale['invert']:.1f}, precondition "
+                       f"{t['invert']*scale['invert']:.1f}, precondition and update "
                        f"{t['precondition']*scale['precondition']:.1f}, BN {t['bn']*scale['bn']:.1f} s)")}
 
 
@@ -200,6 +204,18 @@ def make_inputs(layers, bns, device, seed=3, grad_dtype=None, gout_std=1.0):
     return act, gout, grads, xhat, bgout
 
 
+def make_params(layers, bns, device, seed=4):
+    """fp32 weights N(0, 0.05^2) per layer ([d_g, d_a], bias in the last column) and
+    BatchNorm parameters gamma = 1, beta = 0, the tensors the update writes."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    weights = [torch.randn((l.d_g, l.d_a), generator=g, device=device) * 0.05 for l in layers]
+    bn_params = [torch.stack([torch.ones(b.c, device=device), torch.zeros(b.c, device=device)])
+                 for b in bns]
+    return weights, bn_params
+
+
 def run_stale(args):
     """Stale curvature at batch 128: every 10th step refreshes the factors (EMA 0.95,
     the first refresh overwrites) and the inverses; every step preconditions one of
@@ -218,6 +234,7 @@ def run_stale(args):
     grads = [[(torch.randn((l.d_g, l.d_a), generator=gen, device=dev) * 0.1).half() for l in layers]
              for _ in range(10)]
     st = kfac.KfacStep(layers, bns, dev)
+    weights, bn_params = make_params(layers, bns, dev)
     nref = [0]
 
     def step(t):
@@ -225,7 +242,8 @@ def run_stale(args):
         s = nref[0] % 2 if refresh else (nref[0] - 1) % 2
         act, gout, _, xhat, bgout = sets[s]
         decay = 0.0 if (refresh and nref[0] == 0) else 0.95
-        st.step(act, gout, grads[t % 10], xhat, bgout, ema_decay=decay, refresh=refresh)
+        st.step(act, gout, grads[t % 10], xhat, bgout, ema_decay=decay, refresh=refresh,
+                weights=weights, bn_params=bn_params, lr=LR)
         if refresh:
             nref[0] += 1
 
@@ -246,7 +264,7 @@ def run_stale(args):
         "ms_per_step": round(1e3 * elapsed / steps, 3), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": "resnet50_kfac_stale_schedule", "batch_per_gpu": batch, "refresh_every": 10,
-                   "ema_decay": 0.95, "grad_dtype": "f16"},
+                   "ema_decay": 0.95, "grad_dtype": "f16", "lr": LR},
         "roofline": None, "cpu_baseline": None,
     }
     print(json.dumps(out), flush=True)
@@ -271,11 +289,11 @@ def main():
     bns = synth.bn_layers(args.batch)
     w = work(layers, bns)
     act, gout, grads, xhat, bgout = make_inputs(layers, bns, dev)
+    weights, bn_params = make_params(layers, bns, dev)
     st = kfac.KfacStep(layers, bns, dev)
-    stream = torch.cuda.current_stream()
 
     def step():
-        st.step(act, gout, grads, xhat, bgout)
+        st.step(act, gout, grads, xhat, bgout, weights=weights, bn_params=bn_params, lr=LR)
 
     for _ in range(args.warmup):
         step()
@@ -363,8 +381,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": "resnet50_kfac_step", "batch_per_gpu": args.batch,
                    "kfac_layers": len(layers), "factors": 2 * len(layers), "bn_layers": len(bns),
-                   "damping": 1e-3, "inputs": "fp16 ReLU(N(0,1)) activations, fp16 N(0,1) output "
-                   "and BN gradients, fp32 N(0,1e-2) weight gradients"},
+                   "damping": 1e-3, "lr": LR, "inputs": "fp16 ReLU(N(0,1)) activations, fp16 N(0,1) "
+                   "output and BN gradients, fp32 N(0,1e-2) weight gradients, fp32 N(0,2.5e-3) weights"},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels_ms_per_step": {k: round(v[0], 4) for k, v in

@@ -69,9 +69,13 @@ _sig("kfac_invert", _i32, _i32, _P(_i32), _P(_vp), _P(_vp), _P(_f32), _vp, _P(_v
 _sig("kfac_precondition_workspace", _i32, _i32, _P(_i32), _P(_i32), _P(_sz))
 _sig("kfac_precondition", _i32, _i32, _P(_i32), _P(_i32), _P(_vp), _P(_vp), _P(_vp), _i32, _P(_vp),
      _vp, _sz, _vp)
+_sig("kfac_precondition_update", _i32, _i32, _P(_i32), _P(_i32), _P(_vp), _P(_vp), _P(_vp), _i32,
+     _P(_vp), _P(_vp), _f32, _vp, _sz, _vp)
 _sig("kfac_bn_diag_workspace", _i32, _P(kfac_bn), _i32, _P(_sz))
 _sig("kfac_bn_diag", _i32, _P(kfac_bn), _i32, _i32, _P(_vp), _P(_vp), _P(_vp), _P(_vp), _f32, _f32,
      _vp, _sz, _vp)
+_sig("kfac_bn_update", _i32, _P(kfac_bn), _i32, _i32, _P(_vp), _P(_vp), _P(_vp), _P(_vp), _P(_vp),
+     _f32, _f32, _f32, _vp, _sz, _vp)
 _sig("kfac_timing_kernels", _i32)
 _sig("kfac_kernel_name", _c.c_char_p, _i32)
 _sig("kfac_timing_enable", _i32, _i32)
@@ -217,6 +221,17 @@ def kfac_precondition(d_g, d_a, G_inv, A_inv, grad, out, workspace=None, stream=
            "kfac_precondition")
 
 
+def kfac_precondition_update(d_g, d_a, G_inv, A_inv, grad, out, w, lr, workspace=None, stream=None):
+    """w[l] <- w[l] - lr * G_inv[l] @ grad[l] @ A_inv[l]; out[l] <- the product unless out is None."""
+    dt = _dtype_code(grad[0])
+    need = kfac_precondition_workspace(d_g, d_a)
+    ws, wsb = _ws(workspace, need, grad[0].device)
+    _check(_lib.kfac_precondition_update(len(d_g), _ints(d_g), _ints(d_a), _ptrs(G_inv), _ptrs(A_inv),
+                                         _ptrs(grad), dt, None if out is None else _ptrs(out), _ptrs(w),
+                                         float(lr), ws, wsb, _stream(stream)),
+           "kfac_precondition_update")
+
+
 def kfac_bn_diag_workspace(layers):
     out = _sz()
     _check(_lib.kfac_bn_diag_workspace(_bns(layers), len(layers), _c.byref(out)), "kfac_bn_diag_workspace")
@@ -232,6 +247,17 @@ def kfac_bn_diag(layers, xhat, gout, fisher, precond, ema_decay=0.0, shift=1e-3,
     _check(_lib.kfac_bn_diag(_bns(layers), len(layers), dt, _ptrs(xhat), _ptrs(gout), _ptrs(fisher),
                              _ptrs(precond), float(ema_decay), float(shift), ws, wsb, _stream(stream)),
            "kfac_bn_diag")
+
+
+def kfac_bn_update(layers, xhat, gout, fisher, precond, params, lr, ema_decay=0.0, shift=1e-3,
+                   workspace=None, stream=None):
+    """kfac_bn_diag, then params[l] ([2, c] fp32: gamma, beta) <- params[l] - lr * precond[l]."""
+    dt = _dtype_code(xhat[0])
+    need = kfac_bn_diag_workspace(layers)
+    ws, wsb = _ws(workspace, need, xhat[0].device)
+    _check(_lib.kfac_bn_update(_bns(layers), len(layers), dt, _ptrs(xhat), _ptrs(gout), _ptrs(fisher),
+                               _ptrs(precond), _ptrs(params), float(lr), float(ema_decay), float(shift),
+                               ws, wsb, _stream(stream)), "kfac_bn_update")
 
 
 # timing -------------------------------------------------------------------

@@ -9,7 +9,8 @@
 // per-channel partial sums (sum g*x, sum g) to the workspace.
 // Stage 2 (bn_finish_kernel), 8 lanes per channel over the samples, adds the chunks
 // of each sample in a fixed order (deterministic), squares the per-sample sums,
-// averages over samples, blends with the stored Fisher when asked and divides.
+// averages over samples, blends with the stored Fisher when asked and divides; with
+// parameters given it also applies the update of eq. (8), gamma/beta -= lr * precond.
 #include "common.hpp"
 
 namespace kfac {
@@ -20,6 +21,8 @@ struct BnDesc {
   float* fisher;
   float* precond;
   v2f* partial;     // [n][nchunk][c] (sum g*x, sum g)
+  float* params;    // [2][c] gamma, beta updated in place, or NULL
+  float lr;
   int32_t n, hw, c;
   int32_t vl;       // vector lanes per row segment (<= 256)
   int32_t rowpar;   // rows processed side by side (256 / vl)
@@ -166,8 +169,13 @@ __global__ void __launch_bounds__(256) bn_finish_kernel(const BnDesc* __restrict
   }
   gp(d.fisher)[c] = fg;
   gp(d.fisher)[d.c + c] = fb;
-  gp(d.precond)[c] = gg / (fg + shift);
-  gp(d.precond)[d.c + c] = gb / (fb + shift);
+  const float pg = gg / (fg + shift), pb = gb / (fb + shift);
+  gp(d.precond)[c] = pg;
+  gp(d.precond)[d.c + c] = pb;
+  if (d.params) {
+    gp(d.params)[c] = fmaf(-d.lr, pg, gp(d.params)[c]);
+    gp(d.params)[d.c + c] = fmaf(-d.lr, pb, gp(d.params)[d.c + c]);
+  }
 }
 
 // Plans one layer: 16-byte vectors along channels when `vec`, else scalar loads.
@@ -238,12 +246,14 @@ extern "C" kfac_status kfac_bn_diag_workspace(const kfac_bn* layers, int32_t cou
   return KFAC_OK;
 }
 
-extern "C" kfac_status kfac_bn_diag(const kfac_bn* layers, int32_t count, kfac_dtype in_dtype,
-                                    const void* const* xhat, const void* const* gout,
-                                    float* const* fisher, float* const* precond, float ema_decay,
-                                    float shift, void* workspace, size_t ws_bytes, void* stream) {
+// kfac_bn_diag, and with params the update of eq. (8).
+static kfac_status bn_impl(const kfac_bn* layers, int32_t count, kfac_dtype in_dtype, const void* const* xhat,
+                           const void* const* gout, float* const* fisher, float* const* precond,
+                           float* const* params, float lr, float ema_decay, float shift, void* workspace,
+                           size_t ws_bytes, void* stream) {
   kfac_status st = bn_validate(layers, count, in_dtype);
   if (st) return st;
+  if (params && !(lr - lr == 0.f)) return fail(KFAC_ERR_INVALID, "lr must be finite");
   if (!(ema_decay >= 0.f && ema_decay <= 1.f)) return fail(KFAC_ERR_INVALID, "ema_decay must be in [0, 1]");
   if (!(shift == shift)) return fail(KFAC_ERR_INVALID, "shift is NaN");
   if (count == 0) return KFAC_OK;
@@ -254,8 +264,12 @@ extern "C" kfac_status kfac_bn_diag(const kfac_bn* layers, int32_t count, kfac_d
   int64_t items = 0, channels = 0;
   size_t part = 0;
   for (int l = 0; l < count; ++l) {
-    if (!xhat[l] || !gout[l] || !fisher[l] || !precond[l])
+    if (!xhat[l] || !gout[l] || !fisher[l] || !precond[l] || (params && !params[l]))
       return fail(KFAC_ERR_INVALID, "bn layer %d: NULL pointer", l);
+    if (params && (reinterpret_cast<uintptr_t>(params[l]) & 3))
+      return fail(KFAC_ERR_INVALID, "bn layer %d: misaligned pointer", l);
+    if (params && (params[l] == precond[l] || params[l] == fisher[l]))
+      return fail(KFAC_ERR_INVALID, "bn layer %d: params overlaps fisher or precond", l);
     const uintptr_t a = reinterpret_cast<uintptr_t>(xhat[l]) | reinterpret_cast<uintptr_t>(gout[l]);
     if (a % esize || (reinterpret_cast<uintptr_t>(fisher[l]) | reinterpret_cast<uintptr_t>(precond[l])) & 3)
       return fail(KFAC_ERR_INVALID, "bn layer %d: misaligned pointer", l);
@@ -286,6 +300,8 @@ extern "C" kfac_status kfac_bn_diag(const kfac_bn* layers, int32_t count, kfac_d
     d.gout = gout[l];
     d.fisher = fisher[l];
     d.precond = precond[l];
+    d.params = params ? params[l] : nullptr;
+    d.lr = lr;
     d.partial = partial + off;
     off += partial_count(d);
   }
@@ -303,4 +319,22 @@ extern "C" kfac_status kfac_bn_diag(const kfac_bn* layers, int32_t count, kfac_d
               d_cbegin, count, ema_decay, shift);
   KFAC_CHECK_LAUNCH("bn_finish_kernel");
   return KFAC_OK;
+}
+
+extern "C" kfac_status kfac_bn_diag(const kfac_bn* layers, int32_t count, kfac_dtype in_dtype,
+                                    const void* const* xhat, const void* const* gout,
+                                    float* const* fisher, float* const* precond, float ema_decay,
+                                    float shift, void* workspace, size_t ws_bytes, void* stream) {
+  return bn_impl(layers, count, in_dtype, xhat, gout, fisher, precond, nullptr, 0.f, ema_decay, shift, workspace,
+                 ws_bytes, stream);
+}
+
+extern "C" kfac_status kfac_bn_update(const kfac_bn* layers, int32_t count, kfac_dtype in_dtype,
+                                      const void* const* xhat, const void* const* gout,
+                                      float* const* fisher, float* const* precond, float* const* params,
+                                      float lr, float ema_decay, float shift, void* workspace, size_t ws_bytes,
+                                      void* stream) {
+  if (count > 0 && !params) return fail(KFAC_ERR_INVALID, "NULL parameter array");
+  return bn_impl(layers, count, in_dtype, xhat, gout, fisher, precond, params, lr, ema_decay, shift, workspace,
+                 ws_bytes, stream);
 }

@@ -1,6 +1,7 @@
 // Preconditioned gradients G^-1 dW A^-1 of many layers, two grouped launches.
 // Osawa et al. (CVPR 2019), Section 3.2, eq. (6)-(7): with dW stored [d_G, d_A]
-// and vec taken row by row, (G (x) A)^-1 vec(dW) = vec(G^-1 dW A^-1).
+// and vec taken row by row, (G (x) A)^-1 vec(dW) = vec(G^-1 dW A^-1). Optionally the
+// update of eq. (8), w <- w - lr P, in the epilogue of the second product.
 //
 // Both GEMMs run on the fp32 MFMA tile engine in the form C = A_rows^T B_rows, so
 // every operand is read along its rows:
@@ -16,7 +17,9 @@ namespace kfac {
 struct GemmDesc {
   const float* A;  // A operand, read as A[k][m] (row-major, lda)
   const void* B;   // B operand, read as B[k][n] (row-major, ldb)
-  float* C;        // C[m][n] (ldc), or C[n][m] when c_trans
+  float* C;        // C[m][n] (ldc), or C[n][m] when c_trans; NULL: not stored
+  float* W;        // when set: W[m][n] (ldc) -= lr * tile (not with c_trans)
+  float lr;
   int32_t M, N, K;
   int32_t lda, ldb, ldc;
   int32_t b_f16;
@@ -48,8 +51,12 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))
     oct_gemm<LD_V4, LD_V4, true>(q, A, B, d.K, 1.f, lds);
   }
   const int rv = min(TB, d.M - m0), cv = min(TB, d.N - n0);
-  if (d.c_trans) oct_store_t(q, d.C + int64_t(n0) * d.ldc + m0, d.ldc, rv, cv, lds);
-  else oct_store(q, d.C + int64_t(m0) * d.ldc + n0, d.ldc, rv, cv);
+  if (d.c_trans) {
+    oct_store_t(q, d.C + int64_t(n0) * d.ldc + m0, d.ldc, rv, cv, lds);
+  } else {
+    if (d.W) oct_axpy(q, d.W + int64_t(m0) * d.ldc + n0, d.ldc, rv, cv, -d.lr);
+    if (d.C) oct_store(q, d.C + int64_t(m0) * d.ldc + n0, d.ldc, rv, cv);
+  }
 }
 
 // Load forms of a problem's operands: 16-byte groups for fp32 rows whose pitch is a
@@ -93,23 +100,29 @@ extern "C" kfac_status kfac_precondition_workspace(int32_t count, const int32_t*
   return KFAC_OK;
 }
 
-extern "C" kfac_status kfac_precondition(int32_t count, const int32_t* d_g, const int32_t* d_a,
-                                         const float* const* G_inv, const float* const* A_inv,
-                                         const void* const* grad, kfac_dtype grad_dtype,
-                                         float* const* out, void* workspace, size_t ws_bytes,
-                                         void* stream) {
+// kfac_precondition, and with w the update of eq. (8) (out may then be NULL).
+static kfac_status precond_impl(int32_t count, const int32_t* d_g, const int32_t* d_a,
+                                const float* const* G_inv, const float* const* A_inv,
+                                const void* const* grad, kfac_dtype grad_dtype, float* const* out,
+                                float* const* w, float lr, void* workspace, size_t ws_bytes, void* stream) {
   kfac_status st = precond_validate(count, d_g, d_a);
   if (st) return st;
   if (grad_dtype != KFAC_F16 && grad_dtype != KFAC_F32)
     return fail(KFAC_ERR_UNSUPPORTED, "grad dtype %d not supported", grad_dtype);
+  if (w && !(lr - lr == 0.f)) return fail(KFAC_ERR_INVALID, "lr must be finite");
   if (count == 0) return KFAC_OK;
-  if (!G_inv || !A_inv || !grad || !out) return fail(KFAC_ERR_INVALID, "NULL pointer array");
+  if (!G_inv || !A_inv || !grad || (!out && !w)) return fail(KFAC_ERR_INVALID, "NULL pointer array");
   const int esize = grad_dtype == KFAC_F16 ? 2 : 4;
   for (int l = 0; l < count; ++l) {
-    if (!G_inv[l] || !A_inv[l] || !grad[l] || !out[l]) return fail(KFAC_ERR_INVALID, "layer %d: NULL pointer", l);
+    float* o = out ? out[l] : nullptr;
+    float* wl = w ? w[l] : nullptr;
+    if (!G_inv[l] || !A_inv[l] || !grad[l] || (out && !o) || (w && !wl))
+      return fail(KFAC_ERR_INVALID, "layer %d: NULL pointer", l);
     if ((reinterpret_cast<uintptr_t>(G_inv[l]) | reinterpret_cast<uintptr_t>(A_inv[l]) |
-         reinterpret_cast<uintptr_t>(out[l])) & 3 || reinterpret_cast<uintptr_t>(grad[l]) % esize)
+         reinterpret_cast<uintptr_t>(o) | reinterpret_cast<uintptr_t>(wl)) & 3 ||
+        reinterpret_cast<uintptr_t>(grad[l]) % esize)
       return fail(KFAC_ERR_INVALID, "layer %d: misaligned pointer", l);
+    if (o && o == wl) return fail(KFAC_ERR_INVALID, "layer %d: out and w are the same buffer", l);
   }
   st = check_device();
   if (st) return st;
@@ -145,7 +158,8 @@ extern "C" kfac_status kfac_precondition(int32_t count, const int32_t* d_g, cons
     set_modes(x, esize);
     x1[l] = x;
     GemmDesc y{};
-    y.A = T; y.B = A_inv[l]; y.C = out[l];
+    y.A = T; y.B = A_inv[l]; y.C = out ? out[l] : nullptr;
+    y.W = w ? w[l] : nullptr; y.lr = lr;
     y.M = G; y.N = A; y.K = A;
     y.lda = G; y.ldb = A; y.ldc = A;
     y.b_f16 = 0; y.c_trans = 0;
@@ -172,4 +186,23 @@ extern "C" kfac_status kfac_precondition(int32_t count, const int32_t* d_g, cons
   KFAC_LAUNCH(K_GEMM, gemm_tn_kernel, dim3(static_cast<unsigned>(n2)), dim3(512), 0, s, d2, b2, count);
   KFAC_CHECK_LAUNCH("gemm_tn_kernel (T A^-1)");
   return KFAC_OK;
+}
+
+extern "C" kfac_status kfac_precondition(int32_t count, const int32_t* d_g, const int32_t* d_a,
+                                         const float* const* G_inv, const float* const* A_inv,
+                                         const void* const* grad, kfac_dtype grad_dtype,
+                                         float* const* out, void* workspace, size_t ws_bytes,
+                                         void* stream) {
+  if (count > 0 && !out) return fail(KFAC_ERR_INVALID, "NULL pointer array");
+  return precond_impl(count, d_g, d_a, G_inv, A_inv, grad, grad_dtype, out, nullptr, 0.f, workspace, ws_bytes,
+                      stream);
+}
+
+extern "C" kfac_status kfac_precondition_update(int32_t count, const int32_t* d_g, const int32_t* d_a,
+                                                const float* const* G_inv, const float* const* A_inv,
+                                                const void* const* grad, kfac_dtype grad_dtype,
+                                                float* const* out, float* const* w, float lr,
+                                                void* workspace, size_t ws_bytes, void* stream) {
+  if (count > 0 && !w) return fail(KFAC_ERR_INVALID, "NULL weight array");
+  return precond_impl(count, d_g, d_a, G_inv, A_inv, grad, grad_dtype, out, w, lr, workspace, ws_bytes, stream);
 }

@@ -386,6 +386,35 @@ __device__ inline void oct_store(const Oct& o, float* dst, int64_t ld, int rvali
     }
 }
 
+// dst += alpha * tile (row-major, leading dimension ld), rows < rvalid, cols < cvalid.
+__device__ inline void oct_axpy(const Oct& o, float* dst, int64_t ld, int rvalid, int cvalid, float alpha) {
+  const int lane = threadIdx.x & 63;
+  if (rvalid >= TB && cvalid >= TB) {
+    // Full tile: all 32 reads in flight before the first write.
+    KG float* d = gp(dst) + int64_t(oct_row(lane, 0)) * ld + oct_col(lane, 0);
+    float v[2][16];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) v[b][e] = d[int64_t(8 * (e >> 2) + (e & 3)) * ld + 32 * b];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) d[int64_t(8 * (e >> 2) + (e & 3)) * ld + 32 * b] = fmaf(alpha, o.c[b][e], v[b][e]);
+    return;
+  }
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int r = oct_row(lane, e), c = oct_col(lane, b);
+      if (r < rvalid && c < cvalid) {
+        KG float* x = gp(dst) + int64_t(r) * ld + c;
+        *x = fmaf(alpha, o.c[b][e], *x);
+      }
+    }
+}
+
 // Transposed store through LDS (coalesced): dst[c*ld + r] = tile[r][c] for r < rvalid,
 // c < cvalid. lds needs TB*LDT floats; ends with a barrier.
 __device__ inline void oct_store_t(const Oct& o, float* dst, int64_t ld, int rvalid, int cvalid, float* lds) {

@@ -5,8 +5,9 @@ by libkfac's HIP kernels.
 
 Step order follows Osawa et al. (CVPR 2019): stage 1-2 of their Figure 1 (factors
 from the forward activations and backward gradients), eq. (6) (inverses of the
-damped factors) and eq. (7) (preconditioned gradients); BatchNorm uses the
-diagonal Fisher (Section 1, contributions)."""
+damped factors), eq. (7) (preconditioned gradients) and, when parameters are
+given, eq. (8) (the update with learning rate lr); BatchNorm uses the diagonal
+Fisher (Section 1, contributions)."""
 import math
 
 import torch
@@ -67,21 +68,36 @@ class KfacStep:
         K.kfac_invert(self.n_all, self.full, self.full, [self.shift] * len(self.n_all), self.info,
                       None, self.workspace, stream)
 
-    def precondition(self, grads, stream=None):
-        K.kfac_precondition(self.d_g, self.d_a, self.G_inv, self.A_inv, grads, self.out,
-                            self.workspace, stream)
+    def precondition(self, grads, weights=None, lr=0.0, stream=None):
+        """self.out <- preconditioned gradients; with weights (fp32 [d_g, d_a] per layer)
+        also weights -= lr * self.out, in the same kernel."""
+        if weights is None:
+            K.kfac_precondition(self.d_g, self.d_a, self.G_inv, self.A_inv, grads, self.out,
+                                self.workspace, stream)
+        else:
+            K.kfac_precondition_update(self.d_g, self.d_a, self.G_inv, self.A_inv, grads, self.out,
+                                       weights, lr, self.workspace, stream)
 
-    def bn(self, xhat, bn_gout, ema_decay=0.0, stream=None):
-        if self.bn_layers:
+    def bn(self, xhat, bn_gout, ema_decay=0.0, bn_params=None, lr=0.0, stream=None):
+        """BN Fisher and preconditioned gradients; with bn_params (fp32 [2, c]: gamma,
+        beta) also bn_params -= lr * self.bn_pre."""
+        if not self.bn_layers:
+            return
+        if bn_params is None:
             K.kfac_bn_diag(self.bn_layers, xhat, bn_gout, self.fisher, self.bn_pre, ema_decay,
                            self.bn_shift, self.workspace, stream)
+        else:
+            K.kfac_bn_update(self.bn_layers, xhat, bn_gout, self.fisher, self.bn_pre, bn_params, lr,
+                             ema_decay, self.bn_shift, self.workspace, stream)
 
-    def step(self, act, gout, grads, xhat=(), bn_gout=(), ema_decay=0.0, refresh=True, stream=None):
+    def step(self, act, gout, grads, xhat=(), bn_gout=(), ema_decay=0.0, refresh=True,
+             weights=None, bn_params=None, lr=0.0, stream=None):
         """One step. refresh=False is a stale-curvature step: factors and inverses are
         kept, the gradients are preconditioned with them, and BN divides its fresh
-        gradient by the stored Fisher (decay 1 keeps it)."""
+        gradient by the stored Fisher (decay 1 keeps it). Given weights and/or
+        bn_params, those are updated in place with learning rate lr."""
         if refresh:
             self.factors(act, gout, ema_decay, stream)
             self.invert(stream)
-        self.precondition(grads, stream)
-        self.bn(xhat, bn_gout, ema_decay if refresh else 1.0, stream)
+        self.precondition(grads, weights, lr, stream)
+        self.bn(xhat, bn_gout, ema_decay if refresh else 1.0, bn_params, lr, stream)

@@ -165,6 +165,22 @@ kfac_status kfac_precondition(int32_t count, const int32_t* d_g, const int32_t* 
                               void* stream);
 
 /* ---------------------------------------------------------------------------
+ * kfac_precondition_update - kfac_precondition followed by the parameter update
+ * of [OTUNYM] eq. (8), w <- w - lr * P with P the preconditioned gradient of
+ * eq. (7), applied to each tile of P as it is formed (P is never re-read).
+ *
+ * w[l] (device, d_g x d_a row-major fp32, the layout of grad[l]; bias weights in
+ * the last column) is updated in place. out may be NULL (P is then not stored) or
+ * an array as for kfac_precondition; out[l] must not be w[l]. lr must be finite.
+ * Workspace: kfac_precondition_workspace. Errors as for kfac_precondition.
+ * ------------------------------------------------------------------------- */
+kfac_status kfac_precondition_update(int32_t count, const int32_t* d_g, const int32_t* d_a,
+                                     const float* const* G_inv, const float* const* A_inv,
+                                     const void* const* grad, kfac_dtype grad_dtype,
+                                     float* const* out, float* const* w, float lr,
+                                     void* workspace, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * kfac_bn_diag - diagonal Fisher of BatchNorm gamma/beta ([OTUNYM] Section 1
  * contributions; diagonal of the empirical Fisher of eq. (3)).
  *
@@ -181,6 +197,19 @@ kfac_status kfac_bn_diag(const kfac_bn* layers, int32_t count, kfac_dtype in_dty
                          const void* const* xhat, const void* const* gout,
                          float* const* fisher, float* const* precond, float ema_decay,
                          float shift, void* workspace, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * kfac_bn_update - kfac_bn_diag followed by the update of [OTUNYM] eq. (8) for
+ * the BatchNorm parameters: params[l] ([2][c] fp32 device: row 0 gamma, row 1
+ * beta) <- params[l] - lr * precond[l], in the same kernel that forms precond.
+ * params[l] must not be fisher[l] or precond[l]; lr must be finite. Workspace:
+ * kfac_bn_diag_workspace. Errors as for kfac_bn_diag.
+ * ------------------------------------------------------------------------- */
+kfac_status kfac_bn_update(const kfac_bn* layers, int32_t count, kfac_dtype in_dtype,
+                           const void* const* xhat, const void* const* gout,
+                           float* const* fisher, float* const* precond, float* const* params,
+                           float lr, float ema_decay, float shift, void* workspace,
+                           size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Per-kernel event timing, for measurement. When enabled on a thread, every

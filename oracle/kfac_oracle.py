@@ -23,6 +23,8 @@ convolutional neural networks" (CVPR 2019), cited as [OTUNYM]:
   of the inverses.
 * Section 3.2, eq. (7): the preconditioned gradient is that inverse applied to the
   layer's gradient, G^-1 . dW . A^-1 in matrix form.
+* Section 3.2, eq. (8): the parameters move against the preconditioned gradient,
+  scaled by the learning rate.
 * Section 1, list of contributions: the factors are symmetric (one triangle suffices),
   BatchNorm's Fisher is taken diagonal, and the Fisher is refreshed less often.
 
@@ -42,6 +44,7 @@ __all__ = [
     "im2col_nhwc", "gram", "second_moment", "conv_factors", "ema_update",
     "packed_offset", "pack_upper", "unpack_upper", "cholesky_upper",
     "upper_triangular_inverse", "damped_inverse", "precondition", "bn_diag_fisher",
+    "sgd_update",
 ]
 
 
@@ -265,3 +268,19 @@ def bn_diag_fisher(xhat, gout, shift, ema_decay=0.0, fisher_prev=None):
     if ema_decay != 0.0:
         fisher = ema_update(fisher_prev, fisher, ema_decay)
     return {"fisher": fisher, "grad": grad, "precond": grad / (fisher + np.float64(shift))}
+
+
+# ---------------------------------------------------------------------------
+# Parameter update: [OTUNYM] eq. (8)
+# ---------------------------------------------------------------------------
+
+def sgd_update(w, precond_grad, lr):
+    """New parameters w - lr * G, in fp64.
+
+    [OTUNYM] eq. (8): each layer's parameters take a step of size lr (the learning
+    rate eta) against its preconditioned gradient G of eq. (7) (``precondition``;
+    for BatchNorm gamma and beta the ``precond`` of ``bn_diag_fisher``). The pages
+    give the plain step: no momentum or weight decay is applied here.
+    """
+    return np.asarray(w, dtype=np.float64) - np.float64(lr) * np.asarray(precond_grad, dtype=np.float64)
+

@@ -127,6 +127,34 @@ def test_bn_and_precondition_validation(lib):
     assert so.kfac_precondition_workspace(1, dg, da, c.byref(sz)) == -1
 
 
+def test_update_variants_validation(lib):
+    """The eq. (8) variants refuse a non-finite lr, a missing weight array and an
+    output that is also the weight buffer, before any device work."""
+    so = lib._lib
+    c = ctypes
+    dg = (c.c_int32 * 1)(4)
+    da = (c.c_int32 * 1)(5)
+    fake = (c.c_void_p * 1)(0x10000)
+    other = (c.c_void_p * 1)(0x20000)
+    nan = c.c_float(float("nan"))
+    one = c.c_float(1.0)
+    assert so.kfac_precondition_update(1, dg, da, fake, fake, fake, 1, fake, other, nan, None, 0, None) == -1
+    assert b"lr" in so.kfac_last_error()
+    assert so.kfac_precondition_update(1, dg, da, fake, fake, fake, 1, fake, None, one, None, 0, None) == -1
+    assert so.kfac_precondition_update(1, dg, da, fake, fake, fake, 1, other, other, one, None, 0, None) == -1
+    assert b"same buffer" in so.kfac_last_error()
+    assert so.kfac_precondition_update(0, None, None, None, None, None, 1, None, None, one, None, 0, None) == 0
+    bn = lib._bns([synth.BNLayer("b", 2, 3, 4)])
+    assert so.kfac_bn_update(bn, 1, 1, fake, fake, fake, other, None, one, c.c_float(0.0),
+                             c.c_float(1e-3), None, 0, None) == -1
+    assert so.kfac_bn_update(bn, 1, 1, fake, fake, fake, other, other, one, c.c_float(0.0),
+                             c.c_float(1e-3), None, 0, None) == -1
+    assert b"overlaps" in so.kfac_last_error()
+    inf = c.c_float(float("inf"))
+    assert so.kfac_bn_update(bn, 1, 1, fake, fake, fake, other, (c.c_void_p * 1)(0x30000), inf,
+                             c.c_float(0.0), c.c_float(1e-3), None, 0, None) == -1
+
+
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     """The product path has no fallback: a missing libkfac.so is an ImportError."""
     import importlib.util

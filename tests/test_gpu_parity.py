@@ -315,3 +315,70 @@ def test_precondition(kfac_gpu, gdtype):
         e = relF(host(o), oracle.precondition(G_, dW, A_))
         assert e <= 2e-2, (g, a, e)
         assert e <= 1e-5, (g, a, e)   # fp32 products of exactly widened inputs
+
+
+# ---------------------------------------------------------------------------
+# parameter update of eq. (8), fused into the preconditioning and BN kernels
+# ---------------------------------------------------------------------------
+
+def test_precondition_update(kfac_gpu):
+    """w <- w - lr * G^-1 dW A^-1 in the GEMM epilogue: the step equals -lr times the
+    oracle's preconditioned gradient, the new weights equal the oracle's update, and
+    storing P or not leaves the weights bit-identical."""
+    rng = synth.layer_rng(1010, 0)
+    lr = 0.37
+    Gi = [rng.standard_normal((g, g)).astype(np.float32) for g, _ in PRE_DIMS]
+    Ai = [rng.standard_normal((a, a)).astype(np.float32) for _, a in PRE_DIMS]
+    Gi = [(x + x.T) / 2 for x in Gi]
+    Ai = [(x + x.T) / 2 for x in Ai]
+    grads = [(rng.standard_normal((g, a)) * 0.1).astype(np.float32) for g, a in PRE_DIMS]
+    w0 = [rng.standard_normal((g, a)).astype(np.float32) for g, a in PRE_DIMS]
+    dg, da = [g for g, _ in PRE_DIMS], [a for _, a in PRE_DIMS]
+    args = ([to_dev(x) for x in Gi], [to_dev(x) for x in Ai], [to_dev(x) for x in grads])
+    out = [torch.full((g, a), np.nan, device="cuda") for g, a in PRE_DIMS]
+    w = [to_dev(x) for x in w0]
+    say("kfac_precondition_update", PRE_DIMS)
+    kfac_gpu.kfac_precondition_update(dg, da, *args, out, w, lr)
+    for (g, a), G_, A_, dW, o, wn, wo in zip(PRE_DIMS, Gi, Ai, grads, out, w, w0):
+        P = oracle.precondition(G_, dW, A_)
+        assert relF(host(o), P) <= 1e-5, (g, a)
+        step = host(wn).astype(np.float64) - wo
+        assert relF(step, -lr * P) <= 2e-2, (g, a)
+        assert relF(host(wn), oracle.sgd_update(wo, P, lr)) <= 1e-5, (g, a)
+    say("kfac_precondition_update out=None")
+    w2 = [to_dev(x) for x in w0]
+    kfac_gpu.kfac_precondition_update(dg, da, *args, None, w2, lr)
+    for a_, b_ in zip(w, w2):
+        assert torch.equal(a_, b_)
+    say("kfac_precondition_update lr=0")
+    w3 = [to_dev(x) for x in w0]
+    kfac_gpu.kfac_precondition_update(dg, da, *args, None, w3, 0.0)
+    for a_, b_ in zip(w3, w0):
+        assert np.array_equal(host(a_), b_)
+
+
+@pytest.mark.parametrize("dtype", [np.float16, np.float32])
+def test_bn_update(kfac_gpu, dtype):
+    """gamma/beta <- gamma/beta - lr * precond in the BN finish kernel; fisher and
+    precond as from kfac_bn_diag."""
+    rng = synth.layer_rng(1011, 0)
+    lr = 0.25
+    xs = [rng.standard_normal(b.shape).astype(dtype) for b in BN_CASES]
+    gs = [(rng.standard_normal(b.shape) * 0.1).astype(dtype) for b in BN_CASES]
+    p0 = [rng.standard_normal((2, b.c)).astype(np.float32) for b in BN_CASES]
+    F = [torch.zeros(2, b.c, device="cuda") for b in BN_CASES]
+    P = [torch.zeros(2, b.c, device="cuda") for b in BN_CASES]
+    prm = [to_dev(x) for x in p0]
+    say("kfac_bn_update", dtype.__name__, [b.shape for b in BN_CASES])
+    kfac_gpu.kfac_bn_update(BN_CASES, [to_dev(x) for x in xs], [to_dev(g) for g in gs], F, P, prm, lr,
+                            0.0, 1e-3)
+    for i, b in enumerate(BN_CASES):
+        ref = oracle.bn_diag_fisher(xs[i], gs[i], 1e-3)
+        assert relF(host(F[i]), ref["fisher"]) <= 1e-4, b
+        assert relF(host(P[i]), ref["precond"]) <= 1e-4, b
+        step = host(prm[i]).astype(np.float64) - p0[i]
+        assert relF(step, -lr * ref["precond"]) <= 1e-4, b
+        assert relF(host(prm[i]), oracle.sgd_update(p0[i], ref["precond"], lr)) <= 1e-4, b
+        # the kernel's own update of its own precond is exact up to one fma rounding
+        own = p0[i].astype(np.float64) - lr * host(P[i]).astype(np.float64)
+        assert np.allclose(host(prm[i]), own, rtol=1e-6, atol=1e-6 * np.abs(own).max()), b

@@ -411,6 +411,29 @@ def test_bn_bruteforce_fisher():
     assert np.allclose(out["precond"], HW * c / ((HW * c) ** 2 + 1.0), rtol=0, atol=1e-15)
 
 
+def check_update_rule(update=None):
+    """Pin P12: eq. (8) applied to the eq. (7) gradient of a tiny layer equals
+    w - lr * (G (x) A)^-1 vec(dW), the Kronecker system solved densely."""
+    update = update or oracle.sgd_update
+    rng = np.random.default_rng(12)
+    dg, da, lr = 3, 4, 0.37
+    G = rng.standard_normal((dg, dg)); G = G @ G.T + np.eye(dg)
+    A = rng.standard_normal((da, da)); A = A @ A.T + np.eye(da)
+    dW = rng.standard_normal((dg, da))
+    w = rng.standard_normal((dg, da))
+    P = oracle.precondition(np.linalg.inv(G), dW, np.linalg.inv(A))
+    ref = w - lr * np.linalg.solve(np.kron(G, A), dW.reshape(-1)).reshape(dg, da)
+    return relF(update(w, P, lr), ref)
+
+
+def test_update_rule():
+    assert check_update_rule() < 1e-12
+    w = np.arange(6.0).reshape(2, 3)
+    assert np.array_equal(oracle.sgd_update(w, np.ones_like(w), 0.0), w)
+    assert np.array_equal(oracle.sgd_update(np.zeros(3), np.array([1.0, -2.0, 4.0]), 0.5),
+                          np.array([-0.5, 1.0, -2.0]))
+
+
 def test_bn_ema():
     rng = np.random.default_rng(6)
     x, g = rng.standard_normal((2, 2, 3, 4))
@@ -522,6 +545,7 @@ def _mut_chol_sign(M):
     (check_ema, {"ema": _mut_ema_swapped}, 1e-15),
     (check_pack, {"pack": _mut_pack_lower}, 1e-15),
     (check_cholesky_vs_lapack, {"chol": _mut_chol_sign}, 1e-12),
+    (check_update_rule, {"update": lambda w, g, lr: np.asarray(w) + lr * np.asarray(g)}, 1e-12),
 ])
 def test_planted_mistake_is_caught(check, kwargs, limit):
     try:
