@@ -2,7 +2,7 @@
 
 The functions below carry the names of the C entry points in include/kfac.h and only
 marshal arguments. Importing this package loads libkfac.so and fails loudly if it has
-not been built (python -m fac_second_order_amd.build)."""
+not been built (python fac_second_order_amd/build.py)."""
 from ._lib import (  # noqa: F401
     KFAC_F16, KFAC_F32, KfacError, LIB_PATH, kfac_version,
     kfac_factors_workspace, kfac_factors,

@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libkfac.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is not built; run `python -m fac_second_order_amd.build` "
+        f"{LIB_PATH} is not built; run `python fac_second_order_amd/build.py` "
         "(hipcc, gfx950) first. There is no CPU fallback.")
 
 _lib = ctypes.CDLL(LIB_PATH)

@@ -1,6 +1,6 @@
 """Builds libkfac.so (all HIP sources, gfx950 only) next to this file.
 
-    python -m fac_second_order_amd.build        (or python fac_second_order_amd/build.py)
+    python fac_second_order_amd/build.py
 
 Every call recompiles. Sources are compiled in parallel to objects under
 fac_second_order_amd/_build/ and linked with hipcc into one shared library.
