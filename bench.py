@@ -65,9 +65,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--batch", type=int, default=None, help="default 32 (128 for --workload stale)")
-    ap.add_argument("--workload", choices=["resnet50", "stale"], default="resnet50",
+    ap.add_argument("--workload", choices=["resnet50", "stale", "capture"], default="resnet50",
                     help="resnet50: one full K-FAC step per step (batch 32); stale: refresh "
-                         "every 10 steps with EMA 0.95, preconditioning only otherwise (batch 128)")
+                         "every 10 steps with EMA 0.95, preconditioning only otherwise (batch 128); "
+                         "capture: training iterations of a randomly initialised ResNet-50 on "
+                         "synthetic 224x224 images, factors from its own activations (batch 32)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true",
                     help="time the steps without per-kernel events (roofline then null)")
@@ -270,6 +272,63 @@ def run_stale(args):
     print(json.dumps(out), flush=True)
 
 
+def run_capture(args):
+    """Training iterations of a randomly initialised ResNet-50 (PyTorch forward and
+    backward, fp32, channels-last) on one fixed batch of synthetic 224x224 images with
+    random labels; each iteration's K-FAC step (factors from the captured activations
+    and output gradients, inverses, preconditioning and update of every weight and
+    BatchNorm parameter) runs in libkfac. Reports iterations/s and the K-FAC step's
+    share, timed with events on the stream the library runs on."""
+    import torch
+    import torch.nn.functional as F
+    from fac_second_order_amd.capture import KfacCapture, ResNet50
+    dev = torch.device("cuda:0")
+    batch = args.batch or 32
+    torch.manual_seed(5)
+    model = ResNet50(1000).to(dev).to(memory_format=torch.channels_last)
+    cap = KfacCapture(model, damping=1e-3, ema_decay=0.95)
+    g = torch.Generator(device=dev)
+    g.manual_seed(6)
+    x = torch.randn(batch, 3, 224, 224, generator=g, device=dev).to(memory_format=torch.channels_last)
+    y = torch.randint(0, 1000, (batch,), generator=g, device=dev)
+    ev = []
+
+    def it(timed):
+        model.zero_grad(set_to_none=True)
+        F.cross_entropy(model(x), y).backward()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        cap.step(lr=1e-3)
+        e1.record()
+        if timed:
+            ev.append((e0, e1))
+
+    for _ in range(args.warmup):
+        it(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        it(True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    if int(cap.kstep.info.abs().sum()) != 0:
+        raise RuntimeError("Cholesky breakdown on a damped factor")
+    kfac_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+    out = {
+        "metric": "ResNet-50 training iterations/sec with K-FAC (batch 32, factors from the network's "
+                  "own activations, 1 GPU)",
+        "value": round(args.steps / elapsed, 3), "unit": "iterations/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(1e3 * elapsed / args.steps, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "resnet50_capture", "batch_per_gpu": batch, "image": 224, "classes": 1000,
+                   "damping": 1e-3, "lr": 1e-3, "ema_decay": 0.95,
+                   "kfac_ms_per_step": round(kfac_ms, 3),
+                   "forward_backward_ms_per_step": round(1e3 * elapsed / args.steps - kfac_ms, 3)},
+        "roofline": None, "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -283,6 +342,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.workload == "stale":
         run_stale(args)
+        return
+    if args.workload == "capture":
+        run_capture(args)
         return
     args.batch = args.batch or 32
     layers = synth.conv_layers(args.batch)

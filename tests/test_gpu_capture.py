@@ -1,0 +1,109 @@
+"""The library fed from a network's own forward and backward passes (a randomly
+initialised ResNet-50 on synthetic images): factors, BatchNorm Fisher,
+preconditioned gradients and the update match the fp64 oracle on the captured
+tensors, and a few K-FAC steps on a fixed batch lower its loss."""
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from gpu_helpers import host, relF, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _model(seed, classes=10):
+    from fac_second_order_amd.capture import ResNet50
+    torch.manual_seed(seed)
+    return ResNet50(classes).cuda().to(memory_format=torch.channels_last)
+
+
+def _batch(seed, n=4, hw=32, classes=10):
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    x = torch.randn(n, 3, hw, hw, generator=g, device="cuda").to(memory_format=torch.channels_last)
+    y = torch.randint(0, classes, (n,), generator=g, device="cuda")
+    return x, y
+
+
+def test_capture_parity(kfac_gpu):
+    from fac_second_order_amd.capture import KfacCapture
+    model = _model(11)
+    cap = KfacCapture(model, damping=1e-2)
+    x, y = _batch(12)
+    say("capture: forward/backward, ResNet-50 at 4x3x32x32")
+    F.cross_entropy(model(x), y).backward()
+    fc = model.fc
+    w0 = cap._to_matrix(fc).cpu().numpy().astype(np.float64)
+    lr = 0.1
+    cap.step(lr)
+    torch.cuda.synchronize()
+    st = cap.kstep
+    assert int(st.info.abs().sum()) == 0
+    for l in (0, 2, 4, len(cap.pairs) - 1):  # conv1, a 3x3, a strided projection, the classifier
+        L = st.layers[l]
+        a, g = host(cap.act[l]), host(cap.gout[l])
+        if a.ndim == 2:
+            a, g = a.reshape(L.n, 1, 1, -1), g.reshape(L.n, 1, 1, -1)
+        A, G = oracle.conv_factors(a, g, L.kh, L.kw, L.sh, L.sw, L.ph, L.pw, L.bias)
+        ea, eg = relF(host(st.A_packed[l]), oracle.pack_upper(A)), relF(host(st.G_packed[l]), oracle.pack_upper(G))
+        say(f"layer {l}: relF A {ea:.2e} G {eg:.2e}")
+        assert ea <= 1e-2 and eg <= 1e-2, l
+    # preconditioned gradients and the update: conv1 (full-rank factors) and the
+    # classifier (rank-deficient factors at batch 4, its gradient in their range)
+    for l in (0, len(cap.pairs) - 1):
+        L = st.layers[l]
+        a, g = host(cap.act[l]), host(cap.gout[l])
+        if a.ndim == 2:
+            a, g = a.reshape(L.n, 1, 1, -1), g.reshape(L.n, 1, 1, -1)
+        A, G = oracle.conv_factors(a, g, L.kh, L.kw, L.sh, L.sw, L.ph, L.pw, L.bias)
+        Ai, _ = oracle.damped_inverse(A, st.shift)
+        Gi, _ = oracle.damped_inverse(G, st.shift)
+        m = cap.pairs[l][0]
+        dW = host(cap._to_matrix(m, grad=True)).astype(np.float64)
+        P = oracle.precondition(Gi, dW, Ai)
+        # componentwise size of the two fp32 products against the result: where the
+        # gradient lies in the range of a factor whose other eigenvalues sit at the
+        # damping, the products cancel and fp32 rounding is amplified by this ratio
+        rho = np.linalg.norm(np.abs(Gi) @ np.abs(dW) @ np.abs(Ai)) / np.linalg.norm(P)
+        bound = max(2e-2, 4 * np.sqrt(A.shape[0]) * 6e-8 * rho)
+        e = relF(host(st.out[l]), P)
+        say(f"layer {l}: P relF {e:.2e}, product cancellation {rho:.2e}, bound {bound:.2e}, "
+            f"cond A {np.linalg.cond(A + st.shift * np.eye(A.shape[0])):.2e}")
+        assert e <= bound, (l, e, bound)
+        if l == 0:
+            assert e <= 2e-2
+    # the update of eq. (8) on the classifier, written back into the module
+    w1 = cap._to_matrix(fc).cpu().numpy().astype(np.float64)
+    ref = w0 - lr * host(st.out[len(cap.pairs) - 1]).astype(np.float64)
+    assert np.allclose(w1, ref, rtol=1e-6, atol=1e-7 * np.abs(w0).max())
+    # BatchNorm: Fisher and preconditioned gradient of the first and the last layer
+    for b in (0, len(cap.bns) - 1):
+        ref = oracle.bn_diag_fisher(host(cap.xhat[b]), host(cap.bgout[b]), st.bn_shift)
+        assert relF(host(st.fisher[b]), ref["fisher"]) <= 1e-3, b
+        assert relF(host(st.bn_pre[b]), ref["precond"]) <= 1e-3, b
+        # the per-sample mean of the captured gradients is the batch gradient of gamma, beta
+        bn = cap.bns[b]
+        assert relF(ref["grad"], np.stack([host(bn.weight.grad), host(bn.bias.grad)])) <= 1e-2, b
+    cap.remove()
+
+
+def test_capture_training_smoke(kfac_gpu):
+    from fac_second_order_amd.capture import KfacCapture
+    model = _model(21)
+    cap = KfacCapture(model, damping=3e-2, ema_decay=0.9)
+    x, y = _batch(22, n=16)
+    losses = []
+    for t in range(8):
+        model.zero_grad(set_to_none=True)
+        loss = F.cross_entropy(model(x), y)
+        loss.backward()
+        losses.append(float(loss))
+        cap.step(lr=0.02)
+        say(f"capture training step {t}: loss {losses[-1]:.4f}")
+    torch.cuda.synchronize()
+    assert int(cap.kstep.info.abs().sum()) == 0
+    assert all(np.isfinite(losses))
+    assert losses[-1] < 0.7 * losses[0], losses
+    cap.remove()
