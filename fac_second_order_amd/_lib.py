@@ -23,6 +23,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 KFAC_F16 = 0
 KFAC_F32 = 1
+KFAC_F64 = 2
 _STATUS = {0: "KFAC_OK", -1: "KFAC_ERR_INVALID", -2: "KFAC_ERR_UNSUPPORTED",
            -3: "KFAC_ERR_WORKSPACE", -4: "KFAC_ERR_HIP"}
 
@@ -71,6 +72,8 @@ _sig("kfac_precondition", _i32, _i32, _P(_i32), _P(_i32), _P(_vp), _P(_vp), _P(_
      _vp, _sz, _vp)
 _sig("kfac_precondition_update", _i32, _i32, _P(_i32), _P(_i32), _P(_vp), _P(_vp), _P(_vp), _i32,
      _P(_vp), _P(_vp), _f32, _vp, _sz, _vp)
+_sig("kfac_precondition_ex", _i32, _i32, _P(_i32), _P(_i32), _P(_vp), _P(_vp), _P(_vp), _i32,
+     _P(_vp), _P(_vp), _f32, _i32, _vp, _sz, _vp)
 _sig("kfac_bn_diag_workspace", _i32, _P(kfac_bn), _i32, _P(_sz))
 _sig("kfac_bn_diag", _i32, _P(kfac_bn), _i32, _i32, _P(_vp), _P(_vp), _P(_vp), _P(_vp), _f32, _f32,
      _vp, _sz, _vp)
@@ -230,6 +233,18 @@ def kfac_precondition_update(d_g, d_a, G_inv, A_inv, grad, out, w, lr, workspace
                                          _ptrs(grad), dt, None if out is None else _ptrs(out), _ptrs(w),
                                          float(lr), ws, wsb, _stream(stream)),
            "kfac_precondition_update")
+
+
+def kfac_precondition_ex(d_g, d_a, G_inv, A_inv, grad, out, w=None, lr=0.0, accum=KFAC_F32, workspace=None,
+                         stream=None):
+    """kfac_precondition (w None) or kfac_precondition_update (w given), the products
+    summed in fp32 (accum KFAC_F32) or fp64 (KFAC_F64)."""
+    dt = _dtype_code(grad[0])
+    need = kfac_precondition_workspace(d_g, d_a)
+    ws, wsb = _ws(workspace, need, grad[0].device)
+    _check(_lib.kfac_precondition_ex(len(d_g), _ints(d_g), _ints(d_a), _ptrs(G_inv), _ptrs(A_inv), _ptrs(grad), dt,
+                                     None if out is None else _ptrs(out), None if w is None else _ptrs(w),
+                                     float(lr), int(accum), ws, wsb, _stream(stream)), "kfac_precondition_ex")
 
 
 def kfac_bn_diag_workspace(layers):

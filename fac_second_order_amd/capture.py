@@ -136,8 +136,9 @@ class KfacCapture:
     the weight gradients and updates the weights and the BatchNorm parameters in
     place (eq. 8) through libkfac."""
 
-    def __init__(self, model, damping=1e-3, ema_decay=0.95, refresh_every=1):
+    def __init__(self, model, damping=1e-3, ema_decay=0.95, refresh_every=1, precond_accum="f32"):
         self.model = model
+        self.precond_accum = precond_accum
         self.pairs = list(model.kfac_modules())
         self.damping = damping
         self.ema_decay = ema_decay
@@ -240,7 +241,7 @@ class KfacCapture:
         dev = self.act[0].device
         if self.kstep is None:
             layers, bns = self._geometry()
-            self.kstep = KfacStep(layers, bns, dev, damping=self.damping)
+            self.kstep = KfacStep(layers, bns, dev, damping=self.damping, precond_accum=self.precond_accum)
             self.master = [self._to_matrix(m) for m, _ in self.pairs]
             self.bn_master = [torch.stack([bn.weight.data.float(), bn.bias.data.float()]).contiguous()
                               for bn in self.bns]

@@ -8,9 +8,11 @@
 //   1) T^T = (G^-1 dW)^T: A operand G^-1 (symmetric, so its rows are its
 //      columns), B operand dW; the tile is written transposed into the workspace.
 //   2) P = T A^-1: A operand rows of T^T, B operand A^-1.
+// With fp64 accumulation both products run on the fp64 MFMA engine instead (exact
+// products of the fp32 operands, fp64 sums, one rounding per output element).
 #include <algorithm>
 
-#include "tile_f32.hpp"
+#include "tile_f64.hpp"
 
 namespace kfac {
 
@@ -59,6 +61,37 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))
   }
 }
 
+// The same with fp64 accumulation (its 64 accumulator registers leave room for two
+// waves per SIMD).
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) gemm_tn64_kernel(const GemmDesc* __restrict__ desc,
+                                                        const int32_t* __restrict__ begin, int count) {
+  const int p = find_problem(begin, count, blockIdx.x);
+  const GemmDesc& d = desc[p];
+  const int t = blockIdx.x - begin[p];
+  const int mt = t % d.tm, nt = t / d.tm;
+  const int m0 = mt * TB, n0 = nt * TB;
+  __shared__ __attribute__((aligned(16))) float lds[4 * CHUNK];
+  Oct64 q;
+  oct64_zero(q);
+  const Operand A = op_rows(d.A, d.lda, d.K, m0, d.M);
+  const Operand B = d.b_f16 ? op_rows_h(static_cast<const _Float16*>(d.B), d.ldb, d.K, n0, d.N)
+                            : op_rows(static_cast<const float*>(d.B), d.ldb, d.K, n0, d.N);
+  if (d.buf) {
+    if (d.b_mode == LD_V4) oct64_gemm<LD_V4, LD_V4>(q, A, B, d.K, lds);
+    else if (d.b_mode == LD_F32) oct64_gemm<LD_V4, LD_F32>(q, A, B, d.K, lds);
+    else oct64_gemm<LD_V4, LD_F16>(q, A, B, d.K, lds);
+  } else {
+    oct64_gemm<LD_V4, LD_V4, true>(q, A, B, d.K, lds);
+  }
+  const int rv = min(TB, d.M - m0), cv = min(TB, d.N - n0);
+  if (d.c_trans) {
+    oct64_store_t(q, d.C + int64_t(n0) * d.ldc + m0, d.ldc, rv, cv, lds);
+  } else {
+    if (d.W) oct64_axpy(q, d.W + int64_t(m0) * d.ldc + n0, d.ldc, rv, cv, -d.lr);
+    if (d.C) oct64_store(q, d.C + int64_t(m0) * d.ldc + n0, d.ldc, rv, cv);
+  }
+}
+
 // Load forms of a problem's operands: 16-byte groups for fp32 rows whose pitch is a
 // multiple of 4 floats on a 16-byte aligned base, single elements otherwise. The
 // buffer pipeline takes problems whose operands span less than 2^31 bytes each and
@@ -100,15 +133,19 @@ extern "C" kfac_status kfac_precondition_workspace(int32_t count, const int32_t*
   return KFAC_OK;
 }
 
-// kfac_precondition, and with w the update of eq. (8) (out may then be NULL).
+// kfac_precondition, and with w the update of eq. (8) (out may then be NULL); the
+// products accumulate in fp32 or fp64 (accum).
 static kfac_status precond_impl(int32_t count, const int32_t* d_g, const int32_t* d_a,
                                 const float* const* G_inv, const float* const* A_inv,
                                 const void* const* grad, kfac_dtype grad_dtype, float* const* out,
-                                float* const* w, float lr, void* workspace, size_t ws_bytes, void* stream) {
+                                float* const* w, float lr, kfac_dtype accum, void* workspace, size_t ws_bytes,
+                                void* stream) {
   kfac_status st = precond_validate(count, d_g, d_a);
   if (st) return st;
   if (grad_dtype != KFAC_F16 && grad_dtype != KFAC_F32)
     return fail(KFAC_ERR_UNSUPPORTED, "grad dtype %d not supported", grad_dtype);
+  if (accum != KFAC_F32 && accum != KFAC_F64)
+    return fail(KFAC_ERR_UNSUPPORTED, "accumulation dtype %d not supported", accum);
   if (w && !(lr - lr == 0.f)) return fail(KFAC_ERR_INVALID, "lr must be finite");
   if (count == 0) return KFAC_OK;
   if (!G_inv || !A_inv || !grad || (!out && !w)) return fail(KFAC_ERR_INVALID, "NULL pointer array");
@@ -181,6 +218,13 @@ static kfac_status precond_impl(int32_t count, const int32_t* d_g, const int32_t
   if ((st = upload(d2, g2.data(), sizeof(GemmDesc) * count, s))) return st;
   if ((st = upload(b1, e1.data(), sizeof(int32_t) * count, s))) return st;
   if ((st = upload(b2, e2.data(), sizeof(int32_t) * count, s))) return st;
+  if (accum == KFAC_F64) {
+    KFAC_LAUNCH(K_GEMM, gemm_tn64_kernel, dim3(static_cast<unsigned>(n1)), dim3(512), 0, s, d1, b1, count);
+    KFAC_CHECK_LAUNCH("gemm_tn64_kernel (G^-1 dW)");
+    KFAC_LAUNCH(K_GEMM, gemm_tn64_kernel, dim3(static_cast<unsigned>(n2)), dim3(512), 0, s, d2, b2, count);
+    KFAC_CHECK_LAUNCH("gemm_tn64_kernel (T A^-1)");
+    return KFAC_OK;
+  }
   KFAC_LAUNCH(K_GEMM, gemm_tn_kernel, dim3(static_cast<unsigned>(n1)), dim3(512), 0, s, d1, b1, count);
   KFAC_CHECK_LAUNCH("gemm_tn_kernel (G^-1 dW)");
   KFAC_LAUNCH(K_GEMM, gemm_tn_kernel, dim3(static_cast<unsigned>(n2)), dim3(512), 0, s, d2, b2, count);
@@ -194,8 +238,8 @@ extern "C" kfac_status kfac_precondition(int32_t count, const int32_t* d_g, cons
                                          float* const* out, void* workspace, size_t ws_bytes,
                                          void* stream) {
   if (count > 0 && !out) return fail(KFAC_ERR_INVALID, "NULL pointer array");
-  return precond_impl(count, d_g, d_a, G_inv, A_inv, grad, grad_dtype, out, nullptr, 0.f, workspace, ws_bytes,
-                      stream);
+  return precond_impl(count, d_g, d_a, G_inv, A_inv, grad, grad_dtype, out, nullptr, 0.f, KFAC_F32, workspace,
+                      ws_bytes, stream);
 }
 
 extern "C" kfac_status kfac_precondition_update(int32_t count, const int32_t* d_g, const int32_t* d_a,
@@ -204,5 +248,15 @@ extern "C" kfac_status kfac_precondition_update(int32_t count, const int32_t* d_
                                                 float* const* out, float* const* w, float lr,
                                                 void* workspace, size_t ws_bytes, void* stream) {
   if (count > 0 && !w) return fail(KFAC_ERR_INVALID, "NULL weight array");
-  return precond_impl(count, d_g, d_a, G_inv, A_inv, grad, grad_dtype, out, w, lr, workspace, ws_bytes, stream);
+  return precond_impl(count, d_g, d_a, G_inv, A_inv, grad, grad_dtype, out, w, lr, KFAC_F32, workspace, ws_bytes,
+                      stream);
+}
+
+extern "C" kfac_status kfac_precondition_ex(int32_t count, const int32_t* d_g, const int32_t* d_a,
+                                            const float* const* G_inv, const float* const* A_inv,
+                                            const void* const* grad, kfac_dtype grad_dtype, float* const* out,
+                                            float* const* w, float lr, kfac_dtype accum, void* workspace,
+                                            size_t ws_bytes, void* stream) {
+  return precond_impl(count, d_g, d_a, G_inv, A_inv, grad, grad_dtype, out, w, lr, accum, workspace, ws_bytes,
+                      stream);
 }

@@ -18,13 +18,17 @@ from . import _lib as K
 class KfacStep:
     """Buffers for `layers` (objects with the kfac_layer fields) and `bn_layers`
     (objects with n, hw, c). Tikhonov damping gamma puts sqrt(gamma) on each
-    Kronecker factor (float32-rounded) and gamma on the BN diagonal."""
+    Kronecker factor (float32-rounded) and gamma on the BN diagonal. precond_accum
+    "f64" sums the preconditioning products in fp64 (kfac_precondition_ex)."""
 
     def __init__(self, layers, bn_layers=(), device="cuda", damping=1e-3, bn_shift=None,
-                 in_dtype=torch.float16):
+                 in_dtype=torch.float16, precond_accum="f32"):
         self.layers = list(layers)
         self.bn_layers = list(bn_layers)
         self.device = torch.device(device)
+        if precond_accum not in ("f32", "f64"):
+            raise ValueError("precond_accum must be 'f32' or 'f64'")
+        self.accum = K.KFAC_F64 if precond_accum == "f64" else K.KFAC_F32
         self.shift = float(torch.tensor(math.sqrt(damping), dtype=torch.float32))
         self.bn_shift = float(damping if bn_shift is None else bn_shift)
         self.d_a = [l.c_in * l.kh * l.kw + (1 if l.bias else 0) for l in self.layers]
@@ -71,7 +75,10 @@ class KfacStep:
     def precondition(self, grads, weights=None, lr=0.0, stream=None):
         """self.out <- preconditioned gradients; with weights (fp32 [d_g, d_a] per layer)
         also weights -= lr * self.out, in the same kernel."""
-        if weights is None:
+        if self.accum == K.KFAC_F64:
+            K.kfac_precondition_ex(self.d_g, self.d_a, self.G_inv, self.A_inv, grads, self.out, weights, lr,
+                                   self.accum, self.workspace, stream)
+        elif weights is None:
             K.kfac_precondition(self.d_g, self.d_a, self.G_inv, self.A_inv, grads, self.out,
                                 self.workspace, stream)
         else:

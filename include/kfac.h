@@ -55,6 +55,7 @@ typedef int32_t kfac_status;
 typedef int32_t kfac_dtype;
 #define KFAC_F16 0                 /* IEEE binary16 */
 #define KFAC_F32 1                 /* IEEE binary32 */
+#define KFAC_F64 2                 /* IEEE binary64 (accumulation of kfac_precondition_ex) */
 
 /* One convolution or fully connected layer. Activations are NHWC [n, h, w, c_in];
  * output gradients are NHWC [n, h_out, w_out, c_out] and must satisfy
@@ -179,6 +180,24 @@ kfac_status kfac_precondition_update(int32_t count, const int32_t* d_g, const in
                                      const void* const* grad, kfac_dtype grad_dtype,
                                      float* const* out, float* const* w, float lr,
                                      void* workspace, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * kfac_precondition_ex - kfac_precondition (w NULL) or kfac_precondition_update
+ * (w given) with a choice of accumulation for both products ([OTUNYM] eq. (7),
+ * eq. (8)): accum = KFAC_F32 as those calls, or KFAC_F64, where each product of
+ * fp32 operands is formed exactly and summed in fp64 (fp64 MFMA), rounded once per
+ * output element (the intermediate G^-1 dW is kept in fp32). A real weight
+ * gradient lies in the range of its layer's factors; where a factor is
+ * rank-deficient and the damping small, the terms of the products cancel by a large
+ * factor and fp32 sums lose that many digits of the result, fp64 sums do not. The
+ * fp64 MFMA rate is half the fp32 rate. Workspace: kfac_precondition_workspace.
+ * Errors as for kfac_precondition; another accum gives KFAC_ERR_UNSUPPORTED.
+ * ------------------------------------------------------------------------- */
+kfac_status kfac_precondition_ex(int32_t count, const int32_t* d_g, const int32_t* d_a,
+                                 const float* const* G_inv, const float* const* A_inv,
+                                 const void* const* grad, kfac_dtype grad_dtype,
+                                 float* const* out, float* const* w, float lr, kfac_dtype accum,
+                                 void* workspace, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * kfac_bn_diag - diagonal Fisher of BatchNorm gamma/beta ([OTUNYM] Section 1

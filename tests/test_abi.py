@@ -150,6 +150,9 @@ def test_update_variants_validation(lib):
     assert so.kfac_bn_update(bn, 1, 1, fake, fake, fake, other, other, one, c.c_float(0.0),
                              c.c_float(1e-3), None, 0, None) == -1
     assert b"overlaps" in so.kfac_last_error()
+    # accumulation other than fp32 / fp64
+    assert so.kfac_precondition_ex(1, dg, da, fake, fake, fake, 1, fake, None, one, 3, None, 0, None) == -2
+    assert so.kfac_precondition_ex(1, dg, da, fake, fake, fake, 1, None, None, one, 2, None, 0, None) == -1
     inf = c.c_float(float("inf"))
     assert so.kfac_bn_update(bn, 1, 1, fake, fake, fake, other, (c.c_void_p * 1)(0x30000), inf,
                              c.c_float(0.0), c.c_float(1e-3), None, 0, None) == -1

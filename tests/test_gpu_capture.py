@@ -63,13 +63,18 @@ def test_capture_parity(kfac_gpu):
         m = cap.pairs[l][0]
         dW = host(cap._to_matrix(m, grad=True)).astype(np.float64)
         P = oracle.precondition(Gi, dW, Ai)
-        # componentwise size of the two fp32 products against the result: where the
-        # gradient lies in the range of a factor whose other eigenvalues sit at the
-        # damping, the products cancel and fp32 rounding is amplified by this ratio
+        # Componentwise size of the products against the result: where the gradient
+        # lies in the range of a factor whose other eigenvalues sit at the damping,
+        # the products cancel by rho, and both the inverses' own fp32 error and the
+        # fp32 sums are amplified by it (first-order bound below).
         rho = np.linalg.norm(np.abs(Gi) @ np.abs(dW) @ np.abs(Ai)) / np.linalg.norm(P)
-        bound = max(2e-2, 4 * np.sqrt(A.shape[0]) * 6e-8 * rho)
+        ea, eg = relF(host(st.A_inv[l]), Ai), relF(host(st.G_inv[l]), Gi)
+        bound = max(2e-2, 2 * rho * (ea + eg + 4 * np.sqrt(A.shape[0]) * 6e-8))
         e = relF(host(st.out[l]), P)
-        say(f"layer {l}: P relF {e:.2e}, product cancellation {rho:.2e}, bound {bound:.2e}, "
+        eg_only = relF(host(st.out[l]), oracle.precondition(host(st.G_inv[l]).astype(np.float64), dW,
+                                                             host(st.A_inv[l]).astype(np.float64)))
+        say(f"layer {l}: P relF {e:.2e} ({eg_only:.2e} against the exact product of the library's inverses), "
+            f"cancellation {rho:.2e}, inverses relF {ea:.1e} / {eg:.1e}, bound {bound:.2e}, "
             f"cond A {np.linalg.cond(A + st.shift * np.eye(A.shape[0])):.2e}")
         assert e <= bound, (l, e, bound)
         if l == 0:
@@ -106,4 +111,34 @@ def test_capture_training_smoke(kfac_gpu):
     assert int(cap.kstep.info.abs().sum()) == 0
     assert all(np.isfinite(losses))
     assert losses[-1] < 0.7 * losses[0], losses
+    cap.remove()
+
+
+def test_capture_f64_accumulation(kfac_gpu):
+    """The same capture with the preconditioning products summed in fp64: against the
+    exact product of the library's own fp32 inverses, only the fp32 intermediate and
+    the output rounding remain. (Against the fp64 oracle the classifier's P stays off
+    by what the fp32 inverses carry, amplified by the same cancellation.)"""
+    from fac_second_order_amd.capture import KfacCapture
+    model = _model(11)
+    cap = KfacCapture(model, damping=1e-2, precond_accum="f64")
+    x, y = _batch(12)
+    F.cross_entropy(model(x), y).backward()
+    cap.step(0.0)
+    st = cap.kstep
+    l = len(cap.pairs) - 1
+    L = st.layers[l]
+    dW = host(cap._to_matrix(model.fc, grad=True)).astype(np.float64)
+    Gi32, Ai32 = host(st.G_inv[l]).astype(np.float64), host(st.A_inv[l]).astype(np.float64)
+    Pg = oracle.precondition(Gi32, dW, Ai32)
+    rho = np.linalg.norm(np.abs(Gi32) @ np.abs(dW) @ np.abs(Ai32)) / np.linalg.norm(Pg)
+    e = relF(host(st.out[l]), Pg)
+    A, G = oracle.conv_factors(host(cap.act[l]).reshape(L.n, 1, 1, -1), host(cap.gout[l]).reshape(L.n, 1, 1, -1),
+                               1, 1, 1, 1, 0, 0, 1)
+    Ai, _ = oracle.damped_inverse(A, st.shift)
+    Gi, _ = oracle.damped_inverse(G, st.shift)
+    eo = relF(host(st.out[l]), oracle.precondition(Gi, dW, Ai))
+    say(f"classifier P with fp64 sums: relF {e:.2e} against the exact product of the library's inverses "
+        f"(rho {rho:.2e}), {eo:.2e} against the oracle")
+    assert e <= 4 * 6e-8 * rho and e <= 2e-2
     cap.remove()

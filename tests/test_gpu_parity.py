@@ -382,3 +382,68 @@ def test_bn_update(kfac_gpu, dtype):
         # the kernel's own update of its own precond is exact up to one fma rounding
         own = p0[i].astype(np.float64) - lr * host(P[i]).astype(np.float64)
         assert np.allclose(host(prm[i]), own, rtol=1e-6, atol=1e-6 * np.abs(own).max()), b
+
+
+# ---------------------------------------------------------------------------
+# preconditioning with fp64 accumulation
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("gdtype", [np.float32, np.float16])
+def test_precondition_f64_accumulation(kfac_gpu, gdtype):
+    """kfac_precondition_ex with KFAC_F64 on generic inputs: exact products summed in
+    fp64, so only the fp32 intermediate and the output rounding remain."""
+    rng = synth.layer_rng(1012, 0)
+    Gi = [rng.standard_normal((g, g)).astype(np.float32) for g, _ in PRE_DIMS]
+    Ai = [rng.standard_normal((a, a)).astype(np.float32) for _, a in PRE_DIMS]
+    Gi = [(x + x.T) / 2 for x in Gi]
+    Ai = [(x + x.T) / 2 for x in Ai]
+    grads = [(rng.standard_normal((g, a)) * 0.1).astype(gdtype) for g, a in PRE_DIMS]
+    w0 = [rng.standard_normal((g, a)).astype(np.float32) for g, a in PRE_DIMS]
+    dg, da = [g for g, _ in PRE_DIMS], [a for _, a in PRE_DIMS]
+    out = [torch.full((g, a), np.nan, device="cuda") for g, a in PRE_DIMS]
+    w = [to_dev(x) for x in w0]
+    lr = 0.25
+    say("kfac_precondition_ex f64", gdtype.__name__, PRE_DIMS)
+    kfac_gpu.kfac_precondition_ex(dg, da, [to_dev(x) for x in Gi], [to_dev(x) for x in Ai],
+                                  [to_dev(x) for x in grads], out, w, lr, kfac_gpu.KFAC_F64)
+    for (g, a), G_, A_, dW, o, wn, wo in zip(PRE_DIMS, Gi, Ai, grads, out, w, w0):
+        P = oracle.precondition(G_, dW, A_)
+        assert relF(host(o), P) <= 1e-6, (g, a)
+        assert relF(host(wn), oracle.sgd_update(wo, P, lr)) <= 1e-6, (g, a)
+    say("kfac_precondition_ex f64 without update")
+    out2 = [torch.full((g, a), np.nan, device="cuda") for g, a in PRE_DIMS]
+    kfac_gpu.kfac_precondition_ex(dg, da, [to_dev(x) for x in Gi], [to_dev(x) for x in Ai],
+                                  [to_dev(x) for x in grads], out2, None, 0.0, kfac_gpu.KFAC_F64)
+    for a_, b_ in zip(out, out2):
+        assert torch.equal(a_, b_)
+
+
+def test_precondition_cancellation(kfac_gpu):
+    """A gradient in the range of rank-deficient factors (dW = Gamma^T X / R, factors
+    from the same 8 rows, damping 1e-3): the products cancel by a factor rho, the fp32
+    sums lose about rho*u, the fp64 sums do not. Inputs are the oracle's inverses
+    rounded to fp32; the reference is their exact product."""
+    rng = synth.layer_rng(1013, 0)
+    R, dg, da = 8, 96, 1025
+    X = np.maximum(rng.standard_normal((R, da)), 0.0)
+    X[:, -1] = 1.0
+    Gam = rng.standard_normal((R, dg))
+    s = S_GAMMA
+    Ai, _ = oracle.damped_inverse(X.T @ X / R, s)
+    Gi, _ = oracle.damped_inverse(Gam.T @ Gam / R, s)
+    Ai32, Gi32 = Ai.astype(np.float32), Gi.astype(np.float32)
+    dW = (Gam.T @ X / R).astype(np.float32)
+    P = oracle.precondition(Gi32.astype(np.float64), dW, Ai32.astype(np.float64))
+    rho = np.linalg.norm(np.abs(Gi32) @ np.abs(dW) @ np.abs(Ai32)) / np.linalg.norm(P)
+    errs = {}
+    for name, accum in (("f32", kfac_gpu.KFAC_F32), ("f64", kfac_gpu.KFAC_F64)):
+        out = [torch.full((dg, da), np.nan, device="cuda")]
+        say("kfac_precondition_ex cancellation", name)
+        kfac_gpu.kfac_precondition_ex([dg], [da], [to_dev(Gi32)], [to_dev(Ai32)], [to_dev(dW)], out, None, 0.0,
+                                      accum)
+        errs[name] = relF(host(out[0]), P)
+    say(f"cancellation rho {rho:.2e}: relF f32 {errs['f32']:.2e}, f64 {errs['f64']:.2e}")
+    assert rho > 1e3                                # the case is what it claims to be
+    assert errs["f64"] <= 4 * 6e-8 * rho            # fp32 rounding of the intermediate only
+    assert errs["f64"] <= 2e-2
+    assert errs["f64"] < errs["f32"]
