@@ -182,7 +182,8 @@ def kfac_pack_sym_workspace(n):
 
 
 def kfac_pack_sym(n, full, packed, direction, workspace=None, stream=None):
-    """direction 0: packed <- upper(full); 1: full <- symmetric(packed)."""
+    """direction 0: packed <- upper(full); 1: full <- symmetric(packed); 2: upper(full)
+    <- packed, strict lower triangle of full left as it was."""
     need = kfac_pack_sym_workspace(n)
     ws, wsb = _ws(workspace, need, full[0].device if full else None)
     _check(_lib.kfac_pack_sym(len(n), _ints(n), _ptrs(full), _ptrs(packed), int(direction), ws, wsb,

@@ -77,7 +77,25 @@ __device__ void bn_partial_body(const BnDesc& d, int item) {
   if (active) {
     const T* X = static_cast<const T*>(d.xhat) + (int64_t(s) * d.hw) * d.c + c0;
     const T* G = static_cast<const T*>(d.gout) + (int64_t(s) * d.hw) * d.c + c0;
-    for (int r = r_begin + rp; r < r_end; r += d.rowpar) {
+    // four rows' loads in flight before their sums; rows are still added in order
+    constexpr int U = 4;
+    int r = r_begin + rp;
+    for (; r + (U - 1) * d.rowpar < r_end; r += U * d.rowpar) {
+      float x[U][EV], g[U][EV];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        load_vec<T, EV>(X + int64_t(r + u * d.rowpar) * d.c, x[u]);
+        load_vec<T, EV>(G + int64_t(r + u * d.rowpar) * d.c, g[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int q = 0; q < EV; ++q) {
+          sg[q] = fmaf(g[u][q], x[u][q], sg[q]);
+          sb[q] += g[u][q];
+        }
+    }
+    for (; r < r_end; r += d.rowpar) {
       float x[EV], g[EV];
       load_vec<T, EV>(X + int64_t(r) * d.c, x);
       load_vec<T, EV>(G + int64_t(r) * d.c, g);

@@ -344,24 +344,34 @@ __global__ void __launch_bounds__(PT) inv_pivot_kernel(const InvDesc* __restrict
   if (failed && tid == 0 && *gp(d.info) == 0) *gp(d.info) = k0 + failed;
 }
 
-// Panel of step k into buffer slot `slot` (Y rows slot*TB ..), 512 threads: for
-// column block j != k, V_j = S_kj (S_jk^T for j < k) is staged in LDS, then two
-// 256-thread engines run side by side: threads 0..255 form Y_j = E V_j (the
-// Cholesky row panel U_kj when j > k) into the panel buffer, threads 256..511 form
-// W_j = P^-1 V_j, which goes into S in place (S_kj = W_j, or S_jk = W_j^T). The
-// pivot kernel wrote S_kk = -P^-1.
+// Panel of step k into buffer slot `slot` (Y rows slot*TB ..). For column block
+// j != k, V_j = S_kj (S_jk^T for j < k); Y_j = E V_j (the Cholesky row panel U_kj
+// when j > k) goes to the panel buffer and W_j = P^-1 V_j into S in place (S_kj =
+// W_j, or S_jk = W_j^T). The pivot kernel wrote S_kk = -P^-1.
+// Two 512-thread blocks share a tile, each forming 64 of the 128 rows of Y_j and W_j
+// (rows h*64 ..): V_j is staged whole in LDS (67.6 KB, so two blocks fit on a compute
+// unit), waves 0-3 form the Y half and waves 4-7 the W half, each wave a 32x64 slab
+// whose A operand (rows of U_kk^-1 = E^T or of P^-1, read as [k][m]) streams from L2
+// straight into MFMA operand registers one 32-deep chunk ahead. E is lower
+// triangular, so a Y row m only sums k <= m. Blocks b and b+8 (same XCD, so the
+// second read of V_j hits that XCD's L2) take the two halves of one tile.
 constexpr int PP = 512;  // panel threads
-__global__ void __launch_bounds__(PP) inv_panel_kernel(const InvDesc* __restrict__ desc,
-                                                       const int32_t* __restrict__ begin,
-                                                       int count, int k, int slot) {
-  const int p = find_problem(begin, count, blockIdx.x);
+constexpr int WTP = 65;  // pitch of the transposed W half in LDS
+__global__ void __launch_bounds__(PP) __attribute__((amdgpu_waves_per_eu(4, 4)))
+inv_panel_kernel(const InvDesc* __restrict__ desc, const int32_t* __restrict__ begin, int count, int k,
+                 int slot, int total) {
+  const int bid = blockIdx.x;
+  const int t = (bid >> 4) * 8 + (bid & 7), h = (bid >> 3) & 1;
+  if (t >= total) return;
+  const int p = find_problem(begin, count, t);
   const InvDesc& d = desc[p];
-  const int j = blockIdx.x - begin[p];
+  const int j = t - begin[p];
   if (j == k) return;
   const int n = d.n, k0 = k * TB, bk = min(TB, n - k0);
   const int j0 = j * TB, bj = min(TB, n - j0);
-  const int tid = threadIdx.x, grp = tid >> 8;
-  __shared__ __attribute__((aligned(16))) float lds[2][2 * CHUNK];
+  const int r0 = h * (TB / 2);
+  if (r0 >= bk) return;  // no pivot rows in this half
+  const int tid = threadIdx.x;
   __shared__ __attribute__((aligned(16))) float Vs[TB * LDP];
   {  // all 32 loads of a thread in flight first (clamped addresses, zero outside)
     const int lo = tid & (TB - 1), hi0 = tid >> 7;  // along a row of S / first row
@@ -388,25 +398,99 @@ __global__ void __launch_bounds__(PP) inv_panel_kernel(const InvDesc* __restrict
       for (int q = 0; q < TB * TB / PP; ++q) Vs[r * LDP + hi0 + 4 * q] = v[q];
     }
   }
+  const int grp = tid >> 8, w = (tid >> 6) & 3, lane = tid & 63;
+  const int ml = lane & 31, kh = lane >> 5;
+  const int mr = r0 + 32 * (w >> 1);  // first row of this wave's slab
+  const int nc = 64 * (w & 1);        // first column
+  // A operand element (k, m) = Ui[k][m] (Y) or P^-1[k][m] (W); zero for k, m >= bk
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(grp == 0 ? d.Ui : d.P), 0, TB * TB * 4, 0x00020000);
+  const int kmax = grp == 0 ? min(bk, mr + 32) : bk;
+  const int nchunk = (kmax + 31) >> 5;  // wave-uniform
+  const int m = mr + ml;
+  auto load_a = [&](float (&a)[16], int c) {
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      const int kk = 32 * c + 2 * s + kh;
+      const bool ok = kk < bk && m < bk && c < nchunk;
+      a[s] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+          rs, ok ? static_cast<unsigned>(kk * TB + m) * 4u : 0x80000000u, 0, 0));
+    }
+  };
+  float acur[16], anext[16];
+  load_a(acur, 0);
+  v16f acc0, acc1;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc0[e] = acc1[e] = 0.f;
   __syncthreads();
-  Quad q;
-  quad_zero(q);
-  // group 0: A[p][m] = Ui[p][m] = E[m][p]; group 1: A[p][m] = P^-1[p][m]
-  const Operand Aop = op_rows(grp == 0 ? d.Ui : d.P, TB, bk, 0, bk);
-  quad_gemm_lds_b(q, Aop, Vs, LDP, bk, 1.f, lds[grp]);  // ends with a barrier
-  if (grp == 0) {
-    quad_store(q, d.Y + int64_t(slot) * TB * d.ldy + j0, d.ldy, bk, bj);
-    if (d.chol && j > k) quad_store(q, d.chol + int64_t(k0) * n + j0, n, bk, bj);
-  } else if (j > k) {
-    quad_store(q, d.S + int64_t(k0) * n + j0, n, bk, bj);  // S_kj = W_j
-  } else {
-    quad_to_lds(q, Vs, LDP);  // Vs is free: both engines have passed their last barrier
+  for (int c = 0; c < nchunk; ++c) {
+    load_a(anext, c + 1);
+    float b0[16], b1[16];
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      const float* br = Vs + (32 * c + 2 * s + kh) * LDP + nc + ml;
+      b0[s] = br[0];
+      b1[s] = br[32];
+    }
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(acur[s], b0[s], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(acur[s], b1[s], acc1, 0, 0, 0);
+    }
+    // LDS reads of four k-steps ahead, then per k-step two MFMAs and two reads
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int s = 0; s < 12; ++s) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+#pragma unroll
+    for (int s = 0; s < 16; ++s) acur[s] = anext[s];
   }
-  if (j < k) {  // S_jk = W_j^T, coalesced along rows of S
+  // accumulator register e of block b: row mr + 8(e/4) + 4kh + e%4, column nc + 32b + ml
+  if (grp == 0) {
+    KG float* Y = gp(d.Y) + int64_t(slot) * TB * d.ldy + j0;
+    KG float* U = (d.chol && j > k) ? gp(d.chol) + int64_t(k0) * n + j0 : nullptr;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int r = mr + 8 * (e >> 2) + 4 * kh + (e & 3);
+      const int c0 = nc + ml, c1 = nc + 32 + ml;
+      if (r < bk) {
+        if (c0 < bj) Y[int64_t(r) * d.ldy + c0] = acc0[e];
+        if (c1 < bj) Y[int64_t(r) * d.ldy + c1] = acc1[e];
+        if (U) {
+          if (c0 < bj) U[int64_t(r) * n + c0] = acc0[e];
+          if (c1 < bj) U[int64_t(r) * n + c1] = acc1[e];
+        }
+      }
+    }
+  } else if (j > k) {  // S_kj = W_j
+    KG float* W = gp(d.S) + int64_t(k0) * n + j0;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int r = mr + 8 * (e >> 2) + 4 * kh + (e & 3);
+      const int c0 = nc + ml, c1 = nc + 32 + ml;
+      if (r < bk) {
+        if (c0 < bj) W[int64_t(r) * n + c0] = acc0[e];
+        if (c1 < bj) W[int64_t(r) * n + c1] = acc1[e];
+      }
+    }
+  }
+  if (j < k) {  // S_jk = W_j^T through LDS (pitch WTP), coalesced along rows of S
+    __syncthreads();  // every wave is done reading Vs
+    if (grp == 1) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int rl = mr - r0 + 8 * (e >> 2) + 4 * kh + (e & 3);
+        Vs[(nc + ml) * WTP + rl] = acc0[e];
+        Vs[(nc + 32 + ml) * WTP + rl] = acc1[e];
+      }
+    }
     __syncthreads();
-    for (int e = tid; e < TB * TB; e += PP) {
-      const int c = e / TB, r = e % TB;
-      if (r < bk && c < bj) gp(d.S)[int64_t(j0 + c) * n + k0 + r] = Vs[r * LDP + c];
+    for (int e = tid; e < TB * (TB / 2); e += PP) {
+      const int c = e >> 6, rl = e & 63;
+      if (r0 + rl < bk && c < bj) gp(d.S)[int64_t(j0 + c) * n + k0 + r0 + rl] = Vs[c * WTP + rl];
     }
   }
 }
@@ -617,6 +701,8 @@ extern "C" kfac_status kfac_invert(int32_t count, const int32_t* n, const float*
   auto tiles_of = [&](int m) { int nb = (n[m] + TB - 1) / TB; return nb * (nb + 1) / 2; };
   auto panels_of = [&](int m) { return (n[m] + TB - 1) / TB; };
   auto t64_of = [&](int m) { int nb = (n[m] + FT - 1) / FT; return nb * (nb + 1) / 2; };
+  // two panel blocks per tile, in groups of 16 blocks covering 8 tiles
+  auto panel_grid = [](unsigned tiles) { return (tiles + 7) / 8 * 16; };
 
   KFAC_LAUNCH(K_INV_PREP, inv_prep_kernel, dim3(grid_of(pl.t64_begin, count, t64_of)), dim3(256), 0, s,
               d_desc, d_t64, count);
@@ -633,8 +719,9 @@ extern "C" kfac_status kfac_invert(int32_t count, const int32_t* n, const float*
     const int a1 = k + 1 < pl.max_nb ? pl.active[k + 1] : 0;
     KFAC_LAUNCH(K_INV_PIVOT, inv_pivot_kernel, dim3(a0), dim3(PT), 0, s, d_desc, k);
     KFAC_CHECK_LAUNCH("inv_pivot_kernel");
-    KFAC_LAUNCH(K_INV_PANEL, inv_panel_kernel, dim3(grid_of(pl.panel_begin, a0, panels_of)), dim3(PP), 0, s,
-                d_desc, d_panel, a0, k, 0);
+    const unsigned pg0 = grid_of(pl.panel_begin, a0, panels_of);
+    KFAC_LAUNCH(K_INV_PANEL, inv_panel_kernel, dim3(panel_grid(pg0)), dim3(PP), 0, s, d_desc, d_panel, a0, k, 0,
+                static_cast<int>(pg0));
     KFAC_CHECK_LAUNCH("inv_panel_kernel");
     if (a1 > 0) {
       const unsigned pg = grid_of(pl.panel_begin, a1, panels_of);
@@ -642,7 +729,8 @@ extern "C" kfac_status kfac_invert(int32_t count, const int32_t* n, const float*
       KFAC_CHECK_LAUNCH("inv_rowupd_kernel");
       KFAC_LAUNCH(K_INV_PIVOT, inv_pivot_kernel, dim3(a1), dim3(PT), 0, s, d_desc, k + 1);
       KFAC_CHECK_LAUNCH("inv_pivot_kernel");
-      KFAC_LAUNCH(K_INV_PANEL, inv_panel_kernel, dim3(pg), dim3(PP), 0, s, d_desc, d_panel, a1, k + 1, 1);
+      KFAC_LAUNCH(K_INV_PANEL, inv_panel_kernel, dim3(panel_grid(pg)), dim3(PP), 0, s, d_desc, d_panel, a1, k + 1,
+                  1, static_cast<int>(pg));
       KFAC_CHECK_LAUNCH("inv_panel_kernel");
     }
     if ((st = update(a0, k, 1))) return st;

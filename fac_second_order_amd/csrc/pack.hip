@@ -4,8 +4,9 @@
 //
 // Work item = one 64x64 tile (ti <= tj) of one matrix. Pack reads the upper tile
 // rows of the full matrix and writes the matching packed row segments. Unpack
-// writes the upper tile directly and its mirror through an LDS transpose, so both
-// global writes are row-contiguous. Pure data movement, bit-exact. HBM-bound.
+// writes the upper tile directly and, for a full symmetric result, its mirror through
+// an LDS transpose, so both global writes are row-contiguous. Pure data movement,
+// bit-exact. HBM-bound.
 #include "common.hpp"
 
 namespace kfac {
@@ -34,28 +35,41 @@ __global__ void __launch_bounds__(256) pack_kernel(const PackDesc* __restrict__ 
   }
 }
 
+// mirror = 0 writes the upper triangle only (the lower triangle of full is left as
+// it was): what a consumer that reads only the upper triangle needs, at half the
+// write traffic.
 __global__ void __launch_bounds__(256) unpack_kernel(const PackDesc* __restrict__ desc,
-                                                     const int32_t* __restrict__ begin, int count) {
+                                                     const int32_t* __restrict__ begin, int count,
+                                                     int mirror) {
   __shared__ float s[PT][PT + 1];
   const int p = find_problem(begin, count, blockIdx.x);
   const PackDesc d = desc[p];
   int ti, tj;
   upper_tile(blockIdx.x - begin[p], d.nb, ti, tj);
   const int64_t n = d.n;
-  const int c = threadIdx.x & (PT - 1);
+  const int c = threadIdx.x & (PT - 1), r0 = threadIdx.x >> 6;
   const int64_t i0 = int64_t(ti) * PT, j0 = int64_t(tj) * PT;
-  for (int r = threadIdx.x >> 6; r < PT; r += 4) {
-    const int64_t i = i0 + r, j = j0 + c;
-    float v = 0.f;
-    if (i < n && j < n && i <= j) {
-      v = gp(d.packed)[packed_off(i, j, n)];
-      gp(d.full)[i * n + j] = v;
-    }
-    s[r][c] = v;
+  constexpr int RQ = PT / 4;  // rows per thread
+  float v[RQ];
+  // all loads of a thread in flight before the first store
+#pragma unroll
+  for (int q = 0; q < RQ; ++q) {
+    const int64_t i = i0 + r0 + 4 * q, j = j0 + c;
+    v[q] = (i < n && j < n && i <= j) ? gp(d.packed)[packed_off(i, j, n)] : 0.f;
   }
+#pragma unroll
+  for (int q = 0; q < RQ; ++q) {
+    const int64_t i = i0 + r0 + 4 * q, j = j0 + c;
+    if (i < n && j < n && i <= j) gp(d.full)[i * n + j] = v[q];
+  }
+  if (!mirror) return;
+#pragma unroll
+  for (int q = 0; q < RQ; ++q) s[r0 + 4 * q][c] = v[q];
   __syncthreads();
   // mirror: full[j][i] = full[i][j] for i < j; this thread writes row j0+r, column i0+c
-  for (int r = threadIdx.x >> 6; r < PT; r += 4) {
+#pragma unroll
+  for (int q = 0; q < RQ; ++q) {
+    const int r = r0 + 4 * q;
     const int64_t j = j0 + r, i = i0 + c;
     if (i < n && j < n && i < j) gp(d.full)[j * n + i] = s[c][r];
   }
@@ -90,7 +104,7 @@ extern "C" kfac_status kfac_pack_sym(int32_t count, const int32_t* n, float* con
                                      size_t ws_bytes, void* stream) {
   kfac_status st = pack_validate(count, n);
   if (st) return st;
-  if (direction != 0 && direction != 1) return fail(KFAC_ERR_INVALID, "direction must be 0 or 1");
+  if (direction < 0 || direction > 2) return fail(KFAC_ERR_INVALID, "direction must be 0, 1 or 2");
   if (count == 0) return KFAC_OK;
   if (!full || !packed) return fail(KFAC_ERR_INVALID, "full or packed is NULL");
   std::vector<PackDesc> desc(count);
@@ -123,7 +137,8 @@ extern "C" kfac_status kfac_pack_sym(int32_t count, const int32_t* n, float* con
     KFAC_LAUNCH(K_PACK, pack_kernel, dim3(static_cast<unsigned>(tiles)), dim3(256), 0, s, d_desc, d_begin, count);
     KFAC_CHECK_LAUNCH("pack_kernel");
   } else {
-    KFAC_LAUNCH(K_UNPACK, unpack_kernel, dim3(static_cast<unsigned>(tiles)), dim3(256), 0, s, d_desc, d_begin, count);
+    KFAC_LAUNCH(K_UNPACK, unpack_kernel, dim3(static_cast<unsigned>(tiles)), dim3(256), 0, s, d_desc, d_begin, count,
+                direction == 1 ? 1 : 0);
     KFAC_CHECK_LAUNCH("unpack_kernel");
   }
   return KFAC_OK;

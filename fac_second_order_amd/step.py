@@ -68,7 +68,8 @@ class KfacStep:
                        self.workspace, stream)
 
     def invert(self, stream=None):
-        K.kfac_pack_sym(self.n_all, self.full, self.packed_all, 1, self.workspace, stream)
+        # kfac_invert reads only the upper triangle: unpack that half
+        K.kfac_pack_sym(self.n_all, self.full, self.packed_all, 2, self.workspace, stream)
         K.kfac_invert(self.n_all, self.full, self.full, [self.shift] * len(self.n_all), self.info,
                       None, self.workspace, stream)
 

@@ -119,6 +119,8 @@ kfac_status kfac_factors(const kfac_layer* layers, int32_t count, kfac_dtype in_
  * row (n(n+1)/2 floats, same order as kfac_factors).
  * direction 0: packed <- upper triangle of full (the lower triangle is not read).
  * direction 1: full <- symmetric matrix (both triangles written from packed).
+ * direction 2: upper triangle of full <- packed; the strict lower triangle of full
+ *              is not written (the input kfac_invert reads, at half the writes).
  * Pure data movement: bit-exact. full and packed must not overlap.
  * ------------------------------------------------------------------------- */
 kfac_status kfac_pack_sym_workspace(int32_t count, const int32_t* n, size_t* bytes);

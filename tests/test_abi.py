@@ -93,7 +93,8 @@ def test_invalid_arguments_return_errors(lib):
     assert b"n[1]" in so.kfac_last_error()
     n = (c.c_int32 * 1)(4)
     ptrs = (c.c_void_p * 1)(None)
-    assert so.kfac_pack_sym(1, n, ptrs, ptrs, 2, None, 0, None) == -1       # bad direction
+    assert so.kfac_pack_sym(1, n, ptrs, ptrs, 3, None, 0, None) == -1       # bad direction
+    assert so.kfac_pack_sym(1, n, ptrs, ptrs, -1, None, 0, None) == -1      # bad direction
     assert so.kfac_pack_sym(1, n, ptrs, ptrs, 0, None, 0, None) == -1       # NULL matrix
     big = (c.c_int32 * 1)(40000)
     assert so.kfac_invert_workspace(1, big, c.byref(sz)) == -1

@@ -41,6 +41,15 @@ def test_pack_unpack_bitexact(kfac_gpu):
     kfac_gpu.kfac_pack_sym(PACK_SIZES, out, packed, 1)
     for n, m, o in zip(PACK_SIZES, mats, out):
         assert np.array_equal(host(o), oracle.unpack_upper(oracle.pack_upper(m), n)), n
+    # direction 2: upper triangle only, the strict lower triangle keeps its contents
+    base = [rng.standard_normal((n, n)).astype(np.float32) for n in PACK_SIZES]
+    out = [to_dev(b) for b in base]
+    say("kfac_pack_sym direction 2")
+    kfac_gpu.kfac_pack_sym(PACK_SIZES, out, packed, 2)
+    for n, m, b, o in zip(PACK_SIZES, mats, base, out):
+        want = np.where(np.triu(np.ones((n, n), dtype=bool)),
+                        oracle.unpack_upper(oracle.pack_upper(m), n), b)
+        assert np.array_equal(host(o), want), n
 
 
 # ---------------------------------------------------------------------------
