@@ -77,6 +77,19 @@ __global__ void __launch_bounds__(256) inv_prep_kernel(const InvDesc* __restrict
   }
 }
 
+// In-place damping when every matrix is inverted in place: one block per 128 rows
+// adds the shift to the diagonal (and block 0 of a matrix zeroes its info), instead of
+// a grid over all prep tiles in which only the diagonal ones have work.
+__global__ void __launch_bounds__(TB) inv_damp_kernel(const InvDesc* __restrict__ desc,
+                                                      const int32_t* __restrict__ begin, int count) {
+  const int p = find_problem(begin, count, blockIdx.x);
+  const InvDesc& d = desc[p];
+  const int kb = blockIdx.x - begin[p];
+  if (kb == 0 && threadIdx.x == 0) *gp(d.info) = 0;
+  const int64_t i = int64_t(kb) * TB + threadIdx.x;
+  if (i < d.n) gp(d.S)[i * d.n + i] += d.shift;
+}
+
 // Pivot of step k: U = chol(P) and E = U^-T of the pivot block P (bk x bk, upper
 // triangle in S; padding rows and columns hold the identity), then P^-1 = E^T E.
 // One 512-thread block keeps the combined matrix M in LDS: its upper triangle
@@ -372,6 +385,27 @@ inv_panel_kernel(const InvDesc* __restrict__ desc, const int32_t* __restrict__ b
   const int r0 = h * (TB / 2);
   if (r0 >= bk) return;  // no pivot rows in this half
   const int tid = threadIdx.x;
+  const int grp = tid >> 8, w = (tid >> 6) & 3, lane = tid & 63;
+  const int ml = lane & 31, kh = lane >> 5;
+  const int mr = r0 + 32 * (w >> 1);  // first row of this wave's slab
+  const int nc = 64 * (w & 1);        // first column
+  // A operand element (k, m) = Ui[k][m] (Y) or P^-1[k][m] (W); zero for k, m >= bk
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(grp == 0 ? d.Ui : d.P), 0, TB * TB * 4, 0x00020000);
+  const int kmax = grp == 0 ? min(bk, mr + 32) : bk;
+  const int nchunk = (kmax + 31) >> 5;  // wave-uniform
+  const int m = mr + ml;
+  auto load_a = [&](float (&a)[16], int c) {
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      const int kk = 32 * c + 2 * s + kh;
+      const bool ok = kk < bk && m < bk && c < nchunk;
+      a[s] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+          rs, ok ? static_cast<unsigned>(kk * TB + m) * 4u : 0x80000000u, 0, 0));
+    }
+  };
+  float acur[16], anext[16];
+  load_a(acur, 0);  // in flight together with the V loads
   __shared__ __attribute__((aligned(16))) float Vs[TB * LDP];
   {  // all 32 loads of a thread in flight first (clamped addresses, zero outside)
     const int lo = tid & (TB - 1), hi0 = tid >> 7;  // along a row of S / first row
@@ -398,27 +432,6 @@ inv_panel_kernel(const InvDesc* __restrict__ desc, const int32_t* __restrict__ b
       for (int q = 0; q < TB * TB / PP; ++q) Vs[r * LDP + hi0 + 4 * q] = v[q];
     }
   }
-  const int grp = tid >> 8, w = (tid >> 6) & 3, lane = tid & 63;
-  const int ml = lane & 31, kh = lane >> 5;
-  const int mr = r0 + 32 * (w >> 1);  // first row of this wave's slab
-  const int nc = 64 * (w & 1);        // first column
-  // A operand element (k, m) = Ui[k][m] (Y) or P^-1[k][m] (W); zero for k, m >= bk
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<float*>(grp == 0 ? d.Ui : d.P), 0, TB * TB * 4, 0x00020000);
-  const int kmax = grp == 0 ? min(bk, mr + 32) : bk;
-  const int nchunk = (kmax + 31) >> 5;  // wave-uniform
-  const int m = mr + ml;
-  auto load_a = [&](float (&a)[16], int c) {
-#pragma unroll
-    for (int s = 0; s < 16; ++s) {
-      const int kk = 32 * c + 2 * s + kh;
-      const bool ok = kk < bk && m < bk && c < nchunk;
-      a[s] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-          rs, ok ? static_cast<unsigned>(kk * TB + m) * 4u : 0x80000000u, 0, 0));
-    }
-  };
-  float acur[16], anext[16];
-  load_a(acur, 0);
   v16f acc0, acc1;
 #pragma unroll
   for (int e = 0; e < 16; ++e) acc0[e] = acc1[e] = 0.f;
@@ -704,9 +717,17 @@ extern "C" kfac_status kfac_invert(int32_t count, const int32_t* n, const float*
   // two panel blocks per tile, in groups of 16 blocks covering 8 tiles
   auto panel_grid = [](unsigned tiles) { return (tiles + 7) / 8 * 16; };
 
-  KFAC_LAUNCH(K_INV_PREP, inv_prep_kernel, dim3(grid_of(pl.t64_begin, count, t64_of)), dim3(256), 0, s,
-              d_desc, d_t64, count);
-  KFAC_CHECK_LAUNCH("inv_prep_kernel");
+  bool in_place = true;
+  for (int m = 0; m < count; ++m) in_place = in_place && mat[m] == inv[m];
+  if (in_place) {
+    KFAC_LAUNCH(K_INV_PREP, inv_damp_kernel, dim3(grid_of(pl.panel_begin, count, panels_of)), dim3(TB), 0, s,
+                d_desc, d_panel, count);
+    KFAC_CHECK_LAUNCH("inv_damp_kernel");
+  } else {
+    KFAC_LAUNCH(K_INV_PREP, inv_prep_kernel, dim3(grid_of(pl.t64_begin, count, t64_of)), dim3(256), 0, s,
+                d_desc, d_t64, count);
+    KFAC_CHECK_LAUNCH("inv_prep_kernel");
+  }
   auto update = [&](int a, int k, int pair) -> kfac_status {
     const unsigned ut = grid_of(pl.tile_begin, a, tiles_of);
     KFAC_LAUNCH(K_INV_UPDATE, inv_update_kernel, dim3(xcd_grid(ut)), dim3(512), 0, s, d_desc, d_tile, a, k,

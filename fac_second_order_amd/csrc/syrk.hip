@@ -512,7 +512,19 @@ __global__ void __launch_bounds__(256) syrk_reduce_kernel(const SyrkDesc* __rest
   if (i < d.d_core && j0 + 3 >= i && j0 < d.d_core) {
     const float* P = d.partial + int64_t(t) * ST * ST + e0;
     float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s = 0; s < d.splits; ++s) {
+    // eight splits' loads in flight, then added in split order
+    constexpr int U = 8;
+    int s = 0;
+    for (; s + U <= d.splits; s += U) {
+      v4f x[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) x[u] = *reinterpret_cast<const KG v4f*>(gp(P) + (s + u) * tstride);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        sum.x += x[u].x; sum.y += x[u].y; sum.z += x[u].z; sum.w += x[u].w;
+      }
+    }
+    for (; s < d.splits; ++s) {
       const v4f x = *reinterpret_cast<const KG v4f*>(gp(P) + s * tstride);
       sum.x += x.x; sum.y += x.y; sum.z += x.z; sum.w += x.w;
     }
@@ -529,8 +541,18 @@ __global__ void __launch_bounds__(256) syrk_reduce_kernel(const SyrkDesc* __rest
   if (part == 0 && ti == tj && d.bias && threadIdx.x < ST) {
     const int ib = ti * ST + threadIdx.x;
     if (ib < d.d_core) {
+      const KG float* pc = gp(d.pcol) + int64_t(ti) * ST + threadIdx.x;
+      const int64_t sstride = int64_t(d.nb) * ST;
       float sum = 0.f;
-      for (int s = 0; s < d.splits; ++s) sum += gp(d.pcol)[(int64_t(s) * d.nb + ti) * ST + threadIdx.x];
+      int s = 0;
+      for (; s + 8 <= d.splits; s += 8) {
+        float x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = pc[(s + u) * sstride];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) sum += x[u];
+      }
+      for (; s < d.splits; ++s) sum += pc[s * sstride];
       const int64_t o = packed_off(ib, d.d_core, d.d);
       gp(d.out)[o] = blend(sum * d.inv_r, d.out, o, decay);
     }
