@@ -155,17 +155,33 @@ __global__ void __launch_bounds__(256) bn_finish_kernel(const BnDesc* __restrict
   const int q = threadIdx.x / FIN_CH;
   float fg = 0.f, fb = 0.f, gg = 0.f, gb = 0.f;
   if (c < d.c) {
-    for (int s = q; s < d.n; s += FIN_LANES) {
-      float a = 0.f, b = 0.f;
-      for (int k = 0; k < d.nchunk; ++k) {
-        const v2f v = gp(d.partial)[(int64_t(s) * d.nchunk + k) * d.c + c];
-        a += v.x;
-        b += v.y;
+    // this lane's (sample, chunk) pairs in order, samples q, q + 8, ..., eight loads
+    // in flight; a sample's chunks are added in chunk order
+    const int total = (d.n - q + FIN_LANES - 1) / FIN_LANES * d.nchunk;
+    float a = 0.f, b = 0.f;
+    int k = 0;
+    for (int base = 0; base < total; base += 8) {
+      v2f v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int idx = base + u;
+        const int s = q + FIN_LANES * (idx / d.nchunk), kk = idx % d.nchunk;
+        v[u] = idx < total ? gp(d.partial)[(int64_t(s) * d.nchunk + kk) * d.c + c] : v2f{0.f, 0.f};
       }
-      fg = fmaf(a, a, fg);
-      fb = fmaf(b, b, fb);
-      gg += a;
-      gb += b;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (base + u >= total) break;
+        a += v[u].x;
+        b += v[u].y;
+        if (++k == d.nchunk) {
+          fg = fmaf(a, a, fg);
+          fb = fmaf(b, b, fb);
+          gg += a;
+          gb += b;
+          a = b = 0.f;
+          k = 0;
+        }
+      }
     }
   }
   __shared__ float4 red[256];
@@ -324,12 +340,11 @@ static kfac_status bn_impl(const kfac_bn* layers, int32_t count, kfac_dtype in_d
     off += partial_count(d);
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  st = upload(d_desc, desc.data(), sizeof(BnDesc) * count, s);
-  if (st) return st;
-  st = upload(d_begin, begin.data(), sizeof(int32_t) * count, s);
-  if (st) return st;
-  st = upload(d_cbegin, cbegin.data(), sizeof(int32_t) * count, s);
-  if (st) return st;
+  TableUpload tu;
+  tu.add(d_desc, desc.data(), sizeof(BnDesc) * count);
+  tu.add(d_begin, begin.data(), sizeof(int32_t) * count);
+  tu.add(d_cbegin, cbegin.data(), sizeof(int32_t) * count);
+  if ((st = tu.flush(s))) return st;
   KFAC_LAUNCH(K_BN_PARTIAL, bn_partial_kernel, dim3(static_cast<unsigned>(items)), dim3(256), 0, s,
               d_desc, d_begin, count, in_dtype == KFAC_F32 ? 1 : 0);
   KFAC_CHECK_LAUNCH("bn_partial_kernel");

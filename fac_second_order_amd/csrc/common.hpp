@@ -54,6 +54,25 @@ kfac_status check_workspace(const void* ws, size_t ws_bytes, size_t need);
 // stream-ordered, needs no pinned host memory and keeps no host pointer.
 kfac_status upload(void* dst_device, const void* src_host, size_t bytes, hipStream_t stream);
 
+// The descriptor tables of one call, carved one after another from the workspace,
+// sent as one image (the alignment gaps between them are written with zeros), so a
+// call pays for as few upload launches as its total table size needs.
+class TableUpload {
+ public:
+  void add(void* dst_device, const void* src_host, size_t bytes) {
+    if (bytes) parts_.push_back({static_cast<char*>(dst_device), static_cast<const char*>(src_host), bytes});
+  }
+  kfac_status flush(hipStream_t stream);
+
+ private:
+  struct Part {
+    char* dst;
+    const char* src;
+    size_t bytes;
+  };
+  std::vector<Part> parts_;
+};
+
 // ---- per-kernel timing ----------------------------------------------------
 enum KernelId {
   K_UPLOAD = 0,

@@ -71,6 +71,21 @@ kfac_status upload(void* dst_device, const void* src_host, size_t bytes, hipStre
   return KFAC_OK;
 }
 
+kfac_status TableUpload::flush(hipStream_t stream) {
+  if (parts_.empty()) return KFAC_OK;
+  char* base = parts_.front().dst;
+  size_t end = 0;
+  for (const Part& q : parts_) {  // tables in carve order, none overlapping the next
+    if (q.dst < base + end) return fail(KFAC_ERR_INVALID, "internal: descriptor tables out of order");
+    end = static_cast<size_t>(q.dst - base) + q.bytes;
+  }
+  if (end % 4 != 0) return fail(KFAC_ERR_INVALID, "internal: table size not a multiple of 4");
+  std::vector<char> image(end, 0);
+  for (const Part& q : parts_) std::memcpy(image.data() + (q.dst - base), q.src, q.bytes);
+  parts_.clear();
+  return upload(base, image.data(), end, stream);
+}
+
 // ---- timing ------------------------------------------------------------------
 struct TimingRec {
   int id;

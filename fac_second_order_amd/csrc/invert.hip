@@ -698,14 +698,12 @@ extern "C" kfac_status kfac_invert(int32_t count, const int32_t* n, const float*
     d.Y = wsf + off; off += size_t(2) * TB * d.ldy;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  st = upload(d_desc, desc.data(), sizeof(InvDesc) * count, s);
-  if (st) return st;
-  st = upload(d_tile, pl.tile_begin.data(), sizeof(int32_t) * count, s);
-  if (st) return st;
-  st = upload(d_panel, pl.panel_begin.data(), sizeof(int32_t) * count, s);
-  if (st) return st;
-  st = upload(d_t64, pl.t64_begin.data(), sizeof(int32_t) * count, s);
-  if (st) return st;
+  TableUpload tu;
+  tu.add(d_desc, desc.data(), sizeof(InvDesc) * count);
+  tu.add(d_tile, pl.tile_begin.data(), sizeof(int32_t) * count);
+  tu.add(d_panel, pl.panel_begin.data(), sizeof(int32_t) * count);
+  tu.add(d_t64, pl.t64_begin.data(), sizeof(int32_t) * count);
+  if ((st = tu.flush(s))) return st;
   // grid sizes for the active prefix [0, a): begin[a] or the grand total
   auto grid_of = [&](const std::vector<int32_t>& begin, int a, auto per) -> unsigned {
     if (a < count) return static_cast<unsigned>(begin[a]);

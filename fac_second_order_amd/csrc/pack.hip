@@ -129,10 +129,10 @@ extern "C" kfac_status kfac_pack_sym(int32_t count, const int32_t* n, float* con
   Carver cv(workspace);
   PackDesc* d_desc = cv.take<PackDesc>(count);
   int32_t* d_begin = cv.take<int32_t>(count);
-  st = upload(d_desc, desc.data(), sizeof(PackDesc) * count, s);
-  if (st) return st;
-  st = upload(d_begin, begin.data(), sizeof(int32_t) * count, s);
-  if (st) return st;
+  TableUpload tu;
+  tu.add(d_desc, desc.data(), sizeof(PackDesc) * count);
+  tu.add(d_begin, begin.data(), sizeof(int32_t) * count);
+  if ((st = tu.flush(s))) return st;
   if (direction == 0) {
     KFAC_LAUNCH(K_PACK, pack_kernel, dim3(static_cast<unsigned>(tiles)), dim3(256), 0, s, d_desc, d_begin, count);
     KFAC_CHECK_LAUNCH("pack_kernel");

@@ -214,10 +214,12 @@ static kfac_status precond_impl(int32_t count, const int32_t* d_g, const int32_t
   }
   if (n1 >= (int64_t(1) << 31)) return fail(KFAC_ERR_INVALID, "too many tiles");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if ((st = upload(d1, g1.data(), sizeof(GemmDesc) * count, s))) return st;
-  if ((st = upload(d2, g2.data(), sizeof(GemmDesc) * count, s))) return st;
-  if ((st = upload(b1, e1.data(), sizeof(int32_t) * count, s))) return st;
-  if ((st = upload(b2, e2.data(), sizeof(int32_t) * count, s))) return st;
+  TableUpload tu;
+  tu.add(d1, g1.data(), sizeof(GemmDesc) * count);
+  tu.add(d2, g2.data(), sizeof(GemmDesc) * count);
+  tu.add(b1, e1.data(), sizeof(int32_t) * count);
+  tu.add(b2, e2.data(), sizeof(int32_t) * count);
+  if ((st = tu.flush(s))) return st;
   if (accum == KFAC_F64) {
     KFAC_LAUNCH(K_GEMM, gemm_tn64_kernel, dim3(static_cast<unsigned>(n1)), dim3(512), 0, s, d1, b1, count);
     KFAC_CHECK_LAUNCH("gemm_tn64_kernel (G^-1 dW)");

@@ -816,16 +816,14 @@ extern "C" kfac_status kfac_factors(const kfac_layer* layers, int32_t count, kfa
     }
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  st = upload(d_desc, pl.desc.data(), sizeof(SyrkDesc) * np, s);
-  if (st) return st;
-  st = upload(d_begin, pl.begin.data(), sizeof(int32_t) * np, s);
-  if (st) return st;
+  TableUpload tu;
+  tu.add(d_desc, pl.desc.data(), sizeof(SyrkDesc) * np);
+  tu.add(d_begin, pl.begin.data(), sizeof(int32_t) * np);
   if (nr) {
-    st = upload(d_rbegin, pl.rbegin.data(), sizeof(int32_t) * nr, s);
-    if (st) return st;
-    st = upload(d_rprob, pl.rprob.data(), sizeof(int32_t) * nr, s);
-    if (st) return st;
+    tu.add(d_rbegin, pl.rbegin.data(), sizeof(int32_t) * nr);
+    tu.add(d_rprob, pl.rprob.data(), sizeof(int32_t) * nr);
   }
+  if ((st = tu.flush(s))) return st;
   const unsigned grid = static_cast<unsigned>(8 * pl.seg_max);
   if (in_dtype == KFAC_F16) {
     KFAC_LAUNCH(K_SYRK, syrk_f16_kernel, dim3(grid), dim3(256), 0, s, d_desc, d_begin, np, pl.segs, ema_decay);
