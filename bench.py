@@ -119,11 +119,36 @@ def work(layers, bns):
     n_all = [l.d_a for l in layers] + [l.d_g for l in layers]
     inv = sum(n ** 3 for n in n_all)
     pre = sum(2 * l.d_g ** 2 * l.d_a + 2 * l.d_g * l.d_a ** 2 for l in layers)
-    pack_bytes = sum(n * (n + 1) // 2 * 4 + n * n * 4 for n in n_all)
+    # the step unpacks the upper triangle only (the inverse reads no more): read + write
+    pack_bytes = sum(2 * (n * (n + 1) // 2 * 4) for n in n_all)
+    finish_bytes = sum(n * (n + 1) // 2 * 4 + n * n * 4 for n in n_all)
     bn_bytes = sum(2 * b.n * b.hw * b.c * 2 + 4 * b.c * 4 for b in bns)
     upd, row = inverse_update_flops(n_all)
     return {"syrk_flop": syrk, "inv_flop": inv, "pre_flop": pre, "pack_bytes": pack_bytes,
-            "bn_bytes": bn_bytes, "update_flop": upd, "rowupd_flop": row}
+            "finish_bytes": finish_bytes, "bn_bytes": bn_bytes, "update_flop": upd, "rowupd_flop": row}
+
+
+def stage_rates(kern, w):
+    """Per-stage rates from the per-kernel breakdown (ms per step): algorithmic work of
+    the stage over the summed time of its kernels, against the stage's bound."""
+    def ms(*names):
+        return sum(kern.get(n, (0.0, 0))[0] for n in names)
+    out = {}
+    for stage, names, work_, unit, peak in (
+            ("factors", ("syrk_tile_kernel", "syrk_reduce_kernel"), w["syrk_flop"], "TFLOP/s", PEAK_FP16_MFMA),
+            ("inverse", ("inv_prep_kernel", "inv_pivot_kernel", "inv_panel_kernel", "inv_rowupd_kernel",
+                         "inv_update_kernel", "inv_finish_kernel"), w["inv_flop"], "TFLOP/s", PEAK_FP32_MFMA),
+            ("precondition", ("gemm_tn_kernel",), w["pre_flop"], "TFLOP/s", PEAK_FP32_MFMA),
+            ("bn", ("bn_partial_kernel", "bn_finish_kernel"), w["bn_bytes"], "GB/s", PEAK_HBM),
+            ("unpack", ("unpack_kernel",), w["pack_bytes"], "GB/s", PEAK_HBM),
+            ("inverse_finish", ("inv_finish_kernel",), w["finish_bytes"], "GB/s", PEAK_HBM)):
+        t = ms(*names)
+        if t <= 0:
+            continue
+        rate = work_ / (t * 1e-3) / (1e12 if unit == "TFLOP/s" else 1e9)
+        out[stage] = {"ms": round(t, 4), "achieved": round(rate, 1), "unit": unit, "peak": peak,
+                      "frac": round(rate / peak, 4)}
+    return out
 
 
 # ---------------------------------------------------------------------------
@@ -451,6 +476,7 @@ def main():
         "cpu_baseline": cpu,
         "kernels_ms_per_step": {k: round(v[0], 4) for k, v in
                                 sorted(kern.items(), key=lambda kv: -kv[1][0])},
+        "stage_rates": stage_rates(kern, w) if kern else None,
         "step_tflop": round((w["syrk_flop"] + w["inv_flop"] + w["pre_flop"]) / 1e12, 4),
     }
     print(json.dumps(out), flush=True)
