@@ -50,6 +50,21 @@ def test_pack_unpack_bitexact(kfac_gpu):
         want = np.where(np.triu(np.ones((n, n), dtype=bool)),
                         oracle.unpack_upper(oracle.pack_upper(m), n), b)
         assert np.array_equal(host(o), want), n
+    # direction 2 from packed buffers that are only 4-byte aligned (element loads)
+    sizes = [3, 129, 577]
+    src = [oracle.pack_upper(m) for m in mats if m.shape[0] in sizes]
+    store = [torch.zeros(p.size + 1, device="cuda") for p in src]
+    views = []
+    for st_, p in zip(store, src):
+        st_[1:] = to_dev(p)
+        views.append(st_[1:])
+    base = [rng.standard_normal((n, n)).astype(np.float32) for n in sizes]
+    out = [to_dev(b) for b in base]
+    say("kfac_pack_sym direction 2, unaligned packed", sizes)
+    kfac_gpu.kfac_pack_sym(sizes, out, views, 2)
+    for n, p, b, o in zip(sizes, src, base, out):
+        want = np.where(np.triu(np.ones((n, n), dtype=bool)), oracle.unpack_upper(p, n), b)
+        assert np.array_equal(host(o), want), n
 
 
 # ---------------------------------------------------------------------------
