@@ -136,7 +136,7 @@ def stage_rates(kern, w):
     out = {}
     for stage, names, work_, unit, peak in (
             ("factors", ("syrk_tile_kernel", "syrk_reduce_kernel"), w["syrk_flop"], "TFLOP/s", PEAK_FP16_MFMA),
-            ("inverse", ("inv_prep_kernel", "inv_pivot_kernel", "inv_panel_kernel", "inv_rowupd_kernel",
+            ("inverse", ("inv_prep_kernel", "inv_pivot_kernel", "inv_panel_kernel",
                          "inv_update_kernel", "inv_finish_kernel"), w["inv_flop"], "TFLOP/s", PEAK_FP32_MFMA),
             ("precondition", ("gemm_tn_kernel",), w["pre_flop"], "TFLOP/s", PEAK_FP32_MFMA),
             ("bn", ("bn_partial_kernel", "bn_finish_kernel"), w["bn_bytes"], "GB/s", PEAK_HBM),

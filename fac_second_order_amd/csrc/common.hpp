@@ -84,7 +84,6 @@ enum KernelId {
   K_INV_PIVOT,
   K_INV_PANEL,
   K_INV_UPDATE,
-  K_INV_ROWUPD,
   K_INV_FINISH,
   K_GEMM,
   K_BN_PARTIAL,

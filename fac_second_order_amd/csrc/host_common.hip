@@ -127,7 +127,7 @@ TimerScope::~TimerScope() {
 static const char* const kKernelNames[K_COUNT] = {
     "upload_kernel",      "syrk_tile_kernel",   "syrk_reduce_kernel", "pack_kernel",
     "unpack_kernel",      "inv_prep_kernel",    "inv_pivot_kernel",   "inv_panel_kernel",
-    "inv_update_kernel",  "inv_rowupd_kernel",  "inv_finish_kernel",  "gemm_tn_kernel",     "bn_partial_kernel",
+    "inv_update_kernel",  "inv_finish_kernel",  "gemm_tn_kernel",     "bn_partial_kernel",
     "bn_finish_kernel"};
 
 }  // namespace kfac

@@ -19,7 +19,9 @@
 // The update works on the square root Y of V^T P^-1 V, so its rounding errors scale
 // with |Y|^2 rather than with |V| |P^-1 V| (which an explicit P^-1 would give).
 // Steps are taken in pairs (k, k+1): after panel k only the tiles of block row
-// k+1 take step k's update (row update), then pivot and panel k+1 run, and one
+// k+1 take step k's update (row update; the pivot of k+1 applies it to its own
+// diagonal block, and the other tiles are extra blocks of that pivot's launch), then
+// panel k+1 runs, and one
 // update applies both steps, S_ij -= [Y_i; Y'_i]^T [Y_j; Y'_j], a rank-256 product
 // that reads and writes each tile once for two steps (tiles in block row k take
 // only step k+1's half). After the last step S = -M^-1; the finish kernel negates
@@ -36,7 +38,6 @@ struct InvDesc {
   float* S;        // working matrix = the output buffer
   float* chol;     // optional U output (nullptr)
   int32_t* info;   // this matrix's info entry
-  float* E;        // [TB][TB]  U_kk^-T (lower triangular)
   float* Ui;       // [TB][TB]  U_kk^-1 (upper triangular)
   float* P;        // [TB][TB]  P^-1 = E^T E (full)
   float* Y;        // [2*TB][ldy] Y panels of steps k (rows 0..) and k+1 (rows TB..)
@@ -106,9 +107,9 @@ __global__ void __launch_bounds__(TB) inv_damp_kernel(const InvDesc* __restrict_
 //      blocks it still needs: K > J with I <= K (the trailing upper triangle),
 //      K < J (the E part) and K = J, which becomes -M_JI^T E_JJ.
 // The lower blocks right of the current sub-step are never read before their own
-// sub-step overwrites them, so they start as zero. Writes E and U^-1 = E^T
-// (row-major, TB x TB), P^-1 to the workspace, S_kk = -P^-1, U into chol when asked,
-// and the 1-based failing column into info.
+// sub-step overwrites them, so they start as zero. Writes U^-1 = E^T (row-major,
+// TB x TB) and P^-1 to the workspace (the operands of the panel), S_kk = -P^-1, U into
+// chol when asked, and the 1-based failing column into info.
 constexpr int PT = 512;           // threads of the pivot kernel
 constexpr int SB = 32;            // sub-step width
 constexpr int MLD = TB + 4;       // LDS pitch of M
@@ -211,20 +212,52 @@ __device__ __forceinline__ int chol32(float* blk, float* ej, float* ejt, float* 
   return failed;
 }
 
+// Update of step k: S_ij -= Y_i^T Y_j over the upper 128-tile of row blocks i, j,
+// with rows [kb, ke) of the stacked panel buffer.
+// 512-thread blocks (the oct engine).
+__device__ __forceinline__ void update_tile(const InvDesc& d, int ti, int tj, int kb, int ke, float* lds) {
+  const int n = d.n, i0 = ti * TB, j0 = tj * TB;
+  const int bi = min(TB, n - i0), bj = min(TB, n - j0);
+  Oct o;
+  float* C = d.S + int64_t(i0) * n + j0;
+  oct_load(o, C, n, bi, bj);
+  // panel rows are 16-byte aligned with pitch ldy = n rounded up to 4 (workspace carve-out)
+  const float* Y = d.Y + int64_t(kb) * d.ldy;
+  oct_gemm(o, op_rows(Y, d.ldy, ke - kb, i0, n), op_rows(Y, d.ldy, ke - kb, j0, n), ke - kb, -1.f, lds);
+  oct_store(o, C, n, bi, bj);
+}
+
 // Pivot of step k. Sub-step J runs, after barriers: A (wave 0 factors the diagonal
 // block while waves 1..7 finish sub-step J-1's updates outside block row J),
 // B (block row J times E_JJ), C (sub-step J's update of the next diagonal block
 // only, which A of J+1 needs first).
-__global__ void __launch_bounds__(PT) inv_pivot_kernel(const InvDesc* __restrict__ desc, int k) {
-  const InvDesc& d = desc[blockIdx.x];
-  const int n = d.n, k0 = k * TB, bk = min(TB, n - k0);
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, scalar
+// Blocks [0, a) are the pivots of matrices 0..a-1. For the second step of a pair
+// (pre = 1), the first step's update of block row k has not been applied yet: each
+// pivot first applies it to its own diagonal block (S_kk -= Y_k^T Y_k, Y_k the first
+// step's panel), and blocks [a, a + rows) apply it to the other tiles of block row k,
+// (k, j) for j != k-1, k, which nothing else in the launch reads or writes; they find
+// their tile through the panel offsets `begin`.
+__global__ void __launch_bounds__(PT) inv_pivot_kernel(const InvDesc* __restrict__ desc,
+                                                       const int32_t* __restrict__ begin, int a, int k,
+                                                       int pre, int rows) {
   __shared__ __attribute__((aligned(16))) float M[TB * MLD];
   __shared__ __attribute__((aligned(16))) float PL[TB * MLD];  // U^-1 = E^T, then P^-1
   __shared__ __attribute__((aligned(16))) float EJ[2][SB * ELD], EJT[2][SB * ELD];
   __shared__ __attribute__((aligned(16))) float urow[2][SB / 2];
   __shared__ float diagU[TB];
+  if (static_cast<int>(blockIdx.x) >= a) {  // a tile of block row k (M is the staging LDS)
+    const int t = blockIdx.x - a;
+    if (t >= rows) return;
+    const int p = find_problem(begin, a, t);
+    const int j = t - begin[p];
+    if (j == k - 1 || j == k) return;
+    update_tile(desc[p], min(j, k), max(j, k), 0, TB, M);
+    return;
+  }
+  const InvDesc& d = desc[blockIdx.x];
+  const int n = d.n, k0 = k * TB, bk = min(TB, n - k0);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, scalar
 
   {  // thread: column tid % 128, rows tid / 128 + 4q; all 32 loads in flight first
     const int j = tid & (TB - 1), r0 = tid >> 7;
@@ -237,6 +270,23 @@ __global__ void __launch_bounds__(PT) inv_pivot_kernel(const InvDesc* __restrict
     }
 #pragma unroll
     for (int q = 0; q < TB / 4; ++q) M[(r0 + 4 * q) * MLD + j] = v[q];
+  }
+  if (pre) {  // S_kk -= Y_k^T Y_k on the upper triangle, PL as the staging buffer
+    __syncthreads();
+    Oct o;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o.c[b][e] = M[oct_row(lane, e) * MLD + oct_col(lane, b)];
+    const float* Y = d.Y;  // rows 0..TB of the panel buffer: the first step's panel
+    oct_gemm(o, op_rows(Y, d.ldy, TB, k0, n), op_rows(Y, d.ldy, TB, k0, n), TB, -1.f, PL);  // ends with a barrier
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int r = oct_row(lane, e), c = oct_col(lane, b);
+        if (r <= c && c < bk) M[r * MLD + c] = o.c[b][e];
+      }
   }
   for (int e = tid; e < TB * TB / 4; e += PT)
     *reinterpret_cast<float4*>(PL + (e >> 5) * MLD + 4 * (e & 31)) = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -301,7 +351,7 @@ __global__ void __launch_bounds__(PT) inv_pivot_kernel(const InvDesc* __restrict
       if (i <= j && j < bk) gp(d.chol)[int64_t(k0 + i) * n + k0 + j] = i == j ? diagU[i] : M[i * MLD + j];
     }
   __syncthreads();
-  // M <- E (zero above the diagonal), E and U^-1 to the workspace (16-byte stores)
+  // M <- E (zero above the diagonal), U^-1 to the workspace (16-byte stores)
   for (int e = tid; e < TB * TB / 4; e += PT) {
     const int i = e >> 5, j = 4 * (e & 31);
     float4 x = *reinterpret_cast<const float4*>(M + i * MLD + j);
@@ -310,7 +360,6 @@ __global__ void __launch_bounds__(PT) inv_pivot_kernel(const InvDesc* __restrict
     if (j + 2 > i) x.z = 0.f;
     if (j + 3 > i) x.w = 0.f;
     *reinterpret_cast<float4*>(M + i * MLD + j) = x;
-    *reinterpret_cast<KG v4f*>(gp(d.E) + i * TB + j) = v4f{x.x, x.y, x.z, x.w};
     const float4 y = *reinterpret_cast<const float4*>(PL + i * MLD + j);
     *reinterpret_cast<KG v4f*>(gp(d.Ui) + i * TB + j) = v4f{y.x, y.y, y.z, y.w};
   }
@@ -508,21 +557,6 @@ inv_panel_kernel(const InvDesc* __restrict__ desc, const int32_t* __restrict__ b
   }
 }
 
-// Update of step k: S_ij -= Y_i^T Y_j over the upper 128-tile of row blocks i, j,
-// with rows [kb, ke) of the stacked panel buffer.
-// 512-thread blocks (the oct engine).
-__device__ __forceinline__ void update_tile(const InvDesc& d, int ti, int tj, int kb, int ke, float* lds) {
-  const int n = d.n, i0 = ti * TB, j0 = tj * TB;
-  const int bi = min(TB, n - i0), bj = min(TB, n - j0);
-  Oct o;
-  float* C = d.S + int64_t(i0) * n + j0;
-  oct_load(o, C, n, bi, bj);
-  // panel rows are 16-byte aligned with pitch ldy = n rounded up to 4 (workspace carve-out)
-  const float* Y = d.Y + int64_t(kb) * d.ldy;
-  oct_gemm(o, op_rows(Y, d.ldy, ke - kb, i0, n), op_rows(Y, d.ldy, ke - kb, j0, n), ke - kb, -1.f, lds);
-  oct_store(o, C, n, bi, bj);
-}
-
 // Update after step k, or after steps k and k+1 when `pair` is set and the matrix
 // has block k+1: every upper tile outside block row k+1 (k when unpaired) takes the
 // rank-(bk + bk1) product of both steps, tiles in block row k only step k+1's half.
@@ -546,19 +580,6 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))
   }
   __shared__ __attribute__((aligned(16))) float lds[4 * CHUNK];
   update_tile(d, ti, tj, kb, ke, lds);
-}
-
-// Step k's update of block row k+1 before its pivot (paired steps): the tiles
-// (k+1, j) for j != k, stored as upper tiles (min, max).
-__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) inv_rowupd_kernel(const InvDesc* __restrict__ desc,
-                                                         const int32_t* __restrict__ begin,
-                                                         int count, int k) {
-  const int p = find_problem(begin, count, blockIdx.x);
-  const InvDesc& d = desc[p];
-  const int j = blockIdx.x - begin[p];
-  if (j == k) return;
-  __shared__ __attribute__((aligned(16))) float lds[4 * CHUNK];
-  update_tile(d, min(j, k + 1), max(j, k + 1), 0, TB, lds);
 }
 
 // inv <- -S with both triangles written (S = inv in place).
@@ -613,7 +634,7 @@ static void plan_inv(int count, const int32_t* n, InvPlan& pl) {
     tiles += int64_t(nb) * (nb + 1) / 2;
     panels += nb;
     t64 += int64_t(nb64) * (nb64 + 1) / 2;
-    pl.floats += size_t(3) * TB * TB + size_t(2) * TB * ((nn + 3) / 4 * 4);
+    pl.floats += size_t(2) * TB * TB + size_t(2) * TB * ((nn + 3) / 4 * 4);
     if (nb > pl.max_nb) pl.max_nb = nb;
   }
   pl.active.assign(pl.max_nb, 0);
@@ -691,7 +712,6 @@ extern "C" kfac_status kfac_invert(int32_t count, const int32_t* n, const float*
     d.nb = (n[m] + TB - 1) / TB;
     d.nb64 = (n[m] + FT - 1) / FT;
     d.shift = shift[m];
-    d.E = wsf + off; off += size_t(TB) * TB;
     d.Ui = wsf + off; off += size_t(TB) * TB;
     d.P = wsf + off; off += size_t(TB) * TB;
     d.ldy = (n[m] + 3) / 4 * 4;
@@ -736,7 +756,7 @@ extern "C" kfac_status kfac_invert(int32_t count, const int32_t* n, const float*
   for (int k = 0; k < pl.max_nb; k += 2) {  // steps in pairs
     const int a0 = pl.active[k];
     const int a1 = k + 1 < pl.max_nb ? pl.active[k + 1] : 0;
-    KFAC_LAUNCH(K_INV_PIVOT, inv_pivot_kernel, dim3(a0), dim3(PT), 0, s, d_desc, k);
+    KFAC_LAUNCH(K_INV_PIVOT, inv_pivot_kernel, dim3(a0), dim3(PT), 0, s, d_desc, d_panel, a0, k, 0, 0);
     KFAC_CHECK_LAUNCH("inv_pivot_kernel");
     const unsigned pg0 = grid_of(pl.panel_begin, a0, panels_of);
     KFAC_LAUNCH(K_INV_PANEL, inv_panel_kernel, dim3(panel_grid(pg0)), dim3(PP), 0, s, d_desc, d_panel, a0, k, 0,
@@ -744,9 +764,9 @@ extern "C" kfac_status kfac_invert(int32_t count, const int32_t* n, const float*
     KFAC_CHECK_LAUNCH("inv_panel_kernel");
     if (a1 > 0) {
       const unsigned pg = grid_of(pl.panel_begin, a1, panels_of);
-      KFAC_LAUNCH(K_INV_ROWUPD, inv_rowupd_kernel, dim3(pg), dim3(512), 0, s, d_desc, d_panel, a1, k);
-      KFAC_CHECK_LAUNCH("inv_rowupd_kernel");
-      KFAC_LAUNCH(K_INV_PIVOT, inv_pivot_kernel, dim3(a1), dim3(PT), 0, s, d_desc, k + 1);
+      // pivot k+1 with step k's update of block row k+1 in the same launch
+      KFAC_LAUNCH(K_INV_PIVOT, inv_pivot_kernel, dim3(a1 + pg), dim3(PT), 0, s, d_desc, d_panel, a1, k + 1, 1,
+                  static_cast<int>(pg));
       KFAC_CHECK_LAUNCH("inv_pivot_kernel");
       KFAC_LAUNCH(K_INV_PANEL, inv_panel_kernel, dim3(panel_grid(pg)), dim3(PP), 0, s, d_desc, d_panel, a1, k + 1,
                   1, static_cast<int>(pg));
