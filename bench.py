@@ -84,14 +84,16 @@ def parse():
 # algorithmic work (what the method must do), per step
 # ---------------------------------------------------------------------------
 
-def inverse_update_flops(n_all):
-    """Algorithmic flops of the inverse's update and row-update kernels per call.
+def inverse_update_flops(n_all, group=2):
+    """Algorithmic flops of the inverse's update launches and of its row updates per
+    call, for block steps taken in groups of `group` (kfac_invert_schedule).
 
-    Block steps run in pairs (k, k+1). A pair's row update gives block row k+1
-    step k's rank-128 product; the pair's update gives every other upper tile both
-    steps (rank 128 + b_{k+1}), or only step k+1's half in block row k; an unpaired
-    last step gives every upper tile outside block row k its rank-b_k product. A
-    tile counts its entries on or above the diagonal, 2 flops per multiply-add."""
+    Before pivot k = kg + s of a group starting at kg, block row k takes the group's
+    earlier steps (rows kg+s' of the group take only the steps after s', having been
+    rewritten by that step's panel). After the group, one update gives every other
+    upper tile the group's steps it has not had: all of them outside the group's
+    rows, the steps after the latest of its own rows inside them. A tile counts its
+    entries on or above the diagonal, 2 flops per multiply-add."""
     upd = row = 0
     for n in n_all:
         nb = -(-n // TB)
@@ -100,21 +102,25 @@ def inverse_update_flops(n_all):
         def area(i, j):
             return bs[i] * bs[j] if i < j else bs[i] * (bs[i] + 1) // 2
 
-        for k in range(0, nb, 2):
-            if k + 1 < nb:
-                row += sum(2 * area(min(j, k + 1), max(j, k + 1)) * bs[k] for j in range(nb) if j != k)
-                for i in range(nb):
-                    for j in range(i, nb):
-                        if k + 1 in (i, j):
-                            continue
-                        kk = bs[k + 1] if k in (i, j) else bs[k] + bs[k + 1]
+        for kg in range(0, nb, group):
+            g = min(group, nb - kg)
+            for s in range(1, g):
+                k = kg + s
+                for j in range(nb):
+                    lo = j - kg + 1 if kg <= j < k else 0
+                    kk = sum(bs[kg + t] for t in range(lo, s))
+                    if kk:
+                        row += 2 * area(min(j, k), max(j, k)) * kk
+            for i in range(nb):
+                for j in range(i, nb):
+                    m = max([x - kg for x in (i, j) if kg <= x < kg + g], default=-1)
+                    kk = sum(bs[kg + t] for t in range(m + 1, g))
+                    if kk:
                         upd += 2 * area(i, j) * kk
-            else:
-                upd += sum(2 * area(i, j) * bs[k] for i in range(nb) for j in range(i, nb) if k not in (i, j))
     return upd, row
 
 
-def work(layers, bns):
+def work(layers, bns, group=2):
     syrk = sum(l.rows * l.d_a * (l.d_a + 1) + l.rows * l.d_g * (l.d_g + 1) for l in layers)
     n_all = [l.d_a for l in layers] + [l.d_g for l in layers]
     inv = sum(n ** 3 for n in n_all)
@@ -123,7 +129,7 @@ def work(layers, bns):
     pack_bytes = sum(2 * (n * (n + 1) // 2 * 4) for n in n_all)
     finish_bytes = sum(n * (n + 1) // 2 * 4 + n * n * 4 for n in n_all)
     bn_bytes = sum(2 * b.n * b.hw * b.c * 2 + 4 * b.c * 4 for b in bns)
-    upd, row = inverse_update_flops(n_all)
+    upd, row = inverse_update_flops(n_all, group)
     return {"syrk_flop": syrk, "inv_flop": inv, "pre_flop": pre, "pack_bytes": pack_bytes,
             "finish_bytes": finish_bytes, "bn_bytes": bn_bytes, "update_flop": upd, "rowupd_flop": row}
 
@@ -376,7 +382,7 @@ def main():
     args.batch = args.batch or 32
     layers = synth.conv_layers(args.batch)
     bns = synth.bn_layers(args.batch)
-    w = work(layers, bns)
+    w = work(layers, bns, kfac.kfac_invert_schedule()[1])
     act, gout, grads, xhat, bgout = make_inputs(layers, bns, dev)
     weights, bn_params = make_params(layers, bns, dev)
     st = kfac.KfacStep(layers, bns, dev, precond_accum=args.precond_accum)

@@ -66,6 +66,7 @@ _sig("kfac_factors", _i32, _P(kfac_layer), _i32, _i32, _P(_vp), _P(_vp), _P(_vp)
 _sig("kfac_pack_sym_workspace", _i32, _i32, _P(_i32), _P(_sz))
 _sig("kfac_pack_sym", _i32, _i32, _P(_i32), _P(_vp), _P(_vp), _i32, _vp, _sz, _vp)
 _sig("kfac_invert_workspace", _i32, _i32, _P(_i32), _P(_sz))
+_sig("kfac_invert_schedule", _i32, _P(_i32), _P(_i32))
 _sig("kfac_invert", _i32, _i32, _P(_i32), _P(_vp), _P(_vp), _P(_f32), _vp, _P(_vp), _vp, _sz, _vp)
 _sig("kfac_precondition_workspace", _i32, _i32, _P(_i32), _P(_i32), _P(_sz))
 _sig("kfac_precondition", _i32, _i32, _P(_i32), _P(_i32), _P(_vp), _P(_vp), _P(_vp), _i32, _P(_vp),
@@ -194,6 +195,13 @@ def kfac_invert_workspace(n):
     out = _sz()
     _check(_lib.kfac_invert_workspace(len(n), _ints(n), _c.byref(out)), "kfac_invert_workspace")
     return out.value
+
+
+def kfac_invert_schedule():
+    """(block size, block steps per update launch) of kfac_invert."""
+    b, g = _i32(), _i32()
+    _check(_lib.kfac_invert_schedule(_c.byref(b), _c.byref(g)), "kfac_invert_schedule")
+    return b.value, g.value
 
 
 def kfac_invert(n, mat, inv, shift, info, chol=None, workspace=None, stream=None):

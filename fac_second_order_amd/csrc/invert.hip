@@ -18,13 +18,14 @@
 //   update: S_ij -= Y_i^T Y_j for all upper tiles i, j != k (fp32 MFMA).
 // The update works on the square root Y of V^T P^-1 V, so its rounding errors scale
 // with |Y|^2 rather than with |V| |P^-1 V| (which an explicit P^-1 would give).
-// Steps are taken in pairs (k, k+1): after panel k only the tiles of block row
-// k+1 take step k's update (row update; the pivot of k+1 applies it to its own
-// diagonal block, and the other tiles are extra blocks of that pivot's launch), then
-// panel k+1 runs, and one
-// update applies both steps, S_ij -= [Y_i; Y'_i]^T [Y_j; Y'_j], a rank-256 product
-// that reads and writes each tile once for two steps (tiles in block row k take
-// only step k+1's half). After the last step S = -M^-1; the finish kernel negates
+// Steps are taken in groups of GS (kg .. kg+GS-1) with one update per group: before
+// pivot k of a group, block row k takes the group's earlier steps (row update; the
+// pivot applies it to its own diagonal block, and the other tiles of the row are
+// extra blocks of that pivot's launch), then panel k writes its Y into slot k - kg of
+// the panel buffer; after the last step one update applies the whole group,
+// S_ij -= [Y_i; Y'_i; ..]^T [Y_j; Y'_j; ..], a rank-(GS*TB) product that reads and
+// writes each tile once per group (tiles in a row of the group take only the steps
+// after that row's own). After the last step S = -M^-1; the finish kernel negates
 // it and writes both triangles. All matrices of a call step together: they are
 // ordered by block count, so the ones still active at step k are a prefix.
 #include <algorithm>
@@ -40,7 +41,7 @@ struct InvDesc {
   int32_t* info;   // this matrix's info entry
   float* Ui;       // [TB][TB]  U_kk^-1 (upper triangular)
   float* P;        // [TB][TB]  P^-1 = E^T E (full)
-  float* Y;        // [2*TB][ldy] Y panels of steps k (rows 0..) and k+1 (rows TB..)
+  float* Y;        // [GS*TB][ldy] Y panels of the steps of a group (step kg+s in rows s*TB..)
   int32_t n, nb;
   float shift;
   int32_t nb64;    // 64-wide blocks (prep/finish tiles)
@@ -49,6 +50,13 @@ struct InvDesc {
 };
 
 constexpr int FT = 64;  // prep/finish tile edge
+// Block steps per update launch (a group): the update of a group applies all its
+// steps at once as one rank-(G*TB) product.
+#ifndef KFAC_INV_GROUP
+#define KFAC_INV_GROUP 3
+#endif
+constexpr int GS = KFAC_INV_GROUP;
+static_assert(GS >= 1 && GS <= 8, "group size");
 
 // S <- upper(mat) + shift*I (S may equal mat); info <- 0.
 __global__ void __launch_bounds__(256) inv_prep_kernel(const InvDesc* __restrict__ desc,
@@ -231,12 +239,13 @@ __device__ __forceinline__ void update_tile(const InvDesc& d, int ti, int tj, in
 // block while waves 1..7 finish sub-step J-1's updates outside block row J),
 // B (block row J times E_JJ), C (sub-step J's update of the next diagonal block
 // only, which A of J+1 needs first).
-// Blocks [0, a) are the pivots of matrices 0..a-1. For the second step of a pair
-// (pre = 1), the first step's update of block row k has not been applied yet: each
-// pivot first applies it to its own diagonal block (S_kk -= Y_k^T Y_k, Y_k the first
-// step's panel), and blocks [a, a + rows) apply it to the other tiles of block row k,
-// (k, j) for j != k-1, k, which nothing else in the launch reads or writes; they find
-// their tile through the panel offsets `begin`.
+// Blocks [0, a) are the pivots of matrices 0..a-1. For step k = kg + pre of a group
+// starting at kg, the updates of the group's earlier steps kg..k-1 have not reached
+// block row k yet: each pivot first applies them to its own diagonal block (S_kk -=
+// Y^T Y over panel rows [0, pre*TB)), and blocks [a, a + rows) apply them to the other
+// tiles (k, j) of the row, which nothing else in the launch reads or writes; they find
+// their tile through the panel offsets `begin`. A tile (k, j) with j = kg + s', s' <
+// pre, was rewritten by the panel of step j and takes only the steps after it.
 __global__ void __launch_bounds__(PT) inv_pivot_kernel(const InvDesc* __restrict__ desc,
                                                        const int32_t* __restrict__ begin, int a, int k,
                                                        int pre, int rows) {
@@ -250,8 +259,10 @@ __global__ void __launch_bounds__(PT) inv_pivot_kernel(const InvDesc* __restrict
     if (t >= rows) return;
     const int p = find_problem(begin, a, t);
     const int j = t - begin[p];
-    if (j == k - 1 || j == k) return;
-    update_tile(desc[p], min(j, k), max(j, k), 0, TB, M);
+    const int kg = k - pre;
+    const int kb = (j >= kg && j < k) ? (j - kg + 1) * TB : 0, ke = pre * TB;
+    if (j == k || kb >= ke) return;
+    update_tile(desc[p], min(j, k), max(j, k), kb, ke, M);
     return;
   }
   const InvDesc& d = desc[blockIdx.x];
@@ -278,8 +289,9 @@ __global__ void __launch_bounds__(PT) inv_pivot_kernel(const InvDesc* __restrict
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int e = 0; e < 16; ++e) o.c[b][e] = M[oct_row(lane, e) * MLD + oct_col(lane, b)];
-    const float* Y = d.Y;  // rows 0..TB of the panel buffer: the first step's panel
-    oct_gemm(o, op_rows(Y, d.ldy, TB, k0, n), op_rows(Y, d.ldy, TB, k0, n), TB, -1.f, PL);  // ends with a barrier
+    const float* Y = d.Y;  // panel rows [0, pre*TB): the group's earlier steps
+    const int K = pre * TB;
+    oct_gemm(o, op_rows(Y, d.ldy, K, k0, n), op_rows(Y, d.ldy, K, k0, n), K, -1.f, PL);  // ends with a barrier
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
@@ -557,27 +569,26 @@ inv_panel_kernel(const InvDesc* __restrict__ desc, const int32_t* __restrict__ b
   }
 }
 
-// Update after step k, or after steps k and k+1 when `pair` is set and the matrix
-// has block k+1: every upper tile outside block row k+1 (k when unpaired) takes the
-// rank-(bk + bk1) product of both steps, tiles in block row k only step k+1's half.
+// Update after the group of steps kg .. kg+g-1 (g = min(GS, nb - kg) per matrix):
+// a tile outside the group's block rows takes the product of all g steps; a tile in
+// block row kg+s (the larger s if both of its indices are in the group) was rewritten
+// by that step's panel and takes only the later steps; the last step's row is left
+// as its panel wrote it.
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) inv_update_kernel(const InvDesc* __restrict__ desc,
                                                          const int32_t* __restrict__ begin,
-                                                         int count, int k, int total, int pair) {
+                                                         int count, int kg, int total) {
   const int v = xcd_virtual(blockIdx.x, gridDim.x, total);
   if (v < 0) return;
   const int p = find_problem(begin, count, v);
   const InvDesc& d = desc[p];
   int ti, tj;
   upper_tile(v - begin[p], d.nb, ti, tj);
-  const bool paired = pair && k + 1 < d.nb;
-  const int kx = paired ? k + 1 : k;  // written by its panel kernel
-  if (ti == kx || tj == kx) return;
-  const int bk = min(TB, d.n - k * TB);
-  int kb = 0, ke = bk;
-  if (paired) {
-    kb = (ti == k || tj == k) ? TB : 0;
-    ke = TB + min(TB, d.n - (k + 1) * TB);
-  }
+  const int g = min(GS, d.nb - kg), last = kg + g - 1;
+  int m = -1;  // latest group step whose panel wrote this tile
+  if (ti >= kg && ti <= last) m = ti - kg;
+  if (tj >= kg && tj <= last) m = max(m, tj - kg);
+  if (m == g - 1) return;
+  const int kb = (m + 1) * TB, ke = (g - 1) * TB + min(TB, d.n - last * TB);
   __shared__ __attribute__((aligned(16))) float lds[4 * CHUNK];
   update_tile(d, ti, tj, kb, ke, lds);
 }
@@ -634,7 +645,7 @@ static void plan_inv(int count, const int32_t* n, InvPlan& pl) {
     tiles += int64_t(nb) * (nb + 1) / 2;
     panels += nb;
     t64 += int64_t(nb64) * (nb64 + 1) / 2;
-    pl.floats += size_t(2) * TB * TB + size_t(2) * TB * ((nn + 3) / 4 * 4);
+    pl.floats += size_t(2) * TB * TB + size_t(GS) * TB * ((nn + 3) / 4 * 4);
     if (nb > pl.max_nb) pl.max_nb = nb;
   }
   pl.active.assign(pl.max_nb, 0);
@@ -715,7 +726,7 @@ extern "C" kfac_status kfac_invert(int32_t count, const int32_t* n, const float*
     d.Ui = wsf + off; off += size_t(TB) * TB;
     d.P = wsf + off; off += size_t(TB) * TB;
     d.ldy = (n[m] + 3) / 4 * 4;
-    d.Y = wsf + off; off += size_t(2) * TB * d.ldy;
+    d.Y = wsf + off; off += size_t(GS) * TB * d.ldy;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   TableUpload tu;
@@ -746,36 +757,34 @@ extern "C" kfac_status kfac_invert(int32_t count, const int32_t* n, const float*
                 d_desc, d_t64, count);
     KFAC_CHECK_LAUNCH("inv_prep_kernel");
   }
-  auto update = [&](int a, int k, int pair) -> kfac_status {
-    const unsigned ut = grid_of(pl.tile_begin, a, tiles_of);
-    KFAC_LAUNCH(K_INV_UPDATE, inv_update_kernel, dim3(xcd_grid(ut)), dim3(512), 0, s, d_desc, d_tile, a, k,
-                static_cast<int>(ut), pair);
-    KFAC_CHECK_LAUNCH("inv_update_kernel");
-    return KFAC_OK;
-  };
-  for (int k = 0; k < pl.max_nb; k += 2) {  // steps in pairs
-    const int a0 = pl.active[k];
-    const int a1 = k + 1 < pl.max_nb ? pl.active[k + 1] : 0;
-    KFAC_LAUNCH(K_INV_PIVOT, inv_pivot_kernel, dim3(a0), dim3(PT), 0, s, d_desc, d_panel, a0, k, 0, 0);
-    KFAC_CHECK_LAUNCH("inv_pivot_kernel");
-    const unsigned pg0 = grid_of(pl.panel_begin, a0, panels_of);
-    KFAC_LAUNCH(K_INV_PANEL, inv_panel_kernel, dim3(panel_grid(pg0)), dim3(PP), 0, s, d_desc, d_panel, a0, k, 0,
-                static_cast<int>(pg0));
-    KFAC_CHECK_LAUNCH("inv_panel_kernel");
-    if (a1 > 0) {
-      const unsigned pg = grid_of(pl.panel_begin, a1, panels_of);
-      // pivot k+1 with step k's update of block row k+1 in the same launch
-      KFAC_LAUNCH(K_INV_PIVOT, inv_pivot_kernel, dim3(a1 + pg), dim3(PT), 0, s, d_desc, d_panel, a1, k + 1, 1,
-                  static_cast<int>(pg));
+  for (int kg = 0; kg < pl.max_nb; kg += GS) {  // steps in groups of GS
+    for (int sg = 0; sg < GS && kg + sg < pl.max_nb; ++sg) {
+      const int k = kg + sg, a = pl.active[k];
+      const unsigned pg = grid_of(pl.panel_begin, a, panels_of);
+      // pivot k; after the first step of a group, with the group's earlier steps
+      // applied to block row k in the same launch
+      KFAC_LAUNCH(K_INV_PIVOT, inv_pivot_kernel, dim3(sg == 0 ? a : a + pg), dim3(PT), 0, s, d_desc, d_panel, a,
+                  k, sg, sg == 0 ? 0 : static_cast<int>(pg));
       KFAC_CHECK_LAUNCH("inv_pivot_kernel");
-      KFAC_LAUNCH(K_INV_PANEL, inv_panel_kernel, dim3(panel_grid(pg)), dim3(PP), 0, s, d_desc, d_panel, a1, k + 1,
-                  1, static_cast<int>(pg));
+      KFAC_LAUNCH(K_INV_PANEL, inv_panel_kernel, dim3(panel_grid(pg)), dim3(PP), 0, s, d_desc, d_panel, a, k, sg,
+                  static_cast<int>(pg));
       KFAC_CHECK_LAUNCH("inv_panel_kernel");
     }
-    if ((st = update(a0, k, 1))) return st;
+    const int a0 = pl.active[kg];
+    const unsigned ut = grid_of(pl.tile_begin, a0, tiles_of);
+    KFAC_LAUNCH(K_INV_UPDATE, inv_update_kernel, dim3(xcd_grid(ut)), dim3(512), 0, s, d_desc, d_tile, a0, kg,
+                static_cast<int>(ut));
+    KFAC_CHECK_LAUNCH("inv_update_kernel");
   }
   KFAC_LAUNCH(K_INV_FINISH, inv_finish_kernel, dim3(grid_of(pl.t64_begin, count, t64_of)), dim3(256), 0, s,
               d_desc, d_t64, count);
   KFAC_CHECK_LAUNCH("inv_finish_kernel");
+  return KFAC_OK;
+}
+
+extern "C" kfac_status kfac_invert_schedule(int32_t* block, int32_t* group) {
+  if (!block || !group) return fail(KFAC_ERR_INVALID, "NULL pointer argument");
+  *block = TB;
+  *group = GS;
   return KFAC_OK;
 }

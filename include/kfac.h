@@ -146,6 +146,10 @@ kfac_status kfac_pack_sym(int32_t count, const int32_t* n, float* const* full,
  * triangle is not written).
  * ------------------------------------------------------------------------- */
 kfac_status kfac_invert_workspace(int32_t count, const int32_t* n, size_t* bytes);
+/* The schedule kfac_invert runs (informational, e.g. for counting the work of its
+ * kernels): *block = the block size of the factorisation, *group = block steps per
+ * update launch. Returns KFAC_ERR_INVALID for NULL pointers. */
+kfac_status kfac_invert_schedule(int32_t* block, int32_t* group);
 kfac_status kfac_invert(int32_t count, const int32_t* n, const float* const* mat,
                         float* const* inv, const float* shift, int32_t* info,
                         float* const* chol, void* workspace, size_t ws_bytes, void* stream);
