@@ -37,7 +37,7 @@ LR = 0.01                # learning rate of the parameter update
 # (FETCH_SIZE, then WRITE_SIZE), calibrated by a plain 1 GiB device copy (fetch x2.0,
 # write x1.0) and summarised in profiles/resnet50_step_hbm_counters.md. Reported only
 # while the kernel's source text still hashes to the value it was measured with.
-MEASURED_TRAFFIC = {"inv_update_kernel": (601554749, "6b628aec1f9b6ac1ea8276187292fc0dee9a1001")}
+MEASURED_TRAFFIC = {"inv_update_kernel": (719749120, "55aceff558b44f8fcc5c788ef3a0d3adaa1a832f")}
 CSRC = os.path.join(ROOT, "fac_second_order_amd", "csrc")
 
 
