@@ -93,17 +93,19 @@ def inverse_update_flops(n_all, group=2):
     rewritten by that step's panel). After the group, one update gives every other
     upper tile the group's steps it has not had: all of them outside the group's
     rows, the steps after the latest of its own rows inside them. A tile counts its
-    entries on or above the diagonal, 2 flops per multiply-add."""
+    entries on or above the diagonal, 2 flops per multiply-add. An order 128m + 1 takes
+    m block steps; its last column is a bordered step of the finish kernel."""
     upd = row = 0
     for n in n_all:
         nb = -(-n // TB)
+        ns = n // TB if (n > TB and n % TB == 1) else nb  # block steps (bordered last column)
         bs = [min(TB, n - i * TB) for i in range(nb)]
 
         def area(i, j):
             return bs[i] * bs[j] if i < j else bs[i] * (bs[i] + 1) // 2
 
-        for kg in range(0, nb, group):
-            g = min(group, nb - kg)
+        for kg in range(0, ns, group):
+            g = min(group, ns - kg)
             for s in range(1, g):
                 k = kg + s
                 for j in range(nb):

@@ -27,7 +27,13 @@
 // writes each tile once per group (tiles in a row of the group take only the steps
 // after that row's own). After the last step S = -M^-1; the finish kernel negates
 // it and writes both triangles. All matrices of a call step together: they are
-// ordered by block count, so the ones still active at step k are a prefix.
+// ordered by order n, so the ones still active at step k are a prefix.
+// An order n = 128m + 1 (a factor with its bias column) would end with a 1-wide block:
+// a whole pivot, panel and rank-1 pass over the matrix for one column. Its last
+// column is instead taken as a bordered step: the sweep runs m block steps (which
+// still update the last column), inv_border_kernel saves the last column v and
+// pivot p, and the finish applies the step as it writes the inverse (with
+// y = p^-1/2 v: S_ij - y_i y_j inside, p^-1 v on the border, -p^-1 at the corner).
 #include <algorithm>
 
 #include "tile_f32.hpp"
@@ -43,6 +49,7 @@ struct InvDesc {
   float* P;        // [TB][TB]  P^-1 = E^T E (full)
   float* Y;        // [GS*TB][ldy] Y panels of the steps of a group (step kg+s in rows s*TB..)
   int32_t n, nb;
+  int32_t ns;      // block steps of the sweep: nb, or nb - 1 with a bordered last column
   float shift;
   int32_t nb64;    // 64-wide blocks (prep/finish tiles)
   int32_t ldy;     // n rounded up to a multiple of 4 (16-byte rows)
@@ -50,6 +57,12 @@ struct InvDesc {
 };
 
 constexpr int FT = 64;  // prep/finish tile edge
+
+// Block steps of the sweep for order n: the last column of an order 128m + 1 (m >= 1)
+// is a bordered step of the finish instead of a 1-wide block step.
+__host__ __device__ inline int block_steps(int n) {
+  return (n > TB && n % TB == 1) ? n / TB : (n + TB - 1) / TB;
+}
 // Block steps per update launch (a group): the update of a group applies all its
 // steps at once as one rank-(G*TB) product.
 #ifndef KFAC_INV_GROUP
@@ -583,7 +596,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))
   const InvDesc& d = desc[p];
   int ti, tj;
   upper_tile(v - begin[p], d.nb, ti, tj);
-  const int g = min(GS, d.nb - kg), last = kg + g - 1;
+  const int g = min(GS, d.ns - kg), last = kg + g - 1;
   int m = -1;  // latest group step whose panel wrote this tile
   if (ti >= kg && ti <= last) m = ti - kg;
   if (tj >= kg && tj <= last) m = max(m, tj - kg);
@@ -593,7 +606,27 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))
   update_tile(d, ti, tj, kb, ke, lds);
 }
 
-// inv <- -S with both triangles written (S = inv in place).
+// Bordered last column (matrix m of the call when ns < nb): after the sweep's last
+// update, saves v_i = S_i,n-1 (i < n-1) and the pivot p = S_n-1,n-1 into the free panel
+// buffer (p at index n-1), sets info to n if p is not a positive finite number (and no
+// earlier pivot failed) and writes U_n-1,n-1 = p^1/2 into chol. One block per matrix.
+__global__ void __launch_bounds__(256) inv_border_kernel(const InvDesc* __restrict__ desc) {
+  const InvDesc& d = desc[blockIdx.x];
+  if (d.ns == d.nb) return;
+  const int64_t n = d.n;
+  KG float* v = gp(d.Y);
+  for (int64_t i = threadIdx.x; i < n; i += 256) v[i] = gp(d.S)[i * n + n - 1];
+  if (threadIdx.x == 0) {
+    const float p = gp(d.S)[(n - 1) * n + n - 1];
+    if (!(p > 0.f && isfinite(p)) && *gp(d.info) == 0) *gp(d.info) = static_cast<int32_t>(n);
+    if (d.chol) gp(d.chol)[(n - 1) * n + n - 1] = p * rsqrtf(p);
+  }
+}
+
+// inv <- -S with both triangles written (S = inv in place); with a bordered last
+// column, the last step applied on the way (saved column v, pivot p, e = p^-1/2 as
+// the pivot kernel forms it: y = e v, S_ij - y_i y_j for i, j < n-1, W_i = e^2 v_i on
+// the border, -e^2 at the corner; the inverse is minus each).
 __global__ void __launch_bounds__(256) inv_finish_kernel(const InvDesc* __restrict__ desc,
                                                          const int32_t* __restrict__ begin, int count) {
   __shared__ float s[FT][FT + 1];
@@ -604,11 +637,27 @@ __global__ void __launch_bounds__(256) inv_finish_kernel(const InvDesc* __restri
   const int64_t n = d.n;
   const int c = threadIdx.x & (FT - 1);
   const int64_t i0 = int64_t(ti) * FT, j0 = int64_t(tj) * FT;
+  const bool border = d.ns != d.nb;
+  float e = 0.f, ee = 0.f, yj = 0.f, vj = 0.f;
+  const KG float* bv = gp(static_cast<const float*>(d.Y));
+  if (border) {
+    e = rsqrtf(bv[n - 1]);
+    ee = e * e;
+    if (j0 + c < n - 1) {
+      vj = bv[j0 + c];
+      yj = e * vj;
+    }
+  }
   for (int r = threadIdx.x >> 6; r < FT; r += 4) {
     const int64_t i = i0 + r, j = j0 + c;
     float v = 0.f;
     if (i < n && j < n && i <= j) {
-      v = -gp(d.S)[i * n + j];
+      float x = gp(d.S)[i * n + j];
+      if (border) {
+        if (j < n - 1) x = fmaf(-(e * bv[i]), yj, x);  // i <= j < n-1
+        else x = i < n - 1 ? ee * bv[i] : -ee;         // border column, corner
+      }
+      v = -x;
       gp(d.S)[i * n + j] = v;
     }
     s[r][c] = v;
@@ -623,9 +672,9 @@ __global__ void __launch_bounds__(256) inv_finish_kernel(const InvDesc* __restri
 struct InvPlan {
   std::vector<int> order;  // matrices sorted by block count, descending
   std::vector<int32_t> tile_begin, panel_begin, t64_begin;
-  std::vector<int32_t> active;  // active[k] = matrices with nb > k
+  std::vector<int32_t> active;  // active[k] = matrices with more than k block steps
   size_t floats = 0;            // E, Ui, P, Y for all matrices
-  int max_nb = 0;
+  int max_ns = 0;               // block steps of the longest sweep
 };
 
 static void plan_inv(int count, const int32_t* n, InvPlan& pl) {
@@ -646,12 +695,12 @@ static void plan_inv(int count, const int32_t* n, InvPlan& pl) {
     panels += nb;
     t64 += int64_t(nb64) * (nb64 + 1) / 2;
     pl.floats += size_t(2) * TB * TB + size_t(GS) * TB * ((nn + 3) / 4 * 4);
-    if (nb > pl.max_nb) pl.max_nb = nb;
+    pl.max_ns = std::max(pl.max_ns, block_steps(nn));
   }
-  pl.active.assign(pl.max_nb, 0);
+  pl.active.assign(pl.max_ns, 0);
   for (int q = 0; q < count; ++q) {
-    const int nb = (n[pl.order[q]] + TB - 1) / TB;
-    for (int k = 0; k < nb; ++k) pl.active[k] = q + 1;
+    const int ns = block_steps(n[pl.order[q]]);  // non-increasing in q (n descending)
+    for (int k = 0; k < ns; ++k) pl.active[k] = q + 1;
   }
 }
 
@@ -721,6 +770,7 @@ extern "C" kfac_status kfac_invert(int32_t count, const int32_t* n, const float*
     d.info = info + m;
     d.n = n[m];
     d.nb = (n[m] + TB - 1) / TB;
+    d.ns = block_steps(n[m]);
     d.nb64 = (n[m] + FT - 1) / FT;
     d.shift = shift[m];
     d.Ui = wsf + off; off += size_t(TB) * TB;
@@ -757,8 +807,8 @@ extern "C" kfac_status kfac_invert(int32_t count, const int32_t* n, const float*
                 d_desc, d_t64, count);
     KFAC_CHECK_LAUNCH("inv_prep_kernel");
   }
-  for (int kg = 0; kg < pl.max_nb; kg += GS) {  // steps in groups of GS
-    for (int sg = 0; sg < GS && kg + sg < pl.max_nb; ++sg) {
+  for (int kg = 0; kg < pl.max_ns; kg += GS) {  // steps in groups of GS
+    for (int sg = 0; sg < GS && kg + sg < pl.max_ns; ++sg) {
       const int k = kg + sg, a = pl.active[k];
       const unsigned pg = grid_of(pl.panel_begin, a, panels_of);
       // pivot k; after the first step of a group, with the group's earlier steps
@@ -775,6 +825,12 @@ extern "C" kfac_status kfac_invert(int32_t count, const int32_t* n, const float*
     KFAC_LAUNCH(K_INV_UPDATE, inv_update_kernel, dim3(xcd_grid(ut)), dim3(512), 0, s, d_desc, d_tile, a0, kg,
                 static_cast<int>(ut));
     KFAC_CHECK_LAUNCH("inv_update_kernel");
+  }
+  bool bordered = false;
+  for (int q = 0; q < count; ++q) bordered = bordered || desc[q].ns != desc[q].nb;
+  if (bordered) {
+    KFAC_LAUNCH(K_INV_FINISH, inv_border_kernel, dim3(count), dim3(256), 0, s, d_desc);
+    KFAC_CHECK_LAUNCH("inv_border_kernel");
   }
   KFAC_LAUNCH(K_INV_FINISH, inv_finish_kernel, dim3(grid_of(pl.t64_begin, count, t64_of)), dim3(256), 0, s,
               d_desc, d_t64, count);

@@ -288,7 +288,8 @@ def test_invert_in_place_matches(kfac_gpu):
 
 def test_invert_breakdown_info(kfac_gpu):
     """Non-positive pivots report the 1-based column (LAPACK potrf convention),
-    including in a later 128-block and for NaN input."""
+    including in a later 128-block, at the bordered last column of an order
+    128m + 1, and for NaN input."""
     n = 300
     cases = []
     F1 = np.eye(n, dtype=np.float32) * 2
@@ -302,12 +303,23 @@ def test_invert_breakdown_info(kfac_gpu):
     F4 = np.eye(4, dtype=np.float32)
     F4[2, 2] = 0.0
     cases.append((F4, 0.0))                          # exact zero pivot 3
+    # orders 128m + 1 end with a bordered column (taken after the block sweep)
+    F5 = np.eye(257, dtype=np.float32) * 2
+    F5[256, 256] = 0.5
+    cases.append((F5, -1.0))                         # last pivot (257) negative
+    F6 = np.eye(129, dtype=np.float32)
+    F6[5, 128] = np.nan
+    cases.append((F6, 0.1))                          # NaN reaches the last pivot 129
+    F7 = np.eye(129, dtype=np.float32) * 2
+    F7[3, 3] = 0.5
+    F7[128, 128] = 0.5
+    cases.append((F7, -1.0))                         # pivot 4 fails first, the last one too
     sizes = [F.shape[0] for F, _ in cases]
     expect = []
     for F, s in cases:
         M = np.triu(F.astype(np.float64)) + np.triu(F.astype(np.float64), 1).T + s * np.eye(F.shape[0])
         expect.append(oracle.cholesky_upper(M)[1])
-    assert expect == [1, 200, 8, 3]
+    assert expect == [1, 200, 8, 3, 257, 129, 4]
     mats = [to_dev(F) for F, _ in cases]
     info = torch.zeros(len(cases), dtype=torch.int32, device="cuda")
     say("kfac_invert breakdown cases")
