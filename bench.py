@@ -37,7 +37,7 @@ LR = 0.01                # learning rate of the parameter update
 # (FETCH_SIZE, then WRITE_SIZE), calibrated by a plain 1 GiB device copy (fetch x2.0,
 # write x1.0) and summarised in profiles/resnet50_step_hbm_counters.md. Reported only
 # while the kernel's source text still hashes to the value it was measured with.
-MEASURED_TRAFFIC = {"inv_update_kernel": (719749120, "55aceff558b44f8fcc5c788ef3a0d3adaa1a832f")}
+MEASURED_TRAFFIC = {"inv_update_kernel": (870325760, "8fc1728f9a418b913c8d2250986191f791d93273")}
 CSRC = os.path.join(ROOT, "fac_second_order_amd", "csrc")
 
 
@@ -90,7 +90,8 @@ def inverse_update_flops(n_all, group=2):
 
     Before pivot k = kg + s of a group starting at kg, block row k takes the group's
     earlier steps (rows kg+s' of the group take only the steps after s', having been
-    rewritten by that step's panel). After the group, one update gives every other
+    rewritten by that step's panel; of the diagonal block, the pivot takes step k-1 and
+    the panel launches the steps before it). After the group, one update gives every other
     upper tile the group's steps it has not had: all of them outside the group's
     rows, the steps after the latest of its own rows inside them. A tile counts its
     entries on or above the diagonal, 2 flops per multiply-add. An order 128m + 1 takes

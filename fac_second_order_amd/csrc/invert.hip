@@ -20,9 +20,10 @@
 // with |Y|^2 rather than with |V| |P^-1 V| (which an explicit P^-1 would give).
 // Steps are taken in groups of GS (kg .. kg+GS-1) with one update per group: before
 // pivot k of a group, block row k takes the group's earlier steps (row update; the
-// pivot applies it to its own diagonal block, and the other tiles of the row are
-// extra blocks of that pivot's launch), then panel k writes its Y into slot k - kg of
-// the panel buffer; after the last step one update applies the whole group,
+// other tiles of the row are extra blocks of that pivot's launch; of the diagonal
+// block, which the pivot needs first, the pivot applies only step k-1: each earlier
+// step kg+t-1 reached it as an extra block of panel launch kg+t), then panel k writes
+// its Y into slot k - kg of the panel buffer; after the last step one update applies the whole group,
 // S_ij -= [Y_i; Y'_i; ..]^T [Y_j; Y'_j; ..], a rank-(GS*TB) product that reads and
 // writes each tile once per group (tiles in a row of the group take only the steps
 // after that row's own). After the last step S = -M^-1; the finish kernel negates
@@ -66,7 +67,7 @@ __host__ __device__ inline int block_steps(int n) {
 // Block steps per update launch (a group): the update of a group applies all its
 // steps at once as one rank-(G*TB) product.
 #ifndef KFAC_INV_GROUP
-#define KFAC_INV_GROUP 3
+#define KFAC_INV_GROUP 4
 #endif
 constexpr int GS = KFAC_INV_GROUP;
 static_assert(GS >= 1 && GS <= 8, "group size");
@@ -254,8 +255,9 @@ __device__ __forceinline__ void update_tile(const InvDesc& d, int ti, int tj, in
 // only, which A of J+1 needs first).
 // Blocks [0, a) are the pivots of matrices 0..a-1. For step k = kg + pre of a group
 // starting at kg, the updates of the group's earlier steps kg..k-1 have not reached
-// block row k yet: each pivot first applies them to its own diagonal block (S_kk -=
-// Y^T Y over panel rows [0, pre*TB)), and blocks [a, a + rows) apply them to the other
+// block row k yet, except that the panel launches applied steps kg..k-2 to the
+// diagonal block: each pivot first applies step k-1 to its own diagonal block (S_kk -=
+// Y^T Y over panel rows [(pre-1)*TB, pre*TB)), and blocks [a, a + rows) apply them all to the other
 // tiles (k, j) of the row, which nothing else in the launch reads or writes; they find
 // their tile through the panel offsets `begin`. A tile (k, j) with j = kg + s', s' <
 // pre, was rewritten by the panel of step j and takes only the steps after it.
@@ -302,9 +304,10 @@ __global__ void __launch_bounds__(PT) inv_pivot_kernel(const InvDesc* __restrict
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int e = 0; e < 16; ++e) o.c[b][e] = M[oct_row(lane, e) * MLD + oct_col(lane, b)];
-    const float* Y = d.Y;  // panel rows [0, pre*TB): the group's earlier steps
-    const int K = pre * TB;
-    oct_gemm(o, op_rows(Y, d.ldy, K, k0, n), op_rows(Y, d.ldy, K, k0, n), K, -1.f, PL);  // ends with a barrier
+    // panel rows [(pre-1)*TB, pre*TB): step k-1 (a full block: a matrix's narrow
+    // last step is never followed by a pivot)
+    const float* Y = d.Y + int64_t(pre - 1) * TB * d.ldy;
+    oct_gemm(o, op_rows(Y, d.ldy, TB, k0, n), op_rows(Y, d.ldy, TB, k0, n), TB, -1.f, PL);  // ends with a barrier
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
@@ -442,12 +445,26 @@ __global__ void __launch_bounds__(PT) inv_pivot_kernel(const InvDesc* __restrict
 // straight into MFMA operand registers one 32-deep chunk ahead. E is lower
 // triangular, so a Y row m only sums k <= m. Blocks b and b+8 (same XCD, so the
 // second read of V_j hits that XCD's L2) take the two halves of one tile.
+// For slot >= 1, blocks from `base` on give step k-1 (panel slot-1) to the diagonal
+// blocks of the group's later pivots k+1.. (block (p, u): matrix p, pivot kg+1+u),
+// which nothing else in the launch reads or writes; Vs is their staging LDS.
 constexpr int PP = 512;  // panel threads
 constexpr int WTP = 65;  // pitch of the transposed W half in LDS
 __global__ void __launch_bounds__(PP) __attribute__((amdgpu_waves_per_eu(4, 4)))
 inv_panel_kernel(const InvDesc* __restrict__ desc, const int32_t* __restrict__ begin, int count, int k,
-                 int slot, int total) {
+                 int slot, int total, int base) {
+  __shared__ __attribute__((aligned(16))) float Vs[TB * LDP];
+  static_assert(TB * LDP >= 4 * CHUNK, "panel LDS too small for the update engine");
   const int bid = blockIdx.x;
+  if (bid >= base) {  // step k-1 on a later pivot's diagonal block
+    const int e = bid - base, p = e / (GS - 1), u = e - p * (GS - 1);
+    if (p >= count) return;
+    const InvDesc& d = desc[p];
+    const int kp = k - slot + 1 + u;  // the later pivot kg+1+u
+    if (kp <= k || kp >= d.ns) return;
+    update_tile(d, kp, kp, (slot - 1) * TB, slot * TB, Vs);
+    return;
+  }
   const int t = (bid >> 4) * 8 + (bid & 7), h = (bid >> 3) & 1;
   if (t >= total) return;
   const int p = find_problem(begin, count, t);
@@ -480,7 +497,6 @@ inv_panel_kernel(const InvDesc* __restrict__ desc, const int32_t* __restrict__ b
   };
   float acur[16], anext[16];
   load_a(acur, 0);  // in flight together with the V loads
-  __shared__ __attribute__((aligned(16))) float Vs[TB * LDP];
   {  // all 32 loads of a thread in flight first (clamped addresses, zero outside)
     const int lo = tid & (TB - 1), hi0 = tid >> 7;  // along a row of S / first row
     float v[TB * TB / PP];
@@ -816,8 +832,11 @@ extern "C" kfac_status kfac_invert(int32_t count, const int32_t* n, const float*
       KFAC_LAUNCH(K_INV_PIVOT, inv_pivot_kernel, dim3(sg == 0 ? a : a + pg), dim3(PT), 0, s, d_desc, d_panel, a,
                   k, sg, sg == 0 ? 0 : static_cast<int>(pg));
       KFAC_CHECK_LAUNCH("inv_pivot_kernel");
-      KFAC_LAUNCH(K_INV_PANEL, inv_panel_kernel, dim3(panel_grid(pg)), dim3(PP), 0, s, d_desc, d_panel, a, k, sg,
-                  static_cast<int>(pg));
+      // after the first step of a group, with step k-1 given to the later pivots'
+      // diagonal blocks in the same launch
+      const unsigned pb = panel_grid(pg), diag = sg >= 1 && GS > 2 ? a * (GS - 1) : 0;
+      KFAC_LAUNCH(K_INV_PANEL, inv_panel_kernel, dim3(pb + diag), dim3(PP), 0, s, d_desc, d_panel, a, k, sg,
+                  static_cast<int>(pg), static_cast<int>(pb));
       KFAC_CHECK_LAUNCH("inv_panel_kernel");
     }
     const int a0 = pl.active[kg];
