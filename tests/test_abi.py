@@ -74,10 +74,12 @@ def test_workspace_queries_resnet50(lib):
 
 
 def test_invert_workspace_covers_panels(lib):
-    # per matrix: two 128x128 blocks (U_kk^-1 and P^-1 of the pivot) and a 256 x n
-    # panel buffer (the Y panels of both steps of a pair) with rows padded to 16 bytes
+    # per matrix: two blocks (U_kk^-1 and P^-1 of the pivot) and a (group x block) x n
+    # panel buffer (the Y panels of a group's steps) with rows padded to 16 bytes
+    block, group = lib.kfac_invert_schedule()
+    assert block == 128 and 1 <= group <= 8
     b = lib.kfac_invert_workspace([4609])
-    assert b >= 4 * (2 * 128 * 128 + 256 * 4612)
+    assert b >= 4 * (2 * block * block + group * block * 4612)
 
 
 def _status(fn, *args):
