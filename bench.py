@@ -37,17 +37,20 @@ LR = 0.01                # learning rate of the parameter update
 # (FETCH_SIZE, then WRITE_SIZE), calibrated by a plain 1 GiB device copy (fetch x2.0,
 # write x1.0) and summarised in profiles/resnet50_step_hbm_counters.md. Reported only
 # while the kernel's source text still hashes to the value it was measured with.
-MEASURED_TRAFFIC = {"inv_update_kernel": (870325760, "8fc1728f9a418b913c8d2250986191f791d93273")}
+MEASURED_TRAFFIC = {"inv_update_kernel": (870325760, "a2c805f9f32f399450811f94b638e708c6575732")}
 CSRC = os.path.join(ROOT, "fac_second_order_amd", "csrc")
 
 
 def kernel_source_sha(name):
+    """Hash of the update kernel's own source: its tile routine, the kernel, and the
+    tile engine headers they use."""
     import hashlib
     if name != "inv_update_kernel":
         return None
     inv = open(os.path.join(CSRC, "invert.hip")).read()
-    body = inv[inv.index("// Update of step k:"):inv.index("// inv <- -S with both")]
-    text = body + open(os.path.join(CSRC, "tile_f32.hpp")).read() + \
+    tile = inv[inv.index("// Update of step k:"):inv.index("// Pivot of step k. Sub-step J runs")]
+    kern = inv[inv.index("// Update after the group of steps"):inv.index("// Bordered last column")]
+    text = tile + kern + open(os.path.join(CSRC, "tile_f32.hpp")).read() + \
         open(os.path.join(CSRC, "common.hpp")).read()
     return hashlib.sha1(text.encode()).hexdigest()
 

@@ -456,8 +456,9 @@ inv_panel_kernel(const InvDesc* __restrict__ desc, const int32_t* __restrict__ b
   __shared__ __attribute__((aligned(16))) float Vs[TB * LDP];
   static_assert(TB * LDP >= 4 * CHUNK, "panel LDS too small for the update engine");
   const int bid = blockIdx.x;
-  if (bid >= base) {  // step k-1 on a later pivot's diagonal block
-    const int e = bid - base, p = e / (GS - 1), u = e - p * (GS - 1);
+  if (GS > 2 && bid >= base) {  // step k-1 on a later pivot's diagonal block
+    constexpr int L = GS > 2 ? GS - 1 : 1;  // later pivots per matrix at most
+    const int e = bid - base, p = e / L, u = e - p * L;
     if (p >= count) return;
     const InvDesc& d = desc[p];
     const int kp = k - slot + 1 + u;  // the later pivot kg+1+u
