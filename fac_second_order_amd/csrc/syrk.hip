@@ -54,6 +54,7 @@ struct SyrkDesc {
   float* pcol;     // [splits][nb][ST] bias column partial sums
   int32_t mode;    // 0: rows [R, ld]; 1: im2col of NHWC [n, H, W, C]
   int32_t vec;     // 16-byte gathers (buffer loads) allowed
+  int32_t padded;  // > 0: rows written out by im2row job padded-1, zeros from d_core to ld
   int32_t nbytes;  // input tensor bytes when vec (< 2^31): the buffer range
   int32_t d_core;  // columns of X (without the bias column)
   int32_t d;       // factor order (d_core + bias)
@@ -564,8 +565,52 @@ __global__ void __launch_bounds__(256) syrk_reduce_kernel(const SyrkDesc* __rest
 }
 
 // ---- host planning ------------------------------------------------------------
+// A patch matrix written out before the factor pass: for fp16 convolutions whose
+// channel count rules out 16-byte gathers from the NHWC tensor (e.g. 3 input
+// channels), element gathers cost several times the 16-byte ones per patch row, so
+// the rows are gathered once into the workspace (row pitch ld = d_core rounded up to
+// 8, zeros past d_core) and the factor pass reads them as plain rows with 16-byte
+// loads. The conv geometry is kept here; the factor problem becomes a row problem.
+struct Im2Row {
+  const _Float16* src;
+  _Float16* dst;
+  int32_t R, ld, d_core, H, W, C, Ho, Wo, kh, kw, sh, sw, ph, pw;
+  double rhw, rwo;
+};
+
+__global__ void __launch_bounds__(256) im2row_kernel(Im2Row j, int64_t total) {
+  const int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x;  // (row, group of 8 columns)
+  if (e >= total) return;
+  const int groups = j.ld / 8;
+  const int row = static_cast<int>(e / groups), c0 = static_cast<int>(e - int64_t(row) * groups) * 8;
+  const int hw = j.Ho * j.Wo;
+  const int n = fast_div(row, hw, j.rhw);
+  const int rem = row - n * hw;
+  const int oh = fast_div(rem, j.Wo, j.rwo);
+  const int ow = rem - oh * j.Wo;
+  const int ih0 = oh * j.sh - j.ph, iw0 = ow * j.sw - j.pw;
+  const KG _Float16* src = gp(j.src) + int64_t(n) * j.H * j.W * j.C;
+  v8h v;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int c = c0 + q;
+    _Float16 x = static_cast<_Float16>(0.f);
+    if (c < j.d_core) {
+      const int tap = c / j.C, ci = c - tap * j.C;
+      const int ki = tap / j.kw, kj = tap - ki * j.kw;
+      const int ih = ih0 + ki, iw = iw0 + kj;
+      if (unsigned(ih) < unsigned(j.H) && unsigned(iw) < unsigned(j.W)) x = src[(int64_t(ih) * j.W + iw) * j.C + ci];
+    }
+    v[q] = x;
+  }
+  *reinterpret_cast<KG v8h*>(gp(j.dst) + int64_t(row) * j.ld + c0) = v;
+}
+
 struct SyrkPlan {
   std::vector<SyrkDesc> desc;
+  std::vector<Im2Row> im2row;        // patch matrices written out first (dst set at launch)
+  std::vector<int32_t> im2row_prob;  // the problem in desc that reads each
+  size_t im2row_bytes = 0;
   std::vector<int32_t> begin;        // work-item offsets
   std::vector<int32_t> rbegin, rprob;  // reduce tiles of split problems
   int64_t items = 0, ritems = 0;
@@ -612,7 +657,7 @@ static SyrkDesc make_problem(const kfac_layer& L, int which) {
 // on gfx950 (about 4x per row).
 static double row_cost(const SyrkDesc& d, kfac_dtype dt) {
   const int width = d.mode == 1 ? d.C : d.ld;
-  return (dt == KFAC_F16 && width % 8 == 0 && d.d_core % 8 == 0) ? 1.0 : 4.0;
+  return (dt == KFAC_F16 && width % 8 == 0 && (d.d_core % 8 == 0 || d.padded)) ? 1.0 : 4.0;
 }
 
 // Row splits: spread the work so that the launch holds several thousand work items
@@ -656,7 +701,8 @@ static void finish_plan(SyrkPlan& pl) {
 static size_t syrk_ws_bytes(const SyrkPlan& pl) {
   const size_t np = pl.desc.size(), nr = pl.rprob.size();
   return align256(sizeof(SyrkDesc) * np) + align256(sizeof(int32_t) * np) +
-         2 * align256(sizeof(int32_t) * (nr ? nr : 1)) + align256(sizeof(float) * pl.partial_floats);
+         2 * align256(sizeof(int32_t) * (nr ? nr : 1)) + align256(sizeof(float) * pl.partial_floats) +
+         pl.im2row_bytes;
 }
 
 }  // namespace kfac
@@ -692,8 +738,22 @@ static kfac_status build_plan(const kfac_layer* L, int32_t count, kfac_dtype dt,
                               const void* const* gout, float* const* A, float* const* G, SyrkPlan& pl) {
   const int esize = dt == KFAC_F16 ? 2 : 4;
   std::vector<SyrkDesc> all;
+  std::vector<Im2Row> geo;  // conv geometry of the problems converted to rows (by index in all)
   for (int l = 0; l < count; ++l)
-    for (int which = 0; which < 2; ++which) all.push_back(make_problem(L[l], which));
+    for (int which = 0; which < 2; ++which) {
+      SyrkDesc d = make_problem(L[l], which);
+      Im2Row g{};
+      if (dt == KFAC_F16 && d.mode == 1 && d.C % 8 != 0) {
+        g = Im2Row{nullptr, nullptr, d.R, (d.d_core + 7) / 8 * 8, d.d_core, d.H, d.W, d.C, d.Ho, d.Wo,
+                   d.kh, d.kw, d.sh, d.sw, d.ph, d.pw, d.rhw, d.rwo};
+        d.mode = 0;
+        d.ld = g.ld;
+        d.H = d.W = 1;
+        d.padded = 1;
+      }
+      all.push_back(d);
+      geo.push_back(g);
+    }
   plan_splits(all, dt);
   for (int l = 0; l < count; ++l) {
     for (int which = 0; which < 2; ++which) {
@@ -710,9 +770,26 @@ static kfac_status build_plan(const kfac_layer* L, int32_t count, kfac_dtype dt,
         const int width = d.mode == 1 ? d.C : d.ld;
         const int64_t bytes = d.mode == 1 ? int64_t(L[l].n) * d.H * d.W * d.C * esize
                                           : int64_t(d.R) * d.ld * esize;
-        d.vec = (dt == KFAC_F16 && width % 8 == 0 && d.d_core % 8 == 0 &&
-                 reinterpret_cast<uintptr_t>(src) % 16 == 0 && bytes < (int64_t(1) << 31)) ? 1 : 0;
+        d.vec = (dt == KFAC_F16 && width % 8 == 0 && bytes < (int64_t(1) << 31) &&
+                 (d.padded || (d.d_core % 8 == 0 && reinterpret_cast<uintptr_t>(src) % 16 == 0))) ? 1 : 0;
         d.nbytes = d.vec ? static_cast<int32_t>(bytes) : 0;
+      }
+      if (d.padded) {
+        const int64_t pb = int64_t(d.R) * d.ld * 2;
+        if (pb < (int64_t(1) << 31)) {  // rows in the workspace, read with 16-byte loads
+          Im2Row g = geo[2 * l + which];
+          g.src = static_cast<const _Float16*>(d.src);
+          pl.im2row.push_back(g);
+          d.padded = static_cast<int32_t>(pl.im2row.size());
+          pl.im2row_bytes += align256(static_cast<size_t>(pb));
+        } else {  // too large for one buffer range: element gathers from the NHWC tensor
+          SyrkDesc c = make_problem(L[l], which);
+          c.splits = d.splits;
+          c.rows_per_split = d.rows_per_split;
+          c.src = d.src;
+          c.out = d.out;
+          d = c;
+        }
       }
       pl.desc.push_back(d);
     }
@@ -725,6 +802,9 @@ static kfac_status build_plan(const kfac_layer* L, int32_t count, kfac_dtype dt,
   };
   std::stable_sort(pl.desc.begin(), pl.desc.end(),
                    [&](const SyrkDesc& a, const SyrkDesc& b) { return item_cost(a) > item_cost(b); });
+  pl.im2row_prob.assign(pl.im2row.size(), 0);
+  for (size_t p = 0; p < pl.desc.size(); ++p)
+    if (pl.desc[p].padded) pl.im2row_prob[pl.desc[p].padded - 1] = static_cast<int32_t>(p);
   finish_plan(pl);
   if (pl.items >= (int64_t(1) << 31) - 8 || pl.ritems >= (int64_t(1) << 31))
     return fail(KFAC_ERR_INVALID, "too many tiles");
@@ -806,6 +886,11 @@ extern "C" kfac_status kfac_factors(const kfac_layer* layers, int32_t count, kfa
   int32_t* d_rbegin = cv.take<int32_t>(nr ? nr : 1);
   int32_t* d_rprob = cv.take<int32_t>(nr ? nr : 1);
   float* part = cv.take<float>(pl.partial_floats);
+  for (size_t q = 0; q < pl.im2row.size(); ++q) {
+    Im2Row& g = pl.im2row[q];
+    g.dst = cv.take<_Float16>(size_t(g.R) * g.ld);
+    pl.desc[pl.im2row_prob[q]].src = g.dst;
+  }
   size_t off = 0;
   for (auto& d : pl.desc) {
     if (d.splits > 1) {
@@ -824,6 +909,11 @@ extern "C" kfac_status kfac_factors(const kfac_layer* layers, int32_t count, kfa
     tu.add(d_rprob, pl.rprob.data(), sizeof(int32_t) * nr);
   }
   if ((st = tu.flush(s))) return st;
+  for (const Im2Row& g : pl.im2row) {
+    const int64_t total = int64_t(g.R) * (g.ld / 8);
+    KFAC_LAUNCH(K_SYRK, im2row_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, s, g, total);
+    KFAC_CHECK_LAUNCH("im2row_kernel");
+  }
   const unsigned grid = static_cast<unsigned>(8 * pl.seg_max);
   if (in_dtype == KFAC_F16) {
     KFAC_LAUNCH(K_SYRK, syrk_f16_kernel, dim3(grid), dim3(256), 0, s, d_desc, d_begin, np, pl.segs, ema_decay);
