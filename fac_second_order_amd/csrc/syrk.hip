@@ -590,18 +590,24 @@ __global__ void __launch_bounds__(256) im2row_kernel(Im2Row j, int64_t total) {
   const int ow = rem - oh * j.Wo;
   const int ih0 = oh * j.sh - j.ph, iw0 = ow * j.sw - j.pw;
   const KG _Float16* src = gp(j.src) + int64_t(n) * j.H * j.W * j.C;
+  // column c0 decoded once, then stepped: c = (ki * kw + kj) * C + ci
+  const int tap = c0 / j.C;
+  int ci = c0 - tap * j.C, ki = tap / j.kw, kj = tap - ki * j.kw;
   v8h v;
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
-    const int c = c0 + q;
     _Float16 x = static_cast<_Float16>(0.f);
-    if (c < j.d_core) {
-      const int tap = c / j.C, ci = c - tap * j.C;
-      const int ki = tap / j.kw, kj = tap - ki * j.kw;
-      const int ih = ih0 + ki, iw = iw0 + kj;
-      if (unsigned(ih) < unsigned(j.H) && unsigned(iw) < unsigned(j.W)) x = src[(int64_t(ih) * j.W + iw) * j.C + ci];
-    }
+    const int ih = ih0 + ki, iw = iw0 + kj;
+    if (c0 + q < j.d_core && unsigned(ih) < unsigned(j.H) && unsigned(iw) < unsigned(j.W))
+      x = src[(int64_t(ih) * j.W + iw) * j.C + ci];
     v[q] = x;
+    if (++ci == j.C) {
+      ci = 0;
+      if (++kj == j.kw) {
+        kj = 0;
+        ++ki;
+      }
+    }
   }
   *reinterpret_cast<KG v8h*>(gp(j.dst) + int64_t(row) * j.ld + c0) = v;
 }
@@ -660,14 +666,16 @@ static double row_cost(const SyrkDesc& d, kfac_dtype dt) {
   return (dt == KFAC_F16 && width % 8 == 0 && (d.d_core % 8 == 0 || d.padded)) ? 1.0 : 4.0;
 }
 
-// Row splits: spread the work so that the launch holds several thousand work items
-// (a tile over a range of rows) of about equal cost, and at least 1024 rows each;
-// the split count of a factor never exceeds 256. Equal item costs keep the
-// per-XCD ranges of items (contiguous, equal in count) equal in time.
+// Row splits: spread the work so that the launch holds about 2048 work items (a
+// tile over a range of rows; four per block slot of the chip) of about equal cost,
+// and at least 1024 rows each; the split count of a factor never exceeds 256. Equal
+// item costs keep the per-XCD ranges of items (contiguous, equal in count) equal in
+// time. (Measured on ResNet-50 at batch 32: 2048 items 1.80-1.82 ms plus 0.026 ms of
+// split reduction, 4096 items 1.83-1.87 + 0.036, 8192 items 1.81-1.82 + 0.116.)
 static void plan_splits(std::vector<SyrkDesc>& ds, kfac_dtype dt) {
   double work = 0;
   for (auto& d : ds) work += double(d.nt) * d.R * row_cost(d, dt);
-  const double per_cost = work / 4096.0;
+  const double per_cost = work / 2048.0;
   for (auto& d : ds) {
     double per = per_cost / row_cost(d, dt);
     if (per < 1024) per = 1024;
