@@ -172,3 +172,19 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     mod = importlib.util.module_from_spec(spec)
     with pytest.raises(ImportError, match="not built"):
         spec.loader.exec_module(mod)
+
+
+def test_patch_rows_workspace(lib):
+    """An fp16 convolution whose channel count rules out 16-byte gathers (conv1, 3
+    channels) has its patch rows written to the workspace (row pitch rounded up to 8
+    halves); a matrix of 2 GiB or more stays on the per-element gathers instead."""
+    def conv1(n):
+        return [synth.Layer("conv1", n, 224, 224, 3, 112, 112, 64, 7, 7, 2, 2, 3, 3, 1)]
+    rows32 = 32 * 112 * 112
+    small = lib.kfac_factors_workspace(conv1(32), lib.KFAC_F16)
+    fp32 = lib.kfac_factors_workspace(conv1(32), lib.KFAC_F32)
+    assert small >= rows32 * 152 * 2                 # 147 patch columns padded to 152
+    assert fp32 < rows32 * 152 * 2                   # fp32 inputs take their own path
+    big = lib.kfac_factors_workspace(conv1(600), lib.KFAC_F16)
+    assert 600 * 112 * 112 * 152 * 2 >= 1 << 31
+    assert big < 600 * 112 * 112 * 152 * 2           # no row buffer at this size
