@@ -48,8 +48,10 @@ kfac_status check_workspace(const void* ws, size_t ws_bytes, size_t need) {
 }
 
 // ---- descriptor upload ------------------------------------------------------
+// Descriptor tables travel as kernel arguments, up to 1000 words (just under 4 KB of
+// arguments) per launch.
 struct UploadChunk {
-  uint32_t w[512];
+  uint32_t w[1000];
 };
 
 __global__ void __launch_bounds__(256) upload_kernel(uint32_t* dst, UploadChunk c, int n) {
@@ -61,9 +63,9 @@ kfac_status upload(void* dst_device, const void* src_host, size_t bytes, hipStre
   const uint32_t* src = static_cast<const uint32_t*>(src_host);
   uint32_t* dst = static_cast<uint32_t*>(dst_device);
   size_t words = bytes / 4;
-  for (size_t off = 0; off < words; off += 512) {
+  for (size_t off = 0; off < words; off += 1000) {
     UploadChunk c;
-    int n = static_cast<int>(words - off < 512 ? words - off : 512);
+    int n = static_cast<int>(words - off < 1000 ? words - off : 1000);
     std::memcpy(c.w, src + off, n * 4);
     KFAC_LAUNCH(K_UPLOAD, upload_kernel, dim3(1), dim3(256), 0, stream, dst + off, c, n);
     KFAC_CHECK_LAUNCH("upload_kernel");
