@@ -604,22 +604,58 @@ inv_panel_kernel(const InvDesc* __restrict__ desc, const int32_t* __restrict__ b
 // block row kg+s (the larger s if both of its indices are in the group) was rewritten
 // by that step's panel and takes only the later steps; the last step's row is left
 // as its panel wrote it.
+// The last column of a matrix with a bordered last column (ns < nb) is 1 wide: it is
+// not updated as tiles but by blocks from `tgrid` on, four per row block (p, j) of the
+// panel enumeration (offsets pbegin, ptotal row blocks in all), each 32 rows, as a
+// matrix-vector product over the same steps a tile (j, nb-1) would take: K split into
+// 16 slices over the block's threads, the slices summed through LDS.
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) inv_update_kernel(const InvDesc* __restrict__ desc,
                                                          const int32_t* __restrict__ begin,
-                                                         int count, int kg, int total) {
-  const int v = xcd_virtual(blockIdx.x, gridDim.x, total);
+                                                         int count, int kg, int total, int tgrid,
+                                                         const int32_t* __restrict__ pbegin, int ptotal) {
+  __shared__ __attribute__((aligned(16))) float lds[4 * CHUNK];
+  if (static_cast<int>(blockIdx.x) >= tgrid) {
+    const int u = (blockIdx.x - tgrid) >> 2, part = (blockIdx.x - tgrid) & 3;
+    if (u >= ptotal) return;
+    const int p = find_problem(pbegin, count, u);
+    const InvDesc& d = desc[p];
+    if (d.ns == d.nb) return;
+    const int j = u - pbegin[p];
+    const int g = min(GS, d.ns - kg), last = kg + g - 1;
+    const int m = (j >= kg && j <= last) ? j - kg : -1;
+    if (m == g - 1) return;
+    const int kb = (m + 1) * TB, ke = (g - 1) * TB + min(TB, d.n - last * TB);
+    const int r = threadIdx.x & 31, q = threadIdx.x >> 5;  // row in the part, K slice
+    const int64_t n = d.n, i = int64_t(j) * TB + part * 32 + r, c = n - 1;
+    const KG float* Y = gp(static_cast<const float*>(d.Y));
+    float acc = 0.f;
+    if (i < n) {
+#pragma unroll 8
+      for (int t = kb + q; t < ke; t += 16) acc = fmaf(Y[int64_t(t) * d.ldy + i], Y[int64_t(t) * d.ldy + c], acc);
+    }
+    lds[q * 32 + r] = acc;
+    __syncthreads();
+    if (q == 0 && i < n) {
+      float sum = 0.f;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) sum += lds[k * 32 + r];
+      gp(d.S)[i * n + c] -= sum;
+    }
+    return;
+  }
+  const int v = xcd_virtual(blockIdx.x, tgrid, total);
   if (v < 0) return;
   const int p = find_problem(begin, count, v);
   const InvDesc& d = desc[p];
   int ti, tj;
   upper_tile(v - begin[p], d.nb, ti, tj);
+  if (d.ns < d.nb && tj == d.nb - 1) return;  // the bordered column: blocks above
   const int g = min(GS, d.ns - kg), last = kg + g - 1;
   int m = -1;  // latest group step whose panel wrote this tile
   if (ti >= kg && ti <= last) m = ti - kg;
   if (tj >= kg && tj <= last) m = max(m, tj - kg);
   if (m == g - 1) return;
   const int kb = (m + 1) * TB, ke = (g - 1) * TB + min(TB, d.n - last * TB);
-  __shared__ __attribute__((aligned(16))) float lds[4 * CHUNK];
   update_tile(d, ti, tj, kb, ke, lds);
 }
 
@@ -841,9 +877,12 @@ extern "C" kfac_status kfac_invert(int32_t count, const int32_t* n, const float*
       KFAC_CHECK_LAUNCH("inv_panel_kernel");
     }
     const int a0 = pl.active[kg];
-    const unsigned ut = grid_of(pl.tile_begin, a0, tiles_of);
-    KFAC_LAUNCH(K_INV_UPDATE, inv_update_kernel, dim3(xcd_grid(ut)), dim3(512), 0, s, d_desc, d_tile, a0, kg,
-                static_cast<int>(ut));
+    const unsigned ut = grid_of(pl.tile_begin, a0, tiles_of), tg = xcd_grid(ut);
+    bool any_border = false;  // matrices [0, a0) with a bordered last column
+    for (int q = 0; q < a0; ++q) any_border = any_border || desc[q].ns != desc[q].nb;
+    const unsigned pt = any_border ? grid_of(pl.panel_begin, a0, panels_of) : 0;
+    KFAC_LAUNCH(K_INV_UPDATE, inv_update_kernel, dim3(tg + 4 * pt), dim3(512), 0, s, d_desc, d_tile, a0, kg,
+                static_cast<int>(ut), static_cast<int>(tg), d_panel, static_cast<int>(pt));
     KFAC_CHECK_LAUNCH("inv_update_kernel");
   }
   bool bordered = false;
