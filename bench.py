@@ -37,7 +37,7 @@ LR = 0.01                # learning rate of the parameter update
 # (FETCH_SIZE, then WRITE_SIZE), calibrated by a plain 1 GiB device copy (fetch x2.0,
 # write x1.0) and summarised in profiles/resnet50_step_hbm_counters.md. Reported only
 # while the kernel's source text still hashes to the value it was measured with.
-MEASURED_TRAFFIC = {"inv_update_kernel": (869679514, "a2c805f9f32f399450811f94b638e708c6575732")}
+MEASURED_TRAFFIC = {"inv_update_kernel": (970451456, "3d5e4963843e59a4a5a228c1bd1c9c537f3130f2")}
 CSRC = os.path.join(ROOT, "fac_second_order_amd", "csrc")
 
 
