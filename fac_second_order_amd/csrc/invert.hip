@@ -23,8 +23,8 @@
 // other tiles of the row are extra blocks of that pivot's launch; of the diagonal
 // block, which the pivot needs first, the pivot applies only step k-1: each earlier
 // step kg+t-1 reached it as an extra block of panel launch kg+t), then panel k writes
-// its Y into slot k - kg of the panel buffer; after the last step one update applies the whole group,
-// S_ij -= [Y_i; Y'_i; ..]^T [Y_j; Y'_j; ..], a rank-(GS*TB) product that reads and
+// its Y into slot k - kg of the panel buffer; after the last step one update applies
+// the whole group, S_ij -= [Y_i; Y'_i; ..]^T [Y_j; Y'_j; ..], a rank-(GS*TB) product that reads and
 // writes each tile once per group (tiles in a row of the group take only the steps
 // after that row's own). After the last step S = -M^-1; the finish kernel negates
 // it and writes both triangles. All matrices of a call step together: they are
@@ -32,7 +32,8 @@
 // An order n = 128m + 1 (a factor with its bias column) would end with a 1-wide block:
 // a whole pivot, panel and rank-1 pass over the matrix for one column. Its last
 // column is instead taken as a bordered step: the sweep runs m block steps (which
-// still update the last column), inv_border_kernel saves the last column v and
+// still update the last column, in the group updates as a matrix-vector product
+// rather than as 1-wide tiles), inv_border_kernel saves the last column v and
 // pivot p, and the finish applies the step as it writes the inverse (with
 // y = p^-1/2 v: S_ij - y_i y_j inside, p^-1 v on the border, -p^-1 at the corner).
 #include <algorithm>
