@@ -75,6 +75,8 @@ def parse():
                          "synthetic 224x224 images, factors from its own activations (batch 32)")
     ap.add_argument("--precond-accum", choices=["f32", "f64"], default="f32",
                     help="accumulation of the preconditioning products (f64: kfac_precondition_ex)")
+    ap.add_argument("--refine-inverse", action="store_true",
+                    help="one fp64-residual refinement step of every inverse (kfac_invert_refine)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true",
                     help="time the steps without per-kernel events (roofline then null)")
@@ -391,7 +393,7 @@ def main():
     w = work(layers, bns, kfac.kfac_invert_schedule()[1])
     act, gout, grads, xhat, bgout = make_inputs(layers, bns, dev)
     weights, bn_params = make_params(layers, bns, dev)
-    st = kfac.KfacStep(layers, bns, dev, precond_accum=args.precond_accum)
+    st = kfac.KfacStep(layers, bns, dev, precond_accum=args.precond_accum, refine_inverse=args.refine_inverse)
 
     def step():
         st.step(act, gout, grads, xhat, bgout, weights=weights, bn_params=bn_params, lr=LR)
@@ -482,7 +484,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": "resnet50_kfac_step", "batch_per_gpu": args.batch,
                    "kfac_layers": len(layers), "factors": 2 * len(layers), "bn_layers": len(bns),
-                   "damping": 1e-3, "lr": LR, "precond_accum": args.precond_accum, "inputs": "fp16 ReLU(N(0,1)) activations, fp16 N(0,1) "
+                   "damping": 1e-3, "lr": LR, "precond_accum": args.precond_accum, "refine_inverse": args.refine_inverse, "inputs": "fp16 ReLU(N(0,1)) activations, fp16 N(0,1) "
                    "output and BN gradients, fp32 N(0,1e-2) weight gradients, fp32 N(0,2.5e-3) weights"},
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -68,6 +68,8 @@ _sig("kfac_pack_sym", _i32, _i32, _P(_i32), _P(_vp), _P(_vp), _i32, _vp, _sz, _v
 _sig("kfac_invert_workspace", _i32, _i32, _P(_i32), _P(_sz))
 _sig("kfac_invert_schedule", _i32, _P(_i32), _P(_i32))
 _sig("kfac_invert", _i32, _i32, _P(_i32), _P(_vp), _P(_vp), _P(_f32), _vp, _P(_vp), _vp, _sz, _vp)
+_sig("kfac_invert_refine_workspace", _i32, _i32, _P(_i32), _P(_sz))
+_sig("kfac_invert_refine", _i32, _i32, _P(_i32), _P(_vp), _P(_f32), _P(_vp), _vp, _sz, _vp)
 _sig("kfac_precondition_workspace", _i32, _i32, _P(_i32), _P(_i32), _P(_sz))
 _sig("kfac_precondition", _i32, _i32, _P(_i32), _P(_i32), _P(_vp), _P(_vp), _P(_vp), _i32, _P(_vp),
      _vp, _sz, _vp)
@@ -202,6 +204,21 @@ def kfac_invert_schedule():
     b, g = _i32(), _i32()
     _check(_lib.kfac_invert_schedule(_c.byref(b), _c.byref(g)), "kfac_invert_schedule")
     return b.value, g.value
+
+
+def kfac_invert_refine_workspace(n):
+    out = _sz()
+    _check(_lib.kfac_invert_refine_workspace(len(n), _ints(n), _c.byref(out)), "kfac_invert_refine_workspace")
+    return out.value
+
+
+def kfac_invert_refine(n, mat, shift, inv, workspace=None, stream=None):
+    """inv[m] <- X + X (I - (mat[m] + shift[m] I) X), X = inv[m] (see kfac.h)."""
+    need = kfac_invert_refine_workspace(n)
+    ws, wsb = _ws(workspace, need, inv[0].device)
+    shifts = (_f32 * len(n))(*[float(v) for v in shift])
+    _check(_lib.kfac_invert_refine(len(n), _ints(n), _ptrs(mat), shifts, _ptrs(inv), ws, wsb, _stream(stream)),
+           "kfac_invert_refine")
 
 
 def kfac_invert(n, mat, inv, shift, info, chol=None, workspace=None, stream=None):

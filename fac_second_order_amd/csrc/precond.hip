@@ -262,3 +262,162 @@ extern "C" kfac_status kfac_precondition_ex(int32_t count, const int32_t* d_g, c
   return precond_impl(count, d_g, d_a, G_inv, A_inv, grad, grad_dtype, out, w, lr, accum, workspace, ws_bytes,
                       stream);
 }
+
+// ---- refinement of a computed inverse -------------------------------------------
+// One step of X <- X + X E with E = I - (F + sI) X, for inverses X of damped factors
+// (the fp64-residual refinement of an approximate inverse; Osawa et al. (CVPR 2019),
+// Section 3.2, eq. (6), for the inverse itself). E is formed as (I - sX) - F X: the
+// product F X summed in fp64 on the fp64 engine and subtracted from the fp32 I - sX in
+// its epilogue, so E carries only the roundings of I - sX and of E itself (adding s
+// to F first would round F's diagonal and perturb M by far more than the residual).
+// The correction X E (fp32 sums) is added symmetrised, (C + C^T) / 2.
+namespace kfac {
+
+// E <- I - s X over matrix p's elements, blocks of 1024 elements (offsets ebegin).
+__global__ void __launch_bounds__(256) refine_init_kernel(const float* const* __restrict__ X, float* const* __restrict__ E,
+                                                          const int32_t* __restrict__ n, const float* __restrict__ s,
+                                                          const int32_t* __restrict__ ebegin, int count) {
+  const int p = find_problem(ebegin, count, blockIdx.x);
+  const int64_t nn = n[p], total = nn * nn;
+  const int64_t e0 = int64_t(blockIdx.x - ebegin[p]) * 1024;
+  for (int64_t e = e0 + threadIdx.x; e < min(total, e0 + 1024); e += 256) {
+    const int64_t i = e / nn, j = e - i * nn;
+    gp(E[p])[e] = (i == j ? 1.f : 0.f) - s[p] * gp(X[p])[e];
+  }
+}
+
+// X <- X + (C + C^T) / 2, 64x64 tiles (offsets tbegin), the transposed tile through LDS.
+__global__ void __launch_bounds__(256) refine_apply_kernel(float* const* __restrict__ X, const float* const* __restrict__ C,
+                                                           const int32_t* __restrict__ n, const int32_t* __restrict__ tbegin,
+                                                           int count) {
+  __shared__ float t[64][65];
+  const int p = find_problem(tbegin, count, blockIdx.x);
+  const int64_t nn = n[p];
+  const int nb = static_cast<int>((nn + 63) / 64);
+  const int q = blockIdx.x - tbegin[p], ti = q / nb, tj = q - ti * nb;
+  const int c = threadIdx.x & 63;
+  const int64_t i0 = int64_t(ti) * 64, j0 = int64_t(tj) * 64;
+  for (int r = threadIdx.x >> 6; r < 64; r += 4) {  // t[c][r] = C[j0 + r][i0 + c]
+    const int64_t a = j0 + r, b = i0 + c;
+    t[c][r] = (a < nn && b < nn) ? gp(C[p])[a * nn + b] : 0.f;
+  }
+  __syncthreads();
+  for (int r = threadIdx.x >> 6; r < 64; r += 4) {
+    const int64_t i = i0 + r, j = j0 + c;
+    if (i < nn && j < nn) {
+      const int64_t o = i * nn + j;
+      gp(X[p])[o] += 0.5f * (gp(C[p])[o] + t[r][c]);
+    }
+  }
+}
+
+// Workspace in carve order: two descriptor tables, four offset tables, three pointer
+// tables, orders and shifts, then E and C (n x n each) per matrix.
+static size_t refine_ws(int count, const int32_t* n) {
+  size_t f = 0;
+  for (int m = 0; m < count; ++m) f += 2 * size_t(n[m]) * n[m];
+  return 2 * align256(sizeof(GemmDesc) * count) + 4 * align256(sizeof(int32_t) * count) +
+         3 * align256(sizeof(void*) * count) + align256(sizeof(int32_t) * count) + align256(sizeof(float) * count) +
+         align256(sizeof(float) * f);
+}
+
+}  // namespace kfac
+
+extern "C" kfac_status kfac_invert_refine_workspace(int32_t count, const int32_t* n, size_t* bytes) {
+  if (!bytes) return fail(KFAC_ERR_INVALID, "bytes is NULL");
+  kfac_status st = precond_validate(count, n, n);
+  if (st) return st;
+  *bytes = count ? refine_ws(count, n) : 0;
+  return KFAC_OK;
+}
+
+extern "C" kfac_status kfac_invert_refine(int32_t count, const int32_t* n, const float* const* mat,
+                                          const float* shift, float* const* inv, void* workspace,
+                                          size_t ws_bytes, void* stream) {
+  kfac_status st = precond_validate(count, n, n);
+  if (st) return st;
+  if (count == 0) return KFAC_OK;
+  if (!mat || !shift || !inv) return fail(KFAC_ERR_INVALID, "NULL pointer argument");
+  for (int m = 0; m < count; ++m) {
+    if (!mat[m] || !inv[m]) return fail(KFAC_ERR_INVALID, "matrix %d: NULL pointer", m);
+    if ((reinterpret_cast<uintptr_t>(mat[m]) | reinterpret_cast<uintptr_t>(inv[m])) & 3)
+      return fail(KFAC_ERR_INVALID, "matrix %d: misaligned pointer", m);
+    if (mat[m] == inv[m]) return fail(KFAC_ERR_INVALID, "matrix %d: mat and inv are the same buffer", m);
+    if (!(shift[m] - shift[m] == 0.f)) return fail(KFAC_ERR_INVALID, "matrix %d: shift is not finite", m);
+  }
+  st = check_device();
+  if (st) return st;
+  st = check_workspace(workspace, ws_bytes, refine_ws(count, n));
+  if (st) return st;
+  Carver cv(workspace);
+  GemmDesc* d1 = cv.take<GemmDesc>(count);
+  GemmDesc* d2 = cv.take<GemmDesc>(count);
+  int32_t* b1 = cv.take<int32_t>(count);
+  int32_t* b2 = cv.take<int32_t>(count);
+  int32_t* eb = cv.take<int32_t>(count);
+  int32_t* tb = cv.take<int32_t>(count);
+  float** dX = cv.take<float*>(count);
+  float** dE = cv.take<float*>(count);
+  float** dC = cv.take<float*>(count);
+  int32_t* dn = cv.take<int32_t>(count);
+  float* ds = cv.take<float>(count);
+  size_t f = 0;
+  for (int m = 0; m < count; ++m) f += 2 * size_t(n[m]) * n[m];
+  float* buf = cv.take<float>(f);
+  std::vector<int> order(count);
+  for (int m = 0; m < count; ++m) order[m] = m;
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return n[a] > n[b]; });
+  std::vector<GemmDesc> g1(count), g2(count);
+  std::vector<int32_t> e1(count), e2(count), ebv(count), tbv(count), nv(count);
+  std::vector<float*> xv(count), ev(count), cvv(count);
+  std::vector<float> sv(count);
+  int64_t n1 = 0, n2 = 0, ne = 0, nt = 0;
+  size_t off = 0;
+  for (int q = 0; q < count; ++q) {
+    const int m = order[q], N = n[m];
+    float* E = buf + off; off += size_t(N) * N;
+    float* C = buf + off; off += size_t(N) * N;
+    GemmDesc x{};  // E -= F X (fp64 sums): A operand F (symmetric: rows are columns)
+    x.A = mat[m]; x.B = inv[m]; x.W = E; x.lr = 1.f;
+    x.M = N; x.N = N; x.K = N; x.lda = N; x.ldb = N; x.ldc = N;
+    x.tm = x.tn = (N + TB - 1) / TB;
+    set_modes(x, 4);
+    GemmDesc y{};  // C = X E: A operand X (symmetric)
+    y.A = inv[m]; y.B = E; y.C = C;
+    y.M = N; y.N = N; y.K = N; y.lda = N; y.ldb = N; y.ldc = N;
+    y.tm = y.tn = x.tm;
+    set_modes(y, 4);
+    g1[q] = x; g2[q] = y;
+    e1[q] = static_cast<int32_t>(n1); n1 += int64_t(x.tm) * x.tn;
+    e2[q] = static_cast<int32_t>(n2); n2 += int64_t(y.tm) * y.tn;
+    ebv[q] = static_cast<int32_t>(ne); ne += (int64_t(N) * N + 1023) / 1024;
+    tbv[q] = static_cast<int32_t>(nt); nt += int64_t((N + 63) / 64) * ((N + 63) / 64);
+    xv[q] = inv[m]; ev[q] = E; cvv[q] = C;
+    nv[q] = N; sv[q] = shift[m];
+  }
+  if (n1 >= (int64_t(1) << 31) || ne >= (int64_t(1) << 31) || nt >= (int64_t(1) << 31))
+    return fail(KFAC_ERR_INVALID, "too many tiles");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  TableUpload tu;
+  tu.add(d1, g1.data(), sizeof(GemmDesc) * count);
+  tu.add(d2, g2.data(), sizeof(GemmDesc) * count);
+  tu.add(b1, e1.data(), sizeof(int32_t) * count);
+  tu.add(b2, e2.data(), sizeof(int32_t) * count);
+  tu.add(eb, ebv.data(), sizeof(int32_t) * count);
+  tu.add(tb, tbv.data(), sizeof(int32_t) * count);
+  tu.add(dX, xv.data(), sizeof(float*) * count);
+  tu.add(dE, ev.data(), sizeof(float*) * count);
+  tu.add(dC, cvv.data(), sizeof(float*) * count);
+  tu.add(dn, nv.data(), sizeof(int32_t) * count);
+  tu.add(ds, sv.data(), sizeof(float) * count);
+  if ((st = tu.flush(s))) return st;
+  KFAC_LAUNCH(K_GEMM, refine_init_kernel, dim3(static_cast<unsigned>(ne)), dim3(256), 0, s, dX, dE, dn, ds, eb, count);
+  KFAC_CHECK_LAUNCH("refine_init_kernel");
+  KFAC_LAUNCH(K_GEMM, gemm_tn64_kernel, dim3(static_cast<unsigned>(n1)), dim3(512), 0, s, d1, b1, count);
+  KFAC_CHECK_LAUNCH("gemm_tn64_kernel (E -= F X)");
+  KFAC_LAUNCH(K_GEMM, gemm_tn_kernel, dim3(static_cast<unsigned>(n2)), dim3(512), 0, s, d2, b2, count);
+  KFAC_CHECK_LAUNCH("gemm_tn_kernel (X E)");
+  KFAC_LAUNCH(K_GEMM, refine_apply_kernel, dim3(static_cast<unsigned>(nt)), dim3(256), 0, s, dX, dC, dn, tb, count);
+  KFAC_CHECK_LAUNCH("refine_apply_kernel");
+  return KFAC_OK;
+}

@@ -19,10 +19,12 @@ class KfacStep:
     """Buffers for `layers` (objects with the kfac_layer fields) and `bn_layers`
     (objects with n, hw, c). Tikhonov damping gamma puts sqrt(gamma) on each
     Kronecker factor (float32-rounded) and gamma on the BN diagonal. precond_accum
-    "f64" sums the preconditioning products in fp64 (kfac_precondition_ex)."""
+    "f64" sums the preconditioning products in fp64 (kfac_precondition_ex).
+    refine_inverse applies one fp64-residual refinement step to every inverse
+    (kfac_invert_refine), which keeps a full symmetric copy of each factor."""
 
     def __init__(self, layers, bn_layers=(), device="cuda", damping=1e-3, bn_shift=None,
-                 in_dtype=torch.float16, precond_accum="f32"):
+                 in_dtype=torch.float16, precond_accum="f32", refine_inverse=False):
         self.layers = list(layers)
         self.bn_layers = list(bn_layers)
         self.device = torch.device(device)
@@ -43,6 +45,8 @@ class KfacStep:
         self.packed_all = self.A_packed + self.G_packed
         self.info = torch.zeros(len(self.n_all), dtype=torch.int32, device=dev)
         self.out = [torch.empty(g, a, dtype=f32, device=dev) for g, a in zip(self.d_g, self.d_a)]
+        self.refine = bool(refine_inverse)
+        self.factor_full = [torch.empty(d, d, dtype=f32, device=dev) for d in self.n_all] if self.refine else []
         self.fisher = [torch.zeros(2, b.c, dtype=f32, device=dev) for b in self.bn_layers]
         self.bn_pre = [torch.empty(2, b.c, dtype=f32, device=dev) for b in self.bn_layers]
         code = K.KFAC_F16 if in_dtype == torch.float16 else K.KFAC_F32
@@ -50,6 +54,8 @@ class KfacStep:
                  K.kfac_pack_sym_workspace(self.n_all),
                  K.kfac_invert_workspace(self.n_all),
                  K.kfac_precondition_workspace(self.d_g, self.d_a)]
+        if self.refine:
+            sizes.append(K.kfac_invert_refine_workspace(self.n_all))
         if self.bn_layers:
             sizes.append(K.kfac_bn_diag_workspace(self.bn_layers))
         # one workspace serves every call: they run one after another on one stream
@@ -72,6 +78,10 @@ class KfacStep:
         K.kfac_pack_sym(self.n_all, self.full, self.packed_all, 2, self.workspace, stream)
         K.kfac_invert(self.n_all, self.full, self.full, [self.shift] * len(self.n_all), self.info,
                       None, self.workspace, stream)
+        if self.refine:
+            K.kfac_pack_sym(self.n_all, self.factor_full, self.packed_all, 1, self.workspace, stream)
+            K.kfac_invert_refine(self.n_all, self.factor_full, [self.shift] * len(self.n_all), self.full,
+                                 self.workspace, stream)
 
     def precondition(self, grads, weights=None, lr=0.0, stream=None):
         """self.out <- preconditioned gradients; with weights (fp32 [d_g, d_a] per layer)

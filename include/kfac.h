@@ -155,6 +155,24 @@ kfac_status kfac_invert(int32_t count, const int32_t* n, const float* const* mat
                         float* const* chol, void* workspace, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * kfac_invert_refine - one refinement step of damped inverses ([OTUNYM] eq. (6)):
+ *   inv[m] <- X + X E,  E = I - (mat[m] + shift[m] I) X,  X = inv[m] on entry,
+ * the product mat[m] X summed in fp64 from the fp32 operands and subtracted from
+ * I - shift[m] X (formed in fp32) once per element, X E summed in fp32, and the
+ * correction added symmetrised ((X E + (X E)^T) / 2). mat[m] is the undamped factor
+ * as a full symmetric n x n row-major fp32 matrix (both triangles, e.g. kfac_pack_sym
+ * direction 1), inv[m] a full symmetric n x n approximate inverse (e.g. from
+ * kfac_invert); both device, caller-owned, not overlapping; inv is updated in place.
+ * shift: host array of finite values. Costs two n x n x n products per matrix.
+ * Errors: KFAC_ERR_INVALID for bad sizes, NULL, misaligned or aliased pointers and
+ * non-finite shifts, KFAC_ERR_WORKSPACE for a missing or short workspace.
+ * ------------------------------------------------------------------------- */
+kfac_status kfac_invert_refine_workspace(int32_t count, const int32_t* n, size_t* bytes);
+kfac_status kfac_invert_refine(int32_t count, const int32_t* n, const float* const* mat,
+                               const float* shift, float* const* inv, void* workspace,
+                               size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * kfac_precondition - G^-1 dW A^-1 per layer ([OTUNYM] eq. (7)).
  *
  * Layer l: G_inv[l] is d_g[l] x d_g[l], A_inv[l] is d_a[l] x d_a[l] (full symmetric,
