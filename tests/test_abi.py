@@ -188,3 +188,28 @@ def test_patch_rows_workspace(lib):
     big = lib.kfac_factors_workspace(conv1(600), lib.KFAC_F16)
     assert 600 * 112 * 112 * 152 * 2 >= 1 << 31
     assert big < 600 * 112 * 112 * 152 * 2           # no row buffer at this size
+
+
+def test_invert_refine_validation(lib):
+    """kfac_invert_refine rejects bad sizes, NULL, aliased or misaligned pointers and
+    non-finite shifts before touching the device; its workspace holds E and C per matrix."""
+    so = lib._lib
+    c = ctypes
+    sz = c.c_size_t()
+    n = (c.c_int32 * 2)(300, 7)
+    assert so.kfac_invert_refine_workspace(2, n, c.byref(sz)) == 0
+    assert sz.value >= 4 * 2 * (300 * 300 + 7 * 7)
+    bad = (c.c_int32 * 1)(0)
+    assert so.kfac_invert_refine_workspace(1, bad, c.byref(sz)) == -1
+    one = (c.c_int32 * 1)(4)
+    shift = (c.c_float * 1)(1e-3)
+    nan = (c.c_float * 1)(float("nan"))
+    nullp = (c.c_void_p * 1)(None)
+    a = (c.c_void_p * 1)(0x1000)
+    b = (c.c_void_p * 1)(0x2000)
+    odd = (c.c_void_p * 1)(0x2002)
+    assert so.kfac_invert_refine(1, one, nullp, shift, b, None, 0, None) == -1   # NULL matrix
+    assert so.kfac_invert_refine(1, one, a, shift, a, None, 0, None) == -1       # mat aliases inv
+    assert so.kfac_invert_refine(1, one, a, shift, odd, None, 0, None) == -1     # misaligned
+    assert so.kfac_invert_refine(1, one, a, nan, b, None, 0, None) == -1         # NaN shift
+    assert so.kfac_invert_refine(0, None, None, None, None, None, 0, None) == 0  # no-op
