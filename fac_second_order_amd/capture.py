@@ -134,11 +134,18 @@ class KfacCapture:
     or None) pairs. Call `step(lr)` after `loss.backward()`: it forms the factors
     from the captured tensors, inverts them (every `refresh`-th call), preconditions
     the weight gradients and updates the weights and the BatchNorm parameters in
-    place (eq. 8) through libkfac."""
+    place (eq. 8) through libkfac. precond_accum and refine_inverse are passed to
+    KfacStep: "f64" sums the preconditioning products in fp64, refine_inverse takes
+    one fp64-residual refinement step of every inverse. A real gradient lies in the
+    range of its layer's factors, so where a factor is rank-deficient (batch smaller
+    than its order) and the damping small, the preconditioning products cancel and
+    amplify the inverses' fp32 error; the two options remove most of it."""
 
-    def __init__(self, model, damping=1e-3, ema_decay=0.95, refresh_every=1, precond_accum="f32"):
+    def __init__(self, model, damping=1e-3, ema_decay=0.95, refresh_every=1, precond_accum="f32",
+                 refine_inverse=False):
         self.model = model
         self.precond_accum = precond_accum
+        self.refine_inverse = bool(refine_inverse)
         self.pairs = list(model.kfac_modules())
         self.damping = damping
         self.ema_decay = ema_decay
@@ -241,7 +248,8 @@ class KfacCapture:
         dev = self.act[0].device
         if self.kstep is None:
             layers, bns = self._geometry()
-            self.kstep = KfacStep(layers, bns, dev, damping=self.damping, precond_accum=self.precond_accum)
+            self.kstep = KfacStep(layers, bns, dev, damping=self.damping, precond_accum=self.precond_accum,
+                                  refine_inverse=self.refine_inverse)
             self.master = [self._to_matrix(m) for m, _ in self.pairs]
             self.bn_master = [torch.stack([bn.weight.data.float(), bn.bias.data.float()]).contiguous()
                               for bn in self.bns]

@@ -280,11 +280,27 @@ extern "C" kfac_status kfac_bn_diag_workspace(const kfac_bn* layers, int32_t cou
   return KFAC_OK;
 }
 
-// kfac_bn_diag, and with params the update of eq. (8).
-static kfac_status bn_impl(const kfac_bn* layers, int32_t count, kfac_dtype in_dtype, const void* const* xhat,
-                           const void* const* gout, float* const* fisher, float* const* precond,
-                           float* const* params, float lr, float ema_decay, float shift, void* workspace,
-                           size_t ws_bytes, void* stream) {
+// A validated call: per layer its plan with the caller's pointers, and the number of
+// partial-sum pairs it needs.
+struct BnCall {
+  std::vector<BnDesc> desc;
+  std::vector<size_t> part;
+  int f32 = 0;
+};
+
+// Workspace of the layers [l0, l1) of a call: descriptors, two offset tables, partials.
+static size_t bn_need(const BnCall& c, int l0, int l1) {
+  size_t part = 0;
+  for (int l = l0; l < l1; ++l) part += c.part[l];
+  const int k = l1 - l0;
+  return align256(sizeof(BnDesc) * k) + 2 * align256(sizeof(int32_t) * k) + align256(sizeof(v2f) * part);
+}
+
+// Argument checks and plans (nothing enqueued). kfac_bn_diag, and with params the
+// update of eq. (8).
+static kfac_status bn_prepare(const kfac_bn* layers, int32_t count, kfac_dtype in_dtype, const void* const* xhat,
+                              const void* const* gout, float* const* fisher, float* const* precond,
+                              float* const* params, float lr, float ema_decay, float shift, BnCall& call) {
   kfac_status st = bn_validate(layers, count, in_dtype);
   if (st) return st;
   if (params && !(lr - lr == 0.f)) return fail(KFAC_ERR_INVALID, "lr must be finite");
@@ -293,10 +309,9 @@ static kfac_status bn_impl(const kfac_bn* layers, int32_t count, kfac_dtype in_d
   if (count == 0) return KFAC_OK;
   if (!xhat || !gout || !fisher || !precond) return fail(KFAC_ERR_INVALID, "NULL pointer array");
   const int esize = in_dtype == KFAC_F16 ? 2 : 4;
-  std::vector<BnDesc> desc(count);
-  std::vector<int32_t> begin(count), cbegin(count);
-  int64_t items = 0, channels = 0;
-  size_t part = 0;
+  call.f32 = in_dtype == KFAC_F32 ? 1 : 0;
+  call.desc.resize(count);
+  call.part.resize(count);
   for (int l = 0; l < count; ++l) {
     if (!xhat[l] || !gout[l] || !fisher[l] || !precond[l] || (params && !params[l]))
       return fail(KFAC_ERR_INVALID, "bn layer %d: NULL pointer", l);
@@ -307,51 +322,74 @@ static kfac_status bn_impl(const kfac_bn* layers, int32_t count, kfac_dtype in_d
     const uintptr_t a = reinterpret_cast<uintptr_t>(xhat[l]) | reinterpret_cast<uintptr_t>(gout[l]);
     if (a % esize || (reinterpret_cast<uintptr_t>(fisher[l]) | reinterpret_cast<uintptr_t>(precond[l])) & 3)
       return fail(KFAC_ERR_INVALID, "bn layer %d: misaligned pointer", l);
-    desc[l] = plan_layer(layers[l], esize, a % 16 == 0);
-    begin[l] = static_cast<int32_t>(items);
-    items += int64_t(desc[l].n) * desc[l].nchunk * desc[l].cblocks;
-    cbegin[l] = static_cast<int32_t>(channels);
-    channels += (desc[l].c + FIN_CH - 1) / FIN_CH;  // finish blocks
-    part += partial_count(desc[l]);
-  }
-  if (items >= (int64_t(1) << 31) || channels >= (int64_t(1) << 31))
-    return fail(KFAC_ERR_INVALID, "bn problem too large");
-  st = check_device();
-  if (st) return st;
-  const size_t need = align256(sizeof(BnDesc) * count) + 2 * align256(sizeof(int32_t) * count) +
-                      align256(sizeof(v2f) * part);
-  st = check_workspace(workspace, ws_bytes, need);
-  if (st) return st;
-  Carver cv(workspace);
-  BnDesc* d_desc = cv.take<BnDesc>(count);
-  int32_t* d_begin = cv.take<int32_t>(count);
-  int32_t* d_cbegin = cv.take<int32_t>(count);
-  v2f* partial = cv.take<v2f>(part);
-  size_t off = 0;
-  for (int l = 0; l < count; ++l) {
-    BnDesc& d = desc[l];
+    BnDesc& d = call.desc[l];
+    d = plan_layer(layers[l], esize, a % 16 == 0);
     d.xhat = xhat[l];
     d.gout = gout[l];
     d.fisher = fisher[l];
     d.precond = precond[l];
     d.params = params ? params[l] : nullptr;
     d.lr = lr;
-    d.partial = partial + off;
-    off += partial_count(d);
+    call.part[l] = partial_count(d);
   }
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  return KFAC_OK;
+}
+
+// Enqueues layers [l0, l1) of a call with their tables and partial sums carved from
+// `ws` (at least bn_need bytes): one table upload, the partial and the finish launch.
+static kfac_status bn_launch(BnCall& c, int l0, int l1, void* ws, float ema_decay, float shift, hipStream_t s) {
+  const int count = l1 - l0;
+  std::vector<int32_t> begin(count), cbegin(count);
+  int64_t items = 0, channels = 0;
+  for (int l = 0; l < count; ++l) {
+    const BnDesc& d = c.desc[l0 + l];
+    begin[l] = static_cast<int32_t>(items);
+    items += int64_t(d.n) * d.nchunk * d.cblocks;
+    cbegin[l] = static_cast<int32_t>(channels);
+    channels += (d.c + FIN_CH - 1) / FIN_CH;  // finish blocks
+  }
+  if (items >= (int64_t(1) << 31) || channels >= (int64_t(1) << 31))
+    return fail(KFAC_ERR_INVALID, "bn problem too large");
+  Carver cv(ws);
+  BnDesc* d_desc = cv.take<BnDesc>(count);
+  int32_t* d_begin = cv.take<int32_t>(count);
+  int32_t* d_cbegin = cv.take<int32_t>(count);
+  size_t part = 0;
+  for (int l = l0; l < l1; ++l) part += c.part[l];
+  v2f* partial = cv.take<v2f>(part);
+  size_t off = 0;
+  for (int l = l0; l < l1; ++l) {
+    c.desc[l].partial = partial + off;
+    off += c.part[l];
+  }
   TableUpload tu;
-  tu.add(d_desc, desc.data(), sizeof(BnDesc) * count);
+  tu.add(d_desc, c.desc.data() + l0, sizeof(BnDesc) * count);
   tu.add(d_begin, begin.data(), sizeof(int32_t) * count);
   tu.add(d_cbegin, cbegin.data(), sizeof(int32_t) * count);
-  if ((st = tu.flush(s))) return st;
+  kfac_status st = tu.flush(s);
+  if (st) return st;
   KFAC_LAUNCH(K_BN_PARTIAL, bn_partial_kernel, dim3(static_cast<unsigned>(items)), dim3(256), 0, s,
-              d_desc, d_begin, count, in_dtype == KFAC_F32 ? 1 : 0);
+              d_desc, d_begin, count, c.f32);
   KFAC_CHECK_LAUNCH("bn_partial_kernel");
   KFAC_LAUNCH(K_BN_FINISH, bn_finish_kernel, dim3(static_cast<unsigned>(channels)), dim3(256), 0, s, d_desc,
               d_cbegin, count, ema_decay, shift);
   KFAC_CHECK_LAUNCH("bn_finish_kernel");
   return KFAC_OK;
+}
+
+static kfac_status bn_impl(const kfac_bn* layers, int32_t count, kfac_dtype in_dtype, const void* const* xhat,
+                           const void* const* gout, float* const* fisher, float* const* precond,
+                           float* const* params, float lr, float ema_decay, float shift, void* workspace,
+                           size_t ws_bytes, void* stream) {
+  BnCall call;
+  kfac_status st = bn_prepare(layers, count, in_dtype, xhat, gout, fisher, precond, params, lr, ema_decay, shift,
+                              call);
+  if (st || count == 0) return st;
+  st = check_device();
+  if (st) return st;
+  st = check_workspace(workspace, ws_bytes, bn_need(call, 0, count));
+  if (st) return st;
+  return bn_launch(call, 0, count, workspace, ema_decay, shift, static_cast<hipStream_t>(stream));
 }
 
 extern "C" kfac_status kfac_bn_diag(const kfac_bn* layers, int32_t count, kfac_dtype in_dtype,

@@ -88,6 +88,10 @@ enum KernelId {
   K_GEMM,
   K_BN_PARTIAL,
   K_BN_FINISH,
+  K_GEMM64,        // gemm_tn64_kernel of the preconditioning (fp64 sums)
+  K_REFINE_EW,     // refine_init_kernel and refine_apply_kernel
+  K_REFINE_RES,    // gemm_tn64_kernel forming the residual of the refinement
+  K_REFINE_CORR,   // gemm_tn_kernel forming the correction of the refinement
   K_COUNT
 };
 

@@ -130,7 +130,8 @@ static const char* const kKernelNames[K_COUNT] = {
     "upload_kernel",      "syrk_tile_kernel",   "syrk_reduce_kernel", "pack_kernel",
     "unpack_kernel",      "inv_prep_kernel",    "inv_pivot_kernel",   "inv_panel_kernel",
     "inv_update_kernel",  "inv_finish_kernel",  "gemm_tn_kernel",     "bn_partial_kernel",
-    "bn_finish_kernel"};
+    "bn_finish_kernel",   "gemm_tn64_kernel",   "refine_elementwise_kernels",
+    "refine_residual_gemm_tn64_kernel",         "refine_correction_gemm_tn_kernel"};
 
 }  // namespace kfac
 

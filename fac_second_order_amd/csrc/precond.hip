@@ -27,12 +27,15 @@ struct GemmDesc {
   int32_t b_f16;
   int32_t c_trans;
   int32_t tm, tn;  // tiles along M and N
-  int32_t buf;             // both operands below 2^31 bytes: branch-free buffer pipeline
   int32_t a_mode, b_mode;  // LD_V4 / LD_F32 (fp32 operands) or LD_F16 (B fp16)
 };
 
-__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) gemm_tn_kernel(const GemmDesc* __restrict__ desc,
-                                                      const int32_t* __restrict__ begin, int count) {
+// MA: load form of every A operand of the launch (one instantiation per form keeps
+// the register use of the common 16-byte form; the element form, with four times the
+// loads in flight, gets room for two waves per SIMD instead of four).
+template <int MA>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(MA == LD_V4 ? 4 : 2, 4)))
+gemm_tn_kernel(const GemmDesc* __restrict__ desc, const int32_t* __restrict__ begin, int count) {
   const int p = find_problem(begin, count, blockIdx.x);
   const GemmDesc& d = desc[p];
   // column-panel major: the tiles that share a B column panel run back to back
@@ -45,13 +48,9 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))
   const Operand A = op_rows(d.A, d.lda, d.K, m0, d.M);
   const Operand B = d.b_f16 ? op_rows_h(static_cast<const _Float16*>(d.B), d.ldb, d.K, n0, d.N)
                             : op_rows(static_cast<const float*>(d.B), d.ldb, d.K, n0, d.N);
-  if (d.buf) {  // A in 16-byte groups (checked on the host), B in its own form
-    if (d.b_mode == LD_V4) oct_gemm<LD_V4, LD_V4>(q, A, B, d.K, 1.f, lds);
-    else if (d.b_mode == LD_F32) oct_gemm<LD_V4, LD_F32>(q, A, B, d.K, 1.f, lds);
-    else oct_gemm<LD_V4, LD_F16>(q, A, B, d.K, 1.f, lds);
-  } else {
-    oct_gemm<LD_V4, LD_V4, true>(q, A, B, d.K, 1.f, lds);
-  }
+  if (d.b_mode == LD_V4) oct_gemm<MA, LD_V4>(q, A, B, d.K, 1.f, lds);
+  else if (d.b_mode == LD_F32) oct_gemm<MA, LD_F32>(q, A, B, d.K, 1.f, lds);
+  else oct_gemm<MA, LD_F16>(q, A, B, d.K, 1.f, lds);
   const int rv = min(TB, d.M - m0), cv = min(TB, d.N - n0);
   if (d.c_trans) {
     oct_store_t(q, d.C + int64_t(n0) * d.ldc + m0, d.ldc, rv, cv, lds);
@@ -63,8 +62,9 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))
 
 // The same with fp64 accumulation (its 64 accumulator registers leave room for two
 // waves per SIMD).
-__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) gemm_tn64_kernel(const GemmDesc* __restrict__ desc,
-                                                        const int32_t* __restrict__ begin, int count) {
+template <int MA>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+gemm_tn64_kernel(const GemmDesc* __restrict__ desc, const int32_t* __restrict__ begin, int count) {
   const int p = find_problem(begin, count, blockIdx.x);
   const GemmDesc& d = desc[p];
   const int t = blockIdx.x - begin[p];
@@ -76,13 +76,9 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   const Operand A = op_rows(d.A, d.lda, d.K, m0, d.M);
   const Operand B = d.b_f16 ? op_rows_h(static_cast<const _Float16*>(d.B), d.ldb, d.K, n0, d.N)
                             : op_rows(static_cast<const float*>(d.B), d.ldb, d.K, n0, d.N);
-  if (d.buf) {
-    if (d.b_mode == LD_V4) oct64_gemm<LD_V4, LD_V4>(q, A, B, d.K, lds);
-    else if (d.b_mode == LD_F32) oct64_gemm<LD_V4, LD_F32>(q, A, B, d.K, lds);
-    else oct64_gemm<LD_V4, LD_F16>(q, A, B, d.K, lds);
-  } else {
-    oct64_gemm<LD_V4, LD_V4, true>(q, A, B, d.K, lds);
-  }
+  if (d.b_mode == LD_V4) oct64_gemm<MA, LD_V4>(q, A, B, d.K, lds);
+  else if (d.b_mode == LD_F32) oct64_gemm<MA, LD_F32>(q, A, B, d.K, lds);
+  else oct64_gemm<MA, LD_F16>(q, A, B, d.K, lds);
   const int rv = min(TB, d.M - m0), cv = min(TB, d.N - n0);
   if (d.c_trans) {
     oct64_store_t(q, d.C + int64_t(n0) * d.ldc + m0, d.ldc, rv, cv, lds);
@@ -93,15 +89,67 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
 }
 
 // Load forms of a problem's operands: 16-byte groups for fp32 rows whose pitch is a
-// multiple of 4 floats on a 16-byte aligned base, single elements otherwise. The
-// buffer pipeline takes problems whose operands span less than 2^31 bytes each and
-// whose A operand has 16-byte groups (A is G^-1 or the T^T workspace, pitch d_G).
-static void set_modes(GemmDesc& g, int b_esize) {
-  const int64_t abytes = int64_t(g.K) * g.lda * 4, bbytes = int64_t(g.K) * g.ldb * b_esize;
+// multiple of 4 floats on a 16-byte aligned base, single elements otherwise. Every
+// operand is read through a raw buffer, so it must span less than 2^31 bytes
+// (operands_fit, checked before anything is enqueued).
+static void set_modes(GemmDesc& g) {
   g.a_mode = (g.lda % 4 == 0 && reinterpret_cast<uintptr_t>(g.A) % 16 == 0) ? LD_V4 : LD_F32;
-  g.buf = abytes < (int64_t(1) << 31) && bbytes < (int64_t(1) << 31) && g.a_mode == LD_V4;
   if (g.b_f16) g.b_mode = LD_F16;
   else g.b_mode = (g.ldb % 4 == 0 && reinterpret_cast<uintptr_t>(g.B) % 16 == 0) ? LD_V4 : LD_F32;
+}
+
+// The largest operand of a layer (G^-1 or A^-1, d x d fp32; dW, d_G x d_A) spans less
+// than 2^31 bytes: d_G, d_A <= 23170.
+static bool operands_fit(int64_t dg, int64_t da) {
+  const int64_t lim = int64_t(1) << 31;
+  return dg * dg * 4 < lim && da * da * 4 < lim && dg * da * 4 < lim;
+}
+
+// One grouped product: its problems in launch order, those whose A operand has
+// 16-byte groups first (stable); begin offsets restart at 0 for the others, which run
+// as a second launch of the element-form instantiation.
+struct Grouped {
+  std::vector<GemmDesc> g;
+  std::vector<int32_t> begin;
+  int n_v4 = 0;
+  int64_t tiles_v4 = 0, tiles_el = 0;
+  bool fits() const { return tiles_v4 < (int64_t(1) << 31) && tiles_el < (int64_t(1) << 31); }
+};
+
+static Grouped group_by_a_mode(const std::vector<GemmDesc>& in) {
+  Grouped r;
+  for (int pass = 0; pass < 2; ++pass) {
+    int64_t t = 0;
+    for (const GemmDesc& x : in) {
+      if ((x.a_mode == LD_V4) != (pass == 0)) continue;
+      r.g.push_back(x);
+      r.begin.push_back(static_cast<int32_t>(t));
+      t += int64_t(x.tm) * x.tn;
+    }
+    (pass == 0 ? r.tiles_v4 : r.tiles_el) = t;
+    if (pass == 0) r.n_v4 = static_cast<int>(r.g.size());
+  }
+  return r;
+}
+
+// Launches a grouped product whose tables are at desc/begin on the device.
+static kfac_status launch_grouped(int kid, bool f64, const Grouped& gr, const GemmDesc* desc, const int32_t* begin,
+                                  hipStream_t s, const char* what) {
+  const int count = static_cast<int>(gr.g.size());
+  if (gr.n_v4 > 0) {
+    const dim3 grid(static_cast<unsigned>(gr.tiles_v4));
+    if (f64) KFAC_LAUNCH(kid, gemm_tn64_kernel<LD_V4>, grid, dim3(512), 0, s, desc, begin, gr.n_v4);
+    else KFAC_LAUNCH(kid, gemm_tn_kernel<LD_V4>, grid, dim3(512), 0, s, desc, begin, gr.n_v4);
+    KFAC_CHECK_LAUNCH(what);
+  }
+  if (count > gr.n_v4) {
+    const dim3 grid(static_cast<unsigned>(gr.tiles_el));
+    const int c = count - gr.n_v4;
+    if (f64) KFAC_LAUNCH(kid, gemm_tn64_kernel<LD_F32>, grid, dim3(512), 0, s, desc + gr.n_v4, begin + gr.n_v4, c);
+    else KFAC_LAUNCH(kid, gemm_tn_kernel<LD_F32>, grid, dim3(512), 0, s, desc + gr.n_v4, begin + gr.n_v4, c);
+    KFAC_CHECK_LAUNCH(what);
+  }
+  return KFAC_OK;
 }
 
 static size_t precond_ws(int count, const int32_t* dg, const int32_t* da) {
@@ -121,6 +169,10 @@ static kfac_status precond_validate(int32_t count, const int32_t* dg, const int3
   for (int l = 0; l < count; ++l)
     if (dg[l] < 1 || da[l] < 1 || dg[l] > 65536 || da[l] > 65536)
       return fail(KFAC_ERR_INVALID, "layer %d: d_g = %d, d_a = %d out of range", l, dg[l], da[l]);
+  for (int l = 0; l < count; ++l)
+    if (!operands_fit(dg[l], da[l]))
+      return fail(KFAC_ERR_UNSUPPORTED, "layer %d: d_g = %d, d_a = %d: operands of 2^31 bytes or more", l, dg[l],
+                  da[l]);
   return KFAC_OK;
 }
 
@@ -179,8 +231,6 @@ static kfac_status precond_impl(int32_t count, const int32_t* d_g, const int32_t
   std::stable_sort(o1.begin(), o1.end(), [&](int a, int b) { return d_g[a] > d_g[b]; });
   std::stable_sort(o2.begin(), o2.end(), [&](int a, int b) { return d_a[a] > d_a[b]; });
   std::vector<GemmDesc> x1(count), x2(count), g1(count), g2(count);
-  std::vector<int32_t> e1(count), e2(count);
-  int64_t n1 = 0, n2 = 0;
   size_t off = 0;
   for (int l = 0; l < count; ++l) {
     const int G = d_g[l], A = d_a[l];
@@ -192,7 +242,7 @@ static kfac_status precond_impl(int32_t count, const int32_t* d_g, const int32_t
     x.lda = G; x.ldb = A; x.ldc = G;
     x.b_f16 = grad_dtype == KFAC_F16; x.c_trans = 1;
     x.tm = (G + TB - 1) / TB; x.tn = (A + TB - 1) / TB;
-    set_modes(x, esize);
+    set_modes(x);
     x1[l] = x;
     GemmDesc y{};
     y.A = T; y.B = A_inv[l]; y.C = out ? out[l] : nullptr;
@@ -201,36 +251,26 @@ static kfac_status precond_impl(int32_t count, const int32_t* d_g, const int32_t
     y.lda = G; y.ldb = A; y.ldc = A;
     y.b_f16 = 0; y.c_trans = 0;
     y.tm = x.tm; y.tn = x.tn;
-    set_modes(y, 4);
+    set_modes(y);
     x2[l] = y;
   }
   for (int q = 0; q < count; ++q) {
     g1[q] = x1[o1[q]];
-    e1[q] = static_cast<int32_t>(n1);
-    n1 += int64_t(g1[q].tm) * g1[q].tn;
     g2[q] = x2[o2[q]];
-    e2[q] = static_cast<int32_t>(n2);
-    n2 += int64_t(g2[q].tm) * g2[q].tn;
   }
-  if (n1 >= (int64_t(1) << 31)) return fail(KFAC_ERR_INVALID, "too many tiles");
+  const Grouped p1 = group_by_a_mode(g1), p2 = group_by_a_mode(g2);
+  if (!p1.fits() || !p2.fits()) return fail(KFAC_ERR_INVALID, "too many tiles");
   hipStream_t s = static_cast<hipStream_t>(stream);
   TableUpload tu;
-  tu.add(d1, g1.data(), sizeof(GemmDesc) * count);
-  tu.add(d2, g2.data(), sizeof(GemmDesc) * count);
-  tu.add(b1, e1.data(), sizeof(int32_t) * count);
-  tu.add(b2, e2.data(), sizeof(int32_t) * count);
+  tu.add(d1, p1.g.data(), sizeof(GemmDesc) * count);
+  tu.add(d2, p2.g.data(), sizeof(GemmDesc) * count);
+  tu.add(b1, p1.begin.data(), sizeof(int32_t) * count);
+  tu.add(b2, p2.begin.data(), sizeof(int32_t) * count);
   if ((st = tu.flush(s))) return st;
-  if (accum == KFAC_F64) {
-    KFAC_LAUNCH(K_GEMM, gemm_tn64_kernel, dim3(static_cast<unsigned>(n1)), dim3(512), 0, s, d1, b1, count);
-    KFAC_CHECK_LAUNCH("gemm_tn64_kernel (G^-1 dW)");
-    KFAC_LAUNCH(K_GEMM, gemm_tn64_kernel, dim3(static_cast<unsigned>(n2)), dim3(512), 0, s, d2, b2, count);
-    KFAC_CHECK_LAUNCH("gemm_tn64_kernel (T A^-1)");
-    return KFAC_OK;
-  }
-  KFAC_LAUNCH(K_GEMM, gemm_tn_kernel, dim3(static_cast<unsigned>(n1)), dim3(512), 0, s, d1, b1, count);
-  KFAC_CHECK_LAUNCH("gemm_tn_kernel (G^-1 dW)");
-  KFAC_LAUNCH(K_GEMM, gemm_tn_kernel, dim3(static_cast<unsigned>(n2)), dim3(512), 0, s, d2, b2, count);
-  KFAC_CHECK_LAUNCH("gemm_tn_kernel (T A^-1)");
+  const bool f64 = accum == KFAC_F64;
+  const int kid = f64 ? K_GEMM64 : K_GEMM;
+  if ((st = launch_grouped(kid, f64, p1, d1, b1, s, "gemm_tn kernel (G^-1 dW)"))) return st;
+  if ((st = launch_grouped(kid, f64, p2, d2, b2, s, "gemm_tn kernel (T A^-1)"))) return st;
   return KFAC_OK;
 }
 
@@ -342,8 +382,28 @@ extern "C" kfac_status kfac_invert_refine(int32_t count, const int32_t* n, const
     if (!mat[m] || !inv[m]) return fail(KFAC_ERR_INVALID, "matrix %d: NULL pointer", m);
     if ((reinterpret_cast<uintptr_t>(mat[m]) | reinterpret_cast<uintptr_t>(inv[m])) & 3)
       return fail(KFAC_ERR_INVALID, "matrix %d: misaligned pointer", m);
-    if (mat[m] == inv[m]) return fail(KFAC_ERR_INVALID, "matrix %d: mat and inv are the same buffer", m);
     if (!(shift[m] - shift[m] == 0.f)) return fail(KFAC_ERR_INVALID, "matrix %d: shift is not finite", m);
+  }
+  {  // no inv buffer may overlap any mat or inv buffer (mat buffers are only read)
+    struct Range { uintptr_t lo, hi; int m; bool out; };
+    std::vector<Range> r;
+    r.reserve(2 * count);
+    for (int m = 0; m < count; ++m) {
+      const uintptr_t bytes = uintptr_t(n[m]) * uintptr_t(n[m]) * 4;
+      r.push_back({reinterpret_cast<uintptr_t>(mat[m]), reinterpret_cast<uintptr_t>(mat[m]) + bytes, m, false});
+      r.push_back({reinterpret_cast<uintptr_t>(inv[m]), reinterpret_cast<uintptr_t>(inv[m]) + bytes, m, true});
+    }
+    std::sort(r.begin(), r.end(), [](const Range& a, const Range& b) { return a.lo < b.lo; });
+    // sweep in address order: each range against the furthest-reaching earlier one of
+    // each kind (an overlap of two mat ranges is allowed)
+    uintptr_t end_in = 0, end_out = 0;
+    int m_in = -1, m_out = -1;
+    for (const Range& x : r) {
+      if (x.out && x.lo < end_in) return fail(KFAC_ERR_INVALID, "inv[%d] overlaps mat[%d]", x.m, m_in);
+      if (x.lo < end_out) return fail(KFAC_ERR_INVALID, "%s[%d] overlaps inv[%d]", x.out ? "inv" : "mat", x.m, m_out);
+      if (x.out) { if (x.hi > end_out) { end_out = x.hi; m_out = x.m; } }
+      else if (x.hi > end_in) { end_in = x.hi; m_in = x.m; }
+    }
   }
   st = check_device();
   if (st) return st;
@@ -368,10 +428,10 @@ extern "C" kfac_status kfac_invert_refine(int32_t count, const int32_t* n, const
   for (int m = 0; m < count; ++m) order[m] = m;
   std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return n[a] > n[b]; });
   std::vector<GemmDesc> g1(count), g2(count);
-  std::vector<int32_t> e1(count), e2(count), ebv(count), tbv(count), nv(count);
+  std::vector<int32_t> ebv(count), tbv(count), nv(count);
   std::vector<float*> xv(count), ev(count), cvv(count);
   std::vector<float> sv(count);
-  int64_t n1 = 0, n2 = 0, ne = 0, nt = 0;
+  int64_t ne = 0, nt = 0;
   size_t off = 0;
   for (int q = 0; q < count; ++q) {
     const int m = order[q], N = n[m];
@@ -381,28 +441,27 @@ extern "C" kfac_status kfac_invert_refine(int32_t count, const int32_t* n, const
     x.A = mat[m]; x.B = inv[m]; x.W = E; x.lr = 1.f;
     x.M = N; x.N = N; x.K = N; x.lda = N; x.ldb = N; x.ldc = N;
     x.tm = x.tn = (N + TB - 1) / TB;
-    set_modes(x, 4);
+    set_modes(x);
     GemmDesc y{};  // C = X E: A operand X (symmetric)
     y.A = inv[m]; y.B = E; y.C = C;
     y.M = N; y.N = N; y.K = N; y.lda = N; y.ldb = N; y.ldc = N;
     y.tm = y.tn = x.tm;
-    set_modes(y, 4);
+    set_modes(y);
     g1[q] = x; g2[q] = y;
-    e1[q] = static_cast<int32_t>(n1); n1 += int64_t(x.tm) * x.tn;
-    e2[q] = static_cast<int32_t>(n2); n2 += int64_t(y.tm) * y.tn;
     ebv[q] = static_cast<int32_t>(ne); ne += (int64_t(N) * N + 1023) / 1024;
     tbv[q] = static_cast<int32_t>(nt); nt += int64_t((N + 63) / 64) * ((N + 63) / 64);
     xv[q] = inv[m]; ev[q] = E; cvv[q] = C;
     nv[q] = N; sv[q] = shift[m];
   }
-  if (n1 >= (int64_t(1) << 31) || ne >= (int64_t(1) << 31) || nt >= (int64_t(1) << 31))
+  const Grouped p1 = group_by_a_mode(g1), p2 = group_by_a_mode(g2);
+  if (!p1.fits() || !p2.fits() || ne >= (int64_t(1) << 31) || nt >= (int64_t(1) << 31))
     return fail(KFAC_ERR_INVALID, "too many tiles");
   hipStream_t s = static_cast<hipStream_t>(stream);
   TableUpload tu;
-  tu.add(d1, g1.data(), sizeof(GemmDesc) * count);
-  tu.add(d2, g2.data(), sizeof(GemmDesc) * count);
-  tu.add(b1, e1.data(), sizeof(int32_t) * count);
-  tu.add(b2, e2.data(), sizeof(int32_t) * count);
+  tu.add(d1, p1.g.data(), sizeof(GemmDesc) * count);
+  tu.add(d2, p2.g.data(), sizeof(GemmDesc) * count);
+  tu.add(b1, p1.begin.data(), sizeof(int32_t) * count);
+  tu.add(b2, p2.begin.data(), sizeof(int32_t) * count);
   tu.add(eb, ebv.data(), sizeof(int32_t) * count);
   tu.add(tb, tbv.data(), sizeof(int32_t) * count);
   tu.add(dX, xv.data(), sizeof(float*) * count);
@@ -411,13 +470,11 @@ extern "C" kfac_status kfac_invert_refine(int32_t count, const int32_t* n, const
   tu.add(dn, nv.data(), sizeof(int32_t) * count);
   tu.add(ds, sv.data(), sizeof(float) * count);
   if ((st = tu.flush(s))) return st;
-  KFAC_LAUNCH(K_GEMM, refine_init_kernel, dim3(static_cast<unsigned>(ne)), dim3(256), 0, s, dX, dE, dn, ds, eb, count);
+  KFAC_LAUNCH(K_REFINE_EW, refine_init_kernel, dim3(static_cast<unsigned>(ne)), dim3(256), 0, s, dX, dE, dn, ds, eb, count);
   KFAC_CHECK_LAUNCH("refine_init_kernel");
-  KFAC_LAUNCH(K_GEMM, gemm_tn64_kernel, dim3(static_cast<unsigned>(n1)), dim3(512), 0, s, d1, b1, count);
-  KFAC_CHECK_LAUNCH("gemm_tn64_kernel (E -= F X)");
-  KFAC_LAUNCH(K_GEMM, gemm_tn_kernel, dim3(static_cast<unsigned>(n2)), dim3(512), 0, s, d2, b2, count);
-  KFAC_CHECK_LAUNCH("gemm_tn_kernel (X E)");
-  KFAC_LAUNCH(K_GEMM, refine_apply_kernel, dim3(static_cast<unsigned>(nt)), dim3(256), 0, s, dX, dC, dn, tb, count);
+  if ((st = launch_grouped(K_REFINE_RES, true, p1, d1, b1, s, "gemm_tn64_kernel (E -= F X)"))) return st;
+  if ((st = launch_grouped(K_REFINE_CORR, false, p2, d2, b2, s, "gemm_tn_kernel (X E)"))) return st;
+  KFAC_LAUNCH(K_REFINE_EW, refine_apply_kernel, dim3(static_cast<unsigned>(nt)), dim3(256), 0, s, dX, dC, dn, tb, count);
   KFAC_CHECK_LAUNCH("refine_apply_kernel");
   return KFAC_OK;
 }

@@ -100,8 +100,7 @@ __device__ __forceinline__ int fast_div(int n, int dv, double rdv) {
 }
 
 struct RowTab {
-  int32_t lo[2 * KC];  // element offset, low and high 32 bits (the 16-byte gathers,
-  int32_t hi[2 * KC];  // whose tensors stay below 2^31 bytes, read the low half only)
+  int32_t lo[2 * KC];  // element offset (input tensors span less than 2^31 bytes)
   int32_t ih[2 * KC];
   int32_t iw[2 * KC];
 };
@@ -114,15 +113,12 @@ __device__ inline void fill_rowtab(const SyrkDesc& d, RowTab& t, int r0, int r_e
   const int row = r0 + tid;
   if (row >= r_end) {
     t.lo[tid] = 0;
-    t.hi[tid] = 0;
     t.ih[tid] = kNoRow;
     t.iw[tid] = 0;
     return;
   }
   if (d.mode == 0) {
-    const int64_t o = int64_t(row) * d.ld;
-    t.lo[tid] = static_cast<int32_t>(o);
-    t.hi[tid] = static_cast<int32_t>(o >> 32);
+    t.lo[tid] = row * d.ld;
     t.ih[tid] = 0;
     t.iw[tid] = 0;
     return;
@@ -133,9 +129,7 @@ __device__ inline void fill_rowtab(const SyrkDesc& d, RowTab& t, int r0, int r_e
   const int oh = fast_div(rem, d.Wo, d.rwo);
   const int ow = rem - oh * d.Wo;
   const int ih0 = oh * d.sh - d.ph, iw0 = ow * d.sw - d.pw;
-  const int64_t o = ((int64_t(n) * d.H + ih0) * d.W + iw0) * d.C;
-  t.lo[tid] = static_cast<int32_t>(o);
-  t.hi[tid] = static_cast<int32_t>(o >> 32);
+  t.lo[tid] = ((n * d.H + ih0) * d.W + iw0) * d.C;
   t.ih[tid] = ih0;
   t.iw[tid] = iw0;
 }
@@ -176,7 +170,7 @@ __device__ inline void fill_coltab(const SyrkDesc& d, int c0, ColTab& ct) {
 __device__ inline v8h gather8_elem(const SyrkDesc& d, const RowTab& t, int rr, const ColTab& ct) {
   const KG _Float16* src = gp(static_cast<const _Float16*>(d.src));
   const int ih = t.ih[rr], iw = t.iw[rr];
-  const int64_t off = (int64_t(t.hi[rr]) << 32) | static_cast<uint32_t>(t.lo[rr]);
+  const int off = t.lo[rr];
   v8h v;
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
@@ -732,9 +726,12 @@ static kfac_status layers_validate(const kfac_layer* L, int32_t count, kfac_dtyp
     if (x.bias != 0 && x.bias != 1) return fail(KFAC_ERR_INVALID, "layer %d: bias must be 0 or 1", l);
     const int64_t rows = int64_t(x.n) * x.h_out * x.w_out;
     const int64_t da = int64_t(x.c_in) * x.kh * x.kw + x.bias;
-    if (rows >= (int64_t(1) << 31) || da > 65536 || x.c_out > 65536 ||
-        int64_t(x.n) * x.h * x.w * x.c_in >= (int64_t(1) << 40))
+    if (rows >= (int64_t(1) << 31) || da > 65536 || x.c_out > 65536)
       return fail(KFAC_ERR_INVALID, "layer %d: too large", l);
+    // every input tensor is addressed with 32-bit offsets (raw buffer loads)
+    const int64_t es = dt == KFAC_F16 ? 2 : 4;
+    if (int64_t(x.n) * x.h * x.w * x.c_in * es >= (int64_t(1) << 31) || rows * x.c_out * es >= (int64_t(1) << 31))
+      return fail(KFAC_ERR_UNSUPPORTED, "layer %d: an input tensor of 2^31 bytes or more", l);
   }
   return KFAC_OK;
 }
@@ -778,7 +775,7 @@ static kfac_status build_plan(const kfac_layer* L, int32_t count, kfac_dtype dt,
         const int width = d.mode == 1 ? d.C : d.ld;
         const int64_t bytes = d.mode == 1 ? int64_t(L[l].n) * d.H * d.W * d.C * esize
                                           : int64_t(d.R) * d.ld * esize;
-        d.vec = (dt == KFAC_F16 && width % 8 == 0 && bytes < (int64_t(1) << 31) &&
+        d.vec = (dt == KFAC_F16 && width % 8 == 0 &&
                  (d.padded || (d.d_core % 8 == 0 && reinterpret_cast<uintptr_t>(src) % 16 == 0))) ? 1 : 0;
         d.nbytes = d.vec ? static_cast<int32_t>(bytes) : 0;
       }

@@ -65,21 +65,13 @@ __device__ inline void oct64_mma(Oct64& o, const float* As, const float* Bs) {
 }
 
 // oct_gemm with fp64 accumulation (same pipeline, same operand forms; no sign).
-template <int MA = LD_V4, int MB = LD_V4, bool PLAIN = false>
+template <int MA = LD_V4, int MB = LD_V4>
 __device__ inline void oct64_gemm(Oct64& o, const Operand& A, const Operand& B, int K, float* lds) {
   const int npair = (K + 2 * KT - 1) / (2 * KT);
-  const __amdgpu_buffer_rsrc_t rsa = PLAIN ? __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(A.src), 0, 0, 0x00020000)
-                                           : op_rsrc<MA>(A);
-  const __amdgpu_buffer_rsrc_t rsb = PLAIN ? __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(B.src), 0, 0, 0x00020000)
-                                           : op_rsrc<MB>(B);
-  auto fa = [&](int k0, float4 (&r)[2]) {
-    if constexpr (PLAIN) oct_fetch_plain(A, k0, r);
-    else oct_fetch<MA>(A, rsa, k0, r);
-  };
-  auto fb = [&](int k0, float4 (&r)[2]) {
-    if constexpr (PLAIN) oct_fetch_plain(B, k0, r);
-    else oct_fetch<MB>(B, rsb, k0, r);
-  };
+  const __amdgpu_buffer_rsrc_t rsa = op_rsrc<MA>(A);
+  const __amdgpu_buffer_rsrc_t rsb = op_rsrc<MB>(B);
+  auto fa = [&](int k0, float4 (&r)[2]) { oct_fetch<MA>(A, rsa, k0, r); };
+  auto fb = [&](int k0, float4 (&r)[2]) { oct_fetch<MB>(B, rsb, k0, r); };
   float4 ra0[2], rb0[2], ra1[2], rb1[2];
   fa(0, ra0);
   fb(0, rb0);

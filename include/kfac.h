@@ -102,7 +102,9 @@ const char* kfac_last_error(void);
  * out = ema_decay*out + (1 - ema_decay)*batch_value (stale curvature, [OTUNYM]
  * Section 1 contributions). 0 <= ema_decay <= 1; 1 keeps the stored factors.
  * A NULL act[l] (or gout[l]) skips that factor. Results are deterministic: the same
- * inputs give bit-identical outputs.
+ * inputs give bit-identical outputs. Each input tensor must span less than 2^31
+ * bytes (the kernels address it with 32-bit offsets); a larger one gives
+ * KFAC_ERR_UNSUPPORTED.
  * ------------------------------------------------------------------------- */
 kfac_status kfac_factors_workspace(const kfac_layer* layers, int32_t count, kfac_dtype in_dtype,
                                    size_t* bytes);
@@ -163,9 +165,13 @@ kfac_status kfac_invert(int32_t count, const int32_t* n, const float* const* mat
  * as a full symmetric n x n row-major fp32 matrix (both triangles, e.g. kfac_pack_sym
  * direction 1), inv[m] a full symmetric n x n approximate inverse (e.g. from
  * kfac_invert); both device, caller-owned, not overlapping; inv is updated in place.
- * shift: host array of finite values. Costs two n x n x n products per matrix.
- * Errors: KFAC_ERR_INVALID for bad sizes, NULL, misaligned or aliased pointers and
- * non-finite shifts, KFAC_ERR_WORKSPACE for a missing or short workspace.
+ * shift: host array of finite values. Costs two n x n x n products per matrix. Where
+ * kfac_invert reported a breakdown (info != 0) for a matrix, inv[m] holds no inverse
+ * and the refined result is unspecified too.
+ * Errors: KFAC_ERR_INVALID for bad sizes, NULL or misaligned pointers, an inv buffer
+ * that overlaps any mat or other inv buffer (mat buffers may overlap each other), and
+ * non-finite shifts; KFAC_ERR_UNSUPPORTED for n > 23170 (matrices of 2^31 bytes or
+ * more); KFAC_ERR_WORKSPACE for a missing or short workspace.
  * ------------------------------------------------------------------------- */
 kfac_status kfac_invert_refine_workspace(int32_t count, const int32_t* n, size_t* bytes);
 kfac_status kfac_invert_refine(int32_t count, const int32_t* n, const float* const* mat,
@@ -179,7 +185,8 @@ kfac_status kfac_invert_refine(int32_t count, const int32_t* n, const float* con
  * row-major fp32, as kfac_invert writes them), grad[l] is d_g x d_a row-major
  * (fp16 or fp32 per grad_dtype; with a bias column its last column is the bias
  * gradient), out[l] is d_g x d_a row-major fp32. Computed in fp32 (fp16 gradients
- * are widened exactly). out must not overlap the inputs.
+ * are widened exactly). out must not overlap the inputs. Every operand must span
+ * less than 2^31 bytes (d_g, d_a <= 23170); larger layers give KFAC_ERR_UNSUPPORTED.
  * ------------------------------------------------------------------------- */
 kfac_status kfac_precondition_workspace(int32_t count, const int32_t* d_g, const int32_t* d_a,
                                         size_t* bytes);
@@ -263,7 +270,8 @@ kfac_status kfac_bn_update(const kfac_bn* layers, int32_t count, kfac_dtype in_d
  * names them. Disabled by default; costs nothing when disabled.
  * kfac_timing_only(id) restricts the bracketing to the kernel id (events on every
  * launch cost stream time of their own), id = -1 to every kernel again (the
- * default); ids outside [-1, kfac_timing_kernels()) give KFAC_ERR_INVALID.
+ * default); ids outside [-1, kfac_timing_kernels()) give KFAC_ERR_INVALID. An id
+ * names one role of a kernel (the refinement's products have ids of their own).
  * ------------------------------------------------------------------------- */
 int32_t kfac_timing_kernels(void);
 const char* kfac_kernel_name(int32_t id);

@@ -16,7 +16,7 @@ HEADER = os.path.join(ROOT, "include", "kfac.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:kfac_status|int32_t|const char\s*\*)\s*(kfac_\w+)\s*\(",
+    return sorted(set(re.findall(r"^\s*(?:kfac_status|int32_t|size_t|const char\s*\*)\s*(kfac_\w+)\s*\(",
                                  text, flags=re.M)))
 
 
@@ -213,3 +213,46 @@ def test_invert_refine_validation(lib):
     assert so.kfac_invert_refine(1, one, a, shift, odd, None, 0, None) == -1     # misaligned
     assert so.kfac_invert_refine(1, one, a, nan, b, None, 0, None) == -1         # NaN shift
     assert so.kfac_invert_refine(0, None, None, None, None, None, 0, None) == 0  # no-op
+
+
+def test_refine_rejects_partial_overlaps(lib):
+    """Any byte shared by an inv buffer and a mat or another inv buffer is refused on
+    the host; mat buffers may overlap each other."""
+    so = lib._lib
+    c = ctypes
+    two = (c.c_int32 * 2)(4, 4)            # 64 bytes per matrix
+    shift = (c.c_float * 2)(1e-3, 1e-3)
+
+    def ptrs(*v):
+        return (c.c_void_p * len(v))(*v)
+
+    assert so.kfac_invert_refine(2, two, ptrs(0x1000, 0x2000), shift, ptrs(0x3000, 0x1020), None, 0, None) == -1
+    assert b"overlaps" in so.kfac_last_error()
+    assert so.kfac_invert_refine(2, two, ptrs(0x1000, 0x2000), shift, ptrs(0x2000, 0x3000), None, 0, None) == -1
+    assert so.kfac_invert_refine(2, two, ptrs(0x1000, 0x2000), shift, ptrs(0x3000, 0x3030), None, 0, None) == -1
+    # adjacent (not overlapping) buffers and overlapping mats pass the check; the call
+    # then stops at the device check or the missing workspace, not at the arguments
+    assert so.kfac_invert_refine(2, two, ptrs(0x1000, 0x1020), shift, ptrs(0x3000, 0x3040), None, 0, None) != -1
+
+
+def test_sizes_past_32bit_offsets_are_unsupported(lib):
+    """Input tensors of 2^31 bytes or more (factors) and operands of 2^31 bytes or more
+    (preconditioning, refinement: d > 23170) are refused with KFAC_ERR_UNSUPPORTED."""
+    so = lib._lib
+    c = ctypes
+    sz = c.c_size_t()
+    big_act = synth.Layer("big", 64, 512, 512, 64, 512, 512, 8, 1, 1, 1, 1, 0, 0, 1)   # 2 GiB fp16
+    with pytest.raises(lib.KfacError) as e:
+        lib.kfac_factors_workspace([big_act], lib.KFAC_F16)
+    assert e.value.status == -2
+    ok = synth.Layer("ok", 32, 512, 512, 64, 512, 512, 8, 1, 1, 1, 1, 0, 0, 1)       # 1 GiB fp16
+    assert lib.kfac_factors_workspace([ok], lib.KFAC_F16) > 0
+    with pytest.raises(lib.KfacError):
+        lib.kfac_factors_workspace([ok], lib.KFAC_F32)                                # 2 GiB fp32
+    d = (c.c_int32 * 1)(23171)
+    s = (c.c_int32 * 1)(64)
+    assert so.kfac_precondition_workspace(1, s, d, c.byref(sz)) == -2
+    assert so.kfac_precondition_workspace(1, d, s, c.byref(sz)) == -2
+    assert so.kfac_invert_refine_workspace(1, d, c.byref(sz)) == -2
+    d[0] = 23170
+    assert so.kfac_precondition_workspace(1, s, d, c.byref(sz)) == 0
