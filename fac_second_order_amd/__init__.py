@@ -10,7 +10,7 @@ from ._lib import (  # noqa: F401
     kfac_invert_workspace, kfac_invert_schedule, kfac_invert,
     kfac_invert_refine_workspace, kfac_invert_refine,
     kfac_precondition_workspace, kfac_precondition, kfac_precondition_update, kfac_precondition_ex,
-    kfac_bn_diag_workspace, kfac_bn_diag, kfac_bn_update,
+    kfac_bn_diag_workspace, kfac_bn_diag, kfac_bn_update, kfac_bn_diag_noalloc,
     kfac_timing_kernels, kfac_kernel_name, kfac_timing_enable, kfac_timing_only, kfac_timing_reset,
     kfac_timing_read,
 )

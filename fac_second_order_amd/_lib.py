@@ -82,6 +82,8 @@ _sig("kfac_bn_diag", _i32, _P(kfac_bn), _i32, _i32, _P(_vp), _P(_vp), _P(_vp), _
      _vp, _sz, _vp)
 _sig("kfac_bn_update", _i32, _P(kfac_bn), _i32, _i32, _P(_vp), _P(_vp), _P(_vp), _P(_vp), _P(_vp),
      _f32, _f32, _f32, _vp, _sz, _vp)
+_sig("kfac_bn_diag_noalloc", _i32, _P(kfac_bn), _i32, _i32, _P(_vp), _P(_vp), _P(_vp), _P(_vp), _P(_vp),
+     _f32, _f32, _f32, _vp)
 _sig("kfac_timing_kernels", _i32)
 _sig("kfac_kernel_name", _c.c_char_p, _i32)
 _sig("kfac_timing_enable", _i32, _i32)
@@ -299,6 +301,19 @@ def kfac_bn_update(layers, xhat, gout, fisher, precond, params, lr, ema_decay=0.
     _check(_lib.kfac_bn_update(_bns(layers), len(layers), dt, _ptrs(xhat), _ptrs(gout), _ptrs(fisher),
                                _ptrs(precond), _ptrs(params), float(lr), float(ema_decay), float(shift),
                                ws, wsb, _stream(stream)), "kfac_bn_update")
+
+
+KFAC_BN_NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def kfac_bn_diag_noalloc(layers, xhat, gout, fisher, precond, params=None, lr=0.0, ema_decay=0.0, shift=1e-3,
+                         stream=None):
+    """kfac_bn_diag (params None) or kfac_bn_update (params given) with the library's
+    static scratch instead of a workspace: allocates nothing (see kfac.h)."""
+    dt = _dtype_code(xhat[0])
+    _check(_lib.kfac_bn_diag_noalloc(_bns(layers), len(layers), dt, _ptrs(xhat), _ptrs(gout), _ptrs(fisher),
+                                     _ptrs(precond), None if params is None else _ptrs(params), float(lr),
+                                     float(ema_decay), float(shift), _stream(stream)), "kfac_bn_diag_noalloc")
 
 
 # timing -------------------------------------------------------------------

@@ -11,6 +11,8 @@
 // of each sample in a fixed order (deterministic), squares the per-sample sums,
 // averages over samples, blends with the stored Fisher when asked and divides; with
 // parameters given it also applies the update of eq. (8), gamma/beta -= lr * precond.
+#include <mutex>
+
 #include "common.hpp"
 
 namespace kfac {
@@ -392,6 +394,35 @@ static kfac_status bn_impl(const kfac_bn* layers, int32_t count, kfac_dtype in_d
   return bn_launch(call, 0, count, workspace, ema_decay, shift, static_cast<hipStream_t>(stream));
 }
 
+// ---- the variant that allocates nothing -------------------------------------------
+// Its scratch (tables and partial sums) is this file-scope device array, one copy per
+// GPU, held until the process ends. Its device address is looked up once per device
+// (hipGetSymbolAddress with that device current) and only that address is used from
+// the host. A call whose layers need more than the array holds runs in passes of
+// consecutive layers, each pass reusing the array after the previous pass's kernels
+// (stream order). Every partial sum a finish block reads was written by the partial
+// launch of its own pass, so nothing needs clearing between calls.
+constexpr size_t kBnScratchBytes = KFAC_BN_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kBnScratchBytes];
+
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[64];
+
+static kfac_status scratch_address(void** out) {
+  int dev = 0;
+  KFAC_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= 64) return fail(KFAC_ERR_UNSUPPORTED, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    KFAC_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) return fail(KFAC_ERR_HIP, "hipGetSymbolAddress returned NULL for the BN scratch");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return KFAC_OK;
+}
+
 extern "C" kfac_status kfac_bn_diag(const kfac_bn* layers, int32_t count, kfac_dtype in_dtype,
                                     const void* const* xhat, const void* const* gout,
                                     float* const* fisher, float* const* precond, float ema_decay,
@@ -408,4 +439,33 @@ extern "C" kfac_status kfac_bn_update(const kfac_bn* layers, int32_t count, kfac
   if (count > 0 && !params) return fail(KFAC_ERR_INVALID, "NULL parameter array");
   return bn_impl(layers, count, in_dtype, xhat, gout, fisher, precond, params, lr, ema_decay, shift, workspace,
                  ws_bytes, stream);
+}
+
+extern "C" kfac_status kfac_bn_diag_noalloc(const kfac_bn* layers, int32_t count, kfac_dtype in_dtype,
+                                            const void* const* xhat, const void* const* gout,
+                                            float* const* fisher, float* const* precond, float* const* params,
+                                            float lr, float ema_decay, float shift, void* stream) {
+  BnCall call;
+  kfac_status st = bn_prepare(layers, count, in_dtype, xhat, gout, fisher, precond, params, lr, ema_decay, shift,
+                              call);
+  if (st || count == 0) return st;
+  for (int l = 0; l < count; ++l)
+    if (bn_need(call, l, l + 1) > kBnScratchBytes)
+      return fail(KFAC_ERR_INVALID,
+                  "kfac_bn_diag_noalloc: bn layer %d needs %zu bytes of scratch, more than the %zu of the "
+                  "static buffer (use kfac_bn_diag with a workspace)",
+                  l, bn_need(call, l, l + 1), kBnScratchBytes);
+  st = check_device();
+  if (st) return st;
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws))) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  int l0 = 0;
+  while (l0 < count) {  // the longest run of layers from l0 that fits
+    int l1 = l0 + 1;
+    while (l1 < count && bn_need(call, l0, l1 + 1) <= kBnScratchBytes) ++l1;
+    if ((st = bn_launch(call, l0, l1, ws, ema_decay, shift, s))) return st;
+    l0 = l1;
+  }
+  return KFAC_OK;
 }

@@ -262,6 +262,27 @@ kfac_status kfac_bn_update(const kfac_bn* layers, int32_t count, kfac_dtype in_d
                            size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * kfac_bn_diag_noalloc - kfac_bn_diag (params NULL) or kfac_bn_update (params
+ * given) for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation. There is no
+ * workspace argument and the call allocates nothing: its scratch (descriptor tables
+ * and partial sums) is a static device buffer of KFAC_BN_NOALLOC_SCRATCH_BYTES per
+ * GPU, part of the loaded library and held until the process ends. Layers whose
+ * scratch exceeds the buffer together run in several passes; a single layer that
+ * needs more than the buffer gives KFAC_ERR_INVALID (kfac_bn_diag with a workspace
+ * has no such limit; at 64 channels and 112x112 positions a layer fits up to about
+ * 1200 samples). Every call on a GPU shares that GPU's buffer: calls that overlap in
+ * time on one GPU (other streams, other threads) race and must be ordered by the
+ * caller. Results are bit-identical to kfac_bn_diag / kfac_bn_update on the same
+ * inputs. Other arguments, layouts and errors as for those calls.
+ * ------------------------------------------------------------------------- */
+#define KFAC_BN_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+kfac_status kfac_bn_diag_noalloc(const kfac_bn* layers, int32_t count, kfac_dtype in_dtype,
+                                 const void* const* xhat, const void* const* gout,
+                                 float* const* fisher, float* const* precond, float* const* params,
+                                 float lr, float ema_decay, float shift, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Per-kernel event timing, for measurement. When enabled on a thread, every
  * kernel the library launches from that thread is bracketed by two HIP events on
  * the launch stream. kfac_timing_read synchronises those events and returns, per
