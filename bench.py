@@ -42,7 +42,7 @@ LR = 0.01                # learning rate of the parameter update
 # (FETCH_SIZE, then WRITE_SIZE), calibrated by a plain 1 GiB device copy (fetch x2.0,
 # write x1.0) and summarised in profiles/resnet50_step_hbm_counters.md. Reported only
 # while the kernel's source text still hashes to the value it was measured with.
-MEASURED_TRAFFIC = {"inv_update_kernel": (970451456, "3d5e4963843e59a4a5a228c1bd1c9c537f3130f2")}
+MEASURED_TRAFFIC = {"inv_update_kernel": (970500000, "7b1700f02b5494fea626966eaa089f2725564924")}
 CSRC = os.path.join(ROOT, "fac_second_order_amd", "csrc")
 
 
