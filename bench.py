@@ -163,7 +163,8 @@ def stage_rates(kern, w, precond_accum="f32"):
     pre_peak = PEAK_FP64_MFMA if precond_accum == "f64" else PEAK_FP32_MFMA
     out = {}
     for stage, names, work_, unit, peak in (
-            ("factors", ("syrk_tile_kernel", "syrk_reduce_kernel"), w["syrk_flop"], "TFLOP/s", PEAK_FP16_MFMA),
+            ("factors", ("syrk_tile_kernel", "syrk_reduce_kernel", "shift_assemble_kernel"), w["syrk_flop"], "TFLOP/s",
+             PEAK_FP16_MFMA),
             ("inverse", ("inv_prep_kernel", "inv_pivot_kernel", "inv_panel_kernel",
                          "inv_update_kernel", "inv_finish_kernel"), w["inv_flop"], "TFLOP/s", PEAK_FP32_MFMA),
             ("precondition", ("gemm_tn_kernel", "gemm_tn64_kernel"), w["pre_flop"], "TFLOP/s", pre_peak),

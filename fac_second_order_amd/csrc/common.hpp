@@ -92,6 +92,7 @@ enum KernelId {
   K_REFINE_EW,     // refine_init_kernel and refine_apply_kernel
   K_REFINE_RES,    // gemm_tn64_kernel forming the residual of the refinement
   K_REFINE_CORR,   // gemm_tn_kernel forming the correction of the refinement
+  K_SHIFT_ASM,     // shift_assemble_kernel (3x3 activation factors from shift products)
   K_COUNT
 };
 

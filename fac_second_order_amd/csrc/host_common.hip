@@ -74,18 +74,26 @@ kfac_status upload(void* dst_device, const void* src_host, size_t bytes, hipStre
 }
 
 kfac_status TableUpload::flush(hipStream_t stream) {
-  if (parts_.empty()) return KFAC_OK;
-  char* base = parts_.front().dst;
-  size_t end = 0;
-  for (const Part& q : parts_) {  // tables in carve order, none overlapping the next
-    if (q.dst < base + end) return fail(KFAC_ERR_INVALID, "internal: descriptor tables out of order");
-    end = static_cast<size_t>(q.dst - base) + q.bytes;
+  // tables in carve order, none overlapping the next; runs of tables with gaps of at
+  // most 1 KB between them go up as one image (the gaps written with zeros)
+  for (size_t a = 1; a < parts_.size(); ++a)
+    if (parts_[a].dst < parts_[a - 1].dst + parts_[a - 1].bytes)
+      return fail(KFAC_ERR_INVALID, "internal: descriptor tables out of order");
+  size_t a = 0;
+  while (a < parts_.size()) {
+    size_t b = a + 1;
+    while (b < parts_.size() && parts_[b].dst - (parts_[b - 1].dst + parts_[b - 1].bytes) <= 1024) ++b;
+    char* base = parts_[a].dst;
+    const size_t end = static_cast<size_t>(parts_[b - 1].dst - base) + parts_[b - 1].bytes;
+    if (end % 4 != 0) return fail(KFAC_ERR_INVALID, "internal: table size not a multiple of 4");
+    std::vector<char> image(end, 0);
+    for (size_t q = a; q < b; ++q) std::memcpy(image.data() + (parts_[q].dst - base), parts_[q].src, parts_[q].bytes);
+    kfac_status st = upload(base, image.data(), end, stream);
+    if (st) return st;
+    a = b;
   }
-  if (end % 4 != 0) return fail(KFAC_ERR_INVALID, "internal: table size not a multiple of 4");
-  std::vector<char> image(end, 0);
-  for (const Part& q : parts_) std::memcpy(image.data() + (q.dst - base), q.src, q.bytes);
   parts_.clear();
-  return upload(base, image.data(), end, stream);
+  return KFAC_OK;
 }
 
 // ---- timing ------------------------------------------------------------------
@@ -131,7 +139,8 @@ static const char* const kKernelNames[K_COUNT] = {
     "unpack_kernel",      "inv_prep_kernel",    "inv_pivot_kernel",   "inv_panel_kernel",
     "inv_update_kernel",  "inv_finish_kernel",  "gemm_tn_kernel",     "bn_partial_kernel",
     "bn_finish_kernel",   "gemm_tn64_kernel",   "refine_elementwise_kernels",
-    "refine_residual_gemm_tn64_kernel",         "refine_correction_gemm_tn_kernel"};
+    "refine_residual_gemm_tn64_kernel",         "refine_correction_gemm_tn_kernel",
+    "shift_assemble_kernel"};
 
 }  // namespace kfac
 

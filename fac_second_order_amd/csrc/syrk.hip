@@ -23,6 +23,12 @@
 // triangle. Work items are renumbered so that each of the 8 XCDs runs a contiguous
 // range (tiles of one row split share that XCD's L2).
 //
+// The activation factor of a 3x3 convolution with stride 1 and padding 1 is not
+// formed from its 9C patch columns but from 13 shift products of the C channels
+// (a block-Toeplitz structure, see shift_assemble_kernel): the same work items and
+// tile loop compute them as rectangular C x 13C products, and a last kernel
+// assembles the packed factor, about a third of the multiplications of the patch Gram.
+//
 // fp32 inputs take a plain path (element gathers, v_mfma_f32_32x32x2f32).
 #include <algorithm>
 #include <cmath>
@@ -65,6 +71,17 @@ struct SyrkDesc {
   int32_t nb, nt, splits, rows_per_split;
   float inv_r, r_f;
   double rhw, rwo;  // 1 / (Ho Wo) and 1 / Wo for the row decode
+  // kind 1, a shift product: T[c][t*C + c'] = sum over the rows' pixels p of
+  // x[p][c] * x[p + (tdh[t], tdw[t])][c'] (zero outside the image), raw fp32 sums in
+  // `out` (dense, leading dimension c_col), and the column sums of the row operand
+  // (sum over p of x[p][c]) in csum. The rows are the pixels of an Ho x Wo window at
+  // (-ph, -pw) of every image (mode 1 with stride 1 and a negative padding).
+  int32_t kind;          // 0: a factor (packed upper triangle), 1: a shift product
+  int32_t ntap;          // kind 1: column taps
+  int32_t c_row, c_col;  // kind 1: C and ntap * C
+  int32_t nbr, nbc;      // kind 1: 128-blocks along the rows and the columns of T
+  float* csum;
+  int8_t tdh[16], tdw[16];
 };
 
 // Value of X[row][c] (0 outside the image or beyond d_core), any input dtype
@@ -142,11 +159,27 @@ struct ColTab {
   int32_t kj[8];
 };
 
-__device__ inline void fill_coltab(const SyrkDesc& d, int c0, ColTab& ct) {
+__device__ inline void fill_coltab(const SyrkDesc& d, int op, int c0, ColTab& ct) {
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
     const int c = c0 + q;
-    if (c >= d.d_core) {
+    if (d.kind == 1) {  // op 0: the pixel's own channels; op 1: channel c % C of tap c / C
+      if (c >= (op ? d.c_col : d.c_row)) {
+        ct.coff[q] = 0;
+        ct.ki[q] = kNoRow;
+        ct.kj[q] = 0;
+      } else if (op == 0) {
+        ct.coff[q] = c;
+        ct.ki[q] = 0;
+        ct.kj[q] = 0;
+      } else {
+        const int tap = c / d.C, ci = c - tap * d.C;
+        const int dh = d.tdh[tap], dw = d.tdw[tap];
+        ct.coff[q] = (dh * d.W + dw) * d.C + ci;
+        ct.ki[q] = dh;
+        ct.kj[q] = dw;
+      }
+    } else if (c >= d.d_core) {
       ct.coff[q] = 0;
       ct.ki[q] = kNoRow;
       ct.kj[q] = 0;
@@ -237,11 +270,13 @@ __device__ inline void write_bias_direct(const SyrkDesc& d, int ti, int t, float
 // (row block ti into X0, tj into X1) over chunks of KC rows; a diagonal tile has one
 // operand and stages chunks of 2 KC rows, the first KC in X0 and the rest in X1, so
 // that every thread gathers the same 8 rows x 8 columns in both kinds. VEC: 16-byte
-// buffer-load gathers.
+// buffer-load gathers. want_col: thread tid < 128 adds up column tid of the row
+// operand. mma_on (wave-uniform): this wave's 64x64 quadrant is needed (not the one
+// below a diagonal tile's diagonal, not past the last row of a shift product).
 template <bool DIAG, bool VEC>
 __device__ __forceinline__ void syrk_rows(const SyrkDesc& d, RowTab* tab, _Float16* X0, _Float16* X1,
                                           const ColTab& ct, int r_begin, int r_end, bool want_col,
-                                          v16f (&acc)[2][2], float& colsum) {
+                                          bool mma_on, v16f (&acc)[2][2], float& colsum) {
   constexpr int CK = DIAG ? 2 * KC : KC;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -315,10 +350,20 @@ __device__ __forceinline__ void syrk_rows(const SyrkDesc& d, RowTab* tab, _Float
             for (int q = 0; q < 8; ++q) colsum += static_cast<float>(cv[q]);
           }
       }
-      mma(X0, X0);
-      mma(X1, X1);
+      if (mma_on) {
+        mma(X0, X0);
+        mma(X1, X1);
+      }
     } else {
-      mma(X0, X1);
+      if (want_col) {  // the KC rows of column tid of the row operand, in swizzled order
+#pragma unroll
+        for (int k = 0; k < KC; k += 8) {
+          v8h cv = *reinterpret_cast<const v8h*>(X0 + tid * LDK + k);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) colsum += static_cast<float>(cv[q]);
+        }
+      }
+      if (mma_on) mma(X0, X1);
     }
   }
 }
@@ -332,9 +377,15 @@ __global__ void __launch_bounds__(256) syrk_f16_kernel(const SyrkDesc* __restric
   const SyrkDesc& d = desc[p];
   const int local = v - begin[p];
   const int t = local % d.nt, s = local / d.nt;
+  const bool shp = d.kind == 1;  // a shift product: a rectangular grid of tiles
   int ti, tj;
-  upper_tile(t, d.nb, ti, tj);
-  const bool diag = ti == tj;
+  if (shp) {
+    ti = t % d.nbr;
+    tj = t / d.nbr;
+  } else {
+    upper_tile(t, d.nb, ti, tj);
+  }
+  const bool diag = !shp && ti == tj;
 
   __shared__ __attribute__((aligned(16))) _Float16 lds[2][ST * LDK];
   __shared__ RowTab tab[2];
@@ -342,12 +393,15 @@ __global__ void __launch_bounds__(256) syrk_f16_kernel(const SyrkDesc* __restric
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const bool skip = diag && wm > wn;  // quadrant strictly below the diagonal
+  // rows of a shift product past C (C = 64: the lower half of the tile)
+  const bool idle = shp && ti * ST + wm * 64 >= d.c_row;
   ColTab ct;  // the 8 columns this thread stages: of row block tj in threads 128.. of an
               // off-diagonal tile, else of row block ti
-  fill_coltab(d, ((tid >> 7) ? tj : ti) * ST + (tid & 15) * 8, ct);
+  const int op = diag ? 0 : (tid >> 7);
+  fill_coltab(d, op, (op ? tj : ti) * ST + (tid & 15) * 8, ct);
   const int r_begin = s * d.rows_per_split;
   const int r_end = min(d.R, r_begin + d.rows_per_split);
-  const bool want_col = diag && d.bias && tid < ST;
+  const bool want_col = tid < ST && (shp ? tj == 0 : diag && d.bias);
 
   v16f acc[2][2];
 #pragma unroll
@@ -357,35 +411,52 @@ __global__ void __launch_bounds__(256) syrk_f16_kernel(const SyrkDesc* __restric
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
   float colsum = 0.f;
+  const bool mma_on = !skip && !idle;
   // block-uniform specialisations of the main loop
   if (diag) {
-    if (d.vec) syrk_rows<true, true>(d, tab, lds[0], lds[1], ct, r_begin, r_end, want_col, acc, colsum);
-    else syrk_rows<true, false>(d, tab, lds[0], lds[1], ct, r_begin, r_end, want_col, acc, colsum);
+    if (d.vec) syrk_rows<true, true>(d, tab, lds[0], lds[1], ct, r_begin, r_end, want_col, mma_on, acc, colsum);
+    else syrk_rows<true, false>(d, tab, lds[0], lds[1], ct, r_begin, r_end, want_col, mma_on, acc, colsum);
   } else {
-    if (d.vec) syrk_rows<false, true>(d, tab, lds[0], lds[1], ct, r_begin, r_end, want_col, acc, colsum);
-    else syrk_rows<false, false>(d, tab, lds[0], lds[1], ct, r_begin, r_end, want_col, acc, colsum);
+    if (d.vec) syrk_rows<false, true>(d, tab, lds[0], lds[1], ct, r_begin, r_end, want_col, mma_on, acc, colsum);
+    else syrk_rows<false, false>(d, tab, lds[0], lds[1], ct, r_begin, r_end, want_col, mma_on, acc, colsum);
   }
 
   if (d.splits == 1) {
-    if (!skip) {
+    if (shp) {  // raw sums into T, rows < C, columns < ntap * C
+      if (!idle) {
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
+        for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+          for (int b = 0; b < 2; ++b)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int i = ti * ST + wm * 64 + a * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-            const int j = tj * ST + wn * 64 + b * 32 + (lane & 31);
-            if (i <= j && j < d.d_core) {
-              const int64_t o = packed_off(i, j, d.d);
-              gp(d.out)[o] = blend(acc[a][b][e] * d.inv_r, d.out, o, decay);
+            for (int e = 0; e < 16; ++e) {
+              const int i = ti * ST + wm * 64 + a * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+              const int j = tj * ST + wn * 64 + b * 32 + (lane & 31);
+              if (i < d.c_row && j < d.c_col) gp(d.out)[int64_t(i) * d.c_col + j] = acc[a][b][e];
             }
-          }
+      }
+      if (want_col && ti * ST + tid < d.c_row) gp(d.csum)[ti * ST + tid] = colsum;
+    } else {
+      if (!skip) {
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+          for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int i = ti * ST + wm * 64 + a * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+              const int j = tj * ST + wn * 64 + b * 32 + (lane & 31);
+              if (i <= j && j < d.d_core) {
+                const int64_t o = packed_off(i, j, d.d);
+                gp(d.out)[o] = blend(acc[a][b][e] * d.inv_r, d.out, o, decay);
+              }
+            }
+      }
+      if (diag && d.bias) write_bias_direct(d, ti, t, colsum, decay);
     }
-    if (diag && d.bias) write_bias_direct(d, ti, t, colsum, decay);
   } else {
     float* P = d.partial + (int64_t(s) * d.nt + t) * (ST * ST);
-    if (!skip) {
+    if (!skip && !idle) {
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -499,9 +570,39 @@ __global__ void __launch_bounds__(256) syrk_reduce_kernel(const SyrkDesc* __rest
   const SyrkDesc& d = desc[rprob[q]];
   const int local = blockIdx.x - rbegin[q];
   const int t = local / RED_PARTS, part = local % RED_PARTS;
+  if (d.kind == 1) {  // a shift product: dense raw sums, and the row operand's column sums
+    const int ti = t % d.nbr, tj = t / d.nbr;
+    const int64_t tstride = int64_t(d.nt) * ST * ST;
+    const int e0 = part * 1024 + threadIdx.x * 4;
+    const int i = ti * ST + e0 / ST, j0 = tj * ST + e0 % ST;
+    if (i < d.c_row && j0 < d.c_col) {
+      const KG float* P = gp(d.partial) + int64_t(t) * ST * ST + e0;
+      v4f sum = {0.f, 0.f, 0.f, 0.f};
+      constexpr int U = 8;
+      int s = 0;
+      for (; s + U <= d.splits; s += U) {
+        v4f x[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) x[u] = *reinterpret_cast<const KG v4f*>(P + (s + u) * tstride);
+#pragma unroll
+        for (int u = 0; u < U; ++u) sum += x[u];
+      }
+      for (; s < d.splits; ++s) sum += *reinterpret_cast<const KG v4f*>(P + s * tstride);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (j0 + u < d.c_col) gp(d.out)[int64_t(i) * d.c_col + j0 + u] = sum[u];
+    }
+    if (part == 0 && tj == 0 && threadIdx.x < ST && ti * ST + int(threadIdx.x) < d.c_row) {
+      const KG float* pc = gp(d.pcol) + int64_t(ti) * ST + threadIdx.x;
+      const int64_t sstride = int64_t(d.nb) * ST;
+      float sum = 0.f;
+      for (int s = 0; s < d.splits; ++s) sum += pc[s * sstride];
+      gp(d.csum)[ti * ST + threadIdx.x] = sum;
+    }
+    return;
+  }
   int ti, tj;
-  upper_tile(t, d.nb, ti, tj);
-  const int64_t tstride = int64_t(d.nt) * ST * ST;
+  upper_tile(t, d.nb, ti, tj);  const int64_t tstride = int64_t(d.nt) * ST * ST;
   const int e0 = part * 1024 + threadIdx.x * 4;
   const int i = ti * ST + e0 / ST, j0 = tj * ST + e0 % ST;
   if (i < d.d_core && j0 + 3 >= i && j0 < d.d_core) {
@@ -555,6 +656,123 @@ __global__ void __launch_bounds__(256) syrk_reduce_kernel(const SyrkDesc* __rest
   if (t == 0 && part == 0 && d.bias && threadIdx.x == 0) {
     const int64_t o = packed_off(d.d_core, d.d_core, d.d);
     gp(d.out)[o] = blend(d.r_f * d.inv_r, d.out, o, decay);
+  }
+}
+
+// ---- 3x3 activation factors from shift products ---------------------------------
+// For a 3x3 convolution with stride 1 and zero padding 1, column t*C + c of the patch
+// matrix is channel c of the pixel o + (i-1, j-1) for tap t = 3i + j and output
+// position o. Block (t1, t2) of A sums x[u][c1] x[u + delta][c2], delta = tap t2's offset
+// minus tap t1's, over the pixels u that tap t1 sees: all pixels u with u + delta inside
+// the image, except that tap row i1 = 0 never sees the last image row and i1 = 2 never
+// the first (the same for the columns). With the full-image shift product
+//   T_delta[c1][c2] = sum over all pixels u of x[u][c1] x[u + delta][c2]
+// (zero outside the image), a block is therefore T_delta minus a one-row strip when
+// delta_h = 0 and i1 != 1, minus a one-column strip when delta_w = 0 and j1 != 1, plus
+// the corner pixel where both were taken off. With t1 <= t2, delta is one of 13 offsets
+// (delta_h = 0, delta_w = 0..2; delta_h = 1, 2, delta_w = -2..2), so A's upper triangle
+// needs 13 C x C products over all rows instead of 45 blocks, plus strips over one
+// image row or column: about three times fewer multiplications. The bias column is the
+// column sum over the pixels each tap sees, formed the same way.
+// Per layer the workspace region holds (floats): T [C][13C]; row strips [2][C][3C]
+// (top, bottom; taps (0,0), (0,1), (0,2)); column strips [2][C][3C] (left, right; taps
+// (0,0), (1,0), (2,0)); corners [4][C][C] (top-left, top-right, bottom-left,
+// bottom-right); column sums [9][C] (all pixels, the two row strips, the two column
+// strips, the four corners).
+constexpr int kShiftTaps = 13;
+__host__ __device__ inline int64_t sr_rows(int C) { return int64_t(13) * C * C; }           // row strips
+__host__ __device__ inline int64_t sr_cols(int C) { return int64_t(19) * C * C; }           // column strips
+__host__ __device__ inline int64_t sr_corners(int C) { return int64_t(25) * C * C; }
+__host__ __device__ inline int64_t sr_sums(int C) { return int64_t(29) * C * C; }
+__host__ __device__ inline int64_t sr_floats(int C) { return int64_t(29) * C * C + 9 * C; }
+__host__ __device__ inline int tap_index(int dh, int dw) { return dh == 0 ? dw : 3 + (dh - 1) * 5 + (dw + 2); }
+
+struct ShiftAsm {
+  const float* base;  // the layer's region
+  float* out;         // packed A
+  int32_t C, d, bias, pad_;
+  float inv_r, r_f;
+};
+
+// One block per channel c1 of a job (blocks of all jobs numbered by offsets `begin`):
+// the nine packed rows i = t1*C + c1 of A (t1 = 0..8), which all read row c1 of T and
+// of the strips (cache hits after the first), block 0 also the bias corner. Each
+// thread forms four entries of a row with their loads in flight before the stores;
+// every entry as above times fp32(1/R), blended with the stored factor when decay != 0.
+__global__ void __launch_bounds__(256) shift_assemble_kernel(const ShiftAsm* __restrict__ jobs,
+                                                             const int32_t* __restrict__ begin, int count,
+                                                             float decay) {
+  const int q = find_problem(begin, count, blockIdx.x);
+  const ShiftAsm& a = jobs[q];
+  const int c1 = blockIdx.x - begin[q];
+  const int C = a.C, d = a.d, tid = threadIdx.x;
+  const int64_t C3 = int64_t(3) * C;
+  // the region is only read and the factor only written here: restrict lets every
+  // entry's loads issue before the previous entries' stores
+  const KG float* __restrict__ T = gp(a.base) + int64_t(c1) * (kShiftTaps * C);
+  const KG float* __restrict__ Su = gp(a.base) + sr_sums(C);
+  const KG float* __restrict__ R0 = gp(a.base) + sr_rows(C) + int64_t(c1) * C3;    // + hs*3C^2 + dw*C + c2
+  const KG float* __restrict__ C0 = gp(a.base) + sr_cols(C) + int64_t(c1) * C3;    // + ws*3C^2 + dh*C + c2
+  const KG float* __restrict__ X0 = gp(a.base) + sr_corners(C) + int64_t(c1) * C;  // + (2hs+ws)*C^2 + c2
+  const int64_t cc = int64_t(C) * C;
+  // j / C by a shift when C is a power of two (block-uniform choice)
+  const bool pow2 = (C & (C - 1)) == 0;
+  const int lg = 31 - __builtin_clz(static_cast<unsigned>(C));
+  auto put = [&](KG float* o, float v) {
+    const float x = v * a.inv_r;
+    *o = decay != 0.f ? decay * *o + (1.f - decay) * x : x;
+  };
+  if (a.bias && c1 == 0 && tid == 0) put(gp(a.out) + packed_off(d - 1, d - 1, d), a.r_f);
+  for (int t1 = 0; t1 < 9; ++t1) {
+    const int i = t1 * C + c1, i1 = t1 / 3, j1 = t1 - 3 * i1;
+    const int hs = i1 == 0 ? 1 : 0, ws = j1 == 0 ? 1 : 0;  // strips left out: bottom/top, right/left
+    KG float* __restrict__ orow = gp(a.out) + packed_off(i, i, d) - i;  // orow[j] for j >= i
+    float bias_v = 0.f;
+    if (a.bias) {  // the bias column: sum over the pixels tap t1 sees
+      bias_v = Su[c1];
+      if (i1 != 1) bias_v -= Su[(1 + hs) * C + c1];
+      if (j1 != 1) bias_v -= Su[(3 + ws) * C + c1];
+      if (i1 != 1 && j1 != 1) bias_v += Su[(5 + 2 * hs + ws) * C + c1];
+    }
+    constexpr int U = 8;  // entries per thread in flight
+    for (int j0 = i + tid; j0 < d; j0 += 256 * U) {
+      // branch-free: every entry issues its four loads (T, row strip, column strip,
+      // corner; an in-range stand-in where a term does not apply) before any is used
+      float xt[U], xr[U], xc[U], xx[U];
+      bool fr[U], fc[U], fx[U], fb[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int j = min(j0 + 256 * u, d - 1);
+        fb[u] = a.bias && j == d - 1;
+        const int jj = fb[u] ? i : j;  // the bias column reads a stand-in
+        const int t2 = pow2 ? (jj >> lg) : jj / C, c2 = jj - t2 * C, i2 = t2 / 3, j2 = t2 - 3 * i2;
+        const int dh = i2 - i1, dw = j2 - j1;
+        fr[u] = dh == 0 && i1 != 1;
+        fc[u] = dw == 0 && j1 != 1;
+        fx[u] = fr[u] && fc[u];
+        xt[u] = T[tap_index(dh, dw) * C + c2];
+        xr[u] = R0[fr[u] ? hs * C3 * C + dw * C + c2 : c2];
+        xc[u] = C0[fc[u] ? ws * C3 * C + dh * C + c2 : c2];
+        xx[u] = X0[fx[u] ? (2 * hs + ws) * cc + c2 : c2];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float x = xt[u];
+        if (fr[u]) x -= xr[u];
+        if (fc[u]) x -= xc[u];
+        if (fx[u]) x += xx[u];
+        xt[u] = fb[u] ? bias_v : x;
+      }
+      if (decay == 0.f) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (j0 + 256 * u < d) orow[j0 + 256 * u] = xt[u] * a.inv_r;
+      } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (j0 + 256 * u < d) put(orow + j0 + 256 * u, xt[u]);
+      }
+    }
   }
 }
 
@@ -617,7 +835,81 @@ struct SyrkPlan {
   size_t partial_floats = 0;
   XcdSegs segs{};
   int64_t seg_max = 0;               // longest XCD segment (items)
+  // 3x3 activation factors formed from shift products: one assembly job per layer,
+  // its region (sr_floats(C) floats) carved at launch; problem p of kind 1 belongs to
+  // job shift_job[p] as sub-problem shift_sub[p]
+  std::vector<ShiftAsm> jobs;
+  std::vector<int32_t> jbegin;       // assembly tiles
+  std::vector<int32_t> shift_job, shift_sub;
+  int64_t jtiles = 0;
+  size_t shift_floats = 0;
 };
+
+// Whether layer L's activation factor is formed from shift products: fp16 inputs, a
+// 3x3 kernel with stride 1 and padding 1, channels in groups of 8.
+static bool shift_eligible(const kfac_layer& L, kfac_dtype dt) {
+  return dt == KFAC_F16 && L.kh == 3 && L.kw == 3 && L.sh == 1 && L.sw == 1 && L.ph == 1 && L.pw == 1 &&
+         L.c_in % 8 == 0 && L.h_out == L.h && L.w_out == L.w && int64_t(L.c_in) * kShiftTaps <= 65536;
+}
+
+// Sub-problem `sub` of the shift products of a 3x3 layer: 0 the full image (13 taps),
+// 1/2 the top/bottom row, 3/4 the left/right column (3 taps each), 5..8 the corners
+// top-left, top-right, bottom-left, bottom-right (1 tap). Its rows are the pixels of
+// the window, in mode-1 form: stride 1, padding minus the window's origin.
+static SyrkDesc make_shift(const kfac_layer& L, int sub) {
+  static const int8_t full_dh[kShiftTaps] = {0, 0, 0, 1, 1, 1, 1, 1, 2, 2, 2, 2, 2};
+  static const int8_t full_dw[kShiftTaps] = {0, 1, 2, -2, -1, 0, 1, 2, -2, -1, 0, 1, 2};
+  SyrkDesc d{};
+  d.kind = 1;
+  d.mode = 1;
+  d.H = L.h; d.W = L.w; d.C = L.c_in;
+  int oh0 = 0, ow0 = 0, ho = L.h, wo = L.w;
+  if (sub == 0) {
+    d.ntap = kShiftTaps;
+    for (int t = 0; t < kShiftTaps; ++t) { d.tdh[t] = full_dh[t]; d.tdw[t] = full_dw[t]; }
+  } else if (sub <= 2) {           // row strip
+    oh0 = sub == 1 ? 0 : L.h - 1;
+    ho = 1;
+    d.ntap = 3;
+    for (int t = 0; t < 3; ++t) { d.tdh[t] = 0; d.tdw[t] = static_cast<int8_t>(t); }
+  } else if (sub <= 4) {           // column strip
+    ow0 = sub == 3 ? 0 : L.w - 1;
+    wo = 1;
+    d.ntap = 3;
+    for (int t = 0; t < 3; ++t) { d.tdh[t] = static_cast<int8_t>(t); d.tdw[t] = 0; }
+  } else {                         // corner
+    const int k = sub - 5;
+    oh0 = (k >> 1) ? L.h - 1 : 0;
+    ow0 = (k & 1) ? L.w - 1 : 0;
+    ho = wo = 1;
+    d.ntap = 1;
+  }
+  d.Ho = ho; d.Wo = wo;
+  d.sh = d.sw = 1; d.kh = d.kw = 1;
+  d.ph = -oh0; d.pw = -ow0;
+  d.R = L.n * ho * wo;
+  d.rhw = 1.0 / static_cast<double>(int64_t(ho) * wo);
+  d.rwo = 1.0 / static_cast<double>(wo);
+  d.c_row = L.c_in;
+  d.c_col = d.ntap * L.c_in;
+  d.d_core = d.c_col;
+  d.d = d.c_col;
+  d.nbr = (d.c_row + ST - 1) / ST;
+  d.nbc = (d.c_col + ST - 1) / ST;
+  d.nb = d.nbr;
+  d.nt = d.nbr * d.nbc;
+  return d;
+}
+
+// Where sub-problem `sub` writes in a region: (products, column sums), offsets in floats.
+static void shift_out(int C, int sub, int64_t& prod, int64_t& sums) {
+  const int64_t c2 = int64_t(C) * C;
+  if (sub == 0) prod = 0;
+  else if (sub <= 2) prod = sr_rows(C) + (sub - 1) * 3 * c2;
+  else if (sub <= 4) prod = sr_cols(C) + (sub - 3) * 3 * c2;
+  else prod = sr_corners(C) + (sub - 5) * c2;
+  sums = sr_sums(C) + int64_t(sub) * C;
+}
 
 // One factor problem from a layer (which = 0: A, 1: G).
 static SyrkDesc make_problem(const kfac_layer& L, int which) {
@@ -701,10 +993,11 @@ static void finish_plan(SyrkPlan& pl) {
 }
 
 static size_t syrk_ws_bytes(const SyrkPlan& pl) {
-  const size_t np = pl.desc.size(), nr = pl.rprob.size();
+  const size_t np = pl.desc.size(), nr = pl.rprob.size(), nj = pl.jobs.size();
   return align256(sizeof(SyrkDesc) * np) + align256(sizeof(int32_t) * np) +
          2 * align256(sizeof(int32_t) * (nr ? nr : 1)) + align256(sizeof(float) * pl.partial_floats) +
-         pl.im2row_bytes;
+         pl.im2row_bytes + align256(sizeof(ShiftAsm) * (nj ? nj : 1)) + align256(sizeof(int32_t) * (nj ? nj : 1)) +
+         sizeof(float) * pl.shift_floats;
 }
 
 }  // namespace kfac
@@ -736,16 +1029,25 @@ static kfac_status layers_validate(const kfac_layer* L, int32_t count, kfac_dtyp
   return KFAC_OK;
 }
 
-// Problems in call order: A of layer l, then G of layer l. Row splits are planned
-// over all 2*count factors (so the workspace query bounds every call); factors whose
-// input pointer is NULL are then dropped.
+// Problems in call order: A of layer l (or its nine shift products), then G of layer
+// l. Row splits are planned over all factors (so the workspace query bounds every
+// call); factors whose input pointer is NULL are then dropped.
 static kfac_status build_plan(const kfac_layer* L, int32_t count, kfac_dtype dt, const void* const* act,
                               const void* const* gout, float* const* A, float* const* G, SyrkPlan& pl) {
   const int esize = dt == KFAC_F16 ? 2 : 4;
   std::vector<SyrkDesc> all;
-  std::vector<Im2Row> geo;  // conv geometry of the problems converted to rows (by index in all)
+  std::vector<Im2Row> geo;            // conv geometry of the problems converted to rows (by index in all)
+  std::vector<int32_t> owner, which_of, sub_of;  // layer, factor (0 A, 1 G), shift sub-problem (-1: none)
   for (int l = 0; l < count; ++l)
     for (int which = 0; which < 2; ++which) {
+      if (which == 0 && shift_eligible(L[l], dt)) {
+        for (int sub = 0; sub < 9; ++sub) {
+          all.push_back(make_shift(L[l], sub));
+          geo.push_back(Im2Row{});
+          owner.push_back(l); which_of.push_back(0); sub_of.push_back(sub);
+        }
+        continue;
+      }
       SyrkDesc d = make_problem(L[l], which);
       Im2Row g{};
       if (dt == KFAC_F16 && d.mode == 1 && d.C % 8 != 0) {
@@ -758,46 +1060,64 @@ static kfac_status build_plan(const kfac_layer* L, int32_t count, kfac_dtype dt,
       }
       all.push_back(d);
       geo.push_back(g);
+      owner.push_back(l); which_of.push_back(which); sub_of.push_back(-1);
     }
   plan_splits(all, dt);
-  for (int l = 0; l < count; ++l) {
-    for (int which = 0; which < 2; ++which) {
-      SyrkDesc d = all[2 * l + which];
-      if (act) {
-        const void* src = which == 0 ? act[l] : gout[l];
-        if (!src) continue;
-        float* out = which == 0 ? A[l] : G[l];
-        if (!out) return fail(KFAC_ERR_INVALID, "layer %d: output for factor %d is NULL", l, which);
-        if (reinterpret_cast<uintptr_t>(src) % esize || reinterpret_cast<uintptr_t>(out) % 4)
-          return fail(KFAC_ERR_INVALID, "layer %d: misaligned pointer", l);
-        d.src = src;
-        d.out = out;
-        const int width = d.mode == 1 ? d.C : d.ld;
-        const int64_t bytes = d.mode == 1 ? int64_t(L[l].n) * d.H * d.W * d.C * esize
-                                          : int64_t(d.R) * d.ld * esize;
-        d.vec = (dt == KFAC_F16 && width % 8 == 0 &&
-                 (d.padded || (d.d_core % 8 == 0 && reinterpret_cast<uintptr_t>(src) % 16 == 0))) ? 1 : 0;
-        d.nbytes = d.vec ? static_cast<int32_t>(bytes) : 0;
-      }
-      if (d.padded) {
-        const int64_t pb = int64_t(d.R) * d.ld * 2;
-        if (pb < (int64_t(1) << 31)) {  // rows in the workspace, read with 16-byte loads
-          Im2Row g = geo[2 * l + which];
-          g.src = static_cast<const _Float16*>(d.src);
-          pl.im2row.push_back(g);
-          d.padded = static_cast<int32_t>(pl.im2row.size());
-          pl.im2row_bytes += align256(static_cast<size_t>(pb));
-        } else {  // too large for one buffer range: element gathers from the NHWC tensor
-          SyrkDesc c = make_problem(L[l], which);
-          c.splits = d.splits;
-          c.rows_per_split = d.rows_per_split;
-          c.src = d.src;
-          c.out = d.out;
-          d = c;
-        }
-      }
-      pl.desc.push_back(d);
+  std::vector<int32_t> job_of_layer(count, -1);
+  for (size_t q = 0; q < all.size(); ++q) {
+    const int l = owner[q], which = which_of[q], sub = sub_of[q];
+    SyrkDesc d = all[q];
+    if (act) {
+      const void* src = which == 0 ? act[l] : gout[l];
+      if (!src) continue;
+      float* out = which == 0 ? A[l] : G[l];
+      if (!out) return fail(KFAC_ERR_INVALID, "layer %d: output for factor %d is NULL", l, which);
+      if (reinterpret_cast<uintptr_t>(src) % esize || reinterpret_cast<uintptr_t>(out) % 4)
+        return fail(KFAC_ERR_INVALID, "layer %d: misaligned pointer", l);
+      d.src = src;
+      d.out = out;  // shift products: replaced by the region at launch
+      const int width = d.mode == 1 ? d.C : d.ld;
+      const int64_t bytes = d.mode == 1 ? int64_t(L[l].n) * d.H * d.W * d.C * esize
+                                        : int64_t(d.R) * d.ld * esize;
+      d.vec = (dt == KFAC_F16 && width % 8 == 0 &&
+               (d.padded || (d.d_core % 8 == 0 && reinterpret_cast<uintptr_t>(src) % 16 == 0))) ? 1 : 0;
+      d.nbytes = d.vec ? static_cast<int32_t>(bytes) : 0;
     }
+    if (sub >= 0 && sub_of[q] == 0) {  // the layer's assembly job (first sub-problem)
+      job_of_layer[l] = static_cast<int32_t>(pl.jobs.size());
+      ShiftAsm j{};
+      j.out = act ? A[l] : nullptr;
+      j.C = L[l].c_in;
+      j.bias = L[l].bias ? 1 : 0;
+      j.d = 9 * j.C + j.bias;
+      const int64_t rows = int64_t(L[l].n) * L[l].h_out * L[l].w_out;
+      j.inv_r = 1.0f / static_cast<float>(rows);
+      j.r_f = static_cast<float>(rows);
+      pl.jobs.push_back(j);
+      pl.jbegin.push_back(static_cast<int32_t>(pl.jtiles));
+      pl.jtiles += j.C;  // one assembly block per channel
+      pl.shift_floats += align256(sizeof(float) * sr_floats(j.C)) / sizeof(float);
+    }
+    if (d.padded) {
+      const int64_t pb = int64_t(d.R) * d.ld * 2;
+      if (pb < (int64_t(1) << 31)) {  // rows in the workspace, read with 16-byte loads
+        Im2Row g = geo[q];
+        g.src = static_cast<const _Float16*>(d.src);
+        pl.im2row.push_back(g);
+        d.padded = static_cast<int32_t>(pl.im2row.size());
+        pl.im2row_bytes += align256(static_cast<size_t>(pb));
+      } else {  // too large for one buffer range: element gathers from the NHWC tensor
+        SyrkDesc c = make_problem(L[l], which);
+        c.splits = d.splits;
+        c.rows_per_split = d.rows_per_split;
+        c.src = d.src;
+        c.out = d.out;
+        d = c;
+      }
+    }
+    pl.desc.push_back(d);
+    pl.shift_job.push_back(sub >= 0 ? job_of_layer[l] : -1);
+    pl.shift_sub.push_back(sub);
   }
   // Problems in decreasing cost per item (stable): each problem's items stay together
   // (its tiles over one row range are neighbours, sharing those rows in L2), and each
@@ -805,13 +1125,27 @@ static kfac_status build_plan(const kfac_layer* L, int32_t count, kfac_dtype dt,
   auto item_cost = [&](const SyrkDesc& d) {  // per-row cost as in row_cost, now that vec is known
     return double(d.rows_per_split) * ((dt == KFAC_F16 && d.vec) ? 1.0 : 4.0);
   };
-  std::stable_sort(pl.desc.begin(), pl.desc.end(),
-                   [&](const SyrkDesc& a, const SyrkDesc& b) { return item_cost(a) > item_cost(b); });
+  std::vector<int> order(pl.desc.size());
+  for (size_t q = 0; q < order.size(); ++q) order[q] = static_cast<int>(q);
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int a, int b) { return item_cost(pl.desc[a]) > item_cost(pl.desc[b]); });
+  {
+    std::vector<SyrkDesc> ds(order.size());
+    std::vector<int32_t> sj(order.size()), ss(order.size());
+    for (size_t q = 0; q < order.size(); ++q) {
+      ds[q] = pl.desc[order[q]];
+      sj[q] = pl.shift_job[order[q]];
+      ss[q] = pl.shift_sub[order[q]];
+    }
+    pl.desc.swap(ds);
+    pl.shift_job.swap(sj);
+    pl.shift_sub.swap(ss);
+  }
   pl.im2row_prob.assign(pl.im2row.size(), 0);
   for (size_t p = 0; p < pl.desc.size(); ++p)
     if (pl.desc[p].padded) pl.im2row_prob[pl.desc[p].padded - 1] = static_cast<int32_t>(p);
   finish_plan(pl);
-  if (pl.items >= (int64_t(1) << 31) - 8 || pl.ritems >= (int64_t(1) << 31))
+  if (pl.items >= (int64_t(1) << 31) - 8 || pl.ritems >= (int64_t(1) << 31) || pl.jtiles >= (int64_t(1) << 31))
     return fail(KFAC_ERR_INVALID, "too many tiles");
   // XCD segments of about equal cost (rows x per-row cost over the items in order)
   double total = 0;
@@ -890,19 +1224,38 @@ extern "C" kfac_status kfac_factors(const kfac_layer* layers, int32_t count, kfa
   int32_t* d_begin = cv.take<int32_t>(np);
   int32_t* d_rbegin = cv.take<int32_t>(nr ? nr : 1);
   int32_t* d_rprob = cv.take<int32_t>(nr ? nr : 1);
+  const int nj = static_cast<int>(pl.jobs.size());
+  ShiftAsm* d_jobs = cv.take<ShiftAsm>(nj ? nj : 1);  // tables first: they go up as one image
+  int32_t* d_jbegin = cv.take<int32_t>(nj ? nj : 1);
   float* part = cv.take<float>(pl.partial_floats);
   for (size_t q = 0; q < pl.im2row.size(); ++q) {
     Im2Row& g = pl.im2row[q];
     g.dst = cv.take<_Float16>(size_t(g.R) * g.ld);
     pl.desc[pl.im2row_prob[q]].src = g.dst;
   }
+  float* regions = cv.take<float>(pl.shift_floats);
+  {
+    size_t roff = 0;
+    for (ShiftAsm& j : pl.jobs) {
+      j.base = regions + roff;
+      roff += align256(sizeof(float) * sr_floats(j.C)) / sizeof(float);
+    }
+  }
   size_t off = 0;
-  for (auto& d : pl.desc) {
+  for (size_t q = 0; q < pl.desc.size(); ++q) {
+    SyrkDesc& d = pl.desc[q];
     if (d.splits > 1) {
       d.partial = part + off;
       off += size_t(d.splits) * d.nt * ST * ST;
       d.pcol = part + off;
       off += size_t(d.splits) * d.nb * ST;
+    }
+    if (pl.shift_job[q] >= 0) {  // a shift product writes into its layer's region
+      const ShiftAsm& j = pl.jobs[pl.shift_job[q]];
+      int64_t prod = 0, sums = 0;
+      shift_out(j.C, pl.shift_sub[q], prod, sums);
+      d.out = const_cast<float*>(j.base) + prod;
+      d.csum = const_cast<float*>(j.base) + sums;
     }
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -912,6 +1265,10 @@ extern "C" kfac_status kfac_factors(const kfac_layer* layers, int32_t count, kfa
   if (nr) {
     tu.add(d_rbegin, pl.rbegin.data(), sizeof(int32_t) * nr);
     tu.add(d_rprob, pl.rprob.data(), sizeof(int32_t) * nr);
+  }
+  if (nj) {
+    tu.add(d_jobs, pl.jobs.data(), sizeof(ShiftAsm) * nj);
+    tu.add(d_jbegin, pl.jbegin.data(), sizeof(int32_t) * nj);
   }
   if ((st = tu.flush(s))) return st;
   for (const Im2Row& g : pl.im2row) {
@@ -930,6 +1287,11 @@ extern "C" kfac_status kfac_factors(const kfac_layer* layers, int32_t count, kfa
     KFAC_LAUNCH(K_SYRK_REDUCE, syrk_reduce_kernel, dim3(static_cast<unsigned>(pl.ritems)), dim3(256), 0, s,
                 d_desc, d_rbegin, d_rprob, nr, ema_decay);
     KFAC_CHECK_LAUNCH("syrk_reduce_kernel");
+  }
+  if (nj) {
+    KFAC_LAUNCH(K_SHIFT_ASM, shift_assemble_kernel, dim3(static_cast<unsigned>(pl.jtiles)), dim3(256), 0, s,
+                d_jobs, d_jbegin, nj, ema_decay);
+    KFAC_CHECK_LAUNCH("shift_assemble_kernel");
   }
   return KFAC_OK;
 }

@@ -159,6 +159,11 @@ def resnet_step(kfac_gpu):
     say("ResNet-50 step at batch 32 (factors, unpack, 108 inverses, precondition, 53 BN)")
     st.step(dev_in["act"], dev_in["gout"], dev_in["grad"], dev_in["xhat"], dev_in["bgout"])
     torch.cuda.synchronize()
+    info = host(st.info).tolist()
+    bad = {name: [i for i, t in enumerate(ts) if not bool(torch.isfinite(t).all())]
+           for name, ts in (("A", st.A_packed), ("G", st.G_packed), ("inverse", st.full), ("P", st.out))}
+    say("  info", [(i, x) for i, x in enumerate(info) if x], "non-finite", bad)
+    assert not any(info) and not any(bad.values()), (info, bad)
     return L, B, st, host_in
 
 

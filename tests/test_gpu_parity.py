@@ -198,6 +198,30 @@ def test_factors_integer_inputs_bitexact(kfac_gpu):
             assert np.array_equal(host(got), expect), layer.name
 
 
+SHIFT_EDGE_LAYERS = [   # 3x3, stride 1, padding 1: factors formed from shift products
+    synth.Layer("row_image", 2, 1, 5, 8, 1, 5, 8, 3, 3, 1, 1, 1, 1, 0),
+    synth.Layer("column_image", 1, 4, 1, 24, 4, 1, 16, 3, 3, 1, 1, 1, 1, 1),
+    synth.Layer("two_row_blocks", 3, 2, 3, 136, 2, 3, 8, 3, 3, 1, 1, 1, 1, 1),
+    synth.Layer("single_pixel", 4, 1, 1, 16, 1, 1, 8, 3, 3, 1, 1, 1, 1, 1),
+]
+
+
+def test_factors_shift_products_edge_cases(kfac_gpu):
+    """[OTUNYM] eq. (5) for 3x3 stride-1 convolutions on images of one row, one
+    column, one pixel and with more than 128 channels, integer inputs: bit-exact, as
+    every sum (the shift products, their border strips and corners) is an exact integer."""
+    rng = synth.layer_rng(1013, 0)
+    act = [rng.integers(-2, 3, size=l.act_shape).astype(np.float16) for l in SHIFT_EDGE_LAYERS]
+    gout = [rng.integers(-2, 3, size=l.gout_shape).astype(np.float16) for l in SHIFT_EDGE_LAYERS]
+    say("kfac_factors shift-product edge cases")
+    A, G = _run_factors(kfac_gpu, SHIFT_EDGE_LAYERS, act, gout)
+    for l, layer in enumerate(SHIFT_EDGE_LAYERS):
+        X = oracle.im2col_nhwc(act[l], 3, 3, 1, 1, 1, 1, layer.bias)
+        inv_r = np.float32(1.0) / np.float32(X.shape[0])
+        expect = oracle.pack_upper(oracle.gram(X)).astype(np.float32) * inv_r
+        assert np.array_equal(host(A[l]), expect), layer.name
+
+
 def test_factors_fp32_fc_and_kronecker(kfac_gpu):
     """The fc workload in fp32 (a[32x64], g[32x16], no bias): factors, damped inverses
     and G^-1 dW A^-1 through the library, checked against the oracle and against the
