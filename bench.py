@@ -37,6 +37,11 @@ PEAK_FP16_MFMA = 2516.6  # TFLOP/s, MI355X dense fp16 (and bf16) matrix
 # update, the preconditioning and the refinement's correction): the bf16 peak over six
 # is the bound of their algorithmic fp32 flops.
 PEAK_X3 = round(PEAK_FP16_MFMA / 6, 1)
+
+# kernels whose algorithmic work per launch bench.py models (roofline candidates)
+MODELLED = {"inv_update_kernel", "syrk_tile_kernel", "gemm_tn_kernel", "gemm_tn64_kernel",
+            "refine_residual_gemm_tn64_kernel", "refine_correction_gemm_tn_kernel", "bn_partial_kernel",
+            "unpack_kernel"}
 PEAK_HBM = 8000.0        # GB/s
 TB = 128                 # block of the inverse
 LR = 0.01                # learning rate of the parameter update
@@ -88,6 +93,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra-configs", action="store_true",
                     help="only the ResNet-50 step (no fc, 3x3, inversion-stress and stale-schedule keys)")
+    ap.add_argument("--no-side-stream", action="store_true",
+                    help="run the whole step on one stream (default: the 4609-order inverses and "
+                         "their layers' preconditioning on a second stream)")
     ap.add_argument("--no-kernel-timing", action="store_true",
                     help="time the steps without per-kernel events (roofline then null)")
     ap.add_argument("--copy-calibration", type=float, default=0.0,
@@ -635,7 +643,8 @@ def main():
     progress("drawing inputs")
     act, gout, grads, xhat, bgout = make_inputs(layers, bns, dev)
     weights, bn_params = make_params(layers, bns, dev)
-    st = kfac.KfacStep(layers, bns, dev, precond_accum=args.precond_accum, refine_inverse=args.refine_inverse)
+    st = kfac.KfacStep(layers, bns, dev, precond_accum=args.precond_accum, refine_inverse=args.refine_inverse,
+                       side_stream=not args.no_side_stream)
     host_in = None
     if not args.no_cpu_baseline:   # the oracle's copy of the very inputs of the timed steps
         host_in = {"act": [a.cpu().numpy() for a in act], "gout": [g.cpu().numpy() for g in gout],
@@ -654,14 +663,20 @@ def main():
         raise RuntimeError("Cholesky breakdown on a damped factor: " + str(st.info.tolist()))
 
     timing = not args.no_kernel_timing
-    kern, dominant = {}, None
+    kern, dominant, top = {}, None, None
     if timing:
-        # breakdown pass (untimed): every launch bracketed by events, over two steps
+        # breakdown pass (untimed): every launch bracketed by events, over two steps of
+        # the one-stream schedule, so that a launch's time is its own and not time spent
+        # waiting behind the other stream's work
+        bst = st if not st.side else kfac.KfacStep(layers, bns, dev, precond_accum=args.precond_accum,
+                                                   refine_inverse=args.refine_inverse, side_stream=False)
+        bst.step(act, gout, grads, xhat, bgout, weights=weights, bn_params=bn_params, lr=LR)
+        torch.cuda.synchronize()
         kfac.kfac_timing_reset()
         kfac.kfac_timing_only(-1)
         kfac.kfac_timing_enable(True)
         for _ in range(2):
-            step()
+            bst.step(act, gout, grads, xhat, bgout, weights=weights, bn_params=bn_params, lr=LR)
         torch.cuda.synchronize()
         kfac.kfac_timing_enable(False)
         for i in range(kfac.kfac_timing_kernels()):
@@ -669,8 +684,14 @@ def main():
             if n:
                 kern[kfac.kfac_kernel_name(i)] = (ms / 2, n // 2)
         kfac.kfac_timing_reset()
-        dominant = max(range(kfac.kfac_timing_kernels()),
-                       key=lambda i: kern.get(kfac.kfac_kernel_name(i), (0.0, 0))[0])
+        del bst
+        torch.cuda.empty_cache()
+        ids = range(kfac.kfac_timing_kernels())
+        by_time = lambda i: kern.get(kfac.kfac_kernel_name(i), (0.0, 0))[0]  # noqa: E731
+        top = kfac.kfac_kernel_name(max(ids, key=by_time))
+        # the roofline kernel: the largest one with an algorithmic work model (the
+        # pivot and panel launches are latency-bound steps of the sweep and have none)
+        dominant = max((i for i in ids if kfac.kfac_kernel_name(i) in MODELLED), key=by_time)
         # timed region: events around the dominant kernel's launches only
         kfac.kfac_timing_only(dominant)
         kfac.kfac_timing_enable(True)
@@ -708,6 +729,7 @@ def main():
             "refine_residual_gemm_tn64_kernel": (w["refine_flop"] / 2 * args.steps, "mfma", PEAK_FP64_MFMA),
             "refine_correction_gemm_tn_kernel": (w["refine_flop"] / 2 * args.steps, "mfma", PEAK_X3),
         }
+        assert set(per_launch) | {"bn_partial_kernel", "unpack_kernel"} == MODELLED
         if name in per_launch:
             total_work, bound, peak = per_launch[name]
             achieved = total_work / (ms * 1e-3) / 1e12      # = per-launch work / average duration
@@ -715,6 +737,8 @@ def main():
                         "frac": round(achieved / peak, 4), "traffic": measured_traffic(name), "kernel": name,
                         "launches": n, "avg_launch_us": round(1e3 * ms / n, 2),
                         "algorithmic_per_launch": total_work / n}
+        if roofline and top != name:
+            roofline["largest_kernel"] = top
         elif name in ("bn_partial_kernel", "unpack_kernel"):
             b = w["bn_bytes"] if name == "bn_partial_kernel" else w["pack_bytes"]
             achieved = b * args.steps / (ms * 1e-3) / 1e9
@@ -732,6 +756,7 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
+    side_stream = bool(st.side)
     extra = {}
     if not args.no_extra_configs:
         with_oracle = not args.no_cpu_baseline
@@ -761,7 +786,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": "resnet50_kfac_step", "batch_per_gpu": args.batch,
                    "kfac_layers": len(layers), "factors": 2 * len(layers), "bn_layers": len(bns),
-                   "damping": 1e-3, "lr": LR, "precond_accum": args.precond_accum, "refine_inverse": args.refine_inverse, "inputs": "fp16 ReLU(N(0,1)) activations, fp16 N(0,1) "
+                   "damping": 1e-3, "lr": LR, "precond_accum": args.precond_accum, "refine_inverse": args.refine_inverse,
+                   "side_stream": side_stream, "inputs": "fp16 ReLU(N(0,1)) activations, fp16 N(0,1) "
                    "output and BN gradients, fp32 N(0,1e-2) weight gradients, fp32 N(0,2.5e-3) weights"},
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -136,7 +136,7 @@ __global__ void __launch_bounds__(TB) inv_damp_kernel(const InvDesc* __restrict_
 constexpr int PT = 512;           // threads of the pivot kernel
 constexpr int SB = 32;            // sub-step width
 constexpr int MLD = TB + 4;       // LDS pitch of M
-constexpr int ELD = SB + 4;       // LDS pitch of the 32x32 E_JJ copies
+constexpr int ELD = SB + 1;       // LDS pitch of the 32x32 E_JJ copies (odd: read along rows and columns)
 
 // acc[m][n] += sign * sum_p a[p*lda + m] * b[p*ldb + n] for p < 32 (one wave, LDS).
 // Accumulator register e of lane l holds element (8*(e/4) + 4*(l/32) + e%4, l%32).
@@ -146,6 +146,16 @@ __device__ __forceinline__ void mma32(v16f& acc, const float* a, int lda, const 
 #pragma unroll
   for (int k = 0; k < SB; k += 2) {
     const float av = a[(k + kh) * lda + ml] * sign;
+    const float bv = b[(k + kh) * ldb + ml];
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
+  }
+}
+// The same with the A operand read transposed: element (m, p) = a[m*lda + p].
+__device__ __forceinline__ void mma32_at(v16f& acc, const float* a, int lda, const float* b, int ldb, int lane) {
+  const int ml = lane & 31, kh = lane >> 5;
+#pragma unroll
+  for (int k = 0; k < SB; k += 2) {
+    const float av = a[ml * lda + k + kh];
     const float bv = b[(k + kh) * ldb + ml];
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
   }
@@ -165,9 +175,9 @@ __device__ __forceinline__ float lane_bcast(float v, int src_lane) {
 // M_tj -= r_t r_j). Row c+1 is updated and published first, and the broadcast of
 // step c+1 is read before the remaining rows of step c are updated, so LDS latency
 // overlaps arithmetic (LDS operations of one wave complete in order). Writes the
-// block back, E_JJ to ej (rows, lower with diagonal) and its transpose to ejt and
-// to uil (pitch MLD), U_cc to diagU; returns the first 1-based failing step or 0.
-__device__ __forceinline__ int chol32(float* blk, float* ej, float* ejt, float* uil, float* diagU,
+// block back, E_JJ to ej (rows, lower with diagonal) and its transpose to uil
+// (global, pitch TB), U_cc to diagU; returns the first 1-based failing step or 0.
+__device__ __forceinline__ int chol32(float* blk, float* ej, KG float* uil, float* diagU,
                                       float (*urow)[SB / 2], int lane) {
   const int j = lane & 31, h = lane >> 5;
   float d[SB / 2];
@@ -229,8 +239,7 @@ __device__ __forceinline__ int chol32(float* blk, float* ej, float* ejt, float* 
     blk[t * MLD + j] = d[q];
     const float e = j <= t ? d[q] : 0.f;  // E_JJ[t][j]
     ej[t * ELD + j] = e;
-    ejt[j * ELD + t] = e;
-    uil[j * MLD + t] = e;
+    uil[j * TB + t] = e;
   }
   return failed;
 }
@@ -265,9 +274,14 @@ __device__ __forceinline__ void update_tile(const InvDesc& d, int ti, int tj, in
 __global__ void __launch_bounds__(PT) inv_pivot_kernel(const InvDesc* __restrict__ desc,
                                                        const int32_t* __restrict__ begin, int a, int k,
                                                        int pre, int rows) {
+  // 80.5 KB in all, at most half the LDS of a compute unit, so that a pivot block fits
+  // next to one block of the other matrix kernels (67.6 KB at most): U^-1 and P^-1 go
+  // straight to global memory, and the staging planes of the diagonal pre-update share
+  // their space with the two E_JJ buffers.
   __shared__ __attribute__((aligned(16))) float M[TB * MLD];
-  __shared__ __attribute__((aligned(16))) float PL[TB * MLD];  // U^-1 = E^T, then P^-1
-  __shared__ __attribute__((aligned(16))) float EJ[2][SB * ELD], EJT[2][SB * ELD];
+  __shared__ __attribute__((aligned(16))) float XU[X3_GRAM_LDS_BYTES / 4];
+  static_assert(X3_GRAM_LDS_BYTES >= 2 * SB * ELD * 4, "E_JJ copies do not fit the shared space");
+  float (*EJ)[SB * ELD] = reinterpret_cast<float (*)[SB * ELD]>(XU);
   __shared__ __attribute__((aligned(16))) float urow[2][SB / 2];
   __shared__ float diagU[TB];
   if (static_cast<int>(blockIdx.x) >= a) {  // a tile of block row k (M is the staging LDS)
@@ -298,27 +312,25 @@ __global__ void __launch_bounds__(PT) inv_pivot_kernel(const InvDesc* __restrict
 #pragma unroll
     for (int q = 0; q < TB / 4; ++q) M[(r0 + 4 * q) * MLD + j] = v[q];
   }
-  if (pre) {  // S_kk -= Y_k^T Y_k on the upper triangle, PL as the staging buffer
+  if (pre) {  // S_kk -= Y_k^T Y_k on the upper triangle, XU as the staging planes
     __syncthreads();
-    Oct o;
+    Oct o;  // -S_kk + Y^T Y, the exact negation of S_kk - Y^T Y summed the same way
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) o.c[b][e] = M[oct_row(lane, e) * MLD + oct_col(lane, b)];
+      for (int e = 0; e < 16; ++e) o.c[b][e] = -M[oct_row(lane, e) * MLD + oct_col(lane, b)];
     // panel rows [(pre-1)*TB, pre*TB): step k-1 (a full block: a matrix's narrow
     // last step is never followed by a pivot)
     const float* Y = d.Y + int64_t(pre - 1) * TB * d.ldy;
-    oct_gemm(o, op_rows(Y, d.ldy, TB, k0, n), op_rows(Y, d.ldy, TB, k0, n), TB, -1.f, PL);  // ends with a barrier
+    oct_gram(o, op_rows(Y, d.ldy, TB, k0, n), reinterpret_cast<__bf16*>(XU));  // ends with a barrier
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int r = oct_row(lane, e), c = oct_col(lane, b);
-        if (r <= c && c < bk) M[r * MLD + c] = o.c[b][e];
+        if (r <= c && c < bk) M[r * MLD + c] = -o.c[b][e];
       }
   }
-  for (int e = tid; e < TB * TB / 4; e += PT)
-    *reinterpret_cast<float4*>(PL + (e >> 5) * MLD + 4 * (e & 31)) = make_float4(0.f, 0.f, 0.f, 0.f);
   __syncthreads();
 
   // one 32x32 block of sub-step J's trailing update: (I, K) -= M_JI^T B_K, with
@@ -335,11 +347,15 @@ __global__ void __launch_bounds__(PT) inv_pivot_kernel(const InvDesc* __restrict
     for (int e = 0; e < 16; ++e) C[acc_row(e, lane) * MLD + (lane & 31)] = acc[e];
   };
   int failed = 0;
+#pragma unroll 1
   for (int J = 0; J < TB / SB; ++J) {
     float* rowJ = M + J * SB * MLD;
     if (w == 0) {
-      const int f = chol32(rowJ + J * SB, EJ[J & 1], EJT[J & 1], PL + J * SB * MLD + J * SB, diagU + J * SB,
-                           urow, lane);
+      // lane index laundered per sub-step: keeps the compiler from hoisting chol32's
+      // 32 lane masks and LDS addresses out of the loop, which spills them
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int f = chol32(rowJ + J * SB, EJ[J & 1], gp(d.Ui) + J * SB * TB + J * SB, diagU + J * SB, urow, ln);
       if (failed == 0 && f) failed = J * SB + f;
     } else if (J > 0) {
       // the rest of sub-step J-1's update: blocks (I, K), I > J-1, (K <= J-1 or
@@ -359,12 +375,12 @@ __global__ void __launch_bounds__(PT) inv_pivot_kernel(const InvDesc* __restrict
       v16f acc;
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[e] = 0.f;
-      mma32(acc, EJT[J & 1], ELD, X, MLD, 1.f, lane);  // sum_p E_JJ[m][p] X[p][n]
+      mma32_at(acc, EJ[J & 1], ELD, X, MLD, lane);  // sum_p E_JJ[m][p] X[p][n]
 #pragma unroll
       for (int e = 0; e < 16; ++e) X[acc_row(e, lane) * MLD + (lane & 31)] = acc[e];
       if (K < J) {  // E_JK is final: its transpose is block (K, J) of U^-1
 #pragma unroll
-        for (int e = 0; e < 16; ++e) PL[(K * SB + (lane & 31)) * MLD + J * SB + acc_row(e, lane)] = acc[e];
+        for (int e = 0; e < 16; ++e) gp(d.Ui)[(K * SB + (lane & 31)) * TB + J * SB + acc_row(e, lane)] = acc[e];
       }
     }
     __syncthreads();
@@ -380,7 +396,7 @@ __global__ void __launch_bounds__(PT) inv_pivot_kernel(const InvDesc* __restrict
       if (i <= j && j < bk) gp(d.chol)[int64_t(k0 + i) * n + k0 + j] = i == j ? diagU[i] : M[i * MLD + j];
     }
   __syncthreads();
-  // M <- E (zero above the diagonal), U^-1 to the workspace (16-byte stores)
+  // M <- E (zero above the diagonal)
   for (int e = tid; e < TB * TB / 4; e += PT) {
     const int i = e >> 5, j = 4 * (e & 31);
     float4 x = *reinterpret_cast<const float4*>(M + i * MLD + j);
@@ -389,14 +405,15 @@ __global__ void __launch_bounds__(PT) inv_pivot_kernel(const InvDesc* __restrict
     if (j + 2 > i) x.z = 0.f;
     if (j + 3 > i) x.w = 0.f;
     *reinterpret_cast<float4*>(M + i * MLD + j) = x;
-    const float4 y = *reinterpret_cast<const float4*>(PL + i * MLD + j);
-    *reinterpret_cast<KG v4f*>(gp(d.Ui) + i * TB + j) = v4f{y.x, y.y, y.z, y.w};
   }
   __syncthreads();
   // P^-1 = E^T E on MFMA, upper 32x32 blocks (bi <= bj) only, mirrored: the sum
   // over p runs over the 32-row blocks kb >= bj (E is lower triangular). Block
-  // costs 4 - bj, dealt so that no wave has more than 4.
+  // costs 4 - bj, dealt so that no wave has more than 4. Each block goes straight to
+  // the workspace (and its mirror), and its upper part, negated, to S_kk.
   {
+    KG float* Pg = gp(d.P);
+    KG float* Sk = gp(d.S) + int64_t(k0) * n + k0;
     constexpr int kBlocks[8][2] = {{0, -1}, {1, -1}, {4, -1}, {2, 3}, {5, 6}, {7, 8}, {9, -1}, {-1, -1}};
     constexpr int kBi[10] = {0, 0, 0, 0, 1, 1, 1, 2, 2, 3}, kBj[10] = {0, 1, 2, 3, 1, 2, 3, 2, 3, 3};
 #pragma unroll
@@ -412,24 +429,11 @@ __global__ void __launch_bounds__(PT) inv_pivot_kernel(const InvDesc* __restrict
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int r = acc_row(e, lane), c = lane & 31;
-        PL[(SB * bi + r) * MLD + SB * bj + c] = acc[e];
-        if (bi != bj) PL[(SB * bj + c) * MLD + SB * bi + r] = acc[e];
+        const int i = SB * bi + r, j = SB * bj + c;  // i <= j off the diagonal blocks
+        Pg[i * TB + j] = acc[e];
+        if (bi != bj) Pg[j * TB + i] = acc[e];
+        if (i <= j && j < bk) Sk[int64_t(i) * n + j] = -acc[e];
       }
-    }
-  }
-  __syncthreads();
-  for (int e = tid; e < TB * TB / 4; e += PT) {
-    const int i = e >> 5, j = 4 * (e & 31);
-    const float4 x = *reinterpret_cast<const float4*>(PL + i * MLD + j);
-    *reinterpret_cast<KG v4f*>(gp(d.P) + i * TB + j) = v4f{x.x, x.y, x.z, x.w};
-  }
-  {  // S_kk = -P^-1, upper triangle, along rows of S
-    const int j = tid & (TB - 1), r0 = tid >> 7;
-    KG float* dst = gp(d.S) + int64_t(k0) * n + k0 + j;
-#pragma unroll 8
-    for (int q = 0; q < TB / 4; ++q) {
-      const int i = r0 + 4 * q;
-      if (i <= j && j < bk) dst[int64_t(i) * n] = -PL[i * MLD + j];
     }
   }
   if (failed && tid == 0 && *gp(d.info) == 0) *gp(d.info) = k0 + failed;
@@ -439,23 +443,27 @@ __global__ void __launch_bounds__(PT) inv_pivot_kernel(const InvDesc* __restrict
 // j != k, V_j = S_kj (S_jk^T for j < k); Y_j = E V_j (the Cholesky row panel U_kj
 // when j > k) goes to the panel buffer and W_j = P^-1 V_j into S in place (S_kj =
 // W_j, or S_jk = W_j^T). The pivot kernel wrote S_kk = -P^-1.
-// Two 512-thread blocks share a tile, each forming 64 of the 128 rows of Y_j and W_j
-// (rows h*64 ..): V_j is staged whole in LDS (67.6 KB, so two blocks fit on a compute
-// unit), waves 0-3 form the Y half and waves 4-7 the W half, each wave a 32x64 slab
-// whose A operand (rows of U_kk^-1 = E^T or of P^-1, read as [k][m]) streams from L2
-// straight into MFMA operand registers one 32-deep chunk ahead. E is lower
-// triangular, so a Y row m only sums k <= m. Blocks b and b+8 (same XCD, so the
-// second read of V_j hits that XCD's L2) take the two halves of one tile.
+// Two 512-thread blocks share a tile, each taking 64 of its 128 columns (h*64 ..):
+// a block reads only its own columns of V_j and writes W back only over them, so
+// neither block can overwrite what the other has still to read. The block stages its
+// 128x64 half of V_j in LDS; waves 0-3 form Y and waves 4-7 W, each wave a 32x64 slab
+// (rows 32w ..) whose A operand (rows of U_kk^-1 = E^T or of P^-1, read as [k][m])
+// streams from L2 straight into MFMA operand registers one 32-deep chunk ahead. E is
+// lower triangular, so a Y row m only sums k <= m. Blocks b and b+8 (one XCD, so the
+// second read of the A operands hits that XCD's L2) take the two halves of one tile.
 // For slot >= 1, blocks from `base` on give step k-1 (panel slot-1) to the diagonal
 // blocks of the group's later pivots k+1.. (block (p, u): matrix p, pivot kg+1+u),
 // which nothing else in the launch reads or writes; Vs is their staging LDS.
-constexpr int PP = 512;  // panel threads
-constexpr int WTP = 65;  // pitch of the transposed W half in LDS
+constexpr int PP = 512;        // panel threads
+constexpr int PH = TB / 2;     // columns of V_j per block
+constexpr int VLD = PH + 4;    // LDS pitch of the staged V half
+constexpr int WTP = TB + 1;    // pitch of the transposed W half in LDS
+constexpr int PANEL_LDS = X3_LDS_BYTES / 4;  // floats
+static_assert(PANEL_LDS >= TB * VLD && PANEL_LDS >= PH * WTP, "panel LDS too small");
 __global__ void __launch_bounds__(PP) __attribute__((amdgpu_waves_per_eu(4, 4)))
 inv_panel_kernel(const InvDesc* __restrict__ desc, const int32_t* __restrict__ begin, int count, int k,
                  int slot, int total, int base) {
-  __shared__ __attribute__((aligned(16))) float Vs[TB * LDP];
-  static_assert(TB * LDP >= 4 * CHUNK, "panel LDS too small for the update engine");
+  __shared__ __attribute__((aligned(16))) float Vs[PANEL_LDS];
   const int bid = blockIdx.x;
   if (GS > 2 && bid >= base) {  // step k-1 on a later pivot's diagonal block
     constexpr int L = GS > 2 ? GS - 1 : 1;  // later pivots per matrix at most
@@ -474,14 +482,13 @@ inv_panel_kernel(const InvDesc* __restrict__ desc, const int32_t* __restrict__ b
   const int j = t - begin[p];
   if (j == k) return;
   const int n = d.n, k0 = k * TB, bk = min(TB, n - k0);
-  const int j0 = j * TB, bj = min(TB, n - j0);
-  const int r0 = h * (TB / 2);
-  if (r0 >= bk) return;  // no pivot rows in this half
+  const int c0 = h * PH;                         // first column of this half
+  const int j0 = j * TB + c0, bj = min(TB, n - j * TB) - c0;  // columns [j0, j0 + bj)
+  if (bj <= 0) return;  // no columns in this half
   const int tid = threadIdx.x;
   const int grp = tid >> 8, w = (tid >> 6) & 3, lane = tid & 63;
   const int ml = lane & 31, kh = lane >> 5;
-  const int mr = r0 + 32 * (w >> 1);  // first row of this wave's slab
-  const int nc = 64 * (w & 1);        // first column
+  const int mr = 32 * w;  // first row of this wave's slab
   // A operand element (k, m) = Ui[k][m] (Y) or P^-1[k][m] (W); zero for k, m >= bk
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<float*>(grp == 0 ? d.Ui : d.P), 0, TB * TB * 4, 0x00020000);
@@ -499,29 +506,28 @@ inv_panel_kernel(const InvDesc* __restrict__ desc, const int32_t* __restrict__ b
   };
   float acur[16], anext[16];
   load_a(acur, 0);  // in flight together with the V loads
-  {  // all 32 loads of a thread in flight first (clamped addresses, zero outside)
-    const int lo = tid & (TB - 1), hi0 = tid >> 7;  // along a row of S / first row
-    float v[TB * TB / PP];
-    if (j > k) {  // V[r][c] = S[k0 + r][j0 + c]: thread column c = lo, rows hi0 + 4q
-      const int c = lo;
+  {  // all 16 loads of a thread in flight first (clamped addresses, zero outside)
+    float v[TB * PH / PP];
+    if (j > k) {  // V[r][c] = S[k0 + r][j0 + c]: thread column c = tid % 64, rows tid / 64 + 8q
+      const int c = tid & (PH - 1), ra = tid >> 6;
 #pragma unroll
-      for (int q = 0; q < TB * TB / PP; ++q) {
-        const int r = hi0 + 4 * q;
+      for (int q = 0; q < TB * PH / PP; ++q) {
+        const int r = ra + 8 * q;
         const float x = gp(d.S)[int64_t(k0 + min(r, bk - 1)) * n + j0 + min(c, bj - 1)];
         v[q] = (r < bk && c < bj) ? x : 0.f;
       }
 #pragma unroll
-      for (int q = 0; q < TB * TB / PP; ++q) Vs[(hi0 + 4 * q) * LDP + c] = v[q];
+      for (int q = 0; q < TB * PH / PP; ++q) Vs[(ra + 8 * q) * VLD + c] = v[q];
     } else {  // V[r][c] = S[j0 + c][k0 + r]: read along rows of S, transpose in LDS
-      const int r = lo;
+      const int r = tid & (TB - 1), ca = tid >> 7;
 #pragma unroll
-      for (int q = 0; q < TB * TB / PP; ++q) {
-        const int c = hi0 + 4 * q;
+      for (int q = 0; q < TB * PH / PP; ++q) {
+        const int c = ca + 4 * q;
         const float x = gp(d.S)[int64_t(j0 + min(c, bj - 1)) * n + k0 + min(r, bk - 1)];
         v[q] = (r < bk && c < bj) ? x : 0.f;
       }
 #pragma unroll
-      for (int q = 0; q < TB * TB / PP; ++q) Vs[r * LDP + hi0 + 4 * q] = v[q];
+      for (int q = 0; q < TB * PH / PP; ++q) Vs[r * VLD + ca + 4 * q] = v[q];
     }
   }
   v16f acc0, acc1;
@@ -533,7 +539,7 @@ inv_panel_kernel(const InvDesc* __restrict__ desc, const int32_t* __restrict__ b
     float b0[16], b1[16];
 #pragma unroll
     for (int s = 0; s < 16; ++s) {
-      const float* br = Vs + (32 * c + 2 * s + kh) * LDP + nc + ml;
+      const float* br = Vs + (32 * c + 2 * s + kh) * VLD + ml;
       b0[s] = br[0];
       b1[s] = br[32];
     }
@@ -553,49 +559,49 @@ inv_panel_kernel(const InvDesc* __restrict__ desc, const int32_t* __restrict__ b
 #pragma unroll
     for (int s = 0; s < 16; ++s) acur[s] = anext[s];
   }
-  // accumulator register e of block b: row mr + 8(e/4) + 4kh + e%4, column nc + 32b + ml
+  // accumulator register e of block b: row mr + 8(e/4) + 4kh + e%4, column 32b + ml
   if (grp == 0) {
     KG float* Y = gp(d.Y) + int64_t(slot) * TB * d.ldy + j0;
     KG float* U = (d.chol && j > k) ? gp(d.chol) + int64_t(k0) * n + j0 : nullptr;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int r = mr + 8 * (e >> 2) + 4 * kh + (e & 3);
-      const int c0 = nc + ml, c1 = nc + 32 + ml;
+      const int ca = ml, cb = 32 + ml;
       if (r < bk) {
-        if (c0 < bj) Y[int64_t(r) * d.ldy + c0] = acc0[e];
-        if (c1 < bj) Y[int64_t(r) * d.ldy + c1] = acc1[e];
+        if (ca < bj) Y[int64_t(r) * d.ldy + ca] = acc0[e];
+        if (cb < bj) Y[int64_t(r) * d.ldy + cb] = acc1[e];
         if (U) {
-          if (c0 < bj) U[int64_t(r) * n + c0] = acc0[e];
-          if (c1 < bj) U[int64_t(r) * n + c1] = acc1[e];
+          if (ca < bj) U[int64_t(r) * n + ca] = acc0[e];
+          if (cb < bj) U[int64_t(r) * n + cb] = acc1[e];
         }
       }
     }
-  } else if (j > k) {  // S_kj = W_j
+  } else if (j > k) {  // S_kj = W_j over this block's columns
     KG float* W = gp(d.S) + int64_t(k0) * n + j0;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int r = mr + 8 * (e >> 2) + 4 * kh + (e & 3);
-      const int c0 = nc + ml, c1 = nc + 32 + ml;
+      const int ca = ml, cb = 32 + ml;
       if (r < bk) {
-        if (c0 < bj) W[int64_t(r) * n + c0] = acc0[e];
-        if (c1 < bj) W[int64_t(r) * n + c1] = acc1[e];
+        if (ca < bj) W[int64_t(r) * n + ca] = acc0[e];
+        if (cb < bj) W[int64_t(r) * n + cb] = acc1[e];
       }
     }
   }
-  if (j < k) {  // S_jk = W_j^T through LDS (pitch WTP), coalesced along rows of S
+  if (j < k) {  // S_jk = W_j^T over this block's rows of S, through LDS (pitch WTP)
     __syncthreads();  // every wave is done reading Vs
     if (grp == 1) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int rl = mr - r0 + 8 * (e >> 2) + 4 * kh + (e & 3);
-        Vs[(nc + ml) * WTP + rl] = acc0[e];
-        Vs[(nc + 32 + ml) * WTP + rl] = acc1[e];
+        const int r = mr + 8 * (e >> 2) + 4 * kh + (e & 3);
+        Vs[ml * WTP + r] = acc0[e];
+        Vs[(32 + ml) * WTP + r] = acc1[e];
       }
     }
     __syncthreads();
-    for (int e = tid; e < TB * (TB / 2); e += PP) {
-      const int c = e >> 6, rl = e & 63;
-      if (r0 + rl < bk && c < bj) gp(d.S)[int64_t(j0 + c) * n + k0 + r0 + rl] = Vs[c * WTP + rl];
+    for (int e = tid; e < PH * TB; e += PP) {
+      const int c = e >> 7, r = e & (TB - 1);
+      if (r < bk && c < bj) gp(d.S)[int64_t(j0 + c) * n + k0 + r] = Vs[c * WTP + r];
     }
   }
 }

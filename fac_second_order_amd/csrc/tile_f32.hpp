@@ -298,16 +298,17 @@ __device__ __forceinline__ v8bf x3_operand(const __bf16* plane, int c0) {
   return v8bf{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-__device__ inline void x3_mma(Oct& o, const __bf16* cur) {
+// acc += A^T B over one staged chunk: A planes at pa, B planes at pb (XPLANE apart)
+__device__ inline void x3_mma(Oct& o, const __bf16* pa, const __bf16* pb) {
   const int wave = threadIdx.x >> 6;
   const int wm = 32 * (wave >> 1), wn = 64 * (wave & 1);
   v8bf a[3], b[2][3];
 #pragma unroll
-  for (int p = 0; p < 3; ++p) a[p] = x3_operand(cur + p * XPLANE, wm);
+  for (int p = 0; p < 3; ++p) a[p] = x3_operand(pa + p * XPLANE, wm);
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int p = 0; p < 3; ++p) b[j][p] = x3_operand(cur + XOP + p * XPLANE, wn + 32 * j);
+    for (int p = 0; p < 3; ++p) b[j][p] = x3_operand(pb + p * XPLANE, wn + 32 * j);
 #pragma unroll
   for (int j = 0; j < 2; ++j) {  // small parts first
     o.c[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[2], b[j][0], o.c[j], 0, 0, 0);
@@ -338,7 +339,7 @@ __device__ inline void oct_gemm(Oct& o, const Operand& A, const Operand& B, int 
   rb0 = x3_fetch<MB>(B, rsb, 2 * XK);
   __syncthreads();
   auto step = [&](int c, v4f& ra, v4f& rb) {
-    x3_mma(o, lds + (c & 1) * XCH);
+    x3_mma(o, lds + (c & 1) * XCH, lds + (c & 1) * XCH + XOP);
     __bf16* nxt = lds + ((c + 1) & 1) * XCH;
     x3_stage(nxt, ra * sign);
     x3_stage(nxt + XOP, rb);
@@ -349,6 +350,25 @@ __device__ inline void oct_gemm(Oct& o, const Operand& A, const Operand& B, int 
   for (int c = 0; c < 2 * npair; c += 2) {
     step(c, ra1, rb1);
     step(c + 1, ra0, rb0);
+  }
+}
+
+// acc += Y^T Y for one rows-form operand Y (16-byte load form, kv rows, under 2^31
+// bytes) with the bf16x3 products: each chunk is staged once and read as both
+// operands, into a single set of planes (X3_GRAM_LDS_BYTES of lds), with the next
+// chunk's loads in flight during the MFMAs. Rows past kv read as zeros. Ends with a
+// barrier.
+constexpr int X3_GRAM_LDS_BYTES = XOP * 2;
+__device__ inline void oct_gram(Oct& o, const Operand& Y, __bf16* lds) {
+  const int nch = (Y.kv + XK - 1) / XK;
+  const __amdgpu_buffer_rsrc_t rs = op_rsrc<LD_V4>(Y);
+  v4f r = x3_fetch<LD_V4>(Y, rs, 0);
+  for (int c = 0; c < nch; ++c) {
+    x3_stage(lds, r);
+    r = x3_fetch<LD_V4>(Y, rs, (c + 1) * XK);
+    __syncthreads();
+    x3_mma(o, lds, lds);
+    __syncthreads();
   }
 }
 

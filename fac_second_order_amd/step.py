@@ -21,10 +21,18 @@ class KfacStep:
     Kronecker factor (float32-rounded) and gamma on the BN diagonal. precond_accum
     "f64" sums the preconditioning products in fp64 (kfac_precondition_ex).
     refine_inverse applies one fp64-residual refinement step to every inverse
-    (kfac_invert_refine), which keeps a full symmetric copy of each factor."""
+    (kfac_invert_refine), which keeps a full symmetric copy of each factor.
+
+    side_stream: the inverses of the factors whose order is more than half the
+    largest order (their block sweep is the long tail of the batch, a chain of
+    latency-bound launches that leaves most compute units idle) run on a second
+    stream, together with the preconditioning of their layers, while the caller's
+    stream inverts the rest, preconditions their layers and does the BatchNorm
+    step. The step joins the two streams before it returns; results are the same
+    bits as with one stream."""
 
     def __init__(self, layers, bn_layers=(), device="cuda", damping=1e-3, bn_shift=None,
-                 in_dtype=torch.float16, precond_accum="f32", refine_inverse=False):
+                 in_dtype=torch.float16, precond_accum="f32", refine_inverse=False, side_stream=True):
         self.layers = list(layers)
         self.bn_layers = list(bn_layers)
         self.device = torch.device(device)
@@ -43,7 +51,19 @@ class KfacStep:
         self.n_all = self.d_a + self.d_g
         self.full = [torch.empty(d, d, dtype=f32, device=dev) for d in self.n_all]
         self.packed_all = self.A_packed + self.G_packed
-        self.info = torch.zeros(len(self.n_all), dtype=torch.int32, device=dev)
+        # matrices (indices into n_all) inverted on the second stream, and the layers
+        # preconditioned there
+        n_max = max(self.n_all) if self.n_all else 0
+        long_ = [i for i, n in enumerate(self.n_all) if 2 * n > n_max + 2]
+        if not side_stream or refine_inverse or len(long_) in (0, len(self.n_all)):
+            long_ = []
+        L = len(self.layers)
+        self.side = long_
+        self.main = [i for i in range(len(self.n_all)) if i not in long_]
+        self.side_layers = sorted({i % L for i in long_})
+        self.main_layers = [l for l in range(L) if l not in self.side_layers]
+        self._info_main = torch.zeros(len(self.main), dtype=torch.int32, device=dev)
+        self._info_side = torch.zeros(len(self.side), dtype=torch.int32, device=dev)
         self.out = [torch.empty(g, a, dtype=f32, device=dev) for g, a in zip(self.d_g, self.d_a)]
         self.refine = bool(refine_inverse)
         self.factor_full = [torch.empty(d, d, dtype=f32, device=dev) for d in self.n_all] if self.refine else []
@@ -58,8 +78,27 @@ class KfacStep:
             sizes.append(K.kfac_invert_refine_workspace(self.n_all))
         if self.bn_layers:
             sizes.append(K.kfac_bn_diag_workspace(self.bn_layers))
-        # one workspace serves every call: they run one after another on one stream
+        # one workspace serves every call on the caller's stream: they run one after
+        # another; the second stream has its own
         self.workspace = torch.empty(max(sizes) + 256, dtype=torch.uint8, device=dev)
+        self.stream2 = None
+        if self.side:
+            sub = lambda v, idx: [v[i] for i in idx]  # noqa: E731
+            side_ws = max(K.kfac_invert_workspace(sub(self.n_all, self.side)),
+                          K.kfac_precondition_workspace(sub(self.d_g, self.side_layers),
+                                                        sub(self.d_a, self.side_layers)))
+            self.workspace2 = torch.empty(side_ws + 256, dtype=torch.uint8, device=dev)
+            self.stream2 = torch.cuda.Stream(device=dev)
+
+    @property
+    def info(self):
+        """Breakdown index of every inverse (order of n_all: A factors, then G)."""
+        out = torch.zeros(len(self.n_all), dtype=torch.int32, device=self.device)
+        if self.main:
+            out[self.main] = self._info_main
+        if self.side:
+            out[self.side] = self._info_side
+        return out
 
     @property
     def A_inv(self):
@@ -73,11 +112,28 @@ class KfacStep:
         K.kfac_factors(self.layers, act, gout, self.A_packed, self.G_packed, ema_decay,
                        self.workspace, stream)
 
+    def _sub(self, v, idx):
+        return [v[i] for i in idx]
+
     def invert(self, stream=None):
+        """Unpacks and inverts every damped factor on `stream` (the side split is
+        applied by step())."""
+        self._unpack(stream)
+        self._invert(self.main, self._info_main, self.workspace, stream)
+        if self.side:
+            self._invert(self.side, self._info_side, self.workspace, stream)
+        self._refine(stream)
+
+    def _unpack(self, stream):
         # kfac_invert reads only the upper triangle: unpack that half
         K.kfac_pack_sym(self.n_all, self.full, self.packed_all, 2, self.workspace, stream)
-        K.kfac_invert(self.n_all, self.full, self.full, [self.shift] * len(self.n_all), self.info,
-                      None, self.workspace, stream)
+
+    def _invert(self, idx, info, ws, stream):
+        if idx:
+            K.kfac_invert(self._sub(self.n_all, idx), self._sub(self.full, idx), self._sub(self.full, idx),
+                          [self.shift] * len(idx), info, None, ws, stream)
+
+    def _refine(self, stream):
         if self.refine:
             K.kfac_pack_sym(self.n_all, self.factor_full, self.packed_all, 1, self.workspace, stream)
             K.kfac_invert_refine(self.n_all, self.factor_full, [self.shift] * len(self.n_all), self.full,
@@ -86,15 +142,21 @@ class KfacStep:
     def precondition(self, grads, weights=None, lr=0.0, stream=None):
         """self.out <- preconditioned gradients; with weights (fp32 [d_g, d_a] per layer)
         also weights -= lr * self.out, in the same kernel."""
+        self._precondition(list(range(len(self.layers))), grads, weights, lr, self.workspace, stream)
+
+    def _precondition(self, ls, grads, weights, lr, ws, stream):
+        if not ls:
+            return
+        sub = self._sub
+        d_g, d_a, G, A, g, o = (sub(self.d_g, ls), sub(self.d_a, ls), sub(self.G_inv, ls), sub(self.A_inv, ls),
+                                sub(grads, ls), sub(self.out, ls))
+        w = sub(weights, ls) if weights is not None else None
         if self.accum == K.KFAC_F64:
-            K.kfac_precondition_ex(self.d_g, self.d_a, self.G_inv, self.A_inv, grads, self.out, weights, lr,
-                                   self.accum, self.workspace, stream)
-        elif weights is None:
-            K.kfac_precondition(self.d_g, self.d_a, self.G_inv, self.A_inv, grads, self.out,
-                                self.workspace, stream)
+            K.kfac_precondition_ex(d_g, d_a, G, A, g, o, w, lr, self.accum, ws, stream)
+        elif w is None:
+            K.kfac_precondition(d_g, d_a, G, A, g, o, ws, stream)
         else:
-            K.kfac_precondition_update(self.d_g, self.d_a, self.G_inv, self.A_inv, grads, self.out,
-                                       weights, lr, self.workspace, stream)
+            K.kfac_precondition_update(d_g, d_a, G, A, g, o, w, lr, ws, stream)
 
     def bn(self, xhat, bn_gout, ema_decay=0.0, bn_params=None, lr=0.0, stream=None):
         """BN Fisher and preconditioned gradients; with bn_params (fp32 [2, c]: gamma,
@@ -114,8 +176,30 @@ class KfacStep:
         kept, the gradients are preconditioned with them, and BN divides its fresh
         gradient by the stored Fisher (decay 1 keeps it). Given weights and/or
         bn_params, those are updated in place with learning rate lr."""
-        if refresh:
-            self.factors(act, gout, ema_decay, stream)
+        if not refresh:
+            self.precondition(grads, weights, lr, stream)
+            self.bn(xhat, bn_gout, 1.0, bn_params, lr, stream)
+            return
+        self.factors(act, gout, ema_decay, stream)
+        if not self.side:
             self.invert(stream)
-        self.precondition(grads, weights, lr, stream)
-        self.bn(xhat, bn_gout, ema_decay if refresh else 1.0, bn_params, lr, stream)
+            self.precondition(grads, weights, lr, stream)
+            self.bn(xhat, bn_gout, ema_decay, bn_params, lr, stream)
+            return
+        main = torch.cuda.current_stream(self.device) if stream is None else stream
+        side = self.stream2
+        self._unpack(main)
+        unpacked = torch.cuda.Event()
+        unpacked.record(main)
+        side.wait_event(unpacked)
+        self._invert(self.side, self._info_side, self.workspace2, side)
+        self._invert(self.main, self._info_main, self.workspace, main)
+        main_inverses = torch.cuda.Event()
+        main_inverses.record(main)
+        self._precondition(self.main_layers, grads, weights, lr, self.workspace, main)
+        self.bn(xhat, bn_gout, ema_decay, bn_params, lr, main)
+        side.wait_event(main_inverses)  # the side layers' other factor
+        self._precondition(self.side_layers, grads, weights, lr, self.workspace2, side)
+        joined = torch.cuda.Event()
+        joined.record(side)
+        main.wait_event(joined)

@@ -233,3 +233,32 @@ def test_resnet50_precondition_and_bn(resnet_step):
         ref = oracle.bn_diag_fisher(h["xhat"][i], h["bgout"][i], st.bn_shift)
         assert relF(host(st.fisher[i]), ref["fisher"]) <= 1e-4, b.name
         assert relF(host(st.bn_pre[i]), ref["precond"]) <= 1e-4, b.name
+
+
+@pytest.mark.timeout(300)
+def test_resnet50_side_stream_same_bits(resnet_step, kfac_gpu):
+    """The step with the 4609-order inverses and their layers' preconditioning on a
+    second stream (the default) gives the bits of the one-stream step, with the eq. (8)
+    parameter updates: two steps each, on the same inputs and starting parameters."""
+    L, B, st, h = resnet_step
+    assert [st.n_all[i] for i in st.side] == [4609, 4609, 4609], st.side
+    dev_in = {k: [to_dev(a) for a in v] for k, v in h.items()}
+    runs = []
+    for side in (True, False):
+        s = kfac_gpu.KfacStep(L, B, "cuda", side_stream=side)
+        assert bool(s.side) == side
+        rng = synth.layer_rng(synth.config_seed("resnet50"), 5000)
+        w = [to_dev(synth.normal_f32(rng, (l.d_g, l.d_a), 0.05)) for l in L]
+        bp = [to_dev(synth.normal_f32(rng, (2, b.c), 1.0)) for b in B]
+        say(f"two steps with side_stream={side}")
+        for decay in (0.0, 0.5):  # the first refresh overwrites the (unset) running factors
+            s.step(dev_in["act"], dev_in["gout"], dev_in["grad"], dev_in["xhat"], dev_in["bgout"],
+                   ema_decay=decay, weights=w, bn_params=bp, lr=0.01)
+        torch.cuda.synchronize()
+        assert int(host(s.info).sum()) == 0
+        runs.append((s, w, bp))
+    (a, wa, ba), (b, wb, bb) = runs
+    for name, x, y in (("inverse", a.full, b.full), ("P", a.out, b.out), ("weights", wa, wb),
+                       ("bn precond", a.bn_pre, b.bn_pre), ("bn params", ba, bb)):
+        for i, (u, v) in enumerate(zip(x, y)):
+            assert torch.equal(u, v), (name, i)

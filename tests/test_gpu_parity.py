@@ -339,6 +339,55 @@ def test_invert_in_place_matches(kfac_gpu):
         assert torch.equal(x, y)
 
 
+def _device_factors(sizes, seed):
+    """Damped-Gram SPD factors drawn and formed on the device (inputs only)."""
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    out = []
+    for n in sizes:
+        X = torch.randn(4 * n, n, device="cuda", generator=g) * torch.logspace(0, -3, n, device="cuda")
+        out.append((X.t().contiguous() @ X) / (4 * n))
+    return out
+
+
+@pytest.mark.timeout(300)
+def test_invert_concurrent_streams_bitexact(kfac_gpu):
+    """Two inversion calls running at the same time on two streams, with a matrix
+    product competing for the compute units, give bit-for-bit the results of the same
+    calls run alone. Regression test for the panel step, whose two blocks per tile
+    once read the whole tile and wrote their halves of it back in place: a block
+    delayed behind other work could then read rows its partner had overwritten."""
+    big, small = [2049, 2049, 1153], [1025, 577, 513, 257, 129, 65, 64]
+    Fb, Fs = _device_factors(big, 71), _device_factors(small, 72)
+    ref_b = [torch.empty_like(F) for F in Fb]
+    ref_s = [torch.empty_like(F) for F in Fs]
+    info_b = torch.zeros(len(big), dtype=torch.int32, device="cuda")
+    info_s = torch.zeros(len(small), dtype=torch.int32, device="cuda")
+    kfac_gpu.kfac_invert(big, Fb, ref_b, [1e-3] * len(big), info_b)
+    kfac_gpu.kfac_invert(small, Fs, ref_s, [1e-3] * len(small), info_s)
+    assert host(info_b).tolist() == [0] * len(big) and host(info_s).tolist() == [0] * len(small)
+    ws_b = torch.empty(kfac_gpu.kfac_invert_workspace(big) + 256, dtype=torch.uint8, device="cuda")
+    ws_s = torch.empty(kfac_gpu.kfac_invert_workspace(small) + 256, dtype=torch.uint8, device="cuda")
+    busy = torch.randn(3072, 3072, device="cuda")
+    s0, s1 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        out_b = [torch.full_like(F, float("nan")) for F in Fb]
+        out_s = [torch.full_like(F, float("nan")) for F in Fs]
+        torch.cuda.synchronize()
+        say(f"concurrent inversion, repetition {rep}: {big} on one stream, {small} and a 3072^2 product on another")
+        with torch.cuda.stream(s0):
+            busy2 = busy @ busy
+            kfac_gpu.kfac_invert(small, Fs, out_s, [1e-3] * len(small), info_s, workspace=ws_s, stream=s0)
+        kfac_gpu.kfac_invert(big, Fb, out_b, [1e-3] * len(big), info_b, workspace=ws_b, stream=s1)
+        with torch.cuda.stream(s0):
+            busy2 = busy2 @ busy
+        torch.cuda.synchronize()
+        assert host(info_b).tolist() == [0] * len(big) and host(info_s).tolist() == [0] * len(small)
+        for x, r in zip(out_b + out_s, ref_b + ref_s):
+            assert torch.equal(x, r), x.shape
+    del busy2
+
+
 def test_invert_breakdown_info(kfac_gpu):
     """Non-positive pivots report the 1-based column (LAPACK potrf convention),
     including in a later 128-block, at the bordered last column of an order
