@@ -46,11 +46,13 @@ PEAK_HBM = 8000.0        # GB/s
 TB = 128                 # block of the inverse
 LR = 0.01                # learning rate of the parameter update
 
-# HBM bytes per launch of the dominant kernel, from two rocprofv3 --pmc passes
-# (FETCH_SIZE, then WRITE_SIZE), calibrated by a plain 1 GiB device copy (fetch x2.0,
-# write x1.0) and summarised in profiles/resnet50_step_hbm_counters.md. Reported only
-# while the kernel's source text still hashes to the value it was measured with.
-MEASURED_TRAFFIC = {"inv_update_kernel": (954500000, "60c9b2e3683ebed827c8e36a3808939902ba220c")}
+# HBM bytes per launch of the dominant kernel in the timed steps, from two rocprofv3
+# --pmc passes (FETCH_SIZE, then WRITE_SIZE) over the launches of the timed steps,
+# calibrated by a plain 1 GiB device copy (fetch x2.0, write x1.0) and summarised in
+# profiles/resnet50_step_hbm_counters.md; keyed by kernel and by whether the step ran
+# on two streams (the launches then hold fewer tiles each). Reported only while the
+# kernel's source text still hashes to the value it was measured with.
+MEASURED_TRAFFIC = {("inv_update_kernel", True): (606900000, "d9ce9c23afe67b70768c7b106777301a6e072e74")}
 CSRC = os.path.join(ROOT, "fac_second_order_amd", "csrc")
 
 
@@ -68,8 +70,8 @@ def kernel_source_sha(name):
     return hashlib.sha1(text.encode()).hexdigest()
 
 
-def measured_traffic(name):
-    rec = MEASURED_TRAFFIC.get(name)
+def measured_traffic(name, side_stream):
+    rec = MEASURED_TRAFFIC.get((name, side_stream))
     if rec is None or kernel_source_sha(name) != rec[1]:
         return None
     return rec[0]
@@ -734,7 +736,7 @@ def main():
             total_work, bound, peak = per_launch[name]
             achieved = total_work / (ms * 1e-3) / 1e12      # = per-launch work / average duration
             roofline = {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
-                        "frac": round(achieved / peak, 4), "traffic": measured_traffic(name), "kernel": name,
+                        "frac": round(achieved / peak, 4), "traffic": measured_traffic(name, bool(st.side)), "kernel": name,
                         "launches": n, "avg_launch_us": round(1e3 * ms / n, 2),
                         "algorithmic_per_launch": total_work / n}
         if roofline and top != name:

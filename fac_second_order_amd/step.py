@@ -128,6 +128,12 @@ class KfacStep:
         # kfac_invert reads only the upper triangle: unpack that half
         K.kfac_pack_sym(self.n_all, self.full, self.packed_all, 2, self.workspace, stream)
 
+    def _unpack_some(self, idx, stream):
+        if idx:
+            sub = self._sub
+            K.kfac_pack_sym(sub(self.n_all, idx), sub(self.full, idx), sub(self.packed_all, idx), 2,
+                            self.workspace, stream)
+
     def _invert(self, idx, info, ws, stream):
         if idx:
             K.kfac_invert(self._sub(self.n_all, idx), self._sub(self.full, idx), self._sub(self.full, idx),
@@ -188,11 +194,12 @@ class KfacStep:
             return
         main = torch.cuda.current_stream(self.device) if stream is None else stream
         side = self.stream2
-        self._unpack(main)
+        self._unpack_some(self.side, main)  # the long sweeps' factors first
         unpacked = torch.cuda.Event()
         unpacked.record(main)
         side.wait_event(unpacked)
         self._invert(self.side, self._info_side, self.workspace2, side)
+        self._unpack_some(self.main, main)
         self._invert(self.main, self._info_main, self.workspace, main)
         main_inverses = torch.cuda.Event()
         main_inverses.record(main)
