@@ -686,7 +686,12 @@ __global__ void __launch_bounds__(256) inv_border_kernel(const InvDesc* __restri
 // inv <- -S with both triangles written (S = inv in place); with a bordered last
 // column, the last step applied on the way (saved column v, pivot p, e = p^-1/2 as
 // the pivot kernel forms it: y = e v, S_ij - y_i y_j for i, j < n-1, W_i = e^2 v_i on
-// the border, -e^2 at the corner; the inverse is minus each).
+// the border, -e^2 at the corner; the inverse is minus each). A thread takes 4
+// adjacent columns of 4 rows: tiles off the diagonal, inside the matrix and left of
+// the border move them as 16-byte accesses (4-byte aligned: rows of an order that
+// is not a multiple of 4 start anywhere), the others entry by entry; the mirror goes
+// through LDS so that its stores also run along rows.
+typedef float f4u __attribute__((ext_vector_type(4), aligned(4)));
 __global__ void __launch_bounds__(256) inv_finish_kernel(const InvDesc* __restrict__ desc,
                                                          const int32_t* __restrict__ begin, int count) {
   __shared__ float s[FT][FT + 1];
@@ -695,37 +700,70 @@ __global__ void __launch_bounds__(256) inv_finish_kernel(const InvDesc* __restri
   int ti, tj;
   upper_tile(blockIdx.x - begin[p], d.nb64, ti, tj);
   const int64_t n = d.n;
-  const int c = threadIdx.x & (FT - 1);
+  const int cg = threadIdx.x & 15, r0 = threadIdx.x >> 4;  // columns 4cg.., rows r0 + 16q
   const int64_t i0 = int64_t(ti) * FT, j0 = int64_t(tj) * FT;
   const bool border = d.ns != d.nb;
-  float e = 0.f, ee = 0.f, yj = 0.f, vj = 0.f;
+  const int64_t jend = border ? n - 1 : n;  // columns of the plain part
+  const bool inner = ti < tj && j0 + FT <= jend;
+  constexpr int RQ = FT / 16;
+  float e = 0.f, ee = 0.f, yj[4] = {0.f, 0.f, 0.f, 0.f};
   const KG float* bv = gp(static_cast<const float*>(d.Y));
   if (border) {
     e = rsqrtf(bv[n - 1]);
     ee = e * e;
-    if (j0 + c < n - 1) {
-      vj = bv[j0 + c];
-      yj = e * vj;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (j0 + 4 * cg + u < n - 1) yj[u] = e * bv[j0 + 4 * cg + u];
+  }
+  f4u x[RQ];
+  float bi[RQ];
+#pragma unroll
+  for (int q = 0; q < RQ; ++q) {  // all loads first
+    const int64_t i = i0 + r0 + 16 * q, j = j0 + 4 * cg;
+    bi[q] = (border && i < n - 1) ? bv[i] : 0.f;
+    if (inner) {
+      x[q] = *reinterpret_cast<const KG f4u*>(gp(d.S) + i * n + j);
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) x[q][u] = (i < n && j + u < n && i <= j + u) ? gp(d.S)[i * n + j + u] : 0.f;
     }
   }
-  for (int r = threadIdx.x >> 6; r < FT; r += 4) {
-    const int64_t i = i0 + r, j = j0 + c;
-    float v = 0.f;
-    if (i < n && j < n && i <= j) {
-      float x = gp(d.S)[i * n + j];
+#pragma unroll
+  for (int q = 0; q < RQ; ++q) {
+    const int64_t i = i0 + r0 + 16 * q, j = j0 + 4 * cg;
+    f4u v;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      float y = x[q][u];
       if (border) {
-        if (j < n - 1) x = fmaf(-(e * bv[i]), yj, x);  // i <= j < n-1
-        else x = i < n - 1 ? ee * bv[i] : -ee;         // border column, corner
+        if (j + u < n - 1) y = fmaf(-(e * bi[q]), yj[u], y);  // i <= j < n-1
+        else y = i < n - 1 ? ee * bi[q] : -ee;                 // border column, corner
       }
-      v = -x;
-      gp(d.S)[i * n + j] = v;
+      v[u] = (i < n && j + u < n && i <= j + u) ? -y : 0.f;
     }
-    s[r][c] = v;
+    if (inner) {
+      *reinterpret_cast<KG f4u*>(gp(d.S) + i * n + j) = v;
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (i < n && j + u < n && i <= j + u) gp(d.S)[i * n + j + u] = v[u];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) s[r0 + 16 * q][4 * cg + u] = v[u];
   }
   __syncthreads();
-  for (int r = threadIdx.x >> 6; r < FT; r += 4) {
-    const int64_t j = j0 + r, i = i0 + c;
-    if (i < n && j < n && i < j) gp(d.S)[j * n + i] = s[c][r];
+#pragma unroll
+  for (int q = 0; q < RQ; ++q) {  // mirror: row j0 + r, columns i0 + 4cg ..
+    const int r = r0 + 16 * q;
+    const int64_t j = j0 + r, i = i0 + 4 * cg;
+    if (ti < tj && j0 + FT <= n) {
+      const f4u w = {s[4 * cg][r], s[4 * cg + 1][r], s[4 * cg + 2][r], s[4 * cg + 3][r]};
+      *reinterpret_cast<KG f4u*>(gp(d.S) + j * n + i) = w;
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (i + u < n && j < n && i + u < j) gp(d.S)[j * n + i + u] = s[4 * cg + u][r];
+    }
   }
 }
 

@@ -37,7 +37,11 @@ __global__ void __launch_bounds__(256) pack_kernel(const PackDesc* __restrict__ 
 
 // mirror = 0 writes the upper triangle only (the lower triangle of full is left as
 // it was): what a consumer that reads only the upper triangle needs, at half the
-// write traffic.
+// write traffic. A thread takes 4 adjacent columns of 4 rows (16 B per row and
+// operand); tiles off the diagonal and inside the matrix move them as 16-byte
+// accesses (4-byte aligned: packed rows and rows of an order that is not a multiple
+// of 4 start anywhere), the diagonal and edge tiles entry by entry.
+typedef float f4u __attribute__((ext_vector_type(4), aligned(4)));
 __global__ void __launch_bounds__(256) unpack_kernel(const PackDesc* __restrict__ desc,
                                                      const int32_t* __restrict__ begin, int count,
                                                      int mirror) {
@@ -47,31 +51,54 @@ __global__ void __launch_bounds__(256) unpack_kernel(const PackDesc* __restrict_
   int ti, tj;
   upper_tile(blockIdx.x - begin[p], d.nb, ti, tj);
   const int64_t n = d.n;
-  const int c = threadIdx.x & (PT - 1), r0 = threadIdx.x >> 6;
+  const int cg = threadIdx.x & 15, r0 = threadIdx.x >> 4;  // columns 4cg.., rows r0 + 16q
   const int64_t i0 = int64_t(ti) * PT, j0 = int64_t(tj) * PT;
-  constexpr int RQ = PT / 4;  // rows per thread
-  float v[RQ];
+  constexpr int RQ = PT / 16;  // rows per thread
+  const bool inner = ti < tj && j0 + PT <= n;  // every entry of the tile is in the upper triangle
+  f4u v[RQ];
   // all loads of a thread in flight before the first store
 #pragma unroll
   for (int q = 0; q < RQ; ++q) {
-    const int64_t i = i0 + r0 + 4 * q, j = j0 + c;
-    v[q] = (i < n && j < n && i <= j) ? gp(d.packed)[packed_off(i, j, n)] : 0.f;
+    const int64_t i = i0 + r0 + 16 * q, j = j0 + 4 * cg;
+    if (inner) {
+      v[q] = *reinterpret_cast<const KG f4u*>(gp(d.packed) + packed_off(i, j, n));
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        v[q][u] = (i < n && j + u < n && i <= j + u) ? gp(d.packed)[packed_off(i, j + u, n)] : 0.f;
+    }
   }
 #pragma unroll
   for (int q = 0; q < RQ; ++q) {
-    const int64_t i = i0 + r0 + 4 * q, j = j0 + c;
-    if (i < n && j < n && i <= j) gp(d.full)[i * n + j] = v[q];
+    const int64_t i = i0 + r0 + 16 * q, j = j0 + 4 * cg;
+    if (inner) {
+      *reinterpret_cast<KG f4u*>(gp(d.full) + i * n + j) = v[q];
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (i < n && j + u < n && i <= j + u) gp(d.full)[i * n + j + u] = v[q][u];
+    }
   }
   if (!mirror) return;
 #pragma unroll
-  for (int q = 0; q < RQ; ++q) s[r0 + 4 * q][c] = v[q];
+  for (int q = 0; q < RQ; ++q)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) s[r0 + 16 * q][4 * cg + u] = v[q][u];
   __syncthreads();
-  // mirror: full[j][i] = full[i][j] for i < j; this thread writes row j0+r, column i0+c
+  // mirror: full[j][i] = full[i][j] for i < j; this thread writes row j0 + r, columns
+  // i0 + 4cg ..
 #pragma unroll
   for (int q = 0; q < RQ; ++q) {
-    const int r = r0 + 4 * q;
-    const int64_t j = j0 + r, i = i0 + c;
-    if (i < n && j < n && i < j) gp(d.full)[j * n + i] = s[c][r];
+    const int r = r0 + 16 * q;
+    const int64_t j = j0 + r, i = i0 + 4 * cg;
+    if (inner) {
+      const f4u w = {s[4 * cg][r], s[4 * cg + 1][r], s[4 * cg + 2][r], s[4 * cg + 3][r]};
+      *reinterpret_cast<KG f4u*>(gp(d.full) + j * n + i) = w;
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (i + u < n && j < n && i + u < j) gp(d.full)[j * n + i + u] = s[4 * cg + u][r];
+    }
   }
 }
 
