@@ -446,20 +446,20 @@ __global__ void __launch_bounds__(PT) inv_pivot_kernel(const InvDesc* __restrict
 // Two 512-thread blocks share a tile, each taking 64 of its 128 columns (h*64 ..):
 // a block reads only its own columns of V_j and writes W back only over them, so
 // neither block can overwrite what the other has still to read. The block stages its
-// 128x64 half of V_j in LDS; waves 0-3 form Y and waves 4-7 W, each wave a 32x64 slab
-// (rows 32w ..) whose A operand (rows of U_kk^-1 = E^T or of P^-1, read as [k][m])
-// streams from L2 straight into MFMA operand registers one 32-deep chunk ahead. E is
-// lower triangular, so a Y row m only sums k <= m. Blocks b and b+8 (one XCD, so the
+// 128x64 half of V_j in LDS, split into three bf16 planes; waves 0-3 form Y and waves
+// 4-7 W, each wave a 32x64 slab (rows 32w ..) whose A operand (rows of U_kk^-1 = E^T
+// or of P^-1, read as [k][m]) streams from L2 into registers one 16-deep step ahead
+// and is split there; every product runs as the six bf16 MFMA products of the tile
+// engine (fp32 accuracy). E is lower triangular, so a Y row m only sums k <= m. Blocks b and b+8 (one XCD, so the
 // second read of the A operands hits that XCD's L2) take the two halves of one tile.
 // For slot >= 1, blocks from `base` on give step k-1 (panel slot-1) to the diagonal
 // blocks of the group's later pivots k+1.. (block (p, u): matrix p, pivot kg+1+u),
 // which nothing else in the launch reads or writes; Vs is their staging LDS.
 constexpr int PP = 512;        // panel threads
 constexpr int PH = TB / 2;     // columns of V_j per block
-constexpr int VLD = PH + 4;    // LDS pitch of the staged V half
 constexpr int WTP = TB + 1;    // pitch of the transposed W half in LDS
 constexpr int PANEL_LDS = X3_LDS_BYTES / 4;  // floats
-static_assert(PANEL_LDS >= TB * VLD && PANEL_LDS >= PH * WTP, "panel LDS too small");
+static_assert(PANEL_LDS * 4 >= 3 * TB * PH * 2 && PANEL_LDS >= PH * WTP, "panel LDS too small");
 __global__ void __launch_bounds__(PP) __attribute__((amdgpu_waves_per_eu(4, 4)))
 inv_panel_kernel(const InvDesc* __restrict__ desc, const int32_t* __restrict__ begin, int count, int k,
                  int slot, int total, int base) {
@@ -493,71 +493,125 @@ inv_panel_kernel(const InvDesc* __restrict__ desc, const int32_t* __restrict__ b
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<float*>(grp == 0 ? d.Ui : d.P), 0, TB * TB * 4, 0x00020000);
   const int kmax = grp == 0 ? min(bk, mr + 32) : bk;
-  const int nchunk = (kmax + 31) >> 5;  // wave-uniform
+  const int nstep = (kmax + 15) >> 4;  // 16-deep steps, wave-uniform
   const int m = mr + ml;
-  auto load_a = [&](float (&a)[16], int c) {
+  // lane (m, kh) loads A(k, m) for k = 16c + 8kh .. +7, one step ahead of the MFMAs
+  auto load_a = [&](float (&a)[8], int c) {
 #pragma unroll
-    for (int s = 0; s < 16; ++s) {
-      const int kk = 32 * c + 2 * s + kh;
-      const bool ok = kk < bk && m < bk && c < nchunk;
-      a[s] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+    for (int i = 0; i < 8; ++i) {
+      const int kk = 16 * c + 8 * kh + i;
+      const bool ok = kk < bk && m < bk && c < nstep;
+      a[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
           rs, ok ? static_cast<unsigned>(kk * TB + m) * 4u : 0x80000000u, 0, 0));
     }
   };
-  float acur[16], anext[16];
+  float acur[8], anext[8];
   load_a(acur, 0);  // in flight together with the V loads
-  {  // all 16 loads of a thread in flight first (clamped addresses, zero outside)
-    float v[TB * PH / PP];
-    if (j > k) {  // V[r][c] = S[k0 + r][j0 + c]: thread column c = tid % 64, rows tid / 64 + 8q
-      const int c = tid & (PH - 1), ra = tid >> 6;
+  // V (128 x 64) staged as three bf16 planes [k][n] (exact split, see oct_gemm), rows
+  // of 64 swizzled so that the transposing operand reads are conflict-free
+  __bf16* vp = reinterpret_cast<__bf16*>(Vs);
+  constexpr int VPL = TB * PH;  // bf16 per plane
+  auto swz = [](int kk, int nn) { return kk * PH + ((((nn >> 2) ^ (((kk >> 1) & 1) << 3))) << 2); };
+  auto split3 = [](float x, __bf16& h0, __bf16& h1, __bf16& h2) {
+    h0 = static_cast<__bf16>(x);
+    const float r1 = x - static_cast<float>(h0);
+    h1 = static_cast<__bf16>(r1);
+    h2 = static_cast<__bf16>(r1 - static_cast<float>(h1));
+  };
+  if (j > k) {  // V[r][c] = S[k0 + r][j0 + c]: thread 4 columns 4(tid % 16).., rows tid / 16 + 32q
+    const int c4 = 4 * (tid & 15), ra = tid >> 4;
+    float v[4][4];
 #pragma unroll
-      for (int q = 0; q < TB * PH / PP; ++q) {
-        const int r = ra + 8 * q;
-        const float x = gp(d.S)[int64_t(k0 + min(r, bk - 1)) * n + j0 + min(c, bj - 1)];
-        v[q] = (r < bk && c < bj) ? x : 0.f;
+    for (int q = 0; q < 4; ++q) {
+      const int r = ra + 32 * q;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float x = gp(d.S)[int64_t(k0 + min(r, bk - 1)) * n + j0 + min(c4 + u, bj - 1)];
+        v[q][u] = (r < bk && c4 + u < bj) ? x : 0.f;
       }
+    }
 #pragma unroll
-      for (int q = 0; q < TB * PH / PP; ++q) Vs[(ra + 8 * q) * VLD + c] = v[q];
-    } else {  // V[r][c] = S[j0 + c][k0 + r]: read along rows of S, transpose in LDS
-      const int r = tid & (TB - 1), ca = tid >> 7;
+    for (int q = 0; q < 4; ++q) {
+      v4bf p0, p1, p2;
 #pragma unroll
-      for (int q = 0; q < TB * PH / PP; ++q) {
-        const int c = ca + 4 * q;
-        const float x = gp(d.S)[int64_t(j0 + min(c, bj - 1)) * n + k0 + min(r, bk - 1)];
-        v[q] = (r < bk && c < bj) ? x : 0.f;
+      for (int u = 0; u < 4; ++u) {
+        __bf16 h0, h1, h2;
+        split3(v[q][u], h0, h1, h2);
+        p0[u] = h0; p1[u] = h1; p2[u] = h2;
       }
+      const int o = swz(ra + 32 * q, c4);
+      *reinterpret_cast<v4bf*>(vp + o) = p0;
+      *reinterpret_cast<v4bf*>(vp + VPL + o) = p1;
+      *reinterpret_cast<v4bf*>(vp + 2 * VPL + o) = p2;
+    }
+  } else {  // V[r][c] = S[j0 + c][k0 + r]: thread 4 rows 4(tid % 8 + 8q).. of column tid / 8
+    const int c = tid >> 3;
+    float v[4][4];
 #pragma unroll
-      for (int q = 0; q < TB * PH / PP; ++q) Vs[r * VLD + ca + 4 * q] = v[q];
+    for (int q = 0; q < 4; ++q) {
+      const int r4 = 4 * ((tid & 7) + 8 * q);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float x = gp(d.S)[int64_t(j0 + min(c, bj - 1)) * n + k0 + min(r4 + u, bk - 1)];
+        v[q][u] = (r4 + u < bk && c < bj) ? x : 0.f;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r4 = 4 * ((tid & 7) + 8 * q);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        __bf16 h0, h1, h2;
+        split3(v[q][u], h0, h1, h2);
+        const int o = swz(r4 + u, c & ~3) + (c & 3);
+        vp[o] = h0;
+        vp[VPL + o] = h1;
+        vp[2 * VPL + o] = h2;
+      }
     }
   }
   v16f acc0, acc1;
 #pragma unroll
   for (int e = 0; e < 16; ++e) acc0[e] = acc1[e] = 0.f;
   __syncthreads();
-  for (int c = 0; c < nchunk; ++c) {
+  // B operand (8 k of column n = lane % 32 of an n-block) from a plane: two
+  // transposing reads (rows +0 and +4), as in the tile engine
+  auto opnd = [&](const __bf16* plane, int c, int n0) {
+    const int s16 = lane & 15;
+    const int nn = n0 + 16 * ((lane >> 4) & 1) + 4 * (s16 & 3);
+    const int kk = 16 * c + 8 * kh + (s16 >> 2);
+    const v4bf lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4bf*)(plane + swz(kk, nn)));
+    const v4bf hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4bf*)(plane + swz(kk + 4, nn)));
+    return v8bf{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  };
+  for (int c = 0; c < nstep; ++c) {
     load_a(anext, c + 1);
-    float b0[16], b1[16];
+    v8bf a0, a1, a2;
 #pragma unroll
-    for (int s = 0; s < 16; ++s) {
-      const float* br = Vs + (32 * c + 2 * s + kh) * VLD + ml;
-      b0[s] = br[0];
-      b1[s] = br[32];
+    for (int i = 0; i < 8; ++i) {
+      __bf16 h0, h1, h2;
+      split3(acur[i], h0, h1, h2);
+      a0[i] = h0; a1[i] = h1; a2[i] = h2;
     }
+    v8bf b[2][3];
 #pragma unroll
-    for (int s = 0; s < 16; ++s) {
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(acur[s], b0[s], acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(acur[s], b1[s], acc1, 0, 0, 0);
-    }
-    // LDS reads of four k-steps ahead, then per k-step two MFMAs and two reads
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-    for (int s = 0; s < 12; ++s) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      for (int pl = 0; pl < 3; ++pl) b[nb][pl] = opnd(vp + pl * VPL, c, 32 * nb);
+    acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, b[0][0], acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, b[1][0], acc1, 0, 0, 0);
+    acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b[0][1], acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b[1][1], acc1, 0, 0, 0);
+    acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b[0][2], acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b[1][2], acc1, 0, 0, 0);
+    acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b[0][0], acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b[1][0], acc1, 0, 0, 0);
+    acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b[0][1], acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b[1][1], acc1, 0, 0, 0);
+    acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b[0][0], acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b[1][0], acc1, 0, 0, 0);
 #pragma unroll
-    for (int s = 0; s < 16; ++s) acur[s] = anext[s];
+    for (int i = 0; i < 8; ++i) acur[i] = anext[i];
   }
   // accumulator register e of block b: row mr + 8(e/4) + 4kh + e%4, column 32b + ml
   if (grp == 0) {
