@@ -23,13 +23,13 @@ class KfacStep:
     refine_inverse applies one fp64-residual refinement step to every inverse
     (kfac_invert_refine), which keeps a full symmetric copy of each factor.
 
-    side_stream: the inverses of the factors whose order is more than half the
-    largest order (their block sweep is the long tail of the batch, a chain of
-    latency-bound launches that leaves most compute units idle) run on a second
-    stream, together with the preconditioning of their layers, while the caller's
-    stream inverts the rest, preconditions their layers and does the BatchNorm
-    step. The step joins the two streams before it returns; results are the same
-    bits as with one stream."""
+    side_stream: when the largest order is 1024 or more, the inverses of the factors
+    whose order is more than half the largest order (their block sweep is the long
+    tail of the batch, a chain of latency-bound launches that leaves most compute
+    units idle) run on a second stream, together with the preconditioning of their
+    layers, while the caller's stream inverts the rest, preconditions their layers
+    and does the BatchNorm step. The step joins the two streams before it returns;
+    results are the same bits as with one stream."""
 
     def __init__(self, layers, bn_layers=(), device="cuda", damping=1e-3, bn_shift=None,
                  in_dtype=torch.float16, precond_accum="f32", refine_inverse=False, side_stream=True):
@@ -55,7 +55,9 @@ class KfacStep:
         # preconditioned there
         n_max = max(self.n_all) if self.n_all else 0
         long_ = [i for i, n in enumerate(self.n_all) if 2 * n > n_max + 2]
-        if not side_stream or refine_inverse or len(long_) in (0, len(self.n_all)):
+        # a second stream pays off only when the long sweeps are long (8 block steps or
+        # more); below that its events cost more than the overlap gains
+        if not side_stream or refine_inverse or n_max < 1024 or len(long_) in (0, len(self.n_all)):
             long_ = []
         L = len(self.layers)
         self.side = long_
