@@ -15,6 +15,18 @@ import torch
 from . import _lib as K
 
 
+def side_split(n_all, min_order=1024):
+    """Indices of the matrices whose inverses go to the second stream: those of order
+    more than half the largest, when the largest order is at least min_order (a sweep
+    of 8 block steps or more; below that the events cost more than the overlap gains)
+    and the split leaves matrices on both streams; else none."""
+    n_max = max(n_all) if n_all else 0
+    long_ = [i for i, n in enumerate(n_all) if 2 * n > n_max + 2]
+    if n_max < min_order or len(long_) in (0, len(n_all)):
+        return []
+    return long_
+
+
 class KfacStep:
     """Buffers for `layers` (objects with the kfac_layer fields) and `bn_layers`
     (objects with n, hw, c). Tikhonov damping gamma puts sqrt(gamma) on each
@@ -53,12 +65,7 @@ class KfacStep:
         self.packed_all = self.A_packed + self.G_packed
         # matrices (indices into n_all) inverted on the second stream, and the layers
         # preconditioned there
-        n_max = max(self.n_all) if self.n_all else 0
-        long_ = [i for i, n in enumerate(self.n_all) if 2 * n > n_max + 2]
-        # a second stream pays off only when the long sweeps are long (8 block steps or
-        # more); below that its events cost more than the overlap gains
-        if not side_stream or refine_inverse or n_max < 1024 or len(long_) in (0, len(self.n_all)):
-            long_ = []
+        long_ = side_split(self.n_all) if side_stream and not refine_inverse else []
         L = len(self.layers)
         self.side = long_
         self.main = [i for i in range(len(self.n_all)) if i not in long_]
@@ -200,15 +207,19 @@ class KfacStep:
         unpacked = torch.cuda.Event()
         unpacked.record(main)
         side.wait_event(unpacked)
-        self._invert(self.side, self._info_side, self.workspace2, side)
-        self._unpack_some(self.main, main)
-        self._invert(self.main, self._info_main, self.workspace, main)
-        main_inverses = torch.cuda.Event()
-        main_inverses.record(main)
-        self._precondition(self.main_layers, grads, weights, lr, self.workspace, main)
-        self.bn(xhat, bn_gout, ema_decay, bn_params, lr, main)
-        side.wait_event(main_inverses)  # the side layers' other factor
-        self._precondition(self.side_layers, grads, weights, lr, self.workspace2, side)
-        joined = torch.cuda.Event()
-        joined.record(side)
-        main.wait_event(joined)
+        try:
+            self._invert(self.side, self._info_side, self.workspace2, side)
+            self._unpack_some(self.main, main)
+            self._invert(self.main, self._info_main, self.workspace, main)
+            main_inverses = torch.cuda.Event()
+            main_inverses.record(main)
+            self._precondition(self.main_layers, grads, weights, lr, self.workspace, main)
+            self.bn(xhat, bn_gout, ema_decay, bn_params, lr, main)
+            side.wait_event(main_inverses)  # the side layers' other factor
+            self._precondition(self.side_layers, grads, weights, lr, self.workspace2, side)
+        finally:
+            # whatever was issued on the second stream is ordered before the caller's
+            # later work, also when a call above raised
+            joined = torch.cuda.Event()
+            joined.record(side)
+            main.wait_event(joined)
