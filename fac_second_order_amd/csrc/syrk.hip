@@ -82,6 +82,11 @@ struct SyrkDesc {
   int32_t nbr, nbc;      // kind 1: 128-blocks along the rows and the columns of T
   float* csum;
   int8_t tdh[16], tdw[16];
+  // 256x256 tiles (syrk_big_kernel): 256-blocks of the factor (kind 0) or of the rows
+  // and the columns of T (kind 1), and the tiles per row split
+  int32_t nb2, nbr2, nbc2, nt2;
+  int32_t big;  // the problem's items run in syrk_big_kernel
+  int32_t pad2_;
 };
 
 // Value of X[row][c] (0 outside the image or beyond d_core), any input dtype
@@ -124,8 +129,7 @@ struct RowTab {
 
 constexpr int32_t kNoRow = -(1 << 29);
 
-__device__ inline void fill_rowtab(const SyrkDesc& d, RowTab& t, int r0, int r_end, int rows) {
-  const int tid = threadIdx.x;
+__device__ inline void fill_rowtab_at(const SyrkDesc& d, RowTab& t, int r0, int r_end, int rows, int tid) {
   if (tid >= rows) return;
   const int row = r0 + tid;
   if (row >= r_end) {
@@ -149,6 +153,10 @@ __device__ inline void fill_rowtab(const SyrkDesc& d, RowTab& t, int r0, int r_e
   t.lo[tid] = ((n * d.H + ih0) * d.W + iw0) * d.C;
   t.ih[tid] = ih0;
   t.iw[tid] = iw0;
+}
+
+__device__ inline void fill_rowtab(const SyrkDesc& d, RowTab& t, int r0, int r_end, int rows) {
+  fill_rowtab_at(d, t, r0, r_end, rows, threadIdx.x);
 }
 
 // Per-thread column data for its 8 columns [c0, c0+8): tap offsets inside the input
@@ -369,10 +377,13 @@ __device__ __forceinline__ void syrk_rows(const SyrkDesc& d, RowTab* tab, _Float
 }
 
 __global__ void __launch_bounds__(256) syrk_f16_kernel(const SyrkDesc* __restrict__ desc,
-                                                       const int32_t* __restrict__ begin,
-                                                       int count, XcdSegs segs, float decay) {
-  const int v = seg_item(blockIdx.x, segs);
-  if (v < 0) return;
+                                                       const int32_t* __restrict__ begin, int count,
+                                                       int32_t* __restrict__ next_item, int total, float decay) {
+  __shared__ int s_item;  // the next item from the counter, longest items first
+  if (threadIdx.x == 0) s_item = atomicAdd(next_item, 1);
+  __syncthreads();
+  const int v = s_item;
+  if (v >= total) return;
   const int p = find_problem(begin, count, v);
   const SyrkDesc& d = desc[p];
   const int local = v - begin[p];
@@ -469,6 +480,262 @@ __global__ void __launch_bounds__(256) syrk_f16_kernel(const SyrkDesc* __restric
           }
     }
     if (want_col) gp(d.pcol)[(int64_t(s) * d.nb + ti) * ST + tid] = colsum;
+  }
+}
+
+// ---- 256x256 tiles ----------------------------------------------------------------
+// Factors of order 256 and more and the shift products of 3x3 layers with 256 or more
+// channels run on 256x256 output tiles: each 16-byte gather then feeds twice the MFMAs
+// of a 128x128 tile (the 128x128 tiles are bound by issuing their gathers). A block of
+// 512 threads (eight waves, each a 128x64 slab: rows wm*128.., columns wn*64..) stages
+// 64-row chunks of its two 256-column operands (a diagonal tile: 128-row chunks of its
+// one operand, halves in the two operand slots) in double-buffered LDS: the gathers of
+// chunk c+2 and the stores of chunk c+1 run during the MFMAs of chunk c, with one
+// barrier per chunk. The LDS layout and the 8x8 register transpose are those of the
+// 128x128 tiles at a 64-row pitch. Results go out as the 128x128 sub-tiles of the
+// other kernel (packed factor, dense T, or split partials in the same layout), so the
+// split reduction and the shift assembly read them unchanged.
+constexpr int BT = 256;      // big tile edge
+constexpr int KB = 64;       // patch rows per LDS operand buffer (big tiles)
+constexpr int LDB = KB + 8;  // LDS row pitch in halves (144 B)
+constexpr int BT_LDS_HALVES = 2 * 2 * BT * LDB;  // [buffer][operand][column][row]
+
+__device__ __forceinline__ int xoffb(int m, int k) {
+  return m * LDB + ((((k >> 3) ^ (m >> 3) ^ (m >> 4)) & 7) << 3) + (k & 7);
+}
+
+// Row loop of a big tile over patch rows [r_begin, r_end), 16-byte gathers only.
+// mma_on (wave-uniform): the wave's slab is needed; lo_on: its lower 64 rows too (not
+// when they lie below the diagonal of a diagonal sub-tile or past the last row).
+template <bool DIAG>
+__device__ __forceinline__ void big_rows(const SyrkDesc& d, RowTab* tab, _Float16* lds, const ColTab& ct,
+                                         int r_begin, int r_end, bool want_col, bool mma_on, bool lo_on,
+                                         v16f (&acc)[4][2], float& colsum) {
+  constexpr int CK = DIAG ? 2 * KB : KB;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 2, wn = wave & 3;
+  // staging: thread = (operand slot op, column group cg of 8, row group rg of 8)
+  const int op = tid >> 8, cg = tid & 31, rg = (tid >> 5) & 7;
+  const int rrow = (DIAG ? op * KB : 0) + rg * 8;
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(d.src), 0, d.nbytes, 0x00020000);
+  const int H = d.H, W = d.W;
+  auto slot = [&](int b, int o) { return lds + (b * 2 + o) * (BT * LDB); };
+  auto stage = [&](const v8h(&v)[8], int b) {
+    _Float16* X = slot(b, op);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const v8h w = {v[0][e], v[1][e], v[2][e], v[3][e], v[4][e], v[5][e], v[6][e], v[7][e]};
+      *reinterpret_cast<v8h*>(X + xoffb(cg * 8 + e, rg * 8)) = w;
+    }
+  };
+  // one 16-deep step of the slab: the upper 64 rows' operands first, the lower 64
+  // rows' read while the upper MFMAs run (fewer operand registers live at once)
+  auto step = [&](const _Float16* A, const _Float16* B, int ks) {
+    const int ko = ks * 16 + (lane >> 5) * 8;
+    v8h a[2], b[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) b[j] = *reinterpret_cast<const v8h*>(B + xoffb(wn * 64 + 32 * j + (lane & 31), ko));
+#pragma unroll
+    for (int i = 0; i < 2; ++i) a[i] = *reinterpret_cast<const v8h*>(A + xoffb(wm * 128 + 32 * i + (lane & 31), ko));
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+    if (lo_on) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        a[i] = *reinterpret_cast<const v8h*>(A + xoffb(wm * 128 + 64 + 32 * i + (lane & 31), ko));
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[2 + i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[2 + i][j], 0, 0, 0);
+    }
+  };
+  const int nch = (r_end - r_begin + CK - 1) / CK;
+  fill_rowtab(d, tab[0], r_begin, r_end, CK);
+  if (nch > 1) fill_rowtab(d, tab[1], r_begin + CK, r_end, CK);
+  __syncthreads();
+  v8h v[8];
+  gather8_vec<8>(rsrc, H, W, tab[0], rrow, ct, v);
+  stage(v, 0);
+  if (nch > 1) gather8_vec<8>(rsrc, H, W, tab[1], rrow, ct, v);
+  if (nch > 2) fill_rowtab(d, tab[2], r_begin + 2 * CK, r_end, CK);
+  __syncthreads();
+  // The two waves on a SIMD (w and w + 4) take their chunk's work in opposite orders:
+  // waves 0-3 issue their MFMAs first and stage afterwards, waves 4-7 stage first, so
+  // that one wave's staging runs under the other's MFMAs (in the same order, the two
+  // staged together and left the matrix unit idle for half of each chunk). Staging
+  // chunk c+1 and gathering chunk c+2 do not depend on chunk c's products; the barrier
+  // at the end of the chunk orders everything across waves.
+  const bool mfma_first = wave < 4;
+  for (int c = 0; c < nch; ++c) {
+    const int cur = c & 1;
+    const _Float16* A0 = slot(cur, 0);
+    const _Float16* B0 = DIAG ? A0 : slot(cur, 1);
+    auto products = [&]() {
+      if (mma_on) {
+#pragma unroll
+        for (int ks = 0; ks < KB / 16; ++ks) step(A0, B0, ks);
+        if constexpr (DIAG) {
+          const _Float16* A1 = slot(cur, 1);
+#pragma unroll
+          for (int ks = 0; ks < KB / 16; ++ks) step(A1, A1, ks);
+        }
+      }
+    };
+    // chunk c+1 into the other buffer (last read before the previous barrier), chunk
+    // c+2's gathers, and chunk c+3's row table (its slot last read for chunk c)
+    auto staging = [&]() {
+      if (c + 1 < nch) stage(v, cur ^ 1);
+      if (c + 2 < nch) gather8_vec<8>(rsrc, H, W, tab[(c + 2) % 3], rrow, ct, v);
+      if (c + 3 < nch && !mfma_first) fill_rowtab_at(d, tab[c % 3], r_begin + (c + 3) * CK, r_end, CK, tid - 256);
+    };
+#pragma unroll 1
+    for (int half = 0; half < 2; ++half) {  // one copy of each part, taken in the wave's order
+      if ((half == 0) == mfma_first) products();
+      else staging();
+    }
+    if (want_col) {  // column tid of the row operand over the chunk's rows
+#pragma unroll
+      for (int h = 0; h < (DIAG ? 2 : 1); ++h)
+#pragma unroll
+        for (int k = 0; k < KB; k += 8) {
+          const v8h cv = *reinterpret_cast<const v8h*>(slot(cur, h) + tid * LDB + k);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) colsum += static_cast<float>(cv[q]);
+        }
+    }
+    __syncthreads();
+  }
+}
+
+// Items are taken in order from a counter (zeroed by the call's table upload), longest
+// first: a block starts its item when a compute unit frees up, on whichever XCD that
+// is, so the launch balances itself whatever the items' set-up and store costs.
+__global__ void __launch_bounds__(512) syrk_big_kernel(const SyrkDesc* __restrict__ desc,
+                                                       const int32_t* __restrict__ begin, int count,
+                                                       int32_t* __restrict__ next_item, int total, float decay) {
+  __shared__ int s_item;
+  if (threadIdx.x == 0) s_item = atomicAdd(next_item, 1);
+  __syncthreads();
+  const int v = s_item;
+  if (v >= total) return;
+  const int p = find_problem(begin, count, v);
+  const SyrkDesc& d = desc[p];
+  const int local = v - begin[p];
+  const int t = local % d.nt2, s = local / d.nt2;
+  const bool shp = d.kind == 1;
+  int TI, TJ;
+  if (shp) {
+    TI = t % d.nbr2;
+    TJ = t / d.nbr2;
+  } else {
+    upper_tile(t, d.nb2, TI, TJ);
+  }
+  const bool diag = !shp && TI == TJ;
+
+  __shared__ __attribute__((aligned(16))) _Float16 lds[BT_LDS_HALVES];
+  __shared__ RowTab tab[3];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int rlim = shp ? d.c_row : d.d_core, clim = shp ? d.c_col : d.d_core;
+  const int row0 = TI * BT + wm * 128, col0 = TJ * BT + wn * 64;
+  // the slab below the diagonal of a diagonal tile, or past the valid rows or columns
+  const bool mma_on = !(diag && wm == 1 && wn < 2) && row0 < rlim && col0 < clim;
+  // rows 64.. of the slab: below the diagonal of a diagonal sub-tile, or past the rows
+  const bool lo_on = !(diag && wm == (wn >> 1) && (wn & 1) == 0) && row0 + 64 < rlim;
+  ColTab ct;  // the 8 columns this thread stages
+  const int op = diag ? 0 : (tid >> 8);
+  fill_coltab(d, op, (op ? TJ : TI) * BT + (tid & 31) * 8, ct);
+  const int r_begin = s * d.rows_per_split;
+  const int r_end = min(d.R, r_begin + d.rows_per_split);
+  const bool want_col = tid < BT && (shp ? TJ == 0 : diag && d.bias);
+
+  v16f acc[4][2];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
+  float colsum = 0.f;
+  if (diag) big_rows<true>(d, tab, lds, ct, r_begin, r_end, want_col, mma_on, lo_on, acc, colsum);
+  else big_rows<false>(d, tab, lds, ct, r_begin, r_end, want_col, mma_on, lo_on, acc, colsum);
+
+  const int na = lo_on ? 4 : 2;
+  if (d.splits == 1) {
+    if (mma_on) {
+      // Branch-free stores through a raw buffer over the output (under 2^31 bytes, as
+      // the host checks): an entry outside the valid part gets an offset beyond the
+      // buffer's range and is dropped. Row offsets once per accumulator row, in 32 bits.
+      const unsigned lim = shp ? unsigned(d.c_row) * unsigned(d.c_col) : unsigned(d.d) * unsigned(d.d + 1) / 2u;
+      const __amdgpu_buffer_rsrc_t orsrc =
+          __builtin_amdgcn_make_buffer_rsrc(d.out, 0, static_cast<int>(lim * 4u), 0x00020000);
+      const int jl = col0 + (lane & 31);
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        if (a < na)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int i = row0 + a * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+            const unsigned ui = static_cast<unsigned>(i);
+            // T: row i at i * c_col; packed factor: entry (i, j >= i) at i*d - i(i-1)/2 + j - i
+            const unsigned rb = shp ? ui * unsigned(d.c_col) : ui * unsigned(d.d) - (ui * (ui - 1u)) / 2u - ui;
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+              const int j = jl + b * 32;
+              const bool ok = shp ? (i < d.c_row && j < d.c_col) : (i <= j && j < d.d_core);
+              const unsigned off = ok ? (rb + static_cast<unsigned>(j)) * 4u : 0x80000000u;
+              float val = acc[a][b][e];
+              if (!shp) {  // raw sums of T; the factor scaled by 1/R and blended
+                val *= d.inv_r;
+                if (decay != 0.f)
+                  val = decay * __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(orsrc, off, 0, 0)) +
+                        (1.f - decay) * val;
+              }
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), orsrc, off, 0, 0);
+            }
+          }
+    }
+    if (shp) {
+      if (want_col && TI * BT + tid < d.c_row) gp(d.csum)[TI * BT + tid] = colsum;
+    } else if (want_col) {  // the bias column and, from the first tile, the corner
+      const int i = TI * BT + tid;
+      if (i < d.d_core) {
+        const int64_t o = packed_off(i, d.d_core, d.d);
+        gp(d.out)[o] = blend(colsum * d.inv_r, d.out, o, decay);
+      }
+      if (TI == 0 && tid == 0) {
+        const int64_t o = packed_off(d.d_core, d.d_core, d.d);
+        gp(d.out)[o] = blend(d.r_f * d.inv_r, d.out, o, decay);
+      }
+    }
+  } else {
+    // the slab's 128x128 sub-tile (si, sj) in the partial layout of the other kernel
+    const int si = 2 * TI + wm, sj = 2 * TJ + (wn >> 1);
+    const bool valid = shp ? (si < d.nbr && sj < d.nbc) : (si <= sj && sj < d.nb);
+    if (mma_on && valid) {
+      const int t128 = shp ? si + sj * d.nbr : si * d.nb - (si * (si - 1)) / 2 + (sj - si);
+      float* P = d.partial + (int64_t(s) * d.nt + t128) * (ST * ST);
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        if (a < na)
+#pragma unroll
+          for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int r = a * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+              const int cc = (wn & 1) * 64 + b * 32 + (lane & 31);
+              gp(P)[r * ST + cc] = acc[a][b][e];
+            }
+    }
+    if (want_col) {
+      const int bi = 2 * TI + (tid >> 7);
+      if (bi < d.nb) gp(d.pcol)[(int64_t(s) * d.nb + bi) * ST + (tid & (ST - 1))] = colsum;
+    }
   }
 }
 
@@ -829,12 +1096,14 @@ struct SyrkPlan {
   std::vector<Im2Row> im2row;        // patch matrices written out first (dst set at launch)
   std::vector<int32_t> im2row_prob;  // the problem in desc that reads each
   size_t im2row_bytes = 0;
-  std::vector<int32_t> begin;        // work-item offsets
+  std::vector<int32_t> begin;        // work-item offsets (each launch's problems from 0)
   std::vector<int32_t> rbegin, rprob;  // reduce tiles of split problems
-  int64_t items = 0, ritems = 0;
+  int64_t items = 0, ritems = 0;     // items of the 128x128 launch, reduce blocks
+  int64_t items_big = 0;             // items of the 256x256 launch
+  int nbig = 0;                      // problems desc[0, nbig) run on 256x256 tiles
   size_t partial_floats = 0;
   XcdSegs segs{};
-  int64_t seg_max = 0;               // longest XCD segment (items)
+  int64_t seg_max = 0;               // longest XCD segment (items) of the 128x128 launch
   // 3x3 activation factors formed from shift products: one assembly job per layer,
   // its region (sr_floats(C) floats) carved at launch; problem p of kind 1 belongs to
   // job shift_job[p] as sub-problem shift_sub[p]
@@ -898,6 +1167,10 @@ static SyrkDesc make_shift(const kfac_layer& L, int sub) {
   d.nbc = (d.c_col + ST - 1) / ST;
   d.nb = d.nbr;
   d.nt = d.nbr * d.nbc;
+  d.nbr2 = (d.c_row + BT - 1) / BT;
+  d.nbc2 = (d.c_col + BT - 1) / BT;
+  d.nb2 = d.nbr2;
+  d.nt2 = d.nbr2 * d.nbc2;
   return d;
 }
 
@@ -939,6 +1212,8 @@ static SyrkDesc make_problem(const kfac_layer& L, int which) {
   d.d = d.d_core + d.bias;
   d.nb = (d.d_core + ST - 1) / ST;
   d.nt = d.nb * (d.nb + 1) / 2;
+  d.nb2 = (d.d_core + BT - 1) / BT;
+  d.nt2 = d.nb2 * (d.nb2 + 1) / 2;
   d.inv_r = 1.0f / static_cast<float>(d.R);
   d.r_f = static_cast<float>(d.R);
   return d;
@@ -952,18 +1227,43 @@ static double row_cost(const SyrkDesc& d, kfac_dtype dt) {
   return (dt == KFAC_F16 && width % 8 == 0 && (d.d_core % 8 == 0 || d.padded)) ? 1.0 : 4.0;
 }
 
-// Row splits: spread the work so that the launch holds about 2048 work items (a
-// tile over a range of rows; four per block slot of the chip) of about equal cost,
-// and at least 1024 rows each; the split count of a factor never exceeds 256. Equal
-// item costs keep the per-XCD ranges of items (contiguous, equal in count) equal in
-// time. (Measured on ResNet-50 at batch 32: 2048 items 1.80-1.82 ms plus 0.026 ms of
+// Whether a problem's shape suits 256x256 tiles: fp16 inputs read with 16-byte
+// gathers, and a factor of order 256 or more or a shift product of 256 or more
+// channels (fewer would leave most of a 256-row tile idle), with an output under 2^31
+// bytes (32-bit store offsets). The launch also needs the input pointer's 16-byte
+// alignment (SyrkDesc::vec); the split plan depends on the shape only, so that the
+// workspace query bounds every call.
+static bool big_shape(const SyrkDesc& d, kfac_dtype dt) {
+  const int64_t out_floats = d.kind == 1 ? int64_t(d.c_row) * d.c_col : int64_t(d.d) * (d.d + 1) / 2;
+  return dt == KFAC_F16 && row_cost(d, dt) == 1.0 && (d.kind == 1 ? d.c_row : d.d_core) >= BT &&
+         out_floats * 4 < (int64_t(1) << 31);
+}
+
+// Cost of one patch row of a 256x256 tile in units of one patch row of a 128x128
+// tile with 16-byte gathers: four times the products for twice the gathers.
+constexpr double kBigRowCost = 2.0;
+// Set-up, first loads and result stores of a 256x256 item, in patch rows (measured on
+// gfx950: about 6 us per item against about 2 us per 64 rows).
+constexpr double kBigItemRows = 192.0;
+
+// Cost of one patch row of one work item (a tile over a range of rows).
+static double item_row_cost(const SyrkDesc& d, kfac_dtype dt) {
+  return big_shape(d, dt) ? kBigRowCost : row_cost(d, dt);
+}
+static int64_t tiles_per_split(const SyrkDesc& d, kfac_dtype dt) { return big_shape(d, dt) ? d.nt2 : d.nt; }
+
+// Row splits: spread the work so that the launches hold about 2048 work items (a
+// tile over a range of rows) of about equal cost, and at least 1024 rows each; the
+// split count of a factor never exceeds 256. Equal item costs keep the per-XCD
+// ranges of items (contiguous, equal in count) equal in time. (Measured on ResNet-50
+// at batch 32 with 128x128 tiles only: 2048 items 1.80-1.82 ms plus 0.026 ms of
 // split reduction, 4096 items 1.83-1.87 + 0.036, 8192 items 1.81-1.82 + 0.116.)
 static void plan_splits(std::vector<SyrkDesc>& ds, kfac_dtype dt) {
   double work = 0;
-  for (auto& d : ds) work += double(d.nt) * d.R * row_cost(d, dt);
+  for (auto& d : ds) work += double(tiles_per_split(d, dt)) * d.R * item_row_cost(d, dt);
   const double per_cost = work / 2048.0;
   for (auto& d : ds) {
-    double per = per_cost / row_cost(d, dt);
+    double per = per_cost / item_row_cost(d, dt);
     if (per < 1024) per = 1024;
     int64_t splits = static_cast<int64_t>((d.R + per - 1) / per);
     if (splits < 1) splits = 1;
@@ -975,14 +1275,21 @@ static void plan_splits(std::vector<SyrkDesc>& ds, kfac_dtype dt) {
   }
 }
 
+// Work-item offsets: the problems of the big-tile launch (desc[0, nbig)) and those of
+// the 128x128 launch (desc[nbig, ..)) are each numbered from 0.
 static void finish_plan(SyrkPlan& pl) {
   pl.begin.clear(); pl.rbegin.clear(); pl.rprob.clear();
-  pl.items = pl.ritems = 0;
+  pl.items = pl.items_big = pl.ritems = 0;
   pl.partial_floats = 0;
   for (size_t p = 0; p < pl.desc.size(); ++p) {
     SyrkDesc& d = pl.desc[p];
-    pl.begin.push_back(static_cast<int32_t>(pl.items));
-    pl.items += int64_t(d.splits) * d.nt;
+    if (d.big) {
+      pl.begin.push_back(static_cast<int32_t>(pl.items_big));
+      pl.items_big += int64_t(d.splits) * d.nt2;
+    } else {
+      pl.begin.push_back(static_cast<int32_t>(pl.items));
+      pl.items += int64_t(d.splits) * d.nt;
+    }
     if (d.splits > 1) {
       pl.rbegin.push_back(static_cast<int32_t>(pl.ritems));
       pl.rprob.push_back(static_cast<int32_t>(p));
@@ -994,7 +1301,7 @@ static void finish_plan(SyrkPlan& pl) {
 
 static size_t syrk_ws_bytes(const SyrkPlan& pl) {
   const size_t np = pl.desc.size(), nr = pl.rprob.size(), nj = pl.jobs.size();
-  return align256(sizeof(SyrkDesc) * np) + align256(sizeof(int32_t) * np) +
+  return align256(sizeof(SyrkDesc) * np) + align256(sizeof(int32_t) * np) + align256(sizeof(int32_t) * 2) +
          2 * align256(sizeof(int32_t) * (nr ? nr : 1)) + align256(sizeof(float) * pl.partial_floats) +
          pl.im2row_bytes + align256(sizeof(ShiftAsm) * (nj ? nj : 1)) + align256(sizeof(int32_t) * (nj ? nj : 1)) +
          sizeof(float) * pl.shift_floats;
@@ -1119,16 +1426,25 @@ static kfac_status build_plan(const kfac_layer* L, int32_t count, kfac_dtype dt,
     pl.shift_job.push_back(sub >= 0 ? job_of_layer[l] : -1);
     pl.shift_sub.push_back(sub);
   }
-  // Problems in decreasing cost per item (stable): each problem's items stay together
-  // (its tiles over one row range are neighbours, sharing those rows in L2), and each
-  // XCD segment starts with its longest items.
-  auto item_cost = [&](const SyrkDesc& d) {  // per-row cost as in row_cost, now that vec is known
-    return double(d.rows_per_split) * ((dt == KFAC_F16 && d.vec) ? 1.0 : 4.0);
+  // The big-tile problems first, then the rest; within each launch, problems in
+  // decreasing cost per item (stable): each problem's items stay together (its tiles
+  // over one row range are neighbours, sharing those rows in L2), and each XCD segment
+  // starts with its longest items.
+  for (SyrkDesc& d : pl.desc) d.big = (big_shape(d, dt) && d.vec) ? 1 : 0;
+  // cost of an item of `rows` rows (per-row cost as in item_row_cost, now that vec is
+  // known); a 256x256 item also costs about kBigItemRows rows' worth of set-up, first
+  // loads and result stores, so that XCD segments of short items are not overfilled
+  auto cost_of = [&](const SyrkDesc& d, int rows) {
+    return d.big ? (double(rows) + kBigItemRows) * kBigRowCost
+                 : double(rows) * ((dt == KFAC_F16 && d.vec) ? 1.0 : 4.0);
   };
+  auto item_cost = [&](const SyrkDesc& d) { return cost_of(d, d.rows_per_split); };
   std::vector<int> order(pl.desc.size());
   for (size_t q = 0; q < order.size(); ++q) order[q] = static_cast<int>(q);
-  std::stable_sort(order.begin(), order.end(),
-                   [&](int a, int b) { return item_cost(pl.desc[a]) > item_cost(pl.desc[b]); });
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) {
+    if (pl.desc[a].big != pl.desc[b].big) return pl.desc[a].big > pl.desc[b].big;
+    return item_cost(pl.desc[a]) > item_cost(pl.desc[b]);
+  });
   {
     std::vector<SyrkDesc> ds(order.size());
     std::vector<int32_t> sj(order.size()), ss(order.size());
@@ -1141,47 +1457,59 @@ static kfac_status build_plan(const kfac_layer* L, int32_t count, kfac_dtype dt,
     pl.shift_job.swap(sj);
     pl.shift_sub.swap(ss);
   }
+  pl.nbig = 0;
+  while (pl.nbig < static_cast<int>(pl.desc.size()) && pl.desc[pl.nbig].big) ++pl.nbig;
   pl.im2row_prob.assign(pl.im2row.size(), 0);
   for (size_t p = 0; p < pl.desc.size(); ++p)
     if (pl.desc[p].padded) pl.im2row_prob[pl.desc[p].padded - 1] = static_cast<int32_t>(p);
   finish_plan(pl);
-  if (pl.items >= (int64_t(1) << 31) - 8 || pl.ritems >= (int64_t(1) << 31) || pl.jtiles >= (int64_t(1) << 31))
+  if (pl.items >= (int64_t(1) << 31) - 8 || pl.items_big >= (int64_t(1) << 31) - 8 ||
+      pl.ritems >= (int64_t(1) << 31) || pl.jtiles >= (int64_t(1) << 31))
     return fail(KFAC_ERR_INVALID, "too many tiles");
-  // XCD segments of about equal cost (rows x per-row cost over the items in order)
-  double total = 0;
-  for (const SyrkDesc& d : pl.desc) total += item_cost(d) * d.nt * (double(d.R) / d.rows_per_split);
-  int64_t item = 0;
-  double acc = 0;
-  int x = 0;
-  pl.segs.begin[0] = 0;
-  for (const SyrkDesc& d : pl.desc) {
-    for (int sp = 0; sp < d.splits; ++sp) {
-      const int rows = std::min(d.rows_per_split, d.R - sp * d.rows_per_split);
-      const double c = item_cost(d) * (double(rows) / d.rows_per_split);
-      int64_t t = 0;
-      while (t < d.nt) {  // a segment starts at the first item reached with acc >= its share
-        int64_t k = d.nt - t;
-        if (x < 7) {
-          const double thr = total * (x + 1) / 8;
-          if (acc >= thr) {
-            pl.segs.begin[++x] = static_cast<int32_t>(item);
-            continue;
+  // XCD segments of about equal cost (rows x per-row cost over the items in order),
+  // for each launch over its own problems
+  auto make_segs = [&](int p0, int p1, XcdSegs& segs, int64_t& seg_max) {
+    double total = 0;
+    for (int p = p0; p < p1; ++p) {
+      const SyrkDesc& d = pl.desc[p];
+      for (int sp = 0; sp < d.splits; ++sp)
+        total += cost_of(d, std::min(d.rows_per_split, d.R - sp * d.rows_per_split)) * (d.big ? d.nt2 : d.nt);
+    }
+    int64_t item = 0;
+    double acc = 0;
+    int x = 0;
+    segs.begin[0] = 0;
+    for (int p = p0; p < p1; ++p) {
+      const SyrkDesc& d = pl.desc[p];
+      const int64_t nt = d.big ? d.nt2 : d.nt;
+      for (int sp = 0; sp < d.splits; ++sp) {
+        const double c = cost_of(d, std::min(d.rows_per_split, d.R - sp * d.rows_per_split));
+        int64_t t = 0;
+        while (t < nt) {  // a segment starts at the first item reached with acc >= its share
+          int64_t k = nt - t;
+          if (x < 7) {
+            const double thr = total * (x + 1) / 8;
+            if (acc >= thr) {
+              segs.begin[++x] = static_cast<int32_t>(item);
+              continue;
+            }
+            k = std::min<int64_t>(k, std::max<int64_t>(1, static_cast<int64_t>(std::ceil((thr - acc) / c))));
           }
-          k = std::min<int64_t>(k, std::max<int64_t>(1, static_cast<int64_t>(std::ceil((thr - acc) / c))));
+          acc += double(k) * c;
+          item += k;
+          t += k;
         }
-        acc += double(k) * c;
-        item += k;
-        t += k;
       }
     }
-  }
-  while (x < 7) pl.segs.begin[++x] = static_cast<int32_t>(item);
-  pl.seg_max = 0;
-  for (int k = 0; k < 8; ++k) {
-    const int64_t e = k < 7 ? pl.segs.begin[k + 1] : pl.items;
-    pl.segs.len[k] = static_cast<int32_t>(e - pl.segs.begin[k]);
-    pl.seg_max = std::max<int64_t>(pl.seg_max, pl.segs.len[k]);
-  }
+    while (x < 7) segs.begin[++x] = static_cast<int32_t>(item);
+    seg_max = 0;
+    for (int k = 0; k < 8; ++k) {
+      const int64_t e = k < 7 ? segs.begin[k + 1] : item;
+      segs.len[k] = static_cast<int32_t>(e - segs.begin[k]);
+      seg_max = std::max<int64_t>(seg_max, segs.len[k]);
+    }
+  };
+  make_segs(pl.nbig, static_cast<int>(pl.desc.size()), pl.segs, pl.seg_max);
   return KFAC_OK;
 }
 
@@ -1222,6 +1550,7 @@ extern "C" kfac_status kfac_factors(const kfac_layer* layers, int32_t count, kfa
   Carver cv(workspace);
   SyrkDesc* d_desc = cv.take<SyrkDesc>(np);
   int32_t* d_begin = cv.take<int32_t>(np);
+  int32_t* d_next = cv.take<int32_t>(2);  // item counters of the 256x256 and 128x128 launches
   int32_t* d_rbegin = cv.take<int32_t>(nr ? nr : 1);
   int32_t* d_rprob = cv.take<int32_t>(nr ? nr : 1);
   const int nj = static_cast<int>(pl.jobs.size());
@@ -1260,8 +1589,10 @@ extern "C" kfac_status kfac_factors(const kfac_layer* layers, int32_t count, kfa
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   TableUpload tu;
+  const int32_t zero[2] = {0, 0};
   tu.add(d_desc, pl.desc.data(), sizeof(SyrkDesc) * np);
   tu.add(d_begin, pl.begin.data(), sizeof(int32_t) * np);
+  tu.add(d_next, zero, sizeof(zero));
   if (nr) {
     tu.add(d_rbegin, pl.rbegin.data(), sizeof(int32_t) * nr);
     tu.add(d_rprob, pl.rprob.data(), sizeof(int32_t) * nr);
@@ -1276,13 +1607,23 @@ extern "C" kfac_status kfac_factors(const kfac_layer* layers, int32_t count, kfa
     KFAC_LAUNCH(K_SYRK, im2row_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, s, g, total);
     KFAC_CHECK_LAUNCH("im2row_kernel");
   }
-  const unsigned grid = static_cast<unsigned>(8 * pl.seg_max);
-  if (in_dtype == KFAC_F16) {
-    KFAC_LAUNCH(K_SYRK, syrk_f16_kernel, dim3(grid), dim3(256), 0, s, d_desc, d_begin, np, pl.segs, ema_decay);
-  } else {
-    KFAC_LAUNCH(K_SYRK, syrk_f32_kernel, dim3(grid), dim3(256), 0, s, d_desc, d_begin, np, pl.segs, ema_decay);
+  const int nbig = pl.nbig, nsmall = np - nbig;
+  if (pl.items_big > 0) {  // problems desc[0, nbig) on 256x256 tiles, one block per item
+    KFAC_LAUNCH(K_SYRK, syrk_big_kernel, dim3(static_cast<unsigned>(pl.items_big)), dim3(512), 0, s, d_desc,
+                d_begin, nbig, d_next, static_cast<int>(pl.items_big), ema_decay);
+    KFAC_CHECK_LAUNCH("syrk_big_kernel");
   }
-  KFAC_CHECK_LAUNCH("syrk kernel");
+  if (nsmall > 0 && pl.items > 0) {  // the rest on 128x128 tiles
+    const unsigned grid = static_cast<unsigned>(8 * pl.seg_max);
+    if (in_dtype == KFAC_F16) {  // one block per item, from the counter
+      KFAC_LAUNCH(K_SYRK, syrk_f16_kernel, dim3(static_cast<unsigned>(pl.items)), dim3(256), 0, s, d_desc + nbig,
+                  d_begin + nbig, nsmall, d_next + 1, static_cast<int>(pl.items), ema_decay);
+    } else {
+      KFAC_LAUNCH(K_SYRK, syrk_f32_kernel, dim3(grid), dim3(256), 0, s, d_desc + nbig, d_begin + nbig, nsmall,
+                  pl.segs, ema_decay);
+    }
+    KFAC_CHECK_LAUNCH("syrk kernel");
+  }
   if (nr) {
     KFAC_LAUNCH(K_SYRK_REDUCE, syrk_reduce_kernel, dim3(static_cast<unsigned>(pl.ritems)), dim3(256), 0, s,
                 d_desc, d_rbegin, d_rprob, nr, ema_decay);

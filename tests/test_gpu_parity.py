@@ -157,7 +157,9 @@ def test_factors_element_gathers(kfac_gpu):
     gather form (3x3, strided 1x1) and the row form (1x1 stride 1, G factors)."""
     layers = [synth.Layer("c3x3", 3, 9, 7, 16, 9, 7, 24, 3, 3, 1, 1, 1, 1, 1),
               synth.Layer("c1x1s2", 2, 9, 9, 24, 5, 5, 16, 1, 1, 2, 2, 0, 0, 1),
-              synth.Layer("c1x1", 2, 6, 6, 32, 6, 6, 8, 1, 1, 1, 1, 0, 0, 0)]
+              synth.Layer("c1x1", 2, 6, 6, 32, 6, 6, 8, 1, 1, 1, 1, 0, 0, 0),
+              # shaped for 256x256 tiles, which need 16-byte gathers: 128x128 tiles instead
+              synth.Layer("c1x1_256", 2, 6, 6, 256, 6, 6, 264, 1, 1, 1, 1, 0, 0, 1)]
     rng = synth.layer_rng(1012, 0)
     act = [synth.relu_normal_f16(rng, l.act_shape) for l in layers]
     gout = [synth.normal_f16(rng, l.gout_shape, 0.1) for l in layers]
@@ -220,6 +222,61 @@ def test_factors_shift_products_edge_cases(kfac_gpu):
         inv_r = np.float32(1.0) / np.float32(X.shape[0])
         expect = oracle.pack_upper(oracle.gram(X)).astype(np.float32) * inv_r
         assert np.array_equal(host(A[l]), expect), layer.name
+
+
+# Problems of 256 or more columns (factors of order >= 256, shift products of 3x3 layers
+# with >= 256 channels) run on 256x256 tiles: direct and split-reduced results, the bias
+# column, rows and columns that end inside a tile (264, 296, 320, 272 channels), both
+# gather forms (rows, strided 1x1 gathers) and tiles off the diagonal.
+BIG_TILE_LAYERS = [
+    synth.Layer("c3x3_256", 2, 8, 8, 256, 8, 8, 256, 3, 3, 1, 1, 1, 1, 1),         # A 2305, G 256
+    synth.Layer("c3x3_264_split", 40, 8, 8, 264, 8, 8, 24, 3, 3, 1, 1, 1, 1, 1),   # R = 2560
+    synth.Layer("c1x1_296_split", 48, 8, 8, 296, 8, 8, 320, 1, 1, 1, 1, 0, 0, 1),  # R = 3072
+    synth.Layer("c1x1s2_256", 4, 10, 10, 256, 5, 5, 272, 1, 1, 2, 2, 0, 0, 1),
+    synth.Layer("fc_512", 64, 1, 1, 512, 1, 1, 264, 1, 1, 1, 1, 0, 0, 0),
+]
+
+
+def test_factors_big_tiles_integer_bitexact(kfac_gpu):
+    """[OTUNYM] eq. (5) through the 256x256-tile path with inputs in {-2..2}: every sum
+    is an exact integer, so each output is fp32(sum) * fp32(1/R), bit for bit."""
+    rng = synth.layer_rng(1014, 0)
+    act = [rng.integers(-2, 3, size=l.act_shape).astype(np.float16) for l in BIG_TILE_LAYERS]
+    gout = [rng.integers(-2, 3, size=l.gout_shape).astype(np.float16) for l in BIG_TILE_LAYERS]
+    say("kfac_factors 256x256 tiles, integer inputs", [l.name for l in BIG_TILE_LAYERS])
+    A, G = _run_factors(kfac_gpu, BIG_TILE_LAYERS, act, gout)
+    for l, layer in enumerate(BIG_TILE_LAYERS):
+        X = oracle.im2col_nhwc(act[l], layer.kh, layer.kw, layer.sh, layer.sw, layer.ph, layer.pw,
+                               layer.bias)
+        Gam = gout[l].astype(np.float64).reshape(-1, layer.c_out)
+        inv_r = np.float32(1.0) / np.float32(X.shape[0])
+        for which, got, S in (("A", A[l], oracle.gram(X)), ("G", G[l], oracle.gram(Gam))):
+            expect = oracle.pack_upper(S).astype(np.float32) * inv_r
+            g = host(got)
+            bad = int(np.count_nonzero(g != expect))
+            say(f"  {layer.name} {which}: {bad} of {g.size} entries differ")
+            assert bad == 0, (layer.name, which)
+
+
+def test_factors_big_tiles_fp16(kfac_gpu):
+    """The same layers with fp16 ReLU activations and Gaussian output gradients: relF
+    against the fp64 oracle, and bitwise identical results from a second call."""
+    rng = synth.layer_rng(1015, 0)
+    act = [synth.relu_normal_f16(rng, l.act_shape) for l in BIG_TILE_LAYERS]
+    gout = [synth.normal_f16(rng, l.gout_shape, 0.1) for l in BIG_TILE_LAYERS]
+    say("kfac_factors 256x256 tiles, fp16")
+    A, G = _run_factors(kfac_gpu, BIG_TILE_LAYERS, act, gout)
+    A2, G2 = _run_factors(kfac_gpu, BIG_TILE_LAYERS, act, gout)
+    for x, y in zip(A + G, A2 + G2):
+        assert torch.equal(x, y)
+    for l, layer in enumerate(BIG_TILE_LAYERS):
+        Ar, Gr = _oracle_factors(layer, act[l], gout[l])
+        ea = relF(host(A[l]), oracle.pack_upper(Ar))
+        eg = relF(host(G[l]), oracle.pack_upper(Gr))
+        say(f"  {layer.name}: A relF {ea:.2e}  G relF {eg:.2e}")
+        # fp16 products are exact in fp32; fp32 sums of R <= 3072 terms, typically
+        # ~sqrt(R) u = 3e-6 relative: well inside the stated 1e-2 bar
+        assert ea <= 1e-4 and eg <= 1e-4, layer.name
 
 
 def test_factors_fp32_fc_and_kronecker(kfac_gpu):
