@@ -433,35 +433,46 @@ __global__ void __launch_bounds__(256) syrk_f16_kernel(const SyrkDesc* __restric
   }
 
   if (d.splits == 1) {
+    // the descriptor's fields copied first (the stores could alias the table, which
+    // the compiler would otherwise reload after every store); row offsets per row
+    const int c_row = d.c_row, c_col = d.c_col, d_core = d.d_core;
+    const int64_t dd = d.d;
+    const float inv_r = d.inv_r;
+    KG float* const out = gp(d.out);
+    const int jb = tj * ST + wn * 64 + (lane & 31);
     if (shp) {  // raw sums into T, rows < C, columns < ntap * C
       if (!idle) {
 #pragma unroll
         for (int a = 0; a < 2; ++a)
 #pragma unroll
-          for (int b = 0; b < 2; ++b)
+          for (int e = 0; e < 16; ++e) {
+            const int i = ti * ST + wm * 64 + a * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+            KG float* const row = out + int64_t(i) * c_col;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-              const int i = ti * ST + wm * 64 + a * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-              const int j = tj * ST + wn * 64 + b * 32 + (lane & 31);
-              if (i < d.c_row && j < d.c_col) gp(d.out)[int64_t(i) * d.c_col + j] = acc[a][b][e];
+            for (int b = 0; b < 2; ++b) {
+              const int j = jb + b * 32;
+              if (i < c_row && j < c_col) row[j] = acc[a][b][e];
             }
+          }
       }
-      if (want_col && ti * ST + tid < d.c_row) gp(d.csum)[ti * ST + tid] = colsum;
+      if (want_col && ti * ST + tid < c_row) gp(d.csum)[ti * ST + tid] = colsum;
     } else {
       if (!skip) {
 #pragma unroll
         for (int a = 0; a < 2; ++a)
 #pragma unroll
-          for (int b = 0; b < 2; ++b)
+          for (int e = 0; e < 16; ++e) {
+            const int i = ti * ST + wm * 64 + a * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+            KG float* const row = out + (int64_t(i) * dd - (int64_t(i) * (i - 1)) / 2 - i);  // row[j] for j >= i
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-              const int i = ti * ST + wm * 64 + a * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-              const int j = tj * ST + wn * 64 + b * 32 + (lane & 31);
-              if (i <= j && j < d.d_core) {
-                const int64_t o = packed_off(i, j, d.d);
-                gp(d.out)[o] = blend(acc[a][b][e] * d.inv_r, d.out, o, decay);
+            for (int b = 0; b < 2; ++b) {
+              const int j = jb + b * 32;
+              if (i <= j && j < d_core) {
+                const float x = acc[a][b][e] * inv_r;
+                row[j] = decay != 0.f ? decay * row[j] + (1.f - decay) * x : x;
               }
             }
+          }
       }
       if (diag && d.bias) write_bias_direct(d, ti, t, colsum, decay);
     }
@@ -563,57 +574,57 @@ __device__ __forceinline__ void big_rows(const SyrkDesc& d, RowTab* tab, _Float1
   if (nch > 1) gather8_vec<8>(rsrc, H, W, tab[1], rrow, ct, v);
   if (nch > 2) fill_rowtab(d, tab[2], r_begin + 2 * CK, r_end, CK);
   __syncthreads();
-  // The two waves on a SIMD (w and w + 4) take their chunk's work in opposite orders:
-  // waves 0-3 issue their MFMAs first and stage afterwards, waves 4-7 stage first, so
-  // that one wave's staging runs under the other's MFMAs (in the same order, the two
-  // staged together and left the matrix unit idle for half of each chunk). Staging
-  // chunk c+1 and gathering chunk c+2 do not depend on chunk c's products; the barrier
-  // at the end of the chunk orders everything across waves.
-  const bool mfma_first = wave < 4;
+  // Each 16-deep step's MFMAs are followed by a share of the staging, which runs while
+  // the matrix unit works on them (and the other wave on the SIMD fills the gaps): after
+  // step 0 and 1 the stores of chunk c+1 (columns 0-3, 4-7 of each thread's 8x8 block)
+  // into the other buffer, last read before the previous barrier; after step 2 the
+  // gathers of chunk c+2; after step 3 every wave's share of chunk c+3's row table (its
+  // slot last read for chunk c); after the last step the column sums of the row operand
+  // (a column per thread, half the chunk's rows each). Nothing here depends on chunk c's
+  // products; the barrier at the end of the chunk orders everything across waves.
+  constexpr int NS = DIAG ? 8 : 4;  // 16-deep steps per chunk
+  const int tl = lane < CK / 8 ? wave * (CK / 8) + lane : CK;  // this thread's table entry (CK: none)
+  const int chalf = tid >> 8;
   for (int c = 0; c < nch; ++c) {
     const int cur = c & 1;
-    const _Float16* A0 = slot(cur, 0);
-    const _Float16* B0 = DIAG ? A0 : slot(cur, 1);
-    auto products = [&]() {
-      if (mma_on) {
+    const bool st = c + 1 < nch, ga = c + 2 < nch, tb = c + 3 < nch;
+    _Float16* Xs = slot(cur ^ 1, op);
 #pragma unroll
-        for (int ks = 0; ks < KB / 16; ++ks) step(A0, B0, ks);
-        if constexpr (DIAG) {
-          const _Float16* A1 = slot(cur, 1);
+    for (int ks = 0; ks < NS; ++ks) {
+      const _Float16* A = slot(cur, (DIAG && ks >= 4) ? 1 : 0);
+      const _Float16* B = DIAG ? A : slot(cur, 1);
+      if (mma_on) step(A, B, ks & 3);
+      __builtin_amdgcn_sched_barrier(0);
+      if ((ks == 0 || ks == 1) && st) {
 #pragma unroll
-          for (int ks = 0; ks < KB / 16; ++ks) step(A1, A1, ks);
+        for (int e = 4 * ks; e < 4 * ks + 4; ++e) {
+          const v8h w = {v[0][e], v[1][e], v[2][e], v[3][e], v[4][e], v[5][e], v[6][e], v[7][e]};
+          *reinterpret_cast<v8h*>(Xs + xoffb(cg * 8 + e, rg * 8)) = w;
         }
       }
-    };
-    // chunk c+1 into the other buffer (last read before the previous barrier), chunk
-    // c+2's gathers, and chunk c+3's row table (its slot last read for chunk c)
-    auto staging = [&]() {
-      if (c + 1 < nch) stage(v, cur ^ 1);
-      if (c + 2 < nch) gather8_vec<8>(rsrc, H, W, tab[(c + 2) % 3], rrow, ct, v);
-      if (c + 3 < nch && !mfma_first) fill_rowtab_at(d, tab[c % 3], r_begin + (c + 3) * CK, r_end, CK, tid - 256);
-    };
-#pragma unroll 1
-    for (int half = 0; half < 2; ++half) {  // one copy of each part, taken in the wave's order
-      if ((half == 0) == mfma_first) products();
-      else staging();
-    }
-    if (want_col) {  // column tid of the row operand over the chunk's rows
+      if (ks == 2 && ga) gather8_vec<8>(rsrc, H, W, tab[(c + 2) % 3], rrow, ct, v);
+      if (ks == 3 && tb) fill_rowtab_at(d, tab[c % 3], r_begin + (c + 3) * CK, r_end, CK, tl);
+      if (ks == NS - 1 && want_col) {
+        const _Float16* X = slot(cur, DIAG ? chalf : 0) + (tid & (BT - 1)) * LDB + (DIAG ? 0 : 32 * chalf);
 #pragma unroll
-      for (int h = 0; h < (DIAG ? 2 : 1); ++h)
-#pragma unroll
-        for (int k = 0; k < KB; k += 8) {
-          const v8h cv = *reinterpret_cast<const v8h*>(slot(cur, h) + tid * LDB + k);
+        for (int k = 0; k < (DIAG ? KB : KB / 2); k += 8) {
+          const v8h cv = *reinterpret_cast<const v8h*>(X + k);
 #pragma unroll
           for (int q = 0; q < 8; ++q) colsum += static_cast<float>(cv[q]);
         }
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
   }
+  if (want_col) {  // threads t and t + 256 summed the two halves of column t
+    float* part = reinterpret_cast<float*>(tab);
+    if (tid >= BT) part[tid - BT] = colsum;
+    __syncthreads();
+    if (tid < BT) colsum += part[tid];
+  }
 }
 
-// Items are taken in order from a counter (zeroed by the call's table upload), longest
-// first: a block starts its item when a compute unit frees up, on whichever XCD that
-// is, so the launch balances itself whatever the items' set-up and store costs.
 __global__ void __launch_bounds__(512) syrk_big_kernel(const SyrkDesc* __restrict__ desc,
                                                        const int32_t* __restrict__ begin, int count,
                                                        int32_t* __restrict__ next_item, int total, float decay) {
@@ -652,7 +663,8 @@ __global__ void __launch_bounds__(512) syrk_big_kernel(const SyrkDesc* __restric
   fill_coltab(d, op, (op ? TJ : TI) * BT + (tid & 31) * 8, ct);
   const int r_begin = s * d.rows_per_split;
   const int r_end = min(d.R, r_begin + d.rows_per_split);
-  const bool want_col = tid < BT && (shp ? TJ == 0 : diag && d.bias);
+  const bool want_cols = shp ? TJ == 0 : diag && d.bias;  // the block forms column sums
+  const bool want_col = tid < BT && want_cols;               // this thread holds column tid's
 
   v16f acc[4][2];
 #pragma unroll
@@ -662,8 +674,8 @@ __global__ void __launch_bounds__(512) syrk_big_kernel(const SyrkDesc* __restric
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
   float colsum = 0.f;
-  if (diag) big_rows<true>(d, tab, lds, ct, r_begin, r_end, want_col, mma_on, lo_on, acc, colsum);
-  else big_rows<false>(d, tab, lds, ct, r_begin, r_end, want_col, mma_on, lo_on, acc, colsum);
+  if (diag) big_rows<true>(d, tab, lds, ct, r_begin, r_end, want_cols, mma_on, lo_on, acc, colsum);
+  else big_rows<false>(d, tab, lds, ct, r_begin, r_end, want_cols, mma_on, lo_on, acc, colsum);
 
   const int na = lo_on ? 4 : 2;
   if (d.splits == 1) {
@@ -671,34 +683,52 @@ __global__ void __launch_bounds__(512) syrk_big_kernel(const SyrkDesc* __restric
       // Branch-free stores through a raw buffer over the output (under 2^31 bytes, as
       // the host checks): an entry outside the valid part gets an offset beyond the
       // buffer's range and is dropped. Row offsets once per accumulator row, in 32 bits.
-      const unsigned lim = shp ? unsigned(d.c_row) * unsigned(d.c_col) : unsigned(d.d) * unsigned(d.d + 1) / 2u;
+      // The descriptor's fields are copied first: the stores could alias the table, so
+      // the compiler would otherwise reload them after every store.
+      const int c_row = d.c_row, c_col = d.c_col, d_core = d.d_core, dd = d.d;
+      const float inv_r = d.inv_r;
+      const unsigned lim = shp ? unsigned(c_row) * unsigned(c_col) : unsigned(dd) * unsigned(dd + 1) / 2u;
       const __amdgpu_buffer_rsrc_t orsrc =
           __builtin_amdgcn_make_buffer_rsrc(d.out, 0, static_cast<int>(lim * 4u), 0x00020000);
       const int jl = col0 + (lane & 31);
+      // entry (a, b, e) of the slab: row i = i0 + a*32 + 8*(e/4) + e%4, column jl + b*32
+      const int i0 = row0 + 4 * (lane >> 5);
+      auto each = [&](auto&& put) {
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
-        if (a < na)
+        for (int a = 0; a < 4; ++a)
+          if (a < na)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int i = row0 + a * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-            const unsigned ui = static_cast<unsigned>(i);
-            // T: row i at i * c_col; packed factor: entry (i, j >= i) at i*d - i(i-1)/2 + j - i
-            const unsigned rb = shp ? ui * unsigned(d.c_col) : ui * unsigned(d.d) - (ui * (ui - 1u)) / 2u - ui;
+            for (int e = 0; e < 16; ++e) {
+              const int i = i0 + a * 32 + 8 * (e >> 2) + (e & 3);
 #pragma unroll
-            for (int b = 0; b < 2; ++b) {
-              const int j = jl + b * 32;
-              const bool ok = shp ? (i < d.c_row && j < d.c_col) : (i <= j && j < d.d_core);
-              const unsigned off = ok ? (rb + static_cast<unsigned>(j)) * 4u : 0x80000000u;
-              float val = acc[a][b][e];
-              if (!shp) {  // raw sums of T; the factor scaled by 1/R and blended
-                val *= d.inv_r;
-                if (decay != 0.f)
-                  val = decay * __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(orsrc, off, 0, 0)) +
-                        (1.f - decay) * val;
-              }
-              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), orsrc, off, 0, 0);
+              for (int b = 0; b < 2; ++b) put(i, jl + b * 32, acc[a][b][e]);
             }
-          }
+      };
+      if (shp) {  // raw sums of T, row i at i * c_col
+        each([&](int i, int j, float x) {
+          const bool ok = i < c_row && j < c_col;
+          const unsigned off = ok ? (unsigned(i) * unsigned(c_col) + unsigned(j)) * 4u : 0x80000000u;
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), orsrc, off, 0, 0);
+        });
+      } else {  // the factor scaled by 1/R, entry (i, j >= i) at i*d - i(i-1)/2 + j - i
+        auto off_of = [&](int i, int j) {
+          const unsigned ui = static_cast<unsigned>(i);
+          const bool ok = i <= j && j < d_core;
+          return ok ? (ui * unsigned(dd) - (ui * (ui - 1u)) / 2u - ui + unsigned(j)) * 4u : 0x80000000u;
+        };
+        if (decay == 0.f) {
+          each([&](int i, int j, float x) {
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x * inv_r), orsrc, off_of(i, j), 0, 0);
+          });
+        } else {  // blended with the stored factor
+          each([&](int i, int j, float x) {
+            const unsigned off = off_of(i, j);
+            const float old = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(orsrc, off, 0, 0));
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(decay * old + (1.f - decay) * (x * inv_r)),
+                                                  orsrc, off, 0, 0);
+          });
+        }
+      }
     }
     if (shp) {
       if (want_col && TI * BT + tid < d.c_row) gp(d.csum)[TI * BT + tid] = colsum;
@@ -1227,24 +1257,31 @@ static double row_cost(const SyrkDesc& d, kfac_dtype dt) {
   return (dt == KFAC_F16 && width % 8 == 0 && (d.d_core % 8 == 0 || d.padded)) ? 1.0 : 4.0;
 }
 
-// Whether a problem's shape suits 256x256 tiles: fp16 inputs read with 16-byte
-// gathers, and a factor of order 256 or more or a shift product of 256 or more
-// channels (fewer would leave most of a 256-row tile idle), with an output under 2^31
-// bytes (32-bit store offsets). The launch also needs the input pointer's 16-byte
-// alignment (SyrkDesc::vec); the split plan depends on the shape only, so that the
-// workspace query bounds every call.
-static bool big_shape(const SyrkDesc& d, kfac_dtype dt) {
-  const int64_t out_floats = d.kind == 1 ? int64_t(d.c_row) * d.c_col : int64_t(d.d) * (d.d + 1) / 2;
-  return dt == KFAC_F16 && row_cost(d, dt) == 1.0 && (d.kind == 1 ? d.c_row : d.d_core) >= BT &&
-         out_floats * 4 < (int64_t(1) << 31);
-}
-
 // Cost of one patch row of a 256x256 tile in units of one patch row of a 128x128
 // tile with 16-byte gathers: four times the products for twice the gathers.
 constexpr double kBigRowCost = 2.0;
+// Smallest factor order (d_core) taken on 256x256 tiles.
+constexpr int kBigMinOrder = 1024;
 // Set-up, first loads and result stores of a 256x256 item, in patch rows (measured on
 // gfx950: about 6 us per item against about 2 us per 64 rows).
 constexpr double kBigItemRows = 192.0;
+
+// Whether a problem's shape suits 256x256 tiles: fp16 inputs read with 16-byte
+// gathers; a shift product of 256 or more channels (fewer would leave most of a
+// 256-row tile idle) or a factor of order kBigMinOrder or more; an output under 2^31
+// bytes (32-bit store offsets). A factor of order d does about d/2 flop per input
+// byte, against about 540 for the chip's fp16 MFMA rate over its HBM rate: below
+// order ~1000 a factor is bound by its loads, which the 128x128 kernel (two blocks
+// per compute unit, twice the bytes in flight) streams faster (measured on the
+// order-256 factors over 100,352 rows: 82-96 us in 256x256 tiles, less in 128x128).
+// The launch also needs the input pointer's 16-byte alignment (SyrkDesc::vec); the
+// split plan depends on the shape only, so that the workspace query bounds every call.
+static bool big_shape(const SyrkDesc& d, kfac_dtype dt) {
+  const int64_t out_floats = d.kind == 1 ? int64_t(d.c_row) * d.c_col : int64_t(d.d) * (d.d + 1) / 2;
+  return dt == KFAC_F16 && row_cost(d, dt) == 1.0 && (d.kind == 1 ? d.c_row >= BT : d.d_core >= kBigMinOrder) &&
+         out_floats * 4 < (int64_t(1) << 31);
+}
+
 
 // Cost of one patch row of one work item (a tile over a range of rows).
 static double item_row_cost(const SyrkDesc& d, kfac_dtype dt) {

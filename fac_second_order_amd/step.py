@@ -124,6 +124,17 @@ class KfacStep:
     def _sub(self, v, idx):
         return [v[i] for i in idx]
 
+    def _factor_inputs(self, act, gout):
+        """(act, gout) lists of the side matrices' factors and of all the others, with
+        None where a factor is left to the other call."""
+        L = len(self.layers)
+        side = set(self.side)
+        first = ([a if l in side else None for l, a in enumerate(act)],
+                 [g if l + L in side else None for l, g in enumerate(gout)])
+        rest = ([None if l in side else a for l, a in enumerate(act)],
+                [None if l + L in side else g for l, g in enumerate(gout)])
+        return first, rest
+
     def invert(self, stream=None):
         """Unpacks and inverts every damped factor on `stream` (the side split is
         applied by step())."""
@@ -195,20 +206,28 @@ class KfacStep:
             self.precondition(grads, weights, lr, stream)
             self.bn(xhat, bn_gout, 1.0, bn_params, lr, stream)
             return
-        self.factors(act, gout, ema_decay, stream)
         if not self.side:
+            self.factors(act, gout, ema_decay, stream)
             self.invert(stream)
             self.precondition(grads, weights, lr, stream)
             self.bn(xhat, bn_gout, ema_decay, bn_params, lr, stream)
             return
         main = torch.cuda.current_stream(self.device) if stream is None else stream
         side = self.stream2
-        self._unpack_some(self.side, main)  # the long sweeps' factors first
+        # the long sweeps' factors first, so that their inverses start while the other
+        # factors are formed (a factor call plans its row splits over every layer,
+        # whichever inputs it is given: the same bits as one call)
+        first, rest = self._factor_inputs(act, gout)
+        K.kfac_factors(self.layers, first[0], first[1], self.A_packed, self.G_packed, ema_decay,
+                       self.workspace, main)
+        self._unpack_some(self.side, main)
         unpacked = torch.cuda.Event()
         unpacked.record(main)
         side.wait_event(unpacked)
         try:
             self._invert(self.side, self._info_side, self.workspace2, side)
+            K.kfac_factors(self.layers, rest[0], rest[1], self.A_packed, self.G_packed, ema_decay,
+                           self.workspace, main)
             self._unpack_some(self.main, main)
             self._invert(self.main, self._info_main, self.workspace, main)
             main_inverses = torch.cuda.Event()

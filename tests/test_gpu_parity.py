@@ -224,21 +224,24 @@ def test_factors_shift_products_edge_cases(kfac_gpu):
         assert np.array_equal(host(A[l]), expect), layer.name
 
 
-# Problems of 256 or more columns (factors of order >= 256, shift products of 3x3 layers
-# with >= 256 channels) run on 256x256 tiles: direct and split-reduced results, the bias
-# column, rows and columns that end inside a tile (264, 296, 320, 272 channels), both
-# gather forms (rows, strided 1x1 gathers) and tiles off the diagonal.
+# Factors of order >= 1024 and the shift products of 3x3 layers with >= 256 channels run
+# on 256x256 tiles: direct and split-reduced results, the bias column, rows and columns
+# that end inside a tile (264, 1032, 1040 channels), both gather forms (rows, strided 1x1
+# gathers) and tiles off the diagonal. Orders 256-512 next to them take 128x128 tiles.
 BIG_TILE_LAYERS = [
-    synth.Layer("c3x3_256", 2, 8, 8, 256, 8, 8, 256, 3, 3, 1, 1, 1, 1, 1),         # A 2305, G 256
-    synth.Layer("c3x3_264_split", 40, 8, 8, 264, 8, 8, 24, 3, 3, 1, 1, 1, 1, 1),   # R = 2560
-    synth.Layer("c1x1_296_split", 48, 8, 8, 296, 8, 8, 320, 1, 1, 1, 1, 0, 0, 1),  # R = 3072
-    synth.Layer("c1x1s2_256", 4, 10, 10, 256, 5, 5, 272, 1, 1, 2, 2, 0, 0, 1),
+    synth.Layer("c3x3_256", 2, 8, 8, 256, 8, 8, 256, 3, 3, 1, 1, 1, 1, 1),           # A 2305, G 256
+    synth.Layer("c3x3_264_split", 40, 8, 8, 264, 8, 8, 24, 3, 3, 1, 1, 1, 1, 1),     # R = 2560
+    synth.Layer("c1x1_1032_split", 48, 8, 8, 1032, 8, 8, 1040, 1, 1, 1, 1, 0, 0, 1),  # R = 3072
+    synth.Layer("c1x1s2_1024", 2, 10, 10, 1024, 5, 5, 1024, 1, 1, 2, 2, 0, 0, 1),
+    synth.Layer("fc_1024", 64, 1, 1, 1024, 1, 1, 1000, 1, 1, 1, 1, 0, 0, 0),
+    synth.Layer("c1x1_296_split", 48, 8, 8, 296, 8, 8, 320, 1, 1, 1, 1, 0, 0, 1),
     synth.Layer("fc_512", 64, 1, 1, 512, 1, 1, 264, 1, 1, 1, 1, 0, 0, 0),
 ]
 
 
 def test_factors_big_tiles_integer_bitexact(kfac_gpu):
-    """[OTUNYM] eq. (5) through the 256x256-tile path with inputs in {-2..2}: every sum
+    """[OTUNYM] eq. (5) through the 256x256-tile path (and 128x128 tiles for the orders
+    below 1024) with inputs in {-2..2}: every sum
     is an exact integer, so each output is fp32(sum) * fp32(1/R), bit for bit."""
     rng = synth.layer_rng(1014, 0)
     act = [rng.integers(-2, 3, size=l.act_shape).astype(np.float16) for l in BIG_TILE_LAYERS]
