@@ -406,6 +406,9 @@ __global__ void __launch_bounds__(256) syrk_f16_kernel(const SyrkDesc* __restric
   const bool skip = diag && wm > wn;  // quadrant strictly below the diagonal
   // rows of a shift product past C (C = 64: the lower half of the tile)
   const bool idle = shp && ti * ST + wm * 64 >= d.c_row;
+  // a quadrant whose rows or columns all lie past the factor's last (order 64: three
+  // of a diagonal tile's quadrants) multiplies zeros only
+  const bool past = ti * ST + wm * 64 >= (shp ? d.c_row : d.d_core) || tj * ST + wn * 64 >= (shp ? d.c_col : d.d_core);
   ColTab ct;  // the 8 columns this thread stages: of row block tj in threads 128.. of an
               // off-diagonal tile, else of row block ti
   const int op = diag ? 0 : (tid >> 7);
@@ -422,7 +425,7 @@ __global__ void __launch_bounds__(256) syrk_f16_kernel(const SyrkDesc* __restric
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
   float colsum = 0.f;
-  const bool mma_on = !skip && !idle;
+  const bool mma_on = !skip && !idle && !past;
   // block-uniform specialisations of the main loop
   if (diag) {
     if (d.vec) syrk_rows<true, true>(d, tab, lds[0], lds[1], ct, r_begin, r_end, want_col, mma_on, acc, colsum);
