@@ -228,7 +228,7 @@ static BnDesc plan_layer(const kfac_bn& L, int esize, bool vec) {
   d.rowpar = 256 / d.vl;
   d.cblocks = (groups + d.vl - 1) / d.vl;
   const int64_t row_bytes = int64_t(d.vl) * ev * esize;
-  int64_t rpc = (64 * 1024) / row_bytes;  // about 64 KB of each tensor per work item
+  int64_t rpc = (128 * 1024) / row_bytes;  // about 128 KB of each tensor per work item
   if (rpc < d.rowpar) rpc = d.rowpar;
   rpc = (rpc / d.rowpar) * d.rowpar;
   if (rpc > d.hw) rpc = d.hw;

@@ -169,12 +169,18 @@ __device__ inline int find_problem(const int32_t* begin, int count, int w) {
   return lo;
 }
 
-// Upper-triangle tile t (row-major over i <= j) of an nb x nb tile grid.
+// Upper-triangle tile t (row-major over i <= j) of an nb x nb tile grid. Row i starts
+// at S(i) = i*nb - i(i-1)/2; the row is the root of S(i) = t (a float estimate, exact to
+// within a few rows for any grid of fewer than 2^12 blocks per side), then corrected.
 __device__ inline void upper_tile(int t, int nb, int& ti, int& tj) {
-  int i = 0;
-  while (t >= nb - i) { t -= nb - i; ++i; }
+  const float b = 2.f * static_cast<float>(nb) + 1.f;
+  int i = static_cast<int>((b - sqrtf(fmaxf(b * b - 8.f * static_cast<float>(t), 0.f))) * 0.5f);
+  i = max(0, min(i, nb - 1));
+  auto row_start = [nb](int r) { return r * nb - (r * (r - 1)) / 2; };
+  while (i > 0 && row_start(i) > t) --i;
+  while (i + 1 < nb && row_start(i + 1) <= t) ++i;
   ti = i;
-  tj = i + t;
+  tj = i + (t - row_start(i));
 }
 
 // Offset of (i, j), i <= j, in the row-by-row upper-triangle packing of order n.

@@ -65,6 +65,23 @@ def test_pack_unpack_bitexact(kfac_gpu):
     for n, p, b, o in zip(sizes, src, base, out):
         want = np.where(np.triu(np.ones((n, n), dtype=bool)), oracle.unpack_upper(p, n), b)
         assert np.array_equal(host(o), want), n
+    # direction 2 into full matrices that are only 4-byte aligned, at an order whose packed
+    # array spans several 16,384-float slices (row segments cross slice boundaries)
+    sizes = [577, 1000, 2049]
+    mats2 = [rng.standard_normal((n, n)).astype(np.float32) for n in sizes]
+    src = [oracle.pack_upper(m) for m in mats2]
+    base = [rng.standard_normal((n, n)).astype(np.float32) for n in sizes]
+    fstore = [torch.zeros(n * n + 1, device="cuda") for n in sizes]
+    fviews = []
+    for st_, b in zip(fstore, base):
+        st_[1:] = to_dev(b).reshape(-1)
+        fviews.append(st_[1:].view(b.shape))
+        assert fviews[-1].data_ptr() % 16 == 4
+    say("kfac_pack_sym direction 2, unaligned full", sizes)
+    kfac_gpu.kfac_pack_sym(sizes, fviews, [to_dev(p) for p in src], 2)
+    for n, p, b, o in zip(sizes, src, base, fviews):
+        want = np.where(np.triu(np.ones((n, n), dtype=bool)), oracle.unpack_upper(p, n), b)
+        assert np.array_equal(host(o), want), n
 
 
 # ---------------------------------------------------------------------------
