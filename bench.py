@@ -1,7 +1,7 @@
 """Throughput of the single-GPU K-FAC step on ResNet-50 shapes at 32 samples per GPU.
 
 One step = Kronecker factors of all 54 layers (53 convolutions and the classifier,
-fp16 inputs) -> unpack to full symmetric -> 108 damped inverses -> G^-1 dW A^-1 for
+fp16 inputs, also written as the upper triangles the inversion reads) -> 108 damped inverses -> G^-1 dW A^-1 for
 all 54 layers (fp32 gradients) with the update w <- w - lr P of every weight in the
 same kernel -> diagonal Fisher of all 53 BatchNorm layers with the gamma/beta update.
 Inputs are synthetic and seeded, resident in HBM before timing starts.

@@ -5,7 +5,7 @@ marshal arguments. Importing this package loads libkfac.so and fails loudly if i
 not been built (python fac_second_order_amd/build.py)."""
 from ._lib import (  # noqa: F401
     KFAC_F16, KFAC_F32, KFAC_F64, KfacError, LIB_PATH, kfac_version,
-    kfac_factors_workspace, kfac_factors,
+    kfac_factors_workspace, kfac_factors, kfac_factors_full,
     kfac_pack_sym_workspace, kfac_pack_sym,
     kfac_invert_workspace, kfac_invert_schedule, kfac_invert,
     kfac_invert_refine_workspace, kfac_invert_refine,

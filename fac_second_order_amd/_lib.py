@@ -63,6 +63,8 @@ _sig("kfac_last_error", _c.c_char_p)
 _sig("kfac_factors_workspace", _i32, _P(kfac_layer), _i32, _i32, _P(_sz))
 _sig("kfac_factors", _i32, _P(kfac_layer), _i32, _i32, _P(_vp), _P(_vp), _P(_vp), _P(_vp), _f32,
      _vp, _sz, _vp)
+_sig("kfac_factors_full", _i32, _P(kfac_layer), _i32, _i32, _P(_vp), _P(_vp), _P(_vp), _P(_vp), _P(_vp),
+     _P(_vp), _f32, _vp, _sz, _vp)
 _sig("kfac_pack_sym_workspace", _i32, _i32, _P(_i32), _P(_sz))
 _sig("kfac_pack_sym", _i32, _i32, _P(_i32), _P(_vp), _P(_vp), _i32, _vp, _sz, _vp)
 _sig("kfac_invert_workspace", _i32, _i32, _P(_i32), _P(_sz))
@@ -166,8 +168,7 @@ def kfac_factors_workspace(layers, in_dtype=KFAC_F16):
     return out.value
 
 
-def kfac_factors(layers, act, gout, A_packed, G_packed, ema_decay=0.0, workspace=None, stream=None):
-    """A_packed[l], G_packed[l] <- packed factors of layer l (see kfac.h)."""
+def _factor_call_args(layers, act, gout, workspace):
     first = next(t for t in list(act) + list(gout) if t is not None)
     dt = _dtype_code(first)
     for t in list(act) + list(gout):
@@ -175,9 +176,32 @@ def kfac_factors(layers, act, gout, A_packed, G_packed, ema_decay=0.0, workspace
             raise TypeError("factor inputs must share one dtype and be contiguous")
     need = kfac_factors_workspace(layers, dt)
     ws, wsb = _ws(workspace, need, first.device)
+    return dt, ws, wsb
+
+
+def kfac_factors(layers, act, gout, A_packed, G_packed, ema_decay=0.0, workspace=None, stream=None):
+    """A_packed[l], G_packed[l] <- packed factors of layer l (see kfac.h)."""
+    dt, ws, wsb = _factor_call_args(layers, act, gout, workspace)
     _check(_lib.kfac_factors(_layers(layers), len(layers), dt, _ptrs(act), _ptrs(gout),
                              _ptrs(A_packed), _ptrs(G_packed), float(ema_decay), ws, wsb,
                              _stream(stream)), "kfac_factors")
+
+
+def kfac_factors_full(layers, act, gout, A_packed, G_packed, A_full, G_full, ema_decay=0.0, workspace=None,
+                      stream=None):
+    """kfac_factors that also writes the upper triangle of each factor into A_full[l] /
+    G_full[l] (d x d fp32, row-major; None entries skip it; see kfac.h)."""
+    dt, ws, wsb = _factor_call_args(layers, act, gout, workspace)
+    orders = [(l.c_in * l.kh * l.kw + (1 if l.bias else 0), l.c_out) for l in layers]
+    if len(A_full) != len(layers) or len(G_full) != len(layers):
+        raise ValueError("A_full and G_full need one entry per layer")
+    for (da, dg), fa, fg in zip(orders, A_full, G_full):
+        for t, d in ((fa, da), (fg, dg)):
+            if t is not None and (t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != d * d):
+                raise TypeError("full factor outputs must be contiguous float32 d x d")
+    _check(_lib.kfac_factors_full(_layers(layers), len(layers), dt, _ptrs(act), _ptrs(gout),
+                                  _ptrs(A_packed), _ptrs(G_packed), _ptrs(A_full), _ptrs(G_full),
+                                  float(ema_decay), ws, wsb, _stream(stream)), "kfac_factors_full")
 
 
 def kfac_pack_sym_workspace(n):

@@ -87,6 +87,9 @@ struct SyrkDesc {
   int32_t nb2, nbr2, nbc2, nt2;
   int32_t big;  // the problem's items run in syrk_big_kernel
   int32_t pad2_;
+  // kind 0: when not NULL, every entry (i, j >= i) written to `out` is also written to
+  // full[i * d + j] (row-major d x d; the strict lower triangle is not written)
+  float* full;
 };
 
 // Value of X[row][c] (0 outside the image or beyond d_core), any input dtype
@@ -256,6 +259,12 @@ __device__ inline float blend(float v, const float* out, int64_t o, float decay)
   return decay != 0.f ? decay * gp(out)[o] + (1.f - decay) * v : v;
 }
 
+// Entry (i, j >= i) of a factor: the packed store at o and, when asked for, the full one.
+__device__ inline void put_entry(const SyrkDesc& d, int64_t o, int i, int j, float v) {
+  gp(d.out)[o] = v;
+  if (d.full) gp(d.full)[int64_t(i) * d.d + j] = v;
+}
+
 // Writes the bias column entries (column sums) and the bias corner of a direct tile.
 __device__ inline void write_bias_direct(const SyrkDesc& d, int ti, int t, float colsum,
                                          float decay) {
@@ -264,12 +273,12 @@ __device__ inline void write_bias_direct(const SyrkDesc& d, int ti, int t, float
     const int i = ti * ST + tid;
     if (i < d.d_core) {
       const int64_t o = packed_off(i, d.d_core, d.d);
-      gp(d.out)[o] = blend(colsum * d.inv_r, d.out, o, decay);
+      put_entry(d, o, i, d.d_core, blend(colsum * d.inv_r, d.out, o, decay));
     }
   }
   if (t == 0 && tid == 0) {
     const int64_t o = packed_off(d.d_core, d.d_core, d.d);
-    gp(d.out)[o] = blend(d.r_f * d.inv_r, d.out, o, decay);
+    put_entry(d, o, d.d_core, d.d_core, blend(d.r_f * d.inv_r, d.out, o, decay));
   }
 }
 
@@ -442,6 +451,7 @@ __global__ void __launch_bounds__(256) syrk_f16_kernel(const SyrkDesc* __restric
     const int64_t dd = d.d;
     const float inv_r = d.inv_r;
     KG float* const out = gp(d.out);
+    KG float* const full = gp(d.full);
     const int jb = tj * ST + wn * 64 + (lane & 31);
     if (shp) {  // raw sums into T, rows < C, columns < ntap * C
       if (!idle) {
@@ -467,12 +477,15 @@ __global__ void __launch_bounds__(256) syrk_f16_kernel(const SyrkDesc* __restric
           for (int e = 0; e < 16; ++e) {
             const int i = ti * ST + wm * 64 + a * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
             KG float* const row = out + (int64_t(i) * dd - (int64_t(i) * (i - 1)) / 2 - i);  // row[j] for j >= i
+            KG float* const frow = full + int64_t(i) * dd;
 #pragma unroll
             for (int b = 0; b < 2; ++b) {
               const int j = jb + b * 32;
               if (i <= j && j < d_core) {
                 const float x = acc[a][b][e] * inv_r;
-                row[j] = decay != 0.f ? decay * row[j] + (1.f - decay) * x : x;
+                const float v = decay != 0.f ? decay * row[j] + (1.f - decay) * x : x;
+                row[j] = v;
+                if (full) frow[j] = v;
               }
             }
           }
@@ -719,7 +732,24 @@ __global__ void __launch_bounds__(512) syrk_big_kernel(const SyrkDesc* __restric
           const bool ok = i <= j && j < d_core;
           return ok ? (ui * unsigned(dd) - (ui * (ui - 1u)) / 2u - ui + unsigned(j)) * 4u : 0x80000000u;
         };
-        if (decay == 0.f) {
+        // the full matrix's rows from the slab's first one: a buffer based there, so that
+        // the offsets stay small (under 128 rows of the factor)
+        KG float* const full = gp(d.full);
+        const int64_t fbytes = int64_t(dd - row0) * dd * 4;  // <= 0 for a slab past the last row
+        const unsigned frec = fbytes <= 0 ? 0u : fbytes > 0x7fffff00 ? 0x7fffff00u : unsigned(fbytes);
+        const __amdgpu_buffer_rsrc_t frsrc = __builtin_amdgcn_make_buffer_rsrc(
+            full + int64_t(row0) * dd, 0, static_cast<int>(frec), 0x00020000);
+        auto foff_of = [&](int i, int j) {
+          const bool ok = i <= j && j < d_core;
+          return ok ? (unsigned(i - row0) * unsigned(dd) + unsigned(j)) * 4u : 0x80000000u;
+        };
+        if (decay == 0.f && full) {
+          each([&](int i, int j, float x) {
+            const unsigned v = __float_as_uint(x * inv_r);
+            __builtin_amdgcn_raw_buffer_store_b32(v, orsrc, off_of(i, j), 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(v, frsrc, foff_of(i, j), 0, 0);
+          });
+        } else if (decay == 0.f) {
           each([&](int i, int j, float x) {
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x * inv_r), orsrc, off_of(i, j), 0, 0);
           });
@@ -727,8 +757,9 @@ __global__ void __launch_bounds__(512) syrk_big_kernel(const SyrkDesc* __restric
           each([&](int i, int j, float x) {
             const unsigned off = off_of(i, j);
             const float old = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(orsrc, off, 0, 0));
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(decay * old + (1.f - decay) * (x * inv_r)),
-                                                  orsrc, off, 0, 0);
+            const unsigned v = __float_as_uint(decay * old + (1.f - decay) * (x * inv_r));
+            __builtin_amdgcn_raw_buffer_store_b32(v, orsrc, off, 0, 0);
+            if (full) __builtin_amdgcn_raw_buffer_store_b32(v, frsrc, foff_of(i, j), 0, 0);
           });
         }
       }
@@ -739,11 +770,11 @@ __global__ void __launch_bounds__(512) syrk_big_kernel(const SyrkDesc* __restric
       const int i = TI * BT + tid;
       if (i < d.d_core) {
         const int64_t o = packed_off(i, d.d_core, d.d);
-        gp(d.out)[o] = blend(colsum * d.inv_r, d.out, o, decay);
+        put_entry(d, o, i, d.d_core, blend(colsum * d.inv_r, d.out, o, decay));
       }
       if (TI == 0 && tid == 0) {
         const int64_t o = packed_off(d.d_core, d.d_core, d.d);
-        gp(d.out)[o] = blend(d.r_f * d.inv_r, d.out, o, decay);
+        put_entry(d, o, d.d_core, d.d_core, blend(d.r_f * d.inv_r, d.out, o, decay));
       }
     }
   } else {
@@ -838,7 +869,7 @@ __global__ void __launch_bounds__(256) syrk_f32_kernel(const SyrkDesc* __restric
             const int j = tj * ST + wn * 64 + b * 32 + (lane & 31);
             if (i <= j && j < d.d_core) {
               const int64_t o = packed_off(i, j, d.d);
-              gp(d.out)[o] = blend(acc[a][b][e] * d.inv_r, d.out, o, decay);
+              put_entry(d, o, i, j, blend(acc[a][b][e] * d.inv_r, d.out, o, decay));
             }
           }
     }
@@ -930,7 +961,7 @@ __global__ void __launch_bounds__(256) syrk_reduce_kernel(const SyrkDesc* __rest
       const int j = j0 + u;
       if (j >= i && j < d.d_core) {
         const int64_t o = packed_off(i, j, d.d);
-        gp(d.out)[o] = blend(v4[u] * d.inv_r, d.out, o, decay);
+        put_entry(d, o, i, j, blend(v4[u] * d.inv_r, d.out, o, decay));
       }
     }
   }
@@ -950,12 +981,12 @@ __global__ void __launch_bounds__(256) syrk_reduce_kernel(const SyrkDesc* __rest
       }
       for (; s < d.splits; ++s) sum += pc[s * sstride];
       const int64_t o = packed_off(ib, d.d_core, d.d);
-      gp(d.out)[o] = blend(sum * d.inv_r, d.out, o, decay);
+      put_entry(d, o, ib, d.d_core, blend(sum * d.inv_r, d.out, o, decay));
     }
   }
   if (t == 0 && part == 0 && d.bias && threadIdx.x == 0) {
     const int64_t o = packed_off(d.d_core, d.d_core, d.d);
-    gp(d.out)[o] = blend(d.r_f * d.inv_r, d.out, o, decay);
+    put_entry(d, o, d.d_core, d.d_core, blend(d.r_f * d.inv_r, d.out, o, decay));
   }
 }
 
@@ -990,6 +1021,7 @@ __host__ __device__ inline int tap_index(int dh, int dw) { return dh == 0 ? dw :
 struct ShiftAsm {
   const float* base;  // the layer's region
   float* out;         // packed A
+  float* full;        // NULL, or A row-major d x d: the upper triangle written as well
   int32_t C, d, bias, pad_;
   float inv_r, r_f;
 };
@@ -1018,15 +1050,21 @@ __global__ void __launch_bounds__(256) shift_assemble_kernel(const ShiftAsm* __r
   // j / C by a shift when C is a power of two (block-uniform choice)
   const bool pow2 = (C & (C - 1)) == 0;
   const int lg = 31 - __builtin_clz(static_cast<unsigned>(C));
-  auto put = [&](KG float* o, float v) {
+  KG float* const full = gp(a.full);
+  // entry (i, j) with o = its packed address and f its full one (when full is not NULL)
+  auto put = [&](KG float* o, KG float* f, float v) {
     const float x = v * a.inv_r;
-    *o = decay != 0.f ? decay * *o + (1.f - decay) * x : x;
+    const float y = decay != 0.f ? decay * *o + (1.f - decay) * x : x;
+    *o = y;
+    if (full) *f = y;
   };
-  if (a.bias && c1 == 0 && tid == 0) put(gp(a.out) + packed_off(d - 1, d - 1, d), a.r_f);
+  if (a.bias && c1 == 0 && tid == 0)
+    put(gp(a.out) + packed_off(d - 1, d - 1, d), full + (int64_t(d) * d - 1), a.r_f);
   for (int t1 = 0; t1 < 9; ++t1) {
     const int i = t1 * C + c1, i1 = t1 / 3, j1 = t1 - 3 * i1;
     const int hs = i1 == 0 ? 1 : 0, ws = j1 == 0 ? 1 : 0;  // strips left out: bottom/top, right/left
     KG float* __restrict__ orow = gp(a.out) + packed_off(i, i, d) - i;  // orow[j] for j >= i
+    KG float* __restrict__ frow = full + int64_t(i) * d;
     float bias_v = 0.f;
     if (a.bias) {  // the bias column: sum over the pixels tap t1 sees
       bias_v = Su[c1];
@@ -1066,11 +1104,15 @@ __global__ void __launch_bounds__(256) shift_assemble_kernel(const ShiftAsm* __r
       if (decay == 0.f) {
 #pragma unroll
         for (int u = 0; u < U; ++u)
-          if (j0 + 256 * u < d) orow[j0 + 256 * u] = xt[u] * a.inv_r;
+          if (j0 + 256 * u < d) {
+            const float x = xt[u] * a.inv_r;
+            orow[j0 + 256 * u] = x;
+            if (full) frow[j0 + 256 * u] = x;
+          }
       } else {
 #pragma unroll
         for (int u = 0; u < U; ++u)
-          if (j0 + 256 * u < d) put(orow + j0 + 256 * u, xt[u]);
+          if (j0 + 256 * u < d) put(orow + j0 + 256 * u, frow + j0 + 256 * u, xt[u]);
       }
     }
   }
@@ -1380,7 +1422,8 @@ static kfac_status layers_validate(const kfac_layer* L, int32_t count, kfac_dtyp
 // l. Row splits are planned over all factors (so the workspace query bounds every
 // call); factors whose input pointer is NULL are then dropped.
 static kfac_status build_plan(const kfac_layer* L, int32_t count, kfac_dtype dt, const void* const* act,
-                              const void* const* gout, float* const* A, float* const* G, SyrkPlan& pl) {
+                              const void* const* gout, float* const* A, float* const* G, float* const* Af,
+                              float* const* Gf, SyrkPlan& pl) {
   const int esize = dt == KFAC_F16 ? 2 : 4;
   std::vector<SyrkDesc> all;
   std::vector<Im2Row> geo;            // conv geometry of the problems converted to rows (by index in all)
@@ -1418,11 +1461,15 @@ static kfac_status build_plan(const kfac_layer* L, int32_t count, kfac_dtype dt,
       const void* src = which == 0 ? act[l] : gout[l];
       if (!src) continue;
       float* out = which == 0 ? A[l] : G[l];
+      float* const* fl = which == 0 ? Af : Gf;
+      float* full = fl ? fl[l] : nullptr;
       if (!out) return fail(KFAC_ERR_INVALID, "layer %d: output for factor %d is NULL", l, which);
-      if (reinterpret_cast<uintptr_t>(src) % esize || reinterpret_cast<uintptr_t>(out) % 4)
+      if (reinterpret_cast<uintptr_t>(src) % esize || reinterpret_cast<uintptr_t>(out) % 4 ||
+          reinterpret_cast<uintptr_t>(full) % 4)
         return fail(KFAC_ERR_INVALID, "layer %d: misaligned pointer", l);
       d.src = src;
       d.out = out;  // shift products: replaced by the region at launch
+      d.full = sub >= 0 ? nullptr : full;  // a shift product's full copy is its assembly's
       const int width = d.mode == 1 ? d.C : d.ld;
       const int64_t bytes = d.mode == 1 ? int64_t(L[l].n) * d.H * d.W * d.C * esize
                                         : int64_t(d.R) * d.ld * esize;
@@ -1434,6 +1481,7 @@ static kfac_status build_plan(const kfac_layer* L, int32_t count, kfac_dtype dt,
       job_of_layer[l] = static_cast<int32_t>(pl.jobs.size());
       ShiftAsm j{};
       j.out = act ? A[l] : nullptr;
+      j.full = act && Af ? Af[l] : nullptr;
       j.C = L[l].c_in;
       j.bias = L[l].bias ? 1 : 0;
       j.d = 9 * j.C + j.bias;
@@ -1459,6 +1507,7 @@ static kfac_status build_plan(const kfac_layer* L, int32_t count, kfac_dtype dt,
         c.rows_per_split = d.rows_per_split;
         c.src = d.src;
         c.out = d.out;
+        c.full = d.full;
         d = c;
       }
     }
@@ -1560,23 +1609,24 @@ extern "C" kfac_status kfac_factors_workspace(const kfac_layer* layers, int32_t 
   if (st) return st;
   if (count == 0) { *bytes = 0; return KFAC_OK; }
   SyrkPlan pl;
-  st = build_plan(layers, count, in_dtype, nullptr, nullptr, nullptr, nullptr, pl);
+  st = build_plan(layers, count, in_dtype, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, pl);
   if (st) return st;
   *bytes = syrk_ws_bytes(pl);
   return KFAC_OK;
 }
 
-extern "C" kfac_status kfac_factors(const kfac_layer* layers, int32_t count, kfac_dtype in_dtype,
-                                    const void* const* act, const void* const* gout,
-                                    float* const* A_packed, float* const* G_packed, float ema_decay,
-                                    void* workspace, size_t ws_bytes, void* stream) {
+extern "C" kfac_status kfac_factors_full(const kfac_layer* layers, int32_t count, kfac_dtype in_dtype,
+                                         const void* const* act, const void* const* gout,
+                                         float* const* A_packed, float* const* G_packed, float* const* A_full,
+                                         float* const* G_full, float ema_decay, void* workspace,
+                                         size_t ws_bytes, void* stream) {
   kfac_status st = layers_validate(layers, count, in_dtype);
   if (st) return st;
   if (!(ema_decay >= 0.f && ema_decay <= 1.f)) return fail(KFAC_ERR_INVALID, "ema_decay must be in [0, 1]");
   if (count == 0) return KFAC_OK;
   if (!act || !gout || !A_packed || !G_packed) return fail(KFAC_ERR_INVALID, "NULL pointer array");
   SyrkPlan pl;
-  st = build_plan(layers, count, in_dtype, act, gout, A_packed, G_packed, pl);
+  st = build_plan(layers, count, in_dtype, act, gout, A_packed, G_packed, A_full, G_full, pl);
   if (st) return st;
   if (pl.desc.empty()) return KFAC_OK;
   st = check_device();
@@ -1675,4 +1725,12 @@ extern "C" kfac_status kfac_factors(const kfac_layer* layers, int32_t count, kfa
     KFAC_CHECK_LAUNCH("shift_assemble_kernel");
   }
   return KFAC_OK;
+}
+
+extern "C" kfac_status kfac_factors(const kfac_layer* layers, int32_t count, kfac_dtype in_dtype,
+                                    const void* const* act, const void* const* gout,
+                                    float* const* A_packed, float* const* G_packed, float ema_decay,
+                                    void* workspace, size_t ws_bytes, void* stream) {
+  return kfac_factors_full(layers, count, in_dtype, act, gout, A_packed, G_packed, nullptr, nullptr, ema_decay,
+                           workspace, ws_bytes, stream);
 }

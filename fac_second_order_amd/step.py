@@ -1,6 +1,6 @@
 """One K-FAC step over a fixed set of layers: device buffers plus the sequence of
-library calls (factors -> unpack -> damped inverses -> preconditioning, and the
-BatchNorm diagonal). Python only allocates and sequences; every number is computed
+library calls (factors, written packed and as the upper triangle the inversion
+reads -> damped inverses -> preconditioning, and the BatchNorm diagonal). Python only allocates and sequences; every number is computed
 by libkfac's HIP kernels.
 
 Step order follows Osawa et al. (CVPR 2019): stage 1-2 of their Figure 1 (factors
@@ -121,6 +121,13 @@ class KfacStep:
         K.kfac_factors(self.layers, act, gout, self.A_packed, self.G_packed, ema_decay,
                        self.workspace, stream)
 
+    def _factors_full(self, act, gout, ema_decay, stream):
+        # the packed factors (the stored state) and the upper triangles that kfac_invert
+        # reads, from the same kernels: no separate unpack pass
+        L = len(self.layers)
+        K.kfac_factors_full(self.layers, act, gout, self.A_packed, self.G_packed, self.full[:L], self.full[L:],
+                            ema_decay, self.workspace, stream)
+
     def _sub(self, v, idx):
         return [v[i] for i in idx]
 
@@ -147,12 +154,6 @@ class KfacStep:
     def _unpack(self, stream):
         # kfac_invert reads only the upper triangle: unpack that half
         K.kfac_pack_sym(self.n_all, self.full, self.packed_all, 2, self.workspace, stream)
-
-    def _unpack_some(self, idx, stream):
-        if idx:
-            sub = self._sub
-            K.kfac_pack_sym(sub(self.n_all, idx), sub(self.full, idx), sub(self.packed_all, idx), 2,
-                            self.workspace, stream)
 
     def _invert(self, idx, info, ws, stream):
         if idx:
@@ -207,8 +208,9 @@ class KfacStep:
             self.bn(xhat, bn_gout, 1.0, bn_params, lr, stream)
             return
         if not self.side:
-            self.factors(act, gout, ema_decay, stream)
-            self.invert(stream)
+            self._factors_full(act, gout, ema_decay, stream)
+            self._invert(self.main, self._info_main, self.workspace, stream)
+            self._refine(stream)
             self.precondition(grads, weights, lr, stream)
             self.bn(xhat, bn_gout, ema_decay, bn_params, lr, stream)
             return
@@ -218,17 +220,13 @@ class KfacStep:
         # factors are formed (a factor call plans its row splits over every layer,
         # whichever inputs it is given: the same bits as one call)
         first, rest = self._factor_inputs(act, gout)
-        K.kfac_factors(self.layers, first[0], first[1], self.A_packed, self.G_packed, ema_decay,
-                       self.workspace, main)
-        self._unpack_some(self.side, main)
-        unpacked = torch.cuda.Event()
-        unpacked.record(main)
-        side.wait_event(unpacked)
+        self._factors_full(first[0], first[1], ema_decay, main)
+        formed = torch.cuda.Event()
+        formed.record(main)
+        side.wait_event(formed)
         try:
             self._invert(self.side, self._info_side, self.workspace2, side)
-            K.kfac_factors(self.layers, rest[0], rest[1], self.A_packed, self.G_packed, ema_decay,
-                           self.workspace, main)
-            self._unpack_some(self.main, main)
+            self._factors_full(rest[0], rest[1], ema_decay, main)
             self._invert(self.main, self._info_main, self.workspace, main)
             main_inverses = torch.cuda.Event()
             main_inverses.record(main)

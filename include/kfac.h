@@ -114,6 +114,27 @@ kfac_status kfac_factors(const kfac_layer* layers, int32_t count, kfac_dtype in_
                          void* workspace, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * kfac_factors_full - kfac_factors that also writes each factor's upper triangle
+ * into a full matrix, the form kfac_invert reads ([OTUNYM] eq. (5) for the
+ * factor, eq. (6) for the inverse that follows; Section 1 contributions: the
+ * factors are symmetric, so one triangle carries them).
+ *
+ * A_full / G_full: NULL, or arrays of `count` device pointers (an entry may be
+ * NULL) to row-major d x d fp32 matrices, caller-owned. Where given, entry (i, j),
+ * i <= j, of the factor is written to full[i*d + j] with the same bits as its
+ * packed entry (after the EMA blend), i.e. what kfac_pack_sym direction 2 would
+ * write; the strict lower triangle is not written. Each full matrix must not
+ * overlap any other buffer of the call. Arguments and errors otherwise as for
+ * kfac_factors (same workspace query); a misaligned full pointer (not 4-byte
+ * aligned) gives KFAC_ERR_INVALID.
+ * ------------------------------------------------------------------------- */
+kfac_status kfac_factors_full(const kfac_layer* layers, int32_t count, kfac_dtype in_dtype,
+                              const void* const* act, const void* const* gout,
+                              float* const* A_packed, float* const* G_packed,
+                              float* const* A_full, float* const* G_full, float ema_decay,
+                              void* workspace, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * kfac_pack_sym - symmetric storage conversion ([OTUNYM] Section 1: the factors
  * are symmetric, so one triangle carries all of them).
  *

@@ -299,6 +299,52 @@ def test_factors_big_tiles_fp16(kfac_gpu):
         assert ea <= 1e-4 and eg <= 1e-4, layer.name
 
 
+def _upper_bits(full):
+    d = full.shape[0]
+    iu = torch.triu_indices(d, d, device=full.device)
+    return full[iu[0], iu[1]].view(torch.int32), full[iu[1], iu[0]][iu[0] != iu[1]]
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.float32])
+def test_factors_full_matches_packed(kfac_gpu, dtype):
+    """kfac_factors_full: each full matrix's upper triangle holds the packed factor's
+    bits (what direction 2 of kfac_pack_sym writes) and its strict lower triangle is
+    left alone, through every kernel path (256x256 and 128x128 tiles, direct and split,
+    shift products and their assembly, conv1's patch rows, fp32 inputs), with and
+    without the EMA blend; the packed factors equal those of kfac_factors."""
+    layers = FACTOR_LAYERS + (BIG_TILE_LAYERS if dtype == torch.float16 else [])
+    rng = synth.layer_rng(1016, 0)
+    np_dt = np.float16 if dtype == torch.float16 else np.float32
+    inputs = []
+    for _ in range(2):
+        inputs.append(([to_dev(synth.relu_normal_f16(rng, l.act_shape).astype(np_dt)) for l in layers],
+                       [to_dev(synth.normal_f16(rng, l.gout_shape, 0.1).astype(np_dt)) for l in layers]))
+    sentinel = -7.25
+    A = [torch.full((l.d_a * (l.d_a + 1) // 2,), np.nan, device="cuda") for l in layers]
+    G = [torch.full((l.d_g * (l.d_g + 1) // 2,), np.nan, device="cuda") for l in layers]
+    Af = [torch.full((l.d_a, l.d_a), sentinel, device="cuda") for l in layers]
+    Gf = [torch.full((l.d_g, l.d_g), sentinel, device="cuda") for l in layers]
+    A_ref = [torch.full_like(x, np.nan) for x in A]
+    G_ref = [torch.full_like(x, np.nan) for x in G]
+    for step, ema in enumerate((0.0, 0.75)):
+        act, gout = inputs[step]
+        say(f"kfac_factors_full {dtype} ema {ema}", [l.name for l in layers])
+        kfac_gpu.kfac_factors_full(layers, act, gout, A, G, Af, Gf, ema)
+        kfac_gpu.kfac_factors(layers, act, gout, A_ref, G_ref, ema)
+        torch.cuda.synchronize()
+        for l, layer in enumerate(layers):
+            for packed, ref, full in ((A[l], A_ref[l], Af[l]), (G[l], G_ref[l], Gf[l])):
+                up, low = _upper_bits(full)
+                assert torch.equal(packed.view(torch.int32), ref.view(torch.int32)), layer.name
+                assert torch.equal(up, packed.view(torch.int32)), layer.name
+                assert bool((low == sentinel).all()), layer.name
+    # a NULL entry leaves that full matrix alone
+    keep = Af[0].clone()
+    kfac_gpu.kfac_factors_full(layers, inputs[0][0], inputs[0][1], A, G, [None] + Af[1:], Gf, 0.0)
+    torch.cuda.synchronize()
+    assert torch.equal(Af[0], keep)
+
+
 def test_factors_fp32_fc_and_kronecker(kfac_gpu):
     """The fc workload in fp32 (a[32x64], g[32x16], no bias): factors, damped inverses
     and G^-1 dW A^-1 through the library, checked against the oracle and against the
