@@ -128,8 +128,39 @@ class KfacStep:
         K.kfac_factors_full(self.layers, act, gout, self.A_packed, self.G_packed, self.full[:L], self.full[L:],
                             ema_decay, self.workspace, stream)
 
+    # With the second stream, the caller's stream forms its factors in 2 calls,
+    # preconditions in 4 and runs the BatchNorm step in 2 (groups of layers of about
+    # equal work). A pivot block of the long sweeps needs a whole compute unit, and while
+    # a launch of many small blocks runs, the units it frees go to its own next blocks:
+    # the pivot waits for the launch to drain (up to 0.3 ms behind one preconditioning
+    # or BatchNorm launch). Shorter launches bound that wait; more calls cost more than
+    # they save (measured: 6 preconditioning calls or 3 factor calls were slower).
+    MAIN_CALLS = {"factors": 2, "precondition": 4, "bn": 2}
+
+    @staticmethod
+    def _groups(idx, cost, parts):
+        """idx (in order) cut into at most `parts` runs of about equal summed cost."""
+        total = sum(cost(i) for i in idx)
+        out, cur, acc = [], [], 0.0
+        for i in idx:
+            cur.append(i)
+            acc += cost(i)
+            if len(out) < parts - 1 and acc >= total * (len(out) + 1) / parts:
+                out.append(cur)
+                cur = []
+        if cur:
+            out.append(cur)
+        return out
+
     def _sub(self, v, idx):
         return [v[i] for i in idx]
+
+    def _factor_cost(self, l):
+        # products of a layer's two factors: rows x order^2, the 3x3 A factors at about a
+        # third (formed from shift products)
+        L = self.layers[l]
+        rows = L.n * L.h_out * L.w_out
+        return rows * (self.d_a[l] ** 2 / (3.0 if L.kh == 3 and L.sh == 1 else 1.0) + self.d_g[l] ** 2)
 
     def _factor_inputs(self, act, gout):
         """(act, gout) lists of the side matrices' factors and of all the others, with
@@ -188,14 +219,19 @@ class KfacStep:
     def bn(self, xhat, bn_gout, ema_decay=0.0, bn_params=None, lr=0.0, stream=None):
         """BN Fisher and preconditioned gradients; with bn_params (fp32 [2, c]: gamma,
         beta) also bn_params -= lr * self.bn_pre."""
-        if not self.bn_layers:
+        self._bn(list(range(len(self.bn_layers))), xhat, bn_gout, ema_decay, bn_params, lr, stream)
+
+    def _bn(self, idx, xhat, bn_gout, ema_decay, bn_params, lr, stream):
+        if not idx:
             return
+        sub = self._sub
         if bn_params is None:
-            K.kfac_bn_diag(self.bn_layers, xhat, bn_gout, self.fisher, self.bn_pre, ema_decay,
-                           self.bn_shift, self.workspace, stream)
+            K.kfac_bn_diag(sub(self.bn_layers, idx), sub(xhat, idx), sub(bn_gout, idx), sub(self.fisher, idx),
+                           sub(self.bn_pre, idx), ema_decay, self.bn_shift, self.workspace, stream)
         else:
-            K.kfac_bn_update(self.bn_layers, xhat, bn_gout, self.fisher, self.bn_pre, bn_params, lr,
-                             ema_decay, self.bn_shift, self.workspace, stream)
+            K.kfac_bn_update(sub(self.bn_layers, idx), sub(xhat, idx), sub(bn_gout, idx), sub(self.fisher, idx),
+                             sub(self.bn_pre, idx), sub(bn_params, idx), lr, ema_decay, self.bn_shift,
+                             self.workspace, stream)
 
     def step(self, act, gout, grads, xhat=(), bn_gout=(), ema_decay=0.0, refresh=True,
              weights=None, bn_params=None, lr=0.0, stream=None):
@@ -226,12 +262,20 @@ class KfacStep:
         side.wait_event(formed)
         try:
             self._invert(self.side, self._info_side, self.workspace2, side)
-            self._factors_full(rest[0], rest[1], ema_decay, main)
+            lay = [l for l in range(len(self.layers)) if rest[0][l] is not None or rest[1][l] is not None]
+            for part in self._groups(lay, self._factor_cost, self.MAIN_CALLS["factors"]):
+                ps = set(part)
+                self._factors_full([a if l in ps else None for l, a in enumerate(rest[0])],
+                                   [g if l in ps else None for l, g in enumerate(rest[1])], ema_decay, main)
             self._invert(self.main, self._info_main, self.workspace, main)
             main_inverses = torch.cuda.Event()
             main_inverses.record(main)
-            self._precondition(self.main_layers, grads, weights, lr, self.workspace, main)
-            self.bn(xhat, bn_gout, ema_decay, bn_params, lr, main)
+            pcost = lambda l: self.d_g[l] * self.d_a[l] * (self.d_g[l] + self.d_a[l])  # noqa: E731
+            for part in self._groups(self.main_layers, pcost, self.MAIN_CALLS["precondition"]):
+                self._precondition(part, grads, weights, lr, self.workspace, main)
+            bcost = lambda b: self.bn_layers[b].n * self.bn_layers[b].hw * self.bn_layers[b].c  # noqa: E731
+            for part in self._groups(list(range(len(self.bn_layers))), bcost, self.MAIN_CALLS["bn"]):
+                self._bn(part, xhat, bn_gout, ema_decay, bn_params, lr, main)
             side.wait_event(main_inverses)  # the side layers' other factor
             self._precondition(self.side_layers, grads, weights, lr, self.workspace2, side)
         finally:
