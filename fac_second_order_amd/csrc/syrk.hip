@@ -1028,9 +1028,12 @@ struct ShiftAsm {
 
 // One block per channel c1 of a job (blocks of all jobs numbered by offsets `begin`):
 // the nine packed rows i = t1*C + c1 of A (t1 = 0..8), which all read row c1 of T and
-// of the strips (cache hits after the first), block 0 also the bias corner. Each
-// thread forms four entries of a row with their loads in flight before the stores;
-// every entry as above times fp32(1/R), blended with the stored factor when decay != 0.
+// of the strips (cache hits after the first), block 0 also the bias corner. Within a
+// row, the columns of one tap t2 are a segment on which delta and the strips that apply
+// are fixed: an entry loads only the terms that apply to its segment and forms its
+// value in the same order as everywhere (T, minus the row strip, minus the column
+// strip, plus the corner). Every entry times fp32(1/R), blended with the stored factor
+// when decay != 0, goes to the packed factor and, when asked for, to the full matrix.
 __global__ void __launch_bounds__(256) shift_assemble_kernel(const ShiftAsm* __restrict__ jobs,
                                                              const int32_t* __restrict__ begin, int count,
                                                              float decay) {
@@ -1040,20 +1043,21 @@ __global__ void __launch_bounds__(256) shift_assemble_kernel(const ShiftAsm* __r
   const int C = a.C, d = a.d, tid = threadIdx.x;
   const int64_t C3 = int64_t(3) * C;
   // the region is only read and the factor only written here: restrict lets every
-  // entry's loads issue before the previous entries' stores
+  // group's loads issue before the previous groups' stores
   const KG float* __restrict__ T = gp(a.base) + int64_t(c1) * (kShiftTaps * C);
   const KG float* __restrict__ Su = gp(a.base) + sr_sums(C);
   const KG float* __restrict__ R0 = gp(a.base) + sr_rows(C) + int64_t(c1) * C3;    // + hs*3C^2 + dw*C + c2
   const KG float* __restrict__ C0 = gp(a.base) + sr_cols(C) + int64_t(c1) * C3;    // + ws*3C^2 + dh*C + c2
   const KG float* __restrict__ X0 = gp(a.base) + sr_corners(C) + int64_t(c1) * C;  // + (2hs+ws)*C^2 + c2
   const int64_t cc = int64_t(C) * C;
+  KG float* const full = gp(a.full);
+  const float inv_r = a.inv_r;
   // j / C by a shift when C is a power of two (block-uniform choice)
   const bool pow2 = (C & (C - 1)) == 0;
   const int lg = 31 - __builtin_clz(static_cast<unsigned>(C));
-  KG float* const full = gp(a.full);
-  // entry (i, j) with o = its packed address and f its full one (when full is not NULL)
+  // entry (i, j) from its unscaled value: o its packed address, f its full one
   auto put = [&](KG float* o, KG float* f, float v) {
-    const float x = v * a.inv_r;
+    const float x = v * inv_r;
     const float y = decay != 0.f ? decay * *o + (1.f - decay) * x : x;
     *o = y;
     if (full) *f = y;
@@ -1065,54 +1069,44 @@ __global__ void __launch_bounds__(256) shift_assemble_kernel(const ShiftAsm* __r
     const int hs = i1 == 0 ? 1 : 0, ws = j1 == 0 ? 1 : 0;  // strips left out: bottom/top, right/left
     KG float* __restrict__ orow = gp(a.out) + packed_off(i, i, d) - i;  // orow[j] for j >= i
     KG float* __restrict__ frow = full + int64_t(i) * d;
-    float bias_v = 0.f;
-    if (a.bias) {  // the bias column: sum over the pixels tap t1 sees
-      bias_v = Su[c1];
+    if (a.bias && tid == 0) {  // the bias column: sum over the pixels tap t1 sees
+      float bias_v = Su[c1];
       if (i1 != 1) bias_v -= Su[(1 + hs) * C + c1];
       if (j1 != 1) bias_v -= Su[(3 + ws) * C + c1];
       if (i1 != 1 && j1 != 1) bias_v += Su[(5 + 2 * hs + ws) * C + c1];
+      put(orow + (d - 1), frow + (d - 1), bias_v);
     }
-    constexpr int U = 8;  // entries per thread in flight
-    for (int j0 = i + tid; j0 < d; j0 += 256 * U) {
-      // branch-free: every entry issues its four loads (T, row strip, column strip,
-      // corner; an in-range stand-in where a term does not apply) before any is used
+    // entries j = i .. 9C-1 of the row, consecutive across the threads (coalesced stores),
+    // U per thread with their loads in flight before any store; only the terms that apply
+    // to an entry's segment are loaded (the segment changes within a wave only at its
+    // boundaries)
+    constexpr int U = 8;
+    const int jend = 9 * C;
+    for (int jb = i + tid; jb < jend; jb += 256 * U) {
       float xt[U], xr[U], xc[U], xx[U];
-      bool fr[U], fc[U], fx[U], fb[U];
+      bool fr[U], fc[U], fx[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int j = min(j0 + 256 * u, d - 1);
-        fb[u] = a.bias && j == d - 1;
-        const int jj = fb[u] ? i : j;  // the bias column reads a stand-in
-        const int t2 = pow2 ? (jj >> lg) : jj / C, c2 = jj - t2 * C, i2 = t2 / 3, j2 = t2 - 3 * i2;
+        const int j = min(jb + 256 * u, jend - 1);
+        const int t2 = pow2 ? (j >> lg) : j / C, c2 = j - t2 * C, i2 = t2 / 3, j2 = t2 - 3 * i2;
         const int dh = i2 - i1, dw = j2 - j1;
         fr[u] = dh == 0 && i1 != 1;
         fc[u] = dw == 0 && j1 != 1;
         fx[u] = fr[u] && fc[u];
         xt[u] = T[tap_index(dh, dw) * C + c2];
-        xr[u] = R0[fr[u] ? hs * C3 * C + dw * C + c2 : c2];
-        xc[u] = C0[fc[u] ? ws * C3 * C + dh * C + c2 : c2];
-        xx[u] = X0[fx[u] ? (2 * hs + ws) * cc + c2 : c2];
+        xr[u] = fr[u] ? R0[hs * C3 * C + dw * C + c2] : 0.f;
+        xc[u] = fc[u] ? C0[ws * C3 * C + dh * C + c2] : 0.f;
+        xx[u] = fx[u] ? X0[(2 * hs + ws) * cc + c2] : 0.f;
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
+        const int j = jb + 256 * u;
+        if (j >= jend) continue;
         float x = xt[u];
         if (fr[u]) x -= xr[u];
         if (fc[u]) x -= xc[u];
         if (fx[u]) x += xx[u];
-        xt[u] = fb[u] ? bias_v : x;
-      }
-      if (decay == 0.f) {
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-          if (j0 + 256 * u < d) {
-            const float x = xt[u] * a.inv_r;
-            orow[j0 + 256 * u] = x;
-            if (full) frow[j0 + 256 * u] = x;
-          }
-      } else {
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-          if (j0 + 256 * u < d) put(orow + j0 + 256 * u, frow + j0 + 256 * u, xt[u]);
+        put(orow + j, frow + j, x);
       }
     }
   }
