@@ -119,6 +119,36 @@ def test_invalid_layer_geometry(lib):
     assert so.kfac_factors(arr, 1, 7, p, p, p, p, ctypes.c_float(0.0), None, 0, None) == -2
 
 
+def test_factors_full_validation(lib):
+    """kfac_factors_full refuses a full-matrix pointer that is not 4-byte aligned and an
+    out-of-range ema_decay before touching the device; the binding checks the full
+    matrices' dtype, shape and count."""
+    import torch
+    layer = synth.Layer("c1x1", 2, 8, 8, 16, 8, 8, 8, 1, 1, 1, 1, 0, 0, 1)
+    so = lib._lib
+    arr = lib._layers([layer])
+    c = ctypes
+    act = (c.c_void_p * 1)(0x10000)        # never dereferenced: the call fails first
+    gout = (c.c_void_p * 1)(0x20000)
+    A = (c.c_void_p * 1)(0x30000)
+    G = (c.c_void_p * 1)(0x40000)
+    good = (c.c_void_p * 1)(0x50000)
+    odd = (c.c_void_p * 1)(0x50002)
+    assert so.kfac_factors_full(arr, 1, 0, act, gout, A, G, odd, good, c.c_float(0.0), None, 0, None) == -1
+    assert b"misaligned" in so.kfac_last_error()
+    assert so.kfac_factors_full(arr, 1, 0, act, gout, A, G, good, odd, c.c_float(0.0), None, 0, None) == -1
+    assert so.kfac_factors_full(arr, 1, 0, act, gout, A, G, good, good, c.c_float(-0.5), None, 0, None) == -1
+    x = torch.zeros(2, 8, 8, 16, dtype=torch.float16)
+    g = torch.zeros(2, 8, 8, 8, dtype=torch.float16)
+    Ap, Gp = torch.zeros(17 * 18 // 2), torch.zeros(8 * 9 // 2)
+    with pytest.raises(TypeError):
+        lib.kfac_factors_full([layer], [x], [g], [Ap], [Gp], [torch.zeros(16, 16)], [None])   # d_A is 17
+    with pytest.raises(TypeError):
+        lib.kfac_factors_full([layer], [x], [g], [Ap], [Gp], [torch.zeros(17, 17, dtype=torch.float64)], [None])
+    with pytest.raises(ValueError):
+        lib.kfac_factors_full([layer], [x], [g], [Ap], [Gp], [], [None])
+
+
 def test_bn_and_precondition_validation(lib):
     so = lib._lib
     c = ctypes
