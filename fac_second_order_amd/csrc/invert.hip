@@ -47,7 +47,7 @@ struct InvDesc {
   float* S;        // working matrix = the output buffer
   float* chol;     // optional U output (nullptr)
   int32_t* info;   // this matrix's info entry
-  float* Ui;       // [TB][TB]  U_kk^-1 (upper triangular)
+  float* E;        // [TB][TB]  E = U_kk^-T, row-major (lower triangular; U_kk^-1 = E^T)
   float* P;        // [TB][TB]  P^-1 = E^T E (full)
   float* Y;        // [GS*TB][ldy] Y panels of the steps of a group (step kg+s in rows s*TB..)
   int32_t n, nb;
@@ -130,8 +130,8 @@ __global__ void __launch_bounds__(TB) inv_damp_kernel(const InvDesc* __restrict_
 //      blocks it still needs: K > J with I <= K (the trailing upper triangle),
 //      K < J (the E part) and K = J, which becomes -M_JI^T E_JJ.
 // The lower blocks right of the current sub-step are never read before their own
-// sub-step overwrites them, so they start as zero. Writes U^-1 = E^T (row-major,
-// TB x TB) and P^-1 to the workspace (the operands of the panel), S_kk = -P^-1, U into
+// sub-step overwrites them, so they start as zero. Writes E (row-major, TB x TB; its
+// transpose is U^-1) and P^-1 to the workspace (the operands of the panel), S_kk = -P^-1, U into
 // chol when asked, and the 1-based failing column into info.
 constexpr int PT = 512;           // threads of the pivot kernel
 constexpr int SB = 32;            // sub-step width
@@ -176,8 +176,8 @@ __device__ __forceinline__ float lane_bcast(float v, int src_lane) {
 // step c+1 is read before the remaining rows of step c are updated, so LDS latency
 // overlaps arithmetic (LDS operations of one wave complete in order). Writes the
 // block back, E_JJ to ej (rows, lower with diagonal) and its transpose to uil
-// (global, pitch TB), U_cc to diagU; returns the first 1-based failing step or 0.
-__device__ __forceinline__ int chol32(float* blk, float* ej, KG float* uil, float* diagU,
+// (global, row-major, pitch TB), U_cc to diagU; returns the first 1-based failing step or 0.
+__device__ __forceinline__ int chol32(float* blk, float* ej, KG float* eg, float* diagU,
                                       float (*urow)[SB / 2], int lane) {
   const int j = lane & 31, h = lane >> 5;
   float d[SB / 2];
@@ -239,7 +239,7 @@ __device__ __forceinline__ int chol32(float* blk, float* ej, KG float* uil, floa
     blk[t * MLD + j] = d[q];
     const float e = j <= t ? d[q] : 0.f;  // E_JJ[t][j]
     ej[t * ELD + j] = e;
-    uil[j * TB + t] = e;
+    eg[t * TB + j] = e;
   }
   return failed;
 }
@@ -275,7 +275,7 @@ __global__ void __launch_bounds__(PT) inv_pivot_kernel(const InvDesc* __restrict
                                                        const int32_t* __restrict__ begin, int a, int k,
                                                        int pre, int rows) {
   // 80.5 KB in all, at most half the LDS of a compute unit, so that a pivot block fits
-  // next to one block of the other matrix kernels (67.6 KB at most): U^-1 and P^-1 go
+  // next to one block of the other matrix kernels (67.6 KB at most): E and P^-1 go
   // straight to global memory, and the staging planes of the diagonal pre-update share
   // their space with the two E_JJ buffers.
   __shared__ __attribute__((aligned(16))) float M[TB * MLD];
@@ -355,7 +355,7 @@ __global__ void __launch_bounds__(PT) inv_pivot_kernel(const InvDesc* __restrict
       // 32 lane masks and LDS addresses out of the loop, which spills them
       int ln = lane;
       asm volatile("" : "+v"(ln));
-      const int f = chol32(rowJ + J * SB, EJ[J & 1], gp(d.Ui) + J * SB * TB + J * SB, diagU + J * SB, urow, ln);
+      const int f = chol32(rowJ + J * SB, EJ[J & 1], gp(d.E) + J * SB * TB + J * SB, diagU + J * SB, urow, ln);
       if (failed == 0 && f) failed = J * SB + f;
     } else if (J > 0) {
       // the rest of sub-step J-1's update: blocks (I, K), I > J-1, (K <= J-1 or
@@ -378,9 +378,9 @@ __global__ void __launch_bounds__(PT) inv_pivot_kernel(const InvDesc* __restrict
       mma32_at(acc, EJ[J & 1], ELD, X, MLD, lane);  // sum_p E_JJ[m][p] X[p][n]
 #pragma unroll
       for (int e = 0; e < 16; ++e) X[acc_row(e, lane) * MLD + (lane & 31)] = acc[e];
-      if (K < J) {  // E_JK is final: its transpose is block (K, J) of U^-1
+      if (K < J) {  // E_JK is final: block (J, K) of E (row-major, coalesced rows)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) gp(d.Ui)[(K * SB + (lane & 31)) * TB + J * SB + acc_row(e, lane)] = acc[e];
+        for (int e = 0; e < 16; ++e) gp(d.E)[(J * SB + acc_row(e, lane)) * TB + K * SB + (lane & 31)] = acc[e];
       }
     }
     __syncthreads();
@@ -447,8 +447,8 @@ __global__ void __launch_bounds__(PT) inv_pivot_kernel(const InvDesc* __restrict
 // a block reads only its own columns of V_j and writes W back only over them, so
 // neither block can overwrite what the other has still to read. The block stages its
 // 128x64 half of V_j in LDS, split into three bf16 planes; waves 0-3 form Y and waves
-// 4-7 W, each wave a 32x64 slab (rows 32w ..) whose A operand (rows of U_kk^-1 = E^T
-// or of P^-1, read as [k][m]) streams from L2 into registers one 16-deep step ahead
+// 4-7 W, each wave a 32x64 slab (rows 32w ..) whose A operand (U_kk^-1 = E^T or P^-1,
+// read as rows of E or of the symmetric P^-1) streams from L2 into registers one 16-deep step ahead
 // and is split there; every product runs as the six bf16 MFMA products of the tile
 // engine (fp32 accuracy). E is lower triangular, so a Y row m only sums k <= m. Blocks b and b+8 (one XCD, so the
 // second read of the A operands hits that XCD's L2) take the two halves of one tile.
@@ -489,20 +489,26 @@ inv_panel_kernel(const InvDesc* __restrict__ desc, const int32_t* __restrict__ b
   const int grp = tid >> 8, w = (tid >> 6) & 3, lane = tid & 63;
   const int ml = lane & 31, kh = lane >> 5;
   const int mr = 32 * w;  // first row of this wave's slab
-  // A operand element (k, m) = Ui[k][m] (Y) or P^-1[k][m] (W); zero for k, m >= bk
+  // A operand element (k, m) = U_kk^-1[k][m] = E[m][k] (Y) or P^-1[k][m] = P^-1[m][k] (W,
+  // symmetric, both triangles stored with the same bits): row m of E or P^-1, so that a
+  // lane's 8 values of k are 32 consecutive bytes; zero for k, m >= bk
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<float*>(grp == 0 ? d.Ui : d.P), 0, TB * TB * 4, 0x00020000);
+      const_cast<float*>(grp == 0 ? d.E : d.P), 0, TB * TB * 4, 0x00020000);
   const int kmax = grp == 0 ? min(bk, mr + 32) : bk;
   const int nstep = (kmax + 15) >> 4;  // 16-deep steps, wave-uniform
   const int m = mr + ml;
-  // lane (m, kh) loads A(k, m) for k = 16c + 8kh .. +7, one step ahead of the MFMAs
+  // lane (m, kh) loads A(k, m) for k = 16c + 8kh .. +7 as two 16-byte loads, one step
+  // ahead of the MFMAs
   auto load_a = [&](float (&a)[8], int c) {
+    const int k8 = 16 * c + 8 * kh;
+    const bool ok = m < bk && c < nstep;
+    const unsigned off = ok ? static_cast<unsigned>(m * TB + k8) * 4u : 0x80000000u;
+    const v4f lo = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+    const v4f hi = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16u, 0, 0));
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int kk = 16 * c + 8 * kh + i;
-      const bool ok = kk < bk && m < bk && c < nstep;
-      a[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-          rs, ok ? static_cast<unsigned>(kk * TB + m) * 4u : 0x80000000u, 0, 0));
+    for (int i = 0; i < 4; ++i) {
+      a[i] = k8 + i < bk ? lo[i] : 0.f;
+      a[4 + i] = k8 + 4 + i < bk ? hi[i] : 0.f;
     }
   };
   float acur[8], anext[8];
@@ -825,7 +831,7 @@ struct InvPlan {
   std::vector<int> order;  // matrices sorted by block count, descending
   std::vector<int32_t> tile_begin, panel_begin, t64_begin;
   std::vector<int32_t> active;  // active[k] = matrices with more than k block steps
-  size_t floats = 0;            // E, Ui, P, Y for all matrices
+  size_t floats = 0;            // E, P, Y for all matrices
   int max_ns = 0;               // block steps of the longest sweep
 };
 
@@ -925,7 +931,7 @@ extern "C" kfac_status kfac_invert(int32_t count, const int32_t* n, const float*
     d.ns = block_steps(n[m]);
     d.nb64 = (n[m] + FT - 1) / FT;
     d.shift = shift[m];
-    d.Ui = wsf + off; off += size_t(TB) * TB;
+    d.E = wsf + off; off += size_t(TB) * TB;
     d.P = wsf + off; off += size_t(TB) * TB;
     d.ldy = (n[m] + 3) / 4 * 4;
     d.Y = wsf + off; off += size_t(GS) * TB * d.ldy;
