@@ -511,8 +511,10 @@ inv_panel_kernel(const InvDesc* __restrict__ desc, const int32_t* __restrict__ b
       a[4 + i] = k8 + 4 + i < bk ? hi[i] : 0.f;
     }
   };
-  float acur[8], anext[8];
-  load_a(acur, 0);  // in flight together with the V loads
+  constexpr int PF = 2;  // steps of A loaded ahead of the products
+  float abuf[PF + 1][8];
+#pragma unroll
+  for (int c = 0; c < PF; ++c) load_a(abuf[c], c);  // in flight together with the V loads
   // V (128 x 64) staged as three bf16 planes [k][n] (exact split, see oct_gemm), rows
   // of 64 swizzled so that the transposing operand reads are conflict-free
   __bf16* vp = reinterpret_cast<__bf16*>(Vs);
@@ -590,8 +592,9 @@ inv_panel_kernel(const InvDesc* __restrict__ desc, const int32_t* __restrict__ b
     const v4bf hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4bf*)(plane + swz(kk + 4, nn)));
     return v8bf{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   };
-  for (int c = 0; c < nstep; ++c) {
-    load_a(anext, c + 1);
+  // the step loop unrolled by PF + 1 so that the register buffers are named statically
+  auto step = [&](int c, float (&acur)[8], float (&anext)[8]) {
+    load_a(anext, c + PF);
     v8bf a0, a1, a2;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -616,8 +619,11 @@ inv_panel_kernel(const InvDesc* __restrict__ desc, const int32_t* __restrict__ b
     acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b[1][1], acc1, 0, 0, 0);
     acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b[0][0], acc0, 0, 0, 0);
     acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b[1][0], acc1, 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acur[i] = anext[i];
+  };
+  for (int c = 0; c < nstep; c += PF + 1) {
+    step(c, abuf[0], abuf[2]);
+    if (c + 1 < nstep) step(c + 1, abuf[1], abuf[0]);
+    if (c + 2 < nstep) step(c + 2, abuf[2], abuf[1]);
   }
   // accumulator register e of block b: row mr + 8(e/4) + 4kh + e%4, column 32b + ml
   if (grp == 0) {
