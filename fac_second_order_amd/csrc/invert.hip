@@ -431,8 +431,14 @@ __global__ void __launch_bounds__(PT) inv_pivot_kernel(const InvDesc* __restrict
         const int r = acc_row(e, lane), c = lane & 31;
         const int i = SB * bi + r, j = SB * bj + c;  // i <= j off the diagonal blocks
         Pg[i * TB + j] = acc[e];
-        if (bi != bj) Pg[j * TB + i] = acc[e];
         if (i <= j && j < bk) Sk[int64_t(i) * n + j] = -acc[e];
+      }
+      if (bi != bj) {  // the mirror: registers 4g..4g+3 of a lane are 4 consecutive rows i
+        const int j = SB * bj + (lane & 31);
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<KG v4f*>(Pg + j * TB + SB * bi + 8 * g + 4 * (lane >> 5)) =
+              v4f{acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
       }
     }
   }
@@ -455,6 +461,8 @@ __global__ void __launch_bounds__(PT) inv_pivot_kernel(const InvDesc* __restrict
 // For slot >= 1, blocks from `base` on give step k-1 (panel slot-1) to the diagonal
 // blocks of the group's later pivots k+1.. (block (p, u): matrix p, pivot kg+1+u),
 // which nothing else in the launch reads or writes; Vs is their staging LDS.
+// 16 bytes at a 4-byte aligned address (rows of an odd order start anywhere)
+typedef float f4u __attribute__((ext_vector_type(4), aligned(4)));
 constexpr int PP = 512;        // panel threads
 constexpr int PH = TB / 2;     // columns of V_j per block
 constexpr int WTP = TB + 1;    // pitch of the transposed W half in LDS
@@ -552,30 +560,40 @@ inv_panel_kernel(const InvDesc* __restrict__ desc, const int32_t* __restrict__ b
       *reinterpret_cast<v4bf*>(vp + VPL + o) = p1;
       *reinterpret_cast<v4bf*>(vp + 2 * VPL + o) = p2;
     }
-  } else {  // V[r][c] = S[j0 + c][k0 + r]: thread 4 rows 4(tid % 8 + 8q).. of column tid / 8
-    const int c = tid >> 3;
-    float v[4][4];
+  } else {  // V[r][c] = S[j0 + c][k0 + r]: thread the 4x4 block of rows 4(tid / 16).. and
+           // columns 4(tid % 16)..; a column of V is a row of S, read 16 bytes at a time
+    const int c4 = 4 * (tid & 15), r4 = 4 * (tid >> 4);
+    float v[4][4];  // v[row][column]
+    if (r4 + 4 <= bk && c4 + 4 <= bj) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int r4 = 4 * ((tid & 7) + 8 * q);
+      for (int uc = 0; uc < 4; ++uc) {
+        const f4u x = *reinterpret_cast<const KG f4u*>(gp(d.S) + int64_t(j0 + c4 + uc) * n + k0 + r4);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float x = gp(d.S)[int64_t(j0 + min(c, bj - 1)) * n + k0 + min(r4 + u, bk - 1)];
-        v[q][u] = (r4 + u < bk && c < bj) ? x : 0.f;
+        for (int ur = 0; ur < 4; ++ur) v[ur][uc] = x[ur];
       }
+    } else {
+#pragma unroll
+      for (int uc = 0; uc < 4; ++uc)
+#pragma unroll
+        for (int ur = 0; ur < 4; ++ur) {
+          const int r = r4 + ur, c = c4 + uc;
+          const float x = gp(d.S)[int64_t(j0 + min(c, bj - 1)) * n + k0 + min(r, bk - 1)];
+          v[ur][uc] = (r < bk && c < bj) ? x : 0.f;
+        }
     }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int r4 = 4 * ((tid & 7) + 8 * q);
+    for (int ur = 0; ur < 4; ++ur) {
+      v4bf p0, p1, p2;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int uc = 0; uc < 4; ++uc) {
         __bf16 h0, h1, h2;
-        split3(v[q][u], h0, h1, h2);
-        const int o = swz(r4 + u, c & ~3) + (c & 3);
-        vp[o] = h0;
-        vp[VPL + o] = h1;
-        vp[2 * VPL + o] = h2;
+        split3(v[ur][uc], h0, h1, h2);
+        p0[uc] = h0; p1[uc] = h1; p2[uc] = h2;
       }
+      const int o = swz(r4 + ur, c4);
+      *reinterpret_cast<v4bf*>(vp + o) = p0;
+      *reinterpret_cast<v4bf*>(vp + VPL + o) = p1;
+      *reinterpret_cast<v4bf*>(vp + 2 * VPL + o) = p2;
     }
   }
   v16f acc0, acc1;
@@ -757,7 +775,6 @@ __global__ void __launch_bounds__(256) inv_border_kernel(const InvDesc* __restri
 // the border move them as 16-byte accesses (4-byte aligned: rows of an order that
 // is not a multiple of 4 start anywhere), the others entry by entry; the mirror goes
 // through LDS so that its stores also run along rows.
-typedef float f4u __attribute__((ext_vector_type(4), aligned(4)));
 __global__ void __launch_bounds__(256) inv_finish_kernel(const InvDesc* __restrict__ desc,
                                                          const int32_t* __restrict__ begin, int count) {
   __shared__ float s[FT][FT + 1];
