@@ -133,6 +133,8 @@ __global__ void __launch_bounds__(TB) inv_damp_kernel(const InvDesc* __restrict_
 // sub-step overwrites them, so they start as zero. Writes E (row-major, TB x TB; its
 // transpose is U^-1) and P^-1 to the workspace (the operands of the panel), S_kk = -P^-1, U into
 // chol when asked, and the 1-based failing column into info.
+// 16 bytes at a 4-byte aligned address (rows of an odd order start anywhere)
+typedef float f4u __attribute__((ext_vector_type(4), aligned(4)));
 constexpr int PT = 512;           // threads of the pivot kernel
 constexpr int SB = 32;            // sub-step width
 constexpr int MLD = TB + 4;       // LDS pitch of M
@@ -461,8 +463,6 @@ __global__ void __launch_bounds__(PT) inv_pivot_kernel(const InvDesc* __restrict
 // For slot >= 1, blocks from `base` on give step k-1 (panel slot-1) to the diagonal
 // blocks of the group's later pivots k+1.. (block (p, u): matrix p, pivot kg+1+u),
 // which nothing else in the launch reads or writes; Vs is their staging LDS.
-// 16 bytes at a 4-byte aligned address (rows of an odd order start anywhere)
-typedef float f4u __attribute__((ext_vector_type(4), aligned(4)));
 constexpr int PP = 512;        // panel threads
 constexpr int PH = TB / 2;     // columns of V_j per block
 constexpr int WTP = TB + 1;    // pitch of the transposed W half in LDS
@@ -537,13 +537,22 @@ inv_panel_kernel(const InvDesc* __restrict__ desc, const int32_t* __restrict__ b
   if (j > k) {  // V[r][c] = S[k0 + r][j0 + c]: thread 4 columns 4(tid % 16).., rows tid / 16 + 32q
     const int c4 = 4 * (tid & 15), ra = tid >> 4;
     float v[4][4];
+    if (bk == TB && c4 + 4 <= bj) {  // 16-byte row segments
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int r = ra + 32 * q;
+      for (int q = 0; q < 4; ++q) {
+        const f4u x = *reinterpret_cast<const KG f4u*>(gp(d.S) + int64_t(k0 + ra + 32 * q) * n + j0 + c4);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float x = gp(d.S)[int64_t(k0 + min(r, bk - 1)) * n + j0 + min(c4 + u, bj - 1)];
-        v[q][u] = (r < bk && c4 + u < bj) ? x : 0.f;
+        for (int u = 0; u < 4; ++u) v[q][u] = x[u];
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = ra + 32 * q;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float x = gp(d.S)[int64_t(k0 + min(r, bk - 1)) * n + j0 + min(c4 + u, bj - 1)];
+          v[q][u] = (r < bk && c4 + u < bj) ? x : 0.f;
+        }
       }
     }
 #pragma unroll
