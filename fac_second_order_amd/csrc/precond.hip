@@ -88,14 +88,17 @@ gemm_tn64_kernel(const GemmDesc* __restrict__ desc, const int32_t* __restrict__ 
   }
 }
 
-// Load forms of a problem's operands: 16-byte groups for fp32 rows whose pitch is a
-// multiple of 4 floats on a 16-byte aligned base, single elements otherwise. Every
-// operand is read through a raw buffer, so it must span less than 2^31 bytes
-// (operands_fit, checked before anything is enqueued).
+// Load forms of a problem's operands: 16-byte groups for fp32 operands (rows of any
+// pitch, including the odd ones of d_A = 128m + 1: a group only needs 4-byte
+// alignment, and one that runs past a row's end reads the next row or, past the
+// buffer's range, zeros dword by dword, which reach only output rows or columns past
+// the operand's last, never stored), single elements for fp16. Every operand is read
+// through a raw buffer, so it must span less than 2^31 bytes (operands_fit, checked
+// before anything is enqueued).
 static void set_modes(GemmDesc& g) {
-  g.a_mode = (g.lda % 4 == 0 && reinterpret_cast<uintptr_t>(g.A) % 16 == 0) ? LD_V4 : LD_F32;
+  g.a_mode = reinterpret_cast<uintptr_t>(g.A) % 4 == 0 ? LD_V4 : LD_F32;
   if (g.b_f16) g.b_mode = LD_F16;
-  else g.b_mode = (g.ldb % 4 == 0 && reinterpret_cast<uintptr_t>(g.B) % 16 == 0) ? LD_V4 : LD_F32;
+  else g.b_mode = reinterpret_cast<uintptr_t>(g.B) % 4 == 0 ? LD_V4 : LD_F32;
 }
 
 // The largest operand of a layer (G^-1 or A^-1, d x d fp32; dW, d_G x d_A) spans less

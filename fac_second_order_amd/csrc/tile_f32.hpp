@@ -40,9 +40,10 @@ __device__ inline Operand op_rows_h(const _Float16* src, int64_t ld, int kv, int
   return Operand{src, ld, kv, m0, mv};
 }
 
-// Load forms of an operand: 16-byte groups (fp32 rows whose pitch is a multiple of 4
-// floats on a 16-byte aligned base, m0 % 4 == 0), single fp32 values, single fp16
-// values.
+// Load forms of an operand: 16-byte groups (fp32 rows on a 4-byte aligned base, m0 %
+// 4 == 0; a group may run past a row's end into the next row, or past the buffer's
+// range, which a raw buffer load reads as zeros dword by dword), single fp32 values,
+// single fp16 values.
 constexpr int LD_V4 = 0, LD_F32 = 1, LD_F16 = 2;
 
 // Raw buffer over rows [0, kv) of a rows-form operand (callers guarantee that
@@ -165,8 +166,9 @@ __device__ inline void oct_store_t(const Oct& o, float* dst, int64_t ld, int rva
 // issued, and one outside the operand (k >= kv or m >= mv) gets an offset past the
 // buffer's range, for which it returns zeros without touching memory. With the same
 // loads on every path, the wait before an LDS store covers only its own chunk. LD_V4
-// reads each 4-group that starts below mv whole: its entries at or past mv are row
-// padding and reach only output rows or columns >= mv, which callers never store.
+// reads each 4-group that starts below mv whole: its entries at or past mv (row
+// padding, the next row's first entries, or zeros past the buffer's range) reach only
+// output rows or columns >= mv, which callers never store.
 template <int MODE = LD_V4>
 __device__ inline void oct_fetch(const Operand& o, __amdgpu_buffer_rsrc_t rs, int k0, float4 (&r)[2]) {
   const int kg = threadIdx.x >> 5, mg = threadIdx.x & 31;
