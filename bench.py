@@ -37,6 +37,7 @@ PEAK_FP16_MFMA = 2516.6  # TFLOP/s, MI355X dense fp16 (and bf16) matrix
 # update, the preconditioning and the refinement's correction): the bf16 peak over six
 # is the bound of their algorithmic fp32 flops.
 PEAK_X3 = round(PEAK_FP16_MFMA / 6, 1)
+PEAK_FP32_MFMA = 157.3   # TFLOP/s, MI355X dense fp32 matrix (the same products on fp32 MFMA)
 
 # kernels whose algorithmic work per launch bench.py models (roofline candidates)
 MODELLED = {"inv_update_kernel", "syrk_tile_kernel", "gemm_tn_kernel", "gemm_tn64_kernel",
@@ -739,6 +740,9 @@ def main():
                         "frac": round(achieved / peak, 4), "traffic": measured_traffic(name, bool(st.side)), "kernel": name,
                         "launches": n, "avg_launch_us": round(1e3 * ms / n, 2),
                         "algorithmic_per_launch": total_work / n}
+            if peak == PEAK_X3:
+                roofline["peak_basis"] = "bf16 MFMA peak / 6: each fp32 product is six bf16 MFMA products"
+                roofline["frac_fp32_mfma_peak"] = round(achieved / PEAK_FP32_MFMA, 4)
         if roofline and top != name:
             roofline["largest_kernel"] = top
         elif name in ("bn_partial_kernel", "unpack_kernel"):
