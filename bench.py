@@ -53,21 +53,23 @@ LR = 0.01                # learning rate of the parameter update
 # profiles/resnet50_step_hbm_counters.md; keyed by kernel and by whether the step ran
 # on two streams (the launches then hold fewer tiles each). Reported only while the
 # kernel's source text still hashes to the value it was measured with.
-MEASURED_TRAFFIC = {("inv_update_kernel", True): (606600000, "7923abad0c88d1c63fbc3b752be8fc86dea84265")}
+MEASURED_TRAFFIC = {("inv_update_kernel", True): (829600000, "f79e6f820366608df82a3fc2e36bd2ea421f53dc")}
 CSRC = os.path.join(ROOT, "fac_second_order_amd", "csrc")
 
 
 def kernel_source_sha(name):
-    """Hash of the update kernel's own source: its tile routine, the kernel, and the
-    tile engine headers they use."""
+    """Hash of the update kernel's own source: its tile routine, the kernel, the tile
+    engine headers they use, and the group size (the block steps one launch applies)."""
     import hashlib
+    import re
     if name != "inv_update_kernel":
         return None
     inv = open(os.path.join(CSRC, "invert.hip")).read()
     tile = inv[inv.index("// Update of step k:"):inv.index("// Pivot of step k. Sub-step J runs")]
     kern = inv[inv.index("// Update after the group of steps"):inv.index("// Bordered last column")]
+    group = re.search(r"^#define KFAC_INV_GROUP \d+$", inv, re.M).group(0)
     text = tile + kern + open(os.path.join(CSRC, "tile_f32.hpp")).read() + \
-        open(os.path.join(CSRC, "common.hpp")).read()
+        open(os.path.join(CSRC, "common.hpp")).read() + group
     return hashlib.sha1(text.encode()).hexdigest()
 
 

@@ -68,7 +68,7 @@ __host__ __device__ inline int block_steps(int n) {
 // Block steps per update launch (a group): the update of a group applies all its
 // steps at once as one rank-(G*TB) product.
 #ifndef KFAC_INV_GROUP
-#define KFAC_INV_GROUP 4
+#define KFAC_INV_GROUP 6
 #endif
 constexpr int GS = KFAC_INV_GROUP;
 static_assert(GS >= 1 && GS <= 8, "group size");
