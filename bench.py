@@ -53,29 +53,28 @@ LR = 0.01                # learning rate of the parameter update
 # profiles/resnet50_step_hbm_counters.md; keyed by kernel and by whether the step ran
 # on two streams (the launches then hold fewer tiles each). Reported only while the
 # kernel's source text still hashes to the value it was measured with.
-MEASURED_TRAFFIC = {("inv_update_kernel", True): (829600000, "f79e6f820366608df82a3fc2e36bd2ea421f53dc")}
+MEASURED_TRAFFIC = {("inv_update_kernel", True): (829600000, "1882cb717ea2a1ce25667bf516af88a5691a2c8f")}
 CSRC = os.path.join(ROOT, "fac_second_order_amd", "csrc")
 
 
-def kernel_source_sha(name):
-    """Hash of the update kernel's own source: its tile routine, the kernel, the tile
-    engine headers they use, and the group size (the block steps one launch applies)."""
+def kernel_source_sha(name, group):
+    """Hash of the update kernel's own source (its tile routine, the kernel and the tile
+    engine headers they use) and of the group size the library was built with (the block
+    steps one launch applies, from kfac_invert_schedule)."""
     import hashlib
-    import re
     if name != "inv_update_kernel":
         return None
     inv = open(os.path.join(CSRC, "invert.hip")).read()
     tile = inv[inv.index("// Update of step k:"):inv.index("// Pivot of step k. Sub-step J runs")]
     kern = inv[inv.index("// Update after the group of steps"):inv.index("// Bordered last column")]
-    group = re.search(r"^#define KFAC_INV_GROUP \d+$", inv, re.M).group(0)
     text = tile + kern + open(os.path.join(CSRC, "tile_f32.hpp")).read() + \
-        open(os.path.join(CSRC, "common.hpp")).read() + group
+        open(os.path.join(CSRC, "common.hpp")).read() + f"\ngroup {group}"
     return hashlib.sha1(text.encode()).hexdigest()
 
 
-def measured_traffic(name, side_stream):
+def measured_traffic(name, side_stream, group):
     rec = MEASURED_TRAFFIC.get((name, side_stream))
-    if rec is None or kernel_source_sha(name) != rec[1]:
+    if rec is None or kernel_source_sha(name, group) != rec[1]:
         return None
     return rec[0]
 
@@ -644,7 +643,8 @@ def main():
     args.batch = args.batch or 32
     layers = synth.conv_layers(args.batch)
     bns = synth.bn_layers(args.batch)
-    w = work(layers, bns, kfac.kfac_invert_schedule()[1])
+    group = kfac.kfac_invert_schedule()[1]
+    w = work(layers, bns, group)
     progress("drawing inputs")
     act, gout, grads, xhat, bgout = make_inputs(layers, bns, dev)
     weights, bn_params = make_params(layers, bns, dev)
@@ -739,7 +739,7 @@ def main():
             total_work, bound, peak = per_launch[name]
             achieved = total_work / (ms * 1e-3) / 1e12      # = per-launch work / average duration
             roofline = {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
-                        "frac": round(achieved / peak, 4), "traffic": measured_traffic(name, bool(st.side)), "kernel": name,
+                        "frac": round(achieved / peak, 4), "traffic": measured_traffic(name, bool(st.side), group), "kernel": name,
                         "launches": n, "avg_launch_us": round(1e3 * ms / n, 2),
                         "algorithmic_per_launch": total_work / n}
             if peak == PEAK_X3:

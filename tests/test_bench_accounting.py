@@ -53,3 +53,16 @@ def test_resnet50_update_share(bench):
     assert upd + row == total
     # the updates are most of the method's sum of n^3 (the rest is pivots and panels)
     assert 0.85 < total / sum(n ** 3 for n in n_all) < 0.95
+
+
+def test_measured_traffic_keyed_to_source_and_group(bench):
+    """A measured byte count is reported only for the kernel, stream mode and group size
+    it was measured with, and only while the kernel's source hashes to the recorded value."""
+    for (name, side), (value, sha) in bench.MEASURED_TRAFFIC.items():
+        group = next(g for g in range(1, 9) if bench.kernel_source_sha(name, g) == sha)
+        assert bench.measured_traffic(name, side, group) == value
+        assert bench.measured_traffic(name, not side, group) is None
+        for other in range(1, 9):
+            if other != group:
+                assert bench.measured_traffic(name, side, other) is None
+    assert bench.kernel_source_sha("gemm_tn_kernel", 6) is None
